@@ -1,0 +1,255 @@
+"""Seeded synthetic inputs for the Gated DeltaNet prefill forward.
+
+This module only draws numbers. It holds none of the method's arithmetic, so both
+the CPU oracle side and the HIP side can take their inputs from it.
+
+Generator
+---------
+* SplitMix64 (Steele, Lea and Flood, "Fast splittable pseudorandom number
+  generators", OOPSLA 2014) in counter form: value ``i`` of a stream is the
+  SplitMix64 finaliser applied to ``stream_seed + (i + 1) * 0x9E3779B97F4A7C15``.
+* Uniforms take the top 53 bits: ``u = (z >> 11) * 2**-53`` in [0, 1).
+* Normals come from the Box-Muller transform (Box and Muller, 1958) on pairs of
+  uniforms, evaluated in fp64.
+* Every tensor has its own stream: ``stream_seed = mix(seed ^ tensor_id)``.
+* bf16 tensors are the fp64 draw rounded to fp32 (round to nearest even), then
+  to bf16 (round to nearest even). They are returned as raw uint16 bit patterns;
+  the exact value of each is ``float32(bits << 16)``.
+
+Workloads
+---------
+The five named workloads follow the problem statement of the pymllm
+``gdn_extend_chunkwise`` page (packed varlen tokens, H q/k heads, HV value heads,
+fp32 state pool indexed per request) at the sizes listed in ``WORKLOADS``.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Optional, Sequence
+
+import numpy as np
+
+_GOLDEN = np.uint64(0x9E3779B97F4A7C15)
+_M1 = np.uint64(0xBF58476D1CE4E5B9)
+_M2 = np.uint64(0x94D049BB133111EB)
+
+# tensor ids for per-tensor streams
+TID_Q, TID_K, TID_V, TID_A, TID_B, TID_ALOG, TID_DTB, TID_STATE, TID_LEN, TID_PERM = range(1, 11)
+
+
+def _mix(z: np.ndarray) -> np.ndarray:
+    """SplitMix64 finaliser on a uint64 array (wrapping arithmetic)."""
+    with np.errstate(over="ignore"):
+        z = (z ^ (z >> np.uint64(30))) * _M1
+        z = (z ^ (z >> np.uint64(27))) * _M2
+        return z ^ (z >> np.uint64(31))
+
+
+def stream_seed(seed: int, tensor_id: int) -> np.uint64:
+    s = np.array([(seed ^ tensor_id) & 0xFFFFFFFFFFFFFFFF], dtype=np.uint64)
+    return _mix(s)[0]
+
+
+def raw_u64(sseed: np.uint64, start: int, count: int) -> np.ndarray:
+    """Values ``start .. start+count-1`` of the counter stream."""
+    idx = np.arange(start + 1, start + count + 1, dtype=np.uint64)
+    with np.errstate(over="ignore"):
+        return _mix(sseed + idx * _GOLDEN)
+
+
+def uniform(seed: int, tensor_id: int, n: int, start: int = 0) -> np.ndarray:
+    z = raw_u64(stream_seed(seed, tensor_id), start, n)
+    return (z >> np.uint64(11)).astype(np.float64) * (2.0 ** -53)
+
+
+def normal(seed: int, tensor_id: int, n: int, block: int = 1 << 22) -> np.ndarray:
+    """n standard normals in fp64 (Box-Muller on uniform pairs), drawn in blocks."""
+    out = np.empty(n, dtype=np.float64)
+    sseed = stream_seed(seed, tensor_id)
+    npairs = (n + 1) // 2
+    for p0 in range(0, npairs, block):
+        p1 = min(npairs, p0 + block)
+        z = raw_u64(sseed, 2 * p0, 2 * (p1 - p0))
+        u = (z >> np.uint64(11)).astype(np.float64) * (2.0 ** -53)
+        u1 = u[0::2]
+        u2 = u[1::2]
+        r = np.sqrt(-2.0 * np.log1p(-u1))  # 1-u1 in (0,1]: log is finite
+        th = 2.0 * math.pi * u2
+        pair = np.empty(2 * (p1 - p0), dtype=np.float64)
+        pair[0::2] = r * np.cos(th)
+        pair[1::2] = r * np.sin(th)
+        lo = 2 * p0
+        hi = min(n, 2 * p1)
+        out[lo:hi] = pair[: hi - lo]
+    return out
+
+
+def f32_to_bf16_bits(x32: np.ndarray) -> np.ndarray:
+    """Round fp32 to bf16 (nearest even); returns uint16 bit patterns."""
+    u = np.ascontiguousarray(x32, dtype=np.float32).view(np.uint32)
+    bias = ((u >> np.uint32(16)) & np.uint32(1)) + np.uint32(0x7FFF)
+    return ((u + bias) >> np.uint32(16)).astype(np.uint16)
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    return (np.ascontiguousarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+@dataclasses.dataclass
+class Problem:
+    """One prefill call's inputs, host side, exactly as the boundary receives them.
+
+    q, k: [N, H, dk]; v: [N, HV, dv]. For dtype "bf16" they are uint16 bit
+    patterns, for "f32" float32. a, b: [N, HV] fp32. A_log, dt_bias: [HV] fp32.
+    state_pool: [pool, HV, dv, dk] fp32. cache_indices: [B] int64.
+    cu_seqlens: [B+1] int64.
+    """
+    name: str
+    dtype: str
+    H: int
+    HV: int
+    dk: int
+    dv: int
+    q: np.ndarray
+    k: np.ndarray
+    v: np.ndarray
+    a: np.ndarray
+    b: np.ndarray
+    A_log: np.ndarray
+    dt_bias: np.ndarray
+    state_pool: np.ndarray
+    cache_indices: np.ndarray
+    cu_seqlens: np.ndarray
+    chunk_size: int = 64
+    seed: int = 0
+
+    @property
+    def N(self) -> int:
+        return int(self.cu_seqlens[-1])
+
+    @property
+    def B(self) -> int:
+        return int(self.cache_indices.shape[0])
+
+    @property
+    def pool(self) -> int:
+        return int(self.state_pool.shape[0])
+
+    def values_f32(self, name: str) -> np.ndarray:
+        """q, k or v as exact fp32 values (bf16 widens exactly)."""
+        x = getattr(self, name)
+        return bf16_bits_to_f32(x) if self.dtype == "bf16" else x
+
+
+def _draw(seed: int, tid: int, shape: Sequence[int], dtype: str, mean: float = 0.0, std: float = 1.0):
+    n = int(np.prod(shape)) if len(shape) else 1
+    x = normal(seed, tid, n) * std + mean
+    x32 = x.astype(np.float32).reshape(shape)
+    if dtype == "bf16":
+        return f32_to_bf16_bits(x32).reshape(shape)
+    return x32
+
+
+def make_problem(
+    seed: int,
+    lengths: Sequence[int],
+    H: int,
+    HV: int,
+    dk: int,
+    dv: int,
+    dtype: str = "bf16",
+    pool: Optional[int] = None,
+    cache_indices: Optional[Sequence[int]] = None,
+    a_mean: float = 0.0,
+    b_mean: float = 0.0,
+    state_std: float = 0.0,
+    dt_bias_std: float = 0.1,
+    chunk_size: int = 64,
+    name: str = "custom",
+) -> Problem:
+    """Generic seeded problem: q, k, v ~ N(0,1) raw (not normalised), a ~ N(a_mean,1),
+    b ~ N(b_mean,1), A_log = log(1 + 15u) (so exp(A_log) ~ U[1,16]),
+    dt_bias ~ N(0, dt_bias_std^2), state_pool ~ N(0, state_std^2) (zeros if 0)."""
+    assert dtype in ("bf16", "f32")
+    lengths = [int(x) for x in lengths]
+    B = len(lengths)
+    cu = np.zeros(B + 1, dtype=np.int64)
+    cu[1:] = np.cumsum(lengths)
+    N = int(cu[-1])
+    if pool is None:
+        pool = B
+    if cache_indices is None:
+        cache_indices = list(range(B))
+    idx = np.asarray(cache_indices, dtype=np.int64)
+    q = _draw(seed, TID_Q, (N, H, dk), dtype)
+    k = _draw(seed, TID_K, (N, H, dk), dtype)
+    v = _draw(seed, TID_V, (N, HV, dv), dtype)
+    a = _draw(seed, TID_A, (N, HV), "f32", mean=a_mean)
+    b = _draw(seed, TID_B, (N, HV), "f32", mean=b_mean)
+    A_log = np.log1p(15.0 * uniform(seed, TID_ALOG, HV)).astype(np.float32)
+    dt_bias = (normal(seed, TID_DTB, HV) * dt_bias_std).astype(np.float32)
+    if state_std > 0:
+        state = (normal(seed, TID_STATE, pool * HV * dv * dk) * state_std).astype(np.float32)
+        state = state.reshape(pool, HV, dv, dk)
+    else:
+        state = np.zeros((pool, HV, dv, dk), dtype=np.float32)
+    return Problem(name=name, dtype=dtype, H=H, HV=HV, dk=dk, dv=dv, q=q, k=k, v=v, a=a, b=b,
+                   A_log=A_log, dt_bias=dt_bias, state_pool=state, cache_indices=idx,
+                   cu_seqlens=cu, chunk_size=chunk_size, seed=seed)
+
+
+def seeded_permutation(seed: int, tid: int, n: int) -> np.ndarray:
+    """Fisher-Yates shuffle of 0..n-1 driven by the uniform stream."""
+    u = uniform(seed, tid, n)
+    perm = np.arange(n, dtype=np.int64)
+    for i in range(n - 1, 0, -1):
+        j = int(u[n - 1 - i] * (i + 1))
+        perm[i], perm[j] = perm[j], perm[i]
+    return perm
+
+
+# Named workloads. Seeds are 1000 + index.
+WORKLOADS = {
+    0: "tiny fp32: B=1 T=256 H=HV=1 dk=dv=64 C=64, zero state",
+    1: "dense batch bf16: B=4 x T=4096 H=HV=16 dk=dv=128 C=64, zero state",
+    2: "varlen GQA bf16: B=8 lengths U[1,8192] H=16 HV=32 dk=dv=128 C=64, pool 64 ~N(0,0.01)",
+    3: "wide head bf16: B=1 T=16384 H=HV=8 dk=dv=256 C=64, zero state",
+    4: "long prefill decay stress bf16: B=1 T=131072 H=16 HV=32 dk=dv=128 C=64, a~N(-4,1) b~N(2,1)",
+}
+
+
+def workload_lengths(idx: int) -> list:
+    seed = 1000 + idx
+    if idx == 0:
+        return [256]
+    if idx == 1:
+        return [4096] * 4
+    if idx == 2:
+        u = uniform(seed, TID_LEN, 8)
+        return [1 + int(8192 * x) for x in u]
+    if idx == 3:
+        return [16384]
+    if idx == 4:
+        return [131072]
+    raise ValueError(idx)
+
+
+def workload(idx: int) -> Problem:
+    """The five named workloads (see WORKLOADS)."""
+    seed = 1000 + idx
+    L = workload_lengths(idx)
+    if idx == 0:
+        return make_problem(seed, L, 1, 1, 64, 64, dtype="f32", name="tiny_f32")
+    if idx == 1:
+        return make_problem(seed, L, 16, 16, 128, 128, name="dense_batch_bf16")
+    if idx == 2:
+        perm = seeded_permutation(seed, TID_PERM, 64)
+        return make_problem(seed, L, 16, 32, 128, 128, pool=64, cache_indices=perm[:8],
+                            state_std=0.1, name="varlen_gqa_bf16")
+    if idx == 3:
+        return make_problem(seed, L, 8, 8, 256, 256, name="wide_head_bf16")
+    if idx == 4:
+        return make_problem(seed, L, 16, 32, 128, 128, a_mean=-4.0, b_mean=2.0, state_std=0.1,
+                            name="long_decay_bf16")
+    raise ValueError(idx)

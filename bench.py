@@ -1,0 +1,251 @@
+"""Benchmark of the GDN chunkwise prefill forward on one MI355X.
+
+A step is one gdn_prefill_fwd call (every stage of the path) over the dense-batch
+bf16 workload: 4 requests x 4096 tokens, H = HV = 16, dk = dv = 128, C = 64, with
+inputs resident in HBM. Prints one JSON line.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # dense
+WORKLOAD_INDEX = 1
+METRIC = "GDN prefill tokens/sec + effective TFLOPs (% MFMA/HBM roof), dk=dv=128 C=64"
+
+
+def algorithmic_flops_per_token_vhead(dk: int, dv: int, C: int) -> float:
+    """Three state contractions (6 dk dv), the triangular in-chunk products
+    (C (3 dk + 2 dv)) and the inverse (C^2 / 3)."""
+    return 6.0 * dk * dv + C * (3.0 * dk + 2.0 * dv) + C * C / 3.0
+
+
+def path_bytes(p, s_qkv: int) -> float:
+    """q, k, v read once, o written once, a and b (fp32), touched states read and written."""
+    touched = int(sum(1 for L in (p.cu_seqlens[1:] - p.cu_seqlens[:-1]) if L > 0))
+    return (p.N * (2 * p.H * p.dk * s_qkv + 2 * p.HV * p.dv * s_qkv + 8 * p.HV)
+            + touched * p.HV * p.dv * p.dk * 8)
+
+
+def stage_bytes(p, s_qkv: int, s_ws: int, n_chunks: int):
+    """Algorithmic bytes each stage must move: its inputs read once, its outputs written
+    once. Rows are chunk rows (n_chunks * C, padding included) for per-chunk data."""
+    rows = n_chunks * p.chunk_size
+    touched = int(sum(1 for L in (p.cu_seqlens[1:] - p.cu_seqlens[:-1]) if L > 0))
+    gate = p.N * p.HV * 8 + rows * p.HV * 12
+    prep = (p.N * p.H * p.dk * s_qkv + p.N * p.HV * p.dv * s_qkv + rows * p.HV * 12
+            + rows * p.HV * (p.dk + p.dv) * s_ws)
+    state = (2 * p.N * p.H * p.dk * s_qkv + rows * p.HV * (p.dk + p.dv) * s_ws + rows * p.HV * 8
+             + p.N * p.HV * p.dv * s_qkv + touched * p.HV * p.dv * p.dk * 8)
+    return {"gate": gate, "chunk_prep": prep, "state": state}
+
+
+def kernel_source_hash() -> str:
+    csrc = os.path.join(ROOT, "gated_deltanet_prefill_gdn_amd", "csrc")
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".h")):
+            h.update(f.encode())
+            h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(kernel: str, src_hash: str, launches_per_step: int = 1):
+    """HBM bytes per launch from committed rocprofv3 counter summaries, if they were taken
+    on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        d = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    ent = d.get(kernel)
+    if not ent or ent.get("source_hash") != src_hash:
+        return None
+    return ent.get("hbm_bytes_per_launch")
+
+
+class Hip:
+    """hipEvent helpers from the HIP runtime torch already loaded."""
+
+    def __init__(self):
+        self.lib = ctypes.CDLL("libamdhip64.so.7")
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def event(self):
+        e = ctypes.c_void_p()
+        rc = self.lib.hipEventCreate(ctypes.byref(e))
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreate failed: {rc}")
+        return e.value
+
+    def elapsed_ms(self, a, b) -> float:
+        ms = ctypes.c_float()
+        rc = self.lib.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b))
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed: {rc}")
+        return float(ms.value)
+
+    def destroy(self, e):
+        self.lib.hipEventDestroy(ctypes.c_void_p(e))
+
+
+def cpu_baseline(p):
+    """The oracle (fp64 token recurrence) as it stands, on this host's cores, over the
+    whole workload (every request and value head); about 10-20 s of CPU work."""
+    import oracle
+    threads = oracle.default_threads()
+    t0 = time.perf_counter()
+    oracle.prefill(p, nthreads=threads)
+    dt = time.perf_counter() - t0
+    return {"value": p.N / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"whole workload ({p.B} requests x {p.N // p.B} tokens, {p.HV} value heads), "
+                      f"fp64 recurrence, {dt:.2f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cold-steps", type=int, default=5,
+                    help="extra steps timed one by one after a 512 MiB cache flush")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(--gpus {args.gpus} requested).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import gdn_synth
+    import gated_deltanet_prefill_gdn_amd as gdn
+
+    p = gdn_synth.workload(WORKLOAD_INDEX)
+    dev = torch.device("cuda:0")
+
+    def t(x, dt=None):
+        x = torch.from_numpy(np.ascontiguousarray(x))
+        return (x.view(dt) if dt is not None else x).to(dev)
+
+    q = t(p.q.view(np.int16), torch.bfloat16)
+    k = t(p.k.view(np.int16), torch.bfloat16)
+    v = t(p.v.view(np.int16), torch.bfloat16)
+    a, b, A_log, dt_bias = t(p.a), t(p.b), t(p.A_log), t(p.dt_bias)
+    pool = t(p.state_pool.copy())
+    idx, cu = t(p.cache_indices), t(p.cu_seqlens)
+    out = torch.empty((p.N, p.HV, p.dv), dtype=torch.bfloat16, device=dev)
+    prob = gdn.problem_of(q, k, v, pool, idx)
+    ws = torch.empty(gdn.gdn_prefill_workspace_size(prob), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(events=None):
+        if events is None:
+            gdn.gdn_prefill_fwd(q, k, v, a, b, A_log, dt_bias, pool, idx, cu, out=out,
+                                workspace=ws, stream=stream)
+        else:
+            gdn.gdn_prefill_fwd_events(q, k, v, a, b, A_log, dt_bias, pool, idx, cu, events,
+                                       out=out, workspace=ws, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    hip = Hip()
+    nst = gdn.GDN_NUM_STAGES
+    evs = [[hip.event() for _ in range(nst + 1)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    stage_ms = {name: float(np.mean([hip.elapsed_ms(e[j], e[j + 1]) for e in evs]))
+                for j, name in enumerate(gdn.STAGE_NAMES)}
+    call_ms = float(np.mean([hip.elapsed_ms(e[0], e[nst]) for e in evs]))
+    for e in evs:
+        for x in e:
+            hip.destroy(x)
+
+    # cold steps: a 512 MiB write evicts the 256 MiB Infinity Cache before each call
+    cold = []
+    if args.cold_steps > 0:
+        scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        ce = [hip.event() for _ in range(nst + 1)]
+        for _ in range(args.cold_steps):
+            scratch.fill_(1)
+            step(ce)
+            torch.cuda.synchronize()
+            cold.append(hip.elapsed_ms(ce[0], ce[nst]))
+        for x in ce:
+            hip.destroy(x)
+        del scratch
+
+    n_chunks = int(sum((int(L) + p.chunk_size - 1) // p.chunk_size
+                       for L in (p.cu_seqlens[1:] - p.cu_seqlens[:-1])))
+    s_ws = 4   # bytes per element of the W<- / U~ intermediates on the path that ran
+    sb = stage_bytes(p, 2, s_ws, n_chunks)
+    dom = max(stage_ms, key=stage_ms.get)
+    kernel_name = {"gate": "gate_kernel", "chunk_prep": "prep_kernel", "state": "state_kernel"}[dom]
+    achieved = sb[dom] / (stage_ms[dom] * 1e-3) / 1e9
+    src_hash = kernel_source_hash()
+    traffic = stored_traffic(kernel_name, src_hash)
+
+    tok_s = p.N / (ms_per_step * 1e-3)
+    flops = algorithmic_flops_per_token_vhead(p.dk, p.dv, p.chunk_size) * p.N * p.HV
+    pbytes = path_bytes(p, 2)
+    res = {
+        "metric": METRIC,
+        "value": tok_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded SplitMix64/Box-Muller, seed 1001)",
+        "config": {"workload": "dense batch bf16: B=4 x T=4096, H=HV=16, dk=dv=128, C=64, "
+                               "zero initial state",
+                   "global_batch": p.B, "seq_len": int(p.N // p.B), "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "hbm", "kernel": kernel_name, "stage": dom,
+                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "algorithmic_bytes_per_launch": sb[dom], "avg_launch_ms": stage_ms[dom]},
+        "effective": {"tflops": flops / (ms_per_step * 1e-3) / 1e12,
+                      "frac_mfma_bf16": flops / (ms_per_step * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS,
+                      "path_gbs": pbytes / (ms_per_step * 1e-3) / 1e9,
+                      "frac_hbm": pbytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                      "algorithmic_flops": flops, "algorithmic_bytes": pbytes},
+        "stage_ms": stage_ms,
+        "call_ms_events": call_ms,
+        "cold_call_ms": float(np.median(cold)) if cold else None,
+        "kernel_source_hash": src_hash,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(p)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

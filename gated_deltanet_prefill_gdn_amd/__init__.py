@@ -1,0 +1,221 @@
+"""Python binding of libgdn (Gated DeltaNet chunkwise prefill forward on MI355X).
+
+The names match the C ABI in include/gdn.h. This module only marshals
+arguments: it checks tensor shapes, dtypes, devices and contiguity, allocates
+``out`` and the workspace with torch when the caller does not pass them, and
+hands raw device pointers to the library. Every step of the computation runs in
+the library's HIP kernels; there is no fallback. If libgdn.so is not built the
+import of the library fails loudly.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libgdn.so")
+
+GDN_OK = 0
+GDN_ERR_INVALID_ARG = 1
+GDN_ERR_UNSUPPORTED = 2
+GDN_ERR_WORKSPACE = 3
+GDN_ERR_HIP = 4
+GDN_ERR_BAD_INPUT = 5
+GDN_DTYPE_F32 = 0
+GDN_DTYPE_BF16 = 1
+
+GDN_NUM_STAGES = 3
+STAGE_NAMES = ("gate", "chunk_prep", "state")
+
+EXPORTED = ("gdn_prefill_workspace_size", "gdn_prefill_fwd", "gdn_prefill_fwd_events",
+            "gdn_validate_inputs", "gdn_status_str", "gdn_version")
+
+
+class GdnProblem(ctypes.Structure):
+    _fields_ = [
+        ("total_tokens", ctypes.c_int64),
+        ("batch", ctypes.c_int64),
+        ("num_qk_heads", ctypes.c_int32),
+        ("num_v_heads", ctypes.c_int32),
+        ("head_k", ctypes.c_int32),
+        ("head_v", ctypes.c_int32),
+        ("pool_size", ctypes.c_int64),
+        ("qkv_dtype", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+    ]
+
+
+class GdnError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: status {status} ({status_str(status)})")
+        self.status = status
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Open libgdn.so and declare the C signatures. Raises if it is not built."""
+    global _lib
+    if _lib is not None and path == LIB_PATH:
+        return _lib
+    import torch  # noqa: F401  (load torch's HIP runtime first so libgdn shares it)
+    if not os.path.exists(path):
+        raise ImportError(f"libgdn.so is not built at {path}; run __graft_entry__.build() "
+                          "(hipcc --offload-arch=gfx950)")
+    L = ctypes.CDLL(path)
+    P = ctypes.c_void_p
+    PP = ctypes.POINTER(GdnProblem)
+    L.gdn_prefill_workspace_size.restype = ctypes.c_size_t
+    L.gdn_prefill_workspace_size.argtypes = [PP, ctypes.c_int32]
+    L.gdn_prefill_fwd.restype = ctypes.c_int
+    L.gdn_prefill_fwd.argtypes = [P, P, P, P, P, P, P, P, P, P, ctypes.c_int32, P, PP, P,
+                                  ctypes.c_size_t, P]
+    L.gdn_prefill_fwd_events.restype = ctypes.c_int
+    L.gdn_prefill_fwd_events.argtypes = L.gdn_prefill_fwd.argtypes + [P]
+    L.gdn_validate_inputs.restype = ctypes.c_int
+    L.gdn_validate_inputs.argtypes = [P, P, PP, P]
+    L.gdn_status_str.restype = ctypes.c_char_p
+    L.gdn_status_str.argtypes = [ctypes.c_int]
+    L.gdn_version.restype = ctypes.c_int32
+    L.gdn_version.argtypes = []
+    if path == LIB_PATH:
+        _lib = L
+    return L
+
+
+def status_str(status: int) -> str:
+    return load_library().gdn_status_str(int(status)).decode()
+
+
+def gdn_version() -> int:
+    return int(load_library().gdn_version())
+
+
+def make_problem(N: int, B: int, H: int, HV: int, dk: int, dv: int, pool: int,
+                 dtype: int) -> GdnProblem:
+    return GdnProblem(int(N), int(B), int(H), int(HV), int(dk), int(dv), int(pool), int(dtype), 0)
+
+
+def gdn_prefill_workspace_size(prob: GdnProblem, chunk_size: int = 64) -> int:
+    return int(load_library().gdn_prefill_workspace_size(ctypes.byref(prob), int(chunk_size)))
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return GDN_DTYPE_BF16
+    if t.dtype == torch.float32:
+        return GDN_DTYPE_F32
+    raise TypeError(f"q/k/v must be bfloat16 or float32, got {t.dtype}")
+
+
+def _need(t, name, dtype=None, ndim=None, device=None):
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def problem_of(q, k, v, state_pool, cache_indices) -> GdnProblem:
+    N, H, dk = q.shape
+    HV, dv = v.shape[1], v.shape[2]
+    return make_problem(N, cache_indices.shape[0], H, HV, dk, dv, state_pool.shape[0],
+                        _dtype_code(q))
+
+
+def gdn_prefill_fwd(q, k, v, a, b, A_log, dt_bias, state_pool, cache_indices, cu_seqlens,
+                    chunk_size: int = 64, out=None, workspace=None, stream=None):
+    return _prefill(q, k, v, a, b, A_log, dt_bias, state_pool, cache_indices, cu_seqlens,
+                    chunk_size, out, workspace, stream, None)
+
+
+def gdn_prefill_fwd_events(q, k, v, a, b, A_log, dt_bias, state_pool, cache_indices,
+                           cu_seqlens, stage_events, chunk_size: int = 64, out=None,
+                           workspace=None, stream=None):
+    """gdn_prefill_fwd that records the GDN_NUM_STAGES + 1 caller-created hipEvent_t
+    handles in ``stage_events`` (ints) on the stream around the stages."""
+    if len(stage_events) != GDN_NUM_STAGES + 1:
+        raise ValueError("need GDN_NUM_STAGES + 1 events")
+    arr = (ctypes.c_void_p * len(stage_events))(*[int(e) for e in stage_events])
+    return _prefill(q, k, v, a, b, A_log, dt_bias, state_pool, cache_indices, cu_seqlens,
+                    chunk_size, out, workspace, stream, arr)
+
+
+def _prefill(q, k, v, a, b, A_log, dt_bias, state_pool, cache_indices, cu_seqlens,
+             chunk_size, out, workspace, stream, events):
+    """GDN prefill forward on device tensors; returns ``out`` [N, HV, dv] in v's dtype.
+
+    q, k [N, H, dk] and v [N, HV, dv] bf16/fp32; a, b [N, HV] fp32; A_log, dt_bias [HV]
+    fp32; state_pool [pool, HV, dv, dk] fp32 (updated in place); cache_indices [B]
+    int64; cu_seqlens [B+1] int64. ``workspace`` is an optional uint8 device tensor of at
+    least gdn_prefill_workspace_size bytes. ``stream``: a torch stream (default: current).
+    """
+    import torch
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("gdn_prefill_fwd runs on a HIP device; tensors are on " + str(dev))
+    _need(q, "q", ndim=3, device=dev)
+    _need(k, "k", dtype=q.dtype, ndim=3, device=dev)
+    _need(v, "v", dtype=q.dtype, ndim=3, device=dev)
+    N, H, dk = q.shape
+    if tuple(k.shape) != (N, H, dk):
+        raise ValueError(f"k shape {tuple(k.shape)} != q shape {tuple(q.shape)}")
+    HV, dv = v.shape[1], v.shape[2]
+    if v.shape[0] != N:
+        raise ValueError("v must have N rows")
+    for t, name in ((a, "a"), (b, "b")):
+        _need(t, name, dtype=torch.float32, ndim=2, device=dev)
+        if tuple(t.shape) != (N, HV):
+            raise ValueError(f"{name} must be [N, HV] = {(N, HV)}, got {tuple(t.shape)}")
+    for t, name in ((A_log, "A_log"), (dt_bias, "dt_bias")):
+        _need(t, name, dtype=torch.float32, ndim=1, device=dev)
+        if t.shape[0] != HV:
+            raise ValueError(f"{name} must be [HV]")
+    _need(state_pool, "state_pool", dtype=torch.float32, ndim=4, device=dev)
+    if tuple(state_pool.shape[1:]) != (HV, dv, dk):
+        raise ValueError(f"state_pool must be [pool, {HV}, {dv}, {dk}], got {tuple(state_pool.shape)}")
+    _need(cache_indices, "cache_indices", dtype=torch.int64, ndim=1, device=dev)
+    _need(cu_seqlens, "cu_seqlens", dtype=torch.int64, ndim=1, device=dev)
+    if cu_seqlens.shape[0] != cache_indices.shape[0] + 1:
+        raise ValueError("cu_seqlens must have B + 1 entries")
+    prob = problem_of(q, k, v, state_pool, cache_indices)
+    if out is None:
+        out = torch.empty((N, HV, dv), dtype=v.dtype, device=dev)
+    else:
+        _need(out, "out", dtype=v.dtype, ndim=3, device=dev)
+        if tuple(out.shape) != (N, HV, dv):
+            raise ValueError("out must be [N, HV, dv]")
+    need = gdn_prefill_workspace_size(prob, chunk_size)
+    if need == 0 and (N > 0 and cache_indices.shape[0] > 0):
+        raise GdnError(GDN_ERR_UNSUPPORTED, "gdn_prefill_workspace_size")
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    else:
+        _need(workspace, "workspace", dtype=torch.uint8, ndim=1, device=dev)
+    st = (stream or torch.cuda.current_stream(dev)).cuda_stream
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(A_log), _ptr(dt_bias),
+            _ptr(state_pool), _ptr(cache_indices), _ptr(cu_seqlens), int(chunk_size), _ptr(out),
+            ctypes.byref(prob), _ptr(workspace), workspace.numel(), ctypes.c_void_p(st))
+    L = load_library()
+    rc = L.gdn_prefill_fwd(*args) if events is None else L.gdn_prefill_fwd_events(*args, events)
+    if rc != GDN_OK:
+        raise GdnError(rc, "gdn_prefill_fwd")
+    return out
+
+
+def gdn_validate_inputs(cu_seqlens, cache_indices, prob: GdnProblem, stream=None) -> int:
+    """Debug check of cu_seqlens / cache_indices contents (synchronises). Returns a status."""
+    import torch
+    st = (stream or torch.cuda.current_stream(cu_seqlens.device)).cuda_stream
+    return int(load_library().gdn_validate_inputs(_ptr(cu_seqlens), _ptr(cache_indices),
+                                                  ctypes.byref(prob), ctypes.c_void_p(st)))

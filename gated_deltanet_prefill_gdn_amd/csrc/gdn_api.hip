@@ -1,0 +1,207 @@
+// C ABI of libgdn (declared in include/gdn.h): host-side argument checks, the
+// workspace layout and the launch sequence plan -> gate -> chunk prep -> state pass.
+#include <string.h>
+
+#include <vector>
+
+#include "gdn.h"
+#include "gdn_internal.h"
+
+namespace gdn {
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+static bool head_dim_ok(int d) { return d == 64 || d == 128 || d == 256; }
+
+Path choose_path(const Shape& s) {
+  (void)s;
+  return Path::kRef;
+}
+
+WsLayout layout_for(const Shape& s, Path p) {
+  WsLayout L;
+  L.max_chunks = s.N / s.C + s.B;
+  const size_t mc = (size_t)L.max_chunks;
+  const size_t el = (p == Path::kRef) ? 4 : 2;
+  size_t off = 0;
+  L.chunk_off = off;
+  off = align256(off + sizeof(int32_t) * (size_t)(s.B + 1));
+  L.chunk_seq = off;
+  off = align256(off + sizeof(int32_t) * mc);
+  L.gcum = off;
+  off = align256(off + sizeof(double) * mc * s.HV * s.C);
+  L.beta = off;
+  off = align256(off + sizeof(float) * mc * s.HV * s.C);
+  L.w = off;
+  off = align256(off + el * mc * s.HV * s.C * s.dk);
+  L.u = off;
+  off = align256(off + el * mc * s.HV * s.C * s.dv);
+  L.total = off;
+  return L;
+}
+
+// Descriptor checks shared by every entry point. Host only.
+static gdn_status_t check_problem(const gdn_problem_t* p, int32_t chunk_size, Shape* s) {
+  if (!p) return GDN_ERR_INVALID_ARG;
+  if (p->total_tokens < 0 || p->batch < 0 || p->pool_size < 0) return GDN_ERR_INVALID_ARG;
+  if (p->num_qk_heads <= 0 || p->num_v_heads <= 0) return GDN_ERR_INVALID_ARG;
+  if (p->num_v_heads % p->num_qk_heads != 0) return GDN_ERR_INVALID_ARG;
+  if (p->head_k <= 0 || p->head_v <= 0) return GDN_ERR_INVALID_ARG;
+  if (p->qkv_dtype != GDN_DTYPE_F32 && p->qkv_dtype != GDN_DTYPE_BF16) return GDN_ERR_INVALID_ARG;
+  if (p->reserved != 0) return GDN_ERR_INVALID_ARG;
+  if (chunk_size <= 0) return GDN_ERR_INVALID_ARG;
+  if (p->batch > 0 && p->pool_size < 1) return GDN_ERR_INVALID_ARG;
+  s->N = p->total_tokens;
+  s->B = p->batch;
+  s->H = p->num_qk_heads;
+  s->HV = p->num_v_heads;
+  s->dk = p->head_k;
+  s->dv = p->head_v;
+  s->C = chunk_size;
+  s->pool = p->pool_size;
+  s->bf16 = p->qkv_dtype == GDN_DTYPE_BF16;
+  if (chunk_size != 64) return GDN_ERR_UNSUPPORTED;
+  if (!head_dim_ok(p->head_k) || !head_dim_ok(p->head_v)) return GDN_ERR_UNSUPPORTED;
+  if (p->num_v_heads > 65535) return GDN_ERR_UNSUPPORTED;
+  if (p->total_tokens > ((int64_t)1 << 31) - 1 - 64 * (p->batch + 1)) return GDN_ERR_UNSUPPORTED;
+  if (p->batch > ((int64_t)1 << 30)) return GDN_ERR_UNSUPPORTED;
+  return GDN_OK;
+}
+
+}  // namespace gdn
+
+using namespace gdn;
+
+extern "C" {
+
+int32_t gdn_version(void) { return 100; }
+
+const char* gdn_status_str(gdn_status_t st) {
+  switch (st) {
+    case GDN_OK: return "ok";
+    case GDN_ERR_INVALID_ARG: return "invalid argument";
+    case GDN_ERR_UNSUPPORTED: return "unsupported shape or chunk size";
+    case GDN_ERR_WORKSPACE: return "workspace missing or too small";
+    case GDN_ERR_HIP: return "HIP runtime or launch failure";
+    case GDN_ERR_BAD_INPUT: return "cu_seqlens or cache_indices violate their preconditions";
+  }
+  return "unknown status";
+}
+
+size_t gdn_prefill_workspace_size(const gdn_problem_t* prob, int32_t chunk_size) {
+  Shape s;
+  if (check_problem(prob, chunk_size, &s) != GDN_OK) return 0;
+  return layout_for(s, choose_path(s)).total;
+}
+
+}  // extern "C"
+
+namespace {
+
+gdn_status_t run_prefill(const void* q, const void* k, const void* v, const float* a,
+                         const float* b, const float* A_log, const float* dt_bias,
+                         float* state_pool, const int64_t* cache_indices,
+                         const int64_t* cu_seqlens, int32_t chunk_size, void* out,
+                         const gdn_problem_t* prob, void* workspace, size_t workspace_bytes,
+                         void* stream, void* const* events) {
+  Shape s;
+  const gdn_status_t ps = check_problem(prob, chunk_size, &s);
+  if (ps != GDN_OK) return ps;
+  if (s.N == 0 || s.B == 0) return GDN_OK;  // no token: nothing is read or written
+  if (!q || !k || !v || !a || !b || !A_log || !dt_bias || !state_pool || !cache_indices ||
+      !cu_seqlens || !out)
+    return GDN_ERR_INVALID_ARG;
+  const Path path = choose_path(s);
+  const WsLayout L = layout_for(s, path);
+  if (!workspace || workspace_bytes < L.total) return GDN_ERR_WORKSPACE;
+  if (((uintptr_t)workspace & 255) != 0) return GDN_ERR_WORKSPACE;
+  if (events) {
+    for (int i = 0; i <= GDN_NUM_STAGES; ++i)
+      if (!events[i]) return GDN_ERR_INVALID_ARG;
+  }
+  hipStream_t st = (hipStream_t)stream;
+  auto mark = [&](int i) -> bool {
+    return !events || hipEventRecord((hipEvent_t)events[i], st) == hipSuccess;
+  };
+  char* ws = (char*)workspace;
+  int32_t* chunk_off = (int32_t*)(ws + L.chunk_off);
+  int32_t* chunk_seq = (int32_t*)(ws + L.chunk_seq);
+  double* gcum = (double*)(ws + L.gcum);
+  float* beta = (float*)(ws + L.beta);
+
+  if (!mark(0)) return GDN_ERR_HIP;
+  if (launch_plan(cu_seqlens, s, chunk_off, chunk_seq, L.max_chunks, st) != hipSuccess)
+    return GDN_ERR_HIP;
+  if (launch_gate(a, b, A_log, dt_bias, cu_seqlens, chunk_off, chunk_seq, s, L.max_chunks, gcum,
+                  beta, st) != hipSuccess)
+    return GDN_ERR_HIP;
+  if (!mark(1)) return GDN_ERR_HIP;
+  float* w = (float*)(ws + L.w);
+  float* u = (float*)(ws + L.u);
+  if (launch_ref_prep(k, v, cu_seqlens, chunk_off, chunk_seq, gcum, beta, s, L.max_chunks, w, u,
+                      st) != hipSuccess)
+    return GDN_ERR_HIP;
+  if (!mark(2)) return GDN_ERR_HIP;
+  if (launch_ref_state(q, k, cu_seqlens, cache_indices, chunk_off, gcum, w, u, s, state_pool,
+                       out, st) != hipSuccess)
+    return GDN_ERR_HIP;
+  if (!mark(3)) return GDN_ERR_HIP;
+  return GDN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+gdn_status_t gdn_prefill_fwd(const void* q, const void* k, const void* v, const float* a,
+                             const float* b, const float* A_log, const float* dt_bias,
+                             float* state_pool, const int64_t* cache_indices,
+                             const int64_t* cu_seqlens, int32_t chunk_size, void* out,
+                             const gdn_problem_t* prob, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  return run_prefill(q, k, v, a, b, A_log, dt_bias, state_pool, cache_indices, cu_seqlens,
+                     chunk_size, out, prob, workspace, workspace_bytes, stream, nullptr);
+}
+
+gdn_status_t gdn_prefill_fwd_events(const void* q, const void* k, const void* v, const float* a,
+                                    const float* b, const float* A_log, const float* dt_bias,
+                                    float* state_pool, const int64_t* cache_indices,
+                                    const int64_t* cu_seqlens, int32_t chunk_size, void* out,
+                                    const gdn_problem_t* prob, void* workspace,
+                                    size_t workspace_bytes, void* stream,
+                                    void* const* stage_events) {
+  if (!stage_events) return GDN_ERR_INVALID_ARG;
+  return run_prefill(q, k, v, a, b, A_log, dt_bias, state_pool, cache_indices, cu_seqlens,
+                     chunk_size, out, prob, workspace, workspace_bytes, stream, stage_events);
+}
+
+gdn_status_t gdn_validate_inputs(const int64_t* cu_seqlens, const int64_t* cache_indices,
+                                 const gdn_problem_t* prob, void* stream) {
+  Shape s;
+  const gdn_status_t ps = check_problem(prob, 64, &s);
+  if (ps != GDN_OK && ps != GDN_ERR_UNSUPPORTED) return ps;
+  if (s.B == 0) return GDN_OK;
+  if (!cu_seqlens || !cache_indices) return GDN_ERR_INVALID_ARG;
+  std::vector<int64_t> cu((size_t)s.B + 1), idx((size_t)s.B);
+  hipStream_t st = (hipStream_t)stream;
+  if (hipMemcpyAsync(cu.data(), cu_seqlens, sizeof(int64_t) * cu.size(), hipMemcpyDeviceToHost,
+                     st) != hipSuccess)
+    return GDN_ERR_HIP;
+  if (hipMemcpyAsync(idx.data(), cache_indices, sizeof(int64_t) * idx.size(),
+                     hipMemcpyDeviceToHost, st) != hipSuccess)
+    return GDN_ERR_HIP;
+  if (hipStreamSynchronize(st) != hipSuccess) return GDN_ERR_HIP;
+  if (cu[0] != 0 || cu[(size_t)s.B] != s.N) return GDN_ERR_BAD_INPUT;
+  for (int64_t i = 0; i < s.B; ++i)
+    if (cu[(size_t)i + 1] < cu[(size_t)i]) return GDN_ERR_BAD_INPUT;
+  std::vector<char> seen((size_t)s.pool, 0);
+  for (int64_t i = 0; i < s.B; ++i) {
+    const int64_t x = idx[(size_t)i];
+    if (x < 0 || x >= s.pool) return GDN_ERR_BAD_INPUT;
+    if (seen[(size_t)x]) return GDN_ERR_BAD_INPUT;
+    seen[(size_t)x] = 1;
+  }
+  return GDN_OK;
+}
+
+}  // extern "C"

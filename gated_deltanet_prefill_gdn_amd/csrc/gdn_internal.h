@@ -1,0 +1,58 @@
+// Internal declarations of libgdn: workspace layout and kernel launchers.
+// Not part of the public C ABI (include/gdn.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <hip/hip_bf16.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace gdn {
+
+constexpr float kNormEps = 1e-6f;  // added to |x|^2 inside the L2 norm of q and k
+
+// Kernel family that serves a call.
+enum class Path : int {
+  kRef = 0,   // fp32 arithmetic everywhere (fp32 inputs, and any shape the MFMA path lacks)
+  kMfma = 1,  // bf16 inputs: MFMA chunk and state kernels
+};
+
+// Byte offsets of each region inside the caller's workspace (all 256-byte aligned).
+struct WsLayout {
+  int64_t max_chunks = 0;  // upper bound on sum_b ceil(L_b / C) = N / C + B
+  size_t chunk_off = 0;    // int32 [B + 1]: first global chunk of each request
+  size_t chunk_seq = 0;    // int32 [max_chunks]: request of each global chunk, -1 if unused
+  size_t gcum = 0;         // double [max_chunks][HV][C]: chunk-local inclusive sum of log(alpha)
+  size_t beta = 0;         // float  [max_chunks][HV][C]: beta (0 on padding rows)
+  size_t w = 0;            // W<- [max_chunks][HV][C][dk] (fp32 on kRef, fp16 on kMfma)
+  size_t u = 0;            // U~  [max_chunks][HV][C][dv] (fp32 on kRef, fp16 on kMfma)
+  size_t total = 0;
+};
+
+struct Shape {
+  int64_t N, B;
+  int H, HV, dk, dv, C;
+  int64_t pool;
+  bool bf16;
+};
+
+Path choose_path(const Shape& s);
+WsLayout layout_for(const Shape& s, Path p);
+
+// Launchers (host). Each returns hipSuccess or the launch error.
+hipError_t launch_plan(const int64_t* cu_seqlens, const Shape& s, int32_t* chunk_off,
+                       int32_t* chunk_seq, int64_t max_chunks, hipStream_t st);
+hipError_t launch_gate(const float* a, const float* b, const float* A_log, const float* dt_bias,
+                       const int64_t* cu_seqlens, const int32_t* chunk_off,
+                       const int32_t* chunk_seq, const Shape& s, int64_t max_chunks,
+                       double* gcum, float* beta, hipStream_t st);
+hipError_t launch_ref_prep(const void* k, const void* v, const int64_t* cu_seqlens,
+                           const int32_t* chunk_off, const int32_t* chunk_seq, const double* gcum,
+                           const float* beta, const Shape& s, int64_t max_chunks, float* w,
+                           float* u, hipStream_t st);
+hipError_t launch_ref_state(const void* q, const void* k, const int64_t* cu_seqlens,
+                            const int64_t* cache_indices, const int32_t* chunk_off,
+                            const double* gcum, const float* w, const float* u, const Shape& s,
+                            float* state_pool, void* out, hipStream_t st);
+
+}  // namespace gdn

@@ -1,0 +1,126 @@
+// Varlen chunk table and the gate / log-space cumulative-decay kernel.
+//
+// Chunks of C tokens restart at every request (a request's last chunk may be
+// partial). The gate of token t at value head hv is
+//   g_t = log(alpha_t) = -exp(A_log[hv]) * softplus(a[t,hv] + dt_bias[hv]),
+//   beta_t = sigmoid(b[t,hv])
+// (pymllm gdn_chunkwise page, Module Contents: a and b are the raw gate inputs
+// before softplus/exp and sigmoid). The cumulative gate of "Simple math to speed
+// up GDN prefill" (veitner), section Reminder, gamma^r = prod_{j<=r} alpha^j, is
+// kept in log space: G_r = sum_{j<=r} g_j, chunk-local and inclusive, summed in
+// fp64 so that differences G_r - G_i keep their relative accuracy even when G
+// reaches hundreds inside a chunk. Padding rows of a partial chunk get g = 0
+// (alpha = 1) and beta = 0, so G stays at the last real token's value.
+#include "gdn_internal.h"
+
+namespace gdn {
+namespace {
+
+constexpr int kPlanThreads = 1024;
+
+// One workgroup: chunk_off[b] = sum_{b' < b} ceil(L_b' / C), chunk_off[B] = total,
+// then chunk_seq[c] = the request that owns global chunk c (or -1 past the total).
+__global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int64_t* __restrict__ cu,
+                                                            int64_t B, int C,
+                                                            int32_t* __restrict__ chunk_off,
+                                                            int32_t* __restrict__ chunk_seq,
+                                                            int64_t max_chunks) {
+  __shared__ int32_t s_scan[kPlanThreads];
+  __shared__ int32_t s_carry;
+  const int tid = threadIdx.x;
+  if (tid == 0) s_carry = 0;
+  __syncthreads();
+  for (int64_t base = 0; base < B; base += kPlanThreads) {
+    const int64_t bi = base + tid;
+    int32_t n = 0;
+    if (bi < B) {
+      const int64_t L = cu[bi + 1] - cu[bi];
+      n = L > 0 ? (int32_t)((L + C - 1) / C) : 0;
+    }
+    s_scan[tid] = n;
+    __syncthreads();
+    for (int off = 1; off < kPlanThreads; off <<= 1) {  // inclusive Hillis-Steele scan
+      const int32_t x = tid >= off ? s_scan[tid - off] : 0;
+      __syncthreads();
+      s_scan[tid] += x;
+      __syncthreads();
+    }
+    const int32_t carry = s_carry;
+    const int32_t incl = s_scan[tid];
+    if (bi < B) chunk_off[bi] = carry + incl - n;
+    __syncthreads();
+    if (tid == kPlanThreads - 1) s_carry = carry + incl;
+    __syncthreads();
+  }
+  const int32_t total = s_carry;
+  if (tid == 0) chunk_off[B] = total;
+  __threadfence_block();
+  __syncthreads();
+  for (int64_t c = tid; c < max_chunks; c += kPlanThreads) {
+    int32_t seq = -1;
+    if (c < total) {
+      int64_t lo = 0, hi = B;  // chunk_off[lo] <= c < chunk_off[hi]
+      while (hi - lo > 1) {
+        const int64_t mid = (lo + hi) >> 1;
+        if (chunk_off[mid] <= c) lo = mid; else hi = mid;
+      }
+      seq = (int32_t)lo;
+    }
+    chunk_seq[c] = seq;
+  }
+}
+
+// One wavefront per (global chunk, value head); lane r is row r of the chunk (C == 64).
+__global__ __launch_bounds__(256) void gate_kernel(
+    const float* __restrict__ a, const float* __restrict__ b, const float* __restrict__ A_log,
+    const float* __restrict__ dt_bias, const int64_t* __restrict__ cu,
+    const int32_t* __restrict__ chunk_off, const int32_t* __restrict__ chunk_seq, int HV,
+    int64_t max_chunks, double* __restrict__ gcum, float* __restrict__ beta) {
+  constexpr int C = 64;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t pair = (int64_t)blockIdx.x * 4 + wave;
+  if (pair >= max_chunks * HV) return;
+  const int64_t c = pair / HV;
+  const int hv = (int)(pair - c * HV);
+  const int32_t seq = chunk_seq[c];
+  if (seq < 0) return;  // unused chunk slot: never read downstream
+  const int64_t t0 = cu[seq] + (int64_t)(c - chunk_off[seq]) * C;
+  const int64_t n = min((int64_t)C, cu[seq + 1] - t0);
+  float g = 0.f, bt = 0.f;
+  if (lane < n) {
+    const int64_t t = t0 + lane;
+    const float x = a[t * HV + hv] + dt_bias[hv];
+    const float sp = fmaxf(x, 0.f) + log1pf(expf(-fabsf(x)));
+    g = -expf(A_log[hv]) * sp;
+    bt = 1.f / (1.f + expf(-b[t * HV + hv]));
+  }
+  double s = (double)g;
+  for (int off = 1; off < 64; off <<= 1) {
+    const double y = __shfl_up(s, off, 64);
+    if (lane >= off) s += y;
+  }
+  gcum[pair * C + lane] = s;
+  beta[pair * C + lane] = bt;
+}
+
+}  // namespace
+
+hipError_t launch_plan(const int64_t* cu_seqlens, const Shape& s, int32_t* chunk_off,
+                       int32_t* chunk_seq, int64_t max_chunks, hipStream_t st) {
+  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, st, cu_seqlens, s.B, s.C,
+                     chunk_off, chunk_seq, max_chunks);
+  return hipGetLastError();
+}
+
+hipError_t launch_gate(const float* a, const float* b, const float* A_log, const float* dt_bias,
+                       const int64_t* cu_seqlens, const int32_t* chunk_off,
+                       const int32_t* chunk_seq, const Shape& s, int64_t max_chunks,
+                       double* gcum, float* beta, hipStream_t st) {
+  const int64_t pairs = max_chunks * s.HV;
+  const int64_t blocks = (pairs + 3) / 4;
+  hipLaunchKernelGGL(gate_kernel, dim3((unsigned)blocks), dim3(256), 0, st, a, b, A_log, dt_bias,
+                     cu_seqlens, chunk_off, chunk_seq, s.HV, max_chunks, gcum, beta);
+  return hipGetLastError();
+}
+
+}  // namespace gdn

@@ -24,64 +24,75 @@ fp32 state pool indexed per request) at the sizes listed in ``WORKLOADS``.
 """
 from __future__ import annotations
 
+import ctypes
 import dataclasses
-import math
+import os
+import subprocess
 from typing import Optional, Sequence
 
 import numpy as np
 
-_GOLDEN = np.uint64(0x9E3779B97F4A7C15)
-_M1 = np.uint64(0xBF58476D1CE4E5B9)
-_M2 = np.uint64(0x94D049BB133111EB)
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "synth.c")
+_LIB = os.path.join(_HERE, "libgdn_synth.so")
+_lib = None
 
 # tensor ids for per-tensor streams
 TID_Q, TID_K, TID_V, TID_A, TID_B, TID_ALOG, TID_DTB, TID_STATE, TID_LEN, TID_PERM = range(1, 11)
 
 
-def _mix(z: np.ndarray) -> np.ndarray:
-    """SplitMix64 finaliser on a uint64 array (wrapping arithmetic)."""
-    with np.errstate(over="ignore"):
-        z = (z ^ (z >> np.uint64(30))) * _M1
-        z = (z ^ (z >> np.uint64(27))) * _M2
-        return z ^ (z >> np.uint64(31))
+def build(force: bool = True) -> str:
+    """Compile the generator with gcc (IEEE arithmetic, no fast-math)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + f".tmp{os.getpid()}"
+        subprocess.check_call(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-pthread",
+                               "-fno-fast-math", "-ffp-contract=off", "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
 
 
-def stream_seed(seed: int, tensor_id: int) -> np.uint64:
-    s = np.array([(seed ^ tensor_id) & 0xFFFFFFFFFFFFFFFF], dtype=np.uint64)
-    return _mix(s)[0]
+def _c():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build()
+        L = ctypes.CDLL(_LIB)
+        u64, i64, dbl, P = ctypes.c_uint64, ctypes.c_int64, ctypes.c_double, ctypes.c_void_p
+        L.synth_stream_seed.restype = u64
+        L.synth_stream_seed.argtypes = [u64, u64]
+        L.synth_uniform.restype = None
+        L.synth_uniform.argtypes = [u64, u64, i64, i64, P]
+        L.synth_normal.restype = None
+        L.synth_normal.argtypes = [u64, u64, i64, dbl, dbl, ctypes.c_int, P, ctypes.c_int]
+        L.synth_normal_f64.restype = None
+        L.synth_normal_f64.argtypes = [u64, u64, i64, dbl, dbl, P]
+        _lib = L
+    return _lib
 
 
-def raw_u64(sseed: np.uint64, start: int, count: int) -> np.ndarray:
-    """Values ``start .. start+count-1`` of the counter stream."""
-    idx = np.arange(start + 1, start + count + 1, dtype=np.uint64)
-    with np.errstate(over="ignore"):
-        return _mix(sseed + idx * _GOLDEN)
+def _threads() -> int:
+    try:
+        return max(1, min(16, len(os.sched_getaffinity(0))))
+    except AttributeError:  # pragma: no cover
+        return 1
+
+
+def stream_seed(seed: int, tensor_id: int) -> int:
+    return int(_c().synth_stream_seed(seed & 0xFFFFFFFFFFFFFFFF, tensor_id))
 
 
 def uniform(seed: int, tensor_id: int, n: int, start: int = 0) -> np.ndarray:
-    z = raw_u64(stream_seed(seed, tensor_id), start, n)
-    return (z >> np.uint64(11)).astype(np.float64) * (2.0 ** -53)
-
-
-def normal(seed: int, tensor_id: int, n: int, block: int = 1 << 22) -> np.ndarray:
-    """n standard normals in fp64 (Box-Muller on uniform pairs), drawn in blocks."""
     out = np.empty(n, dtype=np.float64)
-    sseed = stream_seed(seed, tensor_id)
-    npairs = (n + 1) // 2
-    for p0 in range(0, npairs, block):
-        p1 = min(npairs, p0 + block)
-        z = raw_u64(sseed, 2 * p0, 2 * (p1 - p0))
-        u = (z >> np.uint64(11)).astype(np.float64) * (2.0 ** -53)
-        u1 = u[0::2]
-        u2 = u[1::2]
-        r = np.sqrt(-2.0 * np.log1p(-u1))  # 1-u1 in (0,1]: log is finite
-        th = 2.0 * math.pi * u2
-        pair = np.empty(2 * (p1 - p0), dtype=np.float64)
-        pair[0::2] = r * np.cos(th)
-        pair[1::2] = r * np.sin(th)
-        lo = 2 * p0
-        hi = min(n, 2 * p1)
-        out[lo:hi] = pair[: hi - lo]
+    if n:
+        _c().synth_uniform(seed, tensor_id, start, n, out.ctypes.data_as(ctypes.c_void_p))
+    return out
+
+
+def normal(seed: int, tensor_id: int, n: int) -> np.ndarray:
+    """n standard normals in fp64 (Box-Muller on uniform pairs)."""
+    out = np.empty(n, dtype=np.float64)
+    if n:
+        _c().synth_normal_f64(seed, tensor_id, n, 0.0, 1.0, out.ctypes.data_as(ctypes.c_void_p))
     return out
 
 
@@ -143,12 +154,14 @@ class Problem:
 
 
 def _draw(seed: int, tid: int, shape: Sequence[int], dtype: str, mean: float = 0.0, std: float = 1.0):
+    """Normals * std + mean, rounded to fp32 (and then bf16 bit patterns for "bf16")."""
     n = int(np.prod(shape)) if len(shape) else 1
-    x = normal(seed, tid, n) * std + mean
-    x32 = x.astype(np.float32).reshape(shape)
-    if dtype == "bf16":
-        return f32_to_bf16_bits(x32).reshape(shape)
-    return x32
+    bf = dtype == "bf16"
+    out = np.empty(n, dtype=np.uint16 if bf else np.float32)
+    if n:
+        _c().synth_normal(seed, tid, n, float(mean), float(std), int(bf),
+                          out.ctypes.data_as(ctypes.c_void_p), _threads())
+    return out.reshape(shape)
 
 
 def make_problem(
@@ -188,10 +201,9 @@ def make_problem(
     a = _draw(seed, TID_A, (N, HV), "f32", mean=a_mean)
     b = _draw(seed, TID_B, (N, HV), "f32", mean=b_mean)
     A_log = np.log1p(15.0 * uniform(seed, TID_ALOG, HV)).astype(np.float32)
-    dt_bias = (normal(seed, TID_DTB, HV) * dt_bias_std).astype(np.float32)
+    dt_bias = _draw(seed, TID_DTB, (HV,), "f32", std=dt_bias_std)
     if state_std > 0:
-        state = (normal(seed, TID_STATE, pool * HV * dv * dk) * state_std).astype(np.float32)
-        state = state.reshape(pool, HV, dv, dk)
+        state = _draw(seed, TID_STATE, (pool, HV, dv, dk), "f32", std=state_std)
     else:
         state = np.zeros((pool, HV, dv, dk), dtype=np.float32)
     return Problem(name=name, dtype=dtype, H=H, HV=HV, dk=dk, dv=dv, q=q, k=k, v=v, a=a, b=b,

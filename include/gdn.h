@@ -1,0 +1,128 @@
+/*
+ * libgdn -- Gated DeltaNet chunkwise prefill forward on MI355X (gfx950).
+ *
+ * The operation (pymllm gdn_chunkwise page, "gdn_extend_chunkwise", Module
+ * Contents; the recurrence is the state-transition equation of "Simple math to
+ * speed up GDN prefill" (veitner), section Reminder):
+ *
+ *   for every request b (tokens cu_seqlens[b] .. cu_seqlens[b+1]-1) and value head hv,
+ *   with q/k head h = hv / (HV / H) and slot s = cache_indices[b]:
+ *     S <- state_pool[s, hv]                                   (dv x dk, fp32)
+ *     for each token t:
+ *       qh = q[t,h] / sqrt(|q[t,h]|^2 + 1e-6),  kh likewise     (q, k NOT pre-normalised)
+ *       alpha = exp(-exp(A_log[hv]) * softplus(a[t,hv] + dt_bias[hv])),  beta = sigmoid(b[t,hv])
+ *       S <- S * alpha * (I - beta kh kh^T) + beta v[t,hv] kh^T
+ *       out[t,hv] = S qh                                       (the token sees its own write)
+ *     state_pool[s, hv] <- S                                   (in place)
+ *
+ * It is evaluated chunkwise (chunks of C tokens restart at every request): one
+ * triangular inverse M^-1 = (I + tril(B K K^T, -1))^-1 per chunk, reused for the
+ * decayed inverse N^-1 = G M^-1 G^-1 (same page, section Save one invert), then a
+ * sequential pass over chunks for the state and the outputs (pymllm page,
+ * Algorithm).
+ *
+ * Layouts: every tensor is dense, contiguous, row-major.
+ *   q, k        [N, H, dk]     fp32 or bf16 (qkv_dtype)
+ *   v, out      [N, HV, dv]    same dtype as q (out has v's dtype)
+ *   a, b        [N, HV]        fp32  (raw gate inputs, before softplus / sigmoid)
+ *   A_log       [HV]           fp32
+ *   dt_bias     [HV]           fp32
+ *   state_pool  [pool, HV, dv, dk] fp32, read and written in place
+ *   cache_indices [B]          int64, distinct slots in [0, pool)
+ *   cu_seqlens  [B + 1]        int64, cu_seqlens[0] = 0, non-decreasing, cu_seqlens[B] = N
+ * All of these are DEVICE pointers. The problem descriptor is a HOST pointer.
+ *
+ * Ownership: the caller allocates and owns every buffer, the workspace included
+ * (size from gdn_prefill_workspace_size). The library allocates nothing, keeps no
+ * pointer after returning, and holds no state: calls are re-entrant. A call is
+ * asynchronous on `stream` (a hipStream_t; NULL = the default stream); buffers
+ * must stay valid until the stream reaches the call. `out` must not alias an input.
+ * Calls that share a state_pool slot or a workspace must be ordered on one stream.
+ *
+ * Errors: every argument check on the host happens before any launch, so a call
+ * that returns an error status has written nothing. Contents of device arrays
+ * (cu_seqlens, cache_indices) are a precondition; gdn_validate_inputs checks them
+ * (it copies them to the host and synchronises, so it is for debugging).
+ * GDN_ERR_HIP means a launch failed; state_pool may then be partly updated.
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  GDN_OK = 0,
+  GDN_ERR_INVALID_ARG = 1, /* null pointer, negative size, HV % H != 0, bad dtype */
+  GDN_ERR_UNSUPPORTED = 2, /* a valid but unsupported shape (head dims, chunk size) */
+  GDN_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required */
+  GDN_ERR_HIP = 4,         /* a HIP runtime call or kernel launch failed */
+  GDN_ERR_BAD_INPUT = 5    /* gdn_validate_inputs found bad cu_seqlens / cache_indices */
+} gdn_status_t;
+
+typedef enum { GDN_DTYPE_F32 = 0, GDN_DTYPE_BF16 = 1 } gdn_dtype_t;
+
+/* Shape of one call (host struct). */
+typedef struct {
+  int64_t total_tokens; /* N: rows of q, k, v, a, b, out; equals cu_seqlens[B]          */
+  int64_t batch;        /* B: requests; cu_seqlens has B + 1 entries, cache_indices B  */
+  int32_t num_qk_heads; /* H                                                          */
+  int32_t num_v_heads;  /* HV, a multiple of H; value head hv uses q/k head hv/(HV/H) */
+  int32_t head_k;       /* dk, one of 64, 128, 256                                    */
+  int32_t head_v;       /* dv, one of 64, 128, 256                                    */
+  int64_t pool_size;    /* slots in state_pool                                        */
+  int32_t qkv_dtype;    /* gdn_dtype_t of q, k, v and out                             */
+  int32_t reserved;     /* must be 0                                                  */
+} gdn_problem_t;
+
+/* Bytes of device workspace gdn_prefill_fwd needs for this problem and chunk size,
+ * or 0 if the problem or chunk size is invalid. Host only, no HIP calls. */
+size_t gdn_prefill_workspace_size(const gdn_problem_t* prob, int32_t chunk_size);
+
+/* The prefill forward (see the top of this file). chunk_size must be 64.
+ * workspace: device memory of at least gdn_prefill_workspace_size bytes, 256-byte
+ * aligned; its contents on entry do not matter. stream: a hipStream_t or NULL. */
+gdn_status_t gdn_prefill_fwd(const void* q, const void* k, const void* v, const float* a,
+                             const float* b, const float* A_log, const float* dt_bias,
+                             float* state_pool, const int64_t* cache_indices,
+                             const int64_t* cu_seqlens, int32_t chunk_size, void* out,
+                             const gdn_problem_t* prob, void* workspace, size_t workspace_bytes,
+                             void* stream);
+
+/* Stages of one call, in launch order, for gdn_prefill_fwd_events. */
+#define GDN_NUM_STAGES 3 /* 0: chunk table + gates/log cumulative decay; 1: chunk prep
+                            (Grams, the one inverse, W<- and U~); 2: state pass + outputs */
+
+/* gdn_prefill_fwd with timing marks: stage_events points to GDN_NUM_STAGES + 1
+ * hipEvent_t handles created by the caller on the current device; event i is recorded
+ * on `stream` just before stage i is launched, the last one after the last stage.
+ * Arguments, results and errors are those of gdn_prefill_fwd; no event is recorded if
+ * the call fails its host checks. For profiling. */
+gdn_status_t gdn_prefill_fwd_events(const void* q, const void* k, const void* v, const float* a,
+                                    const float* b, const float* A_log, const float* dt_bias,
+                                    float* state_pool, const int64_t* cache_indices,
+                                    const int64_t* cu_seqlens, int32_t chunk_size, void* out,
+                                    const gdn_problem_t* prob, void* workspace,
+                                    size_t workspace_bytes, void* stream,
+                                    void* const* stage_events);
+
+/* Debug check of the device-array preconditions: cu_seqlens[0] == 0, non-decreasing,
+ * cu_seqlens[B] == N; cache_indices distinct and in [0, pool). Copies both arrays to
+ * the host and synchronises `stream`. GDN_OK or GDN_ERR_BAD_INPUT. */
+gdn_status_t gdn_validate_inputs(const int64_t* cu_seqlens, const int64_t* cache_indices,
+                                 const gdn_problem_t* prob, void* stream);
+
+/* Static text for a status code. */
+const char* gdn_status_str(gdn_status_t status);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int32_t gdn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GDN_H */

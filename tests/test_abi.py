@@ -1,0 +1,117 @@
+"""The C-ABI library loads and exports every symbol include/gdn.h declares, and its
+host-side checks reject bad arguments before any launch (no GPU needed: none of
+these calls reaches the HIP runtime)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import gated_deltanet_prefill_gdn_amd as gdn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_expected_entry_points():
+    assert declared_functions() == sorted(gdn.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = gdn.load_library()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    nm = subprocess.run(["nm", "-D", "--defined-only", gdn.LIB_PATH], capture_output=True,
+                        text=True, check=True).stdout
+    exported = set(re.findall(r" T (\w+)$", nm, flags=re.M))
+    for name in declared_functions():
+        assert name in exported, name
+
+
+def test_library_carries_gfx950_code():
+    blob = open(gdn.LIB_PATH, "rb").read()
+    assert b"amdgcn-amd-amdhsa--gfx950" in blob
+
+
+def test_status_strings_and_version():
+    for code in range(6):
+        assert gdn.status_str(code)
+    assert gdn.gdn_version() >= 100
+
+
+def prob(**kw):
+    base = dict(N=16384, B=4, H=16, HV=16, dk=128, dv=128, pool=4, dtype=gdn.GDN_DTYPE_BF16)
+    base.update(kw)
+    return gdn.make_problem(base["N"], base["B"], base["H"], base["HV"], base["dk"], base["dv"],
+                            base["pool"], base["dtype"])
+
+
+def test_workspace_size():
+    ws = gdn.gdn_prefill_workspace_size(prob())
+    assert ws > 0 and ws % 256 == 0
+    # grows with the chunk upper bound N / C + B
+    assert gdn.gdn_prefill_workspace_size(prob(B=40)) > ws
+    assert gdn.gdn_prefill_workspace_size(prob(), 32) == 0          # only C = 64
+    assert gdn.gdn_prefill_workspace_size(prob(HV=24)) == 0         # HV % H != 0
+    assert gdn.gdn_prefill_workspace_size(prob(dk=96)) == 0         # unsupported head dim
+    assert gdn.gdn_prefill_workspace_size(prob(dtype=7)) == 0
+
+
+def call(p, chunk=64, ws_bytes=1 << 30, nonnull=True, ws_ptr=1 << 20):
+    lib = gdn.load_library()
+    P = ctypes.c_void_p
+    x = P(4096) if nonnull else P(0)
+    return lib.gdn_prefill_fwd(x, x, x, x, x, x, x, x, x, x, chunk, x, ctypes.byref(p),
+                               P(ws_ptr), ws_bytes, P(0))
+
+
+def test_error_paths_return_before_launch():
+    # every one of these is rejected by host checks before any HIP call
+    assert call(prob(HV=24)) == gdn.GDN_ERR_INVALID_ARG
+    assert call(prob(H=0)) == gdn.GDN_ERR_INVALID_ARG
+    assert call(prob(N=-1)) == gdn.GDN_ERR_INVALID_ARG
+    assert call(prob(dtype=3)) == gdn.GDN_ERR_INVALID_ARG
+    assert call(prob(), chunk=0) == gdn.GDN_ERR_INVALID_ARG
+    assert call(prob(), chunk=128) == gdn.GDN_ERR_UNSUPPORTED
+    assert call(prob(dk=96)) == gdn.GDN_ERR_UNSUPPORTED
+    assert call(prob(dv=512)) == gdn.GDN_ERR_UNSUPPORTED
+    assert call(prob(pool=0)) == gdn.GDN_ERR_INVALID_ARG
+    assert call(prob(), nonnull=False) == gdn.GDN_ERR_INVALID_ARG
+    assert call(prob(), ws_bytes=1024) == gdn.GDN_ERR_WORKSPACE
+    assert call(prob(), ws_ptr=(1 << 20) + 64) == gdn.GDN_ERR_WORKSPACE   # not 256-aligned
+    lib = gdn.load_library()
+    assert lib.gdn_prefill_fwd(None, None, None, None, None, None, None, None, None, None, 64,
+                               None, None, None, 0, None) == gdn.GDN_ERR_INVALID_ARG
+
+
+def test_empty_problem_is_a_no_op():
+    # N == 0 or B == 0: nothing to read or write, so null pointers are fine
+    assert call(prob(N=0, B=3), nonnull=False, ws_bytes=0, ws_ptr=0) == gdn.GDN_OK
+    assert call(prob(N=0, B=0, pool=0), nonnull=False, ws_bytes=0, ws_ptr=0) == gdn.GDN_OK
+
+
+def test_binding_rejects_cpu_tensors():
+    torch = pytest.importorskip("torch")
+    z = torch.zeros(4, 1, 64)
+    with pytest.raises(ValueError):
+        gdn.gdn_prefill_fwd(z, z, z, torch.zeros(4, 1), torch.zeros(4, 1), torch.zeros(1),
+                            torch.zeros(1), torch.zeros(1, 1, 64, 64),
+                            torch.zeros(1, dtype=torch.int64), torch.tensor([0, 4]))
+
+
+def test_package_has_no_oracle_dependency():
+    """The product path never imports the oracle or any CPU fallback."""
+    pkg_dir = os.path.join(ROOT, "gated_deltanet_prefill_gdn_amd")
+    for dirpath, _, files in os.walk(pkg_dir):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "import oracle" not in text and "from oracle" not in text, f
+                assert "gdn_oracle" not in text, f

@@ -10,6 +10,9 @@ import numpy as np
 import gdn_synth
 
 TOL = {"f32": (1e-4, 1e-5), "bf16": (2e-2, 1e-3)}   # (output: x rms(o), state: rel Frobenius)
+# The output has v's dtype (pymllm gdn_chunkwise page, Returns), so a bf16 output carries
+# its own rounding of at most half an ulp, 2^-8 |o|, on top of the computation's error.
+OUT_ROUNDING = {"f32": 0.0, "bf16": 2.0 ** -8}
 
 
 def announce(msg: str):
@@ -54,7 +57,8 @@ def run_gpu(p: gdn_synth.Problem, label: str = "", dev_tensors=None, **kw):
 def compare(p: gdn_synth.Problem, out_gpu, pool_gpu, ref, tol=None, heads=None, rows=None):
     """Check the GPU result against an oracle result at the bars for p.dtype.
 
-    Outputs: max |do| <= tol_o * rms(o_oracle) over the compared outputs.
+    Outputs: |do| <= tol_o * rms(o_oracle) + r |o_oracle| element by element, with r the
+    half-ulp of the output dtype (2^-8 for bf16, 0 for fp32).
     State: for every touched slot (and compared head), ||dS||_F / ||S||_F <= tol_s.
     Slots no request touches must equal their input bit for bit."""
     tol_o, tol_s = tol or TOL[p.dtype]
@@ -63,12 +67,15 @@ def compare(p: gdn_synth.Problem, out_gpu, pool_gpu, ref, tol=None, heads=None, 
     o_gpu = out_gpu[:, heads, r0:r1]
     o_ref = ref.out
     report = {}
+    o_ok = True
     if o_ref.size:
         assert np.all(np.isfinite(o_gpu)), "non-finite outputs"
         rms = float(np.sqrt(np.mean(o_ref ** 2)))
-        err = float(np.max(np.abs(o_gpu - o_ref)))
-        report["o_err_over_rms"] = err / max(rms, 1e-30)
-        assert err <= tol_o * rms, f"max|do| = {err:.3e} > {tol_o} * rms {rms:.3e}"
+        d = np.abs(o_gpu - o_ref)
+        allow = tol_o * rms + OUT_ROUNDING[p.dtype] * np.abs(o_ref)
+        report["o_maxerr_over_rms"] = float(d.max()) / max(rms, 1e-30)
+        report["o_worst_err_over_allowance"] = float((d / allow).max())
+        o_ok = bool(np.all(d <= allow))
     lengths = np.diff(p.cu_seqlens)
     worst = 0.0
     for bi, slot in enumerate(p.cache_indices):
@@ -81,7 +88,8 @@ def compare(p: gdn_synth.Problem, out_gpu, pool_gpu, ref, tol=None, heads=None, 
         rel_err = float(np.linalg.norm(g - r) / denom) if denom > 0 else float(np.linalg.norm(g))
         worst = max(worst, rel_err)
     report["state_rel"] = worst
-    assert worst <= tol_s, f"state rel err {worst:.3e} > {tol_s}"
+    assert o_ok, f"output error above the bar: {report}"
+    assert worst <= tol_s, f"state rel err {worst:.3e} > {tol_s}: {report}"
     touched = set(int(s) for s, L in zip(p.cache_indices, lengths) if L > 0)
     for slot in range(p.pool):
         if slot not in touched:

@@ -201,10 +201,11 @@ def main():
 
     n_chunks = int(sum((int(L) + p.chunk_size - 1) // p.chunk_size
                        for L in (p.cu_seqlens[1:] - p.cu_seqlens[:-1])))
-    s_ws = 4   # bytes per element of the W<- / U~ intermediates on the path that ran
+    s_ws = 2   # bytes per element of the fp16 W<- / U~ intermediates (bf16 inputs)
     sb = stage_bytes(p, 2, s_ws, n_chunks)
     dom = max(stage_ms, key=stage_ms.get)
-    kernel_name = {"gate": "gate_kernel", "chunk_prep": "prep_kernel", "state": "state_kernel"}[dom]
+    kernel_name = {"gate": "gate_kernel", "chunk_prep": "mfma_prep_kernel",
+                   "state": "mfma_state_kernel"}[dom]
     achieved = sb[dom] / (stage_ms[dom] * 1e-3) / 1e9
     src_hash = kernel_source_hash()
     traffic = stored_traffic(kernel_name, src_hash)

@@ -13,10 +13,7 @@ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 static bool head_dim_ok(int d) { return d == 64 || d == 128 || d == 256; }
 
-Path choose_path(const Shape& s) {
-  (void)s;
-  return Path::kRef;
-}
+Path choose_path(const Shape& s) { return s.bf16 ? Path::kMfma : Path::kRef; }
 
 WsLayout layout_for(const Shape& s, Path p) {
   WsLayout L;
@@ -115,6 +112,10 @@ gdn_status_t run_prefill(const void* q, const void* k, const void* v, const floa
   const WsLayout L = layout_for(s, path);
   if (!workspace || workspace_bytes < L.total) return GDN_ERR_WORKSPACE;
   if (((uintptr_t)workspace & 255) != 0) return GDN_ERR_WORKSPACE;
+  if (path == Path::kMfma) {  // 16-byte vector loads and stores
+    for (const void* ptr : {q, k, v, (const void*)out, (const void*)state_pool})
+      if (((uintptr_t)ptr & 15) != 0) return GDN_ERR_INVALID_ARG;
+  }
   if (events) {
     for (int i = 0; i <= GDN_NUM_STAGES; ++i)
       if (!events[i]) return GDN_ERR_INVALID_ARG;
@@ -136,15 +137,25 @@ gdn_status_t run_prefill(const void* q, const void* k, const void* v, const floa
                   beta, st) != hipSuccess)
     return GDN_ERR_HIP;
   if (!mark(1)) return GDN_ERR_HIP;
-  float* w = (float*)(ws + L.w);
-  float* u = (float*)(ws + L.u);
-  if (launch_ref_prep(k, v, cu_seqlens, chunk_off, chunk_seq, gcum, beta, s, L.max_chunks, w, u,
-                      st) != hipSuccess)
-    return GDN_ERR_HIP;
-  if (!mark(2)) return GDN_ERR_HIP;
-  if (launch_ref_state(q, k, cu_seqlens, cache_indices, chunk_off, gcum, w, u, s, state_pool,
-                       out, st) != hipSuccess)
-    return GDN_ERR_HIP;
+  void* w = ws + L.w;
+  void* u = ws + L.u;
+  if (path == Path::kMfma) {
+    if (launch_mfma_prep(k, v, cu_seqlens, chunk_off, chunk_seq, gcum, beta, s, L.max_chunks, w,
+                         u, st) != hipSuccess)
+      return GDN_ERR_HIP;
+    if (!mark(2)) return GDN_ERR_HIP;
+    if (launch_mfma_state(q, k, cu_seqlens, cache_indices, chunk_off, gcum, w, u, s, state_pool,
+                          out, st) != hipSuccess)
+      return GDN_ERR_HIP;
+  } else {
+    if (launch_ref_prep(k, v, cu_seqlens, chunk_off, chunk_seq, gcum, beta, s, L.max_chunks,
+                        (float*)w, (float*)u, st) != hipSuccess)
+      return GDN_ERR_HIP;
+    if (!mark(2)) return GDN_ERR_HIP;
+    if (launch_ref_state(q, k, cu_seqlens, cache_indices, chunk_off, gcum, (const float*)w,
+                         (const float*)u, s, state_pool, out, st) != hipSuccess)
+      return GDN_ERR_HIP;
+  }
   if (!mark(3)) return GDN_ERR_HIP;
   return GDN_OK;
 }

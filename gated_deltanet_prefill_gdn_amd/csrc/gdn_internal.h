@@ -55,4 +55,13 @@ hipError_t launch_ref_state(const void* q, const void* k, const int64_t* cu_seql
                             const double* gcum, const float* w, const float* u, const Shape& s,
                             float* state_pool, void* out, hipStream_t st);
 
+hipError_t launch_mfma_prep(const void* k, const void* v, const int64_t* cu_seqlens,
+                            const int32_t* chunk_off, const int32_t* chunk_seq,
+                            const double* gcum, const float* beta, const Shape& s,
+                            int64_t max_chunks, void* w, void* u, hipStream_t st);
+hipError_t launch_mfma_state(const void* q, const void* k, const int64_t* cu_seqlens,
+                             const int64_t* cache_indices, const int32_t* chunk_off,
+                             const double* gcum, const void* w, const void* u, const Shape& s,
+                             float* state_pool, void* out, hipStream_t st);
+
 }  // namespace gdn

@@ -1,0 +1,79 @@
+// gfx950 matrix-core helpers shared by the MFMA chunk-prep and state kernels.
+//
+// v_mfma_f32_16x16x32_{f16,bf16}: D(16x16) += A(16x32) B(32x16), one wavefront.
+// Lane l (r = l % 16, g = l / 16) holds
+//   A: row r, k = 8g .. 8g+7        B: column r, k = 8g .. 8g+7
+//   C/D: rows 4g .. 4g+3 of column r (4 fp32).
+// A contraction may use any order of k as long as A and B agree. These kernels
+// feed lane group g the k values {4g..4g+3} and {16+4g..16+4g+3} of each 32-wide
+// k step ("kperm"), because that is what a lane holds of two vertically stacked
+// D tiles: the fp32 results of one product then serve as the B (or A) operand of
+// the next product without any data movement across lanes.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn {
+namespace mfma {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4 mma_f16(half8 a, half8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+// fp32 16x16x4: lane l holds A[l%16][l/16], B[l/16][l%16]; D as above.
+__device__ __forceinline__ f32x4 mma_f32(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// Position inside a 32-wide k step of element j (0..7) held by lane group g.
+__device__ __forceinline__ constexpr int kperm(int g, int j) {
+  return j < 4 ? 4 * g + j : 16 + 4 * g + (j - 4);
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
+  return __uint_as_float(((uint32_t)b) << 16);
+}
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += ((u >> 16) & 1u) + 0x7FFFu;
+  return (uint16_t)(u >> 16);
+}
+
+// Two bf16 (bits) -> packed vector pieces.
+__device__ __forceinline__ bf16x8 bf16x8_from_u32x4(u32x4 v) {
+  return __builtin_bit_cast(bf16x8, v);
+}
+__device__ __forceinline__ half8 half8_from_u32x4(u32x4 v) { return __builtin_bit_cast(half8, v); }
+
+__device__ __forceinline__ half4 to_half4(f32x4 x) {
+  half4 h;
+  h[0] = (_Float16)x[0];
+  h[1] = (_Float16)x[1];
+  h[2] = (_Float16)x[2];
+  h[3] = (_Float16)x[3];
+  return h;
+}
+
+__device__ __forceinline__ half8 cat(half4 a, half4 b) {
+  half8 r;
+  r[0] = a[0]; r[1] = a[1]; r[2] = a[2]; r[3] = a[3];
+  r[4] = b[0]; r[5] = b[1]; r[6] = b[2]; r[7] = b[3];
+  return r;
+}
+
+}  // namespace mfma
+}  // namespace gdn

@@ -44,9 +44,15 @@ def stage_bytes(p, s_qkv: int, s_ws: int, n_chunks: int):
     rows = n_chunks * p.chunk_size
     touched = int(sum(1 for L in (p.cu_seqlens[1:] - p.cu_seqlens[:-1]) if L > 0))
     gate = p.N * p.HV * 8 + rows * p.HV * 12
-    prep = (p.N * p.H * p.dk * s_qkv + p.N * p.HV * p.dv * s_qkv + rows * p.HV * 12
-            + rows * p.HV * (p.dk + p.dv) * s_ws)
+    n_pairs = n_chunks * p.HV
+    # prep: reads q, k, v, G and beta; writes W<-, U~, e^{G_n-G} r_k, e^G r_q and A_qk
+    prep = (2 * p.N * p.H * p.dk * s_qkv + p.N * p.HV * p.dv * s_qkv + rows * p.HV * 12
+            + rows * p.HV * (p.dk + p.dv) * s_ws + rows * p.HV * 8
+            + n_pairs * p.chunk_size * p.chunk_size * s_ws)
+    # state: reads q, k, W<-, U~, the two row scales, G_n and A_qk; writes o; reads and
+    # writes the fp32 state of every touched slot
     state = (2 * p.N * p.H * p.dk * s_qkv + rows * p.HV * (p.dk + p.dv) * s_ws + rows * p.HV * 8
+             + n_pairs * 8 + n_pairs * p.chunk_size * p.chunk_size * s_ws
              + p.N * p.HV * p.dv * s_qkv + touched * p.HV * p.dv * p.dk * 8)
     return {"gate": gate, "chunk_prep": prep, "state": state}
 
@@ -126,6 +132,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cold-steps", type=int, default=5,
                     help="extra steps timed one by one after a 512 MiB cache flush")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one plain 512 MiB device copy (calibrates HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path "
@@ -198,6 +206,14 @@ def main():
         for x in ce:
             hip.destroy(x)
         del scratch
+
+    if args.copy_calibration:
+        src = torch.empty(512 << 20, dtype=torch.uint8, device=dev).fill_(3)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     n_chunks = int(sum((int(L) + p.chunk_size - 1) // p.chunk_size
                        for L in (p.cu_seqlens[1:] - p.cu_seqlens[:-1])))

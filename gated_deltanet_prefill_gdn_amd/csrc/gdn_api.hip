@@ -33,6 +33,12 @@ WsLayout layout_for(const Shape& s, Path p) {
   off = align256(off + el * mc * s.HV * s.C * s.dk);
   L.u = off;
   off = align256(off + el * mc * s.HV * s.C * s.dv);
+  L.kd = off;
+  if (p == Path::kMfma) off = align256(off + sizeof(float) * mc * s.HV * s.C);
+  L.aqk = off;
+  if (p == Path::kMfma) off = align256(off + 2 * mc * s.HV * s.C * s.C);
+  L.erq = off;
+  if (p == Path::kMfma) off = align256(off + sizeof(float) * mc * s.HV * s.C);
   L.total = off;
   return L;
 }
@@ -140,12 +146,15 @@ gdn_status_t run_prefill(const void* q, const void* k, const void* v, const floa
   void* w = ws + L.w;
   void* u = ws + L.u;
   if (path == Path::kMfma) {
-    if (launch_mfma_prep(k, v, cu_seqlens, chunk_off, chunk_seq, gcum, beta, s, L.max_chunks, w,
-                         u, st) != hipSuccess)
+    float* kd = (float*)(ws + L.kd);
+    void* aqk = ws + L.aqk;
+    float* erq = (float*)(ws + L.erq);
+    if (launch_mfma_prep(q, k, v, cu_seqlens, chunk_off, chunk_seq, gcum, beta, s,
+                         L.max_chunks, w, u, kd, aqk, erq, st) != hipSuccess)
       return GDN_ERR_HIP;
     if (!mark(2)) return GDN_ERR_HIP;
-    if (launch_mfma_state(q, k, cu_seqlens, cache_indices, chunk_off, gcum, w, u, s, state_pool,
-                          out, st) != hipSuccess)
+    if (launch_mfma_state(q, k, cu_seqlens, cache_indices, chunk_off, gcum, w, u, kd, aqk, erq,
+                          s, state_pool, out, st) != hipSuccess)
       return GDN_ERR_HIP;
   } else {
     if (launch_ref_prep(k, v, cu_seqlens, chunk_off, chunk_seq, gcum, beta, s, L.max_chunks,

@@ -37,6 +37,15 @@ __device__ __forceinline__ f32x4 mma_f32(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
+// Workgroup barrier for LDS traffic only: waits for this wave's LDS operations, not
+// for its outstanding global loads and stores (a plain __syncthreads() also fences
+// global memory, which would drain the next chunk's prefetch at every barrier).
+// Valid only where no thread reads global memory written by another thread of the
+// workgroup.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // Position inside a 32-wide k step of element j (0..7) held by lane group g.
 __device__ __forceinline__ constexpr int kperm(int g, int j) {
   return j < 4 ? 4 * g + j : 16 + 4 * g + (j - 4);

@@ -10,6 +10,8 @@
 //                                                           decay factor, arrow decoration)
 //   U~  = (Gamma o T) diag(beta) V,  Gamma_ri = e^{G_r - G_i}   the decayed inverse
 //        N^-1 = G M^-1 G^-1 of the Save-one-invert section, taken entry by entry.
+//   A_qk = Gamma o tril0(Qh Kh^T)                          the intra-chunk read mask of the
+//        pymllm page's output step ("triu is the causal mask, j <= r"), Qh = diag(r_q) Q.
 // The inverse is blocked in 16 x 16 tiles: diagonal tiles by forward substitution
 // (one lane per column), off-diagonal tiles T_IJ = -T_II sum_{J<=K<I} A_IK T_KJ on
 // fp32 matrix cores. The factors T1 = diag(e^G) T diag(beta r_k) and
@@ -29,13 +31,15 @@ template <int DK, int DV>
 struct PrepSmem {
   static constexpr int SK = (DK > DV ? DK : DV) + 16;  // row stride of the K/V staging tile
   static constexpr int ST = C + 16;                    // row stride of the T1/T2 bf16 tiles
+  static constexpr int SQ = DK + 8;                    // row stride of the Q tile
   uint16_t kv[C * SK];                                 // K rows, later V rows (bf16 bits)
+  uint16_t q[C * SQ];                                  // Q rows (bf16 bits)
   union {
     float A[C][C + 1];            // strictly lower Gram part (until T is complete)
     uint16_t Ts[2][C * ST];       // bf16 hi / lo of T1, later of T2
   } u;
   float T[C][C + 1];
-  float rk[C], bt[C], eg[C];
+  float rk[C], rq[C], bt[C], eg[C];
   double G[C];
 };
 
@@ -71,13 +75,14 @@ __device__ __forceinline__ u32x4 col_frag(const uint16_t* base, int stride, int 
 
 template <int DK, int DV>
 __global__ __launch_bounds__(256) void mfma_prep_kernel(
-    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const int64_t* __restrict__ cu, const int32_t* __restrict__ chunk_off,
     const int32_t* __restrict__ chunk_seq, const double* __restrict__ gcum,
     const float* __restrict__ beta, int H, int HV, _Float16* __restrict__ Wout,
-    _Float16* __restrict__ Uout) {
+    _Float16* __restrict__ Uout, float* __restrict__ kd_out, _Float16* __restrict__ Aout,
+    float* __restrict__ erq_out) {
   using Sm = PrepSmem<DK, DV>;
-  constexpr int SK = Sm::SK, ST = Sm::ST;
+  constexpr int SK = Sm::SK, ST = Sm::ST, SQ = Sm::SQ;
   __shared__ Sm sm;
   const int64_t c = blockIdx.x;
   const int hv = blockIdx.y;
@@ -104,8 +109,13 @@ __global__ __launch_bounds__(256) void mfma_prep_kernel(
   for (int u = 0; u < KP; ++u) {
     const int e = tid + 256 * u, row = e / (DK / 8), c8 = (e % (DK / 8)) * 8;
     u32x4 x = {0u, 0u, 0u, 0u};
-    if (row < n) x = *reinterpret_cast<const u32x4*>(k + ((t0 + row) * H + h) * (int64_t)DK + c8);
+    u32x4 y = {0u, 0u, 0u, 0u};
+    if (row < n) {
+      x = *reinterpret_cast<const u32x4*>(k + ((t0 + row) * H + h) * (int64_t)DK + c8);
+      y = *reinterpret_cast<const u32x4*>(q + ((t0 + row) * H + h) * (int64_t)DK + c8);
+    }
     *reinterpret_cast<u32x4*>(&sm.kv[row * SK + c8]) = x;
+    *reinterpret_cast<u32x4*>(&sm.q[row * SQ + c8]) = y;
   }
   if (tid < C) {
     const double Gv = gcum[pair * C + tid];
@@ -113,26 +123,38 @@ __global__ __launch_bounds__(256) void mfma_prep_kernel(
     sm.eg[tid] = expf((float)Gv);
     sm.bt[tid] = beta[pair * C + tid];
   }
-  __syncthreads();
+  lds_barrier();
 
-  // ---- r_k: wave w, rows 16w..16w+15; lane group g sums a quarter of the row
+  // ---- r_k and r_q: wave w, rows 16w..16w+15; lane group g sums a quarter of a row
   {
     const int row = 16 * w + m;
-    float acc = 0.f;
+    float acck = 0.f, accq = 0.f;
 #pragma unroll
     for (int cc = g * (DK / 4); cc < (g + 1) * (DK / 4); cc += 8) {
       const u32x4 x = *reinterpret_cast<const u32x4*>(&sm.kv[row * SK + cc]);
+      const u32x4 y = *reinterpret_cast<const u32x4*>(&sm.q[row * SQ + cc]);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float a0 = __uint_as_float(x[q] << 16), a1 = __uint_as_float(x[q] & 0xFFFF0000u);
-        acc += a0 * a0 + a1 * a1;
+      for (int j = 0; j < 4; ++j) {
+        const float a0 = __uint_as_float(x[j] << 16), a1 = __uint_as_float(x[j] & 0xFFFF0000u);
+        const float b0 = __uint_as_float(y[j] << 16), b1 = __uint_as_float(y[j] & 0xFFFF0000u);
+        acck += a0 * a0 + a1 * a1;
+        accq += b0 * b0 + b1 * b1;
       }
     }
-    acc += __shfl_xor(acc, 16, 64);
-    acc += __shfl_xor(acc, 32, 64);
-    if (g == 0) sm.rk[row] = 1.0f / sqrtf(acc + kNormEps);
+    acck += __shfl_xor(acck, 16, 64);
+    acck += __shfl_xor(acck, 32, 64);
+    accq += __shfl_xor(accq, 16, 64);
+    accq += __shfl_xor(accq, 32, 64);
+    if (g == 0) {
+      const float r = 1.0f / sqrtf(acck + kNormEps);
+      const float rq = 1.0f / sqrtf(accq + kNormEps);
+      sm.rk[row] = r;
+      sm.rq[row] = rq;
+      kd_out[pair * C + row] = expf((float)(sm.G[C - 1] - sm.G[row])) * r;
+      erq_out[pair * C + row] = sm.eg[row] * rq;
+    }
   }
-  __syncthreads();
+  lds_barrier();
 
   // ---- Gram tiles (I >= J) of raw K K^T -> A (strictly lower, scaled)
   {
@@ -154,7 +176,38 @@ __global__ __launch_bounds__(256) void mfma_prep_kernel(
       }
     }
   }
-  __syncthreads();
+  // ---- A_qk = Gamma o tril0(Qh Kh^T), rows 16w..16w+15, computed transposed
+  // (D[i][r] = (K Q^T)[16J+4g+ii][16w+m] on the raw bf16 values, then scaled by
+  // e^{G_r - G_i} r_k[i] r_q[r], i <= r). Stored as the A fragments of A_qk U in the
+  // state kernel: k step s holds token tiles 2s and 2s + 1.
+  {
+    const int r = 16 * w + m;
+    const double Gr = sm.G[r];
+    const float rq = sm.rq[r];
+    half4 t4[4];
+#pragma unroll
+    for (int J = 0; J < 4; ++J) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      if (J <= w) {
+#pragma unroll
+        for (int s = 0; s < DK / 32; ++s)
+          acc = mma_bf16(bf16x8_from_u32x4(row_frag(sm.kv, SK, 16 * J + m, 32 * s, g)),
+                         bf16x8_from_u32x4(row_frag(sm.q, SQ, r, 32 * s, g)), acc);
+      }
+      f32x4 val;
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        const int i = 16 * J + 4 * g + ii;
+        val[ii] = (i <= r) ? expf((float)(Gr - sm.G[i])) * sm.rk[i] * rq * acc[ii] : 0.f;
+      }
+      t4[J] = to_half4(val);
+    }
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+      *reinterpret_cast<half8*>(Aout + pair * C * C + ((w * 2 + s) * 64 + l) * 8) =
+          cat(t4[2 * s], t4[2 * s + 1]);
+  }
+  lds_barrier();
 
   // ---- T = (I + A)^-1, diagonal 16x16 blocks: wave w, lane = column
   if (l < 16) {
@@ -170,7 +223,7 @@ __global__ __launch_bounds__(256) void mfma_prep_kernel(
 #pragma unroll
     for (int r = 0; r < 16; ++r) sm.T[b0 + r][b0 + col] = t[r];
   }
-  __syncthreads();
+  lds_barrier();
   // off-diagonal blocks by distance d = I - J; X = sum_K A_IK T_KJ, then T_IJ = -T_II X
   for (int d = 1; d < 4; ++d) {
     if (w < 4 - d) {
@@ -188,7 +241,7 @@ __global__ __launch_bounds__(256) void mfma_prep_kernel(
 #pragma unroll
       for (int i = 0; i < 4; ++i) sm.T[16 * I + 4 * g + i][16 * J + m] = -Y[i];
     }
-    __syncthreads();
+    lds_barrier();
   }
 
   // ---- T1 = diag(e^G) T diag(beta r_k) as bf16 hi + lo (overwrites A)
@@ -199,7 +252,7 @@ __global__ __launch_bounds__(256) void mfma_prep_kernel(
     sm.u.Ts[0][r * ST + i] = hi;
     sm.u.Ts[1][r * ST + i] = f32_to_bf16_bits(x - bf16_bits_to_f32(hi));
   }
-  __syncthreads();
+  lds_barrier();
 
   // ---- W<-^T = K^T T1^T: wave w owns 32-wide dk steps s' = w, w + 4, ...; the two
   // 16-row D tiles of a step form exactly the state kernel's A fragment of W<-.
@@ -232,7 +285,7 @@ __global__ __launch_bounds__(256) void mfma_prep_kernel(
       *reinterpret_cast<half8*>(Wout + pair * C * DK + ((I * (DK / 32) + sp) * 64 + l) * 8) = hv8;
     }
   }
-  __syncthreads();
+  lds_barrier();
 
   // ---- V into LDS; T2 = (Gamma o T) diag(beta) as bf16 hi + lo
 #pragma unroll
@@ -247,7 +300,7 @@ __global__ __launch_bounds__(256) void mfma_prep_kernel(
     sm.u.Ts[0][r * ST + i] = hi;
     sm.u.Ts[1][r * ST + i] = f32_to_bf16_bits(x - bf16_bits_to_f32(hi));
   }
-  __syncthreads();
+  lds_barrier();
 
   // ---- U~ = T2 V: wave w owns dv column tiles u = w, w + 4, ...; D tiles are stored as
   // they are, which is the layout the state kernel adds them in.
@@ -273,28 +326,29 @@ __global__ __launch_bounds__(256) void mfma_prep_kernel(
 }
 
 template <int DK, int DV>
-hipError_t launch_prep_t(const void* k, const void* v, const int64_t* cu, const int32_t* off,
-                         const int32_t* cseq, const double* gcum, const float* beta,
-                         const Shape& s, int64_t max_chunks, _Float16* w, _Float16* u,
-                         hipStream_t st) {
+hipError_t launch_prep_t(const void* q, const void* k, const void* v, const int64_t* cu,
+                         const int32_t* off, const int32_t* cseq, const double* gcum,
+                         const float* beta, const Shape& s, int64_t max_chunks, _Float16* w,
+                         _Float16* u, float* kd, _Float16* aqk, float* erq, hipStream_t st) {
   hipLaunchKernelGGL((mfma_prep_kernel<DK, DV>), dim3((unsigned)max_chunks, (unsigned)s.HV),
-                     dim3(256), 0, st, (const uint16_t*)k, (const uint16_t*)v, cu, off, cseq,
-                     gcum, beta, s.H, s.HV, w, u);
+                     dim3(256), 0, st, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
+                     cu, off, cseq, gcum, beta, s.H, s.HV, w, u, kd, aqk, erq);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_mfma_prep(const void* k, const void* v, const int64_t* cu_seqlens,
-                            const int32_t* chunk_off, const int32_t* chunk_seq,
-                            const double* gcum, const float* beta, const Shape& s,
-                            int64_t max_chunks, void* w, void* u, hipStream_t st) {
+hipError_t launch_mfma_prep(const void* q, const void* k, const void* v,
+                            const int64_t* cu_seqlens, const int32_t* chunk_off,
+                            const int32_t* chunk_seq, const double* gcum, const float* beta,
+                            const Shape& s, int64_t max_chunks, void* w, void* u, float* kd,
+                            void* aqk, float* erq, hipStream_t st) {
   _Float16* W = (_Float16*)w;
   _Float16* U = (_Float16*)u;
 #define GDN_PREP_CASE(DKv, DVv)                                                               \
   if (s.dk == DKv && s.dv == DVv)                                                             \
-    return launch_prep_t<DKv, DVv>(k, v, cu_seqlens, chunk_off, chunk_seq, gcum, beta, s,     \
-                                   max_chunks, W, U, st);
+    return launch_prep_t<DKv, DVv>(q, k, v, cu_seqlens, chunk_off, chunk_seq, gcum, beta, s,  \
+                                   max_chunks, W, U, kd, (_Float16*)aqk, erq, st);
   GDN_PREP_CASE(64, 64)
   GDN_PREP_CASE(64, 128)
   GDN_PREP_CASE(64, 256)

@@ -111,17 +111,22 @@ class Hip:
         self.lib.hipEventDestroy(ctypes.c_void_p(e))
 
 
-def cpu_baseline(p):
+def cpu_baseline(p, reps: int = 3):
     """The oracle (fp64 token recurrence) as it stands, on this host's cores, over the
-    whole workload (every request and value head); about 10-20 s of CPU work."""
+    whole workload (every request and value head), run `reps` times; the median wall
+    time gives tokens/s. On 16 cores this is about 15 s of CPU time in total."""
+    import numpy as np
     import oracle
     threads = oracle.default_threads()
-    t0 = time.perf_counter()
-    oracle.prefill(p, nthreads=threads)
-    dt = time.perf_counter() - t0
+    walls = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        oracle.prefill(p, nthreads=threads)
+        walls.append(time.perf_counter() - t0)
+    dt = float(np.median(walls))
     return {"value": p.N / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"whole workload ({p.B} requests x {p.N // p.B} tokens, {p.HV} value heads), "
-                      f"fp64 recurrence, {dt:.2f} s wall"}
+                      f"fp64 recurrence, median of {reps} runs, {dt:.2f} s wall each"}
 
 
 def main():

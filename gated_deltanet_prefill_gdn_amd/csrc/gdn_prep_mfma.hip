@@ -1,23 +1,36 @@
 // Chunk preparation on matrix cores (bf16 inputs): one workgroup per (chunk, value head).
 //
-// Row convention (S is dv x dk; K, V are the chunk's n <= 64 rows; G the chunk-local
-// inclusive log cumulative gate; r_k = 1/|k|):
-//   A   = tril(diag(beta r_k) K K^T diag(r_k), -1)          Gram of raw bf16 keys, exact
-//                                                           products, fp32 accumulation
-//   T   = (I + A)^-1                                        the single inverse, M^-1
-//   W<- = diag(e^G) T diag(beta r_k) K                      ("Simple math to speed up GDN
-//                                                           prefill", Reminder: W up to a
-//                                                           decay factor, arrow decoration)
-//   U~  = (Gamma o T) diag(beta) V,  Gamma_ri = e^{G_r - G_i}   the decayed inverse
-//        N^-1 = G M^-1 G^-1 of the Save-one-invert section, taken entry by entry.
-//   A_qk = Gamma o tril0(Qh Kh^T)                          the intra-chunk read mask of the
-//        pymllm page's output step ("triu is the causal mask, j <= r"), Qh = diag(r_q) Q.
-// The inverse is blocked in 16 x 16 tiles: diagonal tiles by forward substitution
-// (one lane per column), off-diagonal tiles T_IJ = -T_II sum_{J<=K<I} A_IK T_KJ on
-// fp32 matrix cores. The factors T1 = diag(e^G) T diag(beta r_k) and
-// T2 = (Gamma o T) diag(beta) are split into bf16 hi + lo, so the bf16 products
-// with the exact raw K and V keep fp32 accuracy. W<- and U~ are stored as fp16 in
-// the fragment layouts the state kernel reads directly into registers.
+// Row convention (S is dv x dk; K, Q, V are the chunk's n <= 64 rows; G the chunk-local
+// inclusive log cumulative gate; r_k = 1/|k|, r_q = 1/|q|):
+//   A    = tril(diag(beta r_k) K K^T diag(r_k), -1)       Gram of raw bf16 keys, exact
+//                                                         products, fp32 accumulation
+//   T    = (I + A)^-1                                     the single inverse, M^-1
+//   W<-  = diag(e^G) T diag(beta r_k) K                   ("Simple math to speed up GDN
+//                                                         prefill", Reminder: W up to a
+//                                                         decay factor, arrow decoration)
+//   U~   = (Gamma o T) diag(beta) V,  Gamma_ri = e^{G_r - G_i}   the decayed inverse
+//          N^-1 = G M^-1 G^-1 of the Save-one-invert section, taken entry by entry
+//   A_qk = Gamma o tril0(diag(r_q) Q K^T diag(r_k))       the intra-chunk read with the
+//          causal mask that includes the diagonal (pymllm gdn_chunkwise page, Algorithm)
+// plus the row scales e^G r_q and e^{G_n - G} r_k that the state pass applies.
+//
+// Work split: wave w owns chunk rows 16w .. 16w + 15 (row tile w). It loads its q, k and
+// v rows straight from global memory into MFMA operand registers, and the k rows of the
+// earlier tiles J < w as well, so both Grams of its rows are register-only products.
+// The inverse is blocked in 16 x 16 tiles: the diagonal tile by forward substitution in
+// fp32, then T_wJ = -T_ww sum_{J <= K < w} A_wK T_KJ by block distance w - J on fp32
+// matrix cores; only tiles another wave needs pass through LDS. Every wave keeps the
+// transposed tiles T_wJ^T of its own rows, which are exactly the operand fragments of
+// its rows of W<- and U~. K and V are transposed once through LDS for those two token
+// contractions. Four barriers per workgroup.
+//
+// Fragment notation: Dl(X) is the MFMA result layout of a 16 x 16 tile X, lane
+// l = 16 g + m holding X[4g + i][m], i = 0..3. A product P Q takes Dl(P^T) as its A
+// operand and Dl(Q) as its B operand (for 16x16x4 fp32 with k = 4g + s at step s; for
+// 16x16x32, two stacked tiles in kperm order). T1 = diag(e^G) T diag(beta r_k) and
+// T2 = (Gamma o T) diag(beta) are split into bf16 hi + lo so the bf16 products with the
+// exact raw K and V keep fp32 accuracy. W<-, U~ and A_qk are stored as fp16 in the
+// fragment layouts the state kernel loads directly into registers.
 #include "gdn_internal.h"
 #include "gdn_mfma.h"
 
@@ -26,50 +39,99 @@ namespace {
 
 using namespace mfma;
 constexpr int C = 64;
+constexpr double kLog2e = 1.4426950408889634;
+constexpr int STT = C + 4;  // token stride (bf16) of the transposed K and V tiles
+constexpr int SA = 20;      // row stride (fp32) of a wave's 16 x 16 scratch tile
 
 template <int DK, int DV>
 struct PrepSmem {
-  static constexpr int SK = (DK > DV ? DK : DV) + 16;  // row stride of the K/V staging tile
-  static constexpr int ST = C + 16;                    // row stride of the T1/T2 bf16 tiles
-  static constexpr int SQ = DK + 8;                    // row stride of the Q tile
-  uint16_t kv[C * SK];                                 // K rows, later V rows (bf16 bits)
-  uint16_t q[C * SQ];                                  // Q rows (bf16 bits)
-  union {
-    float A[C][C + 1];            // strictly lower Gram part (until T is complete)
-    uint16_t Ts[2][C * ST];       // bf16 hi / lo of T1, later of T2
-  } u;
-  float T[C][C + 1];
-  float rk[C], rq[C], bt[C], eg[C];
-  double G[C];
+  uint16_t kt[DK * STT];  // K^T: dk rows, token columns
+  uint16_t vt[DV * STT];  // V^T
+  f32x4 tex[9][64];       // Dl(T_IJ) tiles that other waves read: diagonal, distance 1, 2
+  float sq[4][16 * SA];   // per-wave scratch: A_ww, then the columns of T_ww
+  double G2[C];           // G log2(e)
+  float bt[C], rk[C];     // beta, r_k
 };
 
-__device__ __forceinline__ u32x2 lds_u32x2(const uint16_t* p) {
-  return *reinterpret_cast<const u32x2*>(p);
+// LDS slot of an exchanged tile T_IJ (I - J <= 2).
+__device__ __forceinline__ int tex_slot(int I, int J) {
+  return I == J ? I : (I - J == 1 ? 4 + J : 7 + J);
 }
 
-// Fragment of a row-major bf16 tile: row `row`, 32-wide k step starting at col0,
-// elements kperm(g, 0..7).
-__device__ __forceinline__ u32x4 row_frag(const uint16_t* base, int stride, int row, int col0,
-                                          int g) {
-  const uint16_t* p = base + row * stride + col0 + 4 * g;
-  const u32x2 lo = lds_u32x2(p), hi = lds_u32x2(p + 16);
+// Row `row` of a row-major bf16 tile in global memory (row stride rs): lane group g
+// takes elements 32s + 8g .. 32s + 8g + 7 of every 32-wide step s (zeros past n rows).
+template <int D>
+__device__ __forceinline__ void load_row(u32x4 (&f)[D / 32], const uint16_t* base, int64_t rs,
+                                         int row, int n, int g) {
+#pragma unroll
+  for (int s = 0; s < D / 32; ++s) {
+    u32x4 z = {0u, 0u, 0u, 0u};
+    if (row < n) z = *reinterpret_cast<const u32x4*>(base + row * rs + 32 * s + 8 * g);
+    f[s] = z;
+  }
+}
+
+// Scatter a lane's row fragment (as loaded by load_row) into a transposed tile:
+// element (s, j) of row `col` goes to xt[(32s + 8g + j) * STT + col].
+template <int D>
+__device__ __forceinline__ void store_transposed(uint16_t* xt, const u32x4 (&f)[D / 32], int col,
+                                                 int g) {
+#pragma unroll
+  for (int s = 0; s < D / 32; ++s)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t x = f[s][j >> 1];
+      xt[(32 * s + 8 * g + j) * STT + col] = (uint16_t)((j & 1) ? (x >> 16) : (x & 0xFFFFu));
+    }
+}
+
+// Fragment of a transposed tile: row `row`, tokens 32s + kperm(g, 0..7).
+__device__ __forceinline__ u32x4 tfrag(const uint16_t* xt, int row, int s, int g) {
+  const uint16_t* p = xt + row * STT + 32 * s + 4 * g;
+  const u32x2 lo = *reinterpret_cast<const u32x2*>(p);
+  const u32x2 hi = *reinterpret_cast<const u32x2*>(p + 16);
   u32x4 r;
   r[0] = lo[0]; r[1] = lo[1]; r[2] = hi[0]; r[3] = hi[1];
   return r;
 }
 
-// Fragment along the row index (a column of a row-major bf16 tile): column `col`,
-// rows row0 + kperm(g, 0..7).
-__device__ __forceinline__ u32x4 col_frag(const uint16_t* base, int stride, int col, int row0,
-                                          int g) {
-  uint16_t e[8];
+__device__ __forceinline__ float bf_lo(uint32_t x) { return __uint_as_float(x << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t x) { return __uint_as_float(x & 0xFFFF0000u); }
+
+// Squared norm of the row a lane group shares (the four lane groups hold one row).
+template <int D>
+__device__ __forceinline__ float sum_sq(const u32x4 (&f)[D / 32]) {
+  float acc = 0.f;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) e[j] = base[(row0 + kperm(g, j)) * stride + col];
-  u32x4 r;
-  r[0] = e[0] | ((uint32_t)e[1] << 16);
-  r[1] = e[2] | ((uint32_t)e[3] << 16);
-  r[2] = e[4] | ((uint32_t)e[5] << 16);
-  r[3] = e[6] | ((uint32_t)e[7] << 16);
+  for (int s = 0; s < D / 32; ++s)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      acc += bf_lo(f[s][j]) * bf_lo(f[s][j]) + bf_hi(f[s][j]) * bf_hi(f[s][j]);
+  acc += __shfl_xor(acc, 16, 64);
+  acc += __shfl_xor(acc, 32, 64);
+  return acc;
+}
+
+__device__ __forceinline__ bf16x4 to_bf16x4(f32x4 x) {
+  bf16x4 h;
+  h[0] = (__bf16)x[0];
+  h[1] = (__bf16)x[1];
+  h[2] = (__bf16)x[2];
+  h[3] = (__bf16)x[3];
+  return h;
+}
+__device__ __forceinline__ f32x4 to_f32x4(bf16x4 h) {
+  f32x4 r;
+  r[0] = (float)h[0];
+  r[1] = (float)h[1];
+  r[2] = (float)h[2];
+  r[3] = (float)h[3];
+  return r;
+}
+__device__ __forceinline__ bf16x8 cat_bf(bf16x4 a, bf16x4 b) {
+  bf16x8 r;
+  r[0] = a[0]; r[1] = a[1]; r[2] = a[2]; r[3] = a[3];
+  r[4] = b[0]; r[5] = b[1]; r[6] = b[2]; r[7] = b[3];
   return r;
 }
 
@@ -81,9 +143,8 @@ __global__ __launch_bounds__(256) void mfma_prep_kernel(
     const float* __restrict__ beta, int H, int HV, _Float16* __restrict__ Wout,
     _Float16* __restrict__ Uout, float* __restrict__ kd_out, _Float16* __restrict__ Aout,
     float* __restrict__ erq_out) {
-  using Sm = PrepSmem<DK, DV>;
-  constexpr int SK = Sm::SK, ST = Sm::ST, SQ = Sm::SQ;
-  __shared__ Sm sm;
+  constexpr int NKS = DK / 32, NVS = DV / 32;
+  __shared__ PrepSmem<DK, DV> sm;
   const int64_t c = blockIdx.x;
   const int hv = blockIdx.y;
   const int32_t seq = chunk_seq[c];
@@ -93,235 +154,216 @@ __global__ __launch_bounds__(256) void mfma_prep_kernel(
   const int n = (int)min((int64_t)C, cu[seq + 1] - t0);
   const int64_t pair = c * HV + hv;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, m = l & 15, g = l >> 4;
+  const int t = 16 * w + m;  // this lane's chunk row
 
-  // ---- stage K (LDS) and V (registers, written to LDS once K is no longer needed)
-  constexpr int KP = C * DK / 8 / 256;  // 16-byte pieces per thread
-  constexpr int VP = C * DV / 8 / 256;
-  u32x4 vreg[VP];
+  // ---- loads: own q, k, v rows; k rows of the earlier tiles; gates (wave 0)
+  const int64_t rsk = (int64_t)H * DK;
+  const uint16_t* kb = k + (t0 * H + h) * (int64_t)DK;
+  u32x4 kw[NKS], qf[NKS], vf[NVS];
+  u32x4 kf[3][NKS];
+  load_row<DK>(kw, kb, rsk, t, n, g);
+  load_row<DK>(qf, q + (t0 * H + h) * (int64_t)DK, rsk, t, n, g);
+  load_row<DV>(vf, v + (t0 * HV + hv) * (int64_t)DV, (int64_t)HV * DV, t, n, g);
 #pragma unroll
-  for (int u = 0; u < VP; ++u) {
-    const int e = tid + 256 * u, row = e / (DV / 8), c8 = (e % (DV / 8)) * 8;
-    u32x4 x = {0u, 0u, 0u, 0u};
-    if (row < n) x = *reinterpret_cast<const u32x4*>(v + ((t0 + row) * HV + hv) * (int64_t)DV + c8);
-    vreg[u] = x;
-  }
+  for (int J = 0; J < 3; ++J) {
+    if (J < w) {
+      load_row<DK>(kf[J], kb, rsk, 16 * J + m, n, g);
+    } else {
 #pragma unroll
-  for (int u = 0; u < KP; ++u) {
-    const int e = tid + 256 * u, row = e / (DK / 8), c8 = (e % (DK / 8)) * 8;
-    u32x4 x = {0u, 0u, 0u, 0u};
-    u32x4 y = {0u, 0u, 0u, 0u};
-    if (row < n) {
-      x = *reinterpret_cast<const u32x4*>(k + ((t0 + row) * H + h) * (int64_t)DK + c8);
-      y = *reinterpret_cast<const u32x4*>(q + ((t0 + row) * H + h) * (int64_t)DK + c8);
+      for (int s = 0; s < NKS; ++s) kf[J][s] = u32x4{0u, 0u, 0u, 0u};
     }
-    *reinterpret_cast<u32x4*>(&sm.kv[row * SK + c8]) = x;
-    *reinterpret_cast<u32x4*>(&sm.q[row * SQ + c8]) = y;
   }
+  double gl = 0.0;
+  float bl = 0.f;
   if (tid < C) {
-    const double Gv = gcum[pair * C + tid];
-    sm.G[tid] = Gv;
-    sm.eg[tid] = expf((float)Gv);
-    sm.bt[tid] = beta[pair * C + tid];
+    gl = gcum[pair * C + tid];
+    bl = beta[pair * C + tid];
   }
-  lds_barrier();
 
-  // ---- r_k and r_q: wave w, rows 16w..16w+15; lane group g sums a quarter of a row
-  {
-    const int row = 16 * w + m;
-    float acck = 0.f, accq = 0.f;
-#pragma unroll
-    for (int cc = g * (DK / 4); cc < (g + 1) * (DK / 4); cc += 8) {
-      const u32x4 x = *reinterpret_cast<const u32x4*>(&sm.kv[row * SK + cc]);
-      const u32x4 y = *reinterpret_cast<const u32x4*>(&sm.q[row * SQ + cc]);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float a0 = __uint_as_float(x[j] << 16), a1 = __uint_as_float(x[j] & 0xFFFF0000u);
-        const float b0 = __uint_as_float(y[j] << 16), b1 = __uint_as_float(y[j] & 0xFFFF0000u);
-        acck += a0 * a0 + a1 * a1;
-        accq += b0 * b0 + b1 * b1;
-      }
-    }
-    acck += __shfl_xor(acck, 16, 64);
-    acck += __shfl_xor(acck, 32, 64);
-    accq += __shfl_xor(accq, 16, 64);
-    accq += __shfl_xor(accq, 32, 64);
-    if (g == 0) {
-      const float r = 1.0f / sqrtf(acck + kNormEps);
-      const float rq = 1.0f / sqrtf(accq + kNormEps);
-      sm.rk[row] = r;
-      sm.rq[row] = rq;
-      kd_out[pair * C + row] = expf((float)(sm.G[C - 1] - sm.G[row])) * r;
-      erq_out[pair * C + row] = sm.eg[row] * rq;
-    }
+  // ---- norms of the own rows; K^T, V^T and the per-row values into LDS
+  const float rkt = 1.0f / sqrtf(sum_sq<DK>(kw) + kNormEps);
+  const float rqt = 1.0f / sqrtf(sum_sq<DK>(qf) + kNormEps);
+  store_transposed<DK>(sm.kt, kw, t, g);
+  store_transposed<DV>(sm.vt, vf, t, g);
+  if (g == 0) sm.rk[t] = rkt;
+  if (tid < C) {
+    sm.G2[tid] = gl * kLog2e;
+    sm.bt[tid] = bl;
   }
-  lds_barrier();
 
-  // ---- Gram tiles (I >= J) of raw K K^T -> A (strictly lower, scaled)
-  {
-    constexpr int TI[10] = {0, 1, 1, 2, 2, 2, 3, 3, 3, 3};
-    constexpr int TJ[10] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3};
-    for (int idx = w; idx < 10; idx += 4) {
-      const int I = TI[idx], J = TJ[idx];
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  // ---- Grams of the own rows against tiles J <= w, transposed:
+  // D[J] = Dl(K_J K_w^T), E[J] = Dl(K_J Q_w^T); lane (g, m): row 16J + 4g + i, column t
+  f32x4 D[4], E[4];
 #pragma unroll
-      for (int s = 0; s < DK / 32; ++s) {
-        const bf16x8 a = bf16x8_from_u32x4(row_frag(sm.kv, SK, 16 * I + m, 32 * s, g));
-        const bf16x8 b = bf16x8_from_u32x4(row_frag(sm.kv, SK, 16 * J + m, 32 * s, g));
-        acc = mma_bf16(a, b, acc);
+  for (int J = 0; J < 4; ++J) {
+    D[J] = f32x4{0.f, 0.f, 0.f, 0.f};
+    E[J] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (J < w) {
+#pragma unroll
+      for (int s = 0; s < NKS; ++s) {
+        const bf16x8 kj = bf16x8_from_u32x4(kf[J < 3 ? J : 0][s]);
+        D[J] = mma_bf16(kj, bf16x8_from_u32x4(kw[s]), D[J]);
+        E[J] = mma_bf16(kj, bf16x8_from_u32x4(qf[s]), E[J]);
       }
+    } else if (J == w) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 16 * I + 4 * g + i, cc = 16 * J + m;
-        sm.u.A[r][cc] = (cc < r) ? sm.bt[r] * sm.rk[r] * sm.rk[cc] * acc[i] : 0.f;
+      for (int s = 0; s < NKS; ++s) {
+        D[J] = mma_bf16(bf16x8_from_u32x4(kw[s]), bf16x8_from_u32x4(kw[s]), D[J]);
+        E[J] = mma_bf16(bf16x8_from_u32x4(kw[s]), bf16x8_from_u32x4(qf[s]), E[J]);
       }
     }
   }
-  // ---- A_qk = Gamma o tril0(Qh Kh^T), rows 16w..16w+15, computed transposed
-  // (D[i][r] = (K Q^T)[16J+4g+ii][16w+m] on the raw bf16 values, then scaled by
-  // e^{G_r - G_i} r_k[i] r_q[r], i <= r). Stored as the A fragments of A_qk U in the
-  // state kernel: k step s holds token tiles 2s and 2s + 1.
-  {
-    const int r = 16 * w + m;
-    const double Gr = sm.G[r];
-    const float rq = sm.rq[r];
-    half4 t4[4];
-#pragma unroll
-    for (int J = 0; J < 4; ++J) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      if (J <= w) {
-#pragma unroll
-        for (int s = 0; s < DK / 32; ++s)
-          acc = mma_bf16(bf16x8_from_u32x4(row_frag(sm.kv, SK, 16 * J + m, 32 * s, g)),
-                         bf16x8_from_u32x4(row_frag(sm.q, SQ, r, 32 * s, g)), acc);
-      }
-      f32x4 val;
-#pragma unroll
-      for (int ii = 0; ii < 4; ++ii) {
-        const int i = 16 * J + 4 * g + ii;
-        val[ii] = (i <= r) ? expf((float)(Gr - sm.G[i])) * sm.rk[i] * rq * acc[ii] : 0.f;
-      }
-      t4[J] = to_half4(val);
-    }
-#pragma unroll
-    for (int s = 0; s < 2; ++s)
-      *reinterpret_cast<half8*>(Aout + pair * C * C + ((w * 2 + s) * 64 + l) * 8) =
-          cat(t4[2 * s], t4[2 * s + 1]);
-  }
-  lds_barrier();
+  lds_barrier();  // (1) K^T, V^T, r_k, G, beta visible
 
-  // ---- T = (I + A)^-1, diagonal 16x16 blocks: wave w, lane = column
-  if (l < 16) {
-    const int b0 = 16 * w, col = l;
-    float t[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      float acc = 0.f;
-#pragma unroll
-      for (int i = 0; i < r; ++i) acc += sm.u.A[b0 + r][b0 + i] * t[i];
-      t[r] = (r < col) ? 0.f : ((r == col) ? 1.f : -acc);
-    }
-#pragma unroll
-    for (int r = 0; r < 16; ++r) sm.T[b0 + r][b0 + col] = t[r];
+  // ---- scale: a[J] = Dl(A_wJ^T) (A[t][i], i = 16J + 4g + ii < t) and the A_qk rows
+  const double G2t = sm.G2[t];
+  const float btt = sm.bt[t];
+  const float egt = __builtin_amdgcn_exp2f((float)G2t);
+  if (g == 0) {
+    erq_out[pair * C + t] = egt * rqt;
+    kd_out[pair * C + t] = __builtin_amdgcn_exp2f((float)(sm.G2[C - 1] - G2t)) * rkt;
   }
-  lds_barrier();
-  // off-diagonal blocks by distance d = I - J; X = sum_K A_IK T_KJ, then T_IJ = -T_II X
+  f32x4 a[4];
+  half4 aq[4];
+#pragma unroll
+  for (int J = 0; J < 4; ++J) {
+    f32x4 x;
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+      const int i = 16 * J + 4 * g + ii;
+      const float rki = sm.rk[i];
+      a[J][ii] = (J <= w && i < t) ? btt * rkt * rki * D[J][ii] : 0.f;
+      x[ii] = (J <= w && i <= t)
+                  ? __builtin_amdgcn_exp2f((float)(G2t - sm.G2[i])) * rqt * rki * E[J][ii]
+                  : 0.f;
+    }
+    aq[J] = to_half4(x);
+  }
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+    *reinterpret_cast<half8*>(Aout + pair * C * C + ((w * 2 + s) * 64 + l) * 8) =
+        cat(aq[2 * s], aq[2 * s + 1]);
+
+  // ---- diagonal tile: T_ww = (I + A_ww)^-1 by forward substitution, lane = column m
+  float* sqw = sm.sq[w];
+  f32x4 aw = a[0];
+#pragma unroll
+  for (int J = 1; J < 4; ++J)
+    if (J == w) aw = a[J];
+  *reinterpret_cast<f32x4*>(&sqw[m * SA + 4 * g]) = aw;  // row m of A_ww, columns 4g..
+  __builtin_amdgcn_wave_barrier();
+  float x[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    float acc = 0.f;
+#pragma unroll
+    for (int i = 0; i < r; ++i) acc += sqw[r * SA + i] * x[i];
+    x[r] = (r < m) ? 0.f : ((r == m) ? 1.f : -acc);
+  }
+  __builtin_amdgcn_wave_barrier();
+  if (g == 0) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sqw[r * SA + m] = x[r];  // column m of T_ww
+  }
+  __builtin_amdgcn_wave_barrier();
+  const f32x4 tww_t = *reinterpret_cast<const f32x4*>(&sqw[m * SA + 4 * g]);  // Dl(T_ww^T)
+  f32x4 tww;                                                                  // Dl(T_ww)
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float y = x[i];
+#pragma unroll
+    for (int gg = 1; gg < 4; ++gg)
+      if (g == gg) y = x[4 * gg + i];
+    tww[i] = y;
+  }
+  sm.tex[tex_slot(w, w)][l] = tww;
+  f32x4 ttr[4];  // Dl(T_wJ^T), J <= w
+#pragma unroll
+  for (int J = 0; J < 4; ++J) ttr[J] = (J == w) ? tww_t : f32x4{0.f, 0.f, 0.f, 0.f};
+  lds_barrier();  // (2)
+
+  // ---- off-diagonal tiles by distance d: X = sum_K A_wK T_KJ, T_wJ = -T_ww X
+#pragma unroll
   for (int d = 1; d < 4; ++d) {
-    if (w < 4 - d) {
-      const int J = w, I = w + d;
+    if (w >= d) {
+      const int J = w - d;
       f32x4 X = {0.f, 0.f, 0.f, 0.f};
-      for (int K = J; K < I; ++K) {
 #pragma unroll
-        for (int s = 0; s < 4; ++s)
-          X = mma_f32(sm.u.A[16 * I + m][16 * K + 4 * s + g], sm.T[16 * K + 4 * s + g][16 * J + m], X);
+      for (int K = 0; K < 3; ++K) {
+        if (K >= J && K < w) {
+          const f32x4 tkj = sm.tex[tex_slot(K, J)][l];
+#pragma unroll
+          for (int s = 0; s < 4; ++s) X = mma_f32(a[K][s], tkj[s], X);
+        }
       }
-      // Y = T_II X with contraction index 4g + s, so lane (g, m) feeds X[4g + s][m] = X[s]
-      f32x4 Y = {0.f, 0.f, 0.f, 0.f};
+      f32x4 Y = {0.f, 0.f, 0.f, 0.f}, Z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s = 0; s < 4; ++s) Y = mma_f32(sm.T[16 * I + m][16 * I + 4 * g + s], X[s], Y);
+      for (int s = 0; s < 4; ++s) {
+        Y = mma_f32(tww_t[s], X[s], Y);  // Dl(T_ww X)
+        Z = mma_f32(X[s], tww_t[s], Z);  // Dl(X^T T_ww^T)
+      }
+      if (w < 3 && d < 3) sm.tex[tex_slot(w, J)][l] = -Y;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sm.T[16 * I + 4 * g + i][16 * J + m] = -Y[i];
+      for (int JJ = 0; JJ < 3; ++JJ)
+        if (JJ == J) ttr[JJ] = -Z;
     }
-    lds_barrier();
+    if (d < 3) lds_barrier();  // (3), (4)
   }
 
-  // ---- T1 = diag(e^G) T diag(beta r_k) as bf16 hi + lo (overwrites A)
-  for (int e = tid; e < C * C; e += 256) {
-    const int r = e >> 6, i = e & 63;
-    const float x = (i <= r) ? sm.eg[r] * sm.T[r][i] * sm.bt[i] * sm.rk[i] : 0.f;
-    const uint16_t hi = f32_to_bf16_bits(x);
-    sm.u.Ts[0][r * ST + i] = hi;
-    sm.u.Ts[1][r * ST + i] = f32_to_bf16_bits(x - bf16_bits_to_f32(hi));
+  // ---- T1^T, T2^T fragments of the own rows (bf16 hi + lo), tiles J <= w
+  bf16x4 t1h[4], t1l[4], t2h[4], t2l[4];
+#pragma unroll
+  for (int J = 0; J < 4; ++J) {
+    f32x4 x1, x2;
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+      const int i = 16 * J + 4 * g + ii;
+      const float tv = ttr[J][ii];  // T[t][i], zero for i > t
+      const float bti = sm.bt[i];
+      x1[ii] = egt * tv * bti * sm.rk[i];
+      // e^{G_t - G_i} overflows for i > t under strong decay: mask, do not multiply by 0
+      x2[ii] = (i <= t) ? __builtin_amdgcn_exp2f((float)(G2t - sm.G2[i])) * tv * bti : 0.f;
+    }
+    t1h[J] = to_bf16x4(x1);
+    t1l[J] = to_bf16x4(x1 - to_f32x4(t1h[J]));
+    t2h[J] = to_bf16x4(x2);
+    t2l[J] = to_bf16x4(x2 - to_f32x4(t2h[J]));
   }
-  lds_barrier();
+  const int ns = (w >> 1) + 1;  // token steps that hold tiles J <= w
 
-  // ---- W<-^T = K^T T1^T: wave w owns 32-wide dk steps s' = w, w + 4, ...; the two
-  // 16-row D tiles of a step form exactly the state kernel's A fragment of W<-.
-  for (int sp = w; sp < DK / 32; sp += 4) {
-    f32x4 acc[2][4];
+  // ---- W<-^T = K^T T1^T for the own token columns: D tiles (dk 32sp + 16tt, rows t)
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
+  for (int sp = 0; sp < NKS; ++sp) {
+    f32x4 acc[2];
 #pragma unroll
-      for (int I = 0; I < 4; ++I) acc[tt][I] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int tt = 0; tt < 2; ++tt) {
+      acc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {  // token k steps
-      bf16x8 a[2];
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt)
-        a[tt] = bf16x8_from_u32x4(col_frag(sm.kv, SK, 32 * sp + 16 * tt + m, 32 * s, g));
-#pragma unroll
-      for (int I = 0; I < 4; ++I) {
-        const bf16x8 bh = bf16x8_from_u32x4(row_frag(sm.u.Ts[0], ST, 16 * I + m, 32 * s, g));
-        const bf16x8 bl = bf16x8_from_u32x4(row_frag(sm.u.Ts[1], ST, 16 * I + m, 32 * s, g));
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-          acc[tt][I] = mma_bf16(a[tt], bh, acc[tt][I]);
-          acc[tt][I] = mma_bf16(a[tt], bl, acc[tt][I]);
+      for (int s = 0; s < 2; ++s) {
+        if (s < ns) {
+          const bf16x8 ka = bf16x8_from_u32x4(tfrag(sm.kt, 32 * sp + 16 * tt + m, s, g));
+          acc[tt] = mma_bf16(ka, cat_bf(t1h[2 * s], t1h[2 * s + 1]), acc[tt]);
+          acc[tt] = mma_bf16(ka, cat_bf(t1l[2 * s], t1l[2 * s + 1]), acc[tt]);
         }
       }
     }
-#pragma unroll
-    for (int I = 0; I < 4; ++I) {
-      const half8 hv8 = cat(to_half4(acc[0][I]), to_half4(acc[1][I]));
-      *reinterpret_cast<half8*>(Wout + pair * C * DK + ((I * (DK / 32) + sp) * 64 + l) * 8) = hv8;
-    }
+    *reinterpret_cast<half8*>(Wout + pair * C * DK + ((w * NKS + sp) * 64 + l) * 8) =
+        cat(to_half4(acc[0]), to_half4(acc[1]));
   }
-  lds_barrier();
 
-  // ---- V into LDS; T2 = (Gamma o T) diag(beta) as bf16 hi + lo
+  // ---- U~ = T2 V for the own rows: D tiles (rows 16w.., dv 16cc..)
 #pragma unroll
-  for (int u = 0; u < VP; ++u) {
-    const int e = tid + 256 * u, row = e / (DV / 8), c8 = (e % (DV / 8)) * 8;
-    *reinterpret_cast<u32x4*>(&sm.kv[row * SK + c8]) = vreg[u];
-  }
-  for (int e = tid; e < C * C; e += 256) {
-    const int r = e >> 6, i = e & 63;
-    const float x = (i <= r) ? expf((float)(sm.G[r] - sm.G[i])) * sm.T[r][i] * sm.bt[i] : 0.f;
-    const uint16_t hi = f32_to_bf16_bits(x);
-    sm.u.Ts[0][r * ST + i] = hi;
-    sm.u.Ts[1][r * ST + i] = f32_to_bf16_bits(x - bf16_bits_to_f32(hi));
-  }
-  lds_barrier();
-
-  // ---- U~ = T2 V: wave w owns dv column tiles u = w, w + 4, ...; D tiles are stored as
-  // they are, which is the layout the state kernel adds them in.
-  for (int ut = w; ut < DV / 16; ut += 4) {
-    f32x4 acc[4];
-#pragma unroll
-    for (int I = 0; I < 4; ++I) acc[I] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int cc = 0; cc < DV / 16; ++cc) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      const bf16x8 b = bf16x8_from_u32x4(col_frag(sm.kv, SK, 16 * ut + m, 32 * s, g));
-#pragma unroll
-      for (int I = 0; I < 4; ++I) {
-        const bf16x8 ah = bf16x8_from_u32x4(row_frag(sm.u.Ts[0], ST, 16 * I + m, 32 * s, g));
-        const bf16x8 al = bf16x8_from_u32x4(row_frag(sm.u.Ts[1], ST, 16 * I + m, 32 * s, g));
-        acc[I] = mma_bf16(ah, b, acc[I]);
-        acc[I] = mma_bf16(al, b, acc[I]);
+      if (s < ns) {
+        const bf16x8 vb = bf16x8_from_u32x4(tfrag(sm.vt, 16 * cc + m, s, g));
+        acc = mma_bf16(cat_bf(t2h[2 * s], t2h[2 * s + 1]), vb, acc);
+        acc = mma_bf16(cat_bf(t2l[2 * s], t2l[2 * s + 1]), vb, acc);
       }
     }
-#pragma unroll
-    for (int I = 0; I < 4; ++I)
-      *reinterpret_cast<half4*>(Uout + pair * C * DV + ((ut * 4 + I) * 64 + l) * 4) = to_half4(acc[I]);
+    *reinterpret_cast<half4*>(Uout + pair * C * DV + ((cc * 4 + w) * 64 + l) * 4) = to_half4(acc);
   }
 }
 

@@ -12,17 +12,21 @@
 //          N^-1 = G M^-1 G^-1 of the Save-one-invert section, taken entry by entry
 //   A_qk = Gamma o tril0(diag(r_q) Q K^T diag(r_k))       the intra-chunk read with the
 //          causal mask that includes the diagonal (pymllm gdn_chunkwise page, Algorithm)
-// plus the row scales e^G r_q and e^{G_n - G} r_k that the state pass applies.
+// plus the row scales e^G and e^{G_n - G} r_k that the state pass applies.
 //
-// Work split: wave w owns chunk rows 16w .. 16w + 15 (row tile w). It loads its q, k and
-// v rows straight from global memory into MFMA operand registers, and the k rows of the
-// earlier tiles J < w as well, so both Grams of its rows are register-only products.
-// The inverse is blocked in 16 x 16 tiles: the diagonal tile by forward substitution in
-// fp32, then T_wJ = -T_ww sum_{J <= K < w} A_wK T_KJ by block distance w - J on fp32
-// matrix cores; only tiles another wave needs pass through LDS. Every wave keeps the
-// transposed tiles T_wJ^T of its own rows, which are exactly the operand fragments of
-// its rows of W<- and U~. K and V are transposed once through LDS for those two token
-// contractions. Four barriers per workgroup.
+// Work split: the chunk's K and Q rows are staged in LDS with row-contiguous loads (a
+// fragment load straight from global memory would touch 16 rows per instruction, which
+// costs the address unit four times as much). Wave w owns chunk rows 16w .. 16w + 15
+// (row tile w): it reads the operand fragments of its rows, and of the earlier tiles
+// J < w, from LDS and forms both Grams of its rows in registers. The inverse is blocked
+// in 16 x 16 tiles: the diagonal tile by forward substitution in fp32, then
+// T_wJ = -T_ww sum_{J <= K < w} A_wK T_KJ by block distance w - J on fp32 matrix cores;
+// only tiles another wave needs pass through LDS. Every wave keeps the transposed tiles
+// T_wJ^T of its own rows, which are exactly the operand fragments of its rows of W<- and
+// U~. The token contractions read column fragments of K and V with the LDS transpose
+// read. Four barriers after staging. For the state pass the kernel also writes raw k
+// (bf16) and normalised q (fp16) in that kernel's operand-fragment order, once per q/k
+// head.
 //
 // Fragment notation: Dl(X) is the MFMA result layout of a 16 x 16 tile X, lane
 // l = 16 g + m holding X[4g + i][m], i = 0..3. A product P Q takes Dl(P^T) as its A
@@ -40,13 +44,16 @@ namespace {
 using namespace mfma;
 constexpr int C = 64;
 constexpr double kLog2e = 1.4426950408889634;
-constexpr int STT = C + 4;  // token stride (bf16) of the transposed K and V tiles
 constexpr int SA = 20;      // row stride (fp32) of a wave's 16 x 16 scratch tile
 
 template <int DK, int DV>
 struct PrepSmem {
-  uint16_t kt[DK * STT];  // K^T: dk rows, token columns
-  uint16_t vt[DV * STT];  // V^T
+  // Row strides (bf16) of the staged tiles: 16 elements of padding put the four rows a
+  // transpose read touches per lane group in different banks.
+  static constexpr int SK = DK + 16;
+  static constexpr int SQV = (DK > DV ? DK : DV) + 16;
+  uint16_t ks[C * SK];    // K rows
+  uint16_t qv[C * SQV];   // Q rows, later V rows
   f32x4 tex[9][64];       // Dl(T_IJ) tiles that other waves read: diagonal, distance 1, 2
   float sq[4][16 * SA];   // per-wave scratch: A_ww, then the columns of T_ww
   double G2[C];           // G log2(e)
@@ -58,40 +65,60 @@ __device__ __forceinline__ int tex_slot(int I, int J) {
   return I == J ? I : (I - J == 1 ? 4 + J : 7 + J);
 }
 
-// Row `row` of a row-major bf16 tile in global memory (row stride rs): lane group g
-// takes elements 32s + 8g .. 32s + 8g + 7 of every 32-wide step s (zeros past n rows).
+// Stage rows of a row-major bf16 tile (global row stride rs, D columns) into LDS (row
+// stride ld), zeros past n rows. Consecutive threads take consecutive 16-byte pieces of
+// a row, so one wavefront instruction covers whole rows.
 template <int D>
-__device__ __forceinline__ void load_row(u32x4 (&f)[D / 32], const uint16_t* base, int64_t rs,
-                                         int row, int n, int g) {
+__device__ __forceinline__ void stage_rows(uint16_t* dst, int ld, const uint16_t* src, int64_t rs,
+                                           int n, int tid) {
 #pragma unroll
-  for (int s = 0; s < D / 32; ++s) {
-    u32x4 z = {0u, 0u, 0u, 0u};
-    if (row < n) z = *reinterpret_cast<const u32x4*>(base + row * rs + 32 * s + 8 * g);
-    f[s] = z;
+  for (int u = 0; u < C * D / 8 / 256; ++u) {
+    const int e = tid + 256 * u, row = e / (D / 8), c8 = (e % (D / 8)) * 8;
+    u32x4 x = {0u, 0u, 0u, 0u};
+    if (row < n) x = *reinterpret_cast<const u32x4*>(src + row * rs + c8);
+    *reinterpret_cast<u32x4*>(&dst[row * ld + c8]) = x;
   }
 }
 
-// Scatter a lane's row fragment (as loaded by load_row) into a transposed tile:
-// element (s, j) of row `col` goes to xt[(32s + 8g + j) * STT + col].
+// Row fragment of an LDS tile: row `row`, elements 32s + 8g .. 32s + 8g + 7 of every
+// 32-wide step s (the contraction order of the Gram products).
 template <int D>
-__device__ __forceinline__ void store_transposed(uint16_t* xt, const u32x4 (&f)[D / 32], int col,
-                                                 int g) {
+__device__ __forceinline__ void row_frags(u32x4 (&f)[D / 32], const uint16_t* base, int ld,
+                                          int row, int g) {
 #pragma unroll
   for (int s = 0; s < D / 32; ++s)
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const uint32_t x = f[s][j >> 1];
-      xt[(32 * s + 8 * g + j) * STT + col] = (uint16_t)((j & 1) ? (x >> 16) : (x & 0xFFFFu));
-    }
+    f[s] = *reinterpret_cast<const u32x4*>(base + row * ld + 32 * s + 8 * g);
 }
 
-// Fragment of a transposed tile: row `row`, tokens 32s + kperm(g, 0..7).
-__device__ __forceinline__ u32x4 tfrag(const uint16_t* xt, int row, int s, int g) {
-  const uint16_t* p = xt + row * STT + 32 * s + 4 * g;
+// Row fragment in kperm order: row `row`, elements col0 + kperm(g, 0..7).
+__device__ __forceinline__ u32x4 row_frag_kperm(const uint16_t* base, int ld, int row, int col0,
+                                                int g) {
+  const uint16_t* p = base + row * ld + col0 + 4 * g;
   const u32x2 lo = *reinterpret_cast<const u32x2*>(p);
   const u32x2 hi = *reinterpret_cast<const u32x2*>(p + 16);
   u32x4 r;
   r[0] = lo[0]; r[1] = lo[1]; r[2] = hi[0]; r[3] = hi[1];
+  return r;
+}
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+// Column fragment of a row-major LDS tile: column col0 + m, rows 32s + kperm(g, 0..7),
+// from two transpose reads. Within a group of 16 lanes, ds_read_b64_tr_b16 hands lane
+// 4a + c element c of the 8-byte chunks that lanes a, a + 4, a + 8, a + 12 address, so
+// lane (a + 4j) points at row 4g + j (+ 16), columns col0 + 4a .. col0 + 4a + 3.
+__device__ __forceinline__ u32x4 col_frag_tr(const uint16_t* base, int ld, int col0, int s, int g,
+                                             int m) {
+  const int a = m & 3, j = m >> 2;
+  const uint16_t* p = base + (32 * s + 4 * g + j) * ld + col0 + 4 * a;
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p);
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 16 * ld));
+  u32x4 r;
+  r[0] = (uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16);
+  r[1] = (uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16);
+  r[2] = (uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16);
+  r[3] = (uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16);
   return r;
 }
 
@@ -142,9 +169,11 @@ __global__ __launch_bounds__(256) void mfma_prep_kernel(
     const int32_t* __restrict__ chunk_seq, const double* __restrict__ gcum,
     const float* __restrict__ beta, int H, int HV, _Float16* __restrict__ Wout,
     _Float16* __restrict__ Uout, float* __restrict__ kd_out, _Float16* __restrict__ Aout,
-    float* __restrict__ erq_out) {
-  constexpr int NKS = DK / 32, NVS = DV / 32;
-  __shared__ PrepSmem<DK, DV> sm;
+    float* __restrict__ eg_out, uint16_t* __restrict__ Kout, _Float16* __restrict__ Qout) {
+  constexpr int NKS = DK / 32;
+  using Sm = PrepSmem<DK, DV>;
+  constexpr int SK = Sm::SK, SQV = Sm::SQV;
+  __shared__ Sm sm;
   const int64_t c = blockIdx.x;
   const int hv = blockIdx.y;
   const int32_t seq = chunk_seq[c];
@@ -156,39 +185,66 @@ __global__ __launch_bounds__(256) void mfma_prep_kernel(
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, m = l & 15, g = l >> 4;
   const int t = 16 * w + m;  // this lane's chunk row
 
-  // ---- loads: own q, k, v rows; k rows of the earlier tiles; gates (wave 0)
+  // ---- stage K and Q rows in LDS; V rows into registers (LDS once Q is consumed);
+  // gates (wave 0)
   const int64_t rsk = (int64_t)H * DK;
-  const uint16_t* kb = k + (t0 * H + h) * (int64_t)DK;
-  u32x4 kw[NKS], qf[NKS], vf[NVS];
+  stage_rows<DK>(sm.ks, SK, k + (t0 * H + h) * (int64_t)DK, rsk, n, tid);
+  stage_rows<DK>(sm.qv, SQV, q + (t0 * H + h) * (int64_t)DK, rsk, n, tid);
+  constexpr int VP = C * DV / 8 / 256;
+  u32x4 vreg[VP];
+#pragma unroll
+  for (int u = 0; u < VP; ++u) {
+    const int e = tid + 256 * u, row = e / (DV / 8), c8 = (e % (DV / 8)) * 8;
+    u32x4 z = {0u, 0u, 0u, 0u};
+    if (row < n) z = *reinterpret_cast<const u32x4*>(v + ((t0 + row) * HV + hv) * (int64_t)DV + c8);
+    vreg[u] = z;
+  }
+  if (tid < C) {
+    sm.G2[tid] = gcum[pair * C + tid] * kLog2e;
+    sm.bt[tid] = beta[pair * C + tid];
+  }
+  lds_barrier();  // (0) K, Q staged
+
+  // ---- operand fragments of the own rows and of the earlier tiles; norms
+  u32x4 kw[NKS], qf[NKS];
   u32x4 kf[3][NKS];
-  load_row<DK>(kw, kb, rsk, t, n, g);
-  load_row<DK>(qf, q + (t0 * H + h) * (int64_t)DK, rsk, t, n, g);
-  load_row<DV>(vf, v + (t0 * HV + hv) * (int64_t)DV, (int64_t)HV * DV, t, n, g);
+  row_frags<DK>(kw, sm.ks, SK, t, g);
+  row_frags<DK>(qf, sm.qv, SQV, t, g);
 #pragma unroll
   for (int J = 0; J < 3; ++J) {
     if (J < w) {
-      load_row<DK>(kf[J], kb, rsk, 16 * J + m, n, g);
+      row_frags<DK>(kf[J], sm.ks, SK, 16 * J + m, g);
     } else {
 #pragma unroll
       for (int s = 0; s < NKS; ++s) kf[J][s] = u32x4{0u, 0u, 0u, 0u};
     }
   }
-  double gl = 0.0;
-  float bl = 0.f;
-  if (tid < C) {
-    gl = gcum[pair * C + tid];
-    bl = beta[pair * C + tid];
-  }
-
-  // ---- norms of the own rows; K^T, V^T and the per-row values into LDS
   const float rkt = 1.0f / sqrtf(sum_sq<DK>(kw) + kNormEps);
   const float rqt = 1.0f / sqrtf(sum_sq<DK>(qf) + kNormEps);
-  store_transposed<DK>(sm.kt, kw, t, g);
-  store_transposed<DV>(sm.vt, vf, t, g);
   if (g == 0) sm.rk[t] = rkt;
-  if (tid < C) {
-    sm.G2[tid] = gl * kLog2e;
-    sm.bt[tid] = bl;
+
+  // ---- q and k in the state pass's operand order, once per q/k head:
+  // Q fragment (I, sp): rows 16I + m of diag(r_q) Q in fp16, columns 32sp + kperm(g, .);
+  // K fragment f = (sp * 2 + tt) * 2 + s: K^T rows 32sp + 16tt + m, tokens 32s + kperm(g, .)
+  if (hv % (HV / H) == 0) {
+    const int64_t fo = (c * H + h) * (int64_t)(C * DK);
+#pragma unroll
+    for (int sp = 0; sp < NKS; ++sp) {
+      const u32x4 x = row_frag_kperm(sm.qv, SQV, t, 32 * sp, g);
+      half8 y;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        y[2 * j] = (_Float16)(bf_lo(x[j]) * rqt);
+        y[2 * j + 1] = (_Float16)(bf_hi(x[j]) * rqt);
+      }
+      *reinterpret_cast<half8*>(Qout + fo + ((w * NKS + sp) * 64 + l) * 8) = y;
+    }
+#pragma unroll
+    for (int f = w; f < NKS * 4; f += 4) {
+      const int sp = f >> 2, tt = (f >> 1) & 1, s = f & 1;
+      *reinterpret_cast<u32x4*>(Kout + fo + (f * 64 + l) * 8) =
+          col_frag_tr(sm.ks, SK, 32 * sp + 16 * tt, s, g, m);
+    }
   }
 
   // ---- Grams of the own rows against tiles J <= w, transposed:
@@ -213,14 +269,21 @@ __global__ __launch_bounds__(256) void mfma_prep_kernel(
       }
     }
   }
-  lds_barrier();  // (1) K^T, V^T, r_k, G, beta visible
+  lds_barrier();  // (1) r_k visible; Q no longer read
+
+  // ---- V rows into the Q region (every wave is done with Q); visible after (2)
+#pragma unroll
+  for (int u = 0; u < VP; ++u) {
+    const int e = tid + 256 * u, row = e / (DV / 8), c8 = (e % (DV / 8)) * 8;
+    *reinterpret_cast<u32x4*>(&sm.qv[row * SQV + c8]) = vreg[u];
+  }
 
   // ---- scale: a[J] = Dl(A_wJ^T) (A[t][i], i = 16J + 4g + ii < t) and the A_qk rows
   const double G2t = sm.G2[t];
   const float btt = sm.bt[t];
   const float egt = __builtin_amdgcn_exp2f((float)G2t);
   if (g == 0) {
-    erq_out[pair * C + t] = egt * rqt;
+    eg_out[pair * C + t] = egt;
     kd_out[pair * C + t] = __builtin_amdgcn_exp2f((float)(sm.G2[C - 1] - G2t)) * rkt;
   }
   f32x4 a[4];
@@ -341,7 +404,7 @@ __global__ __launch_bounds__(256) void mfma_prep_kernel(
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
         if (s < ns) {
-          const bf16x8 ka = bf16x8_from_u32x4(tfrag(sm.kt, 32 * sp + 16 * tt + m, s, g));
+          const bf16x8 ka = bf16x8_from_u32x4(col_frag_tr(sm.ks, SK, 32 * sp + 16 * tt, s, g, m));
           acc[tt] = mma_bf16(ka, cat_bf(t1h[2 * s], t1h[2 * s + 1]), acc[tt]);
           acc[tt] = mma_bf16(ka, cat_bf(t1l[2 * s], t1l[2 * s + 1]), acc[tt]);
         }
@@ -351,19 +414,21 @@ __global__ __launch_bounds__(256) void mfma_prep_kernel(
         cat(to_half4(acc[0]), to_half4(acc[1]));
   }
 
-  // ---- U~ = T2 V for the own rows: D tiles (rows 16w.., dv 16cc..)
+  // ---- U~ = T2 V for the own rows: D tiles (rows 16w.., dv 16cc..), stored in pairs of
+  // row tiles (2s, 2s + 1) per lane so the state pass loads 16 bytes per lane
 #pragma unroll
   for (int cc = 0; cc < DV / 16; ++cc) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       if (s < ns) {
-        const bf16x8 vb = bf16x8_from_u32x4(tfrag(sm.vt, 16 * cc + m, s, g));
+        const bf16x8 vb = bf16x8_from_u32x4(col_frag_tr(sm.qv, SQV, 16 * cc, s, g, m));
         acc = mma_bf16(cat_bf(t2h[2 * s], t2h[2 * s + 1]), vb, acc);
         acc = mma_bf16(cat_bf(t2l[2 * s], t2l[2 * s + 1]), vb, acc);
       }
     }
-    *reinterpret_cast<half4*>(Uout + pair * C * DV + ((cc * 4 + w) * 64 + l) * 4) = to_half4(acc);
+    *reinterpret_cast<half4*>(Uout + pair * C * DV + ((cc * 2 + (w >> 1)) * 64 + l) * 8 +
+                              (w & 1) * 4) = to_half4(acc);
   }
 }
 
@@ -371,10 +436,11 @@ template <int DK, int DV>
 hipError_t launch_prep_t(const void* q, const void* k, const void* v, const int64_t* cu,
                          const int32_t* off, const int32_t* cseq, const double* gcum,
                          const float* beta, const Shape& s, int64_t max_chunks, _Float16* w,
-                         _Float16* u, float* kd, _Float16* aqk, float* erq, hipStream_t st) {
+                         _Float16* u, float* kd, _Float16* aqk, float* eg, uint16_t* kf,
+                         _Float16* qf, hipStream_t st) {
   hipLaunchKernelGGL((mfma_prep_kernel<DK, DV>), dim3((unsigned)max_chunks, (unsigned)s.HV),
                      dim3(256), 0, st, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
-                     cu, off, cseq, gcum, beta, s.H, s.HV, w, u, kd, aqk, erq);
+                     cu, off, cseq, gcum, beta, s.H, s.HV, w, u, kd, aqk, eg, kf, qf);
   return hipGetLastError();
 }
 
@@ -384,13 +450,14 @@ hipError_t launch_mfma_prep(const void* q, const void* k, const void* v,
                             const int64_t* cu_seqlens, const int32_t* chunk_off,
                             const int32_t* chunk_seq, const double* gcum, const float* beta,
                             const Shape& s, int64_t max_chunks, void* w, void* u, float* kd,
-                            void* aqk, float* erq, hipStream_t st) {
+                            void* aqk, float* eg, void* kf, void* qf, hipStream_t st) {
   _Float16* W = (_Float16*)w;
   _Float16* U = (_Float16*)u;
 #define GDN_PREP_CASE(DKv, DVv)                                                               \
   if (s.dk == DKv && s.dv == DVv)                                                             \
     return launch_prep_t<DKv, DVv>(q, k, v, cu_seqlens, chunk_off, chunk_seq, gcum, beta, s,  \
-                                   max_chunks, W, U, kd, (_Float16*)aqk, erq, st);
+                                   max_chunks, W, U, kd, (_Float16*)aqk, eg, (uint16_t*)kf,  \
+                                   (_Float16*)qf, st);
   GDN_PREP_CASE(64, 64)
   GDN_PREP_CASE(64, 128)
   GDN_PREP_CASE(64, 256)

@@ -40,20 +40,25 @@ def path_bytes(p, s_qkv: int) -> float:
 
 def stage_bytes(p, s_qkv: int, s_ws: int, n_chunks: int):
     """Algorithmic bytes each stage must move: its inputs read once, its outputs written
-    once. Rows are chunk rows (n_chunks * C, padding included) for per-chunk data."""
-    rows = n_chunks * p.chunk_size
-    touched = int(sum(1 for L in (p.cu_seqlens[1:] - p.cu_seqlens[:-1]) if L > 0))
-    gate = p.N * p.HV * 8 + rows * p.HV * 12
+    once. Rows are chunk rows (n_chunks * C, padding included) for per-chunk data;
+    fragment copies of q and k exist once per (chunk, q/k head)."""
+    C = p.chunk_size
+    rows = n_chunks * C
     n_pairs = n_chunks * p.HV
-    # prep: reads q, k, v, G and beta; writes W<-, U~, e^{G_n-G} r_k, e^G r_q and A_qk
+    qk_frag = n_chunks * p.H * C * p.dk * 2 * 2   # raw k (bf16) + normalised q (fp16)
+    touched = int(sum(1 for L in (p.cu_seqlens[1:] - p.cu_seqlens[:-1]) if L > 0))
+    # gate: a, b in; G (fp64) and beta out
+    gate = p.N * p.HV * 8 + rows * p.HV * 12
+    # prep: reads q, k, v, G and beta; writes W<-, U~, the row scales e^{G_n-G} r_k and
+    # e^G, A_qk, and the q/k fragment copies
     prep = (2 * p.N * p.H * p.dk * s_qkv + p.N * p.HV * p.dv * s_qkv + rows * p.HV * 12
             + rows * p.HV * (p.dk + p.dv) * s_ws + rows * p.HV * 8
-            + n_pairs * p.chunk_size * p.chunk_size * s_ws)
-    # state: reads q, k, W<-, U~, the two row scales, G_n and A_qk; writes o; reads and
-    # writes the fp32 state of every touched slot
-    state = (2 * p.N * p.H * p.dk * s_qkv + rows * p.HV * (p.dk + p.dv) * s_ws + rows * p.HV * 8
-             + n_pairs * 8 + n_pairs * p.chunk_size * p.chunk_size * s_ws
-             + p.N * p.HV * p.dv * s_qkv + touched * p.HV * p.dv * p.dk * 8)
+            + n_pairs * C * C * s_ws + qk_frag)
+    # state: reads the q/k fragments, W<-, U~, the two row scales, G_n and A_qk; writes o;
+    # reads and writes the fp32 state of every touched slot
+    state = (qk_frag + rows * p.HV * (p.dk + p.dv) * s_ws + rows * p.HV * 8 + n_pairs * 8
+             + n_pairs * C * C * s_ws + p.N * p.HV * p.dv * s_qkv
+             + touched * p.HV * p.dv * p.dk * 8)
     return {"gate": gate, "chunk_prep": prep, "state": state}
 
 

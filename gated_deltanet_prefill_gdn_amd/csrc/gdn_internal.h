@@ -25,8 +25,8 @@ struct WsLayout {
   size_t gcum = 0;         // double [max_chunks][HV][C]: chunk-local inclusive sum of log(alpha)
   size_t beta = 0;         // float  [max_chunks][HV][C]: beta (0 on padding rows)
   size_t w = 0;            // W<- [max_chunks][HV][C][dk] (fp32 on kRef, fp16 on kMfma)
-  size_t u = 0;            // U~  [max_chunks][HV][C][dv] (fp32 on kRef; fp16 on kMfma, pairs
-                           //     of MFMA D tiles per lane)
+  size_t u = 0;            // U~  [max_chunks][HV][C][dv] (fp32 on kRef; fp16 MFMA D tiles on
+                           //     kMfma)
   size_t kd = 0;           // float  [max_chunks][HV][C]: e^{G_n - G} / |k| per chunk row (kMfma only)
   size_t aqk = 0;          // fp16   [max_chunks][HV][C][C]: A_qk in fragment order (kMfma only)
   size_t eg = 0;           // float  [max_chunks][HV][C]: e^G per chunk row (kMfma only)

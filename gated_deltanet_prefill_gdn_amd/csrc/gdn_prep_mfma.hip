@@ -35,6 +35,8 @@
 // T2 = (Gamma o T) diag(beta) are split into bf16 hi + lo so the bf16 products with the
 // exact raw K and V keep fp32 accuracy. W<-, U~ and A_qk are stored as fp16 in the
 // fragment layouts the state kernel loads directly into registers.
+#include <algorithm>
+
 #include "gdn_internal.h"
 #include "gdn_mfma.h"
 
@@ -65,18 +67,30 @@ __device__ __forceinline__ int tex_slot(int I, int J) {
   return I == J ? I : (I - J == 1 ? 4 + J : 7 + J);
 }
 
-// Stage rows of a row-major bf16 tile (global row stride rs, D columns) into LDS (row
-// stride ld), zeros past n rows. Consecutive threads take consecutive 16-byte pieces of
-// a row, so one wavefront instruction covers whole rows.
+// Load rows of a row-major bf16 tile (global row stride rs, D columns) into registers,
+// zeros past n rows. Consecutive threads take consecutive 16-byte pieces of a row, so
+// one wavefront instruction covers whole rows; piece u of thread tid is element
+// e = tid + 256u: row e / (D / 8), columns 8 (e % (D / 8)) ...
 template <int D>
-__device__ __forceinline__ void stage_rows(uint16_t* dst, int ld, const uint16_t* src, int64_t rs,
-                                           int n, int tid) {
+__device__ __forceinline__ void load_tile_rows(u32x4 (&r)[C * D / 8 / 256], const uint16_t* src,
+                                               int64_t rs, int n, int tid) {
 #pragma unroll
   for (int u = 0; u < C * D / 8 / 256; ++u) {
     const int e = tid + 256 * u, row = e / (D / 8), c8 = (e % (D / 8)) * 8;
-    u32x4 x = {0u, 0u, 0u, 0u};
-    if (row < n) x = *reinterpret_cast<const u32x4*>(src + row * rs + c8);
-    *reinterpret_cast<u32x4*>(&dst[row * ld + c8]) = x;
+    u32x4 z = {0u, 0u, 0u, 0u};
+    if (row < n) z = *reinterpret_cast<const u32x4*>(src + row * rs + c8);
+    r[u] = z;
+  }
+}
+
+// Store such pieces into an LDS tile of row stride ld.
+template <int D>
+__device__ __forceinline__ void store_tile_rows(uint16_t* dst, int ld,
+                                                const u32x4 (&r)[C * D / 8 / 256], int tid) {
+#pragma unroll
+  for (int u = 0; u < C * D / 8 / 256; ++u) {
+    const int e = tid + 256 * u, row = e / (D / 8), c8 = (e % (D / 8)) * 8;
+    *reinterpret_cast<u32x4*>(&dst[row * ld + c8]) = r[u];
   }
 }
 
@@ -167,268 +181,305 @@ __global__ __launch_bounds__(256) void mfma_prep_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const int64_t* __restrict__ cu, const int32_t* __restrict__ chunk_off,
     const int32_t* __restrict__ chunk_seq, const double* __restrict__ gcum,
-    const float* __restrict__ beta, int H, int HV, _Float16* __restrict__ Wout,
+    const float* __restrict__ beta, int H, int HV, int64_t max_chunks, _Float16* __restrict__ Wout,
     _Float16* __restrict__ Uout, float* __restrict__ kd_out, _Float16* __restrict__ Aout,
     float* __restrict__ eg_out, uint16_t* __restrict__ Kout, _Float16* __restrict__ Qout) {
   constexpr int NKS = DK / 32;
   using Sm = PrepSmem<DK, DV>;
   constexpr int SK = Sm::SK, SQV = Sm::SQV;
   __shared__ Sm sm;
-  const int64_t c = blockIdx.x;
-  const int hv = blockIdx.y;
-  const int32_t seq = chunk_seq[c];
-  if (seq < 0) return;
-  const int h = hv / (HV / H);
-  const int64_t t0 = cu[seq] + (int64_t)(c - chunk_off[seq]) * C;
-  const int n = (int)min((int64_t)C, cu[seq + 1] - t0);
-  const int64_t pair = c * HV + hv;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, m = l & 15, g = l >> 4;
   const int t = 16 * w + m;  // this lane's chunk row
-
-  // ---- stage K and Q rows in LDS; V rows into registers (LDS once Q is consumed);
-  // gates (wave 0)
   const int64_t rsk = (int64_t)H * DK;
-  stage_rows<DK>(sm.ks, SK, k + (t0 * H + h) * (int64_t)DK, rsk, n, tid);
-  stage_rows<DK>(sm.qv, SQV, q + (t0 * H + h) * (int64_t)DK, rsk, n, tid);
-  constexpr int VP = C * DV / 8 / 256;
-  u32x4 vreg[VP];
-#pragma unroll
-  for (int u = 0; u < VP; ++u) {
-    const int e = tid + 256 * u, row = e / (DV / 8), c8 = (e % (DV / 8)) * 8;
-    u32x4 z = {0u, 0u, 0u, 0u};
-    if (row < n) z = *reinterpret_cast<const u32x4*>(v + ((t0 + row) * HV + hv) * (int64_t)DV + c8);
-    vreg[u] = z;
-  }
-  if (tid < C) {
-    sm.G2[tid] = gcum[pair * C + tid] * kLog2e;
-    sm.bt[tid] = beta[pair * C + tid];
-  }
-  lds_barrier();  // (0) K, Q staged
+  constexpr int KP = C * DK / 8 / 256;  // 16-byte pieces per thread of a K or Q tile
+  constexpr int VP = C * DV / 8 / 256;  // ... of a V tile
 
-  // ---- operand fragments of the own rows and of the earlier tiles; norms
-  u32x4 kw[NKS], qf[NKS];
-  u32x4 kf[3][NKS];
-  row_frags<DK>(kw, sm.ks, SK, t, g);
-  row_frags<DK>(qf, sm.qv, SQV, t, g);
-#pragma unroll
-  for (int J = 0; J < 3; ++J) {
-    if (J < w) {
-      row_frags<DK>(kf[J], sm.ks, SK, 16 * J + m, g);
-    } else {
-#pragma unroll
-      for (int s = 0; s < NKS; ++s) kf[J][s] = u32x4{0u, 0u, 0u, 0u};
+  // Persistent: workgroups stride over the (chunk, value head) items. The next item's
+  // rows are loaded into registers while the current one is processed.
+  struct Item {
+    int hv, h, n;
+    int64_t c, t0;
+  };
+  auto geom = [&](int64_t it, Item& x) -> bool {
+    x.c = it / HV;
+    x.hv = (int)(it % HV);
+    x.h = x.hv / (HV / H);
+    const int32_t sq = chunk_seq[x.c];
+    if (sq < 0) return false;
+    x.t0 = cu[sq] + (int64_t)(x.c - chunk_off[sq]) * C;
+    x.n = (int)min((int64_t)C, cu[sq + 1] - x.t0);
+    return true;
+  };
+  u32x4 kreg[KP], qreg[KP], vreg[VP];
+  double greg = 0.0;
+  float breg = 0.f;
+  auto load_kq = [&](const Item& x) {
+    load_tile_rows<DK>(kreg, k + (x.t0 * H + x.h) * (int64_t)DK, rsk, x.n, tid);
+    load_tile_rows<DK>(qreg, q + (x.t0 * H + x.h) * (int64_t)DK, rsk, x.n, tid);
+  };
+  auto load_vg = [&](const Item& x) {
+    load_tile_rows<DV>(vreg, v + (x.t0 * HV + x.hv) * (int64_t)DV, (int64_t)HV * DV, x.n, tid);
+    if (tid < C) {
+      greg = gcum[(x.c * HV + x.hv) * C + tid];
+      breg = beta[(x.c * HV + x.hv) * C + tid];
+    }
+  };
+  const int64_t n_items = max_chunks * HV;
+  {
+    Item x0;
+    if (blockIdx.x < n_items && geom(blockIdx.x, x0)) {
+      load_kq(x0);
+      load_vg(x0);
     }
   }
-  const float rkt = 1.0f / sqrtf(sum_sq<DK>(kw) + kNormEps);
-  const float rqt = 1.0f / sqrtf(sum_sq<DK>(qf) + kNormEps);
-  if (g == 0) sm.rk[t] = rkt;
-
-  // ---- q and k in the state pass's operand order, once per q/k head:
-  // Q fragment (I, sp): rows 16I + m of diag(r_q) Q in fp16, columns 32sp + kperm(g, .);
-  // K fragment f = (sp * 2 + tt) * 2 + s: K^T rows 32sp + 16tt + m, tokens 32s + kperm(g, .)
-  if (hv % (HV / H) == 0) {
-    const int64_t fo = (c * H + h) * (int64_t)(C * DK);
-#pragma unroll
-    for (int sp = 0; sp < NKS; ++sp) {
-      const u32x4 x = row_frag_kperm(sm.qv, SQV, t, 32 * sp, g);
-      half8 y;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        y[2 * j] = (_Float16)(bf_lo(x[j]) * rqt);
-        y[2 * j + 1] = (_Float16)(bf_hi(x[j]) * rqt);
+  for (int64_t it = blockIdx.x; it < n_items; it += gridDim.x) {
+    Item cur, nx;
+    const bool valid = geom(it, cur);
+    const bool has_next = it + gridDim.x < n_items && geom(it + gridDim.x, nx);
+    if (!valid) {  // padding chunk: just move the prefetch on
+      if (has_next) {
+        load_kq(nx);
+        load_vg(nx);
       }
-      *reinterpret_cast<half8*>(Qout + fo + ((w * NKS + sp) * 64 + l) * 8) = y;
+      continue;
     }
-#pragma unroll
-    for (int f = w; f < NKS * 4; f += 4) {
-      const int sp = f >> 2, tt = (f >> 1) & 1, s = f & 1;
-      *reinterpret_cast<u32x4*>(Kout + fo + (f * 64 + l) * 8) =
-          col_frag_tr(sm.ks, SK, 32 * sp + 16 * tt, s, g, m);
-    }
-  }
+    const int hv = cur.hv, h = cur.h, n = cur.n;
+    const int64_t c = cur.c, t0 = cur.t0;
+    const int64_t pair = c * HV + hv;
 
-  // ---- Grams of the own rows against tiles J <= w, transposed:
-  // D[J] = Dl(K_J K_w^T), E[J] = Dl(K_J Q_w^T); lane (g, m): row 16J + 4g + i, column t
-  f32x4 D[4], E[4];
-#pragma unroll
-  for (int J = 0; J < 4; ++J) {
-    D[J] = f32x4{0.f, 0.f, 0.f, 0.f};
-    E[J] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (J < w) {
-#pragma unroll
-      for (int s = 0; s < NKS; ++s) {
-        const bf16x8 kj = bf16x8_from_u32x4(kf[J < 3 ? J : 0][s]);
-        D[J] = mma_bf16(kj, bf16x8_from_u32x4(kw[s]), D[J]);
-        E[J] = mma_bf16(kj, bf16x8_from_u32x4(qf[s]), E[J]);
+    // ---- stage K and Q rows in LDS from the prefetch registers; gates (wave 0)
+    store_tile_rows<DK>(sm.ks, SK, kreg, tid);
+    store_tile_rows<DK>(sm.qv, SQV, qreg, tid);
+    if (tid < C) {
+      sm.G2[tid] = greg * kLog2e;
+      sm.bt[tid] = breg;
+    }
+    lds_barrier();  // (0) K, Q staged
+    if (has_next) load_kq(nx);
+
+    // ---- operand fragments of the own rows and of the earlier tiles; norms
+    u32x4 kw[NKS], qf[NKS];
+    u32x4 kf[3][NKS];
+    row_frags<DK>(kw, sm.ks, SK, t, g);
+    row_frags<DK>(qf, sm.qv, SQV, t, g);
+  #pragma unroll
+    for (int J = 0; J < 3; ++J) {
+      if (J < w) {
+        row_frags<DK>(kf[J], sm.ks, SK, 16 * J + m, g);
+      } else {
+  #pragma unroll
+        for (int s = 0; s < NKS; ++s) kf[J][s] = u32x4{0u, 0u, 0u, 0u};
       }
-    } else if (J == w) {
-#pragma unroll
-      for (int s = 0; s < NKS; ++s) {
-        D[J] = mma_bf16(bf16x8_from_u32x4(kw[s]), bf16x8_from_u32x4(kw[s]), D[J]);
-        E[J] = mma_bf16(bf16x8_from_u32x4(kw[s]), bf16x8_from_u32x4(qf[s]), E[J]);
+    }
+    const float rkt = 1.0f / sqrtf(sum_sq<DK>(kw) + kNormEps);
+    const float rqt = 1.0f / sqrtf(sum_sq<DK>(qf) + kNormEps);
+    if (g == 0) sm.rk[t] = rkt;
+
+    // ---- q and k in the state pass's operand order, once per q/k head:
+    // Q fragment (I, sp): rows 16I + m of diag(r_q) Q in fp16, columns 32sp + kperm(g, .);
+    // K fragment f = (sp * 2 + tt) * 2 + s: K^T rows 32sp + 16tt + m, tokens 32s + kperm(g, .)
+    if (hv % (HV / H) == 0) {
+      const int64_t fo = (c * H + h) * (int64_t)(C * DK);
+  #pragma unroll
+      for (int sp = 0; sp < NKS; ++sp) {
+        const u32x4 x = row_frag_kperm(sm.qv, SQV, t, 32 * sp, g);
+        half8 y;
+  #pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          y[2 * j] = (_Float16)(bf_lo(x[j]) * rqt);
+          y[2 * j + 1] = (_Float16)(bf_hi(x[j]) * rqt);
+        }
+        *reinterpret_cast<half8*>(Qout + fo + ((w * NKS + sp) * 64 + l) * 8) = y;
+      }
+  #pragma unroll
+      for (int f = w; f < NKS * 4; f += 4) {
+        const int sp = f >> 2, tt = (f >> 1) & 1, s = f & 1;
+        *reinterpret_cast<u32x4*>(Kout + fo + (f * 64 + l) * 8) =
+            col_frag_tr(sm.ks, SK, 32 * sp + 16 * tt, s, g, m);
       }
     }
-  }
-  lds_barrier();  // (1) r_k visible; Q no longer read
 
-  // ---- V rows into the Q region (every wave is done with Q); visible after (2)
-#pragma unroll
-  for (int u = 0; u < VP; ++u) {
-    const int e = tid + 256 * u, row = e / (DV / 8), c8 = (e % (DV / 8)) * 8;
-    *reinterpret_cast<u32x4*>(&sm.qv[row * SQV + c8]) = vreg[u];
-  }
-
-  // ---- scale: a[J] = Dl(A_wJ^T) (A[t][i], i = 16J + 4g + ii < t) and the A_qk rows
-  const double G2t = sm.G2[t];
-  const float btt = sm.bt[t];
-  const float egt = __builtin_amdgcn_exp2f((float)G2t);
-  if (g == 0) {
-    eg_out[pair * C + t] = egt;
-    kd_out[pair * C + t] = __builtin_amdgcn_exp2f((float)(sm.G2[C - 1] - G2t)) * rkt;
-  }
-  f32x4 a[4];
-  half4 aq[4];
-#pragma unroll
-  for (int J = 0; J < 4; ++J) {
-    f32x4 x;
-#pragma unroll
-    for (int ii = 0; ii < 4; ++ii) {
-      const int i = 16 * J + 4 * g + ii;
-      const float rki = sm.rk[i];
-      a[J][ii] = (J <= w && i < t) ? btt * rkt * rki * D[J][ii] : 0.f;
-      x[ii] = (J <= w && i <= t)
-                  ? __builtin_amdgcn_exp2f((float)(G2t - sm.G2[i])) * rqt * rki * E[J][ii]
-                  : 0.f;
-    }
-    aq[J] = to_half4(x);
-  }
-#pragma unroll
-  for (int s = 0; s < 2; ++s)
-    *reinterpret_cast<half8*>(Aout + pair * C * C + ((w * 2 + s) * 64 + l) * 8) =
-        cat(aq[2 * s], aq[2 * s + 1]);
-
-  // ---- diagonal tile: T_ww = (I + A_ww)^-1 by forward substitution, lane = column m
-  float* sqw = sm.sq[w];
-  f32x4 aw = a[0];
-#pragma unroll
-  for (int J = 1; J < 4; ++J)
-    if (J == w) aw = a[J];
-  *reinterpret_cast<f32x4*>(&sqw[m * SA + 4 * g]) = aw;  // row m of A_ww, columns 4g..
-  __builtin_amdgcn_wave_barrier();
-  float x[16];
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    float acc = 0.f;
-#pragma unroll
-    for (int i = 0; i < r; ++i) acc += sqw[r * SA + i] * x[i];
-    x[r] = (r < m) ? 0.f : ((r == m) ? 1.f : -acc);
-  }
-  __builtin_amdgcn_wave_barrier();
-  if (g == 0) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) sqw[r * SA + m] = x[r];  // column m of T_ww
-  }
-  __builtin_amdgcn_wave_barrier();
-  const f32x4 tww_t = *reinterpret_cast<const f32x4*>(&sqw[m * SA + 4 * g]);  // Dl(T_ww^T)
-  f32x4 tww;                                                                  // Dl(T_ww)
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    float y = x[i];
-#pragma unroll
-    for (int gg = 1; gg < 4; ++gg)
-      if (g == gg) y = x[4 * gg + i];
-    tww[i] = y;
-  }
-  sm.tex[tex_slot(w, w)][l] = tww;
-  f32x4 ttr[4];  // Dl(T_wJ^T), J <= w
-#pragma unroll
-  for (int J = 0; J < 4; ++J) ttr[J] = (J == w) ? tww_t : f32x4{0.f, 0.f, 0.f, 0.f};
-  lds_barrier();  // (2)
-
-  // ---- off-diagonal tiles by distance d: X = sum_K A_wK T_KJ, T_wJ = -T_ww X
-#pragma unroll
-  for (int d = 1; d < 4; ++d) {
-    if (w >= d) {
-      const int J = w - d;
-      f32x4 X = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int K = 0; K < 3; ++K) {
-        if (K >= J && K < w) {
-          const f32x4 tkj = sm.tex[tex_slot(K, J)][l];
-#pragma unroll
-          for (int s = 0; s < 4; ++s) X = mma_f32(a[K][s], tkj[s], X);
+    // ---- Grams of the own rows against tiles J <= w, transposed:
+    // D[J] = Dl(K_J K_w^T), E[J] = Dl(K_J Q_w^T); lane (g, m): row 16J + 4g + i, column t
+    f32x4 D[4], E[4];
+  #pragma unroll
+    for (int J = 0; J < 4; ++J) {
+      D[J] = f32x4{0.f, 0.f, 0.f, 0.f};
+      E[J] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (J < w) {
+  #pragma unroll
+        for (int s = 0; s < NKS; ++s) {
+          const bf16x8 kj = bf16x8_from_u32x4(kf[J < 3 ? J : 0][s]);
+          D[J] = mma_bf16(kj, bf16x8_from_u32x4(kw[s]), D[J]);
+          E[J] = mma_bf16(kj, bf16x8_from_u32x4(qf[s]), E[J]);
+        }
+      } else if (J == w) {
+  #pragma unroll
+        for (int s = 0; s < NKS; ++s) {
+          D[J] = mma_bf16(bf16x8_from_u32x4(kw[s]), bf16x8_from_u32x4(kw[s]), D[J]);
+          E[J] = mma_bf16(bf16x8_from_u32x4(kw[s]), bf16x8_from_u32x4(qf[s]), E[J]);
         }
       }
-      f32x4 Y = {0.f, 0.f, 0.f, 0.f}, Z = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        Y = mma_f32(tww_t[s], X[s], Y);  // Dl(T_ww X)
-        Z = mma_f32(X[s], tww_t[s], Z);  // Dl(X^T T_ww^T)
+    }
+    lds_barrier();  // (1) r_k visible; Q no longer read
+
+    // ---- V rows into the Q region (every wave is done with Q); visible after (2)
+    store_tile_rows<DV>(sm.qv, SQV, vreg, tid);
+    if (has_next) load_vg(nx);
+
+    // ---- scale: a[J] = Dl(A_wJ^T) (A[t][i], i = 16J + 4g + ii < t) and the A_qk rows
+    const double G2t = sm.G2[t];
+    const float btt = sm.bt[t];
+    const float egt = __builtin_amdgcn_exp2f((float)G2t);
+    if (g == 0) {
+      eg_out[pair * C + t] = egt;
+      kd_out[pair * C + t] = __builtin_amdgcn_exp2f((float)(sm.G2[C - 1] - G2t)) * rkt;
+    }
+    f32x4 a[4];
+    half4 aq[4];
+  #pragma unroll
+    for (int J = 0; J < 4; ++J) {
+      f32x4 x;
+  #pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        const int i = 16 * J + 4 * g + ii;
+        const float rki = sm.rk[i];
+        a[J][ii] = (J <= w && i < t) ? btt * rkt * rki * D[J][ii] : 0.f;
+        x[ii] = (J <= w && i <= t)
+                    ? __builtin_amdgcn_exp2f((float)(G2t - sm.G2[i])) * rqt * rki * E[J][ii]
+                    : 0.f;
       }
-      if (w < 3 && d < 3) sm.tex[tex_slot(w, J)][l] = -Y;
-#pragma unroll
-      for (int JJ = 0; JJ < 3; ++JJ)
-        if (JJ == J) ttr[JJ] = -Z;
+      aq[J] = to_half4(x);
     }
-    if (d < 3) lds_barrier();  // (3), (4)
-  }
+  #pragma unroll
+    for (int s = 0; s < 2; ++s)
+      *reinterpret_cast<half8*>(Aout + pair * C * C + ((w * 2 + s) * 64 + l) * 8) =
+          cat(aq[2 * s], aq[2 * s + 1]);
 
-  // ---- T1^T, T2^T fragments of the own rows (bf16 hi + lo), tiles J <= w
-  bf16x4 t1h[4], t1l[4], t2h[4], t2l[4];
-#pragma unroll
-  for (int J = 0; J < 4; ++J) {
-    f32x4 x1, x2;
-#pragma unroll
-    for (int ii = 0; ii < 4; ++ii) {
-      const int i = 16 * J + 4 * g + ii;
-      const float tv = ttr[J][ii];  // T[t][i], zero for i > t
-      const float bti = sm.bt[i];
-      x1[ii] = egt * tv * bti * sm.rk[i];
-      // e^{G_t - G_i} overflows for i > t under strong decay: mask, do not multiply by 0
-      x2[ii] = (i <= t) ? __builtin_amdgcn_exp2f((float)(G2t - sm.G2[i])) * tv * bti : 0.f;
+    // ---- diagonal tile: T_ww = (I + A_ww)^-1 by forward substitution, lane = column m
+    float* sqw = sm.sq[w];
+    f32x4 aw = a[0];
+  #pragma unroll
+    for (int J = 1; J < 4; ++J)
+      if (J == w) aw = a[J];
+    *reinterpret_cast<f32x4*>(&sqw[m * SA + 4 * g]) = aw;  // row m of A_ww, columns 4g..
+    __builtin_amdgcn_wave_barrier();
+    float x[16];
+  #pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float acc = 0.f;
+  #pragma unroll
+      for (int i = 0; i < r; ++i) acc += sqw[r * SA + i] * x[i];
+      x[r] = (r < m) ? 0.f : ((r == m) ? 1.f : -acc);
     }
-    t1h[J] = to_bf16x4(x1);
-    t1l[J] = to_bf16x4(x1 - to_f32x4(t1h[J]));
-    t2h[J] = to_bf16x4(x2);
-    t2l[J] = to_bf16x4(x2 - to_f32x4(t2h[J]));
-  }
-  const int ns = (w >> 1) + 1;  // token steps that hold tiles J <= w
+    __builtin_amdgcn_wave_barrier();
+    if (g == 0) {
+  #pragma unroll
+      for (int r = 0; r < 16; ++r) sqw[r * SA + m] = x[r];  // column m of T_ww
+    }
+    __builtin_amdgcn_wave_barrier();
+    const f32x4 tww_t = *reinterpret_cast<const f32x4*>(&sqw[m * SA + 4 * g]);  // Dl(T_ww^T)
+    f32x4 tww;                                                                  // Dl(T_ww)
+  #pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float y = x[i];
+  #pragma unroll
+      for (int gg = 1; gg < 4; ++gg)
+        if (g == gg) y = x[4 * gg + i];
+      tww[i] = y;
+    }
+    sm.tex[tex_slot(w, w)][l] = tww;
+    f32x4 ttr[4];  // Dl(T_wJ^T), J <= w
+  #pragma unroll
+    for (int J = 0; J < 4; ++J) ttr[J] = (J == w) ? tww_t : f32x4{0.f, 0.f, 0.f, 0.f};
+    lds_barrier();  // (2)
 
-  // ---- W<-^T = K^T T1^T for the own token columns: D tiles (dk 32sp + 16tt, rows t)
-#pragma unroll
-  for (int sp = 0; sp < NKS; ++sp) {
-    f32x4 acc[2];
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      acc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
+    // ---- off-diagonal tiles by distance d: X = sum_K A_wK T_KJ, T_wJ = -T_ww X
+  #pragma unroll
+    for (int d = 1; d < 4; ++d) {
+      if (w >= d) {
+        const int J = w - d;
+        f32x4 X = {0.f, 0.f, 0.f, 0.f};
+  #pragma unroll
+        for (int K = 0; K < 3; ++K) {
+          if (K >= J && K < w) {
+            const f32x4 tkj = sm.tex[tex_slot(K, J)][l];
+  #pragma unroll
+            for (int s = 0; s < 4; ++s) X = mma_f32(a[K][s], tkj[s], X);
+          }
+        }
+        f32x4 Y = {0.f, 0.f, 0.f, 0.f}, Z = {0.f, 0.f, 0.f, 0.f};
+  #pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          Y = mma_f32(tww_t[s], X[s], Y);  // Dl(T_ww X)
+          Z = mma_f32(X[s], tww_t[s], Z);  // Dl(X^T T_ww^T)
+        }
+        if (w < 3 && d < 3) sm.tex[tex_slot(w, J)][l] = -Y;
+  #pragma unroll
+        for (int JJ = 0; JJ < 3; ++JJ)
+          if (JJ == J) ttr[JJ] = -Z;
+      }
+      if (d < 3) lds_barrier();  // (3), (4)
+    }
+
+    // ---- T1^T, T2^T fragments of the own rows (bf16 hi + lo), tiles J <= w
+    bf16x4 t1h[4], t1l[4], t2h[4], t2l[4];
+  #pragma unroll
+    for (int J = 0; J < 4; ++J) {
+      f32x4 x1, x2;
+  #pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        const int i = 16 * J + 4 * g + ii;
+        const float tv = ttr[J][ii];  // T[t][i], zero for i > t
+        const float bti = sm.bt[i];
+        x1[ii] = egt * tv * bti * sm.rk[i];
+        // e^{G_t - G_i} overflows for i > t under strong decay: mask, do not multiply by 0
+        x2[ii] = (i <= t) ? __builtin_amdgcn_exp2f((float)(G2t - sm.G2[i])) * tv * bti : 0.f;
+      }
+      t1h[J] = to_bf16x4(x1);
+      t1l[J] = to_bf16x4(x1 - to_f32x4(t1h[J]));
+      t2h[J] = to_bf16x4(x2);
+      t2l[J] = to_bf16x4(x2 - to_f32x4(t2h[J]));
+    }
+    const int ns = (w >> 1) + 1;  // token steps that hold tiles J <= w
+
+    // ---- W<-^T = K^T T1^T for the own token columns: D tiles (dk 32sp + 16tt, rows t)
+  #pragma unroll
+    for (int sp = 0; sp < NKS; ++sp) {
+      f32x4 acc[2];
+  #pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        acc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  #pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          if (s < ns) {
+            const bf16x8 ka = bf16x8_from_u32x4(col_frag_tr(sm.ks, SK, 32 * sp + 16 * tt, s, g, m));
+            acc[tt] = mma_bf16(ka, cat_bf(t1h[2 * s], t1h[2 * s + 1]), acc[tt]);
+            acc[tt] = mma_bf16(ka, cat_bf(t1l[2 * s], t1l[2 * s + 1]), acc[tt]);
+          }
+        }
+      }
+      *reinterpret_cast<half8*>(Wout + pair * C * DK + ((w * NKS + sp) * 64 + l) * 8) =
+          cat(to_half4(acc[0]), to_half4(acc[1]));
+    }
+
+    // ---- U~ = T2 V for the own rows: D tiles (rows 16w.., dv 16cc..), each stored as one
+    // contiguous 512-byte block (a wave writing whole cache lines)
+  #pragma unroll
+    for (int cc = 0; cc < DV / 16; ++cc) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  #pragma unroll
       for (int s = 0; s < 2; ++s) {
         if (s < ns) {
-          const bf16x8 ka = bf16x8_from_u32x4(col_frag_tr(sm.ks, SK, 32 * sp + 16 * tt, s, g, m));
-          acc[tt] = mma_bf16(ka, cat_bf(t1h[2 * s], t1h[2 * s + 1]), acc[tt]);
-          acc[tt] = mma_bf16(ka, cat_bf(t1l[2 * s], t1l[2 * s + 1]), acc[tt]);
+          const bf16x8 vb = bf16x8_from_u32x4(col_frag_tr(sm.qv, SQV, 16 * cc, s, g, m));
+          acc = mma_bf16(cat_bf(t2h[2 * s], t2h[2 * s + 1]), vb, acc);
+          acc = mma_bf16(cat_bf(t2l[2 * s], t2l[2 * s + 1]), vb, acc);
         }
       }
+      *reinterpret_cast<half4*>(Uout + pair * C * DV + ((cc * 4 + w) * 64 + l) * 4) =
+          to_half4(acc);
     }
-    *reinterpret_cast<half8*>(Wout + pair * C * DK + ((w * NKS + sp) * 64 + l) * 8) =
-        cat(to_half4(acc[0]), to_half4(acc[1]));
-  }
-
-  // ---- U~ = T2 V for the own rows: D tiles (rows 16w.., dv 16cc..), stored in pairs of
-  // row tiles (2s, 2s + 1) per lane so the state pass loads 16 bytes per lane
-#pragma unroll
-  for (int cc = 0; cc < DV / 16; ++cc) {
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      if (s < ns) {
-        const bf16x8 vb = bf16x8_from_u32x4(col_frag_tr(sm.qv, SQV, 16 * cc, s, g, m));
-        acc = mma_bf16(cat_bf(t2h[2 * s], t2h[2 * s + 1]), vb, acc);
-        acc = mma_bf16(cat_bf(t2l[2 * s], t2l[2 * s + 1]), vb, acc);
-      }
-    }
-    *reinterpret_cast<half4*>(Uout + pair * C * DV + ((cc * 2 + (w >> 1)) * 64 + l) * 8 +
-                              (w & 1) * 4) = to_half4(acc);
+    lds_barrier();  // (5) every LDS region is free for the next item
   }
 }
 
@@ -438,9 +489,18 @@ hipError_t launch_prep_t(const void* q, const void* k, const void* v, const int6
                          const float* beta, const Shape& s, int64_t max_chunks, _Float16* w,
                          _Float16* u, float* kd, _Float16* aqk, float* eg, uint16_t* kf,
                          _Float16* qf, hipStream_t st) {
-  hipLaunchKernelGGL((mfma_prep_kernel<DK, DV>), dim3((unsigned)max_chunks, (unsigned)s.HV),
-                     dim3(256), 0, st, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
-                     cu, off, cseq, gcum, beta, s.H, s.HV, w, u, kd, aqk, eg, kf, qf);
+  // Persistent grid: as many workgroups as fit on the device at once.
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, mfma_prep_kernel<DK, DV>, 256, 0) !=
+          hipSuccess)
+    return hipErrorInvalidValue;
+  const int64_t items = max_chunks * s.HV;
+  const int64_t grid = std::min<int64_t>(items, (int64_t)std::max(cus, 1) * std::max(per_cu, 1));
+  hipLaunchKernelGGL((mfma_prep_kernel<DK, DV>), dim3((unsigned)grid), dim3(256), 0, st,
+                     (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, cu, off, cseq,
+                     gcum, beta, s.H, s.HV, max_chunks, w, u, kd, aqk, eg, kf, qf);
   return hipGetLastError();
 }
 

@@ -109,7 +109,7 @@ __global__ __launch_bounds__(64 * DS) void mfma_state_kernel(
   // ---- operand registers of one chunk
   u32x4 wf[4][NOWN], qf[4][NOWN];  // W<- and Qh fragments: row tile, own dk step
   u32x4 kf[NOWN][2][2];            // k^T fragments: own dk step, 16-dk half, token step
-  u32x4 uf[2];                     // U~ (fp16 D tiles) of column tile ct, row tiles 2s, 2s+1
+  u32x2 uf[4];                     // U~ (fp16 D tiles) of column tile ct, row tile
   u32x4 af[NOR][2];                // A_qk fragments of the own output row tiles
   f32x4 kdv[4];                    // e^{G_n - G} r_k of rows 16I + 4g + i
   f32x4 egv[NOR];                  // e^G of the own output rows
@@ -131,9 +131,9 @@ __global__ __launch_bounds__(64 * DS) void mfma_state_kernel(
   };
   auto load_ukd = [&](int cl) {
     const int64_t pr = pair_of(cl);
-    const _Float16* ub = Ut + pr * C * DV + (ct * 2 * 64 + l) * 8;
+    const _Float16* ub = Ut + pr * C * DV + (ct * 4 * 64 + l) * 4;
 #pragma unroll
-    for (int s = 0; s < 2; ++s) uf[s] = *reinterpret_cast<const u32x4*>(ub + s * 64 * 8);
+    for (int I = 0; I < 4; ++I) uf[I] = *reinterpret_cast<const u32x2*>(ub + I * 64 * 4);
 #pragma unroll
     for (int I = 0; I < 4; ++I)
       kdv[I] = *reinterpret_cast<const f32x4*>(kdws + pr * C + 16 * I + 4 * g);
@@ -208,10 +208,7 @@ __global__ __launch_bounds__(64 * DS) void mfma_state_kernel(
 #pragma unroll
       for (int o = 0; o < DS; ++o)
         if (o != hs) pt += sm.partP[buf][o][I][l];
-      const half8 ut8 = half8_from_u32x4(uf[I >> 1]);
-      half4 ut;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) ut[i] = ut8[(I & 1) * 4 + i];
+      const half4 ut = __builtin_bit_cast(half4, uf[I]);
 #pragma unroll
       for (int i = 0; i < 4; ++i) U[I][i] = (float)ut[i] - pt[i];
     }
@@ -260,16 +257,16 @@ __global__ __launch_bounds__(64 * DS) void mfma_state_kernel(
         if (s <= (I >> 1))
           AU = mma_f16(half8_from_u32x4(af[r][s]),
                        cat(to_half4(U[2 * s]), to_half4(U[2 * s + 1])), AU);
-      uint16_t* ob = out + ((t0 + 16 * I + 4 * g) * HV + hv) * (int64_t)DV + 16 * ct + m;
+      const bf16x4 ov = to_bf16x4(egv[r] * o1 + AU);  // round to nearest even
+      __bf16* ob = reinterpret_cast<__bf16*>(out) +
+                   ((t0 + 16 * I + 4 * g) * HV + hv) * (int64_t)DV + 16 * ct + m;
       if (n == C) {  // full chunk: no per-row test
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          ob[i * (int64_t)HV * DV] = f32_to_bf16_bits(egv[r][i] * o1[i] + AU[i]);
+        for (int i = 0; i < 4; ++i) ob[i * (int64_t)HV * DV] = ov[i];
       } else {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          if (16 * I + 4 * g + i < n)
-            ob[i * (int64_t)HV * DV] = f32_to_bf16_bits(egv[r][i] * o1[i] + AU[i]);
+          if (16 * I + 4 * g + i < n) ob[i * (int64_t)HV * DV] = ov[i];
       }
     }
     load_out(nx);

@@ -12,16 +12,18 @@
 // state). Chunks of a request are processed in order (pymllm page: the propagation
 // between chunks remains sequential over ceil(T/C) steps).
 //
-// Work split: one workgroup per (request, value head, 16 state rows); its DS wavefronts
-// split dk, wave hs owning dk steps hs * NOWN .. (hs + 1) * NOWN - 1 of the 16 rows of
-// S^T, in fp32 registers for the whole request. Every operand comes straight from
-// global memory into MFMA operand registers, in the fragment orders the prep kernel
-// wrote (one contiguous 1 KiB piece per fragment); each register set is reloaded
-// with the next chunk's data right after its last use, so the loads have about one
-// chunk of time to land. LDS carries only the partial sums over dk (double-buffered by
-// chunk parity): P = W<- S^T for all rows, which every wave completes into U itself,
-// and Q S^T for the rows another wave finishes. One barrier per chunk; none when one
-// wave holds all of dk.
+// Work split: one workgroup per (request, value head, 16 state rows), with two roles.
+//   * DS state waves split dk: wave hs holds dk steps hs * NOWN .. of the 16 rows of S^T
+//     in fp32 registers for the whole request and runs only the chain that carries the
+//     state from chunk to chunk: P = W<- S^T over its dk slice, the exchange of those
+//     partial sums (LDS, double-buffered), U, and the update of its slice.
+//   * NO output waves form O for the previous chunk from the fp16 copies of S^T and U
+//     that the state waves leave in LDS (triple- and double-buffered), so the output
+//     products and stores stay off that chain.
+// Every operand comes straight from global memory into MFMA operand registers, in the
+// fragment orders the prep kernel wrote (one contiguous 1 KiB piece per fragment); each
+// register set is reloaded with the next chunk's data right after its last use. One
+// barrier per chunk for the whole workgroup.
 //
 // Matrix-core operands: W<- and S in fp16 for P = W<- S^T; normalised q and S in fp16
 // for Qh S^T; raw bf16 k with diag(e^{G_n-G} r_k) U as bf16 hi + lo for the update;
@@ -34,11 +36,13 @@ namespace {
 
 using namespace mfma;
 constexpr int C = 64;
+constexpr int NO = 2;  // output waves per workgroup, two row tiles each
 
-template <int DS>
+template <int DS, int NKS>
 struct StateSmem {
   f32x4 partP[2][DS][4][64];  // partial W<- S^T: chunk parity, dk owner, row tile, lane
-  f32x4 partO[2][DS][4][64];  // partial Q S^T
+  half8 s16[3][NKS][64];      // fp16 S^T fragments by dk step: chunk mod 3
+  half8 u16[2][2][64];        // fp16 U fragments (B operand of A_qk U): parity, token step
 };
 
 __device__ __forceinline__ bf16x4 to_bf16x4(f32x4 x) {
@@ -65,7 +69,7 @@ __device__ __forceinline__ bf16x8 cat_bf(bf16x4 a, bf16x4 b) {
 }
 
 template <int DK, int DS>
-__global__ __launch_bounds__(64 * DS) void mfma_state_kernel(
+__global__ __launch_bounds__(64 * (DS + NO)) void mfma_state_kernel(
     const _Float16* __restrict__ Qf, const uint16_t* __restrict__ Kf,
     const int64_t* __restrict__ cu, const int64_t* __restrict__ cache_indices,
     const int32_t* __restrict__ chunk_off, const double* __restrict__ gcum,
@@ -74,12 +78,11 @@ __global__ __launch_bounds__(64 * DS) void mfma_state_kernel(
     const float* __restrict__ egws, int B, int H, int HV, int DV,
     float* __restrict__ state_pool, uint16_t* __restrict__ out) {
   constexpr int NKS = DK / 32;    // 32-wide dk steps
-  constexpr int NOWN = NKS / DS;  // dk steps per wave
-  constexpr int NOR = 4 / DS;     // output row tiles per wave: I = hs + DS * r
-  __shared__ StateSmem<DS> sm;
+  constexpr int NOWN = NKS / DS;  // dk steps per state wave
+  __shared__ StateSmem<DS, NKS> sm;
 
   // Blocks of the same (request, head) share blockIdx.x mod 8, so they run on one
-  // XCD and re-read q, k and W<- from its L2.
+  // XCD and re-read the fragment blocks from its L2.
   const int nvb = DV / 16;
   const int64_t x = blockIdx.x;
   const int64_t rest = x >> 3;
@@ -91,193 +94,203 @@ __global__ __launch_bounds__(64 * DS) void mfma_state_kernel(
   if (L <= 0) return;
   const int h = hv / (HV / H);
   const int64_t slot = cache_indices[seq];
-  const int tid = threadIdx.x, hs = tid >> 6, l = tid & 63, m = l & 15, g = l >> 4;
+  const int tid = threadIdx.x, wv = tid >> 6, l = tid & 63, m = l & 15, g = l >> 4;
   const int nch = (int)((L + C - 1) / C);
   const int64_t cbase = chunk_off[seq];
   const int64_t tseq = cu[seq];
   const int64_t tend = cu[seq + 1];
-
-  // ---- resident state: S^T tiles of the owned dk steps sp' = hs * NOWN + sp
-  float* Sg = state_pool + ((slot * HV + hv) * (int64_t)DV + 16 * ct + m) * DK;
-  f32x4 S[NOWN][2];
-#pragma unroll
-  for (int sp = 0; sp < NOWN; ++sp)
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
-      S[sp][tt] = *reinterpret_cast<const f32x4*>(Sg + 32 * (hs * NOWN + sp) + 16 * tt + 4 * g);
-
-  // ---- operand registers of one chunk
-  u32x4 wf[4][NOWN], qf[4][NOWN];  // W<- and Qh fragments: row tile, own dk step
-  u32x4 kf[NOWN][2][2];            // k^T fragments: own dk step, 16-dk half, token step
-  u32x2 uf[4];                     // U~ (fp16 D tiles) of column tile ct, row tile
-  u32x4 af[NOR][2];                // A_qk fragments of the own output row tiles
-  f32x4 kdv[4];                    // e^{G_n - G} r_k of rows 16I + 4g + i
-  f32x4 egv[NOR];                  // e^G of the own output rows
-  double gn;                       // G_n (the gate pass pads G with zero log-decay)
-
   auto pair_of = [&](int cl) { return (cbase + cl) * HV + hv; };
-  auto load_wq = [&](int cl) {
-    const int64_t pr = pair_of(cl);
-    const _Float16* wb = W + pr * C * DK;
-    const _Float16* qb = Qf + ((cbase + cl) * H + h) * (int64_t)(C * DK);
-#pragma unroll
-    for (int I = 0; I < 4; ++I)
-#pragma unroll
-      for (int sp = 0; sp < NOWN; ++sp) {
-        const int spg = hs * NOWN + sp;
-        wf[I][sp] = *reinterpret_cast<const u32x4*>(wb + ((I * NKS + spg) * 64 + l) * 8);
-        qf[I][sp] = *reinterpret_cast<const u32x4*>(qb + ((I * NKS + spg) * 64 + l) * 8);
-      }
-  };
-  auto load_ukd = [&](int cl) {
-    const int64_t pr = pair_of(cl);
-    const _Float16* ub = Ut + pr * C * DV + (ct * 4 * 64 + l) * 4;
-#pragma unroll
-    for (int I = 0; I < 4; ++I) uf[I] = *reinterpret_cast<const u32x2*>(ub + I * 64 * 4);
-#pragma unroll
-    for (int I = 0; I < 4; ++I)
-      kdv[I] = *reinterpret_cast<const f32x4*>(kdws + pr * C + 16 * I + 4 * g);
-  };
-  auto load_k = [&](int cl) {
-    const int64_t pr = pair_of(cl);
-    const uint16_t* kb = Kf + ((cbase + cl) * H + h) * (int64_t)(C * DK);
+
+  if (wv < DS) {
+    // ======================= state wave =======================
+    const int hs = wv;
+    float* Sg = state_pool + ((slot * HV + hv) * (int64_t)DV + 16 * ct + m) * DK;
+    f32x4 S[NOWN][2];
 #pragma unroll
     for (int sp = 0; sp < NOWN; ++sp)
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-        for (int s = 0; s < 2; ++s)
-          kf[sp][tt][s] = *reinterpret_cast<const u32x4*>(
-              kb + ((((hs * NOWN + sp) * 2 + tt) * 2 + s) * 64 + l) * 8);
-    gn = gcum[pr * C + C - 1];
-  };
-  auto load_out = [&](int cl) {
-    const int64_t pr = pair_of(cl);
-#pragma unroll
-    for (int r = 0; r < NOR; ++r) {
-      const int I = hs + DS * r;
-#pragma unroll
-      for (int s = 0; s < 2; ++s)
-        af[r][s] = *reinterpret_cast<const u32x4*>(Aqk + pr * C * C + ((I * 2 + s) * 64 + l) * 8);
-      egv[r] = *reinterpret_cast<const f32x4*>(egws + pr * C + 16 * I + 4 * g);
-    }
-  };
-  load_wq(0);
-  load_ukd(0);
-  load_k(0);
-  load_out(0);
+        S[sp][tt] = *reinterpret_cast<const f32x4*>(Sg + 32 * (hs * NOWN + sp) + 16 * tt + 4 * g);
 
-  // Each register set is reloaded with chunk cl + 1 right after its last use in chunk
-  // cl (chunk nch - 1 is reloaded on the last step: in bounds, and no branch).
-  for (int cl = 0; cl < nch; ++cl) {
-    const int buf = cl & 1;
-    const int nx = min(cl + 1, nch - 1);
-    const int64_t t0 = tseq + (int64_t)cl * C;
-    const int n = (int)min((int64_t)C, tend - t0);
-
-    // ---- partial P = W<- S^T and O1 = Qh S^T over the owned dk steps
-    half8 s16[NOWN];
+    u32x4 wf[4][NOWN];     // W<- fragments: row tile, own dk step
+    u32x4 kf[NOWN][2][2];  // k^T fragments: own dk step, 16-dk half, token step
+    u32x2 uf[4];           // U~ (fp16 D tiles) of column tile ct, row tile
+    f32x4 kdv[4];          // e^{G_n - G} r_k of rows 16I + 4g + i
+    double gn;             // G_n (the gate pass pads G with zero log-decay)
+    auto load_w = [&](int cl) {
+      const _Float16* wb = W + pair_of(cl) * C * DK;
 #pragma unroll
-    for (int sp = 0; sp < NOWN; ++sp) s16[sp] = cat(to_half4(S[sp][0]), to_half4(S[sp][1]));
-    f32x4 pp[4], po[4];
+      for (int I = 0; I < 4; ++I)
 #pragma unroll
-    for (int I = 0; I < 4; ++I) {
-      pp[I] = f32x4{0.f, 0.f, 0.f, 0.f};
-      po[I] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int sp = 0; sp < NOWN; ++sp) {
-        pp[I] = mma_f16(half8_from_u32x4(wf[I][sp]), s16[sp], pp[I]);
-        po[I] = mma_f16(half8_from_u32x4(qf[I][sp]), s16[sp], po[I]);
-      }
-    }
-    load_wq(nx);
-    if (DS > 1) {
+        for (int sp = 0; sp < NOWN; ++sp)
+          wf[I][sp] = *reinterpret_cast<const u32x4*>(
+              wb + ((I * NKS + hs * NOWN + sp) * 64 + l) * 8);
+    };
+    auto load_ukd = [&](int cl) {
+      const int64_t pr = pair_of(cl);
+      const _Float16* ub = Ut + pr * C * DV + (ct * 4 * 64 + l) * 4;
 #pragma unroll
       for (int I = 0; I < 4; ++I) {
-        sm.partP[buf][hs][I][l] = pp[I];
-        if (I % DS != hs) sm.partO[buf][hs][I][l] = po[I];
+        uf[I] = *reinterpret_cast<const u32x2*>(ub + I * 64 * 4);
+        kdv[I] = *reinterpret_cast<const f32x4*>(kdws + pr * C + 16 * I + 4 * g);
       }
-      lds_barrier();
-    }
+    };
+    auto load_k = [&](int cl) {
+      const uint16_t* kb = Kf + ((cbase + cl) * H + h) * (int64_t)(C * DK);
+#pragma unroll
+      for (int sp = 0; sp < NOWN; ++sp)
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+          for (int s = 0; s < 2; ++s)
+            kf[sp][tt][s] = *reinterpret_cast<const u32x4*>(
+                kb + ((((hs * NOWN + sp) * 2 + tt) * 2 + s) * 64 + l) * 8);
+      gn = gcum[pair_of(cl) * C + C - 1];
+    };
+    load_w(0);
+    load_ukd(0);
+    load_k(0);
 
-    // ---- U = U~ - P for all rows (every wave of the block forms the same U)
-    f32x4 U[4];
-#pragma unroll
-    for (int I = 0; I < 4; ++I) {
-      f32x4 pt = pp[I];
-#pragma unroll
-      for (int o = 0; o < DS; ++o)
-        if (o != hs) pt += sm.partP[buf][o][I][l];
-      const half4 ut = __builtin_bit_cast(half4, uf[I]);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) U[I][i] = (float)ut[i] - pt[i];
-    }
-    // U'' = diag(e^{G_n - G} r_k) U as the bf16 hi + lo B operand of the update
-    bf16x8 bh[2], bl[2];
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const f32x4 ua = U[2 * s] * kdv[2 * s], ub = U[2 * s + 1] * kdv[2 * s + 1];
-      const bf16x4 ha = to_bf16x4(ua), hb = to_bf16x4(ub);
-      bh[s] = cat_bf(ha, hb);
-      bl[s] = cat_bf(to_bf16x4(ua - to_f32x4(ha)), to_bf16x4(ub - to_f32x4(hb)));
-    }
-    load_ukd(nx);
+    // Each register set is reloaded with chunk cl + 1 right after its last use in chunk
+    // cl (chunk nch - 1 is reloaded on the last step: in bounds, and no branch).
+    for (int cl = 0; cl < nch; ++cl) {
+      const int buf = cl & 1;
+      const int nx = min(cl + 1, nch - 1);
 
-    // ---- S^T <- e^{G_n} S^T + K^T U'' on the owned dk steps
-    const float egn = expf((float)gn);
+      // ---- S^T in fp16: operand of P here, and of Qh S^T for the output waves
+      half8 s16[NOWN];
+#pragma unroll
+      for (int sp = 0; sp < NOWN; ++sp) {
+        s16[sp] = cat(to_half4(S[sp][0]), to_half4(S[sp][1]));
+        sm.s16[cl % 3][hs * NOWN + sp][l] = s16[sp];
+      }
+      // ---- partial P = W<- S^T over the owned dk steps
+      f32x4 pp[4];
+#pragma unroll
+      for (int I = 0; I < 4; ++I) {
+        pp[I] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int sp = 0; sp < NOWN; ++sp)
+          pp[I] = mma_f16(half8_from_u32x4(wf[I][sp]), s16[sp], pp[I]);
+      }
+      load_w(nx);
+      if (DS > 1) {
+#pragma unroll
+        for (int I = 0; I < 4; ++I) sm.partP[buf][hs][I][l] = pp[I];
+      }
+      lds_barrier();  // chunk cl: partial sums and S^T copies visible
+
+      // ---- U = U~ - P for all rows (every state wave forms the same U)
+      f32x4 U[4];
+#pragma unroll
+      for (int I = 0; I < 4; ++I) {
+        f32x4 pt = pp[I];
+#pragma unroll
+        for (int o = 0; o < DS; ++o)
+          if (o != hs) pt += sm.partP[buf][o][I][l];
+        const half4 ut = __builtin_bit_cast(half4, uf[I]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) U[I][i] = (float)ut[i] - pt[i];
+      }
+      if (hs == 0) {
+#pragma unroll
+        for (int s = 0; s < 2; ++s) sm.u16[buf][s][l] = cat(to_half4(U[2 * s]), to_half4(U[2 * s + 1]));
+      }
+      // U'' = diag(e^{G_n - G} r_k) U as the bf16 hi + lo B operand of the update
+      bf16x8 bh[2], bl[2];
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const f32x4 ua = U[2 * s] * kdv[2 * s], ub = U[2 * s + 1] * kdv[2 * s + 1];
+        const bf16x4 ha = to_bf16x4(ua), hb = to_bf16x4(ub);
+        bh[s] = cat_bf(ha, hb);
+        bl[s] = cat_bf(to_bf16x4(ua - to_f32x4(ha)), to_bf16x4(ub - to_f32x4(hb)));
+      }
+      load_ukd(nx);
+
+      // ---- S^T <- e^{G_n} S^T + K^T U'' on the owned dk steps
+      const float egn = expf((float)gn);
+#pragma unroll
+      for (int sp = 0; sp < NOWN; ++sp)
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          f32x4 acc = S[sp][tt] * egn;
+#pragma unroll
+          for (int s = 0; s < 2; ++s) {
+            const bf16x8 a = bf16x8_from_u32x4(kf[sp][tt][s]);
+            acc = mma_bf16(a, bh[s], acc);
+            acc = mma_bf16(a, bl[s], acc);
+          }
+          S[sp][tt] = acc;
+        }
+      load_k(nx);
+    }
+    lds_barrier();  // the output waves' last chunk: U of chunk nch - 1 visible
+
+    // ---- write the state back in place
 #pragma unroll
     for (int sp = 0; sp < NOWN; ++sp)
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        f32x4 acc = S[sp][tt] * egn;
+      for (int tt = 0; tt < 2; ++tt)
+        *reinterpret_cast<f32x4*>(Sg + 32 * (hs * NOWN + sp) + 16 * tt + 4 * g) = S[sp][tt];
+  } else {
+    // ======================= output wave =======================
+    // Output wave ow finishes row tiles I = 2 ow and 2 ow + 1 of chunk cl after the
+    // barrier that ends the state waves' chunk cl + 1 prologue, when U of chunk cl is in
+    // LDS: one barrier before the loop and one per chunk, matching the state waves' count.
+    const int ow = wv - DS;
+    u32x4 qf[2][NKS];  // Qh fragments: own row tile, dk step
+    u32x4 af[2][2];    // A_qk fragments: own row tile, token step
+    f32x4 egv[2];      // e^G of rows 16I + 4g + i
+    auto load_q = [&](int cl) {
+      const int64_t pr = pair_of(cl);
+      const _Float16* qb = Qf + ((cbase + cl) * H + h) * (int64_t)(C * DK);
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          const bf16x8 a = bf16x8_from_u32x4(kf[sp][tt][s]);
-          acc = mma_bf16(a, bh[s], acc);
-          acc = mma_bf16(a, bl[s], acc);
+      for (int r = 0; r < 2; ++r) {
+        const int I = 2 * ow + r;
+#pragma unroll
+        for (int sp = 0; sp < NKS; ++sp)
+          qf[r][sp] = *reinterpret_cast<const u32x4*>(qb + ((I * NKS + sp) * 64 + l) * 8);
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+          af[r][s] = *reinterpret_cast<const u32x4*>(Aqk + pr * C * C + ((I * 2 + s) * 64 + l) * 8);
+        egv[r] = *reinterpret_cast<const f32x4*>(egws + pr * C + 16 * I + 4 * g);
+      }
+    };
+    load_q(0);
+    lds_barrier();  // chunk 0 partial sums (state waves)
+    for (int cl = 0; cl < nch; ++cl) {
+      const int buf = cl & 1;
+      const int nx = min(cl + 1, nch - 1);
+      const int64_t t0 = tseq + (int64_t)cl * C;
+      const int n = (int)min((int64_t)C, tend - t0);
+      lds_barrier();  // U of chunk cl visible (S^T copy of chunk cl since the last one)
+      half8 sf[NKS];
+#pragma unroll
+      for (int sp = 0; sp < NKS; ++sp) sf[sp] = sm.s16[cl % 3][sp][l];
+      const half8 uh0 = sm.u16[buf][0][l], uh1 = sm.u16[buf][1][l];
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const int I = 2 * ow + r;
+        f32x4 o1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int sp = 0; sp < NKS; ++sp) o1 = mma_f16(half8_from_u32x4(qf[r][sp]), sf[sp], o1);
+        f32x4 AU = mma_f16(half8_from_u32x4(af[r][0]), uh0, f32x4{0.f, 0.f, 0.f, 0.f});
+        if (I >= 2) AU = mma_f16(half8_from_u32x4(af[r][1]), uh1, AU);
+        const bf16x4 ov = to_bf16x4(egv[r] * o1 + AU);  // round to nearest even
+        __bf16* ob = reinterpret_cast<__bf16*>(out) +
+                     ((t0 + 16 * I + 4 * g) * HV + hv) * (int64_t)DV + 16 * ct + m;
+        if (n == C) {  // full chunk: no per-row test
+#pragma unroll
+          for (int i = 0; i < 4; ++i) ob[i * (int64_t)HV * DV] = ov[i];
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (16 * I + 4 * g + i < n) ob[i * (int64_t)HV * DV] = ov[i];
         }
-        S[sp][tt] = acc;
       }
-    load_k(nx);
-
-    // ---- O for the own row tiles: e^G (Qh S^T) + A_qk U
-#pragma unroll
-    for (int r = 0; r < NOR; ++r) {
-      const int I = hs + DS * r;
-      f32x4 o1 = po[0];  // po[I], selected without indexing registers at run time
-#pragma unroll
-      for (int I2 = 1; I2 < 4; ++I2)
-        if (I2 == I) o1 = po[I2];
-#pragma unroll
-      for (int o = 0; o < DS; ++o)
-        if (o != hs) o1 += sm.partO[buf][o][I][l];
-      f32x4 AU = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < 2; ++s)
-        if (s <= (I >> 1))
-          AU = mma_f16(half8_from_u32x4(af[r][s]),
-                       cat(to_half4(U[2 * s]), to_half4(U[2 * s + 1])), AU);
-      const bf16x4 ov = to_bf16x4(egv[r] * o1 + AU);  // round to nearest even
-      __bf16* ob = reinterpret_cast<__bf16*>(out) +
-                   ((t0 + 16 * I + 4 * g) * HV + hv) * (int64_t)DV + 16 * ct + m;
-      if (n == C) {  // full chunk: no per-row test
-#pragma unroll
-        for (int i = 0; i < 4; ++i) ob[i * (int64_t)HV * DV] = ov[i];
-      } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (16 * I + 4 * g + i < n) ob[i * (int64_t)HV * DV] = ov[i];
-      }
+      load_q(nx);
     }
-    load_out(nx);
   }
-
-  // ---- write the state back in place
-#pragma unroll
-  for (int sp = 0; sp < NOWN; ++sp)
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
-      *reinterpret_cast<f32x4*>(Sg + 32 * (hs * NOWN + sp) + 16 * tt + 4 * g) = S[sp][tt];
 }
 
 template <int DK, int DS>
@@ -288,21 +301,10 @@ hipError_t launch_state_t(const void* qf, const void* kf, const int64_t* cu, con
                           hipStream_t st) {
   const int64_t pairs8 = (s.B * s.HV + 7) / 8;
   const int64_t blocks = pairs8 * 8 * (s.dv / 16);
-  hipLaunchKernelGGL((mfma_state_kernel<DK, DS>), dim3((unsigned)blocks), dim3(64 * DS), 0, st,
-                     (const _Float16*)qf, (const uint16_t*)kf, cu, idx, off, gcum, w, u, kd, aqk,
-                     eg, (int)s.B, s.H, s.HV, s.dv, pool, (uint16_t*)out);
+  hipLaunchKernelGGL((mfma_state_kernel<DK, DS>), dim3((unsigned)blocks), dim3(64 * (DS + NO)),
+                     0, st, (const _Float16*)qf, (const uint16_t*)kf, cu, idx, off, gcum, w, u,
+                     kd, aqk, eg, (int)s.B, s.H, s.HV, s.dv, pool, (uint16_t*)out);
   return hipGetLastError();
-}
-
-// Waves per workgroup (dk split): each wave holds 64 dk (two 32-wide steps) of its 16
-// state rows, or 32 when that is needed to give every SIMD of the 256 compute units a
-// wave (B * HV * dv / 16 workgroups in all). Splitting further costs more in exchanged
-// partial sums than the extra waves win back in hidden latency.
-int choose_ds(const Shape& s) {
-  const int64_t tiles = s.B * s.HV * (s.dv / 16);
-  const int ds = s.dk / 64;
-  if (tiles * ds < 1024 && ds < 4) return 2 * ds;
-  return ds;
 }
 
 }  // namespace
@@ -314,16 +316,15 @@ hipError_t launch_mfma_state(const void* qf, const void* kf, const int64_t* cu_s
                              float* state_pool, void* out, hipStream_t st) {
   const _Float16* W = (const _Float16*)w;
   const _Float16* U = (const _Float16*)u;
-  const int ds = choose_ds(s);
-#define GDN_STATE_CASE(DKv, DSv)                                                              \
-  if (s.dk == DKv && ds == DSv)                                                               \
-    return launch_state_t<DKv, DSv>(qf, kf, cu_seqlens, cache_indices, chunk_off, gcum, W, U,  \
-                                    kd, (const _Float16*)aqk, eg, s, state_pool, out, st);
-  GDN_STATE_CASE(64, 1)
-  GDN_STATE_CASE(64, 2)
-  GDN_STATE_CASE(128, 2)
-  GDN_STATE_CASE(128, 4)
-  GDN_STATE_CASE(256, 4)
+  // Each state wave holds 64 dk (two 32-wide steps) of its 16 state rows.
+#define GDN_STATE_CASE(DKv)                                                                   \
+  if (s.dk == DKv)                                                                            \
+    return launch_state_t<DKv, DKv / 64>(qf, kf, cu_seqlens, cache_indices, chunk_off, gcum,  \
+                                         W, U, kd, (const _Float16*)aqk, eg, s, state_pool,  \
+                                         out, st);
+  GDN_STATE_CASE(64)
+  GDN_STATE_CASE(128)
+  GDN_STATE_CASE(256)
 #undef GDN_STATE_CASE
   return hipErrorInvalidValue;
 }

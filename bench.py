@@ -40,23 +40,24 @@ def path_bytes(p, s_qkv: int) -> float:
 
 def stage_bytes(p, s_qkv: int, s_ws: int, n_chunks: int):
     """Algorithmic bytes each stage must move: its inputs read once, its outputs written
-    once. Rows are chunk rows (n_chunks * C, padding included) for per-chunk data;
-    fragment copies of q and k exist once per (chunk, q/k head)."""
+    once. Rows are chunk rows (n_chunks * C, padding included) for per-chunk data. The
+    decayed keys K~ (fp16) exist once per (chunk, value head), since they carry that head's
+    gates; the normalised q copy (fp16) once per (chunk, q/k head)."""
     C = p.chunk_size
     rows = n_chunks * C
     n_pairs = n_chunks * p.HV
-    qk_frag = n_chunks * p.H * C * p.dk * 2 * 2   # raw k (bf16) + normalised q (fp16)
+    qk_frag = rows * p.HV * p.dk * 2 + rows * p.H * p.dk * 2   # K~ + normalised q
     touched = int(sum(1 for L in (p.cu_seqlens[1:] - p.cu_seqlens[:-1]) if L > 0))
     # gate: a, b in; G (fp64) and beta out
     gate = p.N * p.HV * 8 + rows * p.HV * 12
-    # prep: reads q, k, v, G and beta; writes W<-, U~, the row scales e^{G_n-G} r_k and
-    # e^G, A_qk, and the q/k fragment copies
+    # prep: reads q, k, v, G and beta; writes W<-, U~, the row scale e^G, A_qk, K~ and the
+    # q copy
     prep = (2 * p.N * p.H * p.dk * s_qkv + p.N * p.HV * p.dv * s_qkv + rows * p.HV * 12
-            + rows * p.HV * (p.dk + p.dv) * s_ws + rows * p.HV * 8
+            + rows * p.HV * (p.dk + p.dv) * s_ws + rows * p.HV * 4
             + n_pairs * C * C * s_ws + qk_frag)
-    # state: reads the q/k fragments, W<-, U~, the two row scales, G_n and A_qk; writes o;
-    # reads and writes the fp32 state of every touched slot
-    state = (qk_frag + rows * p.HV * (p.dk + p.dv) * s_ws + rows * p.HV * 8 + n_pairs * 8
+    # state: reads K~, the q copy, W<-, U~, e^G, G_n and A_qk; writes o; reads and writes
+    # the fp32 state of every touched slot
+    state = (qk_frag + rows * p.HV * (p.dk + p.dv) * s_ws + rows * p.HV * 4 + n_pairs * 8
              + n_pairs * C * C * s_ws + p.N * p.HV * p.dv * s_qkv
              + touched * p.HV * p.dv * p.dk * 8)
     return {"gate": gate, "chunk_prep": prep, "state": state}

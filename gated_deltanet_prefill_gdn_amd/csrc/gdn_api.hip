@@ -33,14 +33,12 @@ WsLayout layout_for(const Shape& s, Path p) {
   off = align256(off + el * mc * s.HV * s.C * s.dk);
   L.u = off;
   off = align256(off + el * mc * s.HV * s.C * s.dv);
-  L.kd = off;
-  if (p == Path::kMfma) off = align256(off + sizeof(float) * mc * s.HV * s.C);
   L.aqk = off;
   if (p == Path::kMfma) off = align256(off + 2 * mc * s.HV * s.C * s.C);
   L.eg = off;
   if (p == Path::kMfma) off = align256(off + sizeof(float) * mc * s.HV * s.C);
   L.kf = off;
-  if (p == Path::kMfma) off = align256(off + 2 * mc * s.H * s.C * s.dk);
+  if (p == Path::kMfma) off = align256(off + 2 * mc * s.HV * s.C * s.dk);
   L.qf = off;
   if (p == Path::kMfma) off = align256(off + 2 * mc * s.H * s.C * s.dk);
   L.total = off;
@@ -150,17 +148,16 @@ gdn_status_t run_prefill(const void* q, const void* k, const void* v, const floa
   void* w = ws + L.w;
   void* u = ws + L.u;
   if (path == Path::kMfma) {
-    float* kd = (float*)(ws + L.kd);
     void* aqk = ws + L.aqk;
     float* eg = (float*)(ws + L.eg);
     void* kf = ws + L.kf;
     void* qf = ws + L.qf;
     if (launch_mfma_prep(q, k, v, cu_seqlens, chunk_off, chunk_seq, gcum, beta, s,
-                         L.max_chunks, w, u, kd, aqk, eg, kf, qf, st) != hipSuccess)
+                         L.max_chunks, w, u, aqk, eg, kf, qf, st) != hipSuccess)
       return GDN_ERR_HIP;
     if (!mark(2)) return GDN_ERR_HIP;
-    if (launch_mfma_state(qf, kf, cu_seqlens, cache_indices, chunk_off, gcum, w, u, kd, aqk, eg,
-                          s, state_pool, out, st) != hipSuccess)
+    if (launch_mfma_state(qf, kf, cu_seqlens, cache_indices, chunk_off, gcum, w, u, aqk, eg, s,
+                          state_pool, out, st) != hipSuccess)
       return GDN_ERR_HIP;
   } else {
     if (launch_ref_prep(k, v, cu_seqlens, chunk_off, chunk_seq, gcum, beta, s, L.max_chunks,

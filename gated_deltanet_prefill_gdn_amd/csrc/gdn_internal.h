@@ -27,11 +27,10 @@ struct WsLayout {
   size_t w = 0;            // W<- [max_chunks][HV][C][dk] (fp32 on kRef, fp16 on kMfma)
   size_t u = 0;            // U~  [max_chunks][HV][C][dv] (fp32 on kRef; fp16 MFMA D tiles on
                            //     kMfma)
-  size_t kd = 0;           // float  [max_chunks][HV][C]: e^{G_n - G} / |k| per chunk row (kMfma only)
   size_t aqk = 0;          // fp16   [max_chunks][HV][C][C]: A_qk in fragment order (kMfma only)
   size_t eg = 0;           // float  [max_chunks][HV][C]: e^G per chunk row (kMfma only)
-  size_t kf = 0;           // bf16   [max_chunks][H][C][dk]: raw k in the state update's
-                           //        fragment order (kMfma only)
+  size_t kf = 0;           // fp16   [max_chunks][HV][C][dk]: K~ = diag(e^{G_n - G} r_k) K in
+                           //        the state update's fragment order (kMfma only)
   size_t qf = 0;           // fp16   [max_chunks][H][C][dk]: normalised q in the state
                            //        pass's fragment order (kMfma only)
   size_t total = 0;
@@ -66,12 +65,12 @@ hipError_t launch_ref_state(const void* q, const void* k, const int64_t* cu_seql
 hipError_t launch_mfma_prep(const void* q, const void* k, const void* v,
                             const int64_t* cu_seqlens, const int32_t* chunk_off,
                             const int32_t* chunk_seq, const double* gcum, const float* beta,
-                            const Shape& s, int64_t max_chunks, void* w, void* u, float* kd,
-                            void* aqk, float* eg, void* kf, void* qf, hipStream_t st);
+                            const Shape& s, int64_t max_chunks, void* w, void* u, void* aqk,
+                            float* eg, void* kf, void* qf, hipStream_t st);
 hipError_t launch_mfma_state(const void* qf, const void* kf, const int64_t* cu_seqlens,
                              const int64_t* cache_indices, const int32_t* chunk_off,
-                             const double* gcum, const void* w, const void* u, const float* kd,
-                             const void* aqk, const float* eg, const Shape& s,
-                             float* state_pool, void* out, hipStream_t st);
+                             const double* gcum, const void* w, const void* u, const void* aqk,
+                             const float* eg, const Shape& s, float* state_pool, void* out,
+                             hipStream_t st);
 
 }  // namespace gdn

@@ -12,7 +12,9 @@
 //          N^-1 = G M^-1 G^-1 of the Save-one-invert section, taken entry by entry
 //   A_qk = Gamma o tril0(diag(r_q) Q K^T diag(r_k))       the intra-chunk read with the
 //          causal mask that includes the diagonal (pymllm gdn_chunkwise page, Algorithm)
-// plus the row scales e^G and e^{G_n - G} r_k that the state pass applies.
+//   K~   = diag(e^{G_n - G} r_k) K                      the keys of the state update,
+//          decayed to the chunk end (same Reminder, K decorated with the right arrow)
+// plus the row scale e^G that the state pass applies to the read of the state.
 //
 // Work split: the chunk's K and Q rows are staged in LDS with row-contiguous loads (a
 // fragment load straight from global memory would touch 16 rows per instruction, which
@@ -24,16 +26,16 @@
 // only tiles another wave needs pass through LDS. Every wave keeps the transposed tiles
 // T_wJ^T of its own rows, which are exactly the operand fragments of its rows of W<- and
 // U~. The token contractions read column fragments of K and V with the LDS transpose
-// read. Four barriers after staging. For the state pass the kernel also writes raw k
-// (bf16) and normalised q (fp16) in that kernel's operand-fragment order, once per q/k
-// head.
+// read. Four barriers after staging. For the state pass the kernel also writes K~ (fp16,
+// per value head, since the gates are) and normalised q (fp16, once per q/k head) in
+// that kernel's operand-fragment order.
 //
 // Fragment notation: Dl(X) is the MFMA result layout of a 16 x 16 tile X, lane
 // l = 16 g + m holding X[4g + i][m], i = 0..3. A product P Q takes Dl(P^T) as its A
 // operand and Dl(Q) as its B operand (for 16x16x4 fp32 with k = 4g + s at step s; for
 // 16x16x32, two stacked tiles in kperm order). T1 = diag(e^G) T diag(beta r_k) and
 // T2 = (Gamma o T) diag(beta) are split into bf16 hi + lo so the bf16 products with the
-// exact raw K and V keep fp32 accuracy. W<-, U~ and A_qk are stored as fp16 in the
+// exact raw K and V keep fp32 accuracy. W<-, U~, A_qk and K~ are stored as fp16 in the
 // fragment layouts the state kernel loads directly into registers.
 #include <algorithm>
 
@@ -182,8 +184,8 @@ __global__ __launch_bounds__(256) void mfma_prep_kernel(
     const int64_t* __restrict__ cu, const int32_t* __restrict__ chunk_off,
     const int32_t* __restrict__ chunk_seq, const double* __restrict__ gcum,
     const float* __restrict__ beta, int H, int HV, int64_t max_chunks, _Float16* __restrict__ Wout,
-    _Float16* __restrict__ Uout, float* __restrict__ kd_out, _Float16* __restrict__ Aout,
-    float* __restrict__ eg_out, uint16_t* __restrict__ Kout, _Float16* __restrict__ Qout) {
+    _Float16* __restrict__ Uout, _Float16* __restrict__ Aout, float* __restrict__ eg_out,
+    _Float16* __restrict__ Kout, _Float16* __restrict__ Qout) {
   constexpr int NKS = DK / 32;
   using Sm = PrepSmem<DK, DV>;
   constexpr int SK = Sm::SK, SQV = Sm::SQV;
@@ -275,9 +277,8 @@ __global__ __launch_bounds__(256) void mfma_prep_kernel(
     const float rqt = 1.0f / sqrtf(sum_sq<DK>(qf) + kNormEps);
     if (g == 0) sm.rk[t] = rkt;
 
-    // ---- q and k in the state pass's operand order, once per q/k head:
-    // Q fragment (I, sp): rows 16I + m of diag(r_q) Q in fp16, columns 32sp + kperm(g, .);
-    // K fragment f = (sp * 2 + tt) * 2 + s: K^T rows 32sp + 16tt + m, tokens 32s + kperm(g, .)
+    // ---- q in the state pass's operand order, once per q/k head: fragment (I, sp) holds
+    // rows 16I + m of diag(r_q) Q in fp16, columns 32sp + kperm(g, .)
     if (hv % (HV / H) == 0) {
       const int64_t fo = (c * H + h) * (int64_t)(C * DK);
   #pragma unroll
@@ -290,12 +291,6 @@ __global__ __launch_bounds__(256) void mfma_prep_kernel(
           y[2 * j + 1] = (_Float16)(bf_hi(x[j]) * rqt);
         }
         *reinterpret_cast<half8*>(Qout + fo + ((w * NKS + sp) * 64 + l) * 8) = y;
-      }
-  #pragma unroll
-      for (int f = w; f < NKS * 4; f += 4) {
-        const int sp = f >> 2, tt = (f >> 1) & 1, s = f & 1;
-        *reinterpret_cast<u32x4*>(Kout + fo + (f * 64 + l) * 8) =
-            col_frag_tr(sm.ks, SK, 32 * sp + 16 * tt, s, g, m);
       }
     }
 
@@ -327,14 +322,38 @@ __global__ __launch_bounds__(256) void mfma_prep_kernel(
     store_tile_rows<DV>(sm.qv, SQV, vreg, tid);
     if (has_next) load_vg(nx);
 
+    // ---- K~ = diag(e^{G_n - G} r_k) K in fp16, in the state update's operand order:
+    // fragment f = (sp * 2 + tt) * 2 + s holds K~^T rows 32sp + 16tt + m, tokens
+    // 32s + kperm(g, .). Wave w writes the fragments f = w (mod 4), whose token step is
+    // s = w & 1.
+    {
+      const int s = w & 1;
+      float kdj[8];
+  #pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int tk = 32 * s + kperm(g, j);
+        kdj[j] = __builtin_amdgcn_exp2f((float)(sm.G2[C - 1] - sm.G2[tk])) * sm.rk[tk];
+      }
+      _Float16* kb = Kout + pair * (int64_t)(C * DK);
+  #pragma unroll
+      for (int f = w; f < NKS * 4; f += 4) {
+        const int sp = f >> 2, tt = (f >> 1) & 1;
+        const u32x4 x = col_frag_tr(sm.ks, SK, 32 * sp + 16 * tt, s, g, m);
+        half8 y;
+  #pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          y[2 * j] = (_Float16)(bf_lo(x[j]) * kdj[2 * j]);
+          y[2 * j + 1] = (_Float16)(bf_hi(x[j]) * kdj[2 * j + 1]);
+        }
+        *reinterpret_cast<half8*>(kb + (f * 64 + l) * 8) = y;
+      }
+    }
+
     // ---- scale: a[J] = Dl(A_wJ^T) (A[t][i], i = 16J + 4g + ii < t) and the A_qk rows
     const double G2t = sm.G2[t];
     const float btt = sm.bt[t];
     const float egt = __builtin_amdgcn_exp2f((float)G2t);
-    if (g == 0) {
-      eg_out[pair * C + t] = egt;
-      kd_out[pair * C + t] = __builtin_amdgcn_exp2f((float)(sm.G2[C - 1] - G2t)) * rkt;
-    }
+    if (g == 0) eg_out[pair * C + t] = egt;
     f32x4 a[4];
     half4 aq[4];
   #pragma unroll
@@ -487,8 +506,8 @@ template <int DK, int DV>
 hipError_t launch_prep_t(const void* q, const void* k, const void* v, const int64_t* cu,
                          const int32_t* off, const int32_t* cseq, const double* gcum,
                          const float* beta, const Shape& s, int64_t max_chunks, _Float16* w,
-                         _Float16* u, float* kd, _Float16* aqk, float* eg, uint16_t* kf,
-                         _Float16* qf, hipStream_t st) {
+                         _Float16* u, _Float16* aqk, float* eg, _Float16* kf, _Float16* qf,
+                         hipStream_t st) {
   // Persistent grid: as many workgroups as fit on the device at once.
   int dev = 0, cus = 0, per_cu = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
@@ -500,7 +519,7 @@ hipError_t launch_prep_t(const void* q, const void* k, const void* v, const int6
   const int64_t grid = std::min<int64_t>(items, (int64_t)std::max(cus, 1) * std::max(per_cu, 1));
   hipLaunchKernelGGL((mfma_prep_kernel<DK, DV>), dim3((unsigned)grid), dim3(256), 0, st,
                      (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, cu, off, cseq,
-                     gcum, beta, s.H, s.HV, max_chunks, w, u, kd, aqk, eg, kf, qf);
+                     gcum, beta, s.H, s.HV, max_chunks, w, u, aqk, eg, kf, qf);
   return hipGetLastError();
 }
 
@@ -509,14 +528,14 @@ hipError_t launch_prep_t(const void* q, const void* k, const void* v, const int6
 hipError_t launch_mfma_prep(const void* q, const void* k, const void* v,
                             const int64_t* cu_seqlens, const int32_t* chunk_off,
                             const int32_t* chunk_seq, const double* gcum, const float* beta,
-                            const Shape& s, int64_t max_chunks, void* w, void* u, float* kd,
-                            void* aqk, float* eg, void* kf, void* qf, hipStream_t st) {
+                            const Shape& s, int64_t max_chunks, void* w, void* u, void* aqk,
+                            float* eg, void* kf, void* qf, hipStream_t st) {
   _Float16* W = (_Float16*)w;
   _Float16* U = (_Float16*)u;
 #define GDN_PREP_CASE(DKv, DVv)                                                               \
   if (s.dk == DKv && s.dv == DVv)                                                             \
     return launch_prep_t<DKv, DVv>(q, k, v, cu_seqlens, chunk_off, chunk_seq, gcum, beta, s,  \
-                                   max_chunks, W, U, kd, (_Float16*)aqk, eg, (uint16_t*)kf,  \
+                                   max_chunks, W, U, (_Float16*)aqk, eg, (_Float16*)kf,      \
                                    (_Float16*)qf, st);
   GDN_PREP_CASE(64, 64)
   GDN_PREP_CASE(64, 128)

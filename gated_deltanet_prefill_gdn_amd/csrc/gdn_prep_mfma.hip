@@ -36,7 +36,9 @@
 // 16x16x32, two stacked tiles in kperm order). T1 = diag(e^G) T diag(beta r_k) and
 // T2 = (Gamma o T) diag(beta) are split into bf16 hi + lo so the bf16 products with the
 // exact raw K and V keep fp32 accuracy. W<-, U~, A_qk and K~ are stored as fp16 in the
-// fragment layouts the state kernel loads directly into registers.
+// fragment layouts the state kernel loads directly into registers. These stores are
+// non-temporal: the blocks are read once, by the state pass, and left as dirty lines in the
+// caches they slowed that pass's reads by about 15% (measured).
 #include <algorithm>
 
 #include "gdn_internal.h"
@@ -138,6 +140,15 @@ __device__ __forceinline__ u32x4 col_frag_tr(const uint16_t* base, int ld, int c
   return r;
 }
 
+// A copy of a lane index that the compiler cannot treat as loop-invariant. Per-lane
+// predicates built from it are recomputed where they are used (one compare each) instead
+// of being hoisted out of the item loop as 64-bit lane masks, which exhaust the scalar
+// registers and spill.
+__device__ __forceinline__ int opaque(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
 __device__ __forceinline__ float bf_lo(uint32_t x) { return __uint_as_float(x << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t x) { return __uint_as_float(x & 0xFFFF0000u); }
 
@@ -183,7 +194,7 @@ __global__ __launch_bounds__(256) void mfma_prep_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const int64_t* __restrict__ cu, const int32_t* __restrict__ chunk_off,
     const int32_t* __restrict__ chunk_seq, const double* __restrict__ gcum,
-    const float* __restrict__ beta, int H, int HV, int64_t max_chunks, _Float16* __restrict__ Wout,
+    const float* __restrict__ beta, int B, int H, int HV, _Float16* __restrict__ Wout,
     _Float16* __restrict__ Uout, _Float16* __restrict__ Aout, float* __restrict__ eg_out,
     _Float16* __restrict__ Kout, _Float16* __restrict__ Qout) {
   constexpr int NKS = DK / 32;
@@ -196,21 +207,21 @@ __global__ __launch_bounds__(256) void mfma_prep_kernel(
   constexpr int KP = C * DK / 8 / 256;  // 16-byte pieces per thread of a K or Q tile
   constexpr int VP = C * DV / 8 / 256;  // ... of a V tile
 
-  // Persistent: workgroups stride over the (chunk, value head) items. The next item's
-  // rows are loaded into registers while the current one is processed.
+  // Persistent: workgroups stride over the (chunk, value head) items of the chunk_off[B]
+  // real chunks. The next item's rows are loaded into registers while the current one is
+  // processed; the loads are unconditional (the last item reloads itself), so no register
+  // set is merged or copied at the loop back edge.
   struct Item {
     int hv, h, n;
     int64_t c, t0;
   };
-  auto geom = [&](int64_t it, Item& x) -> bool {
+  auto geom = [&](int64_t it, Item& x) {
     x.c = it / HV;
     x.hv = (int)(it % HV);
     x.h = x.hv / (HV / H);
     const int32_t sq = chunk_seq[x.c];
-    if (sq < 0) return false;
     x.t0 = cu[sq] + (int64_t)(x.c - chunk_off[sq]) * C;
     x.n = (int)min((int64_t)C, cu[sq + 1] - x.t0);
-    return true;
   };
   u32x4 kreg[KP], qreg[KP], vreg[VP];
   double greg = 0.0;
@@ -226,25 +237,15 @@ __global__ __launch_bounds__(256) void mfma_prep_kernel(
       breg = beta[(x.c * HV + x.hv) * C + tid];
     }
   };
-  const int64_t n_items = max_chunks * HV;
-  {
-    Item x0;
-    if (blockIdx.x < n_items && geom(blockIdx.x, x0)) {
-      load_kq(x0);
-      load_vg(x0);
-    }
-  }
+  const int64_t n_items = (int64_t)chunk_off[B] * HV;
+  if ((int64_t)blockIdx.x >= n_items) return;
+  Item cur;
+  geom(blockIdx.x, cur);
+  load_kq(cur);
+  load_vg(cur);
   for (int64_t it = blockIdx.x; it < n_items; it += gridDim.x) {
-    Item cur, nx;
-    const bool valid = geom(it, cur);
-    const bool has_next = it + gridDim.x < n_items && geom(it + gridDim.x, nx);
-    if (!valid) {  // padding chunk: just move the prefetch on
-      if (has_next) {
-        load_kq(nx);
-        load_vg(nx);
-      }
-      continue;
-    }
+    Item nx;
+    geom(it + gridDim.x < n_items ? it + gridDim.x : it, nx);
     const int hv = cur.hv, h = cur.h, n = cur.n;
     const int64_t c = cur.c, t0 = cur.t0;
     const int64_t pair = c * HV + hv;
@@ -257,7 +258,7 @@ __global__ __launch_bounds__(256) void mfma_prep_kernel(
       sm.bt[tid] = breg;
     }
     lds_barrier();  // (0) K, Q staged
-    if (has_next) load_kq(nx);
+    load_kq(nx);
 
     // ---- operand fragments of the own rows and of the earlier tiles; norms
     u32x4 kw[NKS], qf[NKS];
@@ -290,7 +291,7 @@ __global__ __launch_bounds__(256) void mfma_prep_kernel(
           y[2 * j] = (_Float16)(bf_lo(x[j]) * rqt);
           y[2 * j + 1] = (_Float16)(bf_hi(x[j]) * rqt);
         }
-        *reinterpret_cast<half8*>(Qout + fo + ((w * NKS + sp) * 64 + l) * 8) = y;
+        __builtin_nontemporal_store(y, reinterpret_cast<half8*>(Qout + fo + ((w * NKS + sp) * 64 + l) * 8));
       }
     }
 
@@ -320,7 +321,7 @@ __global__ __launch_bounds__(256) void mfma_prep_kernel(
 
     // ---- V rows into the Q region (every wave is done with Q); visible after (2)
     store_tile_rows<DV>(sm.qv, SQV, vreg, tid);
-    if (has_next) load_vg(nx);
+    load_vg(nx);
 
     // ---- K~ = diag(e^{G_n - G} r_k) K in fp16, in the state update's operand order:
     // fragment f = (sp * 2 + tt) * 2 + s holds K~^T rows 32sp + 16tt + m, tokens
@@ -345,7 +346,7 @@ __global__ __launch_bounds__(256) void mfma_prep_kernel(
           y[2 * j] = (_Float16)(bf_lo(x[j]) * kdj[2 * j]);
           y[2 * j + 1] = (_Float16)(bf_hi(x[j]) * kdj[2 * j + 1]);
         }
-        *reinterpret_cast<half8*>(kb + (f * 64 + l) * 8) = y;
+        __builtin_nontemporal_store(y, reinterpret_cast<half8*>(kb + (f * 64 + l) * 8));
       }
     }
 
@@ -356,24 +357,29 @@ __global__ __launch_bounds__(256) void mfma_prep_kernel(
     if (g == 0) eg_out[pair * C + t] = egt;
     f32x4 a[4];
     half4 aq[4];
+    // Tiles J < w lie wholly below the diagonal and J > w wholly above it (uniform
+    // branches); only the diagonal tile J = w needs the per-element tests i < t, i <= t.
+    const int dm = opaque(m) - 4 * g;  // i < t  <=>  ii < dm on the diagonal tile
   #pragma unroll
     for (int J = 0; J < 4; ++J) {
-      f32x4 x;
+      f32x4 x = {0.f, 0.f, 0.f, 0.f};
+      a[J] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (J <= w) {
   #pragma unroll
-      for (int ii = 0; ii < 4; ++ii) {
-        const int i = 16 * J + 4 * g + ii;
-        const float rki = sm.rk[i];
-        a[J][ii] = (J <= w && i < t) ? btt * rkt * rki * D[J][ii] : 0.f;
-        x[ii] = (J <= w && i <= t)
-                    ? __builtin_amdgcn_exp2f((float)(G2t - sm.G2[i])) * rqt * rki * E[J][ii]
-                    : 0.f;
+        for (int ii = 0; ii < 4; ++ii) {
+          const int i = 16 * J + 4 * g + ii;
+          const float rki = sm.rk[i];
+          const float av = btt * rkt * rki * D[J][ii];
+          const float xv = __builtin_amdgcn_exp2f((float)(G2t - sm.G2[i])) * rqt * rki * E[J][ii];
+          a[J][ii] = (J < w || ii < dm) ? av : 0.f;
+          x[ii] = (J < w || ii <= dm) ? xv : 0.f;
+        }
       }
       aq[J] = to_half4(x);
     }
   #pragma unroll
     for (int s = 0; s < 2; ++s)
-      *reinterpret_cast<half8*>(Aout + pair * C * C + ((w * 2 + s) * 64 + l) * 8) =
-          cat(aq[2 * s], aq[2 * s + 1]);
+      __builtin_nontemporal_store(cat(aq[2 * s], aq[2 * s + 1]), reinterpret_cast<half8*>(Aout + pair * C * C + ((w * 2 + s) * 64 + l) * 8));
 
     // ---- diagonal tile: T_ww = (I + A_ww)^-1 by forward substitution, lane = column m
     float* sqw = sm.sq[w];
@@ -384,12 +390,13 @@ __global__ __launch_bounds__(256) void mfma_prep_kernel(
     *reinterpret_cast<f32x4*>(&sqw[m * SA + 4 * g]) = aw;  // row m of A_ww, columns 4g..
     __builtin_amdgcn_wave_barrier();
     float x[16];
+    const int mo = opaque(m);
   #pragma unroll
     for (int r = 0; r < 16; ++r) {
       float acc = 0.f;
   #pragma unroll
       for (int i = 0; i < r; ++i) acc += sqw[r * SA + i] * x[i];
-      x[r] = (r < m) ? 0.f : ((r == m) ? 1.f : -acc);
+      x[r] = (r < mo) ? 0.f : ((r == mo) ? 1.f : -acc);
     }
     __builtin_amdgcn_wave_barrier();
     if (g == 0) {
@@ -399,12 +406,13 @@ __global__ __launch_bounds__(256) void mfma_prep_kernel(
     __builtin_amdgcn_wave_barrier();
     const f32x4 tww_t = *reinterpret_cast<const f32x4*>(&sqw[m * SA + 4 * g]);  // Dl(T_ww^T)
     f32x4 tww;                                                                  // Dl(T_ww)
+    const int go = opaque(g);
   #pragma unroll
     for (int i = 0; i < 4; ++i) {
       float y = x[i];
   #pragma unroll
       for (int gg = 1; gg < 4; ++gg)
-        if (g == gg) y = x[4 * gg + i];
+        if (go == gg) y = x[4 * gg + i];
       tww[i] = y;
     }
     sm.tex[tex_slot(w, w)][l] = tww;
@@ -443,17 +451,21 @@ __global__ __launch_bounds__(256) void mfma_prep_kernel(
 
     // ---- T1^T, T2^T fragments of the own rows (bf16 hi + lo), tiles J <= w
     bf16x4 t1h[4], t1l[4], t2h[4], t2l[4];
+    const int dm2 = opaque(m) - 4 * g;  // i <= t  <=>  ii <= dm2 on the diagonal tile
   #pragma unroll
     for (int J = 0; J < 4; ++J) {
-      f32x4 x1, x2;
+      f32x4 x1 = {0.f, 0.f, 0.f, 0.f}, x2 = {0.f, 0.f, 0.f, 0.f};
+      if (J <= w) {  // T[t][i] = 0 on the tiles above the diagonal
   #pragma unroll
-      for (int ii = 0; ii < 4; ++ii) {
-        const int i = 16 * J + 4 * g + ii;
-        const float tv = ttr[J][ii];  // T[t][i], zero for i > t
-        const float bti = sm.bt[i];
-        x1[ii] = egt * tv * bti * sm.rk[i];
-        // e^{G_t - G_i} overflows for i > t under strong decay: mask, do not multiply by 0
-        x2[ii] = (i <= t) ? __builtin_amdgcn_exp2f((float)(G2t - sm.G2[i])) * tv * bti : 0.f;
+        for (int ii = 0; ii < 4; ++ii) {
+          const int i = 16 * J + 4 * g + ii;
+          const float tv = ttr[J][ii];  // T[t][i], zero for i > t
+          const float bti = sm.bt[i];
+          x1[ii] = egt * tv * bti * sm.rk[i];
+          // e^{G_t - G_i} overflows for i > t under strong decay: mask, do not multiply by 0
+          const float ev = __builtin_amdgcn_exp2f((float)(G2t - sm.G2[i])) * tv * bti;
+          x2[ii] = (J < w || ii <= dm2) ? ev : 0.f;
+        }
       }
       t1h[J] = to_bf16x4(x1);
       t1l[J] = to_bf16x4(x1 - to_f32x4(t1h[J]));
@@ -478,8 +490,7 @@ __global__ __launch_bounds__(256) void mfma_prep_kernel(
           }
         }
       }
-      *reinterpret_cast<half8*>(Wout + pair * C * DK + ((w * NKS + sp) * 64 + l) * 8) =
-          cat(to_half4(acc[0]), to_half4(acc[1]));
+      __builtin_nontemporal_store(cat(to_half4(acc[0]), to_half4(acc[1])), reinterpret_cast<half8*>(Wout + pair * C * DK + ((w * NKS + sp) * 64 + l) * 8));
     }
 
     // ---- U~ = T2 V for the own rows: D tiles (rows 16w.., dv 16cc..), each stored as one
@@ -495,10 +506,10 @@ __global__ __launch_bounds__(256) void mfma_prep_kernel(
           acc = mma_bf16(cat_bf(t2l[2 * s], t2l[2 * s + 1]), vb, acc);
         }
       }
-      *reinterpret_cast<half4*>(Uout + pair * C * DV + ((cc * 4 + w) * 64 + l) * 4) =
-          to_half4(acc);
+      __builtin_nontemporal_store(to_half4(acc), reinterpret_cast<half4*>(Uout + pair * C * DV + ((cc * 4 + w) * 64 + l) * 4));
     }
     lds_barrier();  // (5) every LDS region is free for the next item
+    cur = nx;
   }
 }
 
@@ -519,7 +530,7 @@ hipError_t launch_prep_t(const void* q, const void* k, const void* v, const int6
   const int64_t grid = std::min<int64_t>(items, (int64_t)std::max(cus, 1) * std::max(per_cu, 1));
   hipLaunchKernelGGL((mfma_prep_kernel<DK, DV>), dim3((unsigned)grid), dim3(256), 0, st,
                      (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, cu, off, cseq,
-                     gcum, beta, s.H, s.HV, max_chunks, w, u, aqk, eg, kf, qf);
+                     gcum, beta, (int)s.B, s.H, s.HV, w, u, aqk, eg, kf, qf);
   return hipGetLastError();
 }
 

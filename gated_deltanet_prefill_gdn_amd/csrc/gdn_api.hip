@@ -25,10 +25,10 @@ WsLayout layout_for(const Shape& s, Path p) {
   off = align256(off + sizeof(int32_t) * (size_t)(s.B + 1));
   L.chunk_seq = off;
   off = align256(off + sizeof(int32_t) * mc);
-  L.gcum = off;
-  off = align256(off + sizeof(double) * mc * s.HV * s.C);
+  L.gcum = off;  // the MFMA chunk prep computes its gates itself
+  if (p == Path::kRef) off = align256(off + sizeof(double) * mc * s.HV * s.C);
   L.beta = off;
-  off = align256(off + sizeof(float) * mc * s.HV * s.C);
+  if (p == Path::kRef) off = align256(off + sizeof(float) * mc * s.HV * s.C);
   L.w = off;
   off = align256(off + el * mc * s.HV * s.C * s.dk);
   L.u = off;
@@ -141,7 +141,8 @@ gdn_status_t run_prefill(const void* q, const void* k, const void* v, const floa
   if (!mark(0)) return GDN_ERR_HIP;
   if (launch_plan(cu_seqlens, s, chunk_off, chunk_seq, L.max_chunks, st) != hipSuccess)
     return GDN_ERR_HIP;
-  if (launch_gate(a, b, A_log, dt_bias, cu_seqlens, chunk_off, chunk_seq, s, L.max_chunks, gcum,
+  if (path == Path::kRef &&
+      launch_gate(a, b, A_log, dt_bias, cu_seqlens, chunk_off, chunk_seq, s, L.max_chunks, gcum,
                   beta, st) != hipSuccess)
     return GDN_ERR_HIP;
   if (!mark(1)) return GDN_ERR_HIP;
@@ -152,11 +153,11 @@ gdn_status_t run_prefill(const void* q, const void* k, const void* v, const floa
     float* eg = (float*)(ws + L.eg);
     void* kf = ws + L.kf;
     void* qf = ws + L.qf;
-    if (launch_mfma_prep(q, k, v, cu_seqlens, chunk_off, chunk_seq, gcum, beta, s,
+    if (launch_mfma_prep(q, k, v, cu_seqlens, chunk_off, chunk_seq, a, b, A_log, dt_bias, s,
                          L.max_chunks, w, u, aqk, eg, kf, qf, st) != hipSuccess)
       return GDN_ERR_HIP;
     if (!mark(2)) return GDN_ERR_HIP;
-    if (launch_mfma_state(qf, kf, cu_seqlens, cache_indices, chunk_off, gcum, w, u, aqk, eg, s,
+    if (launch_mfma_state(qf, kf, cu_seqlens, cache_indices, chunk_off, w, u, aqk, eg, s,
                           state_pool, out, st) != hipSuccess)
       return GDN_ERR_HIP;
   } else {

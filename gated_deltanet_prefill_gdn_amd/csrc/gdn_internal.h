@@ -23,7 +23,8 @@ struct WsLayout {
   size_t chunk_off = 0;    // int32 [B + 1]: first global chunk of each request
   size_t chunk_seq = 0;    // int32 [max_chunks]: request of each global chunk, -1 if unused
   size_t gcum = 0;         // double [max_chunks][HV][C]: chunk-local inclusive sum of log(alpha)
-  size_t beta = 0;         // float  [max_chunks][HV][C]: beta (0 on padding rows)
+                           //        (kRef only: the MFMA chunk prep forms its own gates)
+  size_t beta = 0;         // float  [max_chunks][HV][C]: beta (0 on padding rows) (kRef only)
   size_t w = 0;            // W<- [max_chunks][HV][C][dk] (fp32 on kRef, fp16 on kMfma)
   size_t u = 0;            // U~  [max_chunks][HV][C][dv] (fp32 on kRef; fp16 MFMA D tiles on
                            //     kMfma)
@@ -64,12 +65,13 @@ hipError_t launch_ref_state(const void* q, const void* k, const int64_t* cu_seql
 
 hipError_t launch_mfma_prep(const void* q, const void* k, const void* v,
                             const int64_t* cu_seqlens, const int32_t* chunk_off,
-                            const int32_t* chunk_seq, const double* gcum, const float* beta,
-                            const Shape& s, int64_t max_chunks, void* w, void* u, void* aqk,
-                            float* eg, void* kf, void* qf, hipStream_t st);
+                            const int32_t* chunk_seq, const float* a, const float* b,
+                            const float* A_log, const float* dt_bias, const Shape& s,
+                            int64_t max_chunks, void* w, void* u, void* aqk, float* eg, void* kf,
+                            void* qf, hipStream_t st);
 hipError_t launch_mfma_state(const void* qf, const void* kf, const int64_t* cu_seqlens,
                              const int64_t* cache_indices, const int32_t* chunk_off,
-                             const double* gcum, const void* w, const void* u, const void* aqk,
+                             const void* w, const void* u, const void* aqk,
                              const float* eg, const Shape& s, float* state_pool, void* out,
                              hipStream_t st);
 

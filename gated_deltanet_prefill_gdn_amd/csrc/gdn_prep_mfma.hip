@@ -62,8 +62,9 @@ struct PrepSmem {
   uint16_t qv[C * SQV];   // Q rows, later V rows
   f32x4 tex[9][64];       // Dl(T_IJ) tiles that other waves read: diagonal, distance 1, 2
   float sq[4][16 * SA];   // per-wave scratch: A_ww, then the columns of T_ww
-  double G2[C];           // G log2(e)
-  float bt[C], rk[C];     // beta, r_k
+  double G2[2][C];        // G log2(e), by item parity
+  float bt[2][C];         // beta, by item parity
+  float rk[C];            // r_k
 };
 
 // LDS slot of an exchanged tile T_IJ (I - J <= 2).
@@ -190,11 +191,12 @@ __device__ __forceinline__ bf16x8 cat_bf(bf16x4 a, bf16x4 b) {
 }
 
 template <int DK, int DV>
-__global__ __launch_bounds__(256) void mfma_prep_kernel(
+__global__ __launch_bounds__(256, (DK + DV <= 256) ? 2 : 1) void mfma_prep_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const int64_t* __restrict__ cu, const int32_t* __restrict__ chunk_off,
-    const int32_t* __restrict__ chunk_seq, const double* __restrict__ gcum,
-    const float* __restrict__ beta, int B, int H, int HV, _Float16* __restrict__ Wout,
+    const int32_t* __restrict__ chunk_seq, const float* __restrict__ ga,
+    const float* __restrict__ gb, const float* __restrict__ A_log,
+    const float* __restrict__ dt_bias, int B, int H, int HV, _Float16* __restrict__ Wout,
     _Float16* __restrict__ Uout, _Float16* __restrict__ Aout, float* __restrict__ eg_out,
     _Float16* __restrict__ Kout, _Float16* __restrict__ Qout) {
   constexpr int NKS = DK / 32;
@@ -224,8 +226,7 @@ __global__ __launch_bounds__(256) void mfma_prep_kernel(
     x.n = (int)min((int64_t)C, cu[sq + 1] - x.t0);
   };
   u32x4 kreg[KP], qreg[KP], vreg[VP];
-  double greg = 0.0;
-  float breg = 0.f;
+  float areg, breg;  // raw gate inputs a, b of chunk row tid % C
   auto load_kq = [&](const Item& x) {
     load_tile_rows<DK>(kreg, k + (x.t0 * H + x.h) * (int64_t)DK, rsk, x.n, tid);
     load_tile_rows<DK>(qreg, q + (x.t0 * H + x.h) * (int64_t)DK, rsk, x.n, tid);
@@ -233,9 +234,33 @@ __global__ __launch_bounds__(256) void mfma_prep_kernel(
   auto load_vg = [&](const Item& x) {
     load_tile_rows<DV>(vreg, v + (x.t0 * HV + x.hv) * (int64_t)DV, (int64_t)HV * DV, x.n, tid);
     if (tid < C) {
-      greg = gcum[(x.c * HV + x.hv) * C + tid];
-      breg = beta[(x.c * HV + x.hv) * C + tid];
+      // rows past the request's end read its last token (in bounds) and are zeroed later
+      const int64_t tr = x.t0 + min(tid & (C - 1), x.n - 1);
+      areg = ga[tr * HV + x.hv];
+      breg = gb[tr * HV + x.hv];
     }
+  };
+  // Gates of item x (wave 0, one lane per row, from that item's prefetched a and b):
+  // g = log(alpha) = -exp(A_log) softplus(a + dt_bias), beta = sigmoid(b); zero on padding
+  // rows (alpha = 1, beta = 0). G = the chunk-local inclusive sum of g, in fp64. Wave 0
+  // forms the next item's gates at the end of the current one, where it waits for the
+  // waves with more triangular work anyway; the two LDS copies alternate by item parity.
+  auto gates = [&](const Item& x, int buf) {
+    float gt = 0.f, bt = 0.f;
+    if (tid < x.n) {
+      const float xg = areg + dt_bias[x.hv];
+      const float sp = fmaxf(xg, 0.f) + log1pf(expf(-fabsf(xg)));
+      gt = -expf(A_log[x.hv]) * sp;
+      bt = 1.f / (1.f + expf(-breg));
+    }
+    double G = (double)gt;
+  #pragma unroll
+    for (int off = 1; off < C; off <<= 1) {
+      const double y = __shfl_up(G, off, C);
+      if (tid >= off) G += y;
+    }
+    sm.G2[buf][tid] = G * kLog2e;
+    sm.bt[buf][tid] = bt;
   };
   const int64_t n_items = (int64_t)chunk_off[B] * HV;
   if ((int64_t)blockIdx.x >= n_items) return;
@@ -243,21 +268,21 @@ __global__ __launch_bounds__(256) void mfma_prep_kernel(
   geom(blockIdx.x, cur);
   load_kq(cur);
   load_vg(cur);
-  for (int64_t it = blockIdx.x; it < n_items; it += gridDim.x) {
+  if (tid < C) gates(cur, 0);
+  int ib = 0;  // item parity: this item's gate copy
+  for (int64_t it = blockIdx.x; it < n_items; it += gridDim.x, ib ^= 1) {
     Item nx;
     geom(it + gridDim.x < n_items ? it + gridDim.x : it, nx);
     const int hv = cur.hv, h = cur.h, n = cur.n;
     const int64_t c = cur.c, t0 = cur.t0;
     const int64_t pair = c * HV + hv;
 
-    // ---- stage K and Q rows in LDS from the prefetch registers; gates (wave 0)
+    // ---- stage K and Q rows in LDS from the prefetch registers
     store_tile_rows<DK>(sm.ks, SK, kreg, tid);
     store_tile_rows<DK>(sm.qv, SQV, qreg, tid);
-    if (tid < C) {
-      sm.G2[tid] = greg * kLog2e;
-      sm.bt[tid] = breg;
-    }
-    lds_barrier();  // (0) K, Q staged
+    const double* G2 = sm.G2[ib];
+    const float* bts = sm.bt[ib];
+    lds_barrier();  // (0) K, Q staged (and this item's gates)
     load_kq(nx);
 
     // ---- operand fragments of the own rows and of the earlier tiles; norms
@@ -333,7 +358,7 @@ __global__ __launch_bounds__(256) void mfma_prep_kernel(
   #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int tk = 32 * s + kperm(g, j);
-        kdj[j] = __builtin_amdgcn_exp2f((float)(sm.G2[C - 1] - sm.G2[tk])) * sm.rk[tk];
+        kdj[j] = __builtin_amdgcn_exp2f((float)(G2[C - 1] - G2[tk])) * sm.rk[tk];
       }
       _Float16* kb = Kout + pair * (int64_t)(C * DK);
   #pragma unroll
@@ -351,8 +376,8 @@ __global__ __launch_bounds__(256) void mfma_prep_kernel(
     }
 
     // ---- scale: a[J] = Dl(A_wJ^T) (A[t][i], i = 16J + 4g + ii < t) and the A_qk rows
-    const double G2t = sm.G2[t];
-    const float btt = sm.bt[t];
+    const double G2t = G2[t];
+    const float btt = bts[t];
     const float egt = __builtin_amdgcn_exp2f((float)G2t);
     if (g == 0) eg_out[pair * C + t] = egt;
     f32x4 a[4];
@@ -370,7 +395,7 @@ __global__ __launch_bounds__(256) void mfma_prep_kernel(
           const int i = 16 * J + 4 * g + ii;
           const float rki = sm.rk[i];
           const float av = btt * rkt * rki * D[J][ii];
-          const float xv = __builtin_amdgcn_exp2f((float)(G2t - sm.G2[i])) * rqt * rki * E[J][ii];
+          const float xv = __builtin_amdgcn_exp2f((float)(G2t - G2[i])) * rqt * rki * E[J][ii];
           a[J][ii] = (J < w || ii < dm) ? av : 0.f;
           x[ii] = (J < w || ii <= dm) ? xv : 0.f;
         }
@@ -460,10 +485,10 @@ __global__ __launch_bounds__(256) void mfma_prep_kernel(
         for (int ii = 0; ii < 4; ++ii) {
           const int i = 16 * J + 4 * g + ii;
           const float tv = ttr[J][ii];  // T[t][i], zero for i > t
-          const float bti = sm.bt[i];
+          const float bti = bts[i];
           x1[ii] = egt * tv * bti * sm.rk[i];
           // e^{G_t - G_i} overflows for i > t under strong decay: mask, do not multiply by 0
-          const float ev = __builtin_amdgcn_exp2f((float)(G2t - sm.G2[i])) * tv * bti;
+          const float ev = __builtin_amdgcn_exp2f((float)(G2t - G2[i])) * tv * bti;
           x2[ii] = (J < w || ii <= dm2) ? ev : 0.f;
         }
       }
@@ -508,6 +533,7 @@ __global__ __launch_bounds__(256) void mfma_prep_kernel(
       }
       __builtin_nontemporal_store(to_half4(acc), reinterpret_cast<half4*>(Uout + pair * C * DV + ((cc * 4 + w) * 64 + l) * 4));
     }
+    if (tid < C) gates(nx, ib ^ 1);  // wave 0: the next item's gates
     lds_barrier();  // (5) every LDS region is free for the next item
     cur = nx;
   }
@@ -515,8 +541,9 @@ __global__ __launch_bounds__(256) void mfma_prep_kernel(
 
 template <int DK, int DV>
 hipError_t launch_prep_t(const void* q, const void* k, const void* v, const int64_t* cu,
-                         const int32_t* off, const int32_t* cseq, const double* gcum,
-                         const float* beta, const Shape& s, int64_t max_chunks, _Float16* w,
+                         const int32_t* off, const int32_t* cseq, const float* ga,
+                         const float* gb, const float* A_log, const float* dt_bias,
+                         const Shape& s, int64_t max_chunks, _Float16* w,
                          _Float16* u, _Float16* aqk, float* eg, _Float16* kf, _Float16* qf,
                          hipStream_t st) {
   // Persistent grid: as many workgroups as fit on the device at once.
@@ -530,7 +557,7 @@ hipError_t launch_prep_t(const void* q, const void* k, const void* v, const int6
   const int64_t grid = std::min<int64_t>(items, (int64_t)std::max(cus, 1) * std::max(per_cu, 1));
   hipLaunchKernelGGL((mfma_prep_kernel<DK, DV>), dim3((unsigned)grid), dim3(256), 0, st,
                      (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, cu, off, cseq,
-                     gcum, beta, (int)s.B, s.H, s.HV, w, u, aqk, eg, kf, qf);
+                     ga, gb, A_log, dt_bias, (int)s.B, s.H, s.HV, w, u, aqk, eg, kf, qf);
   return hipGetLastError();
 }
 
@@ -538,14 +565,16 @@ hipError_t launch_prep_t(const void* q, const void* k, const void* v, const int6
 
 hipError_t launch_mfma_prep(const void* q, const void* k, const void* v,
                             const int64_t* cu_seqlens, const int32_t* chunk_off,
-                            const int32_t* chunk_seq, const double* gcum, const float* beta,
+                            const int32_t* chunk_seq, const float* a, const float* b,
+                            const float* A_log, const float* dt_bias,
                             const Shape& s, int64_t max_chunks, void* w, void* u, void* aqk,
                             float* eg, void* kf, void* qf, hipStream_t st) {
   _Float16* W = (_Float16*)w;
   _Float16* U = (_Float16*)u;
 #define GDN_PREP_CASE(DKv, DVv)                                                               \
   if (s.dk == DKv && s.dv == DVv)                                                             \
-    return launch_prep_t<DKv, DVv>(q, k, v, cu_seqlens, chunk_off, chunk_seq, gcum, beta, s,  \
+    return launch_prep_t<DKv, DVv>(q, k, v, cu_seqlens, chunk_off, chunk_seq, a, b, A_log,    \
+                                   dt_bias, s,                                                 \
                                    max_chunks, W, U, (_Float16*)aqk, eg, (_Float16*)kf,      \
                                    (_Float16*)qf, st);
   GDN_PREP_CASE(64, 64)

@@ -62,8 +62,7 @@ template <int DK, int NC, int PD>
 __global__ __launch_bounds__(64 * (2 + NO)) void mfma_state_kernel(
     const _Float16* __restrict__ Qf, const _Float16* __restrict__ Kf,
     const int64_t* __restrict__ cu, const int64_t* __restrict__ cache_indices,
-    const int32_t* __restrict__ chunk_off, const double* __restrict__ gcum,
-    const _Float16* __restrict__ W, const _Float16* __restrict__ Ut,
+    const int32_t* __restrict__ chunk_off, const _Float16* __restrict__ W, const _Float16* __restrict__ Ut,
     const _Float16* __restrict__ Aqk, const float* __restrict__ egws, int B, int H, int HV,
     int DV, float* __restrict__ state_pool, uint16_t* __restrict__ out) {
   constexpr int NKS = DK / 32;    // 32-wide dk steps
@@ -112,7 +111,7 @@ __global__ __launch_bounds__(64 * (2 + NO)) void mfma_state_kernel(
       u32x4 wfo[2][NOWN], wfx[2][NOWN];  // W<- fragments, row tiles 2hs + r: own / other dk
       u32x2 uf[NC][2];                   // U~ D tiles: column tile, own row tile
       u32x4 kf[NOWN][2][2];  // K~^T fragments: own dk step, 16-row half, own/other tokens
-      double gn;             // G_n (the gate pass pads G with zero log-decay)
+      float egn;             // e^{G_n}: e^G of the chunk's last row (padding rows do not decay)
     };
     auto load_wu = [&](Regs& R, int cl) {
       const int64_t pr = pair_of(cl);
@@ -145,7 +144,7 @@ __global__ __launch_bounds__(64 * (2 + NO)) void mfma_state_kernel(
           R.kf[sp][tt][0] = *reinterpret_cast<const u32x4*>(kb + ((f + hs) * 64 + l) * 8);
           R.kf[sp][tt][1] = *reinterpret_cast<const u32x4*>(kb + ((f + ho) * 64 + l) * 8);
         }
-      R.gn = gcum[pr * C + C - 1];
+      R.egn = egws[pr * C + C - 1];
     };
 
     // A step with cl >= nch (the loop runs in groups of PD) leaves S unchanged: U = 0
@@ -164,7 +163,7 @@ __global__ __launch_bounds__(64 * (2 + NO)) void mfma_state_kernel(
           so[c][sp] = cat(to_half4(S[c][sp][0]), to_half4(S[c][sp][1]));
           sm.s16[b][c][hs * NOWN + sp][l] = so[c][sp];
         }
-      const float egn = live ? expf((float)R.gn) : 1.0f;
+      const float egn = live ? R.egn : 1.0f;
 #pragma unroll
       for (int c = 0; c < NC; ++c)
 #pragma unroll
@@ -313,13 +312,13 @@ __global__ __launch_bounds__(64 * (2 + NO)) void mfma_state_kernel(
 
 template <int DK, int NC, int PD>
 hipError_t launch_state_t(const void* qf, const void* kf, const int64_t* cu, const int64_t* idx,
-                          const int32_t* off, const double* gcum, const _Float16* w,
+                          const int32_t* off, const _Float16* w,
                           const _Float16* u, const _Float16* aqk, const float* eg, const Shape& s,
                           float* pool, void* out, hipStream_t st) {
   const int64_t pairs8 = (s.B * s.HV + 7) / 8;
   const int64_t blocks = pairs8 * 8 * (s.dv / (16 * NC));
   hipLaunchKernelGGL((mfma_state_kernel<DK, NC, PD>), dim3((unsigned)blocks), dim3(64 * (2 + NO)), 0,
-                     st, (const _Float16*)qf, (const _Float16*)kf, cu, idx, off, gcum, w, u, aqk,
+                     st, (const _Float16*)qf, (const _Float16*)kf, cu, idx, off, w, u, aqk,
                      eg, (int)s.B, s.H, s.HV, s.dv, pool, (uint16_t*)out);
   return hipGetLastError();
 }
@@ -328,7 +327,7 @@ hipError_t launch_state_t(const void* qf, const void* kf, const int64_t* cu, con
 
 hipError_t launch_mfma_state(const void* qf, const void* kf, const int64_t* cu_seqlens,
                              const int64_t* cache_indices, const int32_t* chunk_off,
-                             const double* gcum, const void* w, const void* u, const void* aqk,
+                             const void* w, const void* u, const void* aqk,
                              const float* eg, const Shape& s, float* state_pool, void* out,
                              hipStream_t st) {
   const _Float16* W = (const _Float16*)w;
@@ -337,8 +336,8 @@ hipError_t launch_mfma_state(const void* qf, const void* kf, const int64_t* cu_s
   // two chunks ahead, one at dk = 256, where two register sets would not fit.
 #define GDN_STATE_CASE(DKv, PDv)                                                               \
   if (s.dk == DKv)                                                                             \
-    return launch_state_t<DKv, 2, PDv>(qf, kf, cu_seqlens, cache_indices, chunk_off, gcum, W, \
-                                       U, (const _Float16*)aqk, eg, s, state_pool, out, st);
+    return launch_state_t<DKv, 2, PDv>(qf, kf, cu_seqlens, cache_indices, chunk_off, W, U,    \
+                                       (const _Float16*)aqk, eg, s, state_pool, out, st);
   GDN_STATE_CASE(64, 2)
   GDN_STATE_CASE(128, 2)
   GDN_STATE_CASE(256, 1)

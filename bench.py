@@ -20,6 +20,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000  # hipEventDisableSystemFence
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # dense
 WORKLOAD_INDEX = 1
 METRIC = "GDN prefill tokens/sec + effective TFLOPs (% MFMA/HBM roof), dk=dv=128 C=64"
@@ -94,16 +95,19 @@ class Hip:
 
     def __init__(self):
         self.lib = ctypes.CDLL("libamdhip64.so.7")
-        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p),
+                                                     ctypes.c_uint]
         self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
                                                  ctypes.c_void_p]
         self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
 
     def event(self):
+        # Timing-only events: without the system-scope fence (cache write-back and
+        # invalidate) that a default event record inserts between the kernels it separates.
         e = ctypes.c_void_p()
-        rc = self.lib.hipEventCreate(ctypes.byref(e))
+        rc = self.lib.hipEventCreateWithFlags(ctypes.byref(e), HIP_EVENT_DISABLE_SYSTEM_FENCE)
         if rc != 0:
-            raise RuntimeError(f"hipEventCreate failed: {rc}")
+            raise RuntimeError(f"hipEventCreateWithFlags failed: {rc}")
         return e.value
 
     def elapsed_ms(self, a, b) -> float:
@@ -189,14 +193,21 @@ def main():
 
     hip = Hip()
     nst = gdn.GDN_NUM_STAGES
-    evs = [[hip.event() for _ in range(nst + 1)] for _ in range(args.steps)]
+    # The K timed steps: plain calls, nothing recorded between them.
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(evs[i])
+        step()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
+    # The same K steps again with HIP events on the launch stream around every stage:
+    # per-kernel launch durations for the roofline.
+    evs = [[hip.event() for _ in range(nst + 1)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
     stage_ms = {name: float(np.mean([hip.elapsed_ms(e[j], e[j + 1]) for e in evs]))
                 for j, name in enumerate(gdn.STAGE_NAMES)}
     call_ms = float(np.mean([hip.elapsed_ms(e[0], e[nst]) for e in evs]))

@@ -17,19 +17,23 @@ namespace gdn {
 namespace {
 
 constexpr int kPlanThreads = 1024;
+constexpr int kPlanLds = 4096;  // chunk_off entries kept in LDS for the request search
 
 // One workgroup: chunk_off[b] = sum_{b' < b} ceil(L_b' / C), chunk_off[B] = total,
 // then chunk_seq[c] = the request that owns global chunk c (or -1 past the total).
+// The scan runs per wavefront with shuffles, then across the 16 wavefronts; the search
+// for each chunk's request reads an LDS copy of chunk_off when it fits.
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int64_t* __restrict__ cu,
                                                             int64_t B, int C,
                                                             int32_t* __restrict__ chunk_off,
                                                             int32_t* __restrict__ chunk_seq,
                                                             int64_t max_chunks) {
-  __shared__ int32_t s_scan[kPlanThreads];
-  __shared__ int32_t s_carry;
-  const int tid = threadIdx.x;
-  if (tid == 0) s_carry = 0;
-  __syncthreads();
+  constexpr int NW = kPlanThreads / 64;
+  __shared__ int32_t s_wsum[NW];
+  __shared__ int32_t s_off[kPlanLds];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const bool in_lds = B + 1 <= kPlanLds;
+  int32_t carry = 0;
   for (int64_t base = 0; base < B; base += kPlanThreads) {
     const int64_t bi = base + tid;
     int32_t n = 0;
@@ -37,23 +41,35 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int64_t* __res
       const int64_t L = cu[bi + 1] - cu[bi];
       n = L > 0 ? (int32_t)((L + C - 1) / C) : 0;
     }
-    s_scan[tid] = n;
-    __syncthreads();
-    for (int off = 1; off < kPlanThreads; off <<= 1) {  // inclusive Hillis-Steele scan
-      const int32_t x = tid >= off ? s_scan[tid - off] : 0;
-      __syncthreads();
-      s_scan[tid] += x;
-      __syncthreads();
+    int32_t x = n;  // inclusive scan within the wavefront
+    for (int off = 1; off < 64; off <<= 1) {
+      const int32_t y = __shfl_up(x, off, 64);
+      if (lane >= off) x += y;
     }
-    const int32_t carry = s_carry;
-    const int32_t incl = s_scan[tid];
-    if (bi < B) chunk_off[bi] = carry + incl - n;
+    if (lane == 63) s_wsum[wv] = x;
     __syncthreads();
-    if (tid == kPlanThreads - 1) s_carry = carry + incl;
+    if (wv == 0) {  // inclusive scan of the wavefront totals
+      int32_t ws = lane < NW ? s_wsum[lane] : 0;
+      for (int off = 1; off < NW; off <<= 1) {
+        const int32_t y = __shfl_up(ws, off, 64);
+        if (lane >= off) ws += y;
+      }
+      if (lane < NW) s_wsum[lane] = ws;
+    }
     __syncthreads();
+    const int32_t excl = carry + (wv > 0 ? s_wsum[wv - 1] : 0) + x - n;
+    if (bi < B) {
+      chunk_off[bi] = excl;
+      if (in_lds) s_off[bi] = excl;
+    }
+    carry += s_wsum[NW - 1];
+    __syncthreads();  // s_wsum is rewritten by the next block of requests
   }
-  const int32_t total = s_carry;
-  if (tid == 0) chunk_off[B] = total;
+  const int32_t total = carry;
+  if (tid == 0) {
+    chunk_off[B] = total;
+    if (in_lds) s_off[B] = total;
+  }
   __threadfence_block();
   __syncthreads();
   for (int64_t c = tid; c < max_chunks; c += kPlanThreads) {
@@ -62,7 +78,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int64_t* __res
       int64_t lo = 0, hi = B;  // chunk_off[lo] <= c < chunk_off[hi]
       while (hi - lo > 1) {
         const int64_t mid = (lo + hi) >> 1;
-        if (chunk_off[mid] <= c) lo = mid; else hi = mid;
+        const int32_t om = in_lds ? s_off[mid] : chunk_off[mid];
+        if (om <= c) lo = mid; else hi = mid;
       }
       seq = (int32_t)lo;
     }

@@ -78,6 +78,20 @@ def test_many_short_requests():
     compare(p, out, pool, oracle.prefill(p))
 
 
+@pytest.mark.parametrize("nreq", [1500, 5000])
+def test_thousands_of_requests(nreq):
+    """More requests than one pass of the chunk-table scan (1024 per pass); at 5000 the
+    chunk-to-request search also runs on the global table instead of its LDS copy.
+    Lengths 0..80 give empty, partial, one- and two-chunk requests."""
+    rng = np.random.default_rng(41 + nreq)
+    lengths = list(rng.integers(0, 81, nreq))
+    p = gdn_synth.make_problem(41 + nreq, lengths, 1, 1, 64, 64, dtype="bf16", pool=nreq + 7,
+                               cache_indices=list(rng.permutation(nreq + 7)[:nreq]),
+                               state_std=0.5)
+    out, pool, _ = run_gpu(p, f"requests-{nreq}")
+    compare(p, out, pool, oracle.prefill(p))
+
+
 def test_all_requests_empty_is_a_no_op():
     import torch
     p = gdn_synth.make_problem(35, [0, 0, 0], 1, 1, 64, 64, dtype="bf16", state_std=1.0)

@@ -12,7 +12,7 @@
 // on no state). Chunks of a request are processed in order (pymllm page: the propagation
 // between chunks remains sequential over ceil(T/C) steps).
 //
-// Work split: one workgroup per (request, value head, NC x 16 state rows), with two
+// Work split: one workgroup per (request, value head, NC x 16 state rows), with three
 // roles.
 //   * Two state waves. Wave hs holds dk rows hs * DK/2 .. of the NC x 16 columns of S^T
 //     in fp32 registers for the whole request, and forms P = W<- S^T and U for tokens
@@ -23,7 +23,11 @@
 //     U copies.
 //   * NO output waves form O from those LDS copies off the state chain: Qh S^T between
 //     the two barriers, A_qk U after the second. They compute O^T (operands swapped), so
-//     each lane holds four consecutive columns of one token row and stores 8 bytes.
+//     each lane holds four consecutive columns of one token row, and write O in bf16 to
+//     a double-buffered output tile in LDS.
+//   * One store wave copies each finished tile to out with row-contiguous 16-byte
+//     stores, so that no wave that waits for its prefetched operands has stores queued
+//     among its loads (a wave's loads and stores retire in order).
 // Every operand comes straight from global memory into MFMA operand registers, in the
 // fragment orders the prep kernel wrote (one contiguous 1 KiB piece per fragment). Two
 // register sets (one at dk = 256) alternate between chunks, each reloaded right after its
@@ -32,6 +36,8 @@
 // Matrix-core operands, all fp16 with fp32 accumulation: W<- and S for P; normalised q
 // and S for Qh S^T; K~ and U for the update; A_qk and U for A_qk U. The state itself
 // stays fp32; P starts from -U~ in the accumulator so U needs no separate subtraction.
+#include <type_traits>
+
 #include "gdn_internal.h"
 #include "gdn_mfma.h"
 
@@ -45,8 +51,12 @@ constexpr int NRO = 4 / NO;  // row tiles per output wave
 
 template <int NKS, int NC>
 struct StateSmem {
+  // Row stride (bf16) of the output tile: 16 bytes of padding spread the rows that the
+  // 8-byte writes of one wave touch evenly over the banks.
+  static constexpr int SO = 16 * NC + 8;
   half8 s16[2][NC][NKS][64];  // fp16 S^T fragments: chunk parity, column tile, dk step
   half8 u16[2][NC][2][64];    // fp16 U fragments: chunk parity, column tile, token step
+  uint16_t o16[2][C][SO];     // bf16 rows of O (16 NC columns): chunk parity, token
 };
 
 __device__ __forceinline__ bf16x4 to_bf16x4(f32x4 x) {
@@ -58,8 +68,13 @@ __device__ __forceinline__ bf16x4 to_bf16x4(f32x4 x) {
   return h;
 }
 
+// Store waves: one up to dk = 128. At dk = 256 the state and output waves need more than
+// half of a SIMD's registers, so they keep a SIMD each and store O themselves.
+template <int DK>
+constexpr int kStoreWaves = DK <= 128 ? 1 : 0;
+
 template <int DK, int NC, int PD>
-__global__ __launch_bounds__(64 * (2 + NO)) void mfma_state_kernel(
+__global__ __launch_bounds__(64 * (2 + NO + kStoreWaves<DK>)) void mfma_state_kernel(
     const _Float16* __restrict__ Qf, const _Float16* __restrict__ Kf,
     const int64_t* __restrict__ cu, const int64_t* __restrict__ cache_indices,
     const int32_t* __restrict__ chunk_off, const _Float16* __restrict__ W, const _Float16* __restrict__ Ut,
@@ -225,6 +240,8 @@ __global__ __launch_bounds__(64 * (2 + NO)) void mfma_state_kernel(
       for (int j = 0; j < PD; ++j) step(rs[j], cl + j);
     }
 
+    lds_barrier();  // (F) the store wave reads the last chunk's O
+
     // ---- write the state back in place
 #pragma unroll
     for (int c = 0; c < NC; ++c)
@@ -234,79 +251,130 @@ __global__ __launch_bounds__(64 * (2 + NO)) void mfma_state_kernel(
         for (int tt = 0; tt < 2; ++tt)
           *reinterpret_cast<f32x4*>(Sg + c * 16 * DK + 32 * (hs * NOWN + sp) + 16 * tt + 4 * g) =
               S[c][sp][tt];
-  } else {
+  } else if (wv < 2 + NO) {
     // ======================= output wave =======================
     // Output wave ow finishes row tiles I = NRO ow .. NRO ow + NRO - 1 of every column
     // tile: Qh S^T after barrier (A) of chunk cl, A_qk U after barrier (B). Computed as
-    // O^T = S Qh^T + U^T A_qk^T: lane (g, m) holds row 16 I + m, columns 4g .. 4g + 3.
-    const int ow = wv - 2;
-    struct Regs {
-      u32x4 qf[NRO][NKS];  // Qh fragments: own row tile, dk step
-      u32x4 af[NRO][2];    // A_qk fragments: own row tile, token step
-      float egr[NRO];      // e^G of row 16 I + m
-    };
-    auto load_q = [&](Regs& R, int cl) {
-      const int64_t pr = pair_of(cl);
-      const _Float16* qb = Qf + ((cbase + cl) * H + h) * (int64_t)(C * DK);
-#pragma unroll
-      for (int r = 0; r < NRO; ++r) {
-        const int I = NRO * ow + r;
-#pragma unroll
-        for (int sp = 0; sp < NKS; ++sp)
-          R.qf[r][sp] = *reinterpret_cast<const u32x4*>(qb + ((I * NKS + sp) * 64 + l) * 8);
-#pragma unroll
-        for (int s = 0; s < 2; ++s)
-          R.af[r][s] =
-              *reinterpret_cast<const u32x4*>(Aqk + pr * C * C + ((I * 2 + s) * 64 + l) * 8);
-        R.egr[r] = egws[pr * C + 16 * I + m];
-      }
-    };
-    auto step = [&](Regs& R, int cl) {  // cl >= nch: n <= 0, nothing is stored
-      const int b = cl & 1;
-      const int nx = min(cl + PD, nch - 1);
-      const int64_t t0 = tseq + (int64_t)cl * C;
-      const int n = (int)min((int64_t)C, tend - t0);
-      lds_barrier();  // (A) S^T copies of chunk cl visible
-      f32x4 o1[NRO][NC];
-#pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        half8 sf[NKS];
-#pragma unroll
-        for (int sp = 0; sp < NKS; ++sp) sf[sp] = sm.s16[b][c][sp][l];
+    // O^T = S Qh^T + U^T A_qk^T: lane (g, m) holds row 16 I + m, columns 4g .. 4g + 3,
+    // which it writes as bf16 to the chunk's output tile in LDS. The row tiles are
+    // compile-time constants of each wave's code, so the causal skip of A_qk's upper
+    // token step is static.
+    auto run = [&](auto OWc) {
+      constexpr int ow = decltype(OWc)::value;
+      struct Regs {
+        u32x4 qf[NRO][NKS];  // Qh fragments: own row tile, dk step
+        u32x4 af[NRO][2];    // A_qk fragments: own row tile, token step
+        float egr[NRO];      // e^G of row 16 I + m
+      };
+      auto load_q = [&](Regs& R, int cl) {
+        const int64_t pr = pair_of(cl);
+        const _Float16* qb = Qf + ((cbase + cl) * H + h) * (int64_t)(C * DK);
 #pragma unroll
         for (int r = 0; r < NRO; ++r) {
-          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+          constexpr int I0 = NRO * ow;
+          const int I = I0 + r;
 #pragma unroll
           for (int sp = 0; sp < NKS; ++sp)
-            acc = mma_f16(sf[sp], half8_from_u32x4(R.qf[r][sp]), acc);
-          o1[r][c] = acc;
-        }
-      }
-      lds_barrier();  // (B) U of chunk cl visible
+            R.qf[r][sp] = *reinterpret_cast<const u32x4*>(qb + ((I * NKS + sp) * 64 + l) * 8);
 #pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        const half8 uh0 = sm.u16[b][c][0][l], uh1 = sm.u16[b][c][1][l];
-#pragma unroll
-        for (int r = 0; r < NRO; ++r) {
-          const int I = NRO * ow + r;
-          f32x4 au = mma_f16(uh0, half8_from_u32x4(R.af[r][0]), f32x4{0.f, 0.f, 0.f, 0.f});
-          if (I >= 2) au = mma_f16(uh1, half8_from_u32x4(R.af[r][1]), au);
-          const bf16x4 ov = to_bf16x4(R.egr[r] * o1[r][c] + au);  // round to nearest even
-          if (16 * I + m < n)
-            *reinterpret_cast<bf16x4*>(reinterpret_cast<__bf16*>(out) +
-                                       ((t0 + 16 * I + m) * HV + hv) * (int64_t)DV +
-                                       16 * (ct0 + c) + 4 * g) = ov;
+          for (int s = 0; s < 2; ++s)
+            if (s == 0 || I >= 2)
+              R.af[r][s] =
+                  *reinterpret_cast<const u32x4*>(Aqk + pr * C * C + ((I * 2 + s) * 64 + l) * 8);
+          R.egr[r] = egws[pr * C + 16 * I + m];
         }
+      };
+      auto step = [&](Regs& R, int cl) {
+        const int b = cl & 1;
+        const int nx = min(cl + PD, nch - 1);
+        lds_barrier();  // (A) S^T copies of chunk cl visible
+        f32x4 o1[NRO][NC];
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+          half8 sf[NKS];
+#pragma unroll
+          for (int sp = 0; sp < NKS; ++sp) sf[sp] = sm.s16[b][c][sp][l];
+#pragma unroll
+          for (int r = 0; r < NRO; ++r) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int sp = 0; sp < NKS; ++sp)
+              acc = mma_f16(sf[sp], half8_from_u32x4(R.qf[r][sp]), acc);
+            o1[r][c] = acc;
+          }
+        }
+        lds_barrier();  // (B) U of chunk cl visible
+        f32x4 au[NRO][NC];
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+          const half8 uh0 = sm.u16[b][c][0][l], uh1 = sm.u16[b][c][1][l];
+#pragma unroll
+          for (int r = 0; r < NRO; ++r) {
+            const int I = NRO * ow + r;
+            au[r][c] = mma_f16(uh0, half8_from_u32x4(R.af[r][0]), f32x4{0.f, 0.f, 0.f, 0.f});
+            if (I >= 2) au[r][c] = mma_f16(uh1, half8_from_u32x4(R.af[r][1]), au[r][c]);
+          }
+        }
+        const int64_t t0 = tseq + (int64_t)cl * C;
+        const int n = (int)min((int64_t)C, tend - t0);  // cl >= nch: n <= 0
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+#pragma unroll
+          for (int r = 0; r < NRO; ++r) {
+            const int I = NRO * ow + r;
+            const bf16x4 ov = to_bf16x4(R.egr[r] * o1[r][c] + au[r][c]);  // nearest even
+            if constexpr (kStoreWaves<DK> > 0) {
+              *reinterpret_cast<bf16x4*>(&sm.o16[b][16 * I + m][16 * c + 4 * g]) = ov;
+            } else if (16 * I + m < n) {
+              *reinterpret_cast<bf16x4*>(reinterpret_cast<__bf16*>(out) +
+                                         ((t0 + 16 * I + m) * HV + hv) * (int64_t)DV +
+                                         16 * (ct0 + c) + 4 * g) = ov;
+            }
+          }
+        load_q(R, nx);
+      };
+      Regs rs[PD];
+#pragma unroll
+      for (int j = 0; j < PD; ++j) load_q(rs[j], min(j, nch - 1));
+      for (int cl = 0; cl < nch; cl += PD) {
+#pragma unroll
+        for (int j = 0; j < PD; ++j) step(rs[j], cl + j);
       }
-      load_q(R, nx);
+      lds_barrier();  // (F)
     };
-    Regs rs[PD];
+    static_assert(NO == 2, "one code copy per output wave");
+    if (wv == 2)
+      run(std::integral_constant<int, 0>{});
+    else
+      run(std::integral_constant<int, 1>{});
+  } else if constexpr (kStoreWaves<DK> > 0) {
+    // ======================= store wave =======================
+    // Copies each chunk's output tile from LDS to out once it is complete (after barrier
+    // (A) of the next chunk, or the final barrier), 16 bytes per lane, so that one store
+    // instruction writes whole 32 NC-byte row pieces. Only this wave writes global memory
+    // inside the chunk loop: the loads and stores of a wave retire in order, and stores
+    // among the other waves' prefetches would make their load waits wait for the stores.
+    const int ns = (nch + PD - 1) / PD * PD;  // chunk steps of the other waves
+    constexpr int PR = NC * 16 / 8;           // 16-byte pieces per row
+    auto store_o = [&](int cl) {              // cl >= nch: n <= 0, nothing is stored
+      const int64_t t0 = tseq + (int64_t)cl * C;
+      const int n = (int)min((int64_t)C, tend - t0);
+      const int b = cl & 1;
+      __bf16* ob = reinterpret_cast<__bf16*>(out) + (t0 * HV + hv) * (int64_t)DV + 16 * ct0;
 #pragma unroll
-    for (int j = 0; j < PD; ++j) load_q(rs[j], min(j, nch - 1));
-    for (int cl = 0; cl < nch; cl += PD) {
-#pragma unroll
-      for (int j = 0; j < PD; ++j) step(rs[j], cl + j);
+      for (int i = 0; i < C * PR / 64; ++i) {
+        const int r = (64 * i + l) / PR, pc = l % PR;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(&sm.o16[b][r][8 * pc]);
+        if (r < n) *reinterpret_cast<u32x4*>(ob + (int64_t)r * HV * DV + 8 * pc) = v;
+      }
+    };
+    for (int cl = 0; cl < ns; ++cl) {
+      lds_barrier();  // (A) of chunk cl: the tile of chunk cl - 1 is complete
+      if (cl > 0) store_o(cl - 1);
+      lds_barrier();  // (B)
     }
+    lds_barrier();  // (F)
+    store_o(ns - 1);
   }
 }
 
@@ -317,7 +385,7 @@ hipError_t launch_state_t(const void* qf, const void* kf, const int64_t* cu, con
                           float* pool, void* out, hipStream_t st) {
   const int64_t pairs8 = (s.B * s.HV + 7) / 8;
   const int64_t blocks = pairs8 * 8 * (s.dv / (16 * NC));
-  hipLaunchKernelGGL((mfma_state_kernel<DK, NC, PD>), dim3((unsigned)blocks), dim3(64 * (2 + NO)), 0,
+  hipLaunchKernelGGL((mfma_state_kernel<DK, NC, PD>), dim3((unsigned)blocks), dim3(64 * (2 + NO + kStoreWaves<DK>)), 0,
                      st, (const _Float16*)qf, (const _Float16*)kf, cu, idx, off, w, u, aqk,
                      eg, (int)s.B, s.H, s.HV, s.dv, pool, (uint16_t*)out);
   return hipGetLastError();

@@ -237,8 +237,9 @@ __global__ __launch_bounds__(256, (DK + DV <= 256) ? 3 : 1) void mfma_prep_kerne
   auto load_vg = [&](const Item& x) {
     load_tile_rows<DV>(vreg, v + (x.t0 * HV + x.hv) * (int64_t)DV, (int64_t)HV * DV, x.n, tid);
     if (tid < C) {
-      // rows past the request's end read its last token (in bounds) and are zeroed later
-      const int64_t tr = x.t0 + min(tid & (C - 1), x.n - 1);
+      // rows past the request's end read its last token (in bounds) and are zeroed later;
+      // the empty item after a workgroup's last one reads its first row
+      const int64_t tr = x.t0 + min(tid & (C - 1), max(x.n - 1, 0));
       areg = ga[tr * HV + x.hv];
       breg = gb[tr * HV + x.hv];
     }
@@ -274,8 +275,11 @@ __global__ __launch_bounds__(256, (DK + DV <= 256) ? 3 : 1) void mfma_prep_kerne
   if (tid < C) gates(cur, 0);
   int ib = 0;  // item parity: this item's gate copy
   for (int64_t it = blockIdx.x; it < n_items; it += gridDim.x, ib ^= 1) {
+    // The next item; after the workgroup's last item an empty one (n = 0) whose
+    // prefetch loads nothing, so that the prefetch stays unconditional.
     Item nx;
     geom(it + gridDim.x < n_items ? it + gridDim.x : it, nx);
+    if (it + gridDim.x >= n_items) nx.n = 0;
     const int hv = cur.hv, h = cur.h, n = cur.n;
     const int64_t c = cur.c, t0 = cur.t0;
     const int64_t pair = c * HV + hv;

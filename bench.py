@@ -49,17 +49,20 @@ def stage_bytes(p, s_qkv: int, s_ws: int, n_chunks: int):
     n_pairs = n_chunks * p.HV
     qk_frag = rows * p.HV * p.dk * 2 + rows * p.H * p.dk * 2   # K~ + normalised q
     touched = int(sum(1 for L in (p.cu_seqlens[1:] - p.cu_seqlens[:-1]) if L > 0))
+    # A_qk is causal: of its 2 x 4 fragments (32-token step x 16-row tile) the two above
+    # the diagonal are zero and neither written nor read
+    aqk = n_pairs * C * C * s_ws * 3 // 4
     # stage 0 is the chunk table only: the bf16 chunk prep forms its own gates
     gate = (p.B + 1) * 8 + n_chunks * 4
     # prep: reads q, k, v and the raw gate inputs a, b (fp32); writes W<-, U~, the row
     # scale e^G, A_qk, K~ and the q copy
     prep = (2 * p.N * p.H * p.dk * s_qkv + p.N * p.HV * p.dv * s_qkv + p.N * p.HV * 8
             + rows * p.HV * (p.dk + p.dv) * s_ws + rows * p.HV * 4
-            + n_pairs * C * C * s_ws + qk_frag)
+            + aqk + qk_frag)
     # state: reads K~, the q copy, W<-, U~, e^G (its last row is e^{G_n}) and A_qk; writes
     # o; reads and writes the fp32 state of every touched slot
     state = (qk_frag + rows * p.HV * (p.dk + p.dv) * s_ws + rows * p.HV * 4
-             + n_pairs * C * C * s_ws + p.N * p.HV * p.dv * s_qkv
+             + aqk + p.N * p.HV * p.dv * s_qkv
              + touched * p.HV * p.dv * p.dk * 8)
     return {"gate": gate, "chunk_prep": prep, "state": state}
 

@@ -401,9 +401,12 @@ __global__ __launch_bounds__(256, (DK + DV <= 256) ? 3 : 1) void mfma_prep_kerne
       }
       aq[J] = to_half4(x);
     }
+    // the fragment of row tiles 0 and 1 at token step 1 lies above the diagonal: zero, and
+    // never read by the state pass
   #pragma unroll
     for (int s = 0; s < 2; ++s)
-      __builtin_nontemporal_store(cat(aq[2 * s], aq[2 * s + 1]), reinterpret_cast<half8*>(Aout + pair * C * C + ((w * 2 + s) * 64 + l) * 8));
+      if (s == 0 || w >= 2)
+        __builtin_nontemporal_store(cat(aq[2 * s], aq[2 * s + 1]), reinterpret_cast<half8*>(Aout + pair * C * C + ((w * 2 + s) * 64 + l) * 8));
 
     // ---- diagonal tile: T_ww = (I + A_ww)^-1 by forward substitution, lane = column m
     float* sqw = sm.sq[w];

@@ -266,16 +266,23 @@ __global__ __launch_bounds__(64 * (2 + NO + kStoreWaves<DK>)) void mfma_state_ke
         u32x4 af[NRO][2];    // A_qk fragments: own row tile, token step
         float egr[NRO];      // e^G of row 16 I + m
       };
-      auto load_q = [&](Regs& R, int cl) {
-        const int64_t pr = pair_of(cl);
+      // The Qh fragments are reloaded as soon as Qh S^T has used them, while the wave
+      // waits for barrier (B) anyway; the A_qk fragments and row scales after A_qk U.
+      auto load_qf = [&](Regs& R, int cl) {
         const _Float16* qb = Qf + ((cbase + cl) * H + h) * (int64_t)(C * DK);
 #pragma unroll
         for (int r = 0; r < NRO; ++r) {
-          constexpr int I0 = NRO * ow;
-          const int I = I0 + r;
+          const int I = NRO * ow + r;
 #pragma unroll
           for (int sp = 0; sp < NKS; ++sp)
             R.qf[r][sp] = *reinterpret_cast<const u32x4*>(qb + ((I * NKS + sp) * 64 + l) * 8);
+        }
+      };
+      auto load_af = [&](Regs& R, int cl) {
+        const int64_t pr = pair_of(cl);
+#pragma unroll
+        for (int r = 0; r < NRO; ++r) {
+          const int I = NRO * ow + r;
 #pragma unroll
           for (int s = 0; s < 2; ++s)
             if (s == 0 || I >= 2)
@@ -303,6 +310,7 @@ __global__ __launch_bounds__(64 * (2 + NO + kStoreWaves<DK>)) void mfma_state_ke
             o1[r][c] = acc;
           }
         }
+        load_qf(R, nx);
         lds_barrier();  // (B) U of chunk cl visible
         f32x4 au[NRO][NC];
 #pragma unroll
@@ -331,11 +339,14 @@ __global__ __launch_bounds__(64 * (2 + NO + kStoreWaves<DK>)) void mfma_state_ke
                                          16 * (ct0 + c) + 4 * g) = ov;
             }
           }
-        load_q(R, nx);
+        load_af(R, nx);
       };
       Regs rs[PD];
 #pragma unroll
-      for (int j = 0; j < PD; ++j) load_q(rs[j], min(j, nch - 1));
+      for (int j = 0; j < PD; ++j) {
+        load_qf(rs[j], min(j, nch - 1));
+        load_af(rs[j], min(j, nch - 1));
+      }
       for (int cl = 0; cl < nch; cl += PD) {
 #pragma unroll
         for (int j = 0; j < PD; ++j) step(rs[j], cl + j);

@@ -26,9 +26,11 @@
 // only tiles another wave needs pass through LDS. Every wave keeps the transposed tiles
 // T_wJ^T of its own rows, which are exactly the operand fragments of its rows of W<- and
 // U~. The token contractions read column fragments of K and V with the LDS transpose
-// read. Four barriers after staging. For the state pass the kernel also writes K~ (fp16,
+// read. Five barriers after staging. For the state pass the kernel also writes K~ (fp16,
 // per value head, since the gates are) and normalised q (fp16, once per q/k head) in
-// that kernel's operand-fragment order.
+// that kernel's operand-fragment order. The gates themselves (g, beta and the chunk-local
+// log cumulative decay G) are formed here too, by wave 0 for the next item at the end of
+// the current one.
 //
 // Fragment notation: Dl(X) is the MFMA result layout of a 16 x 16 tile X, lane
 // l = 16 g + m holding X[4g + i][m], i = 0..3. A product P Q takes Dl(P^T) as its A
@@ -83,7 +85,8 @@ __device__ __forceinline__ void load_tile_rows(u32x4 (&r)[C * D / 8 / 256], cons
   for (int u = 0; u < C * D / 8 / 256; ++u) {
     const int e = tid + 256 * u, row = e / (D / 8), c8 = (e % (D / 8)) * 8;
     u32x4 z = {0u, 0u, 0u, 0u};
-    if (row < n) z = *reinterpret_cast<const u32x4*>(src + row * rs + c8);
+    // non-temporal: the rows are read once (measured slightly faster than cached loads)
+    if (row < n) z = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + row * rs + c8));
     r[u] = z;
   }
 }

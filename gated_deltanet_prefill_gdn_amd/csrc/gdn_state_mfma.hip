@@ -27,11 +27,13 @@
 //     a double-buffered output tile in LDS.
 //   * One store wave copies each finished tile to out with row-contiguous 16-byte
 //     stores, so that no wave that waits for its prefetched operands has stores queued
-//     among its loads (a wave's loads and stores retire in order).
+//     among its loads (a wave's loads and stores retire in order). This is up to
+//     dk = 128; at dk = 256 the output waves store O themselves (see kStoreWaves).
 // Every operand comes straight from global memory into MFMA operand registers, in the
 // fragment orders the prep kernel wrote (one contiguous 1 KiB piece per fragment). Two
 // register sets (one at dk = 256) alternate between chunks, each reloaded right after its
-// last use, so every load has about two chunks of the chain to land.
+// last use (the output waves' q fragments right after Qh S^T, before barrier B), so every
+// load has about two chunks of the chain to land.
 //
 // Matrix-core operands, all fp16 with fp32 accumulation: W<- and S for P; normalised q
 // and S for Qh S^T; K~ and U for the update; A_qk and U for A_qk U. The state itself

@@ -92,6 +92,30 @@ def test_thousands_of_requests(nreq):
     compare(p, out, pool, oracle.prefill(p))
 
 
+@pytest.mark.parametrize("case", range(10))
+def test_random_shapes(case):
+    """Seeded random configurations: request counts on both sides of 64, lengths with
+    empty and partial chunks, every grouped-head ratio up to 4, every head-dim pair, both
+    dtypes, a shuffled pool with spare slots, and gates from gentle to strong decay."""
+    rng = np.random.default_rng(500 + case)
+    B = int(rng.choice([1, 3, 17, 70, 130]))
+    lengths = [int(x) if rng.random() > 0.15 else 0 for x in rng.integers(1, 300, B)]
+    H = int(rng.choice([1, 2, 4]))
+    HV = H * int(rng.choice([1, 2, 4]))
+    dims = [(64, 64), (64, 128), (128, 64), (128, 128), (128, 256), (256, 128), (256, 256),
+            (64, 256), (256, 64)]
+    dk, dv = dims[int(rng.integers(len(dims)))]
+    dtype = "bf16" if case % 3 else "f32"
+    pool = B + int(rng.integers(0, 5))
+    p = gdn_synth.make_problem(500 + case, lengths, H, HV, dk, dv, dtype=dtype, pool=pool,
+                               cache_indices=list(rng.permutation(pool)[:B]),
+                               a_mean=float(rng.uniform(-3.0, 1.0)),
+                               b_mean=float(rng.uniform(-1.0, 1.0)),
+                               state_std=float(rng.choice([0.0, 0.1, 0.5])))
+    out, pool_gpu, _ = run_gpu(p, f"random-{case}")
+    compare(p, out, pool_gpu, oracle.prefill(p))
+
+
 def test_all_requests_empty_is_a_no_op():
     import torch
     p = gdn_synth.make_problem(35, [0, 0, 0], 1, 1, 64, 64, dtype="bf16", state_std=1.0)

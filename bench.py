@@ -5,6 +5,10 @@ bf16 workload: 4 requests x 4096 tokens, H = HV = 16, dk = dv = 128, C = 64, wit
 inputs resident in HBM. Prints one JSON line.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+With ``--op decode`` a step is instead one gdn_decode_fwd call over the decode workload
+(512 requests x 1 token, H = 16, HV = 32, dk = dv = 128, bf16, 1 GiB of state), and the
+JSON line reports that.
 """
 from __future__ import annotations
 
@@ -67,13 +71,22 @@ def stage_bytes(p, s_qkv: int, s_ws: int, n_chunks: int):
     return {"gate": gate, "chunk_prep": prep, "state": state}
 
 
-def kernel_source_hash() -> str:
+DECODE_SOURCES = ("gdn_decode.hip", "gdn_internal.h")
+
+
+def kernel_source_hash(kind: str = "prefill") -> str:
+    """sha256[:16] over the kernel sources a measurement depends on: for "prefill" every
+    .hip / .h file of csrc except the decode kernel's, for "decode" DECODE_SOURCES."""
     csrc = os.path.join(ROOT, "gated_deltanet_prefill_gdn_amd", "csrc")
+    if kind == "decode":
+        files = sorted(DECODE_SOURCES)
+    else:
+        files = sorted(f for f in os.listdir(csrc)
+                       if f.endswith((".hip", ".h")) and f != "gdn_decode.hip")
     h = hashlib.sha256()
-    for f in sorted(os.listdir(csrc)):
-        if f.endswith((".hip", ".h")):
-            h.update(f.encode())
-            h.update(open(os.path.join(csrc, f), "rb").read())
+    for f in files:
+        h.update(f.encode())
+        h.update(open(os.path.join(csrc, f), "rb").read())
     return h.hexdigest()[:16]
 
 
@@ -142,8 +155,133 @@ def cpu_baseline(p, reps: int = 3):
                       f"fp64 recurrence, median of {reps} runs, {dt:.2f} s wall each"}
 
 
+DECODE_METRIC = "GDN decode step tokens/sec (one token per request), dk=dv=128"
+
+
+def decode_bytes(p, s_qkv: int) -> int:
+    """Algorithmic HBM bytes of one decode step: the fp32 state of every (request, value
+    head) read and written once; q, k per q/k head, v and out per value head; a, b; the
+    per-head gate parameters and the slot indices."""
+    return (2 * p.B * p.HV * p.dv * p.dk * 4 + 2 * p.B * p.H * p.dk * s_qkv
+            + 2 * p.B * p.HV * p.dv * s_qkv + 8 * p.B * p.HV + 8 * p.HV + 8 * p.B)
+
+
+def decode_cpu_baseline(p, n_req: int = 64, reps: int = 3):
+    """The oracle (fp64 recurrence, one step) as it stands, on this host's cores, over the
+    first n_req requests of the decode workload with every value head; the median wall
+    time gives tokens/s."""
+    import numpy as np
+    import oracle
+    import gdn_synth
+    reqs = np.arange(n_req)
+    sub = gdn_synth.make_decode_problem(p.seed, 0, p.H, p.HV, p.dk, p.dv, dtype=p.dtype, pool=1)
+    sub.q, sub.k, sub.v, sub.a, sub.b = p.q[reqs], p.k[reqs], p.v[reqs], p.a[reqs], p.b[reqs]
+    sub.A_log, sub.dt_bias = p.A_log, p.dt_bias
+    sub.state_pool = p.state_pool[p.cache_indices[reqs]]
+    sub.cache_indices = np.arange(n_req, dtype=np.int64)
+    sub.cu_seqlens = np.arange(n_req + 1, dtype=np.int64)
+    threads = oracle.default_threads()
+    walls = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        oracle.decode(sub, nthreads=threads)
+        walls.append(time.perf_counter() - t0)
+    dt = float(np.median(walls))
+    return {"value": n_req / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n_req} of the {p.B} requests, all {p.HV} value heads, fp64 recurrence "
+                      f"step, median of {reps} runs, {dt:.3f} s wall each"}
+
+
+def bench_decode(args):
+    import numpy as np
+    import torch
+
+    import gdn_synth
+    import gated_deltanet_prefill_gdn_amd as gdn
+
+    p = gdn_synth.decode_workload()
+    dev = torch.device("cuda:0")
+
+    def t(x, dt=None):
+        x = torch.from_numpy(np.ascontiguousarray(x))
+        return (x.view(dt) if dt is not None else x).to(dev)
+
+    q = t(p.q.view(np.int16), torch.bfloat16)
+    k = t(p.k.view(np.int16), torch.bfloat16)
+    v = t(p.v.view(np.int16), torch.bfloat16)
+    a, b, A_log, dt_bias = t(p.a), t(p.b), t(p.A_log), t(p.dt_bias)
+    pool = t(p.state_pool)
+    idx = t(p.cache_indices)
+    out = torch.empty((p.B, p.HV, p.dv), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        gdn.gdn_decode_fwd(q, k, v, a, b, A_log, dt_bias, pool, idx, out=out, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    # the same steps with HIP events on the launch stream around each launch
+    hip = Hip()
+    evs = [(hip.event(), hip.event()) for _ in range(args.steps)]
+    rec = hip.lib.hipEventRecord
+    rec.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    torch.cuda.synchronize()
+    for e0, e1 in evs:
+        rec(ctypes.c_void_p(e0), ctypes.c_void_p(stream.cuda_stream))
+        step()
+        rec(ctypes.c_void_p(e1), ctypes.c_void_p(stream.cuda_stream))
+    torch.cuda.synchronize()
+    launch_ms = float(np.mean([hip.elapsed_ms(e0, e1) for e0, e1 in evs]))
+    for e0, e1 in evs:
+        hip.destroy(e0)
+        hip.destroy(e1)
+    if args.copy_calibration:
+        src = torch.empty(512 << 20, dtype=torch.uint8, device=dev).fill_(3)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    nbytes = decode_bytes(p, 2)
+    achieved = nbytes / (launch_ms * 1e-3) / 1e9
+    src_hash = kernel_source_hash("decode")
+    res = {
+        "metric": DECODE_METRIC,
+        "value": p.B / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded SplitMix64/Box-Muller, seed 1100)",
+        "config": {"workload": gdn_synth.DECODE_WORKLOAD, "global_batch": p.B, "seq_len": 1,
+                   "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "hbm", "kernel": "decode_kernel", "achieved": achieved,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": stored_traffic("decode_kernel", src_hash),
+                     "algorithmic_bytes_per_launch": nbytes, "avg_launch_ms": launch_ms},
+        "kernel_source_hash": src_hash,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = decode_cpu_baseline(p)
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
+    ap.add_argument("--op", choices=("prefill", "decode"), default="prefill",
+                    help="the call a step times (default: the prefill forward)")
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
@@ -157,6 +295,9 @@ def main():
         print(f"bench.py measures one GPU only: this build has no multi-GPU path "
               f"(--gpus {args.gpus} requested).", file=sys.stderr)
         sys.exit(2)
+    if args.op == "decode":
+        bench_decode(args)
+        return
 
     import numpy as np
     import torch

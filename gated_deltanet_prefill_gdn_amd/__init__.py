@@ -1,4 +1,5 @@
-"""Python binding of libgdn (Gated DeltaNet chunkwise prefill forward on MI355X).
+"""Python binding of libgdn (Gated DeltaNet chunkwise prefill forward and decode step on
+MI355X).
 
 The names match the C ABI in include/gdn.h. This module only marshals
 arguments: it checks tensor shapes, dtypes, devices and contiguity, allocates
@@ -29,7 +30,7 @@ GDN_NUM_STAGES = 3
 STAGE_NAMES = ("gate", "chunk_prep", "state")
 
 EXPORTED = ("gdn_prefill_workspace_size", "gdn_prefill_fwd", "gdn_prefill_fwd_events",
-            "gdn_validate_inputs", "gdn_status_str", "gdn_version")
+            "gdn_decode_fwd", "gdn_validate_inputs", "gdn_status_str", "gdn_version")
 
 
 class GdnProblem(ctypes.Structure):
@@ -74,6 +75,8 @@ def load_library(path: str = LIB_PATH):
                                   ctypes.c_size_t, P]
     L.gdn_prefill_fwd_events.restype = ctypes.c_int
     L.gdn_prefill_fwd_events.argtypes = L.gdn_prefill_fwd.argtypes + [P]
+    L.gdn_decode_fwd.restype = ctypes.c_int
+    L.gdn_decode_fwd.argtypes = [P, P, P, P, P, P, P, P, P, P, PP, P]
     L.gdn_validate_inputs.restype = ctypes.c_int
     L.gdn_validate_inputs.argtypes = [P, P, PP, P]
     L.gdn_status_str.restype = ctypes.c_char_p
@@ -210,6 +213,58 @@ def _prefill(q, k, v, a, b, A_log, dt_bias, state_pool, cache_indices, cu_seqlen
     rc = L.gdn_prefill_fwd(*args) if events is None else L.gdn_prefill_fwd_events(*args, events)
     if rc != GDN_OK:
         raise GdnError(rc, "gdn_prefill_fwd")
+    return out
+
+
+def gdn_decode_fwd(q, k, v, a, b, A_log, dt_bias, state_pool, cache_indices, out=None,
+                   stream=None):
+    """One decode step on device tensors (one token per request); returns ``out``
+    [B, HV, dv] in v's dtype.
+
+    q, k [B, H, dk] and v [B, HV, dv] bf16/fp32; a, b [B, HV] fp32; A_log, dt_bias [HV]
+    fp32; state_pool [pool, HV, dv, dk] fp32 (updated in place); cache_indices [B] int64.
+    ``stream``: a torch stream (default: current)."""
+    import torch
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("gdn_decode_fwd runs on a HIP device; tensors are on " + str(dev))
+    _need(q, "q", ndim=3, device=dev)
+    _need(k, "k", dtype=q.dtype, ndim=3, device=dev)
+    _need(v, "v", dtype=q.dtype, ndim=3, device=dev)
+    B, H, dk = q.shape
+    if tuple(k.shape) != (B, H, dk):
+        raise ValueError(f"k shape {tuple(k.shape)} != q shape {tuple(q.shape)}")
+    HV, dv = v.shape[1], v.shape[2]
+    if v.shape[0] != B:
+        raise ValueError("v must have B rows")
+    for t, name in ((a, "a"), (b, "b")):
+        _need(t, name, dtype=torch.float32, ndim=2, device=dev)
+        if tuple(t.shape) != (B, HV):
+            raise ValueError(f"{name} must be [B, HV] = {(B, HV)}, got {tuple(t.shape)}")
+    for t, name in ((A_log, "A_log"), (dt_bias, "dt_bias")):
+        _need(t, name, dtype=torch.float32, ndim=1, device=dev)
+        if t.shape[0] != HV:
+            raise ValueError(f"{name} must be [HV]")
+    _need(state_pool, "state_pool", dtype=torch.float32, ndim=4, device=dev)
+    if tuple(state_pool.shape[1:]) != (HV, dv, dk):
+        raise ValueError(f"state_pool must be [pool, {HV}, {dv}, {dk}], got {tuple(state_pool.shape)}")
+    _need(cache_indices, "cache_indices", dtype=torch.int64, ndim=1, device=dev)
+    if cache_indices.shape[0] != B:
+        raise ValueError("cache_indices must have B entries")
+    prob = problem_of(q, k, v, state_pool, cache_indices)
+    if out is None:
+        out = torch.empty((B, HV, dv), dtype=v.dtype, device=dev)
+    else:
+        _need(out, "out", dtype=v.dtype, ndim=3, device=dev)
+        if tuple(out.shape) != (B, HV, dv):
+            raise ValueError("out must be [B, HV, dv]")
+    st = (stream or torch.cuda.current_stream(dev)).cuda_stream
+    rc = load_library().gdn_decode_fwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(A_log), _ptr(dt_bias),
+        _ptr(state_pool), _ptr(cache_indices), _ptr(out), ctypes.byref(prob),
+        ctypes.c_void_p(st))
+    if rc != GDN_OK:
+        raise GdnError(rc, "gdn_decode_fwd")
     return out
 
 

@@ -1,5 +1,6 @@
 // C ABI of libgdn (declared in include/gdn.h): host-side argument checks, the
-// workspace layout and the launch sequence plan -> gate -> chunk prep -> state pass.
+// workspace layout and the launch sequence plan -> gate -> chunk prep -> state pass of
+// the prefill, and the one-kernel decode step.
 #include <string.h>
 
 #include <vector>
@@ -79,7 +80,7 @@ using namespace gdn;
 
 extern "C" {
 
-int32_t gdn_version(void) { return 100; }
+int32_t gdn_version(void) { return 200; }
 
 const char* gdn_status_str(gdn_status_t st) {
   switch (st) {
@@ -197,6 +198,26 @@ gdn_status_t gdn_prefill_fwd_events(const void* q, const void* k, const void* v,
   if (!stage_events) return GDN_ERR_INVALID_ARG;
   return run_prefill(q, k, v, a, b, A_log, dt_bias, state_pool, cache_indices, cu_seqlens,
                      chunk_size, out, prob, workspace, workspace_bytes, stream, stage_events);
+}
+
+gdn_status_t gdn_decode_fwd(const void* q, const void* k, const void* v, const float* a,
+                            const float* b, const float* A_log, const float* dt_bias,
+                            float* state_pool, const int64_t* cache_indices, void* out,
+                            const gdn_problem_t* prob, void* stream) {
+  Shape s;
+  const gdn_status_t ps = check_problem(prob, 64, &s);  // the chunk size plays no part
+  if (ps != GDN_OK) return ps;
+  if (s.N != s.B) return GDN_ERR_INVALID_ARG;  // exactly one token per request
+  if (s.B == 0) return GDN_OK;
+  if (!q || !k || !v || !a || !b || !A_log || !dt_bias || !state_pool || !cache_indices || !out)
+    return GDN_ERR_INVALID_ARG;
+  for (const void* ptr : {q, k, v, (const void*)state_pool})  // 16-byte vector loads
+    if (((uintptr_t)ptr & 15) != 0) return GDN_ERR_INVALID_ARG;
+  if (decode_blocks(s) > 0x7FFFFFFF) return GDN_ERR_UNSUPPORTED;
+  if (launch_decode(q, k, v, a, b, A_log, dt_bias, cache_indices, s, state_pool, out,
+                    (hipStream_t)stream) != hipSuccess)
+    return GDN_ERR_HIP;
+  return GDN_OK;
 }
 
 gdn_status_t gdn_validate_inputs(const int64_t* cu_seqlens, const int64_t* cache_indices,

@@ -75,4 +75,11 @@ hipError_t launch_mfma_state(const void* qf, const void* kf, const int64_t* cu_s
                              const float* eg, const Shape& s, float* state_pool, void* out,
                              hipStream_t st);
 
+// Decode step (one token per request): workgroups a launch needs, and the launcher.
+int64_t decode_blocks(const Shape& s);
+hipError_t launch_decode(const void* q, const void* k, const void* v, const float* a,
+                         const float* b, const float* A_log, const float* dt_bias,
+                         const int64_t* cache_indices, const Shape& s, float* state_pool,
+                         void* out, hipStream_t st);
+
 }  // namespace gdn

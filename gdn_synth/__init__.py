@@ -265,3 +265,29 @@ def workload(idx: int) -> Problem:
         return make_problem(seed, L, 16, 32, 128, 128, a_mean=-4.0, b_mean=2.0, state_std=0.1,
                             name="long_decay_bf16")
     raise ValueError(idx)
+
+
+# The decode workload: one new token for each of 512 requests, the head layout of the
+# varlen GQA workload (H = 16 q/k heads, HV = 32 value heads, dk = dv = 128, bf16), a pool of
+# 512 slots ~N(0, 0.1^2) (the states a prefill left behind) taken in a seeded order.
+DECODE_WORKLOAD = ("decode batch bf16: B=512 requests x 1 token, H=16 HV=32 dk=dv=128, "
+                   "pool 512 ~N(0,0.01) in seeded order")
+
+
+def make_decode_problem(seed: int, B: int, H: int, HV: int, dk: int, dv: int,
+                        dtype: str = "bf16", pool: Optional[int] = None,
+                        cache_indices: Optional[Sequence[int]] = None, state_std: float = 0.1,
+                        a_mean: float = 0.0, b_mean: float = 0.0,
+                        name: str = "decode") -> Problem:
+    """A decode step's inputs: B requests of one token each (cu_seqlens = 0, 1, .., B),
+    otherwise drawn as by make_problem."""
+    return make_problem(seed, [1] * B, H, HV, dk, dv, dtype=dtype, pool=pool,
+                        cache_indices=cache_indices, a_mean=a_mean, b_mean=b_mean,
+                        state_std=state_std, name=name)
+
+
+def decode_workload() -> Problem:
+    seed = 1100
+    perm = seeded_permutation(seed, TID_PERM, 512)
+    return make_decode_problem(seed, 512, 16, 32, 128, 128, pool=512, cache_indices=perm,
+                               state_std=0.1, name="decode_batch_bf16")

@@ -1,5 +1,6 @@
 /*
- * libgdn -- Gated DeltaNet chunkwise prefill forward on MI355X (gfx950).
+ * libgdn -- Gated DeltaNet chunkwise prefill forward (and the decode step that follows
+ * it) on MI355X (gfx950).
  *
  * The operation (pymllm gdn_chunkwise page, "gdn_extend_chunkwise", Module
  * Contents; the recurrence is the state-transition equation of "Simple math to
@@ -111,6 +112,26 @@ gdn_status_t gdn_prefill_fwd_events(const void* q, const void* k, const void* v,
                                     const gdn_problem_t* prob, void* workspace,
                                     size_t workspace_bytes, void* stream,
                                     void* const* stage_events);
+
+/* One decode step: every request b brings exactly one new token, row b of q, k, v, a, b,
+ * and the token's step of the recurrence at the top of this file is applied to
+ * S = state_pool[cache_indices[b], hv] in place, with out[b, hv] = S qh read after the
+ * write (the step after a prefill in serving: pymllm gdn_chunkwise page, Module
+ * Contents, where the pool and indices serve the later decoding; the step itself is the
+ * state-transition equation of "Simple math to speed up GDN prefill", section Reminder).
+ * It equals gdn_prefill_fwd with cu_seqlens = {0, 1, ..., B}, computed without chunks:
+ *   u = beta (v - alpha S kh),  S <- alpha S + u kh^T,  out = alpha S_old qh + (kh . qh) u.
+ * prob->total_tokens must equal prob->batch (GDN_ERR_INVALID_ARG otherwise); the other
+ * fields, layouts, dtypes and head dims are those of gdn_prefill_fwd:
+ *   q, k [B, H, dk]; v, out [B, HV, dv]; a, b [B, HV]; A_log, dt_bias [HV];
+ *   state_pool [pool, HV, dv, dk] fp32; cache_indices [B] int64, distinct, in [0, pool).
+ * All DEVICE pointers; q, k, v and state_pool 16-byte aligned. No workspace, no
+ * allocation, asynchronous on `stream`; B == 0 is a no-op. Arithmetic in fp32. Errors as
+ * for gdn_prefill_fwd: host checks before any launch. */
+gdn_status_t gdn_decode_fwd(const void* q, const void* k, const void* v, const float* a,
+                            const float* b, const float* A_log, const float* dt_bias,
+                            float* state_pool, const int64_t* cache_indices, void* out,
+                            const gdn_problem_t* prob, void* stream);
 
 /* Debug check of the device-array preconditions: cu_seqlens[0] == 0, non-decreasing,
  * cu_seqlens[B] == N; cache_indices distinct and in [0, pool). Copies both arrays to

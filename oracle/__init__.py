@@ -10,6 +10,9 @@ Contents
   state-pool semantics of the pymllm ``gdn_extend_chunkwise`` page (Module
   Contents: ``state_pool [pool, HV, V, K]`` updated in place at the slot
   ``cache_indices[b]`` of each request; packed tokens split by ``cu_seqlens``).
+* ``decode``: one token per request, i.e. one step of the same recurrence from each
+  request's slot (the same page: the pool and indices carry the state into the
+  decoding that follows the prefill). It is ``prefill`` with ``cu_seqlens`` = 0..B.
 * ``chunked``: the chunkwise forms of the pages in fp64 (self-checks only).
 * ``bruteforce``: dense products of the per-token transition matrices.
 
@@ -171,3 +174,16 @@ def prefill(p, heads: Optional[Sequence[int]] = None, rows=None, eps: float = EP
         for j, hv in enumerate(heads):
             new_pool[slot, hv, r0:r1, :] = S[bi, j]
     return OracleResult(out=out, state_pool=new_pool, heads=heads, rows=(r0, r1))
+
+
+def decode(p, heads: Optional[Sequence[int]] = None, rows=None, eps: float = EPS,
+           fp32_arith: bool = False, nthreads: Optional[int] = None) -> OracleResult:
+    """The decode step on a ``gdn_synth.Problem`` whose requests hold one token each
+    (row b of q, k, v, a, b is request b's token): one step of the recurrence from
+    ``state_pool[cache_indices[b]]``, the state written back to that slot, and
+    ``out[b] = S_new q`` (state-transition equation of "Simple math to speed up GDN
+    prefill", section Reminder). Same arithmetic as ``prefill``."""
+    cu = np.asarray(p.cu_seqlens, dtype=np.int64)
+    if not np.array_equal(cu, np.arange(p.B + 1, dtype=np.int64)):
+        raise ValueError("a decode problem has exactly one token per request")
+    return prefill(p, heads, rows, eps, fp32_arith, nthreads)

@@ -97,6 +97,32 @@ def test_empty_problem_is_a_no_op():
     assert call(prob(N=0, B=0, pool=0), nonnull=False, ws_bytes=0, ws_ptr=0) == gdn.GDN_OK
 
 
+def call_decode(p, nonnull=True, misalign=0):
+    lib = gdn.load_library()
+    P = ctypes.c_void_p
+    x = P(4096) if nonnull else P(0)
+    return lib.gdn_decode_fwd(P(4096 + misalign), x, x, x, x, x, x, x, x, x, ctypes.byref(p),
+                              P(0))
+
+
+def test_decode_error_paths_return_before_launch():
+    dec = dict(N=512, B=512, H=16, HV=32, pool=512)
+    assert call_decode(prob(**{**dec, "N": 511})) == gdn.GDN_ERR_INVALID_ARG  # one token each
+    assert call_decode(prob(**{**dec, "HV": 24})) == gdn.GDN_ERR_INVALID_ARG
+    assert call_decode(prob(**{**dec, "dtype": 2})) == gdn.GDN_ERR_INVALID_ARG
+    assert call_decode(prob(**{**dec, "pool": 0})) == gdn.GDN_ERR_INVALID_ARG
+    assert call_decode(prob(**{**dec, "dk": 32})) == gdn.GDN_ERR_UNSUPPORTED
+    assert call_decode(prob(**dec), nonnull=False) == gdn.GDN_ERR_INVALID_ARG
+    assert call_decode(prob(**dec), misalign=8) == gdn.GDN_ERR_INVALID_ARG   # q not 16-aligned
+    lib = gdn.load_library()
+    assert lib.gdn_decode_fwd(None, None, None, None, None, None, None, None, None, None, None,
+                              None) == gdn.GDN_ERR_INVALID_ARG
+
+
+def test_decode_empty_batch_is_a_no_op():
+    assert call_decode(prob(N=0, B=0, pool=0), nonnull=False) == gdn.GDN_OK
+
+
 def test_binding_rejects_cpu_tensors():
     torch = pytest.importorskip("torch")
     z = torch.zeros(4, 1, 64)

@@ -139,8 +139,12 @@ gdn_status_t run_prefill(const void* q, const void* k, const void* v, const floa
   double* gcum = (double*)(ws + L.gcum);
   float* beta = (float*)(ws + L.beta);
 
+  // Up to 64 requests the MFMA chunk prep forms the chunk table itself (one scan per
+  // workgroup) and writes chunk_off for the state pass: one launch fewer.
+  const bool self_plan = path == Path::kMfma && s.B <= kMaxSelfPlanRequests;
   if (!mark(0)) return GDN_ERR_HIP;
-  if (launch_plan(cu_seqlens, s, chunk_off, chunk_seq, L.max_chunks, st) != hipSuccess)
+  if (!self_plan &&
+      launch_plan(cu_seqlens, s, chunk_off, chunk_seq, L.max_chunks, st) != hipSuccess)
     return GDN_ERR_HIP;
   if (path == Path::kRef &&
       launch_gate(a, b, A_log, dt_bias, cu_seqlens, chunk_off, chunk_seq, s, L.max_chunks, gcum,
@@ -154,8 +158,8 @@ gdn_status_t run_prefill(const void* q, const void* k, const void* v, const floa
     float* eg = (float*)(ws + L.eg);
     void* kf = ws + L.kf;
     void* qf = ws + L.qf;
-    if (launch_mfma_prep(q, k, v, cu_seqlens, chunk_off, chunk_seq, a, b, A_log, dt_bias, s,
-                         L.max_chunks, w, u, aqk, eg, kf, qf, st) != hipSuccess)
+    if (launch_mfma_prep(q, k, v, cu_seqlens, chunk_off, chunk_seq, self_plan, a, b, A_log,
+                         dt_bias, s, L.max_chunks, w, u, aqk, eg, kf, qf, st) != hipSuccess)
       return GDN_ERR_HIP;
     if (!mark(2)) return GDN_ERR_HIP;
     if (launch_mfma_state(qf, kf, cu_seqlens, cache_indices, chunk_off, w, u, aqk, eg, s,

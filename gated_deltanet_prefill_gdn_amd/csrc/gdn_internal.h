@@ -63,12 +63,16 @@ hipError_t launch_ref_state(const void* q, const void* k, const int64_t* cu_seql
                             const double* gcum, const float* w, const float* u, const Shape& s,
                             float* state_pool, void* out, hipStream_t st);
 
+// self_plan (at most kMaxSelfPlanRequests requests): the prep kernel forms the chunk table
+// itself and writes chunk_off (B + 1 entries) for the state pass; chunk_seq is then not
+// read and the plan kernel need not run.
+constexpr int kMaxSelfPlanRequests = 64;
 hipError_t launch_mfma_prep(const void* q, const void* k, const void* v,
-                            const int64_t* cu_seqlens, const int32_t* chunk_off,
-                            const int32_t* chunk_seq, const float* a, const float* b,
-                            const float* A_log, const float* dt_bias, const Shape& s,
-                            int64_t max_chunks, void* w, void* u, void* aqk, float* eg, void* kf,
-                            void* qf, hipStream_t st);
+                            const int64_t* cu_seqlens, int32_t* chunk_off,
+                            const int32_t* chunk_seq, bool self_plan, const float* a,
+                            const float* b, const float* A_log, const float* dt_bias,
+                            const Shape& s, int64_t max_chunks, void* w, void* u, void* aqk,
+                            float* eg, void* kf, void* qf, hipStream_t st);
 hipError_t launch_mfma_state(const void* qf, const void* kf, const int64_t* cu_seqlens,
                              const int64_t* cache_indices, const int32_t* chunk_off,
                              const void* w, const void* u, const void* aqk,

@@ -67,6 +67,7 @@ struct PrepSmem {
   double G2[2][C];        // G log2(e), by item parity
   float bt[2][C];         // beta, by item parity
   float rk[C];            // r_k
+  int32_t coff[kMaxSelfPlanRequests + 1];  // chunk table formed here: first chunk of each request
 };
 
 // LDS slot of an exchanged tile T_IJ (I - J <= 2).
@@ -196,10 +197,10 @@ __device__ __forceinline__ bf16x8 cat_bf(bf16x4 a, bf16x4 b) {
 // Up to dk + dv = 256 three workgroups share a compute unit (168 VGPRs, no spills; the
 // LDS of three fits): the item's phases are short chains separated by barriers, and the
 // third workgroup fills the gaps (about 8% faster than two at dk = dv = 128, measured).
-template <int DK, int DV>
+template <int DK, int DV, bool SELF_PLAN>
 __global__ __launch_bounds__(256, (DK + DV <= 256) ? 3 : 1) void mfma_prep_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    const int64_t* __restrict__ cu, const int32_t* __restrict__ chunk_off,
+    const int64_t* __restrict__ cu, int32_t* __restrict__ chunk_off,
     const int32_t* __restrict__ chunk_seq, const float* __restrict__ ga,
     const float* __restrict__ gb, const float* __restrict__ A_log,
     const float* __restrict__ dt_bias, int B, int H, int HV, _Float16* __restrict__ Wout,
@@ -227,8 +228,20 @@ __global__ __launch_bounds__(256, (DK + DV <= 256) ? 3 : 1) void mfma_prep_kerne
     x.c = it / HV;
     x.hv = (int)(it % HV);
     x.h = x.hv / (HV / H);
-    const int32_t sq = chunk_seq[x.c];
-    x.t0 = cu[sq] + (int64_t)(x.c - chunk_off[sq]) * C;
+    int32_t sq, first;
+    if constexpr (SELF_PLAN) {
+      // the owner of chunk c: the number of requests whose chunks all precede c (the
+      // chunk ends coff[b + 1] do not decrease, so they are the first sq requests)
+      // (the lane index is opaque so the LDS read is not hoisted out of the item loop,
+      // where it would hold a register for the whole loop)
+      const int lo = opaque(l);
+      sq = __popcll(__ballot(lo < B && sm.coff[lo + 1] <= x.c));
+      first = sm.coff[sq];
+    } else {
+      sq = chunk_seq[x.c];
+      first = chunk_off[sq];
+    }
+    x.t0 = cu[sq] + (int64_t)(x.c - first) * C;
     x.n = (int)min((int64_t)C, cu[sq + 1] - x.t0);
   };
   u32x4 kreg[KP], qreg[KP], vreg[VP];
@@ -269,7 +282,29 @@ __global__ __launch_bounds__(256, (DK + DV <= 256) ? 3 : 1) void mfma_prep_kerne
     sm.G2[buf][tid] = G * kLog2e;
     sm.bt[buf][tid] = bt;
   };
-  const int64_t n_items = (int64_t)chunk_off[B] * HV;
+  if constexpr (SELF_PLAN) {
+    // At most 64 requests: wave 0 forms the chunk table with one scan (coff[b] = sum of
+    // ceil(L_b' / C) over b' < b), and workgroup 0 writes it out for the state pass, so no
+    // separate table kernel runs.
+    if (w == 0) {
+      int32_t nb = 0;
+      if (l < B) {
+        const int64_t L = cu[l + 1] - cu[l];
+        nb = L > 0 ? (int32_t)((L + C - 1) / C) : 0;
+      }
+      int32_t x = nb;  // inclusive scan over the wave
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int32_t y = __shfl_up(x, off, 64);
+        if (l >= off) x += y;
+      }
+      sm.coff[l + 1] = x;
+      if (l == 0) sm.coff[0] = 0;
+    }
+    __syncthreads();
+    if (blockIdx.x == 0 && tid <= B) chunk_off[tid] = sm.coff[tid];
+  }
+  const int64_t n_items = (int64_t)(SELF_PLAN ? sm.coff[B] : chunk_off[B]) * HV;
   if ((int64_t)blockIdx.x >= n_items) return;
   Item cur;
   geom(blockIdx.x, cur);
@@ -547,39 +582,41 @@ __global__ __launch_bounds__(256, (DK + DV <= 256) ? 3 : 1) void mfma_prep_kerne
 
 template <int DK, int DV>
 hipError_t launch_prep_t(const void* q, const void* k, const void* v, const int64_t* cu,
-                         const int32_t* off, const int32_t* cseq, const float* ga,
+                         int32_t* off, const int32_t* cseq, bool self_plan, const float* ga,
                          const float* gb, const float* A_log, const float* dt_bias,
                          const Shape& s, int64_t max_chunks, _Float16* w,
                          _Float16* u, _Float16* aqk, float* eg, _Float16* kf, _Float16* qf,
                          hipStream_t st) {
   // Persistent grid: as many workgroups as fit on the device at once.
+  auto kern = self_plan ? mfma_prep_kernel<DK, DV, true> : mfma_prep_kernel<DK, DV, false>;
   int dev = 0, cus = 0, per_cu = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, mfma_prep_kernel<DK, DV>, 256, 0) !=
-          hipSuccess)
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, 256, 0) != hipSuccess)
     return hipErrorInvalidValue;
   const int64_t items = max_chunks * s.HV;
   const int64_t grid = std::min<int64_t>(items, (int64_t)std::max(cus, 1) * std::max(per_cu, 1));
-  hipLaunchKernelGGL((mfma_prep_kernel<DK, DV>), dim3((unsigned)grid), dim3(256), 0, st,
-                     (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, cu, off, cseq,
-                     ga, gb, A_log, dt_bias, (int)s.B, s.H, s.HV, w, u, aqk, eg, kf, qf);
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), 0, st, (const uint16_t*)q,
+                     (const uint16_t*)k, (const uint16_t*)v, cu, off, cseq, ga, gb, A_log,
+                     dt_bias, (int)s.B, s.H, s.HV, w, u, aqk, eg, kf, qf);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_mfma_prep(const void* q, const void* k, const void* v,
-                            const int64_t* cu_seqlens, const int32_t* chunk_off,
-                            const int32_t* chunk_seq, const float* a, const float* b,
-                            const float* A_log, const float* dt_bias,
+                            const int64_t* cu_seqlens, int32_t* chunk_off,
+                            const int32_t* chunk_seq, bool self_plan, const float* a,
+                            const float* b, const float* A_log, const float* dt_bias,
                             const Shape& s, int64_t max_chunks, void* w, void* u, void* aqk,
                             float* eg, void* kf, void* qf, hipStream_t st) {
+  if (self_plan && s.B > kMaxSelfPlanRequests) return hipErrorInvalidValue;
   _Float16* W = (_Float16*)w;
   _Float16* U = (_Float16*)u;
 #define GDN_PREP_CASE(DKv, DVv)                                                               \
   if (s.dk == DKv && s.dv == DVv)                                                             \
-    return launch_prep_t<DKv, DVv>(q, k, v, cu_seqlens, chunk_off, chunk_seq, a, b, A_log,    \
+    return launch_prep_t<DKv, DVv>(q, k, v, cu_seqlens, chunk_off, chunk_seq, self_plan, a, b, \
+                                   A_log,                                                      \
                                    dt_bias, s,                                                 \
                                    max_chunks, W, U, (_Float16*)aqk, eg, (_Float16*)kf,      \
                                    (_Float16*)qf, st);

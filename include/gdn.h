@@ -96,9 +96,10 @@ gdn_status_t gdn_prefill_fwd(const void* q, const void* k, const void* v, const 
 
 /* Stages of one call, in launch order, for gdn_prefill_fwd_events. */
 #define GDN_NUM_STAGES 3 /* 0: chunk table (and, for fp32 inputs, the gates and log
-                            cumulative decay); 1: chunk prep (for bf16 inputs including the
-                            gates; Grams, the one inverse, W<- and U~); 2: state pass +
-                            outputs */
+                            cumulative decay; for bf16 inputs of at most 64 requests the
+                            chunk prep forms the table and this stage launches nothing);
+                            1: chunk prep (for bf16 inputs including the gates; Grams, the
+                            one inverse, W<- and U~); 2: state pass + outputs */
 
 /* gdn_prefill_fwd with timing marks: stage_events points to GDN_NUM_STAGES + 1
  * hipEvent_t handles created by the caller on the current device; event i is recorded

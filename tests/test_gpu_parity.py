@@ -116,6 +116,22 @@ def test_random_shapes(case):
     compare(p, out, pool_gpu, oracle.prefill(p))
 
 
+@pytest.mark.parametrize("B", [64, 65])
+def test_chunk_table_switch(B):
+    """Up to 64 requests the bf16 chunk prep forms the chunk table itself; from 65 on a
+    separate kernel does. Both sides of the switch, with empty requests first, in the
+    middle and last, partial chunks, and a shuffled pool."""
+    rng = np.random.default_rng(900 + B)
+    lengths = [int(x) for x in rng.integers(1, 200, B)]
+    for i in (0, B // 2, B - 1):
+        lengths[i] = 0
+    pool = B + 3
+    p = gdn_synth.make_problem(900 + B, lengths, 2, 4, 128, 128, dtype="bf16", pool=pool,
+                               cache_indices=list(rng.permutation(pool)[:B]), state_std=0.1)
+    out, pool_gpu, _ = run_gpu(p, f"table-switch-{B}")
+    compare(p, out, pool_gpu, oracle.prefill(p))
+
+
 def test_all_requests_empty_is_a_no_op():
     import torch
     p = gdn_synth.make_problem(35, [0, 0, 0], 1, 1, 64, 64, dtype="bf16", state_std=1.0)

@@ -291,3 +291,61 @@ def decode_workload() -> Problem:
     perm = seeded_permutation(seed, TID_PERM, 512)
     return make_decode_problem(seed, 512, 16, 32, 128, 128, pool=512, cache_indices=perm,
                                state_std=0.1, name="decode_batch_bf16")
+
+
+# ---------------------------------------------------------------- Promote update scan
+TID_PK, TID_PV, TID_PBETA, TID_PW, TID_PGAMMA, TID_PM = range(21, 27)
+
+# The Promote workload: batch 8 x 16 heads, dk = dv = 128, 64 pairs per firing (a level's
+# query count), 64 firings (a level firing every second 64-token chunk of an 8192-token
+# sequence), bf16 keys and values, every firing's state kept.
+PROMOTE_WORKLOAD = ("promote scan bf16: BH=8x16, F=64 firings x n=64 pairs, dk=dv=128, "
+                    "states kept")
+
+
+@dataclasses.dataclass
+class PromoteProblem:
+    """One Promote update scan's inputs. K [BH, F, n, dk] (rows of unit length before
+    rounding), V [BH, F, n, dv]: uint16 bf16 bit patterns for "bf16", float32 for "f32".
+    beta, w [BH, F, n] in (0, 1); gamma [BH, F, dk] <= 0; M0 [BH, dk, dv] fp32."""
+    dtype: str
+    K: np.ndarray
+    V: np.ndarray
+    beta: np.ndarray
+    w: np.ndarray
+    gamma: np.ndarray
+    M0: np.ndarray
+    seed: int = 0
+
+    @property
+    def shape(self):
+        BH, F, n, dk = self.K.shape
+        return BH, F, n, dk, self.V.shape[3]
+
+    def values_f32(self, name: str) -> np.ndarray:
+        x = getattr(self, name)
+        return bf16_bits_to_f32(x) if self.dtype == "bf16" else x
+
+
+def make_promote_problem(seed: int, BH: int, F: int, n: int, dk: int, dv: int,
+                         dtype: str = "bf16", gamma_max: float = 0.5,
+                         m_std: float = 0.5) -> PromoteProblem:
+    """Keys: normal rows scaled to unit length in fp64, then rounded; values N(0, 1);
+    beta, w ~ U(0, 1); gamma ~ -U(0, gamma_max) (decay factors in [e^-gamma_max, 1]);
+    M0 ~ N(0, m_std^2)."""
+    assert dtype in ("bf16", "f32")
+    kr = normal(seed, TID_PK, BH * F * n * dk).reshape(BH, F, n, dk)
+    kr /= np.sqrt((kr * kr).sum(axis=-1, keepdims=True))
+    k32 = kr.astype(np.float32)
+    K = f32_to_bf16_bits(k32).reshape(k32.shape) if dtype == "bf16" else k32
+    V = _draw(seed, TID_PV, (BH, F, n, dv), dtype)
+    beta = uniform(seed, TID_PBETA, BH * F * n).astype(np.float32).reshape(BH, F, n)
+    w = uniform(seed, TID_PW, BH * F * n).astype(np.float32).reshape(BH, F, n)
+    gamma = (-gamma_max * uniform(seed, TID_PGAMMA, BH * F * dk)).astype(np.float32)
+    M0 = _draw(seed, TID_PM, (BH, dk, dv), "f32", std=m_std)
+    return PromoteProblem(dtype=dtype, K=K, V=V, beta=beta, w=w,
+                          gamma=gamma.reshape(BH, F, dk), M0=M0, seed=seed)
+
+
+def promote_workload() -> PromoteProblem:
+    return make_promote_problem(1200, 128, 64, 64, 128, 128, dtype="bf16")

@@ -30,7 +30,8 @@ GDN_NUM_STAGES = 3
 STAGE_NAMES = ("gate", "chunk_prep", "state")
 
 EXPORTED = ("gdn_prefill_workspace_size", "gdn_prefill_fwd", "gdn_prefill_fwd_events",
-            "gdn_decode_fwd", "gdn_validate_inputs", "gdn_status_str", "gdn_version")
+            "gdn_decode_fwd", "gdn_promote_scan", "gdn_validate_inputs", "gdn_status_str",
+            "gdn_version")
 
 
 class GdnProblem(ctypes.Structure):
@@ -43,6 +44,18 @@ class GdnProblem(ctypes.Structure):
         ("head_v", ctypes.c_int32),
         ("pool_size", ctypes.c_int64),
         ("qkv_dtype", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+    ]
+
+
+class GdnPromoteProblem(ctypes.Structure):
+    _fields_ = [
+        ("scans", ctypes.c_int64),
+        ("firings", ctypes.c_int32),
+        ("pairs", ctypes.c_int32),
+        ("head_k", ctypes.c_int32),
+        ("head_v", ctypes.c_int32),
+        ("kv_dtype", ctypes.c_int32),
         ("reserved", ctypes.c_int32),
     ]
 
@@ -77,6 +90,8 @@ def load_library(path: str = LIB_PATH):
     L.gdn_prefill_fwd_events.argtypes = L.gdn_prefill_fwd.argtypes + [P]
     L.gdn_decode_fwd.restype = ctypes.c_int
     L.gdn_decode_fwd.argtypes = [P, P, P, P, P, P, P, P, P, P, PP, P]
+    L.gdn_promote_scan.restype = ctypes.c_int
+    L.gdn_promote_scan.argtypes = [P, P, P, P, P, P, P, ctypes.POINTER(GdnPromoteProblem), P]
     L.gdn_validate_inputs.restype = ctypes.c_int
     L.gdn_validate_inputs.argtypes = [P, P, PP, P]
     L.gdn_status_str.restype = ctypes.c_char_p
@@ -266,6 +281,49 @@ def gdn_decode_fwd(q, k, v, a, b, A_log, dt_bias, state_pool, cache_indices, out
     if rc != GDN_OK:
         raise GdnError(rc, "gdn_decode_fwd")
     return out
+
+
+def gdn_promote_scan(K, V, beta, w, gamma, M, keep_states: bool = True, states=None,
+                     stream=None):
+    """The Promote update scan on device tensors; updates ``M`` in place and returns the
+    per-firing states [scans, F, dk, dv] fp32 (or None when keep_states is False).
+
+    K [scans, F, n, dk] and V [scans, F, n, dv] bf16; beta, w [scans, F, n] fp32;
+    gamma [scans, F, dk] fp32; M [scans, dk, dv] fp32."""
+    import torch
+    dev = K.device
+    if dev.type != "cuda":
+        raise ValueError("gdn_promote_scan runs on a HIP device; tensors are on " + str(dev))
+    _need(K, "K", ndim=4, device=dev)
+    _need(V, "V", dtype=K.dtype, ndim=4, device=dev)
+    BH, F, n, dk = K.shape
+    dv = V.shape[3]
+    if tuple(V.shape[:3]) != (BH, F, n):
+        raise ValueError(f"V must be [{BH}, {F}, {n}, dv], got {tuple(V.shape)}")
+    for t, name in ((beta, "beta"), (w, "w")):
+        _need(t, name, dtype=torch.float32, ndim=3, device=dev)
+        if tuple(t.shape) != (BH, F, n):
+            raise ValueError(f"{name} must be [{BH}, {F}, {n}]")
+    _need(gamma, "gamma", dtype=torch.float32, ndim=3, device=dev)
+    if tuple(gamma.shape) != (BH, F, dk):
+        raise ValueError(f"gamma must be [{BH}, {F}, {dk}]")
+    _need(M, "M", dtype=torch.float32, ndim=3, device=dev)
+    if tuple(M.shape) != (BH, dk, dv):
+        raise ValueError(f"M must be [{BH}, {dk}, {dv}]")
+    if keep_states and states is None:
+        states = torch.empty((BH, F, dk, dv), dtype=torch.float32, device=dev)
+    if states is not None:
+        _need(states, "states", dtype=torch.float32, ndim=4, device=dev)
+        if tuple(states.shape) != (BH, F, dk, dv):
+            raise ValueError(f"states must be [{BH}, {F}, {dk}, {dv}]")
+    prob = GdnPromoteProblem(int(BH), int(F), int(n), int(dk), int(dv), _dtype_code(K), 0)
+    st = (stream or torch.cuda.current_stream(dev)).cuda_stream
+    rc = load_library().gdn_promote_scan(_ptr(K), _ptr(V), _ptr(beta), _ptr(w), _ptr(gamma),
+                                         _ptr(M), _ptr(states), ctypes.byref(prob),
+                                         ctypes.c_void_p(st))
+    if rc != GDN_OK:
+        raise GdnError(rc, "gdn_promote_scan")
+    return states
 
 
 def gdn_validate_inputs(cu_seqlens, cache_indices, prob: GdnProblem, stream=None) -> int:

@@ -1,6 +1,6 @@
 // C ABI of libgdn (declared in include/gdn.h): host-side argument checks, the
 // workspace layout and the launch sequence plan -> gate -> chunk prep -> state pass of
-// the prefill, and the one-kernel decode step.
+// the prefill, the one-kernel decode step and the Promote update scan.
 #include <string.h>
 
 #include <vector>
@@ -80,7 +80,7 @@ using namespace gdn;
 
 extern "C" {
 
-int32_t gdn_version(void) { return 200; }
+int32_t gdn_version(void) { return 300; }
 
 const char* gdn_status_str(gdn_status_t st) {
   switch (st) {
@@ -220,6 +220,31 @@ gdn_status_t gdn_decode_fwd(const void* q, const void* k, const void* v, const f
   if (decode_blocks(s) > 0x7FFFFFFF) return GDN_ERR_UNSUPPORTED;
   if (launch_decode(q, k, v, a, b, A_log, dt_bias, cache_indices, s, state_pool, out,
                     (hipStream_t)stream) != hipSuccess)
+    return GDN_ERR_HIP;
+  return GDN_OK;
+}
+
+gdn_status_t gdn_promote_scan(const void* K, const void* V, const float* beta, const float* w,
+                              const float* gamma, float* M, float* states,
+                              const gdn_promote_problem_t* prob, void* stream) {
+  if (!prob || prob->reserved != 0) return GDN_ERR_INVALID_ARG;
+  if (prob->scans < 0 || prob->firings < 0 || prob->pairs <= 0 || prob->head_k <= 0 ||
+      prob->head_v <= 0)
+    return GDN_ERR_INVALID_ARG;
+  if (prob->kv_dtype != GDN_DTYPE_F32 && prob->kv_dtype != GDN_DTYPE_BF16)
+    return GDN_ERR_INVALID_ARG;
+  if (prob->kv_dtype != GDN_DTYPE_BF16) return GDN_ERR_UNSUPPORTED;
+  if (prob->head_k != 64 && prob->head_k != 128) return GDN_ERR_UNSUPPORTED;
+  if (prob->head_v % 64 != 0 || prob->head_v > 256) return GDN_ERR_UNSUPPORTED;
+  if (prob->pairs % 16 != 0 || prob->pairs > prob->head_k) return GDN_ERR_UNSUPPORTED;
+  if (prob->scans > ((int64_t)1 << 28)) return GDN_ERR_UNSUPPORTED;
+  if (prob->scans == 0) return GDN_OK;
+  if (!M) return GDN_ERR_INVALID_ARG;
+  if (prob->firings > 0 && (!K || !V || !beta || !w || !gamma)) return GDN_ERR_INVALID_ARG;
+  for (const void* ptr : {K, V})  // 16-byte vector loads
+    if (((uintptr_t)ptr & 15) != 0) return GDN_ERR_INVALID_ARG;
+  PromoteShape s{prob->scans, prob->firings, prob->pairs, prob->head_k, prob->head_v};
+  if (launch_promote(s, K, V, beta, w, gamma, M, states, (hipStream_t)stream) != hipSuccess)
     return GDN_ERR_HIP;
   return GDN_OK;
 }

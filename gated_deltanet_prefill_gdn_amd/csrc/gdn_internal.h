@@ -86,4 +86,13 @@ hipError_t launch_decode(const void* q, const void* k, const void* v, const floa
                          const int64_t* cache_indices, const Shape& s, float* state_pool,
                          void* out, hipStream_t st);
 
+// Promote update scan: shape and launcher (bf16 keys and values).
+struct PromoteShape {
+  int64_t BH;  // independent scans
+  int F, n, dk, dv;
+};
+hipError_t launch_promote(const PromoteShape& s, const void* K, const void* V, const float* beta,
+                          const float* w, const float* gamma, float* M, float* states,
+                          hipStream_t st);
+
 }  // namespace gdn

@@ -84,5 +84,37 @@ __device__ __forceinline__ half8 cat(half4 a, half4 b) {
   return r;
 }
 
+// Row fragment in kperm order: row `row`, elements col0 + kperm(g, 0..7).
+__device__ __forceinline__ u32x4 row_frag_kperm(const uint16_t* base, int ld, int row, int col0,
+                                                int g) {
+  const uint16_t* p = base + row * ld + col0 + 4 * g;
+  const u32x2 lo = *reinterpret_cast<const u32x2*>(p);
+  const u32x2 hi = *reinterpret_cast<const u32x2*>(p + 16);
+  u32x4 r;
+  r[0] = lo[0]; r[1] = lo[1]; r[2] = hi[0]; r[3] = hi[1];
+  return r;
+}
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+// Column fragment of a row-major LDS tile: column col0 + m, rows 32s + kperm(g, 0..7),
+// from two transpose reads. Within a group of 16 lanes, ds_read_b64_tr_b16 hands lane
+// 4a + c element c of the 8-byte chunks that lanes a, a + 4, a + 8, a + 12 address, so
+// lane (a + 4j) points at row 4g + j (+ 16), columns col0 + 4a .. col0 + 4a + 3.
+__device__ __forceinline__ u32x4 col_frag_tr(const uint16_t* base, int ld, int col0, int s, int g,
+                                             int m) {
+  const int a = m & 3, j = m >> 2;
+  const uint16_t* p = base + (32 * s + 4 * g + j) * ld + col0 + 4 * a;
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p);
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 16 * ld));
+  u32x4 r;
+  r[0] = (uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16);
+  r[1] = (uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16);
+  r[2] = (uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16);
+  r[3] = (uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16);
+  return r;
+}
+
 }  // namespace mfma
 }  // namespace gdn

@@ -1,6 +1,6 @@
 /*
- * libgdn -- Gated DeltaNet chunkwise prefill forward (and the decode step that follows
- * it) on MI355X (gfx950).
+ * libgdn -- Gated DeltaNet chunkwise prefill forward (with the decode step that follows
+ * it, and the Promote update scan of the nested variant) on MI355X (gfx950).
  *
  * The operation (pymllm gdn_chunkwise page, "gdn_extend_chunkwise", Module
  * Contents; the recurrence is the state-transition equation of "Simple math to
@@ -133,6 +133,38 @@ gdn_status_t gdn_decode_fwd(const void* q, const void* k, const void* v, const f
                             const float* b, const float* A_log, const float* dt_bias,
                             float* state_pool, const int64_t* cache_indices, void* out,
                             const gdn_problem_t* prob, void* stream);
+
+/* Shape of one Promote update scan (host struct). */
+typedef struct {
+  int64_t scans;    /* independent (batch, head) scans                                 */
+  int32_t firings;  /* F: firings per scan                                             */
+  int32_t pairs;    /* n: pairs per firing, a multiple of 16, at most head_k           */
+  int32_t head_k;   /* dk: 64 or 128                                                   */
+  int32_t head_v;   /* dv: 64, 128 or 256                                              */
+  int32_t kv_dtype; /* gdn_dtype_t of K and V: GDN_DTYPE_BF16 (fp32 is unsupported)    */
+  int32_t reserved; /* must be 0                                                       */
+} gdn_promote_problem_t;
+
+/* The update scan of one level of the nested model (awehrs.io "NRM training kernels",
+ * section General implementation, the Promote algorithm; section Kernel, a scan over
+ * firings). Each scan holds a memory M (dk x dv, fp32) updated in place; at firing f its
+ * n pairs are written at once, all against the memory as it stood before the firing:
+ *   M <- diag(exp(gamma_f)) M;  M <- M - K_f^T (beta_f o K_f) M;  M <- M + K_f^T (w_f o V_f)
+ * (decay, erase at the new addresses, write; o scales the pairs' rows).
+ * Layouts (dense, row-major, DEVICE pointers):
+ *   K      [scans, F, n, dk]  bf16, unit rows (the probe's normalised write keys)
+ *   V      [scans, F, n, dv]  bf16
+ *   beta, w [scans, F, n]     fp32 erase and write gates
+ *   gamma  [scans, F, dk]     fp32 log-decay, one entry per key row
+ *   M      [scans, dk, dv]    fp32, in: the memory before the first firing; out: after the last
+ *   states [scans, F, dk, dv] fp32 out: the memory after each firing; NULL to skip
+ * K and V 16-byte aligned. Products on matrix cores with fp16 operands (the memory and
+ * U = w o V - beta o K M rounded to fp16, keys converted exactly up to fp16 range) and fp32
+ * accumulation; the memory itself stays fp32. No workspace, no allocation, asynchronous on
+ * `stream`; scans == 0 is a no-op. Errors: host checks before any launch. */
+gdn_status_t gdn_promote_scan(const void* K, const void* V, const float* beta, const float* w,
+                              const float* gamma, float* M, float* states,
+                              const gdn_promote_problem_t* prob, void* stream);
 
 /* Debug check of the device-array preconditions: cu_seqlens[0] == 0, non-decreasing,
  * cu_seqlens[B] == N; cache_indices distinct and in [0, pool). Copies both arrays to

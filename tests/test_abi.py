@@ -123,6 +123,36 @@ def test_decode_empty_batch_is_a_no_op():
     assert call_decode(prob(N=0, B=0, pool=0), nonnull=False) == gdn.GDN_OK
 
 
+def call_promote(scans=4, F=8, n=64, dk=128, dv=128, dtype=gdn.GDN_DTYPE_BF16, reserved=0,
+                 nonnull=True, misalign=0):
+    lib = gdn.load_library()
+    P = ctypes.c_void_p
+    x = P(4096) if nonnull else P(0)
+    p = gdn.GdnPromoteProblem(scans, F, n, dk, dv, dtype, reserved)
+    return lib.gdn_promote_scan(P(4096 + misalign), x, x, x, x, x, x, ctypes.byref(p), P(0))
+
+
+def test_promote_error_paths_return_before_launch():
+    assert call_promote(dtype=5) == gdn.GDN_ERR_INVALID_ARG
+    assert call_promote(reserved=1) == gdn.GDN_ERR_INVALID_ARG
+    assert call_promote(scans=-1) == gdn.GDN_ERR_INVALID_ARG
+    assert call_promote(n=0) == gdn.GDN_ERR_INVALID_ARG
+    assert call_promote(dtype=gdn.GDN_DTYPE_F32) == gdn.GDN_ERR_UNSUPPORTED
+    assert call_promote(dk=256) == gdn.GDN_ERR_UNSUPPORTED
+    assert call_promote(dv=96) == gdn.GDN_ERR_UNSUPPORTED
+    assert call_promote(n=24) == gdn.GDN_ERR_UNSUPPORTED          # not a multiple of 16
+    assert call_promote(dk=64, n=80) == gdn.GDN_ERR_UNSUPPORTED   # more pairs than key rows
+    assert call_promote(nonnull=False) == gdn.GDN_ERR_INVALID_ARG
+    assert call_promote(misalign=8) == gdn.GDN_ERR_INVALID_ARG    # K not 16-byte aligned
+    lib = gdn.load_library()
+    assert lib.gdn_promote_scan(None, None, None, None, None, None, None, None,
+                                None) == gdn.GDN_ERR_INVALID_ARG
+
+
+def test_promote_empty_is_a_no_op():
+    assert call_promote(scans=0, nonnull=False) == gdn.GDN_OK
+
+
 def test_binding_rejects_cpu_tensors():
     torch = pytest.importorskip("torch")
     z = torch.zeros(4, 1, 64)

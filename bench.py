@@ -7,8 +7,10 @@ inputs resident in HBM. Prints one JSON line.
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 
 With ``--op decode`` a step is instead one gdn_decode_fwd call over the decode workload
-(512 requests x 1 token, H = 16, HV = 32, dk = dv = 128, bf16, 1 GiB of state), and the
-JSON line reports that.
+(512 requests x 1 token, H = 16, HV = 32, dk = dv = 128, bf16, 1 GiB of state), and with
+``--op promote`` one gdn_promote_scan call over the Promote workload (128 scans x 64
+firings x 64 pairs, dk = dv = 128, bf16, every firing's state kept); the JSON line then
+reports that call.
 """
 from __future__ import annotations
 
@@ -72,17 +74,21 @@ def stage_bytes(p, s_qkv: int, s_ws: int, n_chunks: int):
 
 
 DECODE_SOURCES = ("gdn_decode.hip", "gdn_internal.h")
+PROMOTE_SOURCES = ("gdn_promote.hip", "gdn_internal.h", "gdn_mfma.h")
 
 
 def kernel_source_hash(kind: str = "prefill") -> str:
     """sha256[:16] over the kernel sources a measurement depends on: for "prefill" every
-    .hip / .h file of csrc except the decode kernel's, for "decode" DECODE_SOURCES."""
+    .hip / .h file of csrc except the decode and Promote kernels' own files, for "decode"
+    DECODE_SOURCES, for "promote" PROMOTE_SOURCES."""
     csrc = os.path.join(ROOT, "gated_deltanet_prefill_gdn_amd", "csrc")
     if kind == "decode":
         files = sorted(DECODE_SOURCES)
+    elif kind == "promote":
+        files = sorted(PROMOTE_SOURCES)
     else:
-        files = sorted(f for f in os.listdir(csrc)
-                       if f.endswith((".hip", ".h")) and f != "gdn_decode.hip")
+        files = sorted(f for f in os.listdir(csrc) if f.endswith((".hip", ".h"))
+                       and f not in ("gdn_decode.hip", "gdn_promote.hip"))
     h = hashlib.sha256()
     for f in files:
         h.update(f.encode())
@@ -299,9 +305,143 @@ def bench_decode(args):
     print(json.dumps(res), flush=True)
 
 
+PROMOTE_METRIC = "Promote update scan pairs/sec (decay, erase, write per firing), dk=dv=128"
+
+
+def promote_bytes(p, s_kv: int) -> int:
+    """Algorithmic HBM bytes of one scan call: keys and values once, the gates and the
+    log-decay, the memory in and out, and every firing's state written (fp32)."""
+    BH, F, n, dk, dv = p.shape
+    return (BH * F * n * (dk + dv) * s_kv + BH * F * (2 * n + dk) * 4
+            + 2 * BH * dk * dv * 4 + BH * F * dk * dv * 4)
+
+
+def promote_cpu_baseline(p, n_scans: int = 16, reps: int = 3):
+    """The Promote oracle (fp64 numpy) as it stands on the first n_scans scans; the median
+    wall time gives pairs/s."""
+    import numpy as np
+    from oracle.promote import promote_scan
+    BH, F, n, dk, dv = p.shape
+    sel = slice(0, n_scans)
+    args = (p.M0[sel], p.values_f32("K")[sel], p.values_f32("V")[sel], p.beta[sel], p.w[sel],
+            p.gamma[sel])
+    walls = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        promote_scan(*args)
+        walls.append(time.perf_counter() - t0)
+    dt = float(np.median(walls))
+    return {"value": n_scans * F * n / dt, "unit": "pairs/s", "cores": _blas_threads(),
+            "kind": "oracle",
+            "sample": f"{n_scans} of the {BH} scans, all {F} firings, fp64 numpy (BLAS matrix "
+                      f"products), median of {reps} runs, {dt:.3f} s wall each"}
+
+
+def _blas_threads() -> int:
+    """Threads numpy's BLAS may use here (OMP_NUM_THREADS if set, else the usable cores)."""
+    env = os.environ.get("OMP_NUM_THREADS")
+    if env and env.isdigit():
+        return int(env)
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+def bench_promote(args):
+    import numpy as np
+    import torch
+
+    import gdn_synth
+    import gated_deltanet_prefill_gdn_amd as gdn
+
+    p = gdn_synth.promote_workload()
+    BH, F, n, dk, dv = p.shape
+    dev = torch.device("cuda:0")
+
+    def t(x, dt=None):
+        x = torch.from_numpy(np.ascontiguousarray(x))
+        return (x.view(dt) if dt is not None else x).to(dev)
+
+    K = t(p.K.view(np.int16), torch.bfloat16)
+    V = t(p.V.view(np.int16), torch.bfloat16)
+    beta, w, gamma = t(p.beta), t(p.w), t(p.gamma)
+    M = t(p.M0.copy())
+    states = torch.empty((BH, F, dk, dv), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        gdn.gdn_promote_scan(K, V, beta, w, gamma, M, states=states, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    hip = Hip()
+    rec = hip.lib.hipEventRecord
+    rec.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    evs = [(hip.event(), hip.event()) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for e0, e1 in evs:
+        rec(ctypes.c_void_p(e0), ctypes.c_void_p(stream.cuda_stream))
+        step()
+        rec(ctypes.c_void_p(e1), ctypes.c_void_p(stream.cuda_stream))
+    torch.cuda.synchronize()
+    events_ms = float(np.mean([hip.elapsed_ms(e0, e1) for e0, e1 in evs]))
+    for e0, e1 in evs:
+        hip.destroy(e0)
+        hip.destroy(e1)
+    pair_ms = hip.empty_pair_ms(stream.cuda_stream)
+    launch_ms = events_ms - pair_ms if events_ms > 2 * pair_ms else events_ms
+    if args.copy_calibration:
+        src = torch.empty(512 << 20, dtype=torch.uint8, device=dev).fill_(3)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    nbytes = promote_bytes(p, 2)
+    flops = 4.0 * BH * F * n * dk * dv
+    achieved = nbytes / (launch_ms * 1e-3) / 1e9
+    src_hash = kernel_source_hash("promote")
+    res = {
+        "metric": PROMOTE_METRIC,
+        "value": BH * F * n / (ms_per_step * 1e-3),
+        "unit": "pairs/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded SplitMix64/Box-Muller, seed 1200)",
+        "config": {"workload": gdn_synth.PROMOTE_WORKLOAD, "global_batch": BH, "seq_len": F,
+                   "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "hbm", "kernel": "promote_scan_kernel", "achieved": achieved,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": stored_traffic("promote_scan_kernel", src_hash),
+                     "algorithmic_bytes_per_launch": nbytes, "avg_launch_ms": launch_ms,
+                     "avg_launch_ms_events": events_ms, "event_pair_ms": pair_ms},
+        "effective": {"tflops": flops / (launch_ms * 1e-3) / 1e12,
+                      "frac_mfma_bf16": flops / (launch_ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS,
+                      "algorithmic_flops": flops},
+        "kernel_source_hash": src_hash,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = promote_cpu_baseline(p)
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
-    ap.add_argument("--op", choices=("prefill", "decode"), default="prefill",
+    ap.add_argument("--op", choices=("prefill", "decode", "promote"), default="prefill",
                     help="the call a step times (default: the prefill forward)")
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
@@ -318,6 +458,9 @@ def main():
         sys.exit(2)
     if args.op == "decode":
         bench_decode(args)
+        return
+    if args.op == "promote":
+        bench_promote(args)
         return
 
     import numpy as np

@@ -29,7 +29,8 @@ namespace gdn {
 namespace {
 
 using namespace mfma;
-constexpr int kPromoteCols = 64;  // value columns per workgroup (16 per wave)
+constexpr int kPromoteCols = 64;                     // value columns per workgroup
+constexpr int kPromoteThreads = 64 * (kPromoteCols / 16);  // one wave per 16 columns
 
 template <int DK, int NP>
 struct PromoteSmem {
@@ -48,7 +49,7 @@ __device__ __forceinline__ uint16_t f32_to_f16_bits(float x) {
 }
 
 template <int DK, int NP>
-__global__ __launch_bounds__(256) void promote_scan_kernel(
+__global__ __launch_bounds__(kPromoteThreads) void promote_scan_kernel(
     const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const float* __restrict__ beta, const float* __restrict__ wg, const float* __restrict__ gamma,
     int64_t BH, int F, int n, int DV, float* __restrict__ M, float* __restrict__ states) {
@@ -58,8 +59,10 @@ __global__ __launch_bounds__(256) void promote_scan_kernel(
   constexpr int NPT = NP / 16;   // pair tiles
   constexpr int NPS = NP / 32;   // 32-pair steps (B operand of the update)
   constexpr int KPC = DK / 8;    // 16-byte pieces per key row
-  constexpr int KPT = (NP * KPC + 255) / 256;             // ... per thread
-  constexpr int VPT = (NP * (kPromoteCols / 8) + 255) / 256;
+  constexpr int NT = kPromoteThreads;
+  constexpr int KPT = (NP * KPC + NT - 1) / NT;           // ... per thread
+  constexpr int VPT = (NP * (kPromoteCols / 8) + NT - 1) / NT;
+  static_assert(NP <= NT && DK <= NT, "one thread per pair and per key row");
   __shared__ PromoteSmem<DK, NP> sm;
 
   const int nvb = DV / kPromoteCols;
@@ -80,14 +83,14 @@ __global__ __launch_bounds__(256) void promote_scan_kernel(
     const uint16_t* vbp = V + bf * (int64_t)n * DV + vb * kPromoteCols;
 #pragma unroll
     for (int u = 0; u < KPT; ++u) {
-      const int e = tid + 256 * u, row = e / KPC, c8 = (e % KPC) * 8;
+      const int e = tid + NT * u, row = e / KPC, c8 = (e % KPC) * 8;
       u32x4 z = {0u, 0u, 0u, 0u};
       if (row < n) z = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kb + (int64_t)row * DK + c8));
       kr[u] = z;
     }
 #pragma unroll
     for (int u = 0; u < VPT; ++u) {
-      const int e = tid + 256 * u, row = e / (kPromoteCols / 8), c8 = (e % (kPromoteCols / 8)) * 8;
+      const int e = tid + NT * u, row = e / (kPromoteCols / 8), c8 = (e % (kPromoteCols / 8)) * 8;
       u32x4 z = {0u, 0u, 0u, 0u};
       if (row < n) z = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vbp + (int64_t)row * DV + c8));
       vr[u] = z;
@@ -100,7 +103,7 @@ __global__ __launch_bounds__(256) void promote_scan_kernel(
   auto stage = [&](typename PromoteSmem<DK, NP>::Buf& B) {
 #pragma unroll
     for (int u = 0; u < KPT; ++u) {
-      const int e = tid + 256 * u, row = e / KPC, c8 = (e % KPC) * 8;
+      const int e = tid + NT * u, row = e / KPC, c8 = (e % KPC) * 8;
       if (row < NP) {
         u32x4 h;
 #pragma unroll
@@ -114,7 +117,7 @@ __global__ __launch_bounds__(256) void promote_scan_kernel(
     }
 #pragma unroll
     for (int u = 0; u < VPT; ++u) {
-      const int e = tid + 256 * u, row = e / (kPromoteCols / 8), c8 = (e % (kPromoteCols / 8)) * 8;
+      const int e = tid + NT * u, row = e / (kPromoteCols / 8), c8 = (e % (kPromoteCols / 8)) * 8;
       if (row < NP) *reinterpret_cast<u32x4*>(&B.vb[row * kPromoteCols + c8]) = vr[u];
     }
     if (tid < NP) {
@@ -200,7 +203,7 @@ hipError_t launch_promote_t(const PromoteShape& s, const void* K, const void* V,
                             float* states, hipStream_t st) {
   const int nvb = s.dv / kPromoteCols;
   const int64_t blocks = (s.BH + 7) / 8 * 8 * nvb;
-  hipLaunchKernelGGL((promote_scan_kernel<DK, NP>), dim3((unsigned)blocks), dim3(256), 0, st,
+  hipLaunchKernelGGL((promote_scan_kernel<DK, NP>), dim3((unsigned)blocks), dim3(kPromoteThreads), 0, st,
                      (const uint16_t*)K, (const uint16_t*)V, beta, w, gamma, s.BH, s.F, s.n,
                      s.dv, M, states);
   return hipGetLastError();

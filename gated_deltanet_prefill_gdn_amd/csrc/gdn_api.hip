@@ -241,7 +241,7 @@ gdn_status_t gdn_promote_scan(const void* K, const void* V, const float* beta, c
   if (prob->scans == 0) return GDN_OK;
   if (!M) return GDN_ERR_INVALID_ARG;
   if (prob->firings > 0 && (!K || !V || !beta || !w || !gamma)) return GDN_ERR_INVALID_ARG;
-  for (const void* ptr : {K, V})  // 16-byte vector loads
+  for (const void* ptr : {K, V, (const void*)states})  // 16-byte vector loads and stores
     if (((uintptr_t)ptr & 15) != 0) return GDN_ERR_INVALID_ARG;
   PromoteShape s{prob->scans, prob->firings, prob->pairs, prob->head_k, prob->head_v};
   if (launch_promote(s, K, V, beta, w, gamma, M, states, (hipStream_t)stream) != hipSuccess)

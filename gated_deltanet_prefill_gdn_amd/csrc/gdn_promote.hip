@@ -12,11 +12,14 @@
 // All pairs act on M as it stood before the firing (no order among them), so unlike the
 // chunked delta rule there is no triangular solve: two products per firing.
 //
-// Work split: one workgroup of four waves per (scan, 64 value columns); wave c holds
-// columns 16 c .. 16 c + 15 of M, all dk rows, as fp32 MFMA D tiles for the whole scan.
+// Work split: one workgroup per (scan, 64 value columns) with four compute waves and one
+// store wave. Compute wave c holds columns 16 c .. 16 c + 15 of M, all dk rows, as fp32
+// MFMA D tiles for the whole scan, and after each firing writes them to an LDS tile; the
+// store wave copies that tile to `states` with row-contiguous 16-byte stores during the
+// next firing (two barriers per firing), so the compute waves issue no global store.
 // Per firing every workgroup stages K (converted to fp16), its V columns, the gates and
 // e^gamma in LDS (double-buffered: the next firing's global loads are in flight while
-// this one computes; one barrier per firing). The fp16 copy of a wave's M', two stacked D
+// this one computes). The fp16 copy of a wave's M', two stacked D
 // tiles per 32 key rows, is exactly the B operand of P = K M'; P's D tiles, two stacked
 // per 32 pairs, become the B operand of the update once turned into U. K is the A
 // operand of both products: read by rows (kperm order) for P and by columns (LDS
@@ -29,12 +32,14 @@ namespace gdn {
 namespace {
 
 using namespace mfma;
-constexpr int kPromoteCols = 64;                     // value columns per workgroup
-constexpr int kPromoteThreads = 64 * (kPromoteCols / 16);  // one wave per 16 columns
+constexpr int kPromoteCols = 64;                       // value columns per workgroup
+constexpr int kComputeWaves = kPromoteCols / 16;        // one wave per 16 columns
+constexpr int kPromoteThreads = 64 * (kComputeWaves + 1);  // and one store wave
 
 template <int DK, int NP>
 struct PromoteSmem {
   static constexpr int SK = DK + 16;  // row stride (fp16) of the key tile: spreads banks
+  static constexpr int SS = kPromoteCols + 4;  // row stride (fp32) of the state tile
   struct Buf {
     uint16_t kh[NP * SK];             // fp16 keys, rows n .. NP - 1 zero
     uint16_t vb[NP * kPromoteCols];   // bf16 values of the workgroup's columns
@@ -42,6 +47,7 @@ struct PromoteSmem {
     float eg[DK];                     // e^gamma
   };
   Buf b[2];
+  float st[DK * SS];                  // the memory after a firing, for the store wave
 };
 
 __device__ __forceinline__ uint16_t f32_to_f16_bits(float x) {
@@ -59,10 +65,11 @@ __global__ __launch_bounds__(kPromoteThreads) void promote_scan_kernel(
   constexpr int NPT = NP / 16;   // pair tiles
   constexpr int NPS = NP / 32;   // 32-pair steps (B operand of the update)
   constexpr int KPC = DK / 8;    // 16-byte pieces per key row
-  constexpr int NT = kPromoteThreads;
+  constexpr int NT = 64 * kComputeWaves;  // threads that stage the operands
   constexpr int KPT = (NP * KPC + NT - 1) / NT;           // ... per thread
   constexpr int VPT = (NP * (kPromoteCols / 8) + NT - 1) / NT;
   static_assert(NP <= NT && DK <= NT, "one thread per pair and per key row");
+  constexpr int SS = PromoteSmem<DK, NP>::SS;
   __shared__ PromoteSmem<DK, NP> sm;
 
   const int nvb = DV / kPromoteCols;
@@ -77,7 +84,7 @@ __global__ __launch_bounds__(kPromoteThreads) void promote_scan_kernel(
   // ---- global -> register prefetch of one firing's operands (zeros past n)
   u32x4 kr[KPT], vr[VPT];
   float br = 0.f, wr = 0.f, gr = 0.f;
-  auto fetch = [&](int f) {
+  auto fetch = [&](int f) {  // compute waves only
     const int64_t bf = bh * F + f;
     const uint16_t* kb = K + bf * (int64_t)n * DK;
     const uint16_t* vbp = V + bf * (int64_t)n * DV + vb * kPromoteCols;
@@ -100,7 +107,7 @@ __global__ __launch_bounds__(kPromoteThreads) void promote_scan_kernel(
     gr = tid < DK ? gamma[bf * DK + tid] : 0.f;
   };
   // ---- registers -> LDS buffer (keys converted to fp16)
-  auto stage = [&](typename PromoteSmem<DK, NP>::Buf& B) {
+  auto stage = [&](typename PromoteSmem<DK, NP>::Buf& B) {  // compute waves only
 #pragma unroll
     for (int u = 0; u < KPT; ++u) {
       const int e = tid + NT * u, row = e / KPC, c8 = (e % KPC) * 8;
@@ -127,7 +134,35 @@ __global__ __launch_bounds__(kPromoteThreads) void promote_scan_kernel(
     if (tid < DK) B.eg[tid] = expf(gr);
   };
 
-  // ---- this wave's 16 columns of M: rows 16 R + 4 g + i, column col
+  if (wv == kComputeWaves) {
+    // ======================= store wave =======================
+    // Writes the memory after firing f - 1 from the LDS tile to states while the compute
+    // waves work on firing f: 16 bytes per lane, whole rows of the workgroup's columns per
+    // instruction. Only this wave writes global memory inside the loop, so the compute
+    // waves' waits for their prefetched operands never wait for these stores.
+    constexpr int LPR = kPromoteCols / 4;  // lanes per tile row (4 fp32 each)
+    constexpr int RPI = 64 / LPR;          // tile rows per store instruction
+    static_assert(kPromoteCols % 4 == 0 && 64 % LPR == 0 && DK % RPI == 0, "store tiling");
+    auto store_state = [&](int f) {
+      const int c = 4 * (l % LPR);
+      float* sg = states + ((bh * F + f) * DK) * (int64_t)DV + vb * kPromoteCols + c;
+#pragma unroll 8
+      for (int r = l / LPR; r < DK; r += RPI)
+        *reinterpret_cast<f32x4*>(sg + (int64_t)r * DV) =
+            *reinterpret_cast<const f32x4*>(&sm.st[r * SS + c]);
+    };
+    for (int f = 0; f < F; ++f) {
+      lds_barrier();  // (A) firing f staged; the tile holds the memory after firing f - 1
+      if (states && f > 0) store_state(f - 1);
+      lds_barrier();  // (B) the tile is read; the compute waves may overwrite it
+    }
+    lds_barrier();    // (F) the tile holds the memory after the last firing
+    if (states && F > 0) store_state(F - 1);
+    return;
+  }
+
+  // ======================= compute waves =======================
+  // This wave's 16 columns of M: rows 16 R + 4 g + i, column col.
   f32x4 Mt[NRT];
   float* Mg = M + (bh * DK) * (int64_t)DV + col;
 #pragma unroll
@@ -139,9 +174,9 @@ __global__ __launch_bounds__(kPromoteThreads) void promote_scan_kernel(
   for (int f = 0; f < F; ++f) {
     auto& B = sm.b[f & 1];
     stage(B);
-    // Buffer f & 1 complete; its previous reader (firing f - 2) finished before the
-    // barrier of firing f - 1. LDS-only barrier: the last firing's state stores may stay
-    // in flight (no thread reads global memory another thread writes).
+    // (A) Buffer f & 1 complete; its previous reader (firing f - 2) finished before the
+    // barrier (A) of firing f - 1. LDS-only barriers: no thread reads global memory that
+    // another thread writes.
     lds_barrier();
     if (f + 1 < F) fetch(f + 1);
 
@@ -182,14 +217,15 @@ __global__ __launch_bounds__(kPromoteThreads) void promote_scan_kernel(
       for (int t = 0; t < NPS; ++t)
         Mt[R] = mma_f16(half8_from_u32x4(col_frag_tr(B.kh, SK, 16 * R, t, g, m)), us[t], Mt[R]);
 
+    lds_barrier();  // (B) the store wave has read the previous firing's tile
     if (states) {
-      float* Sg = states + ((bh * F + f) * DK) * (int64_t)DV + col;
 #pragma unroll
       for (int R = 0; R < NRT; ++R)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) Sg[(int64_t)(16 * R + 4 * g + i) * DV] = Mt[R][i];
+        for (int i = 0; i < 4; ++i) sm.st[(16 * R + 4 * g + i) * SS + 16 * wv + m] = Mt[R][i];
     }
   }
+  lds_barrier();  // (F)
 
 #pragma unroll
   for (int R = 0; R < NRT; ++R)

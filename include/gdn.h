@@ -158,7 +158,7 @@ typedef struct {
  *   gamma  [scans, F, dk]     fp32 log-decay, one entry per key row
  *   M      [scans, dk, dv]    fp32, in: the memory before the first firing; out: after the last
  *   states [scans, F, dk, dv] fp32 out: the memory after each firing; NULL to skip
- * K and V 16-byte aligned. Products on matrix cores with fp16 operands (the memory and
+ * K, V and states 16-byte aligned. Products on matrix cores with fp16 operands (the memory and
  * U = w o V - beta o K M rounded to fp16, keys converted exactly up to fp16 range) and fp32
  * accumulation; the memory itself stays fp32. No workspace, no allocation, asynchronous on
  * `stream`; scans == 0 is a no-op. Errors: host checks before any launch. */

@@ -1,5 +1,5 @@
 """GPU parity of the decode step (gdn_decode_fwd through the C ABI) against the CPU
-oracle: the same seeded inputs, element by element at the spec bars (fp32 inputs:
+oracle: the same seeded inputs, element by element at the bars of the prefill (fp32 inputs:
 max |do| <= 1e-4 rms(o), state 1e-5 relative; bf16: 2e-2 rms(o) plus the output's own
 half-ulp, state 1e-3), untouched slots bit for bit. Also the decode step continuing a
 prefill on the GPU, and several steps in a row."""

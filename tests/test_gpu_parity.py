@@ -44,6 +44,40 @@ def test_workload4_sampled_heads():
     assert np.all(np.isfinite(pool))
 
 
+def test_workspace_offsets_beyond_2gib():
+    """Two requests of 524288 tokens, H = 4, HV = 16, d = 64: 262176 (chunk, head) items, so
+    each intermediate region of the workspace spans more than 2^31 bytes and the chunk
+    chain of each request is 8192 long. The last value head's last 8 state rows against the
+    oracle over the full length, at the bf16 bars; only those output rows come back."""
+    import torch
+    import gated_deltanet_prefill_gdn_amd as gdn
+    p = gdn_synth.make_problem(950, [524288, 524288], 4, 16, 64, 64, dtype="bf16",
+                               state_std=0.1)
+    prob = gdn.make_problem(p.N, p.B, p.H, p.HV, p.dk, p.dv, p.pool, gdn.GDN_DTYPE_BF16)
+    assert (p.N // 64 + p.B) * p.HV * 64 * p.dk * 2 > 2 ** 31
+    d = to_device(p)
+    announce(f"big-offsets gdn_prefill_fwd N={p.N} H={p.H} HV={p.HV} d=64 "
+             f"workspace={gdn.gdn_prefill_workspace_size(prob) / 2**30:.2f} GiB")
+    out = gdn.gdn_prefill_fwd(d["q"], d["k"], d["v"], d["a"], d["b"], d["A_log"], d["dt_bias"],
+                              d["state_pool"], d["cache_indices"], d["cu_seqlens"])
+    torch.cuda.synchronize()
+    announce("big-offsets done")
+    hv, r0, r1 = 15, 56, 64
+    o = out[:, hv, r0:r1].float().cpu().numpy().astype(np.float64)
+    pool = d["state_pool"].cpu().numpy()
+    del out, d
+    ref = oracle.prefill(p, heads=[hv], rows=(r0, r1))
+    o_ref = ref.out[:, 0, :]
+    rms = float(np.sqrt(np.mean(o_ref ** 2)))
+    err = np.abs(o - o_ref) - 2.0 ** -8 * np.abs(o_ref)
+    assert float(err.max()) <= 2e-2 * rms, (float(err.max()) / rms)
+    for slot in p.cache_indices:
+        g = pool[slot, hv, r0:r1].astype(np.float64)
+        r = ref.state_pool[slot, hv, r0:r1]
+        assert np.linalg.norm(g - r) / np.linalg.norm(r) <= 1e-3
+    announce(f"big-offsets: max(|do| - 2^-8|o|)/rms = {float(err.max()) / rms:.3e}")
+
+
 # ------------------------------------------------------------- edge cases
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_ragged_lengths(dtype):

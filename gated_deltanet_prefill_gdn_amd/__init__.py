@@ -30,8 +30,8 @@ GDN_NUM_STAGES = 3
 STAGE_NAMES = ("gate", "chunk_prep", "state")
 
 EXPORTED = ("gdn_prefill_workspace_size", "gdn_prefill_fwd", "gdn_prefill_fwd_events",
-            "gdn_decode_fwd", "gdn_promote_scan", "gdn_validate_inputs", "gdn_status_str",
-            "gdn_version")
+            "gdn_decode_fwd", "gdn_recurrent_fwd", "gdn_promote_scan", "gdn_validate_inputs",
+            "gdn_status_str", "gdn_version")
 
 
 class GdnProblem(ctypes.Structure):
@@ -90,6 +90,8 @@ def load_library(path: str = LIB_PATH):
     L.gdn_prefill_fwd_events.argtypes = L.gdn_prefill_fwd.argtypes + [P]
     L.gdn_decode_fwd.restype = ctypes.c_int
     L.gdn_decode_fwd.argtypes = [P, P, P, P, P, P, P, P, P, P, PP, P]
+    L.gdn_recurrent_fwd.restype = ctypes.c_int
+    L.gdn_recurrent_fwd.argtypes = [P, P, P, P, P, P, P, P, P, P, P, PP, P]
     L.gdn_promote_scan.restype = ctypes.c_int
     L.gdn_promote_scan.argtypes = [P, P, P, P, P, P, P, ctypes.POINTER(GdnPromoteProblem), P]
     L.gdn_validate_inputs.restype = ctypes.c_int
@@ -151,6 +153,23 @@ def problem_of(q, k, v, state_pool, cache_indices) -> GdnProblem:
                         _dtype_code(q))
 
 
+def gdn_recurrent_fwd(q, k, v, a, b, A_log, dt_bias, state_pool, cache_indices, cu_seqlens,
+                      out=None, stream=None):
+    """The prefill's operation evaluated token by token (no chunks, no workspace), for short
+    requests; same arguments and result as gdn_prefill_fwd."""
+    import torch
+    prob, out = _check_prefill_args(q, k, v, a, b, A_log, dt_bias, state_pool, cache_indices,
+                                    cu_seqlens, out)
+    st = (stream or torch.cuda.current_stream(q.device)).cuda_stream
+    rc = load_library().gdn_recurrent_fwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(A_log), _ptr(dt_bias),
+        _ptr(state_pool), _ptr(cache_indices), _ptr(cu_seqlens), _ptr(out), ctypes.byref(prob),
+        ctypes.c_void_p(st))
+    if rc != GDN_OK:
+        raise GdnError(rc, "gdn_recurrent_fwd")
+    return out
+
+
 def gdn_prefill_fwd(q, k, v, a, b, A_log, dt_bias, state_pool, cache_indices, cu_seqlens,
                     chunk_size: int = 64, out=None, workspace=None, stream=None):
     return _prefill(q, k, v, a, b, A_log, dt_bias, state_pool, cache_indices, cu_seqlens,
@@ -169,15 +188,10 @@ def gdn_prefill_fwd_events(q, k, v, a, b, A_log, dt_bias, state_pool, cache_indi
                     chunk_size, out, workspace, stream, arr)
 
 
-def _prefill(q, k, v, a, b, A_log, dt_bias, state_pool, cache_indices, cu_seqlens,
-             chunk_size, out, workspace, stream, events):
-    """GDN prefill forward on device tensors; returns ``out`` [N, HV, dv] in v's dtype.
-
-    q, k [N, H, dk] and v [N, HV, dv] bf16/fp32; a, b [N, HV] fp32; A_log, dt_bias [HV]
-    fp32; state_pool [pool, HV, dv, dk] fp32 (updated in place); cache_indices [B]
-    int64; cu_seqlens [B+1] int64. ``workspace`` is an optional uint8 device tensor of at
-    least gdn_prefill_workspace_size bytes. ``stream``: a torch stream (default: current).
-    """
+def _check_prefill_args(q, k, v, a, b, A_log, dt_bias, state_pool, cache_indices, cu_seqlens,
+                        out):
+    """Shapes, dtypes, devices and contiguity of a prefill call's tensors; allocates ``out``
+    if it is None. Returns (problem descriptor, out)."""
     import torch
     dev = q.device
     if dev.type != "cuda":
@@ -213,6 +227,23 @@ def _prefill(q, k, v, a, b, A_log, dt_bias, state_pool, cache_indices, cu_seqlen
         _need(out, "out", dtype=v.dtype, ndim=3, device=dev)
         if tuple(out.shape) != (N, HV, dv):
             raise ValueError("out must be [N, HV, dv]")
+    return prob, out
+
+
+def _prefill(q, k, v, a, b, A_log, dt_bias, state_pool, cache_indices, cu_seqlens,
+             chunk_size, out, workspace, stream, events):
+    """GDN prefill forward on device tensors; returns ``out`` [N, HV, dv] in v's dtype.
+
+    q, k [N, H, dk] and v [N, HV, dv] bf16/fp32; a, b [N, HV] fp32; A_log, dt_bias [HV]
+    fp32; state_pool [pool, HV, dv, dk] fp32 (updated in place); cache_indices [B]
+    int64; cu_seqlens [B+1] int64. ``workspace`` is an optional uint8 device tensor of at
+    least gdn_prefill_workspace_size bytes. ``stream``: a torch stream (default: current).
+    """
+    import torch
+    dev = q.device
+    N, HV = q.shape[0], v.shape[1]
+    prob, out = _check_prefill_args(q, k, v, a, b, A_log, dt_bias, state_pool, cache_indices,
+                                    cu_seqlens, out)
     need = gdn_prefill_workspace_size(prob, chunk_size)
     if need == 0 and (N > 0 and cache_indices.shape[0] > 0):
         raise GdnError(GDN_ERR_UNSUPPORTED, "gdn_prefill_workspace_size")

@@ -1,6 +1,6 @@
 // C ABI of libgdn (declared in include/gdn.h): host-side argument checks, the
 // workspace layout and the launch sequence plan -> gate -> chunk prep -> state pass of
-// the prefill, the one-kernel decode step and the Promote update scan.
+// the prefill, the chunk-free recurrent path, the decode step and the Promote update scan.
 #include <string.h>
 
 #include <vector>
@@ -80,7 +80,7 @@ using namespace gdn;
 
 extern "C" {
 
-int32_t gdn_version(void) { return 300; }
+int32_t gdn_version(void) { return 400; }
 
 const char* gdn_status_str(gdn_status_t st) {
   switch (st) {
@@ -220,6 +220,27 @@ gdn_status_t gdn_decode_fwd(const void* q, const void* k, const void* v, const f
   if (decode_blocks(s) > 0x7FFFFFFF) return GDN_ERR_UNSUPPORTED;
   if (launch_decode(q, k, v, a, b, A_log, dt_bias, cache_indices, s, state_pool, out,
                     (hipStream_t)stream) != hipSuccess)
+    return GDN_ERR_HIP;
+  return GDN_OK;
+}
+
+gdn_status_t gdn_recurrent_fwd(const void* q, const void* k, const void* v, const float* a,
+                               const float* b, const float* A_log, const float* dt_bias,
+                               float* state_pool, const int64_t* cache_indices,
+                               const int64_t* cu_seqlens, void* out, const gdn_problem_t* prob,
+                               void* stream) {
+  Shape s;
+  const gdn_status_t ps = check_problem(prob, 64, &s);  // the chunk size plays no part
+  if (ps != GDN_OK) return ps;
+  if (s.N == 0 || s.B == 0) return GDN_OK;
+  if (!q || !k || !v || !a || !b || !A_log || !dt_bias || !state_pool || !cache_indices ||
+      !cu_seqlens || !out)
+    return GDN_ERR_INVALID_ARG;
+  for (const void* ptr : {q, k, v, (const void*)state_pool})  // 16-byte vector loads
+    if (((uintptr_t)ptr & 15) != 0) return GDN_ERR_INVALID_ARG;
+  if (decode_blocks(s) > 0x7FFFFFFF) return GDN_ERR_UNSUPPORTED;
+  if (launch_recurrent(q, k, v, a, b, A_log, dt_bias, cache_indices, cu_seqlens, s, state_pool,
+                       out, (hipStream_t)stream) != hipSuccess)
     return GDN_ERR_HIP;
   return GDN_OK;
 }

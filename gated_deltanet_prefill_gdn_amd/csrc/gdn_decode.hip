@@ -214,6 +214,136 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
   }
 }
 
+// The same row split applied to every token of a request in turn (the recurrence itself,
+// with no chunks): the state rows stay in registers from the request's first token to its
+// last, so the state is read and written once per call whatever the number of tokens.
+// For short requests (speculative-decoding verification, a few tokens each) this replaces
+// the chunked path, whose 64-row chunks would be mostly padding; it is correct for any
+// length but runs each request's tokens one after another.
+template <int DK, bool BF16>
+__global__ __launch_bounds__(kDecodeThreads) void recurrent_kernel(
+    const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
+    const float* __restrict__ ga, const float* __restrict__ gb, const float* __restrict__ A_log,
+    const float* __restrict__ dt_bias, const int64_t* __restrict__ cache_indices,
+    const int64_t* __restrict__ cu, int H, int HV, int DV, int nrb,
+    float* __restrict__ state_pool, void* __restrict__ out) {
+  constexpr int LPR = DK / 8;
+  constexpr int RPW = 64 / LPR;
+  constexpr int NR = kRowsPerThread<DK>;
+  constexpr int RWV = RPW * NR;
+  constexpr int RWG = kRowsPerBlock<DK>;
+  const uint32_t x = blockIdx.x;
+  const uint32_t pair32 = x / (uint32_t)nrb;
+  const int rb = (int)(x - pair32 * (uint32_t)nrb);
+  const uint32_t b32 = pair32 / (uint32_t)HV;
+  const int hv = (int)(pair32 - b32 * (uint32_t)HV);
+  const int h = hv / (HV / H);
+  const int64_t bi = b32;
+  const int64_t t_begin = cu[bi], t_end = cu[bi + 1];
+  if (t_begin >= t_end) return;  // an empty request leaves its slot untouched
+  const int tid = threadIdx.x, wv = tid >> 6, l = tid & 63;
+  const int gl = l % LPR, rg = l / LPR;
+  const int64_t slot = cache_indices[bi];
+  const float alog = A_log[hv], dtb = dt_bias[hv];
+  const float decay = expf(alog);
+
+  const int r0 = rb * RWG + wv * RWV + rg;
+  float* Sp = state_pool + ((slot * HV + hv) * (int64_t)DV + r0) * DK + 4 * gl;
+  f32x4 s[NR][2];
+#pragma unroll
+  for (int j = 0; j < NR; ++j) {
+    s[j][0] = *reinterpret_cast<const f32x4*>(Sp + j * RPW * DK);
+    s[j][1] = *reinterpret_cast<const f32x4*>(Sp + j * RPW * DK + DK / 2);
+  }
+
+  for (int64_t t = t_begin; t < t_end; ++t) {
+    const int64_t th = t * HV + hv;
+    float vr[NR];
+#pragma unroll
+    for (int j = 0; j < NR; ++j) {
+      const int64_t vi = th * DV + r0 + j * RPW;
+      vr[j] = BF16 ? bf16_to_f32(reinterpret_cast<const uint16_t*>(v)[vi])
+                   : reinterpret_cast<const float*>(v)[vi];
+    }
+    float kk[8], qq[8];
+    load8<DK, BF16>(k, (t * H + h) * DK, gl, kk);
+    load8<DK, BF16>(q, (t * H + h) * DK, gl, qq);
+    const float a_t = ga[th], b_t = gb[th];
+    float ssk = 0.f, ssq = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      ssk = __builtin_fmaf(kk[e], kk[e], ssk);
+      ssq = __builtin_fmaf(qq[e], qq[e], ssq);
+    }
+    ssk = group_sum<LPR>(ssk);
+    ssq = group_sum<LPR>(ssq);
+    const float rk = 1.0f / sqrtf(ssk + kNormEps), rq = 1.0f / sqrtf(ssq + kNormEps);
+    float kq = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      kk[e] *= rk;
+      qq[e] *= rq;
+      kq = __builtin_fmaf(kk[e], qq[e], kq);
+    }
+    kq = group_sum<LPR>(kq);
+    const float xg = a_t + dtb;
+    const float sp = fmaxf(xg, 0.f) + log1pf(expf(-fabsf(xg)));
+    const float alpha = expf(-decay * sp);
+    const float beta = 1.f / (1.f + expf(-b_t));
+
+    float pk[NR], pq[NR];
+#pragma unroll
+    for (int j = 0; j < NR; ++j) {
+      float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        a0 = __builtin_fmaf(s[j][0][e], kk[e], a0);
+        a0 = __builtin_fmaf(s[j][1][e], kk[4 + e], a0);
+        a1 = __builtin_fmaf(s[j][0][e], qq[e], a1);
+        a1 = __builtin_fmaf(s[j][1][e], qq[4 + e], a1);
+      }
+      pk[j] = group_sum<LPR>(a0);
+      pq[j] = group_sum<LPR>(a1);
+    }
+#pragma unroll
+    for (int j = 0; j < NR; ++j) {
+      const float u = beta * (vr[j] - alpha * pk[j]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        s[j][0][e] = __builtin_fmaf(alpha, s[j][0][e], u * kk[e]);
+        s[j][1][e] = __builtin_fmaf(alpha, s[j][1][e], u * kk[4 + e]);
+      }
+      if (gl == 0) {
+        const float o = __builtin_fmaf(alpha, pq[j], kq * u);
+        const int64_t oi = th * DV + r0 + j * RPW;
+        if constexpr (BF16)
+          reinterpret_cast<uint16_t*>(out)[oi] = f32_to_bf16(o);
+        else
+          reinterpret_cast<float*>(out)[oi] = o;
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < NR; ++j) {
+    *reinterpret_cast<f32x4*>(Sp + j * RPW * DK) = s[j][0];
+    *reinterpret_cast<f32x4*>(Sp + j * RPW * DK + DK / 2) = s[j][1];
+  }
+}
+
+template <int DK, bool BF16>
+hipError_t launch_recurrent_t(const void* q, const void* k, const void* v, const float* a,
+                              const float* b, const float* A_log, const float* dt_bias,
+                              const int64_t* idx, const int64_t* cu, const Shape& s, float* pool,
+                              void* out, hipStream_t st) {
+  if (s.dv % kRowsPerBlock<DK> != 0) return hipErrorInvalidValue;
+  const int nrb = s.dv / kRowsPerBlock<DK>;
+  const int64_t blocks = s.B * (int64_t)s.HV * nrb;
+  hipLaunchKernelGGL((recurrent_kernel<DK, BF16>), dim3((unsigned)blocks), dim3(kDecodeThreads),
+                     0, st, q, k, v, a, b, A_log, dt_bias, idx, cu, s.H, s.HV, s.dv, nrb, pool,
+                     out);
+  return hipGetLastError();
+}
+
 template <int DK, bool BF16>
 hipError_t launch_decode_t(const void* q, const void* k, const void* v, const float* a,
                            const float* b, const float* A_log, const float* dt_bias,
@@ -249,6 +379,25 @@ hipError_t launch_decode(const void* q, const void* k, const void* v, const floa
   GDN_DECODE_CASE(128)
   GDN_DECODE_CASE(256)
 #undef GDN_DECODE_CASE
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_recurrent(const void* q, const void* k, const void* v, const float* a,
+                            const float* b, const float* A_log, const float* dt_bias,
+                            const int64_t* cache_indices, const int64_t* cu_seqlens,
+                            const Shape& s, float* state_pool, void* out, hipStream_t st) {
+#define GDN_RECURRENT_CASE(DKv)                                                             \
+  if (s.dk == DKv)                                                                          \
+    return s.bf16 ? launch_recurrent_t<DKv, true>(q, k, v, a, b, A_log, dt_bias,            \
+                                                  cache_indices, cu_seqlens, s, state_pool, \
+                                                  out, st)                                  \
+                  : launch_recurrent_t<DKv, false>(q, k, v, a, b, A_log, dt_bias,           \
+                                                   cache_indices, cu_seqlens, s, state_pool, \
+                                                   out, st);
+  GDN_RECURRENT_CASE(64)
+  GDN_RECURRENT_CASE(128)
+  GDN_RECURRENT_CASE(256)
+#undef GDN_RECURRENT_CASE
   return hipErrorInvalidValue;
 }
 

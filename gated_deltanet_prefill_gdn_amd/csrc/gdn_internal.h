@@ -86,6 +86,12 @@ hipError_t launch_decode(const void* q, const void* k, const void* v, const floa
                          const int64_t* cache_indices, const Shape& s, float* state_pool,
                          void* out, hipStream_t st);
 
+// The token recurrence without chunks, for short requests (same grid as the decode step).
+hipError_t launch_recurrent(const void* q, const void* k, const void* v, const float* a,
+                            const float* b, const float* A_log, const float* dt_bias,
+                            const int64_t* cache_indices, const int64_t* cu_seqlens,
+                            const Shape& s, float* state_pool, void* out, hipStream_t st);
+
 // Promote update scan: shape and launcher (bf16 keys and values).
 struct PromoteShape {
   int64_t BH;  // independent scans

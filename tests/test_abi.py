@@ -171,3 +171,27 @@ def test_package_has_no_oracle_dependency():
                 text = open(os.path.join(dirpath, f)).read()
                 assert "import oracle" not in text and "from oracle" not in text, f
                 assert "gdn_oracle" not in text, f
+
+
+def call_recurrent(p, nonnull=True, misalign=0):
+    lib = gdn.load_library()
+    P = ctypes.c_void_p
+    x = P(4096) if nonnull else P(0)
+    return lib.gdn_recurrent_fwd(P(4096 + misalign), x, x, x, x, x, x, x, x, x, x,
+                                 ctypes.byref(p), P(0))
+
+
+def test_recurrent_error_paths_return_before_launch():
+    assert call_recurrent(prob(HV=24)) == gdn.GDN_ERR_INVALID_ARG
+    assert call_recurrent(prob(N=-1)) == gdn.GDN_ERR_INVALID_ARG
+    assert call_recurrent(prob(dtype=3)) == gdn.GDN_ERR_INVALID_ARG
+    assert call_recurrent(prob(pool=0)) == gdn.GDN_ERR_INVALID_ARG
+    assert call_recurrent(prob(dk=96)) == gdn.GDN_ERR_UNSUPPORTED
+    assert call_recurrent(prob(dv=32)) == gdn.GDN_ERR_UNSUPPORTED
+    assert call_recurrent(prob(), nonnull=False) == gdn.GDN_ERR_INVALID_ARG
+    assert call_recurrent(prob(), misalign=8) == gdn.GDN_ERR_INVALID_ARG   # q not 16-aligned
+    assert call_recurrent(prob(N=0, B=3), nonnull=False) == gdn.GDN_OK
+    assert call_recurrent(prob(N=5, B=0, pool=0), nonnull=False) == gdn.GDN_OK
+    lib = gdn.load_library()
+    assert lib.gdn_recurrent_fwd(None, None, None, None, None, None, None, None, None, None, None,
+                                 None, None) == gdn.GDN_ERR_INVALID_ARG

@@ -9,8 +9,10 @@ inputs resident in HBM. Prints one JSON line.
 With ``--op decode`` a step is instead one gdn_decode_fwd call over the decode workload
 (512 requests x 1 token, H = 16, HV = 32, dk = dv = 128, bf16, 1 GiB of state), and with
 ``--op promote`` one gdn_promote_scan call over the Promote workload (128 scans x 64
-firings x 64 pairs, dk = dv = 128, bf16, every firing's state kept); the JSON line then
-reports that call.
+firings x 64 pairs, dk = dv = 128, bf16, every firing's state kept); with ``--op verify``
+one gdn_recurrent_fwd call over a speculative-verification batch (512 requests x 4 tokens,
+the decode workload's heads and pool), the chunked gdn_prefill_fwd on the same call timed
+beside it. The JSON line then reports that call.
 """
 from __future__ import annotations
 
@@ -305,6 +307,148 @@ def bench_decode(args):
     print(json.dumps(res), flush=True)
 
 
+VERIFY_METRIC = "GDN short-request (verification) tokens/sec, 4 tokens per request, dk=dv=128"
+
+
+def verify_bytes(p, s_qkv: int) -> int:
+    """Algorithmic HBM bytes of one recurrent call: the fp32 state of every (request, value
+    head) read and written once; per token q, k per q/k head, v and out per value head, a
+    and b; the gate parameters, the slot indices and the sequence offsets."""
+    return (2 * p.B * p.HV * p.dv * p.dk * 4 + 2 * p.N * p.H * p.dk * s_qkv
+            + 2 * p.N * p.HV * p.dv * s_qkv + 8 * p.N * p.HV + 8 * p.HV + 16 * p.B + 8)
+
+
+def _time_launches(step, stream, steps: int, warmup: int):
+    """Wall ms per step over `steps` back-to-back calls after `warmup`, then the average
+    HIP-event time of one call on the launch stream less the empty event pair's."""
+    import numpy as np
+    import torch
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / steps
+    hip = Hip()
+    evs = [(hip.event(), hip.event()) for _ in range(steps)]
+    rec = hip.lib.hipEventRecord
+    rec.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    for e0, e1 in evs:
+        rec(ctypes.c_void_p(e0), ctypes.c_void_p(stream.cuda_stream))
+        step()
+        rec(ctypes.c_void_p(e1), ctypes.c_void_p(stream.cuda_stream))
+    torch.cuda.synchronize()
+    events_ms = float(np.mean([hip.elapsed_ms(e0, e1) for e0, e1 in evs]))
+    for e0, e1 in evs:
+        hip.destroy(e0)
+        hip.destroy(e1)
+    pair_ms = hip.empty_pair_ms(stream.cuda_stream)
+    launch_ms = events_ms - pair_ms if events_ms > 2 * pair_ms else events_ms
+    return ms_per_step, events_ms, pair_ms, launch_ms
+
+
+def verify_cpu_baseline(p, n_req: int = 64, reps: int = 3):
+    """The oracle's prefill as it stands, on this host's cores, over the first n_req
+    requests of the verification workload with every value head; tokens/s."""
+    import numpy as np
+    import oracle
+    import gdn_synth
+    T = int(p.cu_seqlens[1] - p.cu_seqlens[0])
+    sub = gdn_synth.make_problem(p.seed, [T] * n_req, p.H, p.HV, p.dk, p.dv, dtype=p.dtype,
+                                 pool=n_req)
+    rows = np.arange(n_req * T)
+    sub.q, sub.k, sub.v, sub.a, sub.b = p.q[rows], p.k[rows], p.v[rows], p.a[rows], p.b[rows]
+    sub.A_log, sub.dt_bias = p.A_log, p.dt_bias
+    sub.state_pool = p.state_pool[p.cache_indices[:n_req]]
+    sub.cache_indices = np.arange(n_req, dtype=np.int64)
+    threads = oracle.default_threads()
+    walls = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        oracle.prefill(sub, nthreads=threads)
+        walls.append(time.perf_counter() - t0)
+    dt = float(np.median(walls))
+    return {"value": n_req * T / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n_req} of the {p.B} requests ({n_req * T} tokens), all {p.HV} value "
+                      f"heads, fp64 token recurrence, median of {reps} runs, {dt:.3f} s wall each"}
+
+
+def bench_verify(args):
+    import numpy as np
+    import torch
+
+    import gdn_synth
+    import gated_deltanet_prefill_gdn_amd as gdn
+
+    p = gdn_synth.verify_workload()
+    dev = torch.device("cuda:0")
+
+    def t(x, dt=None):
+        x = torch.from_numpy(np.ascontiguousarray(x))
+        return (x.view(dt) if dt is not None else x).to(dev)
+
+    q = t(p.q.view(np.int16), torch.bfloat16)
+    k = t(p.k.view(np.int16), torch.bfloat16)
+    v = t(p.v.view(np.int16), torch.bfloat16)
+    a, b, A_log, dt_bias = t(p.a), t(p.b), t(p.A_log), t(p.dt_bias)
+    pool = t(p.state_pool)
+    idx, cu = t(p.cache_indices), t(p.cu_seqlens)
+    out = torch.empty((p.N, p.HV, p.dv), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(gdn.gdn_prefill_workspace_size(gdn.problem_of(q, k, v, pool, idx)),
+                     dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        gdn.gdn_recurrent_fwd(q, k, v, a, b, A_log, dt_bias, pool, idx, cu, out=out,
+                              stream=stream)
+
+    def chunked():
+        gdn.gdn_prefill_fwd(q, k, v, a, b, A_log, dt_bias, pool, idx, cu, out=out,
+                            workspace=ws, stream=stream)
+
+    ms_per_step, events_ms, pair_ms, launch_ms = _time_launches(step, stream, args.steps,
+                                                                args.warmup)
+    chunked_ms = _time_launches(chunked, stream, args.steps, args.warmup)[0]
+    if args.copy_calibration:
+        src = torch.empty(512 << 20, dtype=torch.uint8, device=dev).fill_(3)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    nbytes = verify_bytes(p, 2)
+    achieved = nbytes / (launch_ms * 1e-3) / 1e9
+    src_hash = kernel_source_hash("decode")
+    res = {
+        "metric": VERIFY_METRIC,
+        "value": p.N / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded SplitMix64/Box-Muller, seed 1300)",
+        "config": {"workload": gdn_synth.VERIFY_WORKLOAD, "global_batch": p.B,
+                   "seq_len": int(p.cu_seqlens[1]), "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "hbm", "kernel": "recurrent_kernel", "achieved": achieved,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": stored_traffic("recurrent_kernel", src_hash),
+                     "algorithmic_bytes_per_launch": nbytes, "avg_launch_ms": launch_ms,
+                     "avg_launch_ms_events": events_ms, "event_pair_ms": pair_ms},
+        "chunked_path_ms_per_step": chunked_ms,
+        "kernel_source_hash": src_hash,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = verify_cpu_baseline(p)
+    print(json.dumps(res), flush=True)
+
+
 PROMOTE_METRIC = "Promote update scan pairs/sec (decay, erase, write per firing), dk=dv=128"
 
 
@@ -441,7 +585,8 @@ def bench_promote(args):
 
 def main():
     ap = argparse.ArgumentParser()
-    ap.add_argument("--op", choices=("prefill", "decode", "promote"), default="prefill",
+    ap.add_argument("--op", choices=("prefill", "decode", "promote", "verify"),
+                    default="prefill",
                     help="the call a step times (default: the prefill forward)")
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
@@ -461,6 +606,9 @@ def main():
         return
     if args.op == "promote":
         bench_promote(args)
+        return
+    if args.op == "verify":
+        bench_verify(args)
         return
 
     import numpy as np

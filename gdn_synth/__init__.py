@@ -293,6 +293,19 @@ def decode_workload() -> Problem:
                                state_std=0.1, name="decode_batch_bf16")
 
 
+# Speculative-decoding verification: 512 requests, each bringing 4 tokens (3 drafted + 1),
+# with the decode workload's heads and pool.
+VERIFY_WORKLOAD = ("verify batch bf16: B=512 requests x 4 tokens, H=16 HV=32 dk=dv=128, "
+                   "pool 512 ~N(0,0.01) in seeded order")
+
+
+def verify_workload(tokens: int = 4) -> Problem:
+    seed = 1300
+    perm = seeded_permutation(seed, TID_PERM, 512)
+    return make_problem(seed, [tokens] * 512, 16, 32, 128, 128, dtype="bf16", pool=512,
+                        cache_indices=perm, state_std=0.1, name="verify_batch_bf16")
+
+
 # ---------------------------------------------------------------- Promote update scan
 TID_PK, TID_PV, TID_PBETA, TID_PW, TID_PGAMMA, TID_PM = range(21, 27)
 

@@ -256,19 +256,39 @@ __global__ __launch_bounds__(kDecodeThreads) void recurrent_kernel(
     s[j][1] = *reinterpret_cast<const f32x4*>(Sp + j * RPW * DK + DK / 2);
   }
 
-  for (int64_t t = t_begin; t < t_end; ++t) {
+  // One token's inputs; the next token's are loaded while the current one is applied
+  // (the last token loads itself again, so every load stays in the request).
+  struct TokenIn {
+    float vr[NR], kk[8], qq[8], a_t, b_t;
+  };
+  auto load_token = [&](int64_t t, TokenIn& x) {
     const int64_t th = t * HV + hv;
-    float vr[NR];
 #pragma unroll
     for (int j = 0; j < NR; ++j) {
       const int64_t vi = th * DV + r0 + j * RPW;
-      vr[j] = BF16 ? bf16_to_f32(reinterpret_cast<const uint16_t*>(v)[vi])
-                   : reinterpret_cast<const float*>(v)[vi];
+      x.vr[j] = BF16 ? bf16_to_f32(reinterpret_cast<const uint16_t*>(v)[vi])
+                     : reinterpret_cast<const float*>(v)[vi];
     }
-    float kk[8], qq[8];
-    load8<DK, BF16>(k, (t * H + h) * DK, gl, kk);
-    load8<DK, BF16>(q, (t * H + h) * DK, gl, qq);
-    const float a_t = ga[th], b_t = gb[th];
+    load8<DK, BF16>(k, (t * H + h) * DK, gl, x.kk);
+    load8<DK, BF16>(q, (t * H + h) * DK, gl, x.qq);
+    x.a_t = ga[th];
+    x.b_t = gb[th];
+  };
+  TokenIn nxt;
+  load_token(t_begin, nxt);
+  for (int64_t t = t_begin; t < t_end; ++t) {
+    const int64_t th = t * HV + hv;
+    const TokenIn cur = nxt;
+    load_token(t + 1 < t_end ? t + 1 : t, nxt);
+    float vr[NR], kk[8], qq[8];
+#pragma unroll
+    for (int j = 0; j < NR; ++j) vr[j] = cur.vr[j];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      kk[e] = cur.kk[e];
+      qq[e] = cur.qq[e];
+    }
+    const float a_t = cur.a_t, b_t = cur.b_t;
     float ssk = 0.f, ssq = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {

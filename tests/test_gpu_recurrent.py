@@ -87,3 +87,24 @@ def test_recurrent_empty_tokens_leave_pool():
     torch.cuda.synchronize()
     assert out.shape == (0, 2, 64)
     assert torch.equal(pool, before)
+
+
+def test_recurrent_verify_workload_sampled():
+    """The benchmarked verification batch (512 requests x 4 tokens, H = 16, HV = 32,
+    dk = dv = 128, bf16, 1 GiB of state) in one launch, as bench.py times it; 12 seeded
+    requests, every head and token, against the oracle."""
+    p = gdn_synth.verify_workload()
+    out, pool_gpu, _ = run_recurrent(p, "verify workload")
+    reqs = np.sort(gdn_synth.seeded_permutation(78, gdn_synth.TID_PERM, p.B)[:12])
+    cu = p.cu_seqlens
+    rows = np.concatenate([np.arange(cu[r], cu[r + 1]) for r in reqs])
+    lengths = [int(cu[r + 1] - cu[r]) for r in reqs]
+    sub = gdn_synth.make_problem(p.seed, lengths, p.H, p.HV, p.dk, p.dv, dtype=p.dtype,
+                                 pool=len(reqs))
+    sub.q, sub.k, sub.v, sub.a, sub.b = p.q[rows], p.k[rows], p.v[rows], p.a[rows], p.b[rows]
+    sub.A_log, sub.dt_bias = p.A_log, p.dt_bias
+    sub.state_pool = p.state_pool[p.cache_indices[reqs]]
+    sub.cache_indices = np.arange(len(reqs), dtype=np.int64)
+    rep = compare(sub, out[rows], pool_gpu[p.cache_indices[reqs]], oracle.prefill(sub))
+    announce(f"verify workload sampled: {rep}")
+    assert np.all(np.isfinite(out))

@@ -135,13 +135,19 @@ gdn_status_t gdn_decode_fwd(const void* q, const void* k, const void* v, const f
                             const gdn_problem_t* prob, void* stream);
 
 /* The same operation as gdn_prefill_fwd (same arguments, layouts, dtypes, head dims and
- * state-pool semantics), evaluated token by token without chunks: each request's state
+ * state-pool semantics), evaluated as the token recurrence itself (the state-transition
+ * equation of "Simple math to speed up GDN prefill", section Reminder, applied to each
+ * token of a request in order) rather than in chunks: each request's state
  * rows stay in registers from its first token to its last, so the state is read and
  * written once per call. No workspace and no chunk size. Meant for short requests
  * (speculative-decoding verification, a few tokens each), where 64-row chunks would be
  * mostly padding; correct for any length, but a request's tokens run one after another.
  * Arithmetic in fp32 (no matrix cores). q, k, v and state_pool 16-byte aligned; N == 0
- * or B == 0 is a no-op; errors as for gdn_prefill_fwd. */
+ * or B == 0 is a no-op; errors as for gdn_prefill_fwd. cu_seqlens and cache_indices are
+ * preconditions as for the prefill (gdn_validate_inputs checks them). Compared with the
+ * chunked path the result differs only by rounding: the recurrence is applied in fp32
+ * token by token instead of chunk by chunk (for bf16 inputs the chunked path also keeps
+ * its per-chunk intermediates in fp16). */
 gdn_status_t gdn_recurrent_fwd(const void* q, const void* k, const void* v, const float* a,
                                const float* b, const float* A_log, const float* dt_bias,
                                float* state_pool, const int64_t* cache_indices,

@@ -590,7 +590,7 @@ def main():
                     help="the call a step times (default: the prefill forward)")
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cold-steps", type=int, default=5,
                     help="extra steps timed one by one after a 512 MiB cache flush")

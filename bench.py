@@ -583,6 +583,291 @@ def bench_promote(args):
     print(json.dumps(res), flush=True)
 
 
+
+SUB_WORKLOADS = (2, 3, 4)   # reported beside the headline workload in the same line
+FLUSH_BYTES = 512 << 20     # more than the 256 MiB Infinity Cache
+
+
+def _pct(xs, q):
+    import numpy as np
+    return float(np.percentile(np.asarray(xs, dtype=np.float64), q))
+
+
+def stored_counters(kernel: str, workload: str, src_hash: str):
+    """Per-launch counter figures (HBM bytes, MFMA busy, executed MFMA flops) of `kernel`
+    on `workload` from the committed rocprofv3 summaries, if they were taken on the
+    current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "counters.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        d = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    ent = d.get(workload, {}).get(kernel)
+    if not ent or ent.get("source_hash") != src_hash:
+        return None
+    return ent
+
+
+def workload_tag(p) -> str:
+    """Short name of a workload: dtype, requests, tokens, heads and head dims."""
+    if p.B == 1 or len(set(int(x) for x in (p.cu_seqlens[1:] - p.cu_seqlens[:-1]))) == 1:
+        t = f"b{p.B}_t{p.N // max(p.B, 1)}"
+    else:
+        t = f"b{p.B}_n{p.N}"
+    hv = f"_hv{p.HV}" if p.HV != p.H else ""
+    return f"{p.name}_{t}_h{p.H}{hv}_d{p.dk}"
+
+
+def prefill_cpu_baseline(p, heads=None, reps: int = 3):
+    """The oracle (fp64 token recurrence) as it stands, threaded over this host's cores, on
+    every request of the workload and the value heads in `heads` (all if None); the median
+    wall time of `reps` runs, scaled to the whole workload by HV / len(heads), gives
+    tokens/s."""
+    import numpy as np
+    import oracle
+    threads = oracle.default_threads()
+    hs = list(range(p.HV)) if heads is None else list(heads)
+    walls = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        oracle.prefill(p, heads=hs, nthreads=threads)
+        walls.append(time.perf_counter() - t0)
+    dt = float(np.median(walls))
+    per_tok = dt * p.HV / len(hs)   # seconds for every head
+    which = ("every value head" if len(hs) == p.HV
+             else f"value heads {hs} of {p.HV} (time scaled by {p.HV}/{len(hs)})")
+    return {"value": p.N / per_tok, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"all {p.B} requests ({p.N} tokens), {which}, fp64 recurrence, "
+                      f"median of {reps} runs, {dt:.2f} s wall each"}
+
+
+def measure_prefill(p, steps: int, warmup: int, cold_steps: int, copy_calibration=False):
+    """Times gdn_prefill_fwd on the workload `p` (inputs resident in HBM, workspace
+    preallocated). Returns a dict of the wall time per call over `steps` back-to-back
+    calls, per-call HIP-event times (warm and after a cache flush: median, p10, p90), the
+    per-stage launch times and the roofline of the dominant kernel."""
+    import numpy as np
+    import torch
+
+    import gated_deltanet_prefill_gdn_amd as gdn
+
+    dev = torch.device("cuda:0")
+
+    def t(x, dt=None):
+        x = torch.from_numpy(np.ascontiguousarray(x))
+        return (x.view(dt) if dt is not None else x).to(dev)
+
+    if p.dtype == "bf16":
+        q = t(p.q.view(np.int16), torch.bfloat16)
+        k = t(p.k.view(np.int16), torch.bfloat16)
+        v = t(p.v.view(np.int16), torch.bfloat16)
+        s_qkv = 2
+    else:
+        q, k, v = t(p.q), t(p.k), t(p.v)
+        s_qkv = 4
+    a, b, A_log, dt_bias = t(p.a), t(p.b), t(p.A_log), t(p.dt_bias)
+    pool = t(p.state_pool.copy())
+    idx, cu = t(p.cache_indices), t(p.cu_seqlens)
+    out = torch.empty((p.N, p.HV, p.dv), dtype=v.dtype, device=dev)
+    prob = gdn.problem_of(q, k, v, pool, idx)
+    ws = torch.empty(gdn.gdn_prefill_workspace_size(prob), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    hip = Hip()
+    rec = hip.lib.hipEventRecord
+    rec.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    sp = ctypes.c_void_p(stream.cuda_stream)
+
+    def step(events=None):
+        if events is None:
+            gdn.gdn_prefill_fwd(q, k, v, a, b, A_log, dt_bias, pool, idx, cu, out=out,
+                                workspace=ws, stream=stream)
+        else:
+            gdn.gdn_prefill_fwd_events(q, k, v, a, b, A_log, dt_bias, pool, idx, cu, events,
+                                       out=out, workspace=ws, stream=stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    # The K timed steps: plain calls, nothing recorded between them.
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / steps
+
+    # Per-call event times: one event pair around each call (none inside it).
+    evs = [(hip.event(), hip.event()) for _ in range(steps)]
+    for e0, e1 in evs:
+        rec(ctypes.c_void_p(e0), sp)
+        step()
+        rec(ctypes.c_void_p(e1), sp)
+    torch.cuda.synchronize()
+    warm = [hip.elapsed_ms(e0, e1) for e0, e1 in evs]
+    for e0, e1 in evs:
+        hip.destroy(e0)
+        hip.destroy(e1)
+
+    # The same calls with HIP events on the launch stream around every stage: per-kernel
+    # launch durations for the roofline.
+    nst = gdn.GDN_NUM_STAGES
+    sev = [[hip.event() for _ in range(nst + 1)] for _ in range(steps)]
+    for i in range(steps):
+        step(sev[i])
+    torch.cuda.synchronize()
+    stage_ms = {name: float(np.mean([hip.elapsed_ms(e[j], e[j + 1]) for e in sev]))
+                for j, name in enumerate(gdn.STAGE_NAMES)}
+    for e in sev:
+        for x in e:
+            hip.destroy(x)
+    pair_ms = hip.empty_pair_ms(stream.cuda_stream)
+
+    # Calls timed one by one after a 512 MiB write has evicted the Infinity Cache.
+    cold = []
+    if cold_steps > 0:
+        scratch = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+        e0, e1 = hip.event(), hip.event()
+        for _ in range(cold_steps):
+            scratch.fill_(1)
+            torch.cuda.synchronize()
+            rec(ctypes.c_void_p(e0), sp)
+            step()
+            rec(ctypes.c_void_p(e1), sp)
+            torch.cuda.synchronize()
+            cold.append(hip.elapsed_ms(e0, e1))
+        hip.destroy(e0)
+        hip.destroy(e1)
+        del scratch
+
+    if copy_calibration:
+        src = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev).fill_(3)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    del q, k, v, a, b, pool, out, ws
+    torch.cuda.empty_cache()
+
+    n_chunks = int(sum((int(L) + p.chunk_size - 1) // p.chunk_size
+                       for L in (p.cu_seqlens[1:] - p.cu_seqlens[:-1])))
+    # launch durations: each event-timed stage less the overhead of an empty event pair
+    launch = {n: (ms - pair_ms if ms > 2 * pair_ms else ms) for n, ms in stage_ms.items()}
+    dom = max(launch, key=launch.get)
+    kernel_name = gdn.STAGE_KERNELS[dom] if p.dtype == "bf16" else dom
+    pbytes = path_bytes(p, s_qkv)
+    flops = algorithmic_flops_per_token_vhead(p.dk, p.dv, p.chunk_size) * p.N * p.HV
+    src_hash = kernel_source_hash()
+    io = stage_bytes(p, s_qkv, 2, n_chunks) if p.dtype == "bf16" else {}
+    tag = workload_tag(p)
+    ctr = stored_counters(kernel_name, tag, src_hash)
+    sec = launch[dom] * 1e-3
+    achieved = pbytes / sec / 1e9
+    roof = {"bound": "hbm", "kernel": kernel_name, "stage": dom,
+            "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS,
+            "traffic": ctr.get("hbm_bytes_per_launch") if ctr else None,
+            "algorithmic_bytes_per_launch": pbytes,
+            "algorithmic_bytes_basis": "the whole path's minimum HBM traffic: q, k, v read "
+                                       "once, out written once, a and b (fp32), every "
+                                       "touched fp32 state read and written once",
+            "avg_launch_ms": launch[dom], "avg_launch_ms_events": stage_ms[dom],
+            "event_pair_ms": pair_ms}
+    if dom in io:
+        roof["kernel_io_bytes_per_launch"] = io[dom]
+        roof["kernel_io_frac"] = io[dom] / sec / 1e9 / HBM_PEAK_GBS
+    if ctr:
+        roof["counters"] = {kk: ctr[kk] for kk in ("mfma_busy_frac", "mfma_tflops_executed",
+                                                   "read_bytes", "write_bytes") if kk in ctr}
+    stages = {}
+    for n in launch:
+        kn = gdn.STAGE_KERNELS[n] if p.dtype == "bf16" else n
+        c = stored_counters(kn, tag, src_hash)
+        ent = {"launch_ms": launch[n], "events_ms": stage_ms[n]}
+        if n in io:
+            ent["kernel_io_bytes"] = io[n]
+            ent["kernel_io_gbs"] = io[n] / max(launch[n], 1e-9) / 1e-3 / 1e9
+        if c:
+            ent["hbm_bytes_counted"] = c.get("hbm_bytes_per_launch")
+            ent["mfma_busy_frac"] = c.get("mfma_busy_frac")
+            ent["mfma_tflops_executed"] = c.get("mfma_tflops_executed")
+        stages[n] = ent
+    call = {"warm": {"p10": _pct(warm, 10), "median": _pct(warm, 50), "p90": _pct(warm, 90),
+                     "n": len(warm)}}
+    if cold:
+        call["flushed"] = {"p10": _pct(cold, 10), "median": _pct(cold, 50),
+                           "p90": _pct(cold, 90), "n": len(cold)}
+    return {
+        "tag": tag, "N": p.N, "B": p.B, "n_chunks": n_chunks,
+        "ms_per_step": ms_per_step,
+        "tokens_per_s": p.N / (ms_per_step * 1e-3),
+        "call_ms_events": call,
+        "roofline": roof,
+        "effective": {"tflops": flops / (ms_per_step * 1e-3) / 1e12,
+                      "frac_mfma_bf16": flops / (ms_per_step * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS,
+                      "path_gbs": pbytes / (ms_per_step * 1e-3) / 1e9,
+                      "frac_hbm": pbytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                      "algorithmic_flops": flops, "algorithmic_bytes": pbytes},
+        "stages": stages,
+        "kernel_source_hash": src_hash,
+    }
+
+
+def bench_prefill(args):
+    import gdn_synth
+
+    main_idx = args.workload if args.workload is not None else WORKLOAD_INDEX
+    p = gdn_synth.workload(main_idx)
+    m = measure_prefill(p, args.steps, args.warmup, args.cold_steps, args.copy_calibration)
+    res = {
+        "metric": METRIC,
+        "value": m["tokens_per_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": m["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": p.dtype,
+        "data": f"synthetic (seeded SplitMix64/Box-Muller, seed {p.seed})",
+        "config": {"workload": gdn_synth.WORKLOADS[main_idx], "global_batch": p.B,
+                   "seq_len": int(p.N // max(p.B, 1)), "parallelism": "none (1 GPU)"},
+        "roofline": m["roofline"],
+        "effective": m["effective"],
+        "call_ms_events": m["call_ms_events"],
+        "stages": m["stages"],
+        "kernel_source_hash": m["kernel_source_hash"],
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = prefill_cpu_baseline(p)
+    subs = []
+    if args.workload is None and not args.no_sub:
+        del p
+        for wi in SUB_WORKLOADS:
+            sp_ = gdn_synth.workload(wi)
+            sm = measure_prefill(sp_, max(3, args.steps // 2), max(3, args.warmup // 2),
+                                 args.cold_steps)
+            ent = {"workload": gdn_synth.WORKLOADS[wi], "index": wi,
+                   "tokens_per_s": sm["tokens_per_s"], "ms_per_step": sm["ms_per_step"],
+                   "call_ms_events": sm["call_ms_events"],
+                   "path_frac_hbm": sm["effective"]["frac_hbm"],
+                   "effective_tflops": sm["effective"]["tflops"],
+                   "dominant_kernel": sm["roofline"]["kernel"],
+                   "dominant_kernel_frac": sm["roofline"]["frac"],
+                   "roofline": sm["roofline"], "stages": sm["stages"]}
+            if not args.no_cpu_baseline:
+                # the long request's 32 heads: two sampled heads bound the oracle's time
+                heads = [0, sp_.HV - 1] if sp_.N * sp_.HV > (1 << 21) else None
+                ent["cpu_baseline"] = prefill_cpu_baseline(sp_, heads=heads, reps=1)
+            subs.append(ent)
+            del sp_
+        res["workloads"] = subs
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--op", choices=("prefill", "decode", "promote", "verify"),
@@ -592,8 +877,13 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cold-steps", type=int, default=5,
-                    help="extra steps timed one by one after a 512 MiB cache flush")
+    ap.add_argument("--cold-steps", type=int, default=10,
+                    help="extra calls timed one by one after a 512 MiB cache flush")
+    ap.add_argument("--workload", type=int, choices=(0, 1, 2, 3, 4), default=None,
+                    help="time only this named workload (default: workload 1, with "
+                         "workloads 2-4 as sub-results)")
+    ap.add_argument("--no-sub", action="store_true",
+                    help="skip the sub-results for workloads 2-4")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 512 MiB device copy (calibrates HBM byte counters)")
     args = ap.parse_args()
@@ -611,139 +901,7 @@ def main():
         bench_verify(args)
         return
 
-    import numpy as np
-    import torch
-
-    import gdn_synth
-    import gated_deltanet_prefill_gdn_amd as gdn
-
-    p = gdn_synth.workload(WORKLOAD_INDEX)
-    dev = torch.device("cuda:0")
-
-    def t(x, dt=None):
-        x = torch.from_numpy(np.ascontiguousarray(x))
-        return (x.view(dt) if dt is not None else x).to(dev)
-
-    q = t(p.q.view(np.int16), torch.bfloat16)
-    k = t(p.k.view(np.int16), torch.bfloat16)
-    v = t(p.v.view(np.int16), torch.bfloat16)
-    a, b, A_log, dt_bias = t(p.a), t(p.b), t(p.A_log), t(p.dt_bias)
-    pool = t(p.state_pool.copy())
-    idx, cu = t(p.cache_indices), t(p.cu_seqlens)
-    out = torch.empty((p.N, p.HV, p.dv), dtype=torch.bfloat16, device=dev)
-    prob = gdn.problem_of(q, k, v, pool, idx)
-    ws = torch.empty(gdn.gdn_prefill_workspace_size(prob), dtype=torch.uint8, device=dev)
-    stream = torch.cuda.current_stream(dev)
-
-    def step(events=None):
-        if events is None:
-            gdn.gdn_prefill_fwd(q, k, v, a, b, A_log, dt_bias, pool, idx, cu, out=out,
-                                workspace=ws, stream=stream)
-        else:
-            gdn.gdn_prefill_fwd_events(q, k, v, a, b, A_log, dt_bias, pool, idx, cu, events,
-                                       out=out, workspace=ws, stream=stream)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-
-    hip = Hip()
-    nst = gdn.GDN_NUM_STAGES
-    # The K timed steps: plain calls, nothing recorded between them.
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
-    # The same K steps again with HIP events on the launch stream around every stage:
-    # per-kernel launch durations for the roofline.
-    evs = [[hip.event() for _ in range(nst + 1)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    for i in range(args.steps):
-        step(evs[i])
-    torch.cuda.synchronize()
-    stage_ms = {name: float(np.mean([hip.elapsed_ms(e[j], e[j + 1]) for e in evs]))
-                for j, name in enumerate(gdn.STAGE_NAMES)}
-    call_ms = float(np.mean([hip.elapsed_ms(e[0], e[nst]) for e in evs]))
-    for e in evs:
-        for x in e:
-            hip.destroy(x)
-    pair_ms = hip.empty_pair_ms(stream.cuda_stream)
-
-    # cold steps: a 512 MiB write evicts the 256 MiB Infinity Cache before each call
-    cold = []
-    if args.cold_steps > 0:
-        scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
-        ce = [hip.event() for _ in range(nst + 1)]
-        for _ in range(args.cold_steps):
-            scratch.fill_(1)
-            step(ce)
-            torch.cuda.synchronize()
-            cold.append(hip.elapsed_ms(ce[0], ce[nst]))
-        for x in ce:
-            hip.destroy(x)
-        del scratch
-
-    if args.copy_calibration:
-        src = torch.empty(512 << 20, dtype=torch.uint8, device=dev).fill_(3)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
-
-    n_chunks = int(sum((int(L) + p.chunk_size - 1) // p.chunk_size
-                       for L in (p.cu_seqlens[1:] - p.cu_seqlens[:-1])))
-    s_ws = 2   # bytes per element of the fp16 W<- / U~ intermediates (bf16 inputs)
-    sb = stage_bytes(p, 2, s_ws, n_chunks)
-    dom = max(stage_ms, key=stage_ms.get)
-    kernel_name = {"gate": "plan_kernel", "chunk_prep": "mfma_prep_kernel",
-                   "state": "mfma_state_kernel"}[dom]
-    # the launch's duration: its event-timed stage less the overhead of an empty event pair
-    launch_ms = stage_ms[dom] - pair_ms if stage_ms[dom] > 2 * pair_ms else stage_ms[dom]
-    achieved = sb[dom] / (launch_ms * 1e-3) / 1e9
-    src_hash = kernel_source_hash()
-    traffic = stored_traffic(kernel_name, src_hash)
-
-    tok_s = p.N / (ms_per_step * 1e-3)
-    flops = algorithmic_flops_per_token_vhead(p.dk, p.dv, p.chunk_size) * p.N * p.HV
-    pbytes = path_bytes(p, 2)
-    res = {
-        "metric": METRIC,
-        "value": tok_s,
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": ms_per_step,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic (seeded SplitMix64/Box-Muller, seed 1001)",
-        "config": {"workload": "dense batch bf16: B=4 x T=4096, H=HV=16, dk=dv=128, C=64, "
-                               "zero initial state",
-                   "global_batch": p.B, "seq_len": int(p.N // p.B), "parallelism": "none (1 GPU)"},
-        "roofline": {"bound": "hbm", "kernel": kernel_name, "stage": dom,
-                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "algorithmic_bytes_per_launch": sb[dom], "avg_launch_ms": launch_ms,
-                     "avg_launch_ms_events": stage_ms[dom], "event_pair_ms": pair_ms},
-        "effective": {"tflops": flops / (ms_per_step * 1e-3) / 1e12,
-                      "frac_mfma_bf16": flops / (ms_per_step * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS,
-                      "path_gbs": pbytes / (ms_per_step * 1e-3) / 1e9,
-                      "frac_hbm": pbytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                      "algorithmic_flops": flops, "algorithmic_bytes": pbytes},
-        "stage_ms": stage_ms,
-        "call_ms_events": call_ms,
-        "cold_call_ms": float(np.median(cold)) if cold else None,
-        "kernel_source_hash": src_hash,
-    }
-    if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(p)
-    print(json.dumps(res), flush=True)
+    bench_prefill(args)
 
 
 if __name__ == "__main__":

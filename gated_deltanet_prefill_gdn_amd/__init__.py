@@ -28,6 +28,9 @@ GDN_DTYPE_BF16 = 1
 
 GDN_NUM_STAGES = 3
 STAGE_NAMES = ("gate", "chunk_prep", "state")
+# The kernel each stage of a bf16 prefill launches (the profilers' names).
+STAGE_KERNELS = {"gate": "plan_kernel", "chunk_prep": "mfma_prep_kernel",
+                 "state": "mfma_state_kernel"}
 
 EXPORTED = ("gdn_prefill_workspace_size", "gdn_prefill_fwd", "gdn_prefill_fwd_events",
             "gdn_decode_fwd", "gdn_recurrent_fwd", "gdn_promote_scan", "gdn_validate_inputs",

@@ -26,11 +26,13 @@ GDN_ERR_BAD_INPUT = 5
 GDN_DTYPE_F32 = 0
 GDN_DTYPE_BF16 = 1
 
-GDN_NUM_STAGES = 3
-STAGE_NAMES = ("gate", "chunk_prep", "state")
-# The kernel each stage of a bf16 prefill launches (the profilers' names).
+GDN_NUM_STAGES = 5
+STAGE_NAMES = ("gate", "chunk_prep", "state_operator", "state_combine", "state")
+# The kernel each stage of a bf16 prefill launches (the profilers' names; dk = 256 runs the
+# column-slice mfma_state_kernel in the last stage instead).
 STAGE_KERNELS = {"gate": "plan_kernel", "chunk_prep": "mfma_prep_kernel",
-                 "state": "mfma_state_kernel"}
+                 "state_operator": "chain_kernel<operator>", "state_combine": "combine_kernel",
+                 "state": "chain_kernel<out>"}
 
 EXPORTED = ("gdn_prefill_workspace_size", "gdn_prefill_fwd", "gdn_prefill_fwd_events",
             "gdn_decode_fwd", "gdn_recurrent_fwd", "gdn_promote_scan", "gdn_validate_inputs",

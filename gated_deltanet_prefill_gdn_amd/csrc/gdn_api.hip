@@ -42,6 +42,11 @@ WsLayout layout_for(const Shape& s, Path p) {
   if (p == Path::kMfma) off = align256(off + 2 * mc * s.HV * s.C * s.dk);
   L.qf = off;
   if (p == Path::kMfma) off = align256(off + 2 * mc * s.H * s.C * s.dk);
+  const ChainPlan cp = p == Path::kMfma ? chain_plan(s) : ChainPlan{};
+  L.rp = off;
+  off = align256(off + chain_rp_bytes(s, cp));
+  L.sstart = off;
+  off = align256(off + chain_sstart_bytes(s, cp));
   L.total = off;
   return L;
 }
@@ -161,20 +166,33 @@ gdn_status_t run_prefill(const void* q, const void* k, const void* v, const floa
     if (launch_mfma_prep(q, k, v, cu_seqlens, chunk_off, chunk_seq, self_plan, a, b, A_log,
                          dt_bias, s, L.max_chunks, w, u, aqk, eg, kf, qf, st) != hipSuccess)
       return GDN_ERR_HIP;
-    if (!mark(2)) return GDN_ERR_HIP;
-    if (launch_mfma_state(qf, kf, cu_seqlens, cache_indices, chunk_off, w, u, aqk, eg, s,
-                          state_pool, out, st) != hipSuccess)
-      return GDN_ERR_HIP;
+    const ChainPlan cp = chain_plan(s);
+    if (cp.use) {
+      float* rp = (float*)(ws + L.rp);
+      float* sstart = (float*)(ws + L.sstart);
+      for (int stage = 0; stage < 3; ++stage) {
+        if (!mark(2 + stage)) return GDN_ERR_HIP;
+        if ((stage < 2 && !cp.segmented)) continue;  // nothing is cut: one pass
+        if (launch_chain(cp, s, qf, kf, cu_seqlens, cache_indices, chunk_off, w, u, aqk, eg, rp,
+                         sstart, state_pool, out, stage, st) != hipSuccess)
+          return GDN_ERR_HIP;
+      }
+    } else {
+      if (!mark(2) || !mark(3) || !mark(4)) return GDN_ERR_HIP;
+      if (launch_mfma_state(qf, kf, cu_seqlens, cache_indices, chunk_off, w, u, aqk, eg, s,
+                            state_pool, out, st) != hipSuccess)
+        return GDN_ERR_HIP;
+    }
   } else {
     if (launch_ref_prep(k, v, cu_seqlens, chunk_off, chunk_seq, gcum, beta, s, L.max_chunks,
                         (float*)w, (float*)u, st) != hipSuccess)
       return GDN_ERR_HIP;
-    if (!mark(2)) return GDN_ERR_HIP;
+    if (!mark(2) || !mark(3) || !mark(4)) return GDN_ERR_HIP;
     if (launch_ref_state(q, k, cu_seqlens, cache_indices, chunk_off, gcum, (const float*)w,
                          (const float*)u, s, state_pool, out, st) != hipSuccess)
       return GDN_ERR_HIP;
   }
-  if (!mark(3)) return GDN_ERR_HIP;
+  if (!mark(5)) return GDN_ERR_HIP;
   return GDN_OK;
 }
 

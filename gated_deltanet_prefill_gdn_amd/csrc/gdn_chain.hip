@@ -1,0 +1,551 @@
+// Sequential state pass over chunks with whole state blocks per workgroup, and the scan over
+// segments of a long request (bf16 inputs, dk <= 128).
+//
+// Per chunk, in row convention (pymllm gdn_chunkwise page, Algorithm steps 2-3; "Simple
+// math to speed up GDN prefill", Reminder, the chunkwise transition with decorated S->,
+// W<-, K->):
+//   U     = U~ - W<- S^T
+//   O     = diag(e^G) Qh S^T + A_qk U                                   (to out)
+//   S^T  <- e^{G_n} S^T + K~^T U,   K~ = diag(e^{G_n - G} r_k) K
+// The chunk-prep kernel has already formed W<-, U~, K~, Qh = diag(r_q) Q, A_qk and e^G
+// (they depend on no state) in MFMA fragment order.
+//
+// One chunk's transition is an affine map of the state: S -> S A_c + U~^T K~ with the
+// dk x dk operator A_c = e^{G_n} I - W<-^T K~. A request of many chunks is therefore cut
+// into segments of at most `lseg` chunks (pymllm page: the inter-chunk propagation is the
+// only sequential part):
+//   operator pass  every segment but the last runs its chunks from the zero state (R_g)
+//                  and from the identity with U~ = 0 (P_g, the product of its operators);
+//   combine        S_{g+1} = S_g P_g + R_g in fp32, in order, from the slot's state;
+//   output pass    every segment runs its chunks again from its true start state S_g,
+//                  writing O; the last one writes the final state back into the slot.
+// Segments of one request run on different compute units, so the chain each workgroup
+// walks is at most lseg chunks long.
+//
+// Workgroup: four compute waves and one loader wave. Compute wave w holds 32 columns of
+// S^T (state rows of the value head; or columns of P) over all of dk in fp32 registers,
+// as MFMA accumulator tiles, and does every product of its columns itself: nothing is
+// exchanged between compute waves. The operands every column needs (W<-, K~, Qh, A_qk,
+// e^G; and the workgroup's columns of U~) are staged once per workgroup by the loader
+// wave with direct global-to-LDS loads into a ring of two chunk slots, one chunk ahead of
+// the compute waves; one barrier per chunk hands a slot over. Compute waves issue no
+// global loads inside the chunk loop, only the stores of O.
+//
+// Matrix-core operands are fp16 with fp32 accumulation: W<- and S for W<- S^T; Qh and S
+// for Qh S^T; A_qk and U for A_qk U; K~ and U for the update. The state stays fp32.
+#include <stdint.h>
+
+#include <algorithm>
+
+#include "gdn_internal.h"
+#include "gdn_mfma.h"
+
+namespace gdn {
+namespace {
+
+using namespace mfma;
+constexpr int C = 64;
+constexpr int kComputeWaves = 4;
+constexpr int kChainThreads = 64 * (kComputeWaves + 1);
+constexpr int kColsPerWave = 32;
+constexpr int kColsPerBlock = kComputeWaves * kColsPerWave;  // 128 state columns
+
+typedef __attribute__((address_space(3))) void* lds_ptr;
+
+// Roles of a workgroup.
+enum : int { kRoleOut = 0, kRoleR = 1, kRoleP = 2 };
+// Kernel modes: the output pass (role out) or the operator pass (roles R and P).
+enum : int { kModeOut = 0, kModeOperator = 1 };
+
+// s_waitcnt vmcnt(N), the other counters not waited for (gfx9 encoding: vmcnt in bits 3:0
+// and 15:14, expcnt 6:4, lgkmcnt 11:8).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// One ring slot: every operand of one chunk, each fragment 1 KiB (lane l's 16 bytes at
+// offset 16 l), exactly as the chunk prep wrote them.
+template <int DK, int MODE>
+struct Slot {
+  static constexpr int NKS = DK / 32;
+  static constexpr int FW = 4 * NKS;                        // W<-: 4 token tiles x dk steps
+  static constexpr int FK = (DK / 16) * 2;                  // K~^T: dk tiles x 2 token steps
+  static constexpr int FQ = MODE == kModeOut ? 4 * NKS : 0; // Qh: 4 token tiles x dk steps
+  static constexpr int FA = MODE == kModeOut ? 8 : 0;       // A_qk: 4 token tiles x 2 steps
+  static constexpr int FU = kColsPerBlock / 8;              // U~: 2 D tiles per KiB
+  half8 w[FW][64];
+  half8 k[FK][64];
+  half8 q[FQ > 0 ? FQ : 1][64];
+  half8 a[FA > 0 ? FA : 1][64];
+  half8 u[FU][64];
+  float eg[C];
+};
+
+template <int DK, int MODE>
+struct ChainSmem {
+  Slot<DK, MODE> s[2];
+};
+
+struct ChainArgs {
+  const _Float16* W;    // W<-  [chunk][HV][C*dk]
+  const _Float16* U;    // U~   [chunk][HV][C*dv]
+  const _Float16* Kf;   // K~   [chunk][HV][C*dk]
+  const _Float16* Qf;   // Qh   [chunk][H][C*dk]
+  const _Float16* Aqk;  // A_qk [chunk][HV][C*C]
+  const float* eg;      // e^G  [chunk][HV][C]
+  const int64_t* cu;
+  const int64_t* cache_indices;
+  const int32_t* chunk_off;
+  float* state_pool;
+  uint16_t* out;
+  float* rp;      // [segment][HV][dv + dk][dk]: R_g rows, then P_g rows
+  float* sstart;  // [segment][HV][dv][dk]: start state of every segment of a cut request
+  int B, H, HV, DV;
+  int lseg;       // chunks per segment
+  int segmented;  // requests may be cut (at most 64 requests)
+  int nb;         // workgroups per (segment, value head)
+  int nb_r;       // of which (operator pass) hold columns of R
+  int64_t units;  // segments x value heads covered by the grid
+};
+
+// Segment sg of the call -> its request b, its index j in the request and the request's
+// segment count. With cut requests (B <= 64) every wave forms the segment table with one
+// scan: request b has ceil(ceil(L_b / C) / lseg) segments. Returns false past the last
+// segment.
+__device__ __forceinline__ bool find_segment(const ChainArgs& a, int64_t sg, int l, int& b,
+                                             int& j, int& nseg, int& seg0) {
+  if (!a.segmented) {
+    if (sg >= a.B) return false;
+    b = (int)sg;
+    j = 0;
+    nseg = 1;
+    seg0 = (int)sg;
+    return true;
+  }
+  int ns = 0;
+  if (l < a.B) {
+    const int64_t L = a.cu[l + 1] - a.cu[l];
+    const int64_t nch = (L + C - 1) / C;
+    ns = (int)((nch + a.lseg - 1) / a.lseg);
+  }
+  int incl = ns;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(incl, off, 64);
+    if (l >= off) incl += y;
+  }
+  const int total = __shfl(incl, 63, 64);
+  if (sg >= total) return false;
+  // the owner of segment sg: the number of requests whose segments all precede it
+  b = __popcll(__ballot(l < a.B && incl <= sg));
+  const int incl_b = __shfl(incl, b, 64);
+  nseg = __shfl(ns, b, 64);
+  seg0 = incl_b - nseg;
+  j = (int)sg - seg0;
+  return true;
+}
+
+template <int DK, int MODE>
+__global__ __launch_bounds__(kChainThreads, 1) void chain_kernel(ChainArgs a) {
+  constexpr int NKS = DK / 32;  // 32-wide dk steps
+  constexpr int NDT = DK / 16;  // 16-row dk tiles
+  using Sl = Slot<DK, MODE>;
+  __shared__ ChainSmem<DK, MODE> sm;
+
+  const int tid = threadIdx.x, wv = tid >> 6, l = tid & 63, m = l & 15, g = l >> 4;
+  // The nb workgroups of one (segment, value head) share blockIdx.x mod 8, so they run on
+  // one XCD and read the chunk blocks once from its L2.
+  const int64_t x = blockIdx.x;
+  const int64_t rest = x >> 3;
+  const int blk = (int)(rest % a.nb);
+  const int64_t unit = (rest / a.nb) * 8 + (x & 7);
+  if (unit >= a.units) return;
+  const int64_t sg = unit / a.HV;
+  const int hv = (int)(unit % a.HV);
+  int b, j, nseg, seg0;
+  if (!find_segment(a, sg, l, b, j, nseg, seg0)) return;
+  const int64_t L = a.cu[b + 1] - a.cu[b];
+  if (L <= 0) return;
+  const int nch = (int)((L + C - 1) / C);
+  const int c_lo = j * a.lseg;
+  const int n = min(c_lo + a.lseg, nch) - c_lo;  // chunks of this segment (>= 1)
+
+  int role, colbase, ncols;
+  if constexpr (MODE == kModeOut) {
+    role = kRoleOut;
+    colbase = blk * kColsPerBlock;
+    ncols = min(kColsPerBlock, a.DV - colbase);
+  } else {
+    if (nseg < 2 || j == nseg - 1) return;  // the last segment's operator is never used
+    if (blk < a.nb_r) {
+      role = kRoleR;
+      colbase = blk * kColsPerBlock;
+      ncols = min(kColsPerBlock, a.DV - colbase);
+    } else {
+      role = kRoleP;
+      colbase = (blk - a.nb_r) * kColsPerBlock;
+      ncols = min(kColsPerBlock, DK - colbase);
+    }
+  }
+  const int h = hv / (a.HV / a.H);
+  const int64_t slot = a.cache_indices[b];
+  const int64_t cbase = (int64_t)a.chunk_off[b] + c_lo;  // global index of chunk 0
+  const int64_t tseq = a.cu[b] + (int64_t)c_lo * C;      // first token of chunk 0
+  const int64_t tend = a.cu[b + 1];
+  const bool use_u = role != kRoleP;
+
+  if (wv == kComputeWaves) {
+    // ======================= loader wave =======================
+    auto issue = [&](int cl) {
+      Sl& s = sm.s[cl & 1];
+      const int64_t pair = (cbase + cl) * a.HV + hv;
+      const char* wsrc = reinterpret_cast<const char*>(a.W + pair * C * DK) + 16 * l;
+      const char* ksrc = reinterpret_cast<const char*>(a.Kf + pair * C * DK) + 16 * l;
+#pragma unroll
+      for (int f = 0; f < Sl::FW; ++f)
+        __builtin_amdgcn_global_load_lds((const void*)(wsrc + 1024 * f), (lds_ptr)&s.w[f][0], 16,
+                                         0, 0);
+#pragma unroll
+      for (int f = 0; f < Sl::FK; ++f)
+        __builtin_amdgcn_global_load_lds((const void*)(ksrc + 1024 * f), (lds_ptr)&s.k[f][0], 16,
+                                         0, 0);
+      if constexpr (MODE == kModeOut) {
+        const char* qsrc =
+            reinterpret_cast<const char*>(a.Qf + ((cbase + cl) * a.H + h) * (int64_t)(C * DK)) +
+            16 * l;
+        const char* asrc = reinterpret_cast<const char*>(a.Aqk + pair * C * C) + 16 * l;
+#pragma unroll
+        for (int f = 0; f < Sl::FQ; ++f)
+          __builtin_amdgcn_global_load_lds((const void*)(qsrc + 1024 * f), (lds_ptr)&s.q[f][0],
+                                           16, 0, 0);
+        // A_qk fragments (token tile I, token step st) = 2 I + st; the two above the
+        // diagonal (I < 2, st = 1) are zero and were never written
+#pragma unroll
+        for (int f = 0; f < 8; ++f)
+          if (f != 1 && f != 3)
+            __builtin_amdgcn_global_load_lds((const void*)(asrc + 1024 * f), (lds_ptr)&s.a[f][0],
+                                             16, 0, 0);
+      }
+      if (use_u) {
+        // the workgroup's 8 column tiles of U~: 16 contiguous KiB
+        const char* usrc =
+            reinterpret_cast<const char*>(a.U + pair * C * a.DV + (int64_t)colbase * C) + 16 * l;
+        const int nu = ncols / 8;  // KiB pieces of this block's columns
+        for (int f = 0; f < nu; ++f)
+          __builtin_amdgcn_global_load_lds((const void*)(usrc + 1024 * f), (lds_ptr)&s.u[f][0],
+                                           16, 0, 0);
+      }
+      __builtin_amdgcn_global_load_lds((const void*)(a.eg + pair * C + l), (lds_ptr)&s.eg[0], 4,
+                                       0, 0);
+    };
+    issue(0);
+    for (int cl = 0; cl < n; ++cl) {
+      wait_vmcnt<0>();  // chunk cl has landed in its slot
+      lds_barrier();    // hand slot cl & 1 over; slot (cl + 1) & 1 is free again
+      if (cl + 1 < n) issue(cl + 1);
+    }
+    return;
+  }
+
+  // ======================= compute waves =======================
+  const bool active = kColsPerWave * wv < ncols;
+  const int col0 = colbase + kColsPerWave * wv;  // first state column of this wave
+  // S^T tiles: dk rows 16 dt + 4 g + i, column col0 + 16 ct + m (fp32)
+  f32x4 S[NDT][2];
+  float* Sinit = nullptr;
+  if (role == kRoleOut)
+    Sinit = (nseg >= 2) ? a.sstart + ((sg * a.HV + hv) * (int64_t)a.DV + col0) * DK
+                        : a.state_pool + ((slot * a.HV + hv) * (int64_t)a.DV + col0) * DK;
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+      if (role == kRoleOut && active) {
+        S[dt][ct] = *reinterpret_cast<const f32x4*>(Sinit + (16 * ct + m) * DK + 16 * dt + 4 * g);
+      } else if (role == kRoleP) {
+        // identity: row 16 dt + 4 g + i equals column col0 + 16 ct + m
+        const int d = col0 + 16 * ct + m - (16 * dt + 4 * g);
+        S[dt][ct] = f32x4{d == 0 ? 1.f : 0.f, d == 1 ? 1.f : 0.f, d == 2 ? 1.f : 0.f,
+                          d == 3 ? 1.f : 0.f};
+      } else {
+        S[dt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+  const int wct = 2 * wv;  // this wave's first column tile inside the block
+
+  for (int cl = 0; cl < n; ++cl) {
+    lds_barrier();  // chunk cl's operands are in slot cl & 1
+    if (!active) continue;
+    const Sl& s = sm.s[cl & 1];
+    // ---- fp16 copy of S^T: B operand (k = dk) of W<- S^T and A operand of S Qh^T
+    half8 s16[NKS][2];
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct)
+        s16[ks][ct] = cat(to_half4(S[2 * ks][ct]), to_half4(S[2 * ks + 1][ct]));
+    // ---- -U = W<- S^T - U~ (token tile tt, column tile ct)
+    f32x4 nu[4][2];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) {
+        if (use_u) {
+          const u32x2 ur = *reinterpret_cast<const u32x2*>(
+              reinterpret_cast<const _Float16*>(&s.u[0][0]) + (((wct + ct) * 4 + tt) * 64 + l) * 4);
+          const half4 uh = __builtin_bit_cast(half4, ur);
+          nu[tt][ct] = f32x4{-(float)uh[0], -(float)uh[1], -(float)uh[2], -(float)uh[3]};
+        } else {
+          nu[tt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+      }
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) {
+        const half8 wf = s.w[tt * NKS + ks][l];
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) nu[tt][ct] = mma_f16(wf, s16[ks][ct], nu[tt][ct]);
+      }
+    // ---- U in fp16, tokens 32 ts + kperm: B operand of the update, A operand of U^T A_qk^T
+    half8 u16[2][2];
+#pragma unroll
+    for (int ts = 0; ts < 2; ++ts)
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct)
+        u16[ts][ct] = cat(to_half4(-nu[2 * ts][ct]), to_half4(-nu[2 * ts + 1][ct]));
+
+    if constexpr (MODE == kModeOut) {
+      // ---- O^T = diag(e^G)-scaled S Qh^T + U^T A_qk^T: lane (m, g) of tile (ct, tt) holds
+      // columns 16 ct + 4 g .. + 3 of token 16 tt + m
+      const int64_t t0 = tseq + (int64_t)cl * C;
+      const int nrow = (int)min((int64_t)C, tend - t0);
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) {
+        f32x4 o[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+          const half8 qf = s.q[tt * NKS + ks][l];
+#pragma unroll
+          for (int ct = 0; ct < 2; ++ct) o[ct] = mma_f16(s16[ks][ct], qf, o[ct]);
+        }
+        const float er = s.eg[16 * tt + m];
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) o[ct] *= er;
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+          if (st == 1 && tt < 2) continue;  // causal: A_qk is zero above the diagonal
+          const half8 af = s.a[2 * tt + st][l];
+#pragma unroll
+          for (int ct = 0; ct < 2; ++ct) o[ct] = mma_f16(u16[st][ct], af, o[ct]);
+        }
+        const int r = 16 * tt + m;
+        if (r < nrow) {
+          __bf16* orow = reinterpret_cast<__bf16*>(a.out) + ((t0 + r) * a.HV + hv) * (int64_t)a.DV +
+                         col0 + 4 * g;
+#pragma unroll
+          for (int ct = 0; ct < 2; ++ct) {
+            bf16x4 ov;
+            ov[0] = (__bf16)o[ct][0];
+            ov[1] = (__bf16)o[ct][1];
+            ov[2] = (__bf16)o[ct][2];
+            ov[3] = (__bf16)o[ct][3];
+            *reinterpret_cast<bf16x4*>(orow + 16 * ct) = ov;
+          }
+        }
+      }
+    }
+
+    // ---- S^T <- e^{G_n} S^T + K~^T U (e^{G_n}: e^G of the chunk's last row; padding rows
+    // do not decay)
+    const float egn = s.eg[C - 1];
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) {
+        f32x4 acc = S[dt][ct] * egn;
+#pragma unroll
+        for (int ts = 0; ts < 2; ++ts) acc = mma_f16(s.k[dt * 2 + ts][l], u16[ts][ct], acc);
+        S[dt][ct] = acc;
+      }
+  }
+
+  if (!active) return;
+  // ---- the state at the end of the segment
+  float* dst = nullptr;
+  if (role == kRoleOut) {
+    if (j != nseg - 1) return;  // a later segment carries the request on
+    dst = a.state_pool + ((slot * a.HV + hv) * (int64_t)a.DV + col0) * DK;
+  } else {
+    const int64_t base = (sg * a.HV + hv) * (int64_t)(a.DV + DK);
+    dst = a.rp + (base + (role == kRoleR ? 0 : a.DV) + col0) * DK;
+  }
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct)
+      *reinterpret_cast<f32x4*>(dst + (16 * ct + m) * DK + 16 * dt + 4 * g) = S[dt][ct];
+}
+
+// Combine: for every cut request and value head, in segment order from the slot's state,
+// S_{g+1} = S_g P_g + R_g (fp32), each S_g stored as the start state of segment g. One
+// workgroup per (request, value head, 16 state rows); thread (row i, column group cg)
+// forms DK / 16 consecutive columns of row i. P_g is staged in LDS per step.
+template <int DK>
+__global__ __launch_bounds__(256) void combine_kernel(ChainArgs a) {
+  constexpr int CPT = DK / 16;  // columns per thread
+  __shared__ float Ps[DK][DK];
+  __shared__ float Ss[16][DK];
+  const int tid = threadIdx.x, l = tid & 63;
+  const int rb = a.DV / 16;
+  const int64_t x = blockIdx.x;
+  const int r0 = (int)(x % rb) * 16;
+  const int64_t p = x / rb;
+  const int b = (int)(p / a.HV), hv = (int)(p % a.HV);
+  if (b >= a.B) return;
+  // the request's segment count and first segment (every wave forms the table)
+  int ns = 0;
+  if (l < a.B) {
+    const int64_t L = a.cu[l + 1] - a.cu[l];
+    const int64_t nch = (L + C - 1) / C;
+    ns = (int)((nch + a.lseg - 1) / a.lseg);
+  }
+  int incl = ns;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(incl, off, 64);
+    if (l >= off) incl += y;
+  }
+  const int nseg = __shfl(ns, b, 64);
+  const int seg0 = __shfl(incl, b, 64) - nseg;
+  if (nseg < 2) return;
+  const int64_t slot = a.cache_indices[b];
+  const int i = tid >> 4, cg = tid & 15;
+  const float* S0 = a.state_pool + ((slot * a.HV + hv) * (int64_t)a.DV + r0) * DK;
+  for (int e = tid; e < 16 * DK; e += 256) Ss[e / DK][e % DK] = S0[e];
+  __syncthreads();
+  for (int jj = 0;; ++jj) {
+    const int64_t sgj = seg0 + jj;
+    float* St = a.sstart + ((sgj * a.HV + hv) * (int64_t)a.DV + r0) * DK;
+    for (int e = tid; e < 16 * DK; e += 256) St[e] = Ss[e / DK][e % DK];
+    if (jj == nseg - 1) break;
+    const int64_t base = (sgj * a.HV + hv) * (int64_t)(a.DV + DK);
+    const float* R = a.rp + (base + r0) * DK;
+    const float* P = a.rp + (base + a.DV) * DK;
+    for (int e = tid * 4; e < DK * DK; e += 256 * 4)
+      *reinterpret_cast<f32x4*>(&Ps[e / DK][e % DK]) = *reinterpret_cast<const f32x4*>(P + e);
+    float acc[CPT];
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) acc[c] = R[i * DK + cg * CPT + c];
+    __syncthreads();
+    for (int jd = 0; jd < DK; ++jd) {
+      const float sv = Ss[i][jd];
+#pragma unroll
+      for (int c = 0; c < CPT; ++c) acc[c] = fmaf(sv, Ps[jd][cg * CPT + c], acc[c]);
+    }
+    __syncthreads();  // every thread has read Ss and Ps
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) Ss[i][cg * CPT + c] = acc[c];
+    __syncthreads();
+  }
+}
+
+}  // namespace
+
+ChainPlan chain_plan(const Shape& s) {
+  ChainPlan p;
+  p.use = s.bf16 && s.dk <= 128 && s.C == C;
+  if (!p.use) return p;
+  p.nb = (s.dv + kColsPerBlock - 1) / kColsPerBlock;
+  p.nb_r = p.nb;
+  p.nb_op = p.nb + (s.dk + kColsPerBlock - 1) / kColsPerBlock;
+  const int64_t mc = s.N / s.C + s.B;  // upper bound on the call's chunks
+  p.segmented = s.B <= kMaxSelfPlanRequests;
+  if (p.segmented) {
+    // segments of about the length that gives every compute unit one output workgroup
+    const int64_t target = 256;
+    int64_t lseg = (mc * s.HV * p.nb + target - 1) / target;
+    lseg = std::max<int64_t>(lseg, 16);
+    p.lseg = (int)std::min<int64_t>(lseg, 1 << 30);
+    p.max_segs = mc / p.lseg + s.B;
+  } else {
+    p.lseg = 1 << 30;
+    p.max_segs = s.B;
+  }
+  return p;
+}
+
+size_t chain_rp_bytes(const Shape& s, const ChainPlan& p) {
+  if (!p.use || !p.segmented) return 0;
+  return sizeof(float) * (size_t)p.max_segs * s.HV * (size_t)(s.dv + s.dk) * s.dk;
+}
+size_t chain_sstart_bytes(const Shape& s, const ChainPlan& p) {
+  if (!p.use || !p.segmented) return 0;
+  return sizeof(float) * (size_t)p.max_segs * s.HV * (size_t)s.dv * s.dk;
+}
+
+int64_t chain_grid(const Shape& s, const ChainPlan& p, int stage) {
+  const int64_t units = p.max_segs * s.HV;
+  const int nb = stage == 0 ? p.nb_op : p.nb;
+  if (stage == 1) return (int64_t)s.B * s.HV * (s.dv / 16);
+  return (units + 7) / 8 * 8 * nb;
+}
+
+hipError_t launch_chain(const ChainPlan& p, const Shape& s, const void* qf, const void* kf,
+                        const int64_t* cu, const int64_t* cache_indices, const int32_t* chunk_off,
+                        const void* w, const void* u, const void* aqk, const float* eg,
+                        float* rp, float* sstart, float* state_pool, void* out, int stage,
+                        hipStream_t st) {
+  ChainArgs a;
+  a.W = (const _Float16*)w;
+  a.U = (const _Float16*)u;
+  a.Kf = (const _Float16*)kf;
+  a.Qf = (const _Float16*)qf;
+  a.Aqk = (const _Float16*)aqk;
+  a.eg = eg;
+  a.cu = cu;
+  a.cache_indices = cache_indices;
+  a.chunk_off = chunk_off;
+  a.state_pool = state_pool;
+  a.out = (uint16_t*)out;
+  a.rp = rp;
+  a.sstart = sstart;
+  a.B = (int)s.B;
+  a.H = s.H;
+  a.HV = s.HV;
+  a.DV = s.dv;
+  a.lseg = p.lseg;
+  a.segmented = p.segmented ? 1 : 0;
+  a.nb_r = p.nb_r;
+  a.units = p.max_segs * s.HV;
+  const int64_t grid = chain_grid(s, p, stage);
+  if (grid <= 0) return hipSuccess;
+  if (stage == 0) {  // operator pass
+    a.nb = p.nb_op;
+    if (s.dk == 64)
+      hipLaunchKernelGGL((chain_kernel<64, kModeOperator>), dim3((unsigned)grid),
+                         dim3(kChainThreads), 0, st, a);
+    else
+      hipLaunchKernelGGL((chain_kernel<128, kModeOperator>), dim3((unsigned)grid),
+                         dim3(kChainThreads), 0, st, a);
+  } else if (stage == 1) {  // combine
+    a.nb = p.nb;
+    if (s.dk == 64)
+      hipLaunchKernelGGL((combine_kernel<64>), dim3((unsigned)grid), dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL((combine_kernel<128>), dim3((unsigned)grid), dim3(256), 0, st, a);
+  } else {  // output pass
+    a.nb = p.nb;
+    if (s.dk == 64)
+      hipLaunchKernelGGL((chain_kernel<64, kModeOut>), dim3((unsigned)grid), dim3(kChainThreads),
+                         0, st, a);
+    else
+      hipLaunchKernelGGL((chain_kernel<128, kModeOut>), dim3((unsigned)grid),
+                         dim3(kChainThreads), 0, st, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace gdn

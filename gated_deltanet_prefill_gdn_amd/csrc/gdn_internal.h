@@ -34,6 +34,10 @@ struct WsLayout {
                            //        the state update's fragment order (kMfma only)
   size_t qf = 0;           // fp16   [max_chunks][H][C][dk]: normalised q in the state
                            //        pass's fragment order (kMfma only)
+  size_t rp = 0;           // float  [segments][HV][dv + dk][dk]: each cut segment's state from
+                           //        zero (R) and its operator product (P) (segment scan only)
+  size_t sstart = 0;       // float  [segments][HV][dv][dk]: start state of every segment of a
+                           //        cut request (segment scan only)
   size_t total = 0;
 };
 
@@ -78,6 +82,28 @@ hipError_t launch_mfma_state(const void* qf, const void* kf, const int64_t* cu_s
                              const void* w, const void* u, const void* aqk,
                              const float* eg, const Shape& s, float* state_pool, void* out,
                              hipStream_t st);
+
+// The state pass with whole 128-column state blocks per workgroup and the segment scan of
+// long requests (bf16 inputs, dk <= 128).
+struct ChainPlan {
+  bool use = false;        // this pass serves the call (else the column-slice state kernel)
+  bool segmented = false;  // requests may be cut into segments (at most 64 requests)
+  int lseg = 1 << 30;      // chunks per segment
+  int nb = 1;              // output-pass workgroups per (segment, value head)
+  int nb_r = 1;            // operator-pass workgroups per (segment, value head) holding R
+  int nb_op = 2;           // operator-pass workgroups per (segment, value head): R and P
+  int64_t max_segs = 0;    // upper bound on the call's segments
+};
+ChainPlan chain_plan(const Shape& s);
+size_t chain_rp_bytes(const Shape& s, const ChainPlan& p);
+size_t chain_sstart_bytes(const Shape& s, const ChainPlan& p);
+// Workgroups of a stage's launch: 0 operator pass, 1 combine, 2 output pass.
+int64_t chain_grid(const Shape& s, const ChainPlan& p, int stage);
+hipError_t launch_chain(const ChainPlan& p, const Shape& s, const void* qf, const void* kf,
+                        const int64_t* cu, const int64_t* cache_indices, const int32_t* chunk_off,
+                        const void* w, const void* u, const void* aqk, const float* eg,
+                        float* rp, float* sstart, float* state_pool, void* out, int stage,
+                        hipStream_t st);
 
 // Decode step (one token per request): workgroups a launch needs, and the launcher.
 int64_t decode_blocks(const Shape& s);

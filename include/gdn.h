@@ -95,11 +95,15 @@ gdn_status_t gdn_prefill_fwd(const void* q, const void* k, const void* v, const 
                              void* stream);
 
 /* Stages of one call, in launch order, for gdn_prefill_fwd_events. */
-#define GDN_NUM_STAGES 3 /* 0: chunk table (and, for fp32 inputs, the gates and log
+#define GDN_NUM_STAGES 5 /* 0: chunk table (and, for fp32 inputs, the gates and log
                             cumulative decay; for bf16 inputs of at most 64 requests the
                             chunk prep forms the table and this stage launches nothing);
                             1: chunk prep (for bf16 inputs including the gates; Grams, the
-                            one inverse, W<- and U~); 2: state pass + outputs */
+                            one inverse, W<- and U~); 2: operator pass of the segment scan
+                            (requests cut into segments: each segment's state from zero and
+                            its transition operator); 3: combine (every segment's start
+                            state); 4: state pass + outputs. Stages 2 and 3 launch nothing
+                            when no request is cut. */
 
 /* gdn_prefill_fwd with timing marks: stage_events points to GDN_NUM_STAGES + 1
  * hipEvent_t handles created by the caller on the current device; event i is recorded

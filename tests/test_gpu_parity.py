@@ -78,6 +78,31 @@ def test_workspace_offsets_beyond_2gib():
     announce(f"big-offsets: max(|do| - 2^-8|o|)/rms = {float(err.max()) / rms:.3e}")
 
 
+# ------------------------------------------------------------- segment scan
+@pytest.mark.parametrize("case", ["nine-segments", "dk64-mixed", "dv256", "strong-decay"])
+def test_segment_scan(case):
+    """Requests long enough to be cut into segments (operator pass, combine, output pass):
+    nine segments of 16 chunks (the shortest cut) with a ragged tail under slow decay, so
+    that each segment's operator product is far from zero and the combine carries the state
+    across every cut; dk = 64 with an empty and a one-token request between two cut ones;
+    dv = 256 (two 128-column blocks per head); and the dense workload's strong decay, where
+    the operators vanish."""
+    if case == "nine-segments":
+        p = gdn_synth.make_problem(61, [8192 + 37], 2, 2, 128, 128, dtype="bf16",
+                                   a_mean=-4.0, b_mean=2.0, state_std=0.1)
+    elif case == "dk64-mixed":
+        p = gdn_synth.make_problem(62, [5000, 0, 1, 3001], 1, 2, 64, 64, dtype="bf16", pool=6,
+                                   cache_indices=[5, 0, 2, 3], a_mean=-4.0, state_std=0.2)
+    elif case == "dv256":
+        p = gdn_synth.make_problem(63, [4100], 1, 1, 128, 256, dtype="bf16", a_mean=-4.0,
+                                   b_mean=1.0, state_std=0.1)
+    else:
+        p = gdn_synth.make_problem(64, [4096, 2048], 2, 2, 128, 128, dtype="bf16", state_std=0.1)
+    out, pool, _ = run_gpu(p, f"segments-{case}")
+    rep = compare(p, out, pool, oracle.prefill(p))
+    announce(f"segments-{case} {rep}")
+
+
 # ------------------------------------------------------------- edge cases
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_ragged_lengths(dtype):
@@ -220,11 +245,14 @@ def test_split_invariance_through_slot():
 
 
 def test_determinism_bitwise():
-    p = gdn_synth.make_problem(39, [500, 130], 2, 4, 128, 128, dtype="bf16", state_std=0.1)
-    o1, s1, _ = run_gpu(p, "det-1")
-    o2, s2, _ = run_gpu(p, "det-2")
-    np.testing.assert_array_equal(o1, o2)
-    np.testing.assert_array_equal(s1, s2)
+    """Ten calls on the same inputs (one cut into segments, one not) give bit-identical
+    outputs and states: no race between the waves, workgroups or passes of a call."""
+    p = gdn_synth.make_problem(39, [3000, 130], 2, 4, 128, 128, dtype="bf16", state_std=0.1)
+    o1, s1, _ = run_gpu(p, "det-0")
+    for i in range(1, 10):
+        o2, s2, _ = run_gpu(p, f"det-{i}")
+        np.testing.assert_array_equal(o1, o2)
+        np.testing.assert_array_equal(s1, s2)
 
 
 def test_validate_inputs():

@@ -36,6 +36,8 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <type_traits>
+#include <utility>
 
 #include "gdn_internal.h"
 #include "gdn_mfma.h"
@@ -46,16 +48,25 @@ namespace {
 using namespace mfma;
 constexpr int C = 64;
 constexpr int kComputeWaves = 4;
-constexpr int kChainThreads = 64 * (kComputeWaves + 1);
+#ifndef GDN_CHAIN_LOADERS
+#define GDN_CHAIN_LOADERS 1
+#endif
+constexpr int kLoaderWaves = GDN_CHAIN_LOADERS;
 constexpr int kColsPerWave = 32;
 constexpr int kColsPerBlock = kComputeWaves * kColsPerWave;  // 128 state columns
 
 typedef __attribute__((address_space(3))) void* lds_ptr;
 
-// Roles of a workgroup.
+// Roles of a compute wave.
 enum : int { kRoleOut = 0, kRoleR = 1, kRoleP = 2 };
-// Kernel modes: the output pass (role out) or the operator pass (roles R and P).
+// Kernel modes: the output pass (four compute waves, role out) or the operator pass (four
+// compute waves of role R, whose state starts at zero, and four of role P, whose state
+// starts at the identity and sees U~ = 0; the two share every staged W<- and K~).
 enum : int { kModeOut = 0, kModeOperator = 1 };
+template <int MODE>
+constexpr int kCompute = MODE == kModeOut ? kComputeWaves : 2 * kComputeWaves;
+template <int MODE>
+constexpr int kThreads = 64 * (kCompute<MODE> + kLoaderWaves);
 
 // s_waitcnt vmcnt(N), the other counters not waited for (gfx9 encoding: vmcnt in bits 3:0
 // and 15:14, expcnt 6:4, lgkmcnt 11:8).
@@ -63,6 +74,17 @@ template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Calls f(std::integral_constant<int, i>) for i = 0 .. N-1: every index is a compile-time
+// constant, so register arrays indexed by it stay in registers.
+template <class F, int... Is>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, Is...>) {
+  (f(std::integral_constant<int, Is>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
 // One ring slot: every operand of one chunk, each fragment 1 KiB (lane l's 16 bytes at
@@ -105,9 +127,8 @@ struct ChainArgs {
   int B, H, HV, DV;
   int lseg;       // chunks per segment
   int segmented;  // requests may be cut (at most 64 requests)
-  int nb;         // workgroups per (segment, value head)
-  int nb_r;       // of which (operator pass) hold columns of R
-  int64_t units;  // segments x value heads covered by the grid
+  int nb;         // workgroups per (segment, value head): 128-column blocks
+  int64_t groups; // (segment, q/k head) groups covered by the grid
 };
 
 // Segment sg of the call -> its request b, its index j in the request and the request's
@@ -148,22 +169,26 @@ __device__ __forceinline__ bool find_segment(const ChainArgs& a, int64_t sg, int
 }
 
 template <int DK, int MODE>
-__global__ __launch_bounds__(kChainThreads, 1) void chain_kernel(ChainArgs a) {
+__global__ __launch_bounds__(kThreads<MODE>, 1) void chain_kernel(ChainArgs a) {
   constexpr int NKS = DK / 32;  // 32-wide dk steps
   constexpr int NDT = DK / 16;  // 16-row dk tiles
   using Sl = Slot<DK, MODE>;
   __shared__ ChainSmem<DK, MODE> sm;
 
   const int tid = threadIdx.x, wv = tid >> 6, l = tid & 63, m = l & 15, g = l >> 4;
-  // The nb workgroups of one (segment, value head) share blockIdx.x mod 8, so they run on
-  // one XCD and read the chunk blocks once from its L2.
+  // The workgroups of one (segment, q/k head) group -- its HV/H value heads times the nb
+  // column blocks -- share blockIdx.x mod 8, so they run on one XCD and read the group's
+  // normalised q blocks once from its L2.
+  const int rv = a.HV / a.H;
+  const int members = rv * a.nb;
   const int64_t x = blockIdx.x;
   const int64_t rest = x >> 3;
-  const int blk = (int)(rest % a.nb);
-  const int64_t unit = (rest / a.nb) * 8 + (x & 7);
-  if (unit >= a.units) return;
-  const int64_t sg = unit / a.HV;
-  const int hv = (int)(unit % a.HV);
+  const int member = (int)(rest % members);
+  const int64_t grp = (rest / members) * 8 + (x & 7);
+  if (grp >= a.groups) return;
+  const int64_t sg = grp / a.H;
+  const int hv = (int)(grp % a.H) * rv + member / a.nb;
+  const int blk = member % a.nb;
   int b, j, nseg, seg0;
   if (!find_segment(a, sg, l, b, j, nseg, seg0)) return;
   const int64_t L = a.cu[b + 1] - a.cu[b];
@@ -171,74 +196,59 @@ __global__ __launch_bounds__(kChainThreads, 1) void chain_kernel(ChainArgs a) {
   const int nch = (int)((L + C - 1) / C);
   const int c_lo = j * a.lseg;
   const int n = min(c_lo + a.lseg, nch) - c_lo;  // chunks of this segment (>= 1)
-
-  int role, colbase, ncols;
-  if constexpr (MODE == kModeOut) {
-    role = kRoleOut;
-    colbase = blk * kColsPerBlock;
-    ncols = min(kColsPerBlock, a.DV - colbase);
-  } else {
+  if constexpr (MODE == kModeOperator)
     if (nseg < 2 || j == nseg - 1) return;  // the last segment's operator is never used
-    if (blk < a.nb_r) {
-      role = kRoleR;
-      colbase = blk * kColsPerBlock;
-      ncols = min(kColsPerBlock, a.DV - colbase);
-    } else {
-      role = kRoleP;
-      colbase = (blk - a.nb_r) * kColsPerBlock;
-      ncols = min(kColsPerBlock, DK - colbase);
-    }
-  }
+  const int colbase = blk * kColsPerBlock;
+  const int ncols_u = max(0, min(kColsPerBlock, a.DV - colbase));  // staged U~ columns
   const int h = hv / (a.HV / a.H);
   const int64_t slot = a.cache_indices[b];
   const int64_t cbase = (int64_t)a.chunk_off[b] + c_lo;  // global index of chunk 0
   const int64_t tseq = a.cu[b] + (int64_t)c_lo * C;      // first token of chunk 0
   const int64_t tend = a.cu[b + 1];
-  const bool use_u = role != kRoleP;
 
-  if (wv == kComputeWaves) {
-    // ======================= loader wave =======================
+  if (wv >= kCompute<MODE>) {
+    // ======================= loader waves =======================
+    // The chunk's fragments are numbered W<-, K~, (Qh, A_qk), (U~), e^G; loader wave lw
+    // copies those with number = lw mod kLoaderWaves.
+    const int lw = wv - kCompute<MODE>;
+    auto copy = [&](int idx, const char* src, void* dst) {
+      if (idx % kLoaderWaves == lw)
+        __builtin_amdgcn_global_load_lds((const void*)src, (lds_ptr)dst, 16, 0, 0);
+    };
     auto issue = [&](int cl) {
       Sl& s = sm.s[cl & 1];
       const int64_t pair = (cbase + cl) * a.HV + hv;
       const char* wsrc = reinterpret_cast<const char*>(a.W + pair * C * DK) + 16 * l;
       const char* ksrc = reinterpret_cast<const char*>(a.Kf + pair * C * DK) + 16 * l;
+      int idx = 0;
 #pragma unroll
-      for (int f = 0; f < Sl::FW; ++f)
-        __builtin_amdgcn_global_load_lds((const void*)(wsrc + 1024 * f), (lds_ptr)&s.w[f][0], 16,
-                                         0, 0);
+      for (int f = 0; f < Sl::FW; ++f) copy(idx++, wsrc + 1024 * f, &s.w[f][0]);
 #pragma unroll
-      for (int f = 0; f < Sl::FK; ++f)
-        __builtin_amdgcn_global_load_lds((const void*)(ksrc + 1024 * f), (lds_ptr)&s.k[f][0], 16,
-                                         0, 0);
+      for (int f = 0; f < Sl::FK; ++f) copy(idx++, ksrc + 1024 * f, &s.k[f][0]);
       if constexpr (MODE == kModeOut) {
         const char* qsrc =
             reinterpret_cast<const char*>(a.Qf + ((cbase + cl) * a.H + h) * (int64_t)(C * DK)) +
             16 * l;
         const char* asrc = reinterpret_cast<const char*>(a.Aqk + pair * C * C) + 16 * l;
 #pragma unroll
-        for (int f = 0; f < Sl::FQ; ++f)
-          __builtin_amdgcn_global_load_lds((const void*)(qsrc + 1024 * f), (lds_ptr)&s.q[f][0],
-                                           16, 0, 0);
+        for (int f = 0; f < Sl::FQ; ++f) copy(idx++, qsrc + 1024 * f, &s.q[f][0]);
         // A_qk fragments (token tile I, token step st) = 2 I + st; the two above the
         // diagonal (I < 2, st = 1) are zero and were never written
 #pragma unroll
         for (int f = 0; f < 8; ++f)
-          if (f != 1 && f != 3)
-            __builtin_amdgcn_global_load_lds((const void*)(asrc + 1024 * f), (lds_ptr)&s.a[f][0],
-                                             16, 0, 0);
+          if (f != 1 && f != 3) copy(idx++, asrc + 1024 * f, &s.a[f][0]);
       }
-      if (use_u) {
-        // the workgroup's 8 column tiles of U~: 16 contiguous KiB
+      if (ncols_u > 0) {
+        // the workgroup's column tiles of U~: ncols_u / 8 contiguous KiB
         const char* usrc =
             reinterpret_cast<const char*>(a.U + pair * C * a.DV + (int64_t)colbase * C) + 16 * l;
-        const int nu = ncols / 8;  // KiB pieces of this block's columns
-        for (int f = 0; f < nu; ++f)
-          __builtin_amdgcn_global_load_lds((const void*)(usrc + 1024 * f), (lds_ptr)&s.u[f][0],
-                                           16, 0, 0);
+        const int nu = ncols_u / 8;
+        for (int f = 0; f < nu; ++f) copy(idx + f, usrc + 1024 * f, &s.u[f][0]);
+        idx += nu;
       }
-      __builtin_amdgcn_global_load_lds((const void*)(a.eg + pair * C + l), (lds_ptr)&s.eg[0], 4,
-                                       0, 0);
+      if (idx % kLoaderWaves == lw)
+        __builtin_amdgcn_global_load_lds((const void*)(a.eg + pair * C + l), (lds_ptr)&s.eg[0], 4,
+                                         0, 0);
     };
     issue(0);
     for (int cl = 0; cl < n; ++cl) {
@@ -250,8 +260,11 @@ __global__ __launch_bounds__(kChainThreads, 1) void chain_kernel(ChainArgs a) {
   }
 
   // ======================= compute waves =======================
-  const bool active = kColsPerWave * wv < ncols;
-  const int col0 = colbase + kColsPerWave * wv;  // first state column of this wave
+  const int role = MODE == kModeOut ? kRoleOut : (wv < kComputeWaves ? kRoleR : kRoleP);
+  const int wq = wv % kComputeWaves;                // position inside the 128-column block
+  const int col0 = colbase + kColsPerWave * wq;     // first state (or P) column of this wave
+  const bool active = col0 < (role == kRoleP ? DK : a.DV);
+  const bool use_u = role != kRoleP;
   // S^T tiles: dk rows 16 dt + 4 g + i, column col0 + 16 ct + m (fp32)
   f32x4 S[NDT][2];
   float* Sinit = nullptr;
@@ -273,12 +286,45 @@ __global__ __launch_bounds__(kChainThreads, 1) void chain_kernel(ChainArgs a) {
         S[dt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
     }
-  const int wct = 2 * wv;  // this wave's first column tile inside the block
+  const int wct = 2 * wq;  // this wave's first column tile inside the block
+
+  // One chunk is a fixed sequence of NF fragment steps; each step reads one operand
+  // fragment from the slot and issues the two MFMAs (one per column tile) that use it:
+  //   W<- S^T     P  = 4 NKS steps (ks-major: consecutive steps feed different tokens)
+  //   Qh S^T      O1 = 4 NKS steps (output pass)
+  //   A_qk U      O2 = 6 steps     (output pass; the two tiles above the diagonal skipped)
+  //   K~^T U      UP = 2 NDT steps (token-step-major)
+  // Fragments are read RING steps ahead into a register ring, and a scheduling barrier
+  // after each step keeps that distance, so an LDS read has RING - 1 steps of matrix work
+  // to land.
+  constexpr int RING = MODE == kModeOut ? 8 : 6;
+  constexpr int P = 4 * NKS;
+  constexpr int O1 = MODE == kModeOut ? 4 * NKS : 0;
+  constexpr int O2 = MODE == kModeOut ? 6 : 0;
+  constexpr int UP = 2 * NDT;
+  constexpr int NF = P + O1 + O2 + UP;
+  // A_qk fragment 2 tt + st of the O2 steps: (tt, st) = (0,0) (1,0) (2,0) (2,1) (3,0) (3,1)
+  auto frag = [&](const Sl& s, auto I) -> const half8* {
+    constexpr int i = decltype(I)::value;
+    if constexpr (i < P) {
+      return &s.w[(i % 4) * NKS + i / 4][l];
+    } else if constexpr (i < P + O1) {
+      return &s.q[((i - P) % 4) * NKS + (i - P) / 4][l];
+    } else if constexpr (i < P + O1 + O2) {
+      constexpr int j2 = i - P - O1;
+      return &s.a[j2 < 2 ? 2 * j2 : j2 + 2][l];
+    } else {
+      constexpr int j2 = i - P - O1 - O2;
+      return &s.k[(j2 % NDT) * 2 + j2 / NDT][l];
+    }
+  };
 
   for (int cl = 0; cl < n; ++cl) {
     lds_barrier();  // chunk cl's operands are in slot cl & 1
     if (!active) continue;
     const Sl& s = sm.s[cl & 1];
+    half8 ring[RING];
+    static_for<RING>([&](auto I) { ring[decltype(I)::value] = *frag(s, I); });
     // ---- fp16 copy of S^T: B operand (k = dk) of W<- S^T and A operand of S Qh^T
     half8 s16[NKS][2];
 #pragma unroll
@@ -286,7 +332,7 @@ __global__ __launch_bounds__(kChainThreads, 1) void chain_kernel(ChainArgs a) {
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct)
         s16[ks][ct] = cat(to_half4(S[2 * ks][ct]), to_half4(S[2 * ks + 1][ct]));
-    // ---- -U = W<- S^T - U~ (token tile tt, column tile ct)
+    // ---- -U = W<- S^T - U~, accumulated from -U~ (token tile tt, column tile ct)
     f32x4 nu[4][2];
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt)
@@ -301,75 +347,81 @@ __global__ __launch_bounds__(kChainThreads, 1) void chain_kernel(ChainArgs a) {
           nu[tt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
       }
+    half8 u16[2][2];          // U in fp16, tokens 32 ts + kperm (B of the update, A of O2)
+    f32x4 o[4][2];            // O^T tiles (column tile ct, token tile tt)
+    const int64_t t0 = tseq + (int64_t)cl * C;
+    const int nrow = (int)min((int64_t)C, tend - t0);
+    static_for<NF>([&](auto I) {
+      constexpr int i = decltype(I)::value;
+      // phase boundaries
+      if constexpr (i == P + O1) {
+        // U in fp16 (P's products finished during the O1 steps)
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks)
+        for (int ts = 0; ts < 2; ++ts)
 #pragma unroll
-      for (int tt = 0; tt < 4; ++tt) {
-        const half8 wf = s.w[tt * NKS + ks][l];
+          for (int ct = 0; ct < 2; ++ct)
+            u16[ts][ct] = cat(to_half4(-nu[2 * ts][ct]), to_half4(-nu[2 * ts + 1][ct]));
+        if constexpr (MODE == kModeOut) {
+          // O1 rows scaled by e^G before A_qk U is added
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct) nu[tt][ct] = mma_f16(wf, s16[ks][ct], nu[tt][ct]);
-      }
-    // ---- U in fp16, tokens 32 ts + kperm: B operand of the update, A operand of U^T A_qk^T
-    half8 u16[2][2];
+          for (int tt = 0; tt < 4; ++tt) {
+            const float er = s.eg[16 * tt + m];
 #pragma unroll
-    for (int ts = 0; ts < 2; ++ts)
-#pragma unroll
-      for (int ct = 0; ct < 2; ++ct)
-        u16[ts][ct] = cat(to_half4(-nu[2 * ts][ct]), to_half4(-nu[2 * ts + 1][ct]));
-
-    if constexpr (MODE == kModeOut) {
-      // ---- O^T = diag(e^G)-scaled S Qh^T + U^T A_qk^T: lane (m, g) of tile (ct, tt) holds
-      // columns 16 ct + 4 g .. + 3 of token 16 tt + m
-      const int64_t t0 = tseq + (int64_t)cl * C;
-      const int nrow = (int)min((int64_t)C, tend - t0);
-#pragma unroll
-      for (int tt = 0; tt < 4; ++tt) {
-        f32x4 o[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-          const half8 qf = s.q[tt * NKS + ks][l];
-#pragma unroll
-          for (int ct = 0; ct < 2; ++ct) o[ct] = mma_f16(s16[ks][ct], qf, o[ct]);
-        }
-        const float er = s.eg[16 * tt + m];
-#pragma unroll
-        for (int ct = 0; ct < 2; ++ct) o[ct] *= er;
-#pragma unroll
-        for (int st = 0; st < 2; ++st) {
-          if (st == 1 && tt < 2) continue;  // causal: A_qk is zero above the diagonal
-          const half8 af = s.a[2 * tt + st][l];
-#pragma unroll
-          for (int ct = 0; ct < 2; ++ct) o[ct] = mma_f16(u16[st][ct], af, o[ct]);
-        }
-        const int r = 16 * tt + m;
-        if (r < nrow) {
-          __bf16* orow = reinterpret_cast<__bf16*>(a.out) + ((t0 + r) * a.HV + hv) * (int64_t)a.DV +
-                         col0 + 4 * g;
-#pragma unroll
-          for (int ct = 0; ct < 2; ++ct) {
-            bf16x4 ov;
-            ov[0] = (__bf16)o[ct][0];
-            ov[1] = (__bf16)o[ct][1];
-            ov[2] = (__bf16)o[ct][2];
-            ov[3] = (__bf16)o[ct][3];
-            *reinterpret_cast<bf16x4*>(orow + 16 * ct) = ov;
+            for (int ct = 0; ct < 2; ++ct) o[tt][ct] *= er;
           }
         }
       }
-    }
-
-    // ---- S^T <- e^{G_n} S^T + K~^T U (e^{G_n}: e^G of the chunk's last row; padding rows
-    // do not decay)
-    const float egn = s.eg[C - 1];
+      if constexpr (i == P + O1 + O2) {
+        if constexpr (MODE == kModeOut) {
+          // O^T lane (m, g) of tile (ct, tt): columns 16 ct + 4 g .. + 3 of token 16 tt + m
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
+          for (int tt = 0; tt < 4; ++tt) {
+            const int r = 16 * tt + m;
+            if (r < nrow) {
+              __bf16* orow = reinterpret_cast<__bf16*>(a.out) +
+                             ((t0 + r) * a.HV + hv) * (int64_t)a.DV + col0 + 4 * g;
 #pragma unroll
-      for (int ct = 0; ct < 2; ++ct) {
-        f32x4 acc = S[dt][ct] * egn;
+              for (int ct = 0; ct < 2; ++ct) {
+                bf16x4 ov;
+                ov[0] = (__bf16)o[tt][ct][0];
+                ov[1] = (__bf16)o[tt][ct][1];
+                ov[2] = (__bf16)o[tt][ct][2];
+                ov[3] = (__bf16)o[tt][ct][3];
+                *reinterpret_cast<bf16x4*>(orow + 16 * ct) = ov;
+              }
+            }
+          }
+        }
+        // S^T <- e^{G_n} S^T (+ K~^T U in the UP steps); e^{G_n} is e^G of the chunk's
+        // last row (padding rows do not decay)
+        const float egn = s.eg[C - 1];
 #pragma unroll
-        for (int ts = 0; ts < 2; ++ts) acc = mma_f16(s.k[dt * 2 + ts][l], u16[ts][ct], acc);
-        S[dt][ct] = acc;
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+          for (int ct = 0; ct < 2; ++ct) S[dt][ct] *= egn;
       }
+      const half8 f = ring[i % RING];
+      if constexpr (i + RING < NF) ring[i % RING] = *frag(s, std::integral_constant<int, i + RING>{});
+      if constexpr (i < P) {
+        constexpr int ks = i / 4, tt = i % 4;
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) nu[tt][ct] = mma_f16(f, s16[ks][ct], nu[tt][ct]);
+      } else if constexpr (i < P + O1) {
+        constexpr int j2 = i - P, ks = j2 / 4, tt = j2 % 4;
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct)
+          o[tt][ct] = mma_f16(s16[ks][ct], f, (ks == 0) ? f32x4{0.f, 0.f, 0.f, 0.f} : o[tt][ct]);
+      } else if constexpr (i < P + O1 + O2) {
+        constexpr int j2 = i - P - O1, fa = j2 < 2 ? 2 * j2 : j2 + 2, tt = fa / 2, st = fa % 2;
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) o[tt][ct] = mma_f16(u16[st][ct], f, o[tt][ct]);
+      } else {
+        constexpr int j2 = i - P - O1 - O2, ts = j2 / NDT, dt = j2 % NDT;
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) S[dt][ct] = mma_f16(f, u16[ts][ct], S[dt][ct]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    });
   }
 
   if (!active) return;
@@ -390,18 +442,23 @@ __global__ __launch_bounds__(kChainThreads, 1) void chain_kernel(ChainArgs a) {
 }
 
 // Combine: for every cut request and value head, in segment order from the slot's state,
-// S_{g+1} = S_g P_g + R_g (fp32), each S_g stored as the start state of segment g. One
-// workgroup per (request, value head, 16 state rows); thread (row i, column group cg)
-// forms DK / 16 consecutive columns of row i. P_g is staged in LDS per step.
+// S_{g+1} = S_g P_g + R_g, each S_g stored as the start state of segment g. One workgroup
+// per (request, value head, 16 state rows), four waves; the products run on fp32 matrix
+// cores (v_mfma_f32_16x16x4f32, full fp32 products and sums). Wave w forms column tiles
+// 2 w and 2 w + 1 of the 16 rows; every wave holds the rows of S_g as A fragments (lane
+// (r, g) of k step ks: S_g[r][4 ks + g]) and takes P_g's B fragments (lane (m, g): P_g[4 ks
+// + g][16 ct + m]) straight from memory, loading the next segment's while it uses the
+// current ones. The new rows go through LDS from the accumulator layout to the A layout.
+constexpr int kCombineRows = 16;
 template <int DK>
 __global__ __launch_bounds__(256) void combine_kernel(ChainArgs a) {
-  constexpr int CPT = DK / 16;  // columns per thread
-  __shared__ float Ps[DK][DK];
-  __shared__ float Ss[16][DK];
-  const int tid = threadIdx.x, l = tid & 63;
-  const int rb = a.DV / 16;
+  constexpr int NKS = DK / 4;         // fp32 k steps
+  constexpr int NCT = DK / 16 / 4;    // column tiles per wave (2 at dk = 128, 1 at 64)
+  __shared__ float Ss[kCombineRows][DK + 4];
+  const int tid = threadIdx.x, wv = tid >> 6, l = tid & 63, m = l & 15, g = l >> 4;
+  const int rb = a.DV / kCombineRows;
   const int64_t x = blockIdx.x;
-  const int r0 = (int)(x % rb) * 16;
+  const int r0 = (int)(x % rb) * kCombineRows;
   const int64_t p = x / rb;
   const int b = (int)(p / a.HV), hv = (int)(p % a.HV);
   if (b >= a.B) return;
@@ -422,32 +479,44 @@ __global__ __launch_bounds__(256) void combine_kernel(ChainArgs a) {
   const int seg0 = __shfl(incl, b, 64) - nseg;
   if (nseg < 2) return;
   const int64_t slot = a.cache_indices[b];
-  const int i = tid >> 4, cg = tid & 15;
+  auto opbase = [&](int jj) { return ((seg0 + jj) * (int64_t)a.HV + hv) * (int64_t)(a.DV + DK); };
+  float pf[NCT][NKS];  // B fragments of this step's P
+  auto load_p = [&](int jj) {
+    const float* P = a.rp + (opbase(jj) + a.DV) * DK;
+#pragma unroll
+    for (int c = 0; c < NCT; ++c)
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) pf[c][ks] = P[(4 * ks + g) * DK + 16 * (NCT * wv + c) + m];
+  };
   const float* S0 = a.state_pool + ((slot * a.HV + hv) * (int64_t)a.DV + r0) * DK;
-  for (int e = tid; e < 16 * DK; e += 256) Ss[e / DK][e % DK] = S0[e];
+  for (int e = tid; e < kCombineRows * DK; e += 256) Ss[e / DK][e % DK] = S0[e];
+  load_p(0);
   __syncthreads();
   for (int jj = 0;; ++jj) {
-    const int64_t sgj = seg0 + jj;
-    float* St = a.sstart + ((sgj * a.HV + hv) * (int64_t)a.DV + r0) * DK;
-    for (int e = tid; e < 16 * DK; e += 256) St[e] = Ss[e / DK][e % DK];
+    float* St = a.sstart + (((seg0 + jj) * (int64_t)a.HV + hv) * a.DV + r0) * DK;
+    for (int e = tid; e < kCombineRows * DK; e += 256) St[e] = Ss[e / DK][e % DK];
     if (jj == nseg - 1) break;
-    const int64_t base = (sgj * a.HV + hv) * (int64_t)(a.DV + DK);
-    const float* R = a.rp + (base + r0) * DK;
-    const float* P = a.rp + (base + a.DV) * DK;
-    for (int e = tid * 4; e < DK * DK; e += 256 * 4)
-      *reinterpret_cast<f32x4*>(&Ps[e / DK][e % DK]) = *reinterpret_cast<const f32x4*>(P + e);
-    float acc[CPT];
+    float sa[NKS];  // A fragments: S_g[m][4 ks + g]
 #pragma unroll
-    for (int c = 0; c < CPT; ++c) acc[c] = R[i * DK + cg * CPT + c];
-    __syncthreads();
-    for (int jd = 0; jd < DK; ++jd) {
-      const float sv = Ss[i][jd];
+    for (int ks = 0; ks < NKS; ++ks) sa[ks] = Ss[m][4 * ks + g];
+    const float* R = a.rp + (opbase(jj) + r0) * DK;
+    f32x4 acc[NCT];
 #pragma unroll
-      for (int c = 0; c < CPT; ++c) acc[c] = fmaf(sv, Ps[jd][cg * CPT + c], acc[c]);
+    for (int c = 0; c < NCT; ++c) {
+      const int col = 16 * (NCT * wv + c) + m;
+      acc[c] = f32x4{R[(4 * g) * DK + col], R[(4 * g + 1) * DK + col], R[(4 * g + 2) * DK + col],
+                     R[(4 * g + 3) * DK + col]};
     }
-    __syncthreads();  // every thread has read Ss and Ps
 #pragma unroll
-    for (int c = 0; c < CPT; ++c) Ss[i][cg * CPT + c] = acc[c];
+    for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+      for (int c = 0; c < NCT; ++c) acc[c] = mma_f32(sa[ks], pf[c][ks], acc[c]);
+    if (jj + 2 < nseg) load_p(jj + 1);  // the last segment has no operator
+    __syncthreads();  // every wave has read S_g from LDS
+#pragma unroll
+    for (int c = 0; c < NCT; ++c)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) Ss[4 * g + i][16 * (NCT * wv + c) + m] = acc[c][i];
     __syncthreads();
   }
 }
@@ -456,24 +525,22 @@ __global__ __launch_bounds__(256) void combine_kernel(ChainArgs a) {
 
 ChainPlan chain_plan(const Shape& s) {
   ChainPlan p;
-  p.use = s.bf16 && s.dk <= 128 && s.C == C;
+  // The column-slice state kernel gives each (request, value head) dv / 32 workgroups of
+  // 32 state rows; where those alone fill the device it serves the call. Otherwise
+  // requests are cut into segments whose whole-block workgroups fill it.
+  const int64_t slices = s.B * s.HV * (s.dv / 32);
+  p.use = s.bf16 && s.dk <= 128 && s.C == C && s.B <= kMaxSelfPlanRequests && slices < 256;
   if (!p.use) return p;
   p.nb = (s.dv + kColsPerBlock - 1) / kColsPerBlock;
-  p.nb_r = p.nb;
-  p.nb_op = p.nb + (s.dk + kColsPerBlock - 1) / kColsPerBlock;
+  p.nb_op = std::max(p.nb, (s.dk + kColsPerBlock - 1) / kColsPerBlock);
   const int64_t mc = s.N / s.C + s.B;  // upper bound on the call's chunks
-  p.segmented = s.B <= kMaxSelfPlanRequests;
-  if (p.segmented) {
-    // segments of about the length that gives every compute unit one output workgroup
-    const int64_t target = 256;
-    int64_t lseg = (mc * s.HV * p.nb + target - 1) / target;
-    lseg = std::max<int64_t>(lseg, 16);
-    p.lseg = (int)std::min<int64_t>(lseg, 1 << 30);
-    p.max_segs = mc / p.lseg + s.B;
-  } else {
-    p.lseg = 1 << 30;
-    p.max_segs = s.B;
-  }
+  p.segmented = true;
+  // segments of about the length that gives every compute unit one output workgroup
+  const int64_t target = 256;
+  int64_t lseg = (mc * s.HV * p.nb + target - 1) / target;
+  lseg = std::max<int64_t>(lseg, 16);
+  p.lseg = (int)std::min<int64_t>(lseg, 1 << 30);
+  p.max_segs = mc / p.lseg + s.B;
   return p;
 }
 
@@ -487,10 +554,14 @@ size_t chain_sstart_bytes(const Shape& s, const ChainPlan& p) {
 }
 
 int64_t chain_grid(const Shape& s, const ChainPlan& p, int stage) {
-  const int64_t units = p.max_segs * s.HV;
-  const int nb = stage == 0 ? p.nb_op : p.nb;
-  if (stage == 1) return (int64_t)s.B * s.HV * (s.dv / 16);
-  return (units + 7) / 8 * 8 * nb;
+  if (stage == 1) return (int64_t)s.B * s.HV * (s.dv / kCombineRows);
+  const int64_t groups = p.max_segs * s.H;
+  const int members = (s.HV / s.H) * (stage == 0 ? p.nb_op : p.nb);
+  return (groups + 7) / 8 * 8 * members;
+}
+
+int chain_threads(int stage) {
+  return stage == 0 ? kThreads<kModeOperator> : stage == 1 ? 256 : kThreads<kModeOut>;
 }
 
 hipError_t launch_chain(const ChainPlan& p, const Shape& s, const void* qf, const void* kf,
@@ -518,32 +589,26 @@ hipError_t launch_chain(const ChainPlan& p, const Shape& s, const void* qf, cons
   a.DV = s.dv;
   a.lseg = p.lseg;
   a.segmented = p.segmented ? 1 : 0;
-  a.nb_r = p.nb_r;
-  a.units = p.max_segs * s.HV;
+  a.nb = stage == 0 ? p.nb_op : p.nb;
+  a.groups = p.max_segs * s.H;
   const int64_t grid = chain_grid(s, p, stage);
   if (grid <= 0) return hipSuccess;
+  const dim3 gd((unsigned)grid), bd((unsigned)chain_threads(stage));
   if (stage == 0) {  // operator pass
-    a.nb = p.nb_op;
     if (s.dk == 64)
-      hipLaunchKernelGGL((chain_kernel<64, kModeOperator>), dim3((unsigned)grid),
-                         dim3(kChainThreads), 0, st, a);
+      hipLaunchKernelGGL((chain_kernel<64, kModeOperator>), gd, bd, 0, st, a);
     else
-      hipLaunchKernelGGL((chain_kernel<128, kModeOperator>), dim3((unsigned)grid),
-                         dim3(kChainThreads), 0, st, a);
+      hipLaunchKernelGGL((chain_kernel<128, kModeOperator>), gd, bd, 0, st, a);
   } else if (stage == 1) {  // combine
-    a.nb = p.nb;
     if (s.dk == 64)
-      hipLaunchKernelGGL((combine_kernel<64>), dim3((unsigned)grid), dim3(256), 0, st, a);
+      hipLaunchKernelGGL((combine_kernel<64>), gd, bd, 0, st, a);
     else
-      hipLaunchKernelGGL((combine_kernel<128>), dim3((unsigned)grid), dim3(256), 0, st, a);
+      hipLaunchKernelGGL((combine_kernel<128>), gd, bd, 0, st, a);
   } else {  // output pass
-    a.nb = p.nb;
     if (s.dk == 64)
-      hipLaunchKernelGGL((chain_kernel<64, kModeOut>), dim3((unsigned)grid), dim3(kChainThreads),
-                         0, st, a);
+      hipLaunchKernelGGL((chain_kernel<64, kModeOut>), gd, bd, 0, st, a);
     else
-      hipLaunchKernelGGL((chain_kernel<128, kModeOut>), dim3((unsigned)grid),
-                         dim3(kChainThreads), 0, st, a);
+      hipLaunchKernelGGL((chain_kernel<128, kModeOut>), gd, bd, 0, st, a);
   }
   return hipGetLastError();
 }

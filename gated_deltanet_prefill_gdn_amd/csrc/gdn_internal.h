@@ -90,15 +90,16 @@ struct ChainPlan {
   bool segmented = false;  // requests may be cut into segments (at most 64 requests)
   int lseg = 1 << 30;      // chunks per segment
   int nb = 1;              // output-pass workgroups per (segment, value head)
-  int nb_r = 1;            // operator-pass workgroups per (segment, value head) holding R
-  int nb_op = 2;           // operator-pass workgroups per (segment, value head): R and P
+  int nb_op = 1;           // operator-pass workgroups per (segment, value head)
   int64_t max_segs = 0;    // upper bound on the call's segments
 };
 ChainPlan chain_plan(const Shape& s);
 size_t chain_rp_bytes(const Shape& s, const ChainPlan& p);
 size_t chain_sstart_bytes(const Shape& s, const ChainPlan& p);
-// Workgroups of a stage's launch: 0 operator pass, 1 combine, 2 output pass.
+// Workgroups and threads per workgroup of a stage's launch: 0 operator pass, 1 combine,
+// 2 output pass.
 int64_t chain_grid(const Shape& s, const ChainPlan& p, int stage);
+int chain_threads(int stage);
 hipError_t launch_chain(const ChainPlan& p, const Shape& s, const void* qf, const void* kf,
                         const int64_t* cu, const int64_t* cache_indices, const int32_t* chunk_off,
                         const void* w, const void* u, const void* aqk, const float* eg,

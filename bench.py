@@ -755,7 +755,11 @@ def measure_prefill(p, steps: int, warmup: int, cold_steps: int, copy_calibratio
     # launch durations: each event-timed stage less the overhead of an empty event pair
     launch = {n: (ms - pair_ms if ms > 2 * pair_ms else ms) for n, ms in stage_ms.items()}
     dom = max(launch, key=launch.get)
-    kernel_name = gdn.STAGE_KERNELS[dom] if p.dtype == "bf16" else dom
+    sched = gdn.gdn_prefill_state_schedule(gdn.make_problem(
+        p.N, p.B, p.H, p.HV, p.dk, p.dv, p.pool,
+        gdn.GDN_DTYPE_BF16 if p.dtype == "bf16" else gdn.GDN_DTYPE_F32))
+    kernels = gdn.STAGE_KERNELS[sched]
+    kernel_name = kernels[dom]
     pbytes = path_bytes(p, s_qkv)
     flops = algorithmic_flops_per_token_vhead(p.dk, p.dv, p.chunk_size) * p.N * p.HV
     src_hash = kernel_source_hash()
@@ -782,9 +786,9 @@ def measure_prefill(p, steps: int, warmup: int, cold_steps: int, copy_calibratio
                                                    "read_bytes", "write_bytes") if kk in ctr}
     stages = {}
     for n in launch:
-        kn = gdn.STAGE_KERNELS[n] if p.dtype == "bf16" else n
+        kn = kernels[n]
         c = stored_counters(kn, tag, src_hash)
-        ent = {"launch_ms": launch[n], "events_ms": stage_ms[n]}
+        ent = {"kernel": kn, "launch_ms": launch[n], "events_ms": stage_ms[n]}
         if n in io:
             ent["kernel_io_bytes"] = io[n]
             ent["kernel_io_gbs"] = io[n] / max(launch[n], 1e-9) / 1e-3 / 1e9
@@ -810,6 +814,7 @@ def measure_prefill(p, steps: int, warmup: int, cold_steps: int, copy_calibratio
                       "frac_hbm": pbytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
                       "algorithmic_flops": flops, "algorithmic_bytes": pbytes},
         "stages": stages,
+        "state_schedule": sched,
         "kernel_source_hash": src_hash,
     }
 

@@ -28,13 +28,24 @@ GDN_DTYPE_BF16 = 1
 
 GDN_NUM_STAGES = 5
 STAGE_NAMES = ("gate", "chunk_prep", "state_operator", "state_combine", "state")
-# The kernel each stage of a bf16 prefill launches (the profilers' names; dk = 256 runs the
-# column-slice mfma_state_kernel in the last stage instead).
-STAGE_KERNELS = {"gate": "plan_kernel", "chunk_prep": "mfma_prep_kernel",
-                 "state_operator": "chain_kernel<operator>", "state_combine": "combine_kernel",
-                 "state": "chain_kernel<out>"}
+# The kernel each stage of a bf16 prefill launches (the profilers' names), by the state
+# schedule gdn_prefill_state_schedule reports.
+STAGE_KERNELS = {
+    0: {"gate": "plan_kernel", "chunk_prep": "mfma_prep_kernel", "state_operator": "-",
+        "state_combine": "-", "state": "mfma_state_kernel"},
+    1: {"gate": "plan_kernel", "chunk_prep": "mfma_prep_kernel",
+        "state_operator": "chain_kernel<operator>", "state_combine": "combine_kernel",
+        "state": "chain_kernel<out>"},
+    2: {"gate": "gate_kernel", "chunk_prep": "ref_prep_kernel", "state_operator": "-",
+        "state_combine": "-", "state": "ref_state_kernel"},
+}
 
-EXPORTED = ("gdn_prefill_workspace_size", "gdn_prefill_fwd", "gdn_prefill_fwd_events",
+GDN_SCHEDULE_COLUMN_SLICES = 0
+GDN_SCHEDULE_SEGMENTS = 1
+GDN_SCHEDULE_FP32 = 2
+
+EXPORTED = ("gdn_prefill_workspace_size", "gdn_prefill_state_schedule", "gdn_prefill_fwd",
+            "gdn_prefill_fwd_events",
             "gdn_decode_fwd", "gdn_recurrent_fwd", "gdn_promote_scan", "gdn_validate_inputs",
             "gdn_status_str", "gdn_version")
 
@@ -88,6 +99,8 @@ def load_library(path: str = LIB_PATH):
     PP = ctypes.POINTER(GdnProblem)
     L.gdn_prefill_workspace_size.restype = ctypes.c_size_t
     L.gdn_prefill_workspace_size.argtypes = [PP, ctypes.c_int32]
+    L.gdn_prefill_state_schedule.restype = ctypes.c_int32
+    L.gdn_prefill_state_schedule.argtypes = [PP, ctypes.c_int32]
     L.gdn_prefill_fwd.restype = ctypes.c_int
     L.gdn_prefill_fwd.argtypes = [P, P, P, P, P, P, P, P, P, P, ctypes.c_int32, P, PP, P,
                                   ctypes.c_size_t, P]
@@ -125,6 +138,11 @@ def make_problem(N: int, B: int, H: int, HV: int, dk: int, dv: int, pool: int,
 
 def gdn_prefill_workspace_size(prob: GdnProblem, chunk_size: int = 64) -> int:
     return int(load_library().gdn_prefill_workspace_size(ctypes.byref(prob), int(chunk_size)))
+
+
+def gdn_prefill_state_schedule(prob: GdnProblem, chunk_size: int = 64) -> int:
+    """GDN_SCHEDULE_* of the kernels that run a call's state pass (-1 if invalid)."""
+    return int(load_library().gdn_prefill_state_schedule(ctypes.byref(prob), int(chunk_size)))
 
 
 def _dtype_code(t) -> int:

@@ -3,6 +3,8 @@
 // the prefill, the chunk-free recurrent path, the decode step and the Promote update scan.
 #include <string.h>
 
+#include <algorithm>
+#include <new>
 #include <vector>
 
 #include "gdn.h"
@@ -49,6 +51,34 @@ WsLayout layout_for(const Shape& s, Path p) {
   off = align256(off + chain_sstart_bytes(s, cp));
   L.total = off;
   return L;
+}
+
+// Requests gdn_validate_inputs copies to the host at most (16 bytes each).
+constexpr int64_t kMaxValidateRequests = (int64_t)1 << 26;
+
+// A launch of `blocks` workgroups of `threads` work-items along x: the dispatch packet
+// holds the grid size in work-items as 32 bits.
+static bool grid_fits(int64_t blocks, int threads) {
+  return blocks >= 0 && blocks * (int64_t)threads <= (int64_t)0xFFFFFFFF;
+}
+
+// Every launch of a prefill call of shape s fits its grid limits.
+static bool prefill_grids_fit(const Shape& s, Path path, int64_t max_chunks) {
+  if (path == Path::kRef) {
+    // gate: 4 (chunk, value head) pairs per 256-thread workgroup; ref prep: (chunk, value
+    // head) grid; ref state: (request, value head, 16 state rows) grid
+    return grid_fits((max_chunks * s.HV + 3) / 4, 256) && grid_fits(max_chunks, 256) &&
+           grid_fits(s.B, 256) && s.HV <= 65535 && s.dv / 16 <= 65535;
+  }
+  const ChainPlan cp = chain_plan(s);
+  if (cp.use) {
+    for (int stage = 0; stage < 3; ++stage)
+      if (!grid_fits(chain_grid(s, cp, stage), chain_threads(stage))) return false;
+    return true;
+  }
+  // column-slice state kernel: (request, value head) pairs rounded up to 8, times dv / 32,
+  // workgroups of five waves (the prep kernel's grid is the device's resident capacity)
+  return grid_fits((s.B * s.HV + 7) / 8 * 8 * (s.dv / 32), 64 * 5);
 }
 
 // Descriptor checks shared by every entry point. Host only.
@@ -105,6 +135,13 @@ size_t gdn_prefill_workspace_size(const gdn_problem_t* prob, int32_t chunk_size)
   return layout_for(s, choose_path(s)).total;
 }
 
+int32_t gdn_prefill_state_schedule(const gdn_problem_t* prob, int32_t chunk_size) {
+  Shape s;
+  if (check_problem(prob, chunk_size, &s) != GDN_OK) return -1;
+  if (choose_path(s) == Path::kRef) return GDN_SCHEDULE_FP32;
+  return chain_plan(s).use ? GDN_SCHEDULE_SEGMENTS : GDN_SCHEDULE_COLUMN_SLICES;
+}
+
 }  // extern "C"
 
 namespace {
@@ -124,6 +161,7 @@ gdn_status_t run_prefill(const void* q, const void* k, const void* v, const floa
     return GDN_ERR_INVALID_ARG;
   const Path path = choose_path(s);
   const WsLayout L = layout_for(s, path);
+  if (!prefill_grids_fit(s, path, L.max_chunks)) return GDN_ERR_UNSUPPORTED;
   if (!workspace || workspace_bytes < L.total) return GDN_ERR_WORKSPACE;
   if (((uintptr_t)workspace & 255) != 0) return GDN_ERR_WORKSPACE;
   if (path == Path::kMfma) {  // 16-byte vector loads and stores
@@ -295,7 +333,16 @@ gdn_status_t gdn_validate_inputs(const int64_t* cu_seqlens, const int64_t* cache
   if (ps != GDN_OK && ps != GDN_ERR_UNSUPPORTED) return ps;
   if (s.B == 0) return GDN_OK;
   if (!cu_seqlens || !cache_indices) return GDN_ERR_INVALID_ARG;
-  std::vector<int64_t> cu((size_t)s.B + 1), idx((size_t)s.B);
+  if (s.B > kMaxValidateRequests) return GDN_ERR_UNSUPPORTED;
+  // host copies of both arrays (16 bytes per request); a descriptor whose arrays cannot be
+  // held on the host is refused rather than thrown through the C ABI
+  std::vector<int64_t> cu, idx;
+  try {
+    cu.resize((size_t)s.B + 1);
+    idx.resize((size_t)s.B);
+  } catch (...) {  // std::bad_alloc or std::length_error
+    return GDN_ERR_UNSUPPORTED;
+  }
   hipStream_t st = (hipStream_t)stream;
   if (hipMemcpyAsync(cu.data(), cu_seqlens, sizeof(int64_t) * cu.size(), hipMemcpyDeviceToHost,
                      st) != hipSuccess)
@@ -307,13 +354,11 @@ gdn_status_t gdn_validate_inputs(const int64_t* cu_seqlens, const int64_t* cache
   if (cu[0] != 0 || cu[(size_t)s.B] != s.N) return GDN_ERR_BAD_INPUT;
   for (int64_t i = 0; i < s.B; ++i)
     if (cu[(size_t)i + 1] < cu[(size_t)i]) return GDN_ERR_BAD_INPUT;
-  std::vector<char> seen((size_t)s.pool, 0);
-  for (int64_t i = 0; i < s.B; ++i) {
-    const int64_t x = idx[(size_t)i];
-    if (x < 0 || x >= s.pool) return GDN_ERR_BAD_INPUT;
-    if (seen[(size_t)x]) return GDN_ERR_BAD_INPUT;
-    seen[(size_t)x] = 1;
-  }
+  for (int64_t i = 0; i < s.B; ++i)
+    if (idx[(size_t)i] < 0 || idx[(size_t)i] >= s.pool) return GDN_ERR_BAD_INPUT;
+  // distinct slots: sort the host copy (O(B) memory, whatever the pool size)
+  std::sort(idx.begin(), idx.end());
+  if (std::adjacent_find(idx.begin(), idx.end()) != idx.end()) return GDN_ERR_BAD_INPUT;
   return GDN_OK;
 }
 

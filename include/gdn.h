@@ -105,6 +105,22 @@ gdn_status_t gdn_prefill_fwd(const void* q, const void* k, const void* v, const 
                             state); 4: state pass + outputs. Stages 2 and 3 launch nothing
                             when no request is cut. */
 
+/* Which kernels run the sequential state pass (stages 2-4 below) of a prefill call of this
+ * shape; a function of the descriptor only. Host only, no HIP calls. Returns -1 for an
+ * invalid or unsupported descriptor or chunk size. For profiling and tests.
+ *   GDN_SCHEDULE_COLUMN_SLICES  bf16 inputs: one workgroup per (request, value head, 32 state
+ *                               rows), each walking its request's chunks; used when those
+ *                               workgroups alone fill the device, when dk = 256 and above 64
+ *                               requests.
+ *   GDN_SCHEDULE_SEGMENTS       bf16 inputs: requests cut into segments of chunks (operator
+ *                               pass, combine, output pass) with one workgroup per
+ *                               (segment, value head, 128 state rows).
+ *   GDN_SCHEDULE_FP32           fp32 inputs: fp32 arithmetic throughout. */
+#define GDN_SCHEDULE_COLUMN_SLICES 0
+#define GDN_SCHEDULE_SEGMENTS 1
+#define GDN_SCHEDULE_FP32 2
+int32_t gdn_prefill_state_schedule(const gdn_problem_t* prob, int32_t chunk_size);
+
 /* gdn_prefill_fwd with timing marks: stage_events points to GDN_NUM_STAGES + 1
  * hipEvent_t handles created by the caller on the current device; event i is recorded
  * on `stream` just before stage i is launched, the last one after the last stage.
@@ -192,7 +208,9 @@ gdn_status_t gdn_promote_scan(const void* K, const void* V, const float* beta, c
 
 /* Debug check of the device-array preconditions: cu_seqlens[0] == 0, non-decreasing,
  * cu_seqlens[B] == N; cache_indices distinct and in [0, pool). Copies both arrays to
- * the host and synchronises `stream`. GDN_OK or GDN_ERR_BAD_INPUT. */
+ * the host (16 bytes per request; at most 2^26 requests, GDN_ERR_UNSUPPORTED above that or
+ * if the host copies cannot be allocated) and synchronises `stream`. GDN_OK or
+ * GDN_ERR_BAD_INPUT. */
 gdn_status_t gdn_validate_inputs(const int64_t* cu_seqlens, const int64_t* cache_indices,
                                  const gdn_problem_t* prob, void* stream);
 

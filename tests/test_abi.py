@@ -91,6 +91,44 @@ def test_error_paths_return_before_launch():
                                None, None, None, 0, None) == gdn.GDN_ERR_INVALID_ARG
 
 
+def test_state_schedule():
+    """The state-pass schedule is a function of the descriptor: column slices where those
+    fill the device (the dense batch), segments for few long requests (the long-decay
+    request), column slices at dk = 256 and above 64 requests, the fp32 kernels for fp32."""
+    S = gdn.gdn_prefill_state_schedule
+    assert S(prob()) == gdn.GDN_SCHEDULE_COLUMN_SLICES
+    assert S(prob(N=131072, B=1, HV=32, pool=1)) == gdn.GDN_SCHEDULE_SEGMENTS
+    assert S(prob(N=16384, B=1, H=8, HV=8, dk=256, dv=256, pool=1)) == \
+        gdn.GDN_SCHEDULE_COLUMN_SLICES
+    assert S(prob(N=8192, B=65, H=1, HV=1, pool=65)) == gdn.GDN_SCHEDULE_COLUMN_SLICES
+    assert S(prob(N=8192, B=63, H=1, HV=1, pool=63)) == gdn.GDN_SCHEDULE_SEGMENTS
+    assert S(prob(dtype=gdn.GDN_DTYPE_F32)) == gdn.GDN_SCHEDULE_FP32
+    assert S(prob(HV=24)) == -1
+    assert S(prob(), 128) == -1
+
+
+def test_grids_beyond_launch_limits_are_refused():
+    """Shapes whose kernel grids would exceed 2^32 work-items are refused on the host,
+    before the workspace is even looked at."""
+    huge = prob(N=1 << 30, B=1 << 24, H=1, HV=1024, dk=128, dv=256, pool=1 << 24)
+    assert call(huge, ws_bytes=0, ws_ptr=0) == gdn.GDN_ERR_UNSUPPORTED
+    huge32 = prob(N=(1 << 31) - (1 << 26), B=1, H=1, HV=65535, pool=1,
+                  dtype=gdn.GDN_DTYPE_F32)
+    assert call(huge32, ws_bytes=0, ws_ptr=0) == gdn.GDN_ERR_UNSUPPORTED
+
+
+def test_validate_inputs_refuses_what_it_cannot_copy():
+    """gdn_validate_inputs copies the arrays to the host: a descriptor with more requests
+    than it copies is refused with a status (no exception through the C ABI, no HIP call);
+    the pool size plays no part in its memory."""
+    lib = gdn.load_library()
+    P = ctypes.c_void_p
+    for B in (1 << 40, (1 << 26) + 1):
+        p = prob(N=0, B=B, pool=B)
+        assert lib.gdn_validate_inputs(P(4096), P(4096), ctypes.byref(p), P(0)) == \
+            gdn.GDN_ERR_UNSUPPORTED
+
+
 def test_empty_problem_is_a_no_op():
     # N == 0 or B == 0: nothing to read or write, so null pointers are fine
     assert call(prob(N=0, B=3), nonnull=False, ws_bytes=0, ws_ptr=0) == gdn.GDN_OK

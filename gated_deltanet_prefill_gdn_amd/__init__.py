@@ -45,7 +45,7 @@ GDN_SCHEDULE_SEGMENTS = 1
 GDN_SCHEDULE_FP32 = 2
 
 EXPORTED = ("gdn_prefill_workspace_size", "gdn_prefill_state_schedule", "gdn_prefill_fwd",
-            "gdn_prefill_fwd_events",
+            "gdn_prefill_fwd_events", "gdn_prefill_nonfinite",
             "gdn_decode_fwd", "gdn_recurrent_fwd", "gdn_promote_scan", "gdn_validate_inputs",
             "gdn_status_str", "gdn_version")
 
@@ -99,6 +99,8 @@ def load_library(path: str = LIB_PATH):
     PP = ctypes.POINTER(GdnProblem)
     L.gdn_prefill_workspace_size.restype = ctypes.c_size_t
     L.gdn_prefill_workspace_size.argtypes = [PP, ctypes.c_int32]
+    L.gdn_prefill_nonfinite.restype = ctypes.c_int
+    L.gdn_prefill_nonfinite.argtypes = [P, ctypes.c_size_t, ctypes.POINTER(ctypes.c_int32), P]
     L.gdn_prefill_state_schedule.restype = ctypes.c_int32
     L.gdn_prefill_state_schedule.argtypes = [PP, ctypes.c_int32]
     L.gdn_prefill_fwd.restype = ctypes.c_int
@@ -283,6 +285,20 @@ def _prefill(q, k, v, a, b, A_log, dt_bias, state_pool, cache_indices, cu_seqlen
     if rc != GDN_OK:
         raise GdnError(rc, "gdn_prefill_fwd")
     return out
+
+
+def gdn_prefill_nonfinite(workspace, stream=None) -> bool:
+    """Whether the last prefill call that ran with this workspace left a non-finite final
+    state (synchronises the stream)."""
+    import torch
+    _need(workspace, "workspace", dtype=torch.uint8, ndim=1)
+    st = (stream or torch.cuda.current_stream(workspace.device)).cuda_stream
+    flag = ctypes.c_int32(0)
+    rc = load_library().gdn_prefill_nonfinite(_ptr(workspace), workspace.numel(),
+                                              ctypes.byref(flag), ctypes.c_void_p(st))
+    if rc != GDN_OK:
+        raise GdnError(rc, "gdn_prefill_nonfinite")
+    return bool(flag.value)
 
 
 def gdn_decode_fwd(q, k, v, a, b, A_log, dt_bias, state_pool, cache_indices, out=None,

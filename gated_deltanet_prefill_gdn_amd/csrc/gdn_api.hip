@@ -24,6 +24,8 @@ WsLayout layout_for(const Shape& s, Path p) {
   const size_t mc = (size_t)L.max_chunks;
   const size_t el = (p == Path::kRef) ? 4 : 2;
   size_t off = 0;
+  L.flags = off;
+  off = align256(off + sizeof(int32_t));
   L.chunk_off = off;
   off = align256(off + sizeof(int32_t) * (size_t)(s.B + 1));
   L.chunk_seq = off;
@@ -181,6 +183,7 @@ gdn_status_t run_prefill(const void* q, const void* k, const void* v, const floa
   int32_t* chunk_seq = (int32_t*)(ws + L.chunk_seq);
   double* gcum = (double*)(ws + L.gcum);
   float* beta = (float*)(ws + L.beta);
+  int32_t* nonfinite = (int32_t*)(ws + L.flags);
 
   // Up to 64 requests the MFMA chunk prep forms the chunk table itself (one scan per
   // workgroup) and writes chunk_off for the state pass: one launch fewer.
@@ -191,7 +194,7 @@ gdn_status_t run_prefill(const void* q, const void* k, const void* v, const floa
     return GDN_ERR_HIP;
   if (path == Path::kRef &&
       launch_gate(a, b, A_log, dt_bias, cu_seqlens, chunk_off, chunk_seq, s, L.max_chunks, gcum,
-                  beta, st) != hipSuccess)
+                  beta, nonfinite, st) != hipSuccess)
     return GDN_ERR_HIP;
   if (!mark(1)) return GDN_ERR_HIP;
   void* w = ws + L.w;
@@ -202,7 +205,8 @@ gdn_status_t run_prefill(const void* q, const void* k, const void* v, const floa
     void* kf = ws + L.kf;
     void* qf = ws + L.qf;
     if (launch_mfma_prep(q, k, v, cu_seqlens, chunk_off, chunk_seq, self_plan, a, b, A_log,
-                         dt_bias, s, L.max_chunks, w, u, aqk, eg, kf, qf, st) != hipSuccess)
+                         dt_bias, s, L.max_chunks, w, u, aqk, eg, kf, qf, nonfinite,
+                         st) != hipSuccess)
       return GDN_ERR_HIP;
     const ChainPlan cp = chain_plan(s);
     if (cp.use) {
@@ -212,13 +216,13 @@ gdn_status_t run_prefill(const void* q, const void* k, const void* v, const floa
         if (!mark(2 + stage)) return GDN_ERR_HIP;
         if ((stage < 2 && !cp.segmented)) continue;  // nothing is cut: one pass
         if (launch_chain(cp, s, qf, kf, cu_seqlens, cache_indices, chunk_off, w, u, aqk, eg, rp,
-                         sstart, state_pool, out, stage, st) != hipSuccess)
+                         sstart, state_pool, out, nonfinite, stage, st) != hipSuccess)
           return GDN_ERR_HIP;
       }
     } else {
       if (!mark(2) || !mark(3) || !mark(4)) return GDN_ERR_HIP;
       if (launch_mfma_state(qf, kf, cu_seqlens, cache_indices, chunk_off, w, u, aqk, eg, s,
-                            state_pool, out, st) != hipSuccess)
+                            state_pool, out, nonfinite, st) != hipSuccess)
         return GDN_ERR_HIP;
     }
   } else {
@@ -227,7 +231,7 @@ gdn_status_t run_prefill(const void* q, const void* k, const void* v, const floa
       return GDN_ERR_HIP;
     if (!mark(2) || !mark(3) || !mark(4)) return GDN_ERR_HIP;
     if (launch_ref_state(q, k, cu_seqlens, cache_indices, chunk_off, gcum, (const float*)w,
-                         (const float*)u, s, state_pool, out, st) != hipSuccess)
+                         (const float*)u, s, state_pool, out, nonfinite, st) != hipSuccess)
       return GDN_ERR_HIP;
   }
   if (!mark(5)) return GDN_ERR_HIP;
@@ -323,6 +327,19 @@ gdn_status_t gdn_promote_scan(const void* K, const void* V, const float* beta, c
   PromoteShape s{prob->scans, prob->firings, prob->pairs, prob->head_k, prob->head_v};
   if (launch_promote(s, K, V, beta, w, gamma, M, states, (hipStream_t)stream) != hipSuccess)
     return GDN_ERR_HIP;
+  return GDN_OK;
+}
+
+gdn_status_t gdn_prefill_nonfinite(const void* workspace, size_t workspace_bytes,
+                                   int32_t* nonfinite, void* stream) {
+  if (!workspace || !nonfinite) return GDN_ERR_INVALID_ARG;
+  if (workspace_bytes < sizeof(int32_t)) return GDN_ERR_WORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  int32_t v = 0;
+  if (hipMemcpyAsync(&v, workspace, sizeof(v), hipMemcpyDeviceToHost, st) != hipSuccess)
+    return GDN_ERR_HIP;
+  if (hipStreamSynchronize(st) != hipSuccess) return GDN_ERR_HIP;
+  *nonfinite = v != 0;
   return GDN_OK;
 }
 

@@ -124,6 +124,7 @@ struct ChainArgs {
   uint16_t* out;
   float* rp;      // [segment][HV][dv + dk][dk]: R_g rows, then P_g rows
   float* sstart;  // [segment][HV][dv][dk]: start state of every segment of a cut request
+  int32_t* nonfinite;  // raised by the output pass if a final state is not finite
   int B, H, HV, DV;
   int lseg;       // chunks per segment
   int segmented;  // requests may be cut (at most 64 requests)
@@ -428,6 +429,14 @@ __global__ __launch_bounds__(kThreads<MODE>, 1) void chain_kernel(ChainArgs a) {
   // ---- the state at the end of the segment
   float* dst = nullptr;
   if (role == kRoleOut) {
+    bool finite = true;  // an fp16 intermediate out of range shows up here
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) finite = finite && __builtin_isfinite(S[dt][ct][i]);
+    if (__ballot(!finite) != 0 && l == 0) *a.nonfinite = 1;
     if (j != nseg - 1) return;  // a later segment carries the request on
     dst = a.state_pool + ((slot * a.HV + hv) * (int64_t)a.DV + col0) * DK;
   } else {
@@ -567,8 +576,8 @@ int chain_threads(int stage) {
 hipError_t launch_chain(const ChainPlan& p, const Shape& s, const void* qf, const void* kf,
                         const int64_t* cu, const int64_t* cache_indices, const int32_t* chunk_off,
                         const void* w, const void* u, const void* aqk, const float* eg,
-                        float* rp, float* sstart, float* state_pool, void* out, int stage,
-                        hipStream_t st) {
+                        float* rp, float* sstart, float* state_pool, void* out,
+                        int32_t* nonfinite, int stage, hipStream_t st) {
   ChainArgs a;
   a.W = (const _Float16*)w;
   a.U = (const _Float16*)u;
@@ -583,6 +592,7 @@ hipError_t launch_chain(const ChainPlan& p, const Shape& s, const void* qf, cons
   a.out = (uint16_t*)out;
   a.rp = rp;
   a.sstart = sstart;
+  a.nonfinite = nonfinite;
   a.B = (int)s.B;
   a.H = s.H;
   a.HV = s.HV;

@@ -20,6 +20,7 @@ enum class Path : int {
 // Byte offsets of each region inside the caller's workspace (all 256-byte aligned).
 struct WsLayout {
   int64_t max_chunks = 0;  // upper bound on sum_b ceil(L_b / C) = N / C + B
+  size_t flags = 0;        // int32 [1]: set when a call's final states are not all finite
   size_t chunk_off = 0;    // int32 [B + 1]: first global chunk of each request
   size_t chunk_seq = 0;    // int32 [max_chunks]: request of each global chunk, -1 if unused
   size_t gcum = 0;         // double [max_chunks][HV][C]: chunk-local inclusive sum of log(alpha)
@@ -57,7 +58,7 @@ hipError_t launch_plan(const int64_t* cu_seqlens, const Shape& s, int32_t* chunk
 hipError_t launch_gate(const float* a, const float* b, const float* A_log, const float* dt_bias,
                        const int64_t* cu_seqlens, const int32_t* chunk_off,
                        const int32_t* chunk_seq, const Shape& s, int64_t max_chunks,
-                       double* gcum, float* beta, hipStream_t st);
+                       double* gcum, float* beta, int32_t* nonfinite, hipStream_t st);
 hipError_t launch_ref_prep(const void* k, const void* v, const int64_t* cu_seqlens,
                            const int32_t* chunk_off, const int32_t* chunk_seq, const double* gcum,
                            const float* beta, const Shape& s, int64_t max_chunks, float* w,
@@ -65,7 +66,7 @@ hipError_t launch_ref_prep(const void* k, const void* v, const int64_t* cu_seqle
 hipError_t launch_ref_state(const void* q, const void* k, const int64_t* cu_seqlens,
                             const int64_t* cache_indices, const int32_t* chunk_off,
                             const double* gcum, const float* w, const float* u, const Shape& s,
-                            float* state_pool, void* out, hipStream_t st);
+                            float* state_pool, void* out, int32_t* nonfinite, hipStream_t st);
 
 // self_plan (at most kMaxSelfPlanRequests requests): the prep kernel forms the chunk table
 // itself and writes chunk_off (B + 1 entries) for the state pass; chunk_seq is then not
@@ -76,12 +77,12 @@ hipError_t launch_mfma_prep(const void* q, const void* k, const void* v,
                             const int32_t* chunk_seq, bool self_plan, const float* a,
                             const float* b, const float* A_log, const float* dt_bias,
                             const Shape& s, int64_t max_chunks, void* w, void* u, void* aqk,
-                            float* eg, void* kf, void* qf, hipStream_t st);
+                            float* eg, void* kf, void* qf, int32_t* nonfinite, hipStream_t st);
 hipError_t launch_mfma_state(const void* qf, const void* kf, const int64_t* cu_seqlens,
                              const int64_t* cache_indices, const int32_t* chunk_off,
                              const void* w, const void* u, const void* aqk,
                              const float* eg, const Shape& s, float* state_pool, void* out,
-                             hipStream_t st);
+                             int32_t* nonfinite, hipStream_t st);
 
 // The state pass with whole 128-column state blocks per workgroup and the segment scan of
 // long requests (bf16 inputs, dk <= 128).
@@ -103,8 +104,8 @@ int chain_threads(int stage);
 hipError_t launch_chain(const ChainPlan& p, const Shape& s, const void* qf, const void* kf,
                         const int64_t* cu, const int64_t* cache_indices, const int32_t* chunk_off,
                         const void* w, const void* u, const void* aqk, const float* eg,
-                        float* rp, float* sstart, float* state_pool, void* out, int stage,
-                        hipStream_t st);
+                        float* rp, float* sstart, float* state_pool, void* out,
+                        int32_t* nonfinite, int stage, hipStream_t st);
 
 // Decode step (one token per request): workgroups a launch needs, and the launcher.
 int64_t decode_blocks(const Shape& s);

@@ -92,9 +92,11 @@ __global__ __launch_bounds__(256) void gate_kernel(
     const float* __restrict__ a, const float* __restrict__ b, const float* __restrict__ A_log,
     const float* __restrict__ dt_bias, const int64_t* __restrict__ cu,
     const int32_t* __restrict__ chunk_off, const int32_t* __restrict__ chunk_seq, int HV,
-    int64_t max_chunks, double* __restrict__ gcum, float* __restrict__ beta) {
+    int64_t max_chunks, double* __restrict__ gcum, float* __restrict__ beta,
+    int32_t* __restrict__ nonfinite) {
   constexpr int C = 64;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  if (blockIdx.x == 0 && threadIdx.x == 0) *nonfinite = 0;  // the state pass raises it
   const int64_t pair = (int64_t)blockIdx.x * 4 + wave;
   if (pair >= max_chunks * HV) return;
   const int64_t c = pair / HV;
@@ -132,11 +134,11 @@ hipError_t launch_plan(const int64_t* cu_seqlens, const Shape& s, int32_t* chunk
 hipError_t launch_gate(const float* a, const float* b, const float* A_log, const float* dt_bias,
                        const int64_t* cu_seqlens, const int32_t* chunk_off,
                        const int32_t* chunk_seq, const Shape& s, int64_t max_chunks,
-                       double* gcum, float* beta, hipStream_t st) {
+                       double* gcum, float* beta, int32_t* nonfinite, hipStream_t st) {
   const int64_t pairs = max_chunks * s.HV;
   const int64_t blocks = (pairs + 3) / 4;
   hipLaunchKernelGGL(gate_kernel, dim3((unsigned)blocks), dim3(256), 0, st, a, b, A_log, dt_bias,
-                     cu_seqlens, chunk_off, chunk_seq, s.HV, max_chunks, gcum, beta);
+                     cu_seqlens, chunk_off, chunk_seq, s.HV, max_chunks, gcum, beta, nonfinite);
   return hipGetLastError();
 }
 

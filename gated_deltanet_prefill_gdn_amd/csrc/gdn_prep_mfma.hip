@@ -173,7 +173,7 @@ __global__ __launch_bounds__(256, (DK + DV <= 256) ? 3 : 1) void mfma_prep_kerne
     const float* __restrict__ gb, const float* __restrict__ A_log,
     const float* __restrict__ dt_bias, int B, int H, int HV, _Float16* __restrict__ Wout,
     _Float16* __restrict__ Uout, _Float16* __restrict__ Aout, float* __restrict__ eg_out,
-    _Float16* __restrict__ Kout, _Float16* __restrict__ Qout) {
+    _Float16* __restrict__ Kout, _Float16* __restrict__ Qout, int32_t* __restrict__ nonfinite) {
   constexpr int NKS = DK / 32;
   using Sm = PrepSmem<DK, DV>;
   constexpr int SK = Sm::SK, SQV = Sm::SQV;
@@ -272,6 +272,7 @@ __global__ __launch_bounds__(256, (DK + DV <= 256) ? 3 : 1) void mfma_prep_kerne
     __syncthreads();
     if (blockIdx.x == 0 && tid <= B) chunk_off[tid] = sm.coff[tid];
   }
+  if (blockIdx.x == 0 && tid == 0) *nonfinite = 0;  // the state pass raises it
   const int64_t n_items = (int64_t)(SELF_PLAN ? sm.coff[B] : chunk_off[B]) * HV;
   if ((int64_t)blockIdx.x >= n_items) return;
   Item cur;
@@ -554,7 +555,7 @@ hipError_t launch_prep_t(const void* q, const void* k, const void* v, const int6
                          const float* gb, const float* A_log, const float* dt_bias,
                          const Shape& s, int64_t max_chunks, _Float16* w,
                          _Float16* u, _Float16* aqk, float* eg, _Float16* kf, _Float16* qf,
-                         hipStream_t st) {
+                         int32_t* nonfinite, hipStream_t st) {
   // Persistent grid: as many workgroups as fit on the device at once.
   auto kern = self_plan ? mfma_prep_kernel<DK, DV, true> : mfma_prep_kernel<DK, DV, false>;
   int dev = 0, cus = 0, per_cu = 0;
@@ -566,7 +567,7 @@ hipError_t launch_prep_t(const void* q, const void* k, const void* v, const int6
   const int64_t grid = std::min<int64_t>(items, (int64_t)std::max(cus, 1) * std::max(per_cu, 1));
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), 0, st, (const uint16_t*)q,
                      (const uint16_t*)k, (const uint16_t*)v, cu, off, cseq, ga, gb, A_log,
-                     dt_bias, (int)s.B, s.H, s.HV, w, u, aqk, eg, kf, qf);
+                     dt_bias, (int)s.B, s.H, s.HV, w, u, aqk, eg, kf, qf, nonfinite);
   return hipGetLastError();
 }
 
@@ -577,7 +578,7 @@ hipError_t launch_mfma_prep(const void* q, const void* k, const void* v,
                             const int32_t* chunk_seq, bool self_plan, const float* a,
                             const float* b, const float* A_log, const float* dt_bias,
                             const Shape& s, int64_t max_chunks, void* w, void* u, void* aqk,
-                            float* eg, void* kf, void* qf, hipStream_t st) {
+                            float* eg, void* kf, void* qf, int32_t* nonfinite, hipStream_t st) {
   if (self_plan && s.B > kMaxSelfPlanRequests) return hipErrorInvalidValue;
   _Float16* W = (_Float16*)w;
   _Float16* U = (_Float16*)u;
@@ -587,7 +588,7 @@ hipError_t launch_mfma_prep(const void* q, const void* k, const void* v,
                                    A_log,                                                      \
                                    dt_bias, s,                                                 \
                                    max_chunks, W, U, (_Float16*)aqk, eg, (_Float16*)kf,      \
-                                   (_Float16*)qf, st);
+                                   (_Float16*)qf, nonfinite, st);
   GDN_PREP_CASE(64, 64)
   GDN_PREP_CASE(64, 128)
   GDN_PREP_CASE(64, 256)

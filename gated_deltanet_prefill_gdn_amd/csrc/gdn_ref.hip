@@ -156,7 +156,8 @@ __global__ __launch_bounds__(256) void ref_state_kernel(
     const Tin* __restrict__ q, const Tin* __restrict__ k, const int64_t* __restrict__ cu,
     const int64_t* __restrict__ cache_indices, const int32_t* __restrict__ chunk_off,
     const double* __restrict__ gcum, const float* __restrict__ W, const float* __restrict__ U,
-    int H, int HV, int dk, int dv, float* __restrict__ state_pool, Tin* __restrict__ out) {
+    int H, int HV, int dk, int dv, float* __restrict__ state_pool, Tin* __restrict__ out,
+    int32_t* __restrict__ nonfinite) {
   __shared__ float s_S[kBV][kMaxDk + 1];
   __shared__ float s_U[C][kBV + 1];
   __shared__ float s_Aqk[C][C + 1];
@@ -235,7 +236,13 @@ __global__ __launch_bounds__(256) void ref_state_kernel(
     }
   }
   __syncthreads();
-  for (int idx = tid; idx < kBV * dk; idx += 256) Sg[idx] = s_S[idx / dk][idx % dk];
+  bool finite = true;
+  for (int idx = tid; idx < kBV * dk; idx += 256) {
+    const float x = s_S[idx / dk][idx % dk];
+    Sg[idx] = x;
+    finite = finite && __builtin_isfinite(x);
+  }
+  if (!finite) *nonfinite = 1;
 }
 
 }  // namespace
@@ -260,17 +267,17 @@ hipError_t launch_ref_prep(const void* k, const void* v, const int64_t* cu_seqle
 hipError_t launch_ref_state(const void* q, const void* k, const int64_t* cu_seqlens,
                             const int64_t* cache_indices, const int32_t* chunk_off,
                             const double* gcum, const float* w, const float* u, const Shape& s,
-                            float* state_pool, void* out, hipStream_t st) {
+                            float* state_pool, void* out, int32_t* nonfinite, hipStream_t st) {
   const dim3 grid((unsigned)s.B, (unsigned)s.HV, (unsigned)(s.dv / kBV));
   if (s.bf16) {
     hipLaunchKernelGGL(ref_state_kernel<__hip_bfloat16>, grid, dim3(256), 0, st,
                        (const __hip_bfloat16*)q, (const __hip_bfloat16*)k, cu_seqlens,
                        cache_indices, chunk_off, gcum, w, u, s.H, s.HV, s.dk, s.dv, state_pool,
-                       (__hip_bfloat16*)out);
+                       (__hip_bfloat16*)out, nonfinite);
   } else {
     hipLaunchKernelGGL(ref_state_kernel<float>, grid, dim3(256), 0, st, (const float*)q,
                        (const float*)k, cu_seqlens, cache_indices, chunk_off, gcum, w, u, s.H,
-                       s.HV, s.dk, s.dv, state_pool, (float*)out);
+                       s.HV, s.dk, s.dv, state_pool, (float*)out, nonfinite);
   }
   return hipGetLastError();
 }

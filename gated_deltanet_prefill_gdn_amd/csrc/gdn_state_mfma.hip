@@ -81,7 +81,8 @@ __global__ __launch_bounds__(64 * (2 + NO + kStoreWaves<DK>)) void mfma_state_ke
     const int64_t* __restrict__ cu, const int64_t* __restrict__ cache_indices,
     const int32_t* __restrict__ chunk_off, const _Float16* __restrict__ W, const _Float16* __restrict__ Ut,
     const _Float16* __restrict__ Aqk, const float* __restrict__ egws, int B, int H, int HV,
-    int DV, float* __restrict__ state_pool, uint16_t* __restrict__ out) {
+    int DV, float* __restrict__ state_pool, uint16_t* __restrict__ out,
+    int32_t* __restrict__ nonfinite) {
   constexpr int NKS = DK / 32;    // 32-wide dk steps
   constexpr int NOWN = NKS / 2;   // dk steps of S^T held by each state wave
   __shared__ StateSmem<NKS, NC> sm;
@@ -244,15 +245,21 @@ __global__ __launch_bounds__(64 * (2 + NO + kStoreWaves<DK>)) void mfma_state_ke
 
     lds_barrier();  // (F) the store wave reads the last chunk's O
 
-    // ---- write the state back in place
+    // ---- write the state back in place; raise the flag if it is not finite (an fp16
+    // intermediate out of range)
+    bool finite = true;
 #pragma unroll
     for (int c = 0; c < NC; ++c)
 #pragma unroll
       for (int sp = 0; sp < NOWN; ++sp)
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
+        for (int tt = 0; tt < 2; ++tt) {
           *reinterpret_cast<f32x4*>(Sg + c * 16 * DK + 32 * (hs * NOWN + sp) + 16 * tt + 4 * g) =
               S[c][sp][tt];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) finite = finite && __builtin_isfinite(S[c][sp][tt][i]);
+        }
+    if (__ballot(!finite) != 0 && l == 0) *nonfinite = 1;
   } else if (wv < 2 + NO) {
     // ======================= output wave =======================
     // Output wave ow finishes row tiles I = NRO ow .. NRO ow + NRO - 1 of every column
@@ -395,12 +402,12 @@ template <int DK, int NC, int PD>
 hipError_t launch_state_t(const void* qf, const void* kf, const int64_t* cu, const int64_t* idx,
                           const int32_t* off, const _Float16* w,
                           const _Float16* u, const _Float16* aqk, const float* eg, const Shape& s,
-                          float* pool, void* out, hipStream_t st) {
+                          float* pool, void* out, int32_t* nonfinite, hipStream_t st) {
   const int64_t pairs8 = (s.B * s.HV + 7) / 8;
   const int64_t blocks = pairs8 * 8 * (s.dv / (16 * NC));
   hipLaunchKernelGGL((mfma_state_kernel<DK, NC, PD>), dim3((unsigned)blocks), dim3(64 * (2 + NO + kStoreWaves<DK>)), 0,
                      st, (const _Float16*)qf, (const _Float16*)kf, cu, idx, off, w, u, aqk,
-                     eg, (int)s.B, s.H, s.HV, s.dv, pool, (uint16_t*)out);
+                     eg, (int)s.B, s.H, s.HV, s.dv, pool, (uint16_t*)out, nonfinite);
   return hipGetLastError();
 }
 
@@ -410,7 +417,7 @@ hipError_t launch_mfma_state(const void* qf, const void* kf, const int64_t* cu_s
                              const int64_t* cache_indices, const int32_t* chunk_off,
                              const void* w, const void* u, const void* aqk,
                              const float* eg, const Shape& s, float* state_pool, void* out,
-                             hipStream_t st) {
+                             int32_t* nonfinite, hipStream_t st) {
   const _Float16* W = (const _Float16*)w;
   const _Float16* U = (const _Float16*)u;
   // Two column tiles (32 state rows) per workgroup; dv is a multiple of 32. Loads run
@@ -418,7 +425,8 @@ hipError_t launch_mfma_state(const void* qf, const void* kf, const int64_t* cu_s
 #define GDN_STATE_CASE(DKv, PDv)                                                               \
   if (s.dk == DKv)                                                                             \
     return launch_state_t<DKv, 2, PDv>(qf, kf, cu_seqlens, cache_indices, chunk_off, W, U,    \
-                                       (const _Float16*)aqk, eg, s, state_pool, out, st);
+                                       (const _Float16*)aqk, eg, s, state_pool, out, nonfinite, \
+                                       st);
   GDN_STATE_CASE(64, 2)
   GDN_STATE_CASE(128, 2)
   GDN_STATE_CASE(256, 1)

@@ -86,7 +86,25 @@ size_t gdn_prefill_workspace_size(const gdn_problem_t* prob, int32_t chunk_size)
 
 /* The prefill forward (see the top of this file). chunk_size must be 64.
  * workspace: device memory of at least gdn_prefill_workspace_size bytes, 256-byte
- * aligned; its contents on entry do not matter. stream: a hipStream_t or NULL. */
+ * aligned; its contents on entry do not matter. stream: a hipStream_t or NULL.
+ *
+ * Magnitude range of bf16 inputs. The state and every output are accumulated in fp32,
+ * but the bf16 path rounds its per-chunk intermediates to fp16 for the matrix cores:
+ * the decayed keys and queries, A_qk and W<- (all bounded by 1 in magnitude, whatever
+ * the inputs), and U~, U and the state's operand copy, which scale with |v| and |state|.
+ * fp16 holds magnitudes up to 65504 with 11 significant bits from 2^-14 (about 6.1e-5)
+ * up; below that its spacing is a fixed 2^-24. So:
+ *   - entries of v and of the initial states up to about 2^12 (4096) in magnitude keep
+ *     every fp16 intermediate finite on inputs like the benchmarked workloads (U~ and the
+ *     state can grow to several times |v|); beyond that an intermediate may overflow,
+ *     the affected outputs and states become inf or NaN, and the call raises the flag
+ *     that gdn_prefill_nonfinite reads;
+ *   - at magnitudes down to about 2^-10 (1e-3) the results keep the bf16 accuracy
+ *     (outputs within 2e-2 rms plus their own bf16 rounding, states within 1e-3 relative
+ *     of the fp64 recurrence); smaller values lose relative precision in fp16's
+ *     subnormal range, silently.
+ * Inputs outside that range belong on the fp32 path (GDN_DTYPE_F32), which holds the
+ * state, every intermediate and the output in fp32. */
 gdn_status_t gdn_prefill_fwd(const void* q, const void* k, const void* v, const float* a,
                              const float* b, const float* A_log, const float* dt_bias,
                              float* state_pool, const int64_t* cache_indices,
@@ -104,6 +122,16 @@ gdn_status_t gdn_prefill_fwd(const void* q, const void* k, const void* v, const 
                             its transition operator); 3: combine (every segment's start
                             state); 4: state pass + outputs. Stages 2 and 3 launch nothing
                             when no request is cut. */
+
+/* Whether the last gdn_prefill_fwd call that ran with `workspace` (and launched kernels:
+ * N > 0 and B > 0) left a non-finite value in any final state it wrote: the sign of an
+ * intermediate outside its range (see the magnitude range above). Each such call clears
+ * the flag before its state pass and raises it if a final state is not finite; the flag
+ * is the workspace's first 4 bytes. Copies it to *nonfinite (1 raised, 0 clear) after
+ * synchronising `stream`, so call it after the prefill on the same stream. Debugging and
+ * tests; GDN_OK, or GDN_ERR_INVALID_ARG / GDN_ERR_WORKSPACE / GDN_ERR_HIP. */
+gdn_status_t gdn_prefill_nonfinite(const void* workspace, size_t workspace_bytes,
+                                   int32_t* nonfinite, void* stream);
 
 /* Which kernels run the sequential state pass (stages 2-4 below) of a prefill call of this
  * shape; a function of the descriptor only. Host only, no HIP calls. Returns -1 for an

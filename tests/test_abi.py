@@ -129,6 +129,18 @@ def test_validate_inputs_refuses_what_it_cannot_copy():
             gdn.GDN_ERR_UNSUPPORTED
 
 
+def test_nonfinite_flag_argument_checks():
+    lib = gdn.load_library()
+    P = ctypes.c_void_p
+    flag = ctypes.c_int32(7)
+    assert lib.gdn_prefill_nonfinite(P(0), 1024, ctypes.byref(flag), P(0)) == \
+        gdn.GDN_ERR_INVALID_ARG
+    assert lib.gdn_prefill_nonfinite(P(4096), 1024, None, P(0)) == gdn.GDN_ERR_INVALID_ARG
+    assert lib.gdn_prefill_nonfinite(P(4096), 2, ctypes.byref(flag), P(0)) == \
+        gdn.GDN_ERR_WORKSPACE
+    assert flag.value == 7
+
+
 def test_empty_problem_is_a_no_op():
     # N == 0 or B == 0: nothing to read or write, so null pointers are fine
     assert call(prob(N=0, B=3), nonnull=False, ws_bytes=0, ws_ptr=0) == gdn.GDN_OK

@@ -1,0 +1,84 @@
+"""Magnitude range of the bf16 path (its per-chunk intermediates are fp16) and the
+non-finite flag, through the C ABI. The operation is linear in (state, v) (state-transition
+equation of "Simple math to speed up GDN prefill", Reminder), so a scaled input has the
+same relative accuracy bar as the unscaled one for as long as every fp16 intermediate stays
+in range: v and the initial state scaled by 10^2 and by 10^-3 must meet the bf16 bars,
+and the flag must stay clear; v scaled far beyond fp16 range must raise it. Each shape
+runs once per state schedule: column slices (the dense batch's head layout) and segments
+(one long request)."""
+import numpy as np
+import pytest
+
+import gdn_synth
+import oracle
+from gpu_util import announce, compare, to_device
+
+pytestmark = pytest.mark.gpu
+
+SHAPES = {
+    # (lengths, H, HV): B * HV * dv / 32 = 256 -> column slices; 4 -> segments
+    "column-slices": ([300, 64, 129, 1], 16, 16),
+    "segments": ([3000], 1, 1),
+}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no HIP device")
+    import gated_deltanet_prefill_gdn_amd as gdn
+    gdn.load_library()
+    yield
+
+
+def _scaled_problem(shape, scale, seed):
+    lengths, H, HV = SHAPES[shape]
+    p = gdn_synth.make_problem(seed, lengths, H, HV, 128, 128, dtype="bf16", a_mean=-3.0,
+                               state_std=0.5)
+    v32 = gdn_synth.bf16_bits_to_f32(p.v).astype(np.float64) * scale
+    p.v = gdn_synth.f32_to_bf16_bits(v32.astype(np.float32)).reshape(p.v.shape)
+    p.state_pool = (p.state_pool.astype(np.float64) * scale).astype(np.float32)
+    return p
+
+
+def _run(p, label):
+    import torch
+    import gated_deltanet_prefill_gdn_amd as gdn
+    d = to_device(p)
+    prob = gdn.problem_of(d["q"], d["k"], d["v"], d["state_pool"], d["cache_indices"])
+    ws = torch.empty(gdn.gdn_prefill_workspace_size(prob), dtype=torch.uint8, device="cuda:0")
+    ws.fill_(0xFF)  # the call itself must clear the flag
+    announce(f"{label} N={p.N} B={p.B} HV={p.HV} schedule={gdn.gdn_prefill_state_schedule(prob)}")
+    out = gdn.gdn_prefill_fwd(d["q"], d["k"], d["v"], d["a"], d["b"], d["A_log"], d["dt_bias"],
+                              d["state_pool"], d["cache_indices"], d["cu_seqlens"], workspace=ws)
+    flag = gdn.gdn_prefill_nonfinite(ws)
+    return (out.float().cpu().numpy().astype(np.float64), d["state_pool"].cpu().numpy(), flag,
+            gdn.gdn_prefill_state_schedule(prob))
+
+
+@pytest.mark.parametrize("shape", list(SHAPES))
+@pytest.mark.parametrize("scale", [1e2, 1e-3])
+def test_scaled_inputs_meet_the_bars(shape, scale):
+    p = _scaled_problem(shape, scale, 71)
+    out, pool, flag, sched = _run(p, f"range-{shape}-x{scale:g}")
+    assert sched == (0 if shape == "column-slices" else 1)
+    assert not flag
+    rep = compare(p, out, pool, oracle.prefill(p))
+    announce(f"range-{shape}-x{scale:g} {rep}")
+
+
+@pytest.mark.parametrize("shape", list(SHAPES))
+def test_overflow_raises_the_flag(shape):
+    """v ~ 1e6 (representable in bf16, beyond fp16's 65504): U~ overflows in fp16."""
+    p = _scaled_problem(shape, 1e6, 72)
+    out, pool, flag, _ = _run(p, f"overflow-{shape}")
+    assert flag
+    assert not np.all(np.isfinite(pool[p.cache_indices]))
+
+
+def test_flag_clear_on_the_fp32_path():
+    p = gdn_synth.make_problem(73, [200, 70], 1, 2, 64, 64, dtype="f32", state_std=0.5)
+    out, pool, flag, sched = _run(p, "flag-fp32")
+    assert sched == 2 and not flag
+    compare(p, out, pool, oracle.prefill(p))

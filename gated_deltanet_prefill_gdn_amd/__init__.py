@@ -40,12 +40,14 @@ STAGE_KERNELS = {
         "state_combine": "-", "state": "ref_state_kernel"},
 }
 
+GDN_NOALLOC_SCRATCH_BYTES = 64 << 20
+
 GDN_SCHEDULE_COLUMN_SLICES = 0
 GDN_SCHEDULE_SEGMENTS = 1
 GDN_SCHEDULE_FP32 = 2
 
 EXPORTED = ("gdn_prefill_workspace_size", "gdn_prefill_state_schedule", "gdn_prefill_fwd",
-            "gdn_prefill_fwd_events", "gdn_prefill_nonfinite",
+            "gdn_prefill_fwd_events", "gdn_prefill_fwd_noalloc", "gdn_prefill_nonfinite",
             "gdn_decode_fwd", "gdn_recurrent_fwd", "gdn_promote_scan", "gdn_validate_inputs",
             "gdn_status_str", "gdn_version")
 
@@ -106,6 +108,8 @@ def load_library(path: str = LIB_PATH):
     L.gdn_prefill_fwd.restype = ctypes.c_int
     L.gdn_prefill_fwd.argtypes = [P, P, P, P, P, P, P, P, P, P, ctypes.c_int32, P, PP, P,
                                   ctypes.c_size_t, P]
+    L.gdn_prefill_fwd_noalloc.restype = ctypes.c_int
+    L.gdn_prefill_fwd_noalloc.argtypes = [P, P, P, P, P, P, P, P, P, P, ctypes.c_int32, P, PP, P]
     L.gdn_prefill_fwd_events.restype = ctypes.c_int
     L.gdn_prefill_fwd_events.argtypes = L.gdn_prefill_fwd.argtypes + [P]
     L.gdn_decode_fwd.restype = ctypes.c_int
@@ -199,6 +203,24 @@ def gdn_prefill_fwd(q, k, v, a, b, A_log, dt_bias, state_pool, cache_indices, cu
                     chunk_size: int = 64, out=None, workspace=None, stream=None):
     return _prefill(q, k, v, a, b, A_log, dt_bias, state_pool, cache_indices, cu_seqlens,
                     chunk_size, out, workspace, stream, None)
+
+
+def gdn_prefill_fwd_noalloc(q, k, v, a, b, A_log, dt_bias, state_pool, cache_indices,
+                            cu_seqlens, out, chunk_size: int = 64, stream=None):
+    """gdn_prefill_fwd on the library's built-in device workspace: allocates nothing, so
+    ``out`` must be given. Problems whose workspace exceeds GDN_NOALLOC_SCRATCH_BYTES raise
+    GdnError(GDN_ERR_WORKSPACE); calls that may overlap on one GPU must be serialised."""
+    import torch
+    prob, out = _check_prefill_args(q, k, v, a, b, A_log, dt_bias, state_pool, cache_indices,
+                                    cu_seqlens, out)
+    st = (stream or torch.cuda.current_stream(q.device)).cuda_stream
+    rc = load_library().gdn_prefill_fwd_noalloc(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(A_log), _ptr(dt_bias),
+        _ptr(state_pool), _ptr(cache_indices), _ptr(cu_seqlens), int(chunk_size), _ptr(out),
+        ctypes.byref(prob), ctypes.c_void_p(st))
+    if rc != GDN_OK:
+        raise GdnError(rc, "gdn_prefill_fwd_noalloc")
+    return out
 
 
 def gdn_prefill_fwd_events(q, k, v, a, b, A_log, dt_bias, state_pool, cache_indices,

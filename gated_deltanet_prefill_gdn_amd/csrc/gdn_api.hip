@@ -4,6 +4,8 @@
 #include <string.h>
 
 #include <algorithm>
+#include <atomic>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -250,6 +252,62 @@ gdn_status_t gdn_prefill_fwd(const void* q, const void* k, const void* v, const 
                              void* stream) {
   return run_prefill(q, k, v, a, b, A_log, dt_bias, state_pool, cache_indices, cu_seqlens,
                      chunk_size, out, prob, workspace, workspace_bytes, stream, nullptr);
+}
+
+}  // extern "C"
+
+// Built-in workspace of gdn_prefill_fwd_noalloc: one array per GPU the library runs on,
+// held until the process ends. In host code `scratch` names a host-side stand-in only; the
+// device address comes from hipGetSymbolAddress, once per device, and only that address is
+// ever passed to a kernel.
+static __device__ __align__(256) char scratch[GDN_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mutex;
+
+// The current device's scratch address (resolved on the first call on that device), or
+// nullptr on a HIP error.
+void* scratch_for_current_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+  if (!p) {
+    void* q = nullptr;
+    if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || !q) return nullptr;
+    g_scratch_ptr[dev].store(q, std::memory_order_release);
+    p = q;
+  }
+  return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+gdn_status_t gdn_prefill_fwd_noalloc(const void* q, const void* k, const void* v,
+                                     const float* a, const float* b, const float* A_log,
+                                     const float* dt_bias, float* state_pool,
+                                     const int64_t* cache_indices, const int64_t* cu_seqlens,
+                                     int32_t chunk_size, void* out, const gdn_problem_t* prob,
+                                     void* stream) {
+  Shape s;
+  const gdn_status_t ps = check_problem(prob, chunk_size, &s);
+  if (ps != GDN_OK) return ps;
+  if (s.N == 0 || s.B == 0) return GDN_OK;
+  // the call's workspace must fit the built-in array
+  if (layout_for(s, choose_path(s)).total > (size_t)GDN_NOALLOC_SCRATCH_BYTES)
+    return GDN_ERR_WORKSPACE;
+  void* ws = scratch_for_current_device();
+  if (!ws) return GDN_ERR_HIP;
+  return run_prefill(q, k, v, a, b, A_log, dt_bias, state_pool, cache_indices, cu_seqlens,
+                     chunk_size, out, prob, ws, (size_t)GDN_NOALLOC_SCRATCH_BYTES, stream,
+                     nullptr);
 }
 
 gdn_status_t gdn_prefill_fwd_events(const void* q, const void* k, const void* v, const float* a,

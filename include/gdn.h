@@ -112,6 +112,24 @@ gdn_status_t gdn_prefill_fwd(const void* q, const void* k, const void* v, const 
                              const gdn_problem_t* prob, void* workspace, size_t workspace_bytes,
                              void* stream);
 
+/* gdn_prefill_fwd for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same operation,
+ * arguments, layouts and errors, without the workspace arguments. Its workspace is a
+ * built-in array of GDN_NOALLOC_SCRATCH_BYTES in device memory, one per GPU, created
+ * when the library is loaded on that GPU and held until the process ends; the first call
+ * on a device looks up that device's copy (hipGetSymbolAddress), and no call allocates or
+ * frees memory. A problem whose workspace (gdn_prefill_workspace_size) exceeds
+ * GDN_NOALLOC_SCRATCH_BYTES is refused with GDN_ERR_WORKSPACE before anything runs. Every
+ * call on one GPU uses that GPU's one array, whose contents on entry do not matter: calls
+ * that may overlap on one GPU (different streams, or concurrent host threads without
+ * ordering) race on it and must be serialised by the caller. */
+#define GDN_NOALLOC_SCRATCH_BYTES (64ull << 20)
+gdn_status_t gdn_prefill_fwd_noalloc(const void* q, const void* k, const void* v, const float* a,
+                                     const float* b, const float* A_log, const float* dt_bias,
+                                     float* state_pool, const int64_t* cache_indices,
+                                     const int64_t* cu_seqlens, int32_t chunk_size, void* out,
+                                     const gdn_problem_t* prob, void* stream);
+
 /* Stages of one call, in launch order, for gdn_prefill_fwd_events. */
 #define GDN_NUM_STAGES 5 /* 0: chunk table (and, for fp32 inputs, the gates and log
                             cumulative decay; for bf16 inputs of at most 64 requests the

@@ -236,7 +236,7 @@ typedef struct {
  * firings). Each scan holds a memory M (dk x dv, fp32) updated in place; at firing f its
  * n pairs are written at once, all against the memory as it stood before the firing:
  *   M <- diag(exp(gamma_f)) M;  M <- M - K_f^T (beta_f o K_f) M;  M <- M + K_f^T (w_f o V_f)
- * (decay, erase at the new addresses, write; o scales the pairs' rows).
+ * (per-row decay, gated removal along the new keys, gated write; o scales the pairs' rows).
  * Layouts (dense, row-major, DEVICE pointers):
  *   K      [scans, F, n, dk]  bf16, unit rows (the probe's normalised write keys)
  *   V      [scans, F, n, dv]  bf16

@@ -1,8 +1,8 @@
 """Chunkwise forms of the GDN forward in fp64 -- TEST INFRASTRUCTURE ONLY.
 
-These follow the pages' chunked algorithm step by step, one (sequence, value head)
-at a time, so the oracle's self-checks can show that the chunked method and the
-token recurrence agree (awehrs.io "NRM training kernels", General implementation
+These evaluate the chunked method's equations, one (sequence, value head) at a time,
+so the oracle's self-checks can show that the chunked method and the token recurrence
+agree (awehrs.io "NRM training kernels", General implementation
 item 1: at level 0 the chunkwise algorithm gives what sequential application
 gives). Row convention: S is dv x dk; K, Q are n x dk with tokens as rows; V is
 n x dv.
@@ -16,8 +16,9 @@ Variants (all must agree with the recurrence):
 * ``saved_inverse`` -- same page, section Save one invert: N^-1 = G M^-1 G^-1 with
   the diagonal matrices G = diag(gamma), G^-1 = diag(1/gamma) taken literally
   (finite only while gamma does not underflow).
-* ``p3_literal`` -- pymllm gdn_chunkwise page, section Algorithm: WY vectors w_i and
-  u~_i = (beta_i/gamma_i) v_i - ..., then O = gamma (...) and S_new = gamma_C (...).
+* ``p3_literal`` -- the pymllm gdn_chunkwise page's form (section Algorithm): values
+  divided by the cumulative decay before the WY solve, u~ = M^-1 B G^-1 V, with the
+  decay multiplied back in the output and state equations.
   The extracted w_i recursion is ill-typed; it is read as the matrix form of the
   Reminder section, (I + tril(B K K^T, -1)) W = B K.
 * ``safe`` -- the same map with every decay written as exp of a non-positive

@@ -3,20 +3,20 @@
 Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 ``bench.py`` may import this module. It shares no code with the HIP library.
 
-What it computes: the update stage of one level of the nested model on the awehrs.io
-page "NRM training kernels" (section General implementation, the Promote algorithm,
-and section Kernel: a scan over firings, split over batch, heads and value blocks). Each
-(batch, head) scan holds a dk x dv memory M. At firing f the level receives n pairs at
-once: unit write keys K_f (n x dk), values V_f (n x dv), erase gates beta_f and write
-gates w_f (n each), and one log-decay vector gamma_f (dk, one entry per key row). The
-firing applies, in the page's order,
+What it computes: the update stage of one level of the nested model (awehrs.io "NRM
+training kernels", section General implementation, Promote algorithm; section Kernel, a
+scan over firings split over batch, heads and value blocks). Each (batch, head) scan
+holds a dk x dv memory M. At firing f the level receives n pairs together: unit write
+keys K_f (n x dk), values V_f (n x dv), erase gates beta_f and write gates w_f (n each),
+and one log-decay vector gamma_f (dk, one entry per key row). A firing is the composition
+of three linear maps of M, taken in this order:
 
-    M <- diag(exp(gamma_f)) M                 decay the whole state
-    M <- M - K_f^T (beta_f o K_f) M           erase at the new addresses
-    M <- M + K_f^T (w_f o V_f)                write every pair at once
+    M <- diag(exp(gamma_f)) M                 (per-row decay)
+    M <- M - K_f^T (beta_f o K_f) M           (gated removal along the n keys)
+    M <- M + K_f^T (w_f o V_f)                (gated rank-n write)
 
-All pairs of a firing act on the state as it stood before the firing (simultaneous
-writes): there is no order among them. The probe that derives K, beta, w and gamma from
+The n pairs enter as sums over pairs, so no pair sees another pair of its own firing and
+their order does not matter. The probe that derives K, beta, w and gamma from
 the level below (dense projections, normalisation, sigmoid, mean of -softplus) is not
 part of this stage; its outputs are this stage's inputs.
 

@@ -15,7 +15,8 @@ import os
 from typing import Optional
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libgdn.so")
+# GDN_LIBRARY names another build of the same sources (the CPU sanitizer runs use it).
+LIB_PATH = os.environ.get("GDN_LIBRARY") or os.path.join(PKG, "libgdn.so")
 
 GDN_OK = 0
 GDN_ERR_INVALID_ARG = 1

@@ -49,6 +49,7 @@ GDN_SCHEDULE_FP32 = 2
 
 EXPORTED = ("gdn_prefill_workspace_size", "gdn_prefill_state_schedule", "gdn_prefill_fwd",
             "gdn_prefill_fwd_events", "gdn_prefill_fwd_noalloc", "gdn_prefill_nonfinite",
+            "gdn_prefill_bwd_workspace_size", "gdn_prefill_bwd",
             "gdn_decode_fwd", "gdn_recurrent_fwd", "gdn_promote_scan", "gdn_validate_inputs",
             "gdn_status_str", "gdn_version")
 
@@ -102,6 +103,11 @@ def load_library(path: str = LIB_PATH):
     PP = ctypes.POINTER(GdnProblem)
     L.gdn_prefill_workspace_size.restype = ctypes.c_size_t
     L.gdn_prefill_workspace_size.argtypes = [PP, ctypes.c_int32]
+    L.gdn_prefill_bwd_workspace_size.restype = ctypes.c_size_t
+    L.gdn_prefill_bwd_workspace_size.argtypes = [PP, ctypes.c_int32]
+    L.gdn_prefill_bwd.restype = ctypes.c_int
+    L.gdn_prefill_bwd.argtypes = [P] * 10 + [ctypes.c_int32] + [P] * 10 + [PP, P, ctypes.c_size_t,
+                                                                          P]
     L.gdn_prefill_nonfinite.restype = ctypes.c_int
     L.gdn_prefill_nonfinite.argtypes = [P, ctypes.c_size_t, ctypes.POINTER(ctypes.c_int32), P]
     L.gdn_prefill_state_schedule.restype = ctypes.c_int32
@@ -237,7 +243,7 @@ def gdn_prefill_fwd_events(q, k, v, a, b, A_log, dt_bias, state_pool, cache_indi
 
 
 def _check_prefill_args(q, k, v, a, b, A_log, dt_bias, state_pool, cache_indices, cu_seqlens,
-                        out):
+                        out, want_out: bool = True):
     """Shapes, dtypes, devices and contiguity of a prefill call's tensors; allocates ``out``
     if it is None. Returns (problem descriptor, out)."""
     import torch
@@ -269,6 +275,8 @@ def _check_prefill_args(q, k, v, a, b, A_log, dt_bias, state_pool, cache_indices
     if cu_seqlens.shape[0] != cache_indices.shape[0] + 1:
         raise ValueError("cu_seqlens must have B + 1 entries")
     prob = problem_of(q, k, v, state_pool, cache_indices)
+    if not want_out:
+        return prob, None
     if out is None:
         out = torch.empty((N, HV, dv), dtype=v.dtype, device=dev)
     else:
@@ -308,6 +316,50 @@ def _prefill(q, k, v, a, b, A_log, dt_bias, state_pool, cache_indices, cu_seqlen
     if rc != GDN_OK:
         raise GdnError(rc, "gdn_prefill_fwd")
     return out
+
+
+def gdn_prefill_bwd_workspace_size(prob: GdnProblem, chunk_size: int = 64) -> int:
+    return int(load_library().gdn_prefill_bwd_workspace_size(ctypes.byref(prob),
+                                                              int(chunk_size)))
+
+
+def gdn_prefill_bwd(q, k, v, a, b, A_log, dt_bias, state_pool, cache_indices, cu_seqlens,
+                    dout, dstate, chunk_size: int = 64, workspace=None, stream=None):
+    """Gradients of a prefill call's inputs (see gdn_prefill_bwd in include/gdn.h).
+    state_pool: the pool as it was BEFORE the forward call; dout [N, HV, dv] in v's dtype;
+    dstate [B, HV, dv, dk] fp32. Returns a dict of fp32 tensors dq, dk, dv, da, db, dA_log,
+    ddt_bias, dstate0."""
+    import torch
+    dev = q.device
+    prob, _ = _check_prefill_args(q, k, v, a, b, A_log, dt_bias, state_pool, cache_indices,
+                                  cu_seqlens, None, want_out=False)
+    N, H, dk_ = q.shape
+    HV, dv_ = v.shape[1], v.shape[2]
+    B = cache_indices.shape[0]
+    _need(dout, "dout", dtype=v.dtype, ndim=3, device=dev)
+    if tuple(dout.shape) != (N, HV, dv_):
+        raise ValueError("dout must be [N, HV, dv]")
+    _need(dstate, "dstate", dtype=torch.float32, ndim=4, device=dev)
+    if tuple(dstate.shape) != (B, HV, dv_, dk_):
+        raise ValueError("dstate must be [B, HV, dv, dk]")
+    f = dict(device=dev, dtype=torch.float32)
+    g = {"dq": torch.empty((N, H, dk_), **f), "dk": torch.empty((N, H, dk_), **f),
+         "dv": torch.empty((N, HV, dv_), **f), "da": torch.empty((N, HV), **f),
+         "db": torch.empty((N, HV), **f), "dA_log": torch.empty((HV,), **f),
+         "ddt_bias": torch.empty((HV,), **f), "dstate0": torch.empty((B, HV, dv_, dk_), **f)}
+    need = gdn_prefill_bwd_workspace_size(prob, chunk_size)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    st = (stream or torch.cuda.current_stream(dev)).cuda_stream
+    rc = load_library().gdn_prefill_bwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(A_log), _ptr(dt_bias),
+        _ptr(state_pool), _ptr(cache_indices), _ptr(cu_seqlens), int(chunk_size), _ptr(dout),
+        _ptr(dstate), *[_ptr(g[n]) for n in ("dq", "dk", "dv", "da", "db", "dA_log",
+                                             "ddt_bias", "dstate0")],
+        ctypes.byref(prob), _ptr(workspace), workspace.numel(), ctypes.c_void_p(st))
+    if rc != GDN_OK:
+        raise GdnError(rc, "gdn_prefill_bwd")
+    return g
 
 
 def gdn_prefill_nonfinite(workspace, stream=None) -> bool:

@@ -388,6 +388,40 @@ gdn_status_t gdn_promote_scan(const void* K, const void* V, const float* beta, c
   return GDN_OK;
 }
 
+size_t gdn_prefill_bwd_workspace_size(const gdn_problem_t* prob, int32_t chunk_size) {
+  Shape s;
+  if (check_problem(prob, chunk_size, &s) != GDN_OK) return 0;
+  return bwd_layout_for(s).total;
+}
+
+gdn_status_t gdn_prefill_bwd(const void* q, const void* k, const void* v, const float* a,
+                             const float* b, const float* A_log, const float* dt_bias,
+                             const float* state_pool, const int64_t* cache_indices,
+                             const int64_t* cu_seqlens, int32_t chunk_size, const void* dout,
+                             const float* dstate, float* dq, float* dk, float* dv, float* da,
+                             float* db, float* dA_log, float* ddt_bias, float* dstate0,
+                             const gdn_problem_t* prob, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  Shape s;
+  const gdn_status_t ps = check_problem(prob, chunk_size, &s);
+  if (ps != GDN_OK) return ps;
+  if (s.B == 0) return GDN_OK;
+  if (!A_log || !dt_bias || !state_pool || !cache_indices || !cu_seqlens || !dstate ||
+      !dA_log || !ddt_bias || !dstate0)
+    return GDN_ERR_INVALID_ARG;
+  if (s.N > 0 && (!q || !k || !v || !a || !b || !dout || !dq || !dk || !dv || !da || !db))
+    return GDN_ERR_INVALID_ARG;
+  if (!bwd_grids_fit(s)) return GDN_ERR_UNSUPPORTED;
+  const BwdLayout L = bwd_layout_for(s);
+  if (!workspace || workspace_bytes < L.total) return GDN_ERR_WORKSPACE;
+  if (((uintptr_t)workspace & 255) != 0) return GDN_ERR_WORKSPACE;
+  if (launch_backward(s, L, (char*)workspace, q, k, v, a, b, A_log, dt_bias, state_pool,
+                      cache_indices, cu_seqlens, dout, dstate, dq, dk, dv, da, db, dA_log,
+                      ddt_bias, dstate0, (hipStream_t)stream) != hipSuccess)
+    return GDN_ERR_HIP;
+  return GDN_OK;
+}
+
 gdn_status_t gdn_prefill_nonfinite(const void* workspace, size_t workspace_bytes,
                                    int32_t* nonfinite, void* stream) {
   if (!workspace || !nonfinite) return GDN_ERR_INVALID_ARG;

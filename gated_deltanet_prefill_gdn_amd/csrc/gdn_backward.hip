@@ -1,0 +1,441 @@
+// Backward of the prefill: gradients of every input given the gradients of the outputs
+// and of each request's final state.
+//
+// The forward is the token recurrence ("Simple math to speed up GDN prefill", section
+// Reminder; gates and normalisation from the pymllm gdn_chunkwise page, Module Contents)
+//   S_t = alpha S_{t-1} - alpha beta (S_{t-1} kh) kh^T + beta v kh^T,   out_t = S_t qh,
+// whose chunked evaluation reaches the same map, so these are the chunked forward's
+// gradients too. Reverse mode carries D = dL/dS_t from the last token to the first; with
+// Sp = S_{t-1} and row i of D, Sp:
+//   D     += dout_t qh^T
+//   dqh   += S_t^T dout_t                       dv_i   = beta (D kh)_i
+//   dbeta += sum_i (D kh)_i (v_i - alpha (Sp kh)_i)
+//   dalpha+= sum_i D_i . Sp_i - beta (D kh)_i (Sp kh)_i
+//   dkh   += sum_i -alpha beta ((Sp kh)_i D_i + (D kh)_i Sp_i) + beta v_i D_i
+//   D     <- alpha (D - beta (D kh) kh^T)
+// The rows of S and D are independent; only dqh, dkh, dalpha and dbeta sum over rows.
+//
+// Kernels (fp32 arithmetic throughout):
+//   rows    one workgroup per (request, value head, 16 rows). A forward sweep keeps the
+//           rows' state every 64 tokens; the reverse sweep recomputes 16 tokens at a time
+//           from the checkpoint before them, holds those 16 states in registers, and
+//           walks them backwards. Wave w holds rows 4w .. 4w+3, lane l the dk elements
+//           l + 64 e. Row dot products are wave sums; the per-token sums over the 16 rows
+//           go through LDS into a partial buffer per row block (no atomics: the result
+//           does not depend on scheduling).
+//   finish  one wave per (token, q/k head): sums the partials over row blocks and over
+//           the value heads that share the q/k head, then the chain rule through the L2
+//           norm (dq = dqh / n - q (q . dqh) / n^3) and the gates (da = dalpha dalpha/dx,
+//           db = dbeta beta (1 - beta)).
+//   gates   one workgroup per value head: dA_log and dt_bias gradients as sums over tokens.
+#include <algorithm>
+
+#include "gdn_internal.h"
+
+namespace gdn {
+namespace {
+
+constexpr int kCk = 64;            // tokens between checkpoints
+constexpr int kBwdRows = 16;       // state rows per workgroup
+constexpr int kRowsPerWave = 4;
+template <int DK>
+constexpr int kSub = DK <= 128 ? 16 : 8;  // tokens recomputed and walked back at a time
+
+__device__ __forceinline__ float ldx(const void* p, int64_t i, bool bf16) {
+  return bf16 ? __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(p)[i] << 16)
+              : reinterpret_cast<const float*>(p)[i];
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
+  return x;
+}
+
+__device__ __forceinline__ float softplusf(float x) {
+  return fmaxf(x, 0.f) + log1pf(expf(-fabsf(x)));
+}
+__device__ __forceinline__ float sigmoidf(float x) {
+  const float e = expf(-fabsf(x));
+  return x >= 0.f ? 1.f / (1.f + e) : e / (1.f + e);
+}
+
+struct BwdArgs {
+  const void *q, *k, *v, *dout;
+  const float *a, *b, *A_log, *dt_bias, *state_pool, *dstate;
+  const int64_t *cu, *cache_indices;
+  const int32_t* chunk_off;
+  float *dq, *dk, *dv, *da, *db, *dA_log, *ddt_bias, *dstate0;
+  float* ck;      // [chunk][HV][dv][dk]: state before the chunk's first token
+  float* part;    // [dv / 16][N][HV][2 dk + 2]: dqh, dkh, dalpha, dbeta per row block
+  float* dal;     // [N][HV]: dalpha * dalpha/dA_log per token
+  int64_t N;
+  int B, H, HV, DV;
+  float eps;
+  int bf16;
+};
+
+template <int DK>
+struct Token {
+  float qh[DK / 64], kh[DK / 64];
+  float alpha, beta;
+  float v[kRowsPerWave];
+};
+
+template <int DK>
+__device__ __forceinline__ void load_token(const BwdArgs& A, int64_t t, int h, int hv, int row0,
+                                           int l, Token<DK>& x) {
+  constexpr int E = DK / 64;
+  float qe[E], ke[E], sq = 0.f, sk = 0.f;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    qe[e] = ldx(A.q, (t * A.H + h) * DK + 64 * e + l, A.bf16);
+    ke[e] = ldx(A.k, (t * A.H + h) * DK + 64 * e + l, A.bf16);
+    sq += qe[e] * qe[e];
+    sk += ke[e] * ke[e];
+  }
+  const float rq = 1.f / sqrtf(wave_sum(sq) + A.eps);
+  const float rk = 1.f / sqrtf(wave_sum(sk) + A.eps);
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    x.qh[e] = qe[e] * rq;
+    x.kh[e] = ke[e] * rk;
+  }
+  const float xg = A.a[t * A.HV + hv] + A.dt_bias[hv];
+  x.alpha = expf(-expf(A.A_log[hv]) * softplusf(xg));
+  x.beta = sigmoidf(A.b[t * A.HV + hv]);
+#pragma unroll
+  for (int j = 0; j < kRowsPerWave; ++j)
+    x.v[j] = ldx(A.v, (t * A.HV + hv) * (int64_t)A.DV + row0 + j, A.bf16);
+}
+
+// One token's step on this wave's rows: s <- alpha s - alpha beta (s kh) kh + beta v kh.
+template <int DK>
+__device__ __forceinline__ void step(const Token<DK>& x, float (&s)[kRowsPerWave][DK / 64]) {
+  constexpr int E = DK / 64;
+#pragma unroll
+  for (int j = 0; j < kRowsPerWave; ++j) {
+    float p = 0.f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) p += s[j][e] * x.kh[e];
+    const float sk = wave_sum(p);
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+      s[j][e] = x.alpha * s[j][e] - x.alpha * x.beta * sk * x.kh[e] + x.beta * x.v[j] * x.kh[e];
+  }
+}
+
+template <int DK>
+__global__ __launch_bounds__(256) void bwd_rows_kernel(BwdArgs A) {
+  constexpr int E = DK / 64;
+  constexpr int SUB = kSub<DK>;
+  constexpr int NF = 2 * DK + 2;  // fields per token of a partial: dqh, dkh, dalpha, dbeta
+  __shared__ float part[4][SUB][NF];
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  const int nrb = A.DV / kBwdRows;
+  const int64_t x = blockIdx.x;
+  const int rb = (int)(x % nrb);
+  const int64_t p = x / nrb;
+  const int bq = (int)(p / A.HV), hv = (int)(p % A.HV);
+  if (bq >= A.B) return;
+  const int h = hv / (A.HV / A.H);
+  const int row0 = rb * kBwdRows + kRowsPerWave * w;  // this wave's first row
+  const int64_t t0 = A.cu[bq], L = A.cu[bq + 1] - t0;
+  const int64_t slot = A.cache_indices[bq];
+  const int64_t cbase = A.chunk_off[bq];
+  auto state_at = [&](const float* base, int j, int e) {
+    return base[((int64_t)(row0 + j)) * DK + 64 * e + l];
+  };
+  const float* S0 = A.state_pool + (slot * A.HV + hv) * (int64_t)A.DV * DK;
+  const float* DS = A.dstate + ((int64_t)bq * A.HV + hv) * A.DV * DK;
+  float* DS0 = A.dstate0 + ((int64_t)bq * A.HV + hv) * A.DV * DK;
+  auto ck_at = [&](int64_t c) { return A.ck + ((cbase + c) * A.HV + hv) * (int64_t)A.DV * DK; };
+
+  // ---- forward sweep: checkpoint every kCk tokens
+  float s[kRowsPerWave][E];
+#pragma unroll
+  for (int j = 0; j < kRowsPerWave; ++j)
+#pragma unroll
+    for (int e = 0; e < E; ++e) s[j][e] = state_at(S0, j, e);
+  for (int64_t t = 0; t < L; ++t) {
+    if (t % kCk == 0) {
+      float* c = ck_at(t / kCk);
+#pragma unroll
+      for (int j = 0; j < kRowsPerWave; ++j)
+#pragma unroll
+        for (int e = 0; e < E; ++e) c[((int64_t)(row0 + j)) * DK + 64 * e + l] = s[j][e];
+    }
+    Token<DK> tk;
+    load_token<DK>(A, t0 + t, h, hv, row0, l, tk);
+    step<DK>(tk, s);
+  }
+  // the checkpoints are read back by the same lanes that wrote them: no barrier needed
+
+  // ---- reverse sweep
+  float D[kRowsPerWave][E];
+#pragma unroll
+  for (int j = 0; j < kRowsPerWave; ++j)
+#pragma unroll
+    for (int e = 0; e < E; ++e) D[j][e] = state_at(DS, j, e);
+  const int64_t nsub = (L + SUB - 1) / SUB;
+  for (int64_t u = nsub - 1; u >= 0; --u) {
+    const int64_t u_lo = u * SUB, u_hi = min(u_lo + SUB, L);
+    const int64_t c = u_lo / kCk;
+    // recompute from the checkpoint before this sub-chunk
+    const float* cp = ck_at(c);
+#pragma unroll
+    for (int j = 0; j < kRowsPerWave; ++j)
+#pragma unroll
+      for (int e = 0; e < E; ++e) s[j][e] = cp[((int64_t)(row0 + j)) * DK + 64 * e + l];
+    for (int64_t t = c * kCk; t < u_lo; ++t) {
+      Token<DK> tk;
+      load_token<DK>(A, t0 + t, h, hv, row0, l, tk);
+      step<DK>(tk, s);
+    }
+    float sb[SUB][kRowsPerWave][E];  // S_{t-1} for the sub-chunk's tokens
+#pragma clang loop unroll(full)
+    for (int i = 0; i < SUB; ++i) {
+      if (u_lo + i < u_hi) {
+#pragma unroll
+        for (int j = 0; j < kRowsPerWave; ++j)
+#pragma unroll
+          for (int e = 0; e < E; ++e) sb[i][j][e] = s[j][e];
+        Token<DK> tk;
+        load_token<DK>(A, t0 + u_lo + i, h, hv, row0, l, tk);
+        step<DK>(tk, s);
+      }
+    }
+#pragma clang loop unroll(full)
+    for (int i = SUB - 1; i >= 0; --i) {
+      if (u_lo + i >= u_hi) continue;  // past the request's end (uniform)
+      const int64_t t = t0 + u_lo + i;
+      Token<DK> tk;
+      load_token<DK>(A, t, h, hv, row0, l, tk);
+      float st[kRowsPerWave][E];
+#pragma unroll
+      for (int j = 0; j < kRowsPerWave; ++j)
+#pragma unroll
+        for (int e = 0; e < E; ++e) st[j][e] = sb[i][j][e];
+      step<DK>(tk, st);  // S_t
+      float dqh[E] = {}, dkh[E] = {};
+      float dal = 0.f, dbe = 0.f;
+#pragma unroll
+      for (int j = 0; j < kRowsPerWave; ++j) {
+        const float dO = ldx(A.dout, (t * A.HV + hv) * (int64_t)A.DV + row0 + j, A.bf16);
+        float pk = 0.f, dk_ = 0.f, ds = 0.f;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          D[j][e] += dO * tk.qh[e];
+          dqh[e] += dO * st[j][e];
+          pk += sb[i][j][e] * tk.kh[e];
+          dk_ += D[j][e] * tk.kh[e];
+          ds += D[j][e] * sb[i][j][e];
+        }
+        const float Spk = wave_sum(pk), Dk = wave_sum(dk_), Ds = wave_sum(ds);
+        if (l == 0) A.dv[(t * A.HV + hv) * (int64_t)A.DV + row0 + j] = tk.beta * Dk;
+        dbe += Dk * (tk.v[j] - tk.alpha * Spk);
+        dal += Ds - tk.beta * Dk * Spk;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          dkh[e] += -tk.alpha * tk.beta * (Spk * D[j][e] + Dk * sb[i][j][e]) +
+                    tk.beta * tk.v[j] * D[j][e];
+          D[j][e] = tk.alpha * (D[j][e] - tk.beta * Dk * tk.kh[e]);
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        part[w][i][64 * e + l] = dqh[e];
+        part[w][i][DK + 64 * e + l] = dkh[e];
+      }
+      if (l == 0) {
+        part[w][i][2 * DK] = dal;
+        part[w][i][2 * DK + 1] = dbe;
+      }
+    }
+    __syncthreads();
+    // this row block's partial sums for the sub-chunk's tokens
+    const int nt = (int)(u_hi - u_lo);
+    for (int idx = tid; idx < nt * NF; idx += 256) {
+      const int i = idx / NF, f = idx % NF;
+      const float v = part[0][i][f] + part[1][i][f] + part[2][i][f] + part[3][i][f];
+      A.part[(((int64_t)rb * A.N + t0 + u_lo + i) * A.HV + hv) * NF + f] = v;
+    }
+    __syncthreads();
+  }
+  // gradient of the request's initial state
+#pragma unroll
+  for (int j = 0; j < kRowsPerWave; ++j)
+#pragma unroll
+    for (int e = 0; e < E; ++e) DS0[((int64_t)(row0 + j)) * DK + 64 * e + l] = D[j][e];
+}
+
+// One wave per (token, q/k head).
+template <int DK>
+__global__ __launch_bounds__(256) void bwd_finish_kernel(BwdArgs A) {
+  constexpr int E = DK / 64;
+  constexpr int NF = 2 * DK + 2;
+  const int l = threadIdx.x & 63;
+  const int64_t wid = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (wid >= A.N * A.H) return;
+  const int64_t t = wid / A.H;
+  const int h = (int)(wid % A.H);
+  const int grp = A.HV / A.H, nrb = A.DV / kBwdRows;
+  float dqh[E] = {}, dkh[E] = {};
+  for (int j = 0; j < grp; ++j) {
+    const int hv = h * grp + j;
+    float dal = 0.f, dbe = 0.f;
+    for (int rb = 0; rb < nrb; ++rb) {
+      const float* P = A.part + (((int64_t)rb * A.N + t) * A.HV + hv) * NF;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        dqh[e] += P[64 * e + l];
+        dkh[e] += P[DK + 64 * e + l];
+      }
+      dal += P[2 * DK];
+      dbe += P[2 * DK + 1];
+    }
+    if (l == 0) {
+      const float xg = A.a[t * A.HV + hv] + A.dt_bias[hv];
+      const float Aexp = expf(A.A_log[hv]);
+      const float sp = softplusf(xg);
+      const float alpha = expf(-Aexp * sp);
+      const float beta = sigmoidf(A.b[t * A.HV + hv]);
+      A.da[t * A.HV + hv] = dal * (-alpha * Aexp * sigmoidf(xg));
+      A.dal[t * A.HV + hv] = dal * (-alpha * Aexp * sp);
+      A.db[t * A.HV + hv] = dbe * beta * (1.f - beta);
+    }
+  }
+  // L2 norm: d(x / n)/dx applied to the summed gradient of the normalised vector
+  float qe[E], ke[E], sq = 0.f, sk = 0.f, qd = 0.f, kd = 0.f;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    qe[e] = ldx(A.q, (t * A.H + h) * DK + 64 * e + l, A.bf16);
+    ke[e] = ldx(A.k, (t * A.H + h) * DK + 64 * e + l, A.bf16);
+    sq += qe[e] * qe[e];
+    sk += ke[e] * ke[e];
+    qd += qe[e] * dqh[e];
+    kd += ke[e] * dkh[e];
+  }
+  const float nq = sqrtf(wave_sum(sq) + A.eps), nk = sqrtf(wave_sum(sk) + A.eps);
+  qd = wave_sum(qd);
+  kd = wave_sum(kd);
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    A.dq[(t * A.H + h) * DK + 64 * e + l] = dqh[e] / nq - qe[e] * qd / (nq * nq * nq);
+    A.dk[(t * A.H + h) * DK + 64 * e + l] = dkh[e] / nk - ke[e] * kd / (nk * nk * nk);
+  }
+}
+
+// One workgroup per value head: sums over every token, in a fixed order.
+__global__ __launch_bounds__(256) void bwd_gates_kernel(BwdArgs A) {
+  __shared__ float s1[256], s2[256];
+  const int hv = blockIdx.x, tid = threadIdx.x;
+  float x1 = 0.f, x2 = 0.f;
+  for (int64_t t = tid; t < A.N; t += 256) {
+    x1 += A.da[t * A.HV + hv];
+    x2 += A.dal[t * A.HV + hv];
+  }
+  s1[tid] = x1;
+  s2[tid] = x2;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if (tid < o) {
+      s1[tid] += s1[tid + o];
+      s2[tid] += s2[tid + o];
+    }
+    __syncthreads();
+  }
+  if (tid == 0) {
+    A.ddt_bias[hv] = s1[0];
+    A.dA_log[hv] = s2[0];
+  }
+}
+
+}  // namespace
+
+BwdLayout bwd_layout_for(const Shape& s) {
+  BwdLayout L;
+  L.max_chunks = s.N / kCk + s.B;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = (off + bytes + 255) & ~(size_t)255;
+    return at;
+  };
+  L.chunk_off = take(sizeof(int32_t) * (size_t)(s.B + 1));
+  L.chunk_seq = take(sizeof(int32_t) * (size_t)L.max_chunks);
+  L.ck = take(sizeof(float) * (size_t)L.max_chunks * s.HV * s.dv * s.dk);
+  L.part = take(sizeof(float) * (size_t)(s.dv / kBwdRows) * s.N * s.HV * (2 * s.dk + 2));
+  L.dal = take(sizeof(float) * (size_t)s.N * s.HV);
+  L.total = off;
+  return L;
+}
+
+bool bwd_grids_fit(const Shape& s) {
+  const int64_t rows = s.B * s.HV * (s.dv / kBwdRows);
+  const int64_t fin = (s.N * s.H + 3) / 4;
+  return rows * 256 <= 0xFFFFFFFFLL && fin * 256 <= 0xFFFFFFFFLL && s.HV <= 0x7FFFFFFF;
+}
+
+hipError_t launch_backward(const Shape& s, const BwdLayout& L, char* ws, const void* q,
+                           const void* k, const void* v, const float* a, const float* b,
+                           const float* A_log, const float* dt_bias, const float* state_pool,
+                           const int64_t* cache_indices, const int64_t* cu_seqlens,
+                           const void* dout, const float* dstate, float* dq, float* dk,
+                           float* dv, float* da, float* db, float* dA_log, float* ddt_bias,
+                           float* dstate0, hipStream_t st) {
+  int32_t* chunk_off = (int32_t*)(ws + L.chunk_off);
+  Shape sp = s;
+  sp.C = kCk;
+  hipError_t e = launch_plan(cu_seqlens, sp, chunk_off, (int32_t*)(ws + L.chunk_seq),
+                             L.max_chunks, st);
+  if (e != hipSuccess) return e;
+  BwdArgs A;
+  A.q = q;
+  A.k = k;
+  A.v = v;
+  A.dout = dout;
+  A.a = a;
+  A.b = b;
+  A.A_log = A_log;
+  A.dt_bias = dt_bias;
+  A.state_pool = state_pool;
+  A.dstate = dstate;
+  A.cu = cu_seqlens;
+  A.cache_indices = cache_indices;
+  A.chunk_off = chunk_off;
+  A.dq = dq;
+  A.dk = dk;
+  A.dv = dv;
+  A.da = da;
+  A.db = db;
+  A.dA_log = dA_log;
+  A.ddt_bias = ddt_bias;
+  A.dstate0 = dstate0;
+  A.ck = (float*)(ws + L.ck);
+  A.part = (float*)(ws + L.part);
+  A.dal = (float*)(ws + L.dal);
+  A.N = s.N;
+  A.B = (int)s.B;
+  A.H = s.H;
+  A.HV = s.HV;
+  A.DV = s.dv;
+  A.eps = kNormEps;
+  A.bf16 = s.bf16 ? 1 : 0;
+  const dim3 rows((unsigned)(s.B * s.HV * (s.dv / kBwdRows))), fin((unsigned)((s.N * s.H + 3) / 4));
+#define GDN_BWD_CASE(DKv)                                                              \
+  if (s.dk == DKv) {                                                                   \
+    hipLaunchKernelGGL((bwd_rows_kernel<DKv>), rows, dim3(256), 0, st, A);             \
+    if ((e = hipGetLastError()) != hipSuccess) return e;                               \
+    if (s.N > 0) hipLaunchKernelGGL((bwd_finish_kernel<DKv>), fin, dim3(256), 0, st, A); \
+  }
+  GDN_BWD_CASE(64)
+  GDN_BWD_CASE(128)
+  GDN_BWD_CASE(256)
+#undef GDN_BWD_CASE
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(bwd_gates_kernel, dim3((unsigned)s.HV), dim3(256), 0, st, A);
+  return hipGetLastError();
+}
+
+}  // namespace gdn

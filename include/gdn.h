@@ -180,6 +180,36 @@ gdn_status_t gdn_prefill_fwd_events(const void* q, const void* k, const void* v,
                                     size_t workspace_bytes, void* stream,
                                     void* const* stage_events);
 
+/* Backward of the prefill forward: gradients of every input of a gdn_prefill_fwd call,
+ * given the gradients of its outputs and of each request's final state. For the scalar
+ *   L = sum_{t,hv} <dout[t,hv], out[t,hv]> + sum_{b,hv} <dstate[b,hv], S_b,hv(final)>
+ * it writes dq, dk [N, H, dk], dv [N, HV, dv], da, db [N, HV], dA_log, ddt_bias [HV]
+ * and dstate0 [B, HV, dv, dk] (the gradient of each request's initial state, in request
+ * order), all fp32, DEVICE pointers, fully overwritten. The recurrence at the top of this
+ * file is differentiated token by token (its chunked evaluation is the same map, pymllm
+ * gdn_chunkwise page, Algorithm; awehrs.io "NRM training kernels", Results: the backward
+ * is expensive because of the sequential structure): a forward sweep keeps each state
+ * every chunk_size tokens, the reverse sweep recomputes from those and walks back.
+ * Inputs: q, k, v, a, b, A_log, dt_bias, cache_indices, cu_seqlens and prob as for
+ * gdn_prefill_fwd (q, k, v and dout in qkv_dtype); state_pool holds the INITIAL states
+ * (the pool as it was before the forward call, which updates it in place; read only);
+ * dout [N, HV, dv] in qkv_dtype; dstate [B, HV, dv, dk] fp32 in request order.
+ * chunk_size must be 64. workspace: at least gdn_prefill_bwd_workspace_size bytes,
+ * 256-byte aligned (checkpoints, about N/64 x HV x dv x dk x 4 bytes, and per-token sums
+ * over blocks of 16 state rows, about N x HV x dv x (2 dk + 2) / 4 bytes).
+ * Arithmetic in fp32 throughout (no matrix cores); deterministic. N == 0 writes
+ * dstate0 = dstate and zero dA_log, ddt_bias; B == 0 is a no-op. Errors as for
+ * gdn_prefill_fwd: host checks before any launch. */
+size_t gdn_prefill_bwd_workspace_size(const gdn_problem_t* prob, int32_t chunk_size);
+gdn_status_t gdn_prefill_bwd(const void* q, const void* k, const void* v, const float* a,
+                             const float* b, const float* A_log, const float* dt_bias,
+                             const float* state_pool, const int64_t* cache_indices,
+                             const int64_t* cu_seqlens, int32_t chunk_size, const void* dout,
+                             const float* dstate, float* dq, float* dk, float* dv, float* da,
+                             float* db, float* dA_log, float* ddt_bias, float* dstate0,
+                             const gdn_problem_t* prob, void* workspace, size_t workspace_bytes,
+                             void* stream);
+
 /* One decode step: every request b brings exactly one new token, row b of q, k, v, a, b,
  * and the token's step of the recurrence at the top of this file is applied to
  * S = state_pool[cache_indices[b], hv] in place, with out[b, hv] = S qh read after the

@@ -22,9 +22,11 @@
 // Segments of one request run on different compute units, so the chain each workgroup
 // walks is at most lseg chunks long.
 //
-// Workgroup: four compute waves and one loader wave. Compute wave w holds 32 columns of
-// S^T (state rows of the value head; or columns of P) over all of dk in fp32 registers,
-// as MFMA accumulator tiles, and does every product of its columns itself: nothing is
+// Workgroup: eight compute waves (two per SIMD: one wave alone cannot keep the matrix
+// core or the LDS busy) and one loader wave. In the output pass compute wave w holds 16
+// columns of S^T (state rows of the value head) over all of dk in fp32 registers, as MFMA
+// accumulator tiles; in the operator pass waves 0-3 hold 32 columns of R^T each and waves
+// 4-7 32 columns of P^T. Each wave does every product of its columns itself: nothing is
 // exchanged between compute waves. The operands every column needs (W<-, K~, Qh, A_qk,
 // e^G; and the workgroup's columns of U~) are staged once per workgroup by the loader
 // wave with direct global-to-LDS loads into a ring of two chunk slots, one chunk ahead of
@@ -52,8 +54,7 @@ constexpr int kComputeWaves = 4;
 #define GDN_CHAIN_LOADERS 1
 #endif
 constexpr int kLoaderWaves = GDN_CHAIN_LOADERS;
-constexpr int kColsPerWave = 32;
-constexpr int kColsPerBlock = kComputeWaves * kColsPerWave;  // 128 state columns
+constexpr int kColsPerBlock = 128;  // state columns of one workgroup
 
 typedef __attribute__((address_space(3))) void* lds_ptr;
 
@@ -64,7 +65,10 @@ enum : int { kRoleOut = 0, kRoleR = 1, kRoleP = 2 };
 // starts at the identity and sees U~ = 0; the two share every staged W<- and K~).
 enum : int { kModeOut = 0, kModeOperator = 1 };
 template <int MODE>
-constexpr int kCompute = MODE == kModeOut ? kComputeWaves : 2 * kComputeWaves;
+constexpr int kCompute = 2 * kComputeWaves;  // two compute waves per SIMD
+// 16-column tiles per compute wave: eight waves of 16 columns (out) or of 32 (R, P)
+template <int MODE>
+constexpr int kTiles = MODE == kModeOut ? 1 : 2;
 template <int MODE>
 constexpr int kThreads = 64 * (kCompute<MODE> + kLoaderWaves);
 
@@ -261,13 +265,14 @@ __global__ __launch_bounds__(kThreads<MODE>, 1) void chain_kernel(ChainArgs a) {
   }
 
   // ======================= compute waves =======================
+  constexpr int CT = kTiles<MODE>;
   const int role = MODE == kModeOut ? kRoleOut : (wv < kComputeWaves ? kRoleR : kRoleP);
-  const int wq = wv % kComputeWaves;                // position inside the 128-column block
-  const int col0 = colbase + kColsPerWave * wq;     // first state (or P) column of this wave
+  const int wct = MODE == kModeOut ? wv : CT * (wv % kComputeWaves);  // first column tile
+  const int col0 = colbase + 16 * wct;  // first state (or P) column of this wave
   const bool active = col0 < (role == kRoleP ? DK : a.DV);
   const bool use_u = role != kRoleP;
   // S^T tiles: dk rows 16 dt + 4 g + i, column col0 + 16 ct + m (fp32)
-  f32x4 S[NDT][2];
+  f32x4 S[NDT][CT];
   float* Sinit = nullptr;
   if (role == kRoleOut)
     Sinit = (nseg >= 2) ? a.sstart + ((sg * a.HV + hv) * (int64_t)a.DV + col0) * DK
@@ -275,7 +280,7 @@ __global__ __launch_bounds__(kThreads<MODE>, 1) void chain_kernel(ChainArgs a) {
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-    for (int ct = 0; ct < 2; ++ct) {
+    for (int ct = 0; ct < CT; ++ct) {
       if (role == kRoleOut && active) {
         S[dt][ct] = *reinterpret_cast<const f32x4*>(Sinit + (16 * ct + m) * DK + 16 * dt + 4 * g);
       } else if (role == kRoleP) {
@@ -287,7 +292,6 @@ __global__ __launch_bounds__(kThreads<MODE>, 1) void chain_kernel(ChainArgs a) {
         S[dt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
     }
-  const int wct = 2 * wq;  // this wave's first column tile inside the block
 
   // One chunk is a fixed sequence of NF fragment steps; each step reads one operand
   // fragment from the slot and issues the two MFMAs (one per column tile) that use it:
@@ -327,18 +331,18 @@ __global__ __launch_bounds__(kThreads<MODE>, 1) void chain_kernel(ChainArgs a) {
     half8 ring[RING];
     static_for<RING>([&](auto I) { ring[decltype(I)::value] = *frag(s, I); });
     // ---- fp16 copy of S^T: B operand (k = dk) of W<- S^T and A operand of S Qh^T
-    half8 s16[NKS][2];
+    half8 s16[NKS][CT];
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
-      for (int ct = 0; ct < 2; ++ct)
+      for (int ct = 0; ct < CT; ++ct)
         s16[ks][ct] = cat(to_half4(S[2 * ks][ct]), to_half4(S[2 * ks + 1][ct]));
     // ---- -U = W<- S^T - U~, accumulated from -U~ (token tile tt, column tile ct)
-    f32x4 nu[4][2];
+    f32x4 nu[4][CT];
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
-      for (int ct = 0; ct < 2; ++ct) {
+      for (int ct = 0; ct < CT; ++ct) {
         if (use_u) {
           const u32x2 ur = *reinterpret_cast<const u32x2*>(
               reinterpret_cast<const _Float16*>(&s.u[0][0]) + (((wct + ct) * 4 + tt) * 64 + l) * 4);
@@ -348,8 +352,8 @@ __global__ __launch_bounds__(kThreads<MODE>, 1) void chain_kernel(ChainArgs a) {
           nu[tt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
       }
-    half8 u16[2][2];          // U in fp16, tokens 32 ts + kperm (B of the update, A of O2)
-    f32x4 o[4][2];            // O^T tiles (column tile ct, token tile tt)
+    half8 u16[2][CT];          // U in fp16, tokens 32 ts + kperm (B of the update, A of O2)
+    f32x4 o[4][CT];            // O^T tiles (column tile ct, token tile tt)
     const int64_t t0 = tseq + (int64_t)cl * C;
     const int nrow = (int)min((int64_t)C, tend - t0);
     static_for<NF>([&](auto I) {
@@ -360,7 +364,7 @@ __global__ __launch_bounds__(kThreads<MODE>, 1) void chain_kernel(ChainArgs a) {
 #pragma unroll
         for (int ts = 0; ts < 2; ++ts)
 #pragma unroll
-          for (int ct = 0; ct < 2; ++ct)
+          for (int ct = 0; ct < CT; ++ct)
             u16[ts][ct] = cat(to_half4(-nu[2 * ts][ct]), to_half4(-nu[2 * ts + 1][ct]));
         if constexpr (MODE == kModeOut) {
           // O1 rows scaled by e^G before A_qk U is added
@@ -368,7 +372,7 @@ __global__ __launch_bounds__(kThreads<MODE>, 1) void chain_kernel(ChainArgs a) {
           for (int tt = 0; tt < 4; ++tt) {
             const float er = s.eg[16 * tt + m];
 #pragma unroll
-            for (int ct = 0; ct < 2; ++ct) o[tt][ct] *= er;
+            for (int ct = 0; ct < CT; ++ct) o[tt][ct] *= er;
           }
         }
       }
@@ -382,7 +386,7 @@ __global__ __launch_bounds__(kThreads<MODE>, 1) void chain_kernel(ChainArgs a) {
               __bf16* orow = reinterpret_cast<__bf16*>(a.out) +
                              ((t0 + r) * a.HV + hv) * (int64_t)a.DV + col0 + 4 * g;
 #pragma unroll
-              for (int ct = 0; ct < 2; ++ct) {
+              for (int ct = 0; ct < CT; ++ct) {
                 bf16x4 ov;
                 ov[0] = (__bf16)o[tt][ct][0];
                 ov[1] = (__bf16)o[tt][ct][1];
@@ -399,27 +403,27 @@ __global__ __launch_bounds__(kThreads<MODE>, 1) void chain_kernel(ChainArgs a) {
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-          for (int ct = 0; ct < 2; ++ct) S[dt][ct] *= egn;
+          for (int ct = 0; ct < CT; ++ct) S[dt][ct] *= egn;
       }
       const half8 f = ring[i % RING];
       if constexpr (i + RING < NF) ring[i % RING] = *frag(s, std::integral_constant<int, i + RING>{});
       if constexpr (i < P) {
         constexpr int ks = i / 4, tt = i % 4;
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct) nu[tt][ct] = mma_f16(f, s16[ks][ct], nu[tt][ct]);
+        for (int ct = 0; ct < CT; ++ct) nu[tt][ct] = mma_f16(f, s16[ks][ct], nu[tt][ct]);
       } else if constexpr (i < P + O1) {
         constexpr int j2 = i - P, ks = j2 / 4, tt = j2 % 4;
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct)
+        for (int ct = 0; ct < CT; ++ct)
           o[tt][ct] = mma_f16(s16[ks][ct], f, (ks == 0) ? f32x4{0.f, 0.f, 0.f, 0.f} : o[tt][ct]);
       } else if constexpr (i < P + O1 + O2) {
         constexpr int j2 = i - P - O1, fa = j2 < 2 ? 2 * j2 : j2 + 2, tt = fa / 2, st = fa % 2;
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct) o[tt][ct] = mma_f16(u16[st][ct], f, o[tt][ct]);
+        for (int ct = 0; ct < CT; ++ct) o[tt][ct] = mma_f16(u16[st][ct], f, o[tt][ct]);
       } else {
         constexpr int j2 = i - P - O1 - O2, ts = j2 / NDT, dt = j2 % NDT;
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct) S[dt][ct] = mma_f16(f, u16[ts][ct], S[dt][ct]);
+        for (int ct = 0; ct < CT; ++ct) S[dt][ct] = mma_f16(f, u16[ts][ct], S[dt][ct]);
       }
       __builtin_amdgcn_sched_barrier(0);
     });
@@ -433,7 +437,7 @@ __global__ __launch_bounds__(kThreads<MODE>, 1) void chain_kernel(ChainArgs a) {
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-      for (int ct = 0; ct < 2; ++ct)
+      for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
         for (int i = 0; i < 4; ++i) finite = finite && __builtin_isfinite(S[dt][ct][i]);
     if (__ballot(!finite) != 0 && l == 0) *a.nonfinite = 1;
@@ -446,7 +450,7 @@ __global__ __launch_bounds__(kThreads<MODE>, 1) void chain_kernel(ChainArgs a) {
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-    for (int ct = 0; ct < 2; ++ct)
+    for (int ct = 0; ct < CT; ++ct)
       *reinterpret_cast<f32x4*>(dst + (16 * ct + m) * DK + 16 * dt + 4 * g) = S[dt][ct];
 }
 

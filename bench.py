@@ -12,7 +12,8 @@ With ``--op decode`` a step is instead one gdn_decode_fwd call over the decode w
 firings x 64 pairs, dk = dv = 128, bf16, every firing's state kept); with ``--op verify``
 one gdn_recurrent_fwd call over a speculative-verification batch (512 requests x 4 tokens,
 the decode workload's heads and pool), the chunked gdn_prefill_fwd on the same call timed
-beside it. The JSON line then reports that call.
+beside it; with ``--op backward`` one gdn_prefill_bwd call on the dense-batch workload. The
+JSON line then reports that call.
 """
 from __future__ import annotations
 
@@ -873,9 +874,121 @@ def bench_prefill(args):
     print(json.dumps(res), flush=True)
 
 
+BACKWARD_METRIC = "GDN prefill backward tokens/sec (every input's gradient), dk=dv=128 C=64"
+
+
+def backward_bytes(p, s_qkv: int) -> int:
+    """Algorithmic HBM bytes of one backward call: q, k, v, dout read and dq, dk, dv written
+    (fp32); a, b read and da, db written; the initial and final-state gradients and the
+    initial states read, the initial-state gradients written (fp32)."""
+    return (p.N * (2 * p.H * p.dk * s_qkv + 2 * p.HV * p.dv * s_qkv + 8 * p.HV)
+            + p.N * (2 * p.H * p.dk + p.HV * p.dv + 2 * p.HV) * 4
+            + 3 * p.B * p.HV * p.dv * p.dk * 4)
+
+
+def backward_cpu_baseline(p, heads, reps: int = 1):
+    """The backward oracle (fp64 numpy reverse mode) as it stands, on a sample of value
+    heads; tokens/s scaled to every head."""
+    import numpy as np
+    from oracle import backward as bw
+    sub = dataclasses_replace_heads(p, heads)
+    rng = np.random.default_rng(5)
+    dout = rng.standard_normal((sub.N, sub.HV, sub.dv))
+    dstate = rng.standard_normal((sub.B, sub.HV, sub.dv, sub.dk))
+    walls = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        bw.prefill_backward(sub, dout, dstate)
+        walls.append(time.perf_counter() - t0)
+    dt = float(np.median(walls)) * p.HV / len(heads)
+    return {"value": p.N / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"value heads {list(heads)} of {p.HV} over all {p.N} tokens (time scaled "
+                      f"by {p.HV}/{len(heads)}), fp64 numpy reverse mode, one thread"}
+
+
+def dataclasses_replace_heads(p, heads):
+    """The workload restricted to the given value heads (with their q/k heads kept whole)."""
+    import copy
+    import numpy as np
+    q = copy.copy(p)
+    hv = np.asarray(heads)
+    grp = p.HV // p.H
+    hs = sorted(set(int(h) // grp for h in hv))
+    assert len(hs) == 1 and len(hv) <= grp, "sample the value heads of one q/k head"
+    q.q, q.k = p.q[:, hs], p.k[:, hs]
+    q.v, q.a, q.b = p.v[:, hv], p.a[:, hv], p.b[:, hv]
+    q.A_log, q.dt_bias = p.A_log[hv], p.dt_bias[hv]
+    q.state_pool = p.state_pool[:, hv]
+    q.H, q.HV = 1, len(hv)
+    return q
+
+
+def bench_backward(args):
+    import numpy as np
+    import torch
+
+    import gdn_synth
+    import gated_deltanet_prefill_gdn_amd as gdn
+
+    p = gdn_synth.workload(WORKLOAD_INDEX)
+    dev = torch.device("cuda:0")
+
+    def t(x, dt=None):
+        x = torch.from_numpy(np.ascontiguousarray(x))
+        return (x.view(dt) if dt is not None else x).to(dev)
+
+    q = t(p.q.view(np.int16), torch.bfloat16)
+    k = t(p.k.view(np.int16), torch.bfloat16)
+    v = t(p.v.view(np.int16), torch.bfloat16)
+    a, b, A_log, dt_bias = t(p.a), t(p.b), t(p.A_log), t(p.dt_bias)
+    pool = t(p.state_pool)
+    idx, cu = t(p.cache_indices), t(p.cu_seqlens)
+    g = torch.Generator(device="cpu").manual_seed(5)
+    dout = torch.randn((p.N, p.HV, p.dv), generator=g).to(torch.bfloat16).to(dev)
+    dstate = torch.randn((p.B, p.HV, p.dv, p.dk), generator=g).to(dev)
+    prob = gdn.problem_of(q, k, v, pool, idx)
+    ws = torch.empty(gdn.gdn_prefill_bwd_workspace_size(prob), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        gdn.gdn_prefill_bwd(q, k, v, a, b, A_log, dt_bias, pool, idx, cu, dout, dstate,
+                            workspace=ws, stream=stream)
+
+    ms_per_step, events_ms, pair_ms, launch_ms = _time_launches(step, stream, args.steps,
+                                                                args.warmup)
+    nbytes = backward_bytes(p, 2)
+    res = {
+        "metric": BACKWARD_METRIC,
+        "value": p.N / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 inputs, fp32 arithmetic and gradients",
+        "data": f"synthetic (seeded SplitMix64/Box-Muller, seed {p.seed}; upstream gradients "
+                "torch.randn seed 5)",
+        "config": {"workload": gdn_synth.WORKLOADS[WORKLOAD_INDEX], "global_batch": p.B,
+                   "seq_len": int(p.N // p.B), "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "hbm", "kernel": "gdn_prefill_bwd (all kernels)",
+                     "achieved": nbytes / (launch_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": nbytes / (launch_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                     "traffic": None, "algorithmic_bytes_per_launch": nbytes,
+                     "avg_launch_ms": launch_ms, "avg_launch_ms_events": events_ms,
+                     "event_pair_ms": pair_ms},
+        "kernel_source_hash": kernel_source_hash(),
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = backward_cpu_baseline(p, heads=[0])
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
-    ap.add_argument("--op", choices=("prefill", "decode", "promote", "verify"),
+    ap.add_argument("--op", choices=("prefill", "decode", "promote", "verify", "backward"),
                     default="prefill",
                     help="the call a step times (default: the prefill forward)")
     ap.add_argument("--gpus", type=int, default=1)
@@ -904,6 +1017,9 @@ def main():
         return
     if args.op == "verify":
         bench_verify(args)
+        return
+    if args.op == "backward":
+        bench_backward(args)
         return
 
     bench_prefill(args)

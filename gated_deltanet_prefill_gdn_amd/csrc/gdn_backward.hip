@@ -17,7 +17,7 @@
 //
 // Kernels (fp32 arithmetic throughout):
 //   rows    one workgroup per (request, value head, 16 rows). A forward sweep keeps the
-//           rows' state every 64 tokens; the reverse sweep recomputes 16 tokens at a time
+//           rows' state every 16 tokens; the reverse sweep recomputes 16 tokens at a time
 //           from the checkpoint before them, holds those 16 states in registers, and
 //           walks them backwards. Wave w holds rows 4w .. 4w+3, lane l the dk elements
 //           l + 64 e. Row dot products are wave sums; the per-token sums over the 16 rows
@@ -35,7 +35,7 @@
 namespace gdn {
 namespace {
 
-constexpr int kCk = 64;            // tokens between checkpoints
+constexpr int kCk = 16;            // tokens between checkpoints
 constexpr int kBwdRows = 16;       // state rows per workgroup
 constexpr int kRowsPerWave = 4;
 template <int DK>
@@ -46,10 +46,26 @@ __device__ __forceinline__ float ldx(const void* p, int64_t i, bool bf16) {
               : reinterpret_cast<const float*>(p)[i];
 }
 
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over the wave, in every lane, without LDS: four DPP steps reduce each row of 16 lanes
+// (quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror, row_mirror), then gfx950's
+// permlane16/permlane32 swaps add row pairs and the wave's halves. Each swap exchanges two
+// disjoint lane sets, so the sum of its two results is the same whichever result is which.
 __device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
-  return x;
+  x += dpp<0xB1>(x);
+  x += dpp<0x4E>(x);
+  x += dpp<0x141>(x);
+  x += dpp<0x140>(x);
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  const auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(h[0]) + __uint_as_float(h[1]);
 }
 
 __device__ __forceinline__ float softplusf(float x) {
@@ -82,31 +98,52 @@ struct Token {
   float v[kRowsPerWave];
 };
 
+// A token's raw inputs for this lane: fetched one token ahead of their use, so the loads
+// of token t + 1 are in flight while token t is processed.
 template <int DK>
-__device__ __forceinline__ void load_token(const BwdArgs& A, int64_t t, int h, int hv, int row0,
-                                           int l, Token<DK>& x) {
+struct Raw {
+  float q[DK / 64], k[DK / 64];
+  float v[kRowsPerWave];
+  float a, b;
+};
+
+template <int DK>
+__device__ __forceinline__ void fetch(const BwdArgs& A, int64_t t, int h, int hv, int row0, int l,
+                                      Raw<DK>& r) {
   constexpr int E = DK / 64;
-  float qe[E], ke[E], sq = 0.f, sk = 0.f;
 #pragma unroll
   for (int e = 0; e < E; ++e) {
-    qe[e] = ldx(A.q, (t * A.H + h) * DK + 64 * e + l, A.bf16);
-    ke[e] = ldx(A.k, (t * A.H + h) * DK + 64 * e + l, A.bf16);
-    sq += qe[e] * qe[e];
-    sk += ke[e] * ke[e];
+    r.q[e] = ldx(A.q, (t * A.H + h) * DK + 64 * e + l, A.bf16);
+    r.k[e] = ldx(A.k, (t * A.H + h) * DK + 64 * e + l, A.bf16);
+  }
+#pragma unroll
+  for (int j = 0; j < kRowsPerWave; ++j)
+    r.v[j] = ldx(A.v, (t * A.HV + hv) * (int64_t)A.DV + row0 + j, A.bf16);
+  r.a = A.a[t * A.HV + hv];
+  r.b = A.b[t * A.HV + hv];
+}
+
+template <int DK>
+__device__ __forceinline__ void finish(const BwdArgs& A, int hv, const Raw<DK>& r, Token<DK>& x) {
+  constexpr int E = DK / 64;
+  float sq = 0.f, sk = 0.f;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    sq += r.q[e] * r.q[e];
+    sk += r.k[e] * r.k[e];
   }
   const float rq = 1.f / sqrtf(wave_sum(sq) + A.eps);
   const float rk = 1.f / sqrtf(wave_sum(sk) + A.eps);
 #pragma unroll
   for (int e = 0; e < E; ++e) {
-    x.qh[e] = qe[e] * rq;
-    x.kh[e] = ke[e] * rk;
+    x.qh[e] = r.q[e] * rq;
+    x.kh[e] = r.k[e] * rk;
   }
-  const float xg = A.a[t * A.HV + hv] + A.dt_bias[hv];
+  const float xg = r.a + A.dt_bias[hv];
   x.alpha = expf(-expf(A.A_log[hv]) * softplusf(xg));
-  x.beta = sigmoidf(A.b[t * A.HV + hv]);
+  x.beta = sigmoidf(r.b);
 #pragma unroll
-  for (int j = 0; j < kRowsPerWave; ++j)
-    x.v[j] = ldx(A.v, (t * A.HV + hv) * (int64_t)A.DV + row0 + j, A.bf16);
+  for (int j = 0; j < kRowsPerWave; ++j) x.v[j] = r.v[j];
 }
 
 // One token's step on this wave's rows: s <- alpha s - alpha beta (s kh) kh + beta v kh.
@@ -157,6 +194,8 @@ __global__ __launch_bounds__(256) void bwd_rows_kernel(BwdArgs A) {
   for (int j = 0; j < kRowsPerWave; ++j)
 #pragma unroll
     for (int e = 0; e < E; ++e) s[j][e] = state_at(S0, j, e);
+  Raw<DK> raw, nxt;
+  if (L > 0) fetch<DK>(A, t0, h, hv, row0, l, raw);
   for (int64_t t = 0; t < L; ++t) {
     if (t % kCk == 0) {
       float* c = ck_at(t / kCk);
@@ -165,9 +204,11 @@ __global__ __launch_bounds__(256) void bwd_rows_kernel(BwdArgs A) {
 #pragma unroll
         for (int e = 0; e < E; ++e) c[((int64_t)(row0 + j)) * DK + 64 * e + l] = s[j][e];
     }
+    fetch<DK>(A, t0 + min(t + 1, L - 1), h, hv, row0, l, nxt);  // the last token again at the end
     Token<DK> tk;
-    load_token<DK>(A, t0 + t, h, hv, row0, l, tk);
+    finish<DK>(A, hv, raw, tk);
     step<DK>(tk, s);
+    raw = nxt;
   }
   // the checkpoints are read back by the same lanes that wrote them: no barrier needed
 
@@ -187,10 +228,13 @@ __global__ __launch_bounds__(256) void bwd_rows_kernel(BwdArgs A) {
     for (int j = 0; j < kRowsPerWave; ++j)
 #pragma unroll
       for (int e = 0; e < E; ++e) s[j][e] = cp[((int64_t)(row0 + j)) * DK + 64 * e + l];
+    fetch<DK>(A, t0 + c * kCk, h, hv, row0, l, raw);
     for (int64_t t = c * kCk; t < u_lo; ++t) {
+      fetch<DK>(A, t0 + t + 1, h, hv, row0, l, nxt);  // t + 1 <= u_lo < L
       Token<DK> tk;
-      load_token<DK>(A, t0 + t, h, hv, row0, l, tk);
+      finish<DK>(A, hv, raw, tk);
       step<DK>(tk, s);
+      raw = nxt;
     }
     float sb[SUB][kRowsPerWave][E];  // S_{t-1} for the sub-chunk's tokens
 #pragma clang loop unroll(full)
@@ -200,17 +244,30 @@ __global__ __launch_bounds__(256) void bwd_rows_kernel(BwdArgs A) {
         for (int j = 0; j < kRowsPerWave; ++j)
 #pragma unroll
           for (int e = 0; e < E; ++e) sb[i][j][e] = s[j][e];
+        fetch<DK>(A, t0 + min(u_lo + i + 1, u_hi - 1), h, hv, row0, l, nxt);
         Token<DK> tk;
-        load_token<DK>(A, t0 + u_lo + i, h, hv, row0, l, tk);
+        finish<DK>(A, hv, raw, tk);
         step<DK>(tk, s);
+        raw = nxt;
       }
     }
+    // the sub-chunk's last token, then each step fetches the one before it
+    fetch<DK>(A, t0 + u_hi - 1, h, hv, row0, l, raw);
+    float dO[kRowsPerWave], dOn[kRowsPerWave];
+#pragma unroll
+    for (int j = 0; j < kRowsPerWave; ++j)
+      dO[j] = ldx(A.dout, ((t0 + u_hi - 1) * A.HV + hv) * (int64_t)A.DV + row0 + j, A.bf16);
 #pragma clang loop unroll(full)
     for (int i = SUB - 1; i >= 0; --i) {
       if (u_lo + i >= u_hi) continue;  // past the request's end (uniform)
       const int64_t t = t0 + u_lo + i;
+      const int64_t tp = t0 + u_lo + max(i - 1, 0);
+      fetch<DK>(A, tp, h, hv, row0, l, nxt);
+#pragma unroll
+      for (int j = 0; j < kRowsPerWave; ++j)
+        dOn[j] = ldx(A.dout, (tp * A.HV + hv) * (int64_t)A.DV + row0 + j, A.bf16);
       Token<DK> tk;
-      load_token<DK>(A, t, h, hv, row0, l, tk);
+      finish<DK>(A, hv, raw, tk);
       float st[kRowsPerWave][E];
 #pragma unroll
       for (int j = 0; j < kRowsPerWave; ++j)
@@ -221,12 +278,11 @@ __global__ __launch_bounds__(256) void bwd_rows_kernel(BwdArgs A) {
       float dal = 0.f, dbe = 0.f;
 #pragma unroll
       for (int j = 0; j < kRowsPerWave; ++j) {
-        const float dO = ldx(A.dout, (t * A.HV + hv) * (int64_t)A.DV + row0 + j, A.bf16);
         float pk = 0.f, dk_ = 0.f, ds = 0.f;
 #pragma unroll
         for (int e = 0; e < E; ++e) {
-          D[j][e] += dO * tk.qh[e];
-          dqh[e] += dO * st[j][e];
+          D[j][e] += dO[j] * tk.qh[e];
+          dqh[e] += dO[j] * st[j][e];
           pk += sb[i][j][e] * tk.kh[e];
           dk_ += D[j][e] * tk.kh[e];
           ds += D[j][e] * sb[i][j][e];
@@ -251,6 +307,9 @@ __global__ __launch_bounds__(256) void bwd_rows_kernel(BwdArgs A) {
         part[w][i][2 * DK] = dal;
         part[w][i][2 * DK + 1] = dbe;
       }
+      raw = nxt;
+#pragma unroll
+      for (int j = 0; j < kRowsPerWave; ++j) dO[j] = dOn[j];
     }
     __syncthreads();
     // this row block's partial sums for the sub-chunk's tokens

@@ -956,6 +956,13 @@ def bench_backward(args):
 
     ms_per_step, events_ms, pair_ms, launch_ms = _time_launches(step, stream, args.steps,
                                                                 args.warmup)
+    if args.copy_calibration:
+        src = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev).fill_(3)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     nbytes = backward_bytes(p, 2)
     res = {
         "metric": BACKWARD_METRIC,

@@ -80,9 +80,11 @@ static bool prefill_grids_fit(const Shape& s, Path path, int64_t max_chunks) {
       if (!grid_fits(chain_grid(s, cp, stage), chain_threads(stage))) return false;
     return true;
   }
-  // column-slice state kernel: (request, value head) pairs rounded up to 8, times dv / 32,
-  // workgroups of five waves (the prep kernel's grid is the device's resident capacity)
-  return grid_fits((s.B * s.HV + 7) / 8 * 8 * (s.dv / 32), 64 * 5);
+  // column-slice state kernel: (request, value head) pairs rounded up to 8, times dv / 32
+  // slices (dv / 16 where those would not fill the device), workgroups of five waves (the
+  // prep kernel's grid is the device's resident capacity)
+  const int64_t slices = s.B * s.HV * (s.dv / 32) < 256 ? s.dv / 16 : s.dv / 32;
+  return grid_fits((s.B * s.HV + 7) / 8 * 8 * slices, 64 * 5);
 }
 
 // Descriptor checks shared by every entry point. Host only.

@@ -420,13 +420,21 @@ hipError_t launch_mfma_state(const void* qf, const void* kf, const int64_t* cu_s
                              int32_t* nonfinite, hipStream_t st) {
   const _Float16* W = (const _Float16*)w;
   const _Float16* U = (const _Float16*)u;
-  // Two column tiles (32 state rows) per workgroup; dv is a multiple of 32. Loads run
-  // two chunks ahead, one at dk = 256, where two register sets would not fit.
-#define GDN_STATE_CASE(DKv, PDv)                                                               \
-  if (s.dk == DKv)                                                                             \
-    return launch_state_t<DKv, 2, PDv>(qf, kf, cu_seqlens, cache_indices, chunk_off, W, U,    \
-                                       (const _Float16*)aqk, eg, s, state_pool, out, nonfinite, \
-                                       st);
+  // Two column tiles (32 state rows) per workgroup where those workgroups fill the device;
+  // otherwise one (16 rows), which doubles the workgroups walking the chains (measured at
+  // dk = dv = 256 on one request of 8 heads: 533 -> 442 us). dv is a multiple of 32. Loads
+  // run two chunks ahead, one at dk = 256, where two register sets would not fit.
+  const bool narrow = s.B * s.HV * (s.dv / 32) < 256;
+#define GDN_STATE_CASE(DKv, PDv)                                                           \
+  if (s.dk == DKv) {                                                                       \
+    if (narrow)                                                                            \
+      return launch_state_t<DKv, 1, PDv>(qf, kf, cu_seqlens, cache_indices, chunk_off, W, U, \
+                                         (const _Float16*)aqk, eg, s, state_pool, out,       \
+                                         nonfinite, st);                                     \
+    return launch_state_t<DKv, 2, PDv>(qf, kf, cu_seqlens, cache_indices, chunk_off, W, U,   \
+                                       (const _Float16*)aqk, eg, s, state_pool, out,         \
+                                       nonfinite, st);                                       \
+  }
   GDN_STATE_CASE(64, 2)
   GDN_STATE_CASE(128, 2)
   GDN_STATE_CASE(256, 1)

@@ -16,13 +16,17 @@
 // The rows of S and D are independent; only dqh, dkh, dalpha and dbeta sum over rows.
 //
 // Kernels (fp32 arithmetic throughout):
+//   token   one wave per (token, q/k head): the normalised q and k rows and, for the value
+//           heads sharing them, alpha and beta, written once so that the sweeps below only
+//           load them.
 //   rows    one workgroup per (request, value head, 16 rows). A forward sweep keeps the
 //           rows' state every 16 tokens; the reverse sweep recomputes 16 tokens at a time
-//           from the checkpoint before them, holds those 16 states in registers, and
-//           walks them backwards. Wave w holds rows 4w .. 4w+3, lane l the dk elements
-//           l + 64 e. Row dot products are wave sums; the per-token sums over the 16 rows
-//           go through LDS into a partial buffer per row block (no atomics: the result
-//           does not depend on scheduling).
+//           from the checkpoint before them, holds the states before each of them in
+//           registers (the state after token i is the one before token i + 1, or the
+//           sub-chunk's end state), and walks them backwards. Wave w holds rows 4w .. 4w+3,
+//           lane l the dk elements l + 64 e. Row dot products are wave sums; the per-token
+//           sums over the 16 rows go through LDS into a partial buffer per row block (no
+//           atomics: the result does not depend on scheduling).
 //   finish  one wave per (token, q/k head): sums the partials over row blocks and over
 //           the value heads that share the q/k head, then the chain rule through the L2
 //           norm (dq = dqh / n - q (q . dqh) / n^3) and the gates (da = dalpha dalpha/dx,
@@ -44,6 +48,23 @@ constexpr int kSub = DK <= 128 ? 16 : 8;  // tokens recomputed and walked back a
 __device__ __forceinline__ float ldx(const void* p, int64_t i, bool bf16) {
   return bf16 ? __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(p)[i] << 16)
               : reinterpret_cast<const float*>(p)[i];
+}
+
+// Four consecutive elements starting at a multiple of 4 (8- or 16-byte aligned).
+__device__ __forceinline__ void ld4(const void* p, int64_t i, bool bf16, float (&x)[4]) {
+  if (bf16) {
+    const uint2 u = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(p) + i);
+    x[0] = __uint_as_float(u.x << 16);
+    x[1] = __uint_as_float(u.x & 0xFFFF0000u);
+    x[2] = __uint_as_float(u.y << 16);
+    x[3] = __uint_as_float(u.y & 0xFFFF0000u);
+  } else {
+    const float4 f = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(p) + i);
+    x[0] = f.x;
+    x[1] = f.y;
+    x[2] = f.z;
+    x[3] = f.w;
+  }
 }
 
 template <int CTRL>
@@ -85,11 +106,48 @@ struct BwdArgs {
   float* ck;      // [chunk][HV][dv][dk]: state before the chunk's first token
   float* part;    // [dv / 16][N][HV][2 dk + 2]: dqh, dkh, dalpha, dbeta per row block
   float* dal;     // [N][HV]: dalpha * dalpha/dA_log per token
+  float* qn;      // [N][H][dk]: q / |q|
+  float* kn;      // [N][H][dk]: k / |k|
+  float* ab;      // [N][HV][2]: alpha, beta
   int64_t N;
   int B, H, HV, DV;
   float eps;
   int bf16;
 };
+
+// One wave per (token, q/k head).
+template <int DK>
+__global__ __launch_bounds__(256) void bwd_token_kernel(BwdArgs A) {
+  constexpr int E = DK / 64;
+  const int l = threadIdx.x & 63;
+  const int64_t wid = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (wid >= A.N * A.H) return;
+  const int64_t t = wid / A.H;
+  const int h = (int)(wid % A.H);
+  float qe[E], ke[E], sq = 0.f, sk = 0.f;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    qe[e] = ldx(A.q, (t * A.H + h) * DK + 64 * e + l, A.bf16);
+    ke[e] = ldx(A.k, (t * A.H + h) * DK + 64 * e + l, A.bf16);
+    sq += qe[e] * qe[e];
+    sk += ke[e] * ke[e];
+  }
+  const float rq = 1.f / sqrtf(wave_sum(sq) + A.eps), rk = 1.f / sqrtf(wave_sum(sk) + A.eps);
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    A.qn[(t * A.H + h) * DK + 64 * e + l] = qe[e] * rq;
+    A.kn[(t * A.H + h) * DK + 64 * e + l] = ke[e] * rk;
+  }
+  const int grp = A.HV / A.H;
+  for (int j = l; j < grp; j += 64) {
+    const int hv = h * grp + j;
+    const float xg = A.a[t * A.HV + hv] + A.dt_bias[hv];
+    float2 ab;
+    ab.x = expf(-expf(A.A_log[hv]) * softplusf(xg));
+    ab.y = sigmoidf(A.b[t * A.HV + hv]);
+    *reinterpret_cast<float2*>(A.ab + (t * A.HV + hv) * 2) = ab;
+  }
+}
 
 template <int DK>
 struct Token {
@@ -98,52 +156,22 @@ struct Token {
   float v[kRowsPerWave];
 };
 
-// A token's raw inputs for this lane: fetched one token ahead of their use, so the loads
-// of token t + 1 are in flight while token t is processed.
-template <int DK>
-struct Raw {
-  float q[DK / 64], k[DK / 64];
-  float v[kRowsPerWave];
-  float a, b;
-};
-
+// Token t's inputs for this lane's elements and this wave's rows (all precomputed).
 template <int DK>
 __device__ __forceinline__ void fetch(const BwdArgs& A, int64_t t, int h, int hv, int row0, int l,
-                                      Raw<DK>& r) {
+                                      Token<DK>& x) {
   constexpr int E = DK / 64;
+  const float* qp = A.qn + (t * A.H + h) * DK + l;
+  const float* kp = A.kn + (t * A.H + h) * DK + l;
 #pragma unroll
   for (int e = 0; e < E; ++e) {
-    r.q[e] = ldx(A.q, (t * A.H + h) * DK + 64 * e + l, A.bf16);
-    r.k[e] = ldx(A.k, (t * A.H + h) * DK + 64 * e + l, A.bf16);
+    x.qh[e] = qp[64 * e];
+    x.kh[e] = kp[64 * e];
   }
-#pragma unroll
-  for (int j = 0; j < kRowsPerWave; ++j)
-    r.v[j] = ldx(A.v, (t * A.HV + hv) * (int64_t)A.DV + row0 + j, A.bf16);
-  r.a = A.a[t * A.HV + hv];
-  r.b = A.b[t * A.HV + hv];
-}
-
-template <int DK>
-__device__ __forceinline__ void finish(const BwdArgs& A, int hv, const Raw<DK>& r, Token<DK>& x) {
-  constexpr int E = DK / 64;
-  float sq = 0.f, sk = 0.f;
-#pragma unroll
-  for (int e = 0; e < E; ++e) {
-    sq += r.q[e] * r.q[e];
-    sk += r.k[e] * r.k[e];
-  }
-  const float rq = 1.f / sqrtf(wave_sum(sq) + A.eps);
-  const float rk = 1.f / sqrtf(wave_sum(sk) + A.eps);
-#pragma unroll
-  for (int e = 0; e < E; ++e) {
-    x.qh[e] = r.q[e] * rq;
-    x.kh[e] = r.k[e] * rk;
-  }
-  const float xg = r.a + A.dt_bias[hv];
-  x.alpha = expf(-expf(A.A_log[hv]) * softplusf(xg));
-  x.beta = sigmoidf(r.b);
-#pragma unroll
-  for (int j = 0; j < kRowsPerWave; ++j) x.v[j] = r.v[j];
+  const float2 ab = *reinterpret_cast<const float2*>(A.ab + (t * A.HV + hv) * 2);
+  x.alpha = ab.x;
+  x.beta = ab.y;
+  ld4(A.v, (t * A.HV + hv) * (int64_t)A.DV + row0, A.bf16, x.v);
 }
 
 // One token's step on this wave's rows: s <- alpha s - alpha beta (s kh) kh + beta v kh.
@@ -156,9 +184,9 @@ __device__ __forceinline__ void step(const Token<DK>& x, float (&s)[kRowsPerWave
 #pragma unroll
     for (int e = 0; e < E; ++e) p += s[j][e] * x.kh[e];
     const float sk = wave_sum(p);
+    const float c = x.beta * (x.v[j] - x.alpha * sk);
 #pragma unroll
-    for (int e = 0; e < E; ++e)
-      s[j][e] = x.alpha * s[j][e] - x.alpha * x.beta * sk * x.kh[e] + x.beta * x.v[j] * x.kh[e];
+    for (int e = 0; e < E; ++e) s[j][e] = x.alpha * s[j][e] + c * x.kh[e];
   }
 }
 
@@ -168,7 +196,8 @@ __global__ __launch_bounds__(256) void bwd_rows_kernel(BwdArgs A) {
   constexpr int SUB = kSub<DK>;
   constexpr int NF = 2 * DK + 2;  // fields per token of a partial: dqh, dkh, dalpha, dbeta
   __shared__ float part[4][SUB][NF];
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  const int tid = threadIdx.x, l = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nrb = A.DV / kBwdRows;
   const int64_t x = blockIdx.x;
   const int rb = (int)(x % nrb);
@@ -194,8 +223,8 @@ __global__ __launch_bounds__(256) void bwd_rows_kernel(BwdArgs A) {
   for (int j = 0; j < kRowsPerWave; ++j)
 #pragma unroll
     for (int e = 0; e < E; ++e) s[j][e] = state_at(S0, j, e);
-  Raw<DK> raw, nxt;
-  if (L > 0) fetch<DK>(A, t0, h, hv, row0, l, raw);
+  Token<DK> tk, nx;
+  if (L > 0) fetch<DK>(A, t0, h, hv, row0, l, tk);
   for (int64_t t = 0; t < L; ++t) {
     if (t % kCk == 0) {
       float* c = ck_at(t / kCk);
@@ -204,11 +233,9 @@ __global__ __launch_bounds__(256) void bwd_rows_kernel(BwdArgs A) {
 #pragma unroll
         for (int e = 0; e < E; ++e) c[((int64_t)(row0 + j)) * DK + 64 * e + l] = s[j][e];
     }
-    fetch<DK>(A, t0 + min(t + 1, L - 1), h, hv, row0, l, nxt);  // the last token again at the end
-    Token<DK> tk;
-    finish<DK>(A, hv, raw, tk);
+    fetch<DK>(A, t0 + min(t + 1, L - 1), h, hv, row0, l, nx);  // the last token again at the end
     step<DK>(tk, s);
-    raw = nxt;
+    tk = nx;
   }
   // the checkpoints are read back by the same lanes that wrote them: no barrier needed
 
@@ -228,13 +255,11 @@ __global__ __launch_bounds__(256) void bwd_rows_kernel(BwdArgs A) {
     for (int j = 0; j < kRowsPerWave; ++j)
 #pragma unroll
       for (int e = 0; e < E; ++e) s[j][e] = cp[((int64_t)(row0 + j)) * DK + 64 * e + l];
-    fetch<DK>(A, t0 + c * kCk, h, hv, row0, l, raw);
+    fetch<DK>(A, t0 + c * kCk, h, hv, row0, l, tk);
     for (int64_t t = c * kCk; t < u_lo; ++t) {
-      fetch<DK>(A, t0 + t + 1, h, hv, row0, l, nxt);  // t + 1 <= u_lo < L
-      Token<DK> tk;
-      finish<DK>(A, hv, raw, tk);
+      fetch<DK>(A, t0 + t + 1, h, hv, row0, l, nx);  // t + 1 <= u_lo < L
       step<DK>(tk, s);
-      raw = nxt;
+      tk = nx;
     }
     float sb[SUB][kRowsPerWave][E];  // S_{t-1} for the sub-chunk's tokens
 #pragma clang loop unroll(full)
@@ -244,60 +269,55 @@ __global__ __launch_bounds__(256) void bwd_rows_kernel(BwdArgs A) {
         for (int j = 0; j < kRowsPerWave; ++j)
 #pragma unroll
           for (int e = 0; e < E; ++e) sb[i][j][e] = s[j][e];
-        fetch<DK>(A, t0 + min(u_lo + i + 1, u_hi - 1), h, hv, row0, l, nxt);
-        Token<DK> tk;
-        finish<DK>(A, hv, raw, tk);
+        fetch<DK>(A, t0 + min(u_lo + i + 1, u_hi - 1), h, hv, row0, l, nx);
         step<DK>(tk, s);
-        raw = nxt;
+        tk = nx;
       }
     }
-    // the sub-chunk's last token, then each step fetches the one before it
-    fetch<DK>(A, t0 + u_hi - 1, h, hv, row0, l, raw);
+    // s is now the state after the sub-chunk's last token. Walk back from that token; each
+    // step fetches the one before it.
+    fetch<DK>(A, t0 + u_hi - 1, h, hv, row0, l, tk);
     float dO[kRowsPerWave], dOn[kRowsPerWave];
-#pragma unroll
-    for (int j = 0; j < kRowsPerWave; ++j)
-      dO[j] = ldx(A.dout, ((t0 + u_hi - 1) * A.HV + hv) * (int64_t)A.DV + row0 + j, A.bf16);
+    ld4(A.dout, ((t0 + u_hi - 1) * A.HV + hv) * (int64_t)A.DV + row0, A.bf16, dO);
 #pragma clang loop unroll(full)
     for (int i = SUB - 1; i >= 0; --i) {
       if (u_lo + i >= u_hi) continue;  // past the request's end (uniform)
       const int64_t t = t0 + u_lo + i;
       const int64_t tp = t0 + u_lo + max(i - 1, 0);
-      fetch<DK>(A, tp, h, hv, row0, l, nxt);
-#pragma unroll
-      for (int j = 0; j < kRowsPerWave; ++j)
-        dOn[j] = ldx(A.dout, (tp * A.HV + hv) * (int64_t)A.DV + row0 + j, A.bf16);
-      Token<DK> tk;
-      finish<DK>(A, hv, raw, tk);
-      float st[kRowsPerWave][E];
-#pragma unroll
-      for (int j = 0; j < kRowsPerWave; ++j)
-#pragma unroll
-        for (int e = 0; e < E; ++e) st[j][e] = sb[i][j][e];
-      step<DK>(tk, st);  // S_t
+      fetch<DK>(A, tp, h, hv, row0, l, nx);
+      ld4(A.dout, (tp * A.HV + hv) * (int64_t)A.DV + row0, A.bf16, dOn);
+      // S_t: the state before the next token, or the sub-chunk's end state
+      const bool last = (i == SUB - 1) || (u_lo + i + 1 >= u_hi);
       float dqh[E] = {}, dkh[E] = {};
       float dal = 0.f, dbe = 0.f;
+      float dvr[kRowsPerWave];
 #pragma unroll
       for (int j = 0; j < kRowsPerWave; ++j) {
         float pk = 0.f, dk_ = 0.f, ds = 0.f;
 #pragma unroll
         for (int e = 0; e < E; ++e) {
+          const float st = last ? s[j][e] : sb[i < SUB - 1 ? i + 1 : i][j][e];
           D[j][e] += dO[j] * tk.qh[e];
-          dqh[e] += dO[j] * st[j][e];
+          dqh[e] += dO[j] * st;
           pk += sb[i][j][e] * tk.kh[e];
           dk_ += D[j][e] * tk.kh[e];
           ds += D[j][e] * sb[i][j][e];
         }
         const float Spk = wave_sum(pk), Dk = wave_sum(dk_), Ds = wave_sum(ds);
-        if (l == 0) A.dv[(t * A.HV + hv) * (int64_t)A.DV + row0 + j] = tk.beta * Dk;
+        dvr[j] = tk.beta * Dk;
         dbe += Dk * (tk.v[j] - tk.alpha * Spk);
         dal += Ds - tk.beta * Dk * Spk;
+        const float cS = -tk.alpha * tk.beta * Spk, cD = -tk.alpha * tk.beta * Dk;
+        const float cV = tk.beta * tk.v[j], cK = tk.alpha * tk.beta * Dk;
 #pragma unroll
         for (int e = 0; e < E; ++e) {
-          dkh[e] += -tk.alpha * tk.beta * (Spk * D[j][e] + Dk * sb[i][j][e]) +
-                    tk.beta * tk.v[j] * D[j][e];
-          D[j][e] = tk.alpha * (D[j][e] - tk.beta * Dk * tk.kh[e]);
+          dkh[e] += cS * D[j][e] + cD * sb[i][j][e] + cV * D[j][e];
+          D[j][e] = tk.alpha * D[j][e] - cK * tk.kh[e];
         }
       }
+      if (l == 0)
+        *reinterpret_cast<float4*>(A.dv + (t * A.HV + hv) * (int64_t)A.DV + row0) =
+            make_float4(dvr[0], dvr[1], dvr[2], dvr[3]);
 #pragma unroll
       for (int e = 0; e < E; ++e) {
         part[w][i][64 * e + l] = dqh[e];
@@ -307,7 +327,7 @@ __global__ __launch_bounds__(256) void bwd_rows_kernel(BwdArgs A) {
         part[w][i][2 * DK] = dal;
         part[w][i][2 * DK + 1] = dbe;
       }
-      raw = nxt;
+      tk = nx;
 #pragma unroll
       for (int j = 0; j < kRowsPerWave; ++j) dO[j] = dOn[j];
     }
@@ -426,6 +446,9 @@ BwdLayout bwd_layout_for(const Shape& s) {
   L.ck = take(sizeof(float) * (size_t)L.max_chunks * s.HV * s.dv * s.dk);
   L.part = take(sizeof(float) * (size_t)(s.dv / kBwdRows) * s.N * s.HV * (2 * s.dk + 2));
   L.dal = take(sizeof(float) * (size_t)s.N * s.HV);
+  L.qn = take(sizeof(float) * (size_t)s.N * s.H * s.dk);
+  L.kn = take(sizeof(float) * (size_t)s.N * s.H * s.dk);
+  L.ab = take(sizeof(float) * 2 * (size_t)s.N * s.HV);
   L.total = off;
   return L;
 }
@@ -474,6 +497,9 @@ hipError_t launch_backward(const Shape& s, const BwdLayout& L, char* ws, const v
   A.ck = (float*)(ws + L.ck);
   A.part = (float*)(ws + L.part);
   A.dal = (float*)(ws + L.dal);
+  A.qn = (float*)(ws + L.qn);
+  A.kn = (float*)(ws + L.kn);
+  A.ab = (float*)(ws + L.ab);
   A.N = s.N;
   A.B = (int)s.B;
   A.H = s.H;
@@ -484,6 +510,7 @@ hipError_t launch_backward(const Shape& s, const BwdLayout& L, char* ws, const v
   const dim3 rows((unsigned)(s.B * s.HV * (s.dv / kBwdRows))), fin((unsigned)((s.N * s.H + 3) / 4));
 #define GDN_BWD_CASE(DKv)                                                              \
   if (s.dk == DKv) {                                                                   \
+    if (s.N > 0) hipLaunchKernelGGL((bwd_token_kernel<DKv>), fin, dim3(256), 0, st, A); \
     hipLaunchKernelGGL((bwd_rows_kernel<DKv>), rows, dim3(256), 0, st, A);             \
     if ((e = hipGetLastError()) != hipSuccess) return e;                               \
     if (s.N > 0) hipLaunchKernelGGL((bwd_finish_kernel<DKv>), fin, dim3(256), 0, st, A); \

@@ -442,7 +442,9 @@ def bench_verify(args):
                      "traffic": stored_traffic("recurrent_kernel", src_hash),
                      "algorithmic_bytes_per_launch": nbytes, "avg_launch_ms": launch_ms,
                      "avg_launch_ms_events": events_ms, "event_pair_ms": pair_ms},
-        "chunked_path_ms_per_step": chunked_ms,
+        # gdn_prefill_fwd on the same requests: it evaluates requests this short with the
+        # same token recurrence (see --op crossover for the chunked path's cost)
+        "prefill_fwd_ms_per_step": chunked_ms,
         "kernel_source_hash": src_hash,
     }
     if not args.no_cpu_baseline:
@@ -993,9 +995,69 @@ def bench_backward(args):
     print(json.dumps(res), flush=True)
 
 
+CROSSOVER_LENGTHS = (1, 2, 4, 8, 12, 16, 20, 24, 32, 48, 64)
+
+
+def bench_crossover(args):
+    """Short requests: gdn_prefill_fwd as shipped (requests of at most GDN_SHORT_REQUEST
+    tokens through the token recurrence), the same call with GDN_FLAG_CHUNK_ALL (every
+    request chunked) and gdn_recurrent_fwd, on 512 requests of equal length L, bf16,
+    H = 16, HV = 32, dk = dv = 128 (seeded torch.randn inputs). Prints one JSON line with
+    the per-call wall time of each at every L: the measurement behind the threshold."""
+    import torch
+
+    import gated_deltanet_prefill_gdn_amd as gdn
+
+    dev = torch.device("cuda:0")
+    B, H, HV, D = 512, 16, 32, 128
+    g = torch.Generator(device="cpu").manual_seed(7)
+    rows = []
+    for L in CROSSOVER_LENGTHS:
+        N = B * L
+        q = torch.randn((N, H, D), generator=g).to(torch.bfloat16).to(dev)
+        k = torch.randn((N, H, D), generator=g).to(torch.bfloat16).to(dev)
+        v = torch.randn((N, HV, D), generator=g).to(torch.bfloat16).to(dev)
+        a = (torch.randn((N, HV), generator=g) - 2.0).to(dev)
+        b = torch.randn((N, HV), generator=g).to(dev)
+        A_log = torch.rand((HV,), generator=g).to(dev)
+        dt_bias = (0.1 * torch.randn((HV,), generator=g)).to(dev)
+        pool = (0.05 * torch.randn((B, HV, D, D), generator=g)).to(dev)
+        idx = torch.arange(B, dtype=torch.int64, device=dev)
+        cu = torch.arange(0, N + 1, L, dtype=torch.int64, device=dev)
+        out = torch.empty((N, HV, D), dtype=torch.bfloat16, device=dev)
+        ws = torch.empty(gdn.gdn_prefill_workspace_size(gdn.problem_of(q, k, v, pool, idx)),
+                         dtype=torch.uint8, device=dev)
+        stream = torch.cuda.current_stream(dev)
+        calls = {
+            "prefill_fwd": lambda: gdn.gdn_prefill_fwd(q, k, v, a, b, A_log, dt_bias, pool, idx,
+                                                       cu, out=out, workspace=ws, stream=stream),
+            "prefill_fwd_chunk_all": lambda: gdn.gdn_prefill_fwd(
+                q, k, v, a, b, A_log, dt_bias, pool, idx, cu, out=out, workspace=ws,
+                stream=stream, flags=gdn.GDN_FLAG_CHUNK_ALL),
+            "recurrent_fwd": lambda: gdn.gdn_recurrent_fwd(q, k, v, a, b, A_log, dt_bias, pool,
+                                                           idx, cu, out=out, stream=stream),
+        }
+        row = {"L": L, "N": N}
+        for name, f in calls.items():
+            row[name + "_ms"] = _time_launches(f, stream, args.steps, args.warmup)[0]
+        rows.append(row)
+        print(json.dumps(row), file=sys.stderr, flush=True)
+        del q, k, v, a, b, pool, out, ws
+        torch.cuda.empty_cache()
+    print(json.dumps({
+        "metric": "short-request dispatch: per-call ms of gdn_prefill_fwd, of the same call "
+                  "with every request chunked, and of gdn_recurrent_fwd",
+        "value": None, "unit": "ms", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "higher_is_better": False, "dtype": "bf16", "data": "synthetic (torch.randn, seed 7)",
+        "config": {"workload": f"B={B} requests of L tokens, H={H} HV={HV} dk=dv={D}",
+                   "short_request_threshold": gdn.GDN_SHORT_REQUEST},
+        "rows": rows, "kernel_source_hash": kernel_source_hash()}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
-    ap.add_argument("--op", choices=("prefill", "decode", "promote", "verify", "backward"),
+    ap.add_argument("--op", choices=("prefill", "decode", "promote", "verify", "backward",
+                                     "crossover"),
                     default="prefill",
                     help="the call a step times (default: the prefill forward)")
     ap.add_argument("--gpus", type=int, default=1)
@@ -1027,6 +1089,9 @@ def main():
         return
     if args.op == "backward":
         bench_backward(args)
+        return
+    if args.op == "crossover":
+        bench_crossover(args)
         return
 
     bench_prefill(args)

@@ -47,6 +47,9 @@ GDN_SCHEDULE_COLUMN_SLICES = 0
 GDN_SCHEDULE_SEGMENTS = 1
 GDN_SCHEDULE_FP32 = 2
 
+GDN_FLAG_CHUNK_ALL = 1   # gdn_problem_t.flags: chunk every request
+GDN_SHORT_REQUEST = 12   # requests of at most this many tokens take the token recurrence
+
 EXPORTED = ("gdn_prefill_workspace_size", "gdn_prefill_state_schedule", "gdn_prefill_fwd",
             "gdn_prefill_fwd_events", "gdn_prefill_fwd_noalloc", "gdn_prefill_nonfinite",
             "gdn_prefill_bwd_workspace_size", "gdn_prefill_bwd",
@@ -64,7 +67,7 @@ class GdnProblem(ctypes.Structure):
         ("head_v", ctypes.c_int32),
         ("pool_size", ctypes.c_int64),
         ("qkv_dtype", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("flags", ctypes.c_int32),
     ]
 
 
@@ -145,8 +148,9 @@ def gdn_version() -> int:
 
 
 def make_problem(N: int, B: int, H: int, HV: int, dk: int, dv: int, pool: int,
-                 dtype: int) -> GdnProblem:
-    return GdnProblem(int(N), int(B), int(H), int(HV), int(dk), int(dv), int(pool), int(dtype), 0)
+                 dtype: int, flags: int = 0) -> GdnProblem:
+    return GdnProblem(int(N), int(B), int(H), int(HV), int(dk), int(dv), int(pool), int(dtype),
+                      int(flags))
 
 
 def gdn_prefill_workspace_size(prob: GdnProblem, chunk_size: int = 64) -> int:
@@ -182,11 +186,11 @@ def _ptr(t):
     return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
 
 
-def problem_of(q, k, v, state_pool, cache_indices) -> GdnProblem:
+def problem_of(q, k, v, state_pool, cache_indices, flags: int = 0) -> GdnProblem:
     N, H, dk = q.shape
     HV, dv = v.shape[1], v.shape[2]
     return make_problem(N, cache_indices.shape[0], H, HV, dk, dv, state_pool.shape[0],
-                        _dtype_code(q))
+                        _dtype_code(q), flags)
 
 
 def gdn_recurrent_fwd(q, k, v, a, b, A_log, dt_bias, state_pool, cache_indices, cu_seqlens,
@@ -207,19 +211,21 @@ def gdn_recurrent_fwd(q, k, v, a, b, A_log, dt_bias, state_pool, cache_indices, 
 
 
 def gdn_prefill_fwd(q, k, v, a, b, A_log, dt_bias, state_pool, cache_indices, cu_seqlens,
-                    chunk_size: int = 64, out=None, workspace=None, stream=None):
+                    chunk_size: int = 64, out=None, workspace=None, stream=None, flags: int = 0):
+    """``flags``: GDN_FLAG_* bits of the problem descriptor (GDN_FLAG_CHUNK_ALL: chunk every
+    request, none through the token recurrence)."""
     return _prefill(q, k, v, a, b, A_log, dt_bias, state_pool, cache_indices, cu_seqlens,
-                    chunk_size, out, workspace, stream, None)
+                    chunk_size, out, workspace, stream, None, flags)
 
 
 def gdn_prefill_fwd_noalloc(q, k, v, a, b, A_log, dt_bias, state_pool, cache_indices,
-                            cu_seqlens, out, chunk_size: int = 64, stream=None):
+                            cu_seqlens, out, chunk_size: int = 64, stream=None, flags: int = 0):
     """gdn_prefill_fwd on the library's built-in device workspace: allocates nothing, so
     ``out`` must be given. Problems whose workspace exceeds GDN_NOALLOC_SCRATCH_BYTES raise
     GdnError(GDN_ERR_WORKSPACE); calls that may overlap on one GPU must be serialised."""
     import torch
     prob, out = _check_prefill_args(q, k, v, a, b, A_log, dt_bias, state_pool, cache_indices,
-                                    cu_seqlens, out)
+                                    cu_seqlens, out, flags=flags)
     st = (stream or torch.cuda.current_stream(q.device)).cuda_stream
     rc = load_library().gdn_prefill_fwd_noalloc(
         _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(A_log), _ptr(dt_bias),
@@ -232,18 +238,18 @@ def gdn_prefill_fwd_noalloc(q, k, v, a, b, A_log, dt_bias, state_pool, cache_ind
 
 def gdn_prefill_fwd_events(q, k, v, a, b, A_log, dt_bias, state_pool, cache_indices,
                            cu_seqlens, stage_events, chunk_size: int = 64, out=None,
-                           workspace=None, stream=None):
+                           workspace=None, stream=None, flags: int = 0):
     """gdn_prefill_fwd that records the GDN_NUM_STAGES + 1 caller-created hipEvent_t
     handles in ``stage_events`` (ints) on the stream around the stages."""
     if len(stage_events) != GDN_NUM_STAGES + 1:
         raise ValueError("need GDN_NUM_STAGES + 1 events")
     arr = (ctypes.c_void_p * len(stage_events))(*[int(e) for e in stage_events])
     return _prefill(q, k, v, a, b, A_log, dt_bias, state_pool, cache_indices, cu_seqlens,
-                    chunk_size, out, workspace, stream, arr)
+                    chunk_size, out, workspace, stream, arr, flags)
 
 
 def _check_prefill_args(q, k, v, a, b, A_log, dt_bias, state_pool, cache_indices, cu_seqlens,
-                        out, want_out: bool = True):
+                        out, want_out: bool = True, flags: int = 0):
     """Shapes, dtypes, devices and contiguity of a prefill call's tensors; allocates ``out``
     if it is None. Returns (problem descriptor, out)."""
     import torch
@@ -274,7 +280,7 @@ def _check_prefill_args(q, k, v, a, b, A_log, dt_bias, state_pool, cache_indices
     _need(cu_seqlens, "cu_seqlens", dtype=torch.int64, ndim=1, device=dev)
     if cu_seqlens.shape[0] != cache_indices.shape[0] + 1:
         raise ValueError("cu_seqlens must have B + 1 entries")
-    prob = problem_of(q, k, v, state_pool, cache_indices)
+    prob = problem_of(q, k, v, state_pool, cache_indices, flags)
     if not want_out:
         return prob, None
     if out is None:
@@ -287,7 +293,7 @@ def _check_prefill_args(q, k, v, a, b, A_log, dt_bias, state_pool, cache_indices
 
 
 def _prefill(q, k, v, a, b, A_log, dt_bias, state_pool, cache_indices, cu_seqlens,
-             chunk_size, out, workspace, stream, events):
+             chunk_size, out, workspace, stream, events, flags=0):
     """GDN prefill forward on device tensors; returns ``out`` [N, HV, dv] in v's dtype.
 
     q, k [N, H, dk] and v [N, HV, dv] bf16/fp32; a, b [N, HV] fp32; A_log, dt_bias [HV]
@@ -299,7 +305,7 @@ def _prefill(q, k, v, a, b, A_log, dt_bias, state_pool, cache_indices, cu_seqlen
     dev = q.device
     N, HV = q.shape[0], v.shape[1]
     prob, out = _check_prefill_args(q, k, v, a, b, A_log, dt_bias, state_pool, cache_indices,
-                                    cu_seqlens, out)
+                                    cu_seqlens, out, flags=flags)
     need = gdn_prefill_workspace_size(prob, chunk_size)
     if need == 0 and (N > 0 and cache_indices.shape[0] > 0):
         raise GdnError(GDN_ERR_UNSUPPORTED, "gdn_prefill_workspace_size")

@@ -12,6 +12,8 @@
 #include "gdn.h"
 #include "gdn_internal.h"
 
+static_assert(gdn::kShortRequest == GDN_SHORT_REQUEST, "one threshold");
+
 namespace gdn {
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -95,7 +97,7 @@ static gdn_status_t check_problem(const gdn_problem_t* p, int32_t chunk_size, Sh
   if (p->num_v_heads % p->num_qk_heads != 0) return GDN_ERR_INVALID_ARG;
   if (p->head_k <= 0 || p->head_v <= 0) return GDN_ERR_INVALID_ARG;
   if (p->qkv_dtype != GDN_DTYPE_F32 && p->qkv_dtype != GDN_DTYPE_BF16) return GDN_ERR_INVALID_ARG;
-  if (p->reserved != 0) return GDN_ERR_INVALID_ARG;
+  if ((p->flags & ~GDN_FLAG_CHUNK_ALL) != 0) return GDN_ERR_INVALID_ARG;
   if (chunk_size <= 0) return GDN_ERR_INVALID_ARG;
   if (p->batch > 0 && p->pool_size < 1) return GDN_ERR_INVALID_ARG;
   s->N = p->total_tokens;
@@ -170,10 +172,14 @@ gdn_status_t run_prefill(const void* q, const void* k, const void* v, const floa
   if (!prefill_grids_fit(s, path, L.max_chunks)) return GDN_ERR_UNSUPPORTED;
   if (!workspace || workspace_bytes < L.total) return GDN_ERR_WORKSPACE;
   if (((uintptr_t)workspace & 255) != 0) return GDN_ERR_WORKSPACE;
-  if (path == Path::kMfma) {  // 16-byte vector loads and stores
-    for (const void* ptr : {q, k, v, (const void*)out, (const void*)state_pool})
-      if (((uintptr_t)ptr & 15) != 0) return GDN_ERR_INVALID_ARG;
-  }
+  bool aligned = true;  // 16-byte vector loads and stores
+  for (const void* ptr : {q, k, v, (const void*)out, (const void*)state_pool})
+    aligned = aligned && ((uintptr_t)ptr & 15) == 0;
+  if (path == Path::kMfma && !aligned) return GDN_ERR_INVALID_ARG;
+  // Short requests go to the token recurrence (its 16-byte loads need the alignment; the
+  // fp32 chunked kernels do not, and take every request otherwise).
+  const bool split = (prob->flags & GDN_FLAG_CHUNK_ALL) == 0;
+  s.short_len = (split && aligned && decode_blocks(s) <= 0x7FFFFFFF) ? kShortRequest : 0;
   if (events) {
     for (int i = 0; i <= GDN_NUM_STAGES; ++i)
       if (!events[i]) return GDN_ERR_INVALID_ARG;
@@ -181,6 +187,12 @@ gdn_status_t run_prefill(const void* q, const void* k, const void* v, const floa
   hipStream_t st = (hipStream_t)stream;
   auto mark = [&](int i) -> bool {
     return !events || hipEventRecord((hipEvent_t)events[i], st) == hipSuccess;
+  };
+  // the requests of at most s.short_len tokens, in the state stage
+  auto short_pass = [&]() -> bool {
+    return s.short_len == 0 ||
+           launch_recurrent(q, k, v, a, b, A_log, dt_bias, cache_indices, cu_seqlens, s,
+                            s.short_len, state_pool, out, st) == hipSuccess;
   };
   char* ws = (char*)workspace;
   int32_t* chunk_off = (int32_t*)(ws + L.chunk_off);
@@ -218,13 +230,14 @@ gdn_status_t run_prefill(const void* q, const void* k, const void* v, const floa
       float* sstart = (float*)(ws + L.sstart);
       for (int stage = 0; stage < 3; ++stage) {
         if (!mark(2 + stage)) return GDN_ERR_HIP;
+        if (stage == 2 && !short_pass()) return GDN_ERR_HIP;
         if ((stage < 2 && !cp.segmented)) continue;  // nothing is cut: one pass
         if (launch_chain(cp, s, qf, kf, cu_seqlens, cache_indices, chunk_off, w, u, aqk, eg, rp,
                          sstart, state_pool, out, nonfinite, stage, st) != hipSuccess)
           return GDN_ERR_HIP;
       }
     } else {
-      if (!mark(2) || !mark(3) || !mark(4)) return GDN_ERR_HIP;
+      if (!mark(2) || !mark(3) || !mark(4) || !short_pass()) return GDN_ERR_HIP;
       if (launch_mfma_state(qf, kf, cu_seqlens, cache_indices, chunk_off, w, u, aqk, eg, s,
                             state_pool, out, nonfinite, st) != hipSuccess)
         return GDN_ERR_HIP;
@@ -233,7 +246,7 @@ gdn_status_t run_prefill(const void* q, const void* k, const void* v, const floa
     if (launch_ref_prep(k, v, cu_seqlens, chunk_off, chunk_seq, gcum, beta, s, L.max_chunks,
                         (float*)w, (float*)u, st) != hipSuccess)
       return GDN_ERR_HIP;
-    if (!mark(2) || !mark(3) || !mark(4)) return GDN_ERR_HIP;
+    if (!mark(2) || !mark(3) || !mark(4) || !short_pass()) return GDN_ERR_HIP;
     if (launch_ref_state(q, k, cu_seqlens, cache_indices, chunk_off, gcum, (const float*)w,
                          (const float*)u, s, state_pool, out, nonfinite, st) != hipSuccess)
       return GDN_ERR_HIP;
@@ -359,8 +372,8 @@ gdn_status_t gdn_recurrent_fwd(const void* q, const void* k, const void* v, cons
   for (const void* ptr : {q, k, v, (const void*)state_pool})  // 16-byte vector loads
     if (((uintptr_t)ptr & 15) != 0) return GDN_ERR_INVALID_ARG;
   if (decode_blocks(s) > 0x7FFFFFFF) return GDN_ERR_UNSUPPORTED;
-  if (launch_recurrent(q, k, v, a, b, A_log, dt_bias, cache_indices, cu_seqlens, s, state_pool,
-                       out, (hipStream_t)stream) != hipSuccess)
+  if (launch_recurrent(q, k, v, a, b, A_log, dt_bias, cache_indices, cu_seqlens, s, INT64_MAX,
+                       state_pool, out, (hipStream_t)stream) != hipSuccess)
     return GDN_ERR_HIP;
   return GDN_OK;
 }

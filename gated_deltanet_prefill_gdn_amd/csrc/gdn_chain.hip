@@ -130,6 +130,7 @@ struct ChainArgs {
   float* sstart;  // [segment][HV][dv][dk]: start state of every segment of a cut request
   int32_t* nonfinite;  // raised by the output pass if a final state is not finite
   int B, H, HV, DV;
+  int64_t short_len;  // requests of at most this many tokens are not chunked
   int lseg;       // chunks per segment
   int segmented;  // requests may be cut (at most 64 requests)
   int nb;         // workgroups per (segment, value head): 128-column blocks
@@ -153,7 +154,7 @@ __device__ __forceinline__ bool find_segment(const ChainArgs& a, int64_t sg, int
   int ns = 0;
   if (l < a.B) {
     const int64_t L = a.cu[l + 1] - a.cu[l];
-    const int64_t nch = (L + C - 1) / C;
+    const int64_t nch = path_chunks(L, C, a.short_len);
     ns = (int)((nch + a.lseg - 1) / a.lseg);
   }
   int incl = ns;
@@ -197,8 +198,8 @@ __global__ __launch_bounds__(kThreads<MODE>, 1) void chain_kernel(ChainArgs a) {
   int b, j, nseg, seg0;
   if (!find_segment(a, sg, l, b, j, nseg, seg0)) return;
   const int64_t L = a.cu[b + 1] - a.cu[b];
-  if (L <= 0) return;
-  const int nch = (int)((L + C - 1) / C);
+  const int nch = (int)path_chunks(L, C, a.short_len);
+  if (nch == 0) return;  // empty (slot untouched) or evaluated by the token recurrence
   const int c_lo = j * a.lseg;
   const int n = min(c_lo + a.lseg, nch) - c_lo;  // chunks of this segment (>= 1)
   if constexpr (MODE == kModeOperator)
@@ -479,7 +480,7 @@ __global__ __launch_bounds__(256) void combine_kernel(ChainArgs a) {
   int ns = 0;
   if (l < a.B) {
     const int64_t L = a.cu[l + 1] - a.cu[l];
-    const int64_t nch = (L + C - 1) / C;
+    const int64_t nch = path_chunks(L, C, a.short_len);
     ns = (int)((nch + a.lseg - 1) / a.lseg);
   }
   int incl = ns;
@@ -601,6 +602,7 @@ hipError_t launch_chain(const ChainPlan& p, const Shape& s, const void* qf, cons
   a.H = s.H;
   a.HV = s.HV;
   a.DV = s.dv;
+  a.short_len = s.short_len;
   a.lseg = p.lseg;
   a.segmented = p.segmented ? 1 : 0;
   a.nb = stage == 0 ? p.nb_op : p.nb;

@@ -225,7 +225,7 @@ __global__ __launch_bounds__(kDecodeThreads) void recurrent_kernel(
     const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
     const float* __restrict__ ga, const float* __restrict__ gb, const float* __restrict__ A_log,
     const float* __restrict__ dt_bias, const int64_t* __restrict__ cache_indices,
-    const int64_t* __restrict__ cu, int H, int HV, int DV, int nrb,
+    const int64_t* __restrict__ cu, int H, int HV, int DV, int nrb, int64_t max_len,
     float* __restrict__ state_pool, void* __restrict__ out) {
   constexpr int LPR = DK / 8;
   constexpr int RPW = 64 / LPR;
@@ -241,6 +241,7 @@ __global__ __launch_bounds__(kDecodeThreads) void recurrent_kernel(
   const int64_t bi = b32;
   const int64_t t_begin = cu[bi], t_end = cu[bi + 1];
   if (t_begin >= t_end) return;  // an empty request leaves its slot untouched
+  if (t_end - t_begin > max_len) return;  // left to the chunked kernels
   const int tid = threadIdx.x, wv = tid >> 6, l = tid & 63;
   const int gl = l % LPR, rg = l / LPR;
   const int64_t slot = cache_indices[bi];
@@ -353,14 +354,14 @@ __global__ __launch_bounds__(kDecodeThreads) void recurrent_kernel(
 template <int DK, bool BF16>
 hipError_t launch_recurrent_t(const void* q, const void* k, const void* v, const float* a,
                               const float* b, const float* A_log, const float* dt_bias,
-                              const int64_t* idx, const int64_t* cu, const Shape& s, float* pool,
-                              void* out, hipStream_t st) {
+                              const int64_t* idx, const int64_t* cu, const Shape& s,
+                              int64_t max_len, float* pool, void* out, hipStream_t st) {
   if (s.dv % kRowsPerBlock<DK> != 0) return hipErrorInvalidValue;
   const int nrb = s.dv / kRowsPerBlock<DK>;
   const int64_t blocks = s.B * (int64_t)s.HV * nrb;
   hipLaunchKernelGGL((recurrent_kernel<DK, BF16>), dim3((unsigned)blocks), dim3(kDecodeThreads),
-                     0, st, q, k, v, a, b, A_log, dt_bias, idx, cu, s.H, s.HV, s.dv, nrb, pool,
-                     out);
+                     0, st, q, k, v, a, b, A_log, dt_bias, idx, cu, s.H, s.HV, s.dv, nrb, max_len,
+                     pool, out);
   return hipGetLastError();
 }
 
@@ -405,15 +406,16 @@ hipError_t launch_decode(const void* q, const void* k, const void* v, const floa
 hipError_t launch_recurrent(const void* q, const void* k, const void* v, const float* a,
                             const float* b, const float* A_log, const float* dt_bias,
                             const int64_t* cache_indices, const int64_t* cu_seqlens,
-                            const Shape& s, float* state_pool, void* out, hipStream_t st) {
-#define GDN_RECURRENT_CASE(DKv)                                                             \
-  if (s.dk == DKv)                                                                          \
-    return s.bf16 ? launch_recurrent_t<DKv, true>(q, k, v, a, b, A_log, dt_bias,            \
-                                                  cache_indices, cu_seqlens, s, state_pool, \
-                                                  out, st)                                  \
-                  : launch_recurrent_t<DKv, false>(q, k, v, a, b, A_log, dt_bias,           \
-                                                   cache_indices, cu_seqlens, s, state_pool, \
-                                                   out, st);
+                            const Shape& s, int64_t max_len, float* state_pool, void* out,
+                            hipStream_t st) {
+#define GDN_RECURRENT_CASE(DKv)                                                              \
+  if (s.dk == DKv)                                                                           \
+    return s.bf16 ? launch_recurrent_t<DKv, true>(q, k, v, a, b, A_log, dt_bias,             \
+                                                  cache_indices, cu_seqlens, s, max_len,     \
+                                                  state_pool, out, st)                       \
+                  : launch_recurrent_t<DKv, false>(q, k, v, a, b, A_log, dt_bias,            \
+                                                   cache_indices, cu_seqlens, s, max_len,    \
+                                                   state_pool, out, st);
   GDN_RECURRENT_CASE(64)
   GDN_RECURRENT_CASE(128)
   GDN_RECURRENT_CASE(256)

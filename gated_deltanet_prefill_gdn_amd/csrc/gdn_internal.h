@@ -47,7 +47,22 @@ struct Shape {
   int H, HV, dk, dv, C;
   int64_t pool;
   bool bf16;
+  int64_t short_len = 0;  // requests of at most this many tokens skip the chunked kernels
 };
+
+// Requests of at most this many tokens are evaluated by the token recurrence inside the
+// prefill call, longer ones in chunks (a one-token request still costs the chunked path a
+// whole 64-row chunk of intermediates per value head and state slice). Measured on bf16
+// inputs, dk = dv = 128, 32 value heads, 512 requests of L tokens, per call: chunking
+// every request takes 1.59 ms at L = 1, 1.61 ms at 12 and 16; with the recurrence for the
+// short ones (whose call still launches the chunked kernels, which find nothing to do)
+// 0.53 ms at 1, 1.36 ms at 12 and 1.68 ms at 16.
+constexpr int64_t kShortRequest = 12;  // GDN_SHORT_REQUEST of the public header
+
+// Chunks of a request of L tokens on the chunked path: none if L <= short_len.
+__host__ __device__ __forceinline__ int64_t path_chunks(int64_t L, int C, int64_t short_len) {
+  return (L > short_len && L > 0) ? (L + C - 1) / C : 0;
+}
 
 Path choose_path(const Shape& s);
 WsLayout layout_for(const Shape& s, Path p);
@@ -140,7 +155,8 @@ hipError_t launch_decode(const void* q, const void* k, const void* v, const floa
 hipError_t launch_recurrent(const void* q, const void* k, const void* v, const float* a,
                             const float* b, const float* A_log, const float* dt_bias,
                             const int64_t* cache_indices, const int64_t* cu_seqlens,
-                            const Shape& s, float* state_pool, void* out, hipStream_t st);
+                            const Shape& s, int64_t max_len, float* state_pool, void* out,
+                            hipStream_t st);  // requests longer than max_len are skipped
 
 // Promote update scan: shape and launcher (bf16 keys and values).
 struct PromoteShape {

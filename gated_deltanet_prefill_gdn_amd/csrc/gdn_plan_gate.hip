@@ -25,6 +25,7 @@ constexpr int kPlanLds = 4096;  // chunk_off entries kept in LDS for the request
 // for each chunk's request reads an LDS copy of chunk_off when it fits.
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int64_t* __restrict__ cu,
                                                             int64_t B, int C,
+                                                            int64_t short_len,
                                                             int32_t* __restrict__ chunk_off,
                                                             int32_t* __restrict__ chunk_seq,
                                                             int64_t max_chunks) {
@@ -39,7 +40,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int64_t* __res
     int32_t n = 0;
     if (bi < B) {
       const int64_t L = cu[bi + 1] - cu[bi];
-      n = L > 0 ? (int32_t)((L + C - 1) / C) : 0;
+      n = (int32_t)path_chunks(L, C, short_len);
     }
     int32_t x = n;  // inclusive scan within the wavefront
     for (int off = 1; off < 64; off <<= 1) {
@@ -127,7 +128,7 @@ __global__ __launch_bounds__(256) void gate_kernel(
 hipError_t launch_plan(const int64_t* cu_seqlens, const Shape& s, int32_t* chunk_off,
                        int32_t* chunk_seq, int64_t max_chunks, hipStream_t st) {
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, st, cu_seqlens, s.B, s.C,
-                     chunk_off, chunk_seq, max_chunks);
+                     s.short_len, chunk_off, chunk_seq, max_chunks);
   return hipGetLastError();
 }
 

@@ -171,7 +171,8 @@ __global__ __launch_bounds__(256, (DK + DV <= 256) ? 3 : 1) void mfma_prep_kerne
     const int64_t* __restrict__ cu, int32_t* __restrict__ chunk_off,
     const int32_t* __restrict__ chunk_seq, const float* __restrict__ ga,
     const float* __restrict__ gb, const float* __restrict__ A_log,
-    const float* __restrict__ dt_bias, int B, int H, int HV, _Float16* __restrict__ Wout,
+    const float* __restrict__ dt_bias, int B, int H, int HV, int64_t short_len,
+    _Float16* __restrict__ Wout,
     _Float16* __restrict__ Uout, _Float16* __restrict__ Aout, float* __restrict__ eg_out,
     _Float16* __restrict__ Kout, _Float16* __restrict__ Qout, int32_t* __restrict__ nonfinite) {
   constexpr int NKS = DK / 32;
@@ -258,7 +259,7 @@ __global__ __launch_bounds__(256, (DK + DV <= 256) ? 3 : 1) void mfma_prep_kerne
       int32_t nb = 0;
       if (l < B) {
         const int64_t L = cu[l + 1] - cu[l];
-        nb = L > 0 ? (int32_t)((L + C - 1) / C) : 0;
+        nb = (int32_t)path_chunks(L, C, short_len);
       }
       int32_t x = nb;  // inclusive scan over the wave
 #pragma unroll
@@ -567,7 +568,7 @@ hipError_t launch_prep_t(const void* q, const void* k, const void* v, const int6
   const int64_t grid = std::min<int64_t>(items, (int64_t)std::max(cus, 1) * std::max(per_cu, 1));
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), 0, st, (const uint16_t*)q,
                      (const uint16_t*)k, (const uint16_t*)v, cu, off, cseq, ga, gb, A_log,
-                     dt_bias, (int)s.B, s.H, s.HV, w, u, aqk, eg, kf, qf, nonfinite);
+                     dt_bias, (int)s.B, s.H, s.HV, s.short_len, w, u, aqk, eg, kf, qf, nonfinite);
   return hipGetLastError();
 }
 

@@ -156,8 +156,8 @@ __global__ __launch_bounds__(256) void ref_state_kernel(
     const Tin* __restrict__ q, const Tin* __restrict__ k, const int64_t* __restrict__ cu,
     const int64_t* __restrict__ cache_indices, const int32_t* __restrict__ chunk_off,
     const double* __restrict__ gcum, const float* __restrict__ W, const float* __restrict__ U,
-    int H, int HV, int dk, int dv, float* __restrict__ state_pool, Tin* __restrict__ out,
-    int32_t* __restrict__ nonfinite) {
+    int H, int HV, int dk, int dv, int64_t short_len, float* __restrict__ state_pool,
+    Tin* __restrict__ out, int32_t* __restrict__ nonfinite) {
   __shared__ float s_S[kBV][kMaxDk + 1];
   __shared__ float s_U[C][kBV + 1];
   __shared__ float s_Aqk[C][C + 1];
@@ -165,13 +165,13 @@ __global__ __launch_bounds__(256) void ref_state_kernel(
   __shared__ double s_G[C];
   const int seq = blockIdx.x, hv = blockIdx.y, v0 = blockIdx.z * kBV;
   const int64_t L = cu[seq + 1] - cu[seq];
-  if (L <= 0) return;  // empty request: its slot stays untouched
+  const int64_t nchunks = path_chunks(L, C, short_len);
+  if (nchunks == 0) return;  // empty (slot untouched) or evaluated by the token recurrence
   const int64_t slot = cache_indices[seq];
   const int h = hv / (HV / H);
   const int tid = threadIdx.x;
   float* Sg = state_pool + ((slot * HV + hv) * (int64_t)dv + v0) * dk;
   for (int idx = tid; idx < kBV * dk; idx += 256) s_S[idx / dk][idx % dk] = Sg[idx];
-  const int64_t nchunks = (L + C - 1) / C;
   for (int64_t cl = 0; cl < nchunks; ++cl) {
     const int64_t c = chunk_off[seq] + cl;
     const int64_t t0 = cu[seq] + cl * C;
@@ -272,12 +272,12 @@ hipError_t launch_ref_state(const void* q, const void* k, const int64_t* cu_seql
   if (s.bf16) {
     hipLaunchKernelGGL(ref_state_kernel<__hip_bfloat16>, grid, dim3(256), 0, st,
                        (const __hip_bfloat16*)q, (const __hip_bfloat16*)k, cu_seqlens,
-                       cache_indices, chunk_off, gcum, w, u, s.H, s.HV, s.dk, s.dv, state_pool,
-                       (__hip_bfloat16*)out, nonfinite);
+                       cache_indices, chunk_off, gcum, w, u, s.H, s.HV, s.dk, s.dv, s.short_len,
+                       state_pool, (__hip_bfloat16*)out, nonfinite);
   } else {
     hipLaunchKernelGGL(ref_state_kernel<float>, grid, dim3(256), 0, st, (const float*)q,
                        (const float*)k, cu_seqlens, cache_indices, chunk_off, gcum, w, u, s.H,
-                       s.HV, s.dk, s.dv, state_pool, (float*)out, nonfinite);
+                       s.HV, s.dk, s.dv, s.short_len, state_pool, (float*)out, nonfinite);
   }
   return hipGetLastError();
 }

@@ -81,7 +81,7 @@ __global__ __launch_bounds__(64 * (2 + NO + kStoreWaves<DK>)) void mfma_state_ke
     const int64_t* __restrict__ cu, const int64_t* __restrict__ cache_indices,
     const int32_t* __restrict__ chunk_off, const _Float16* __restrict__ W, const _Float16* __restrict__ Ut,
     const _Float16* __restrict__ Aqk, const float* __restrict__ egws, int B, int H, int HV,
-    int DV, float* __restrict__ state_pool, uint16_t* __restrict__ out,
+    int DV, int64_t short_len, float* __restrict__ state_pool, uint16_t* __restrict__ out,
     int32_t* __restrict__ nonfinite) {
   constexpr int NKS = DK / 32;    // 32-wide dk steps
   constexpr int NOWN = NKS / 2;   // dk steps of S^T held by each state wave
@@ -97,11 +97,11 @@ __global__ __launch_bounds__(64 * (2 + NO + kStoreWaves<DK>)) void mfma_state_ke
   if (p >= (int64_t)B * HV) return;
   const int seq = (int)(p / HV), hv = (int)(p % HV);
   const int64_t L = cu[seq + 1] - cu[seq];
-  if (L <= 0) return;
+  const int nch = (int)path_chunks(L, C, short_len);
+  if (nch == 0) return;  // empty (slot untouched) or evaluated by the token recurrence
   const int h = hv / (HV / H);
   const int64_t slot = cache_indices[seq];
   const int tid = threadIdx.x, wv = tid >> 6, l = tid & 63, m = l & 15, g = l >> 4;
-  const int nch = (int)((L + C - 1) / C);
   const int64_t cbase = chunk_off[seq];
   const int64_t tseq = cu[seq];
   const int64_t tend = cu[seq + 1];
@@ -407,7 +407,7 @@ hipError_t launch_state_t(const void* qf, const void* kf, const int64_t* cu, con
   const int64_t blocks = pairs8 * 8 * (s.dv / (16 * NC));
   hipLaunchKernelGGL((mfma_state_kernel<DK, NC, PD>), dim3((unsigned)blocks), dim3(64 * (2 + NO + kStoreWaves<DK>)), 0,
                      st, (const _Float16*)qf, (const _Float16*)kf, cu, idx, off, w, u, aqk,
-                     eg, (int)s.B, s.H, s.HV, s.dv, pool, (uint16_t*)out, nonfinite);
+                     eg, (int)s.B, s.H, s.HV, s.dv, s.short_len, pool, (uint16_t*)out, nonfinite);
   return hipGetLastError();
 }
 

@@ -47,15 +47,19 @@ def test_status_strings_and_version():
 
 
 def prob(**kw):
-    base = dict(N=16384, B=4, H=16, HV=16, dk=128, dv=128, pool=4, dtype=gdn.GDN_DTYPE_BF16)
+    base = dict(N=16384, B=4, H=16, HV=16, dk=128, dv=128, pool=4, dtype=gdn.GDN_DTYPE_BF16,
+                flags=0)
     base.update(kw)
     return gdn.make_problem(base["N"], base["B"], base["H"], base["HV"], base["dk"], base["dv"],
-                            base["pool"], base["dtype"])
+                            base["pool"], base["dtype"], base["flags"])
 
 
 def test_workspace_size():
     ws = gdn.gdn_prefill_workspace_size(prob())
     assert ws > 0 and ws % 256 == 0
+    # the chunk-everything flag needs no other workspace (the bound covers every request)
+    assert gdn.gdn_prefill_workspace_size(prob(flags=gdn.GDN_FLAG_CHUNK_ALL)) == ws
+    assert gdn.gdn_prefill_workspace_size(prob(flags=2)) == 0
     # grows with the chunk upper bound N / C + B
     assert gdn.gdn_prefill_workspace_size(prob(B=40)) > ws
     assert gdn.gdn_prefill_workspace_size(prob(), 32) == 0          # only C = 64
@@ -83,6 +87,8 @@ def test_error_paths_return_before_launch():
     assert call(prob(dk=96)) == gdn.GDN_ERR_UNSUPPORTED
     assert call(prob(dv=512)) == gdn.GDN_ERR_UNSUPPORTED
     assert call(prob(pool=0)) == gdn.GDN_ERR_INVALID_ARG
+    assert call(prob(flags=2)) == gdn.GDN_ERR_INVALID_ARG     # an undefined flag bit
+    assert call(prob(flags=1 | 4)) == gdn.GDN_ERR_INVALID_ARG
     assert call(prob(), nonnull=False) == gdn.GDN_ERR_INVALID_ARG
     assert call(prob(), ws_bytes=1024) == gdn.GDN_ERR_WORKSPACE
     assert call(prob(), ws_ptr=(1 << 20) + 64) == gdn.GDN_ERR_WORKSPACE   # not 256-aligned
@@ -245,3 +251,10 @@ def test_recurrent_error_paths_return_before_launch():
     lib = gdn.load_library()
     assert lib.gdn_recurrent_fwd(None, None, None, None, None, None, None, None, None, None, None,
                                  None, None) == gdn.GDN_ERR_INVALID_ARG
+
+
+def test_header_constants_match_the_binding():
+    text = open(HEADER).read()
+    for name in ("GDN_FLAG_CHUNK_ALL", "GDN_SHORT_REQUEST"):
+        m = re.search(rf"#define {name} (\d+)", text)
+        assert m and int(m.group(1)) == getattr(gdn, name), name

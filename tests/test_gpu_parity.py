@@ -288,3 +288,42 @@ def test_error_leaves_buffers_untouched():
     torch.cuda.synchronize()
     assert torch.all(out == 7.0)
     np.testing.assert_array_equal(d["state_pool"].cpu().numpy(), p.state_pool)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_short_requests_take_the_token_recurrence(dtype):
+    """Requests of at most GDN_SHORT_REQUEST tokens are evaluated by the token recurrence
+    inside gdn_prefill_fwd, longer ones in chunks. Both sides of the threshold, with an
+    empty request, match the oracle with and without GDN_FLAG_CHUNK_ALL; the short
+    requests' results equal gdn_recurrent_fwd's bit for bit, and the long ones' equal the
+    chunk-everything call's bit for bit."""
+    import torch
+    import gated_deltanet_prefill_gdn_amd as gdn
+    S = gdn.GDN_SHORT_REQUEST
+    lengths = [1, S - 1, S, S + 1, 0, 3, 2 * S + 5, 150, S, 64]
+    pool = len(lengths) + 2
+    p = gdn_synth.make_problem(77, lengths, 2, 4, 128, 128, dtype=dtype, pool=pool,
+                               cache_indices=list(range(pool - 1, 1, -1))[:len(lengths)],
+                               state_std=0.3)
+    ref = oracle.prefill(p)
+    out_d, pool_d, _ = run_gpu(p, f"split-{dtype}")
+    compare(p, out_d, pool_d, ref)
+    out_c, pool_c, _ = run_gpu(p, f"chunk-all-{dtype}", flags=gdn.GDN_FLAG_CHUNK_ALL)
+    compare(p, out_c, pool_c, ref)
+    d = to_device(p)
+    announce(f"split-{dtype} gdn_recurrent_fwd")
+    o_r = gdn.gdn_recurrent_fwd(d["q"], d["k"], d["v"], d["a"], d["b"], d["A_log"],
+                                d["dt_bias"], d["state_pool"], d["cache_indices"],
+                                d["cu_seqlens"])
+    torch.cuda.synchronize()
+    out_r = o_r.float().cpu().numpy().astype(np.float64)
+    pool_r = d["state_pool"].cpu().numpy()
+    cu = p.cu_seqlens
+    for bi, L in enumerate(lengths):
+        rows, slot = slice(int(cu[bi]), int(cu[bi + 1])), int(p.cache_indices[bi])
+        if 0 < L <= S:
+            np.testing.assert_array_equal(out_d[rows], out_r[rows])
+            np.testing.assert_array_equal(pool_d[slot], pool_r[slot])
+        elif L > S:
+            np.testing.assert_array_equal(out_d[rows], out_c[rows])
+            np.testing.assert_array_equal(pool_d[slot], pool_c[slot])

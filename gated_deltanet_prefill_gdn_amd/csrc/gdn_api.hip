@@ -13,6 +13,7 @@
 #include "gdn_internal.h"
 
 static_assert(gdn::kShortRequest == GDN_SHORT_REQUEST, "one threshold");
+static_assert(gdn::kSplitMeanLength == GDN_SPLIT_MEAN_LENGTH, "one threshold");
 
 namespace gdn {
 
@@ -178,7 +179,7 @@ gdn_status_t run_prefill(const void* q, const void* k, const void* v, const floa
   if (path == Path::kMfma && !aligned) return GDN_ERR_INVALID_ARG;
   // Short requests go to the token recurrence (its 16-byte loads need the alignment; the
   // fp32 chunked kernels do not, and take every request otherwise).
-  const bool split = (prob->flags & GDN_FLAG_CHUNK_ALL) == 0;
+  const bool split = (prob->flags & GDN_FLAG_CHUNK_ALL) == 0 && s.N <= kSplitMeanLength * s.B;
   s.short_len = (split && aligned && decode_blocks(s) <= 0x7FFFFFFF) ? kShortRequest : 0;
   if (events) {
     for (int i = 0; i <= GDN_NUM_STAGES; ++i)

@@ -58,6 +58,10 @@ struct Shape {
 // short ones (whose call still launches the chunked kernels, which find nothing to do)
 // 0.53 ms at 1, 1.36 ms at 12 and 1.68 ms at 16.
 constexpr int64_t kShortRequest = 12;  // GDN_SHORT_REQUEST of the public header
+// The recurrence's launch costs a few microseconds even when it finds no short request
+// (5 us at 8 requests and 32 value heads), so a call splits only when the mean request
+// length N / B is at most this; longer batches are chunked whole.
+constexpr int64_t kSplitMeanLength = 64;  // GDN_SPLIT_MEAN_LENGTH of the public header
 
 // Chunks of a request of L tokens on the chunked path: none if L <= short_len.
 __host__ __device__ __forceinline__ int64_t path_chunks(int64_t L, int C, int64_t short_len) {

@@ -20,8 +20,9 @@
  * triangular inverse M^-1 = (I + tril(B K K^T, -1))^-1 per chunk, reused for the
  * decayed inverse N^-1 = G M^-1 G^-1 (same page, section Save one invert), then a
  * sequential pass over chunks for the state and the outputs (pymllm page,
- * Algorithm). Requests of at most GDN_SHORT_REQUEST tokens are evaluated token by token
- * instead, in the same call, unless the descriptor's flags say GDN_FLAG_CHUNK_ALL.
+ * Algorithm). In batches of short requests on average, requests of at most
+ * GDN_SHORT_REQUEST tokens are evaluated token by token instead, in the same call, unless
+ * the descriptor's flags say GDN_FLAG_CHUNK_ALL.
  *
  * Layouts: every tensor is dense, contiguous, row-major.
  *   q, k        [N, H, dk]     fp32 or bf16 (qkv_dtype)
@@ -82,12 +83,14 @@ typedef struct {
 } gdn_problem_t;
 
 /* gdn_problem_t.flags. GDN_FLAG_CHUNK_ALL: gdn_prefill_fwd evaluates every request in
- * chunks. By default requests of at most GDN_SHORT_REQUEST tokens are evaluated by the
- * token recurrence instead (the kernel of gdn_recurrent_fwd, in the same call and on the
- * same stream), which is faster for them: a request that short still costs the chunked
- * path a whole chunk of intermediates per value head. Any other bit is an error. */
+ * chunks. By default, in a batch whose mean request length N / B is at most
+ * GDN_SPLIT_MEAN_LENGTH tokens, requests of at most GDN_SHORT_REQUEST tokens are evaluated
+ * by the token recurrence instead (the kernel of gdn_recurrent_fwd, in the same call and
+ * on the same stream), which is faster for them: a request that short still costs the
+ * chunked path a whole chunk of intermediates per value head. Any other bit is an error. */
 #define GDN_FLAG_CHUNK_ALL 1
 #define GDN_SHORT_REQUEST 12
+#define GDN_SPLIT_MEAN_LENGTH 64
 
 /* Bytes of device workspace gdn_prefill_fwd needs for this problem and chunk size,
  * or 0 if the problem or chunk size is invalid. Host only, no HIP calls. */
@@ -96,10 +99,11 @@ size_t gdn_prefill_workspace_size(const gdn_problem_t* prob, int32_t chunk_size)
 /* The prefill forward (see the top of this file). chunk_size must be 64.
  * workspace: device memory of at least gdn_prefill_workspace_size bytes, 256-byte
  * aligned; its contents on entry do not matter. stream: a hipStream_t or NULL.
- * Requests of 1 .. GDN_SHORT_REQUEST tokens run through the token recurrence (the kernel
- * of gdn_recurrent_fwd, fp32) and longer ones through the chunked kernels, unless
- * prob->flags has GDN_FLAG_CHUNK_ALL or q, k, v, out or state_pool is not 16-byte aligned
- * (then every request is chunked; the bf16 path requires that alignment anyway).
+ * When N <= GDN_SPLIT_MEAN_LENGTH * B, requests of 1 .. GDN_SHORT_REQUEST tokens run
+ * through the token recurrence (the kernel of gdn_recurrent_fwd, fp32) and longer ones
+ * through the chunked kernels, unless prob->flags has GDN_FLAG_CHUNK_ALL or q, k, v, out
+ * or state_pool is not 16-byte aligned; otherwise every request is chunked (the bf16
+ * path requires that alignment anyway).
  *
  * Magnitude range of bf16 inputs. The state and every output are accumulated in fp32,
  * but the bf16 path rounds its per-chunk intermediates to fp16 for the matrix cores:

@@ -255,6 +255,6 @@ def test_recurrent_error_paths_return_before_launch():
 
 def test_header_constants_match_the_binding():
     text = open(HEADER).read()
-    for name in ("GDN_FLAG_CHUNK_ALL", "GDN_SHORT_REQUEST"):
+    for name in ("GDN_FLAG_CHUNK_ALL", "GDN_SHORT_REQUEST", "GDN_SPLIT_MEAN_LENGTH"):
         m = re.search(rf"#define {name} (\d+)", text)
         assert m and int(m.group(1)) == getattr(gdn, name), name

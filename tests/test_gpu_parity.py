@@ -292,15 +292,17 @@ def test_error_leaves_buffers_untouched():
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_short_requests_take_the_token_recurrence(dtype):
-    """Requests of at most GDN_SHORT_REQUEST tokens are evaluated by the token recurrence
-    inside gdn_prefill_fwd, longer ones in chunks. Both sides of the threshold, with an
-    empty request, match the oracle with and without GDN_FLAG_CHUNK_ALL; the short
-    requests' results equal gdn_recurrent_fwd's bit for bit, and the long ones' equal the
-    chunk-everything call's bit for bit."""
+    """In a batch of mean length at most GDN_SPLIT_MEAN_LENGTH, requests of at most
+    GDN_SHORT_REQUEST tokens are evaluated by the token recurrence inside gdn_prefill_fwd,
+    longer ones in chunks. Both sides of the threshold, with an empty request, match the
+    oracle with and without GDN_FLAG_CHUNK_ALL; the short requests' results equal
+    gdn_recurrent_fwd's bit for bit, and the long ones' equal the chunk-everything call's
+    bit for bit."""
     import torch
     import gated_deltanet_prefill_gdn_amd as gdn
     S = gdn.GDN_SHORT_REQUEST
     lengths = [1, S - 1, S, S + 1, 0, 3, 2 * S + 5, 150, S, 64]
+    assert sum(lengths) <= gdn.GDN_SPLIT_MEAN_LENGTH * len(lengths)
     pool = len(lengths) + 2
     p = gdn_synth.make_problem(77, lengths, 2, 4, 128, 128, dtype=dtype, pool=pool,
                                cache_indices=list(range(pool - 1, 1, -1))[:len(lengths)],
@@ -327,3 +329,17 @@ def test_short_requests_take_the_token_recurrence(dtype):
         elif L > S:
             np.testing.assert_array_equal(out_d[rows], out_c[rows])
             np.testing.assert_array_equal(pool_d[slot], pool_c[slot])
+
+
+def test_long_batches_are_chunked_whole():
+    """Above the mean length GDN_SPLIT_MEAN_LENGTH the call chunks every request, short
+    ones included: its results equal the chunk-everything call's bit for bit."""
+    import gated_deltanet_prefill_gdn_amd as gdn
+    lengths = [5, 300, 1]
+    assert sum(lengths) > gdn.GDN_SPLIT_MEAN_LENGTH * len(lengths)
+    p = gdn_synth.make_problem(78, lengths, 1, 2, 64, 64, dtype="bf16", state_std=0.3)
+    out_d, pool_d, _ = run_gpu(p, "long-batch")
+    compare(p, out_d, pool_d, oracle.prefill(p))
+    out_c, pool_c, _ = run_gpu(p, "long-batch-chunk-all", flags=gdn.GDN_FLAG_CHUNK_ALL)
+    np.testing.assert_array_equal(out_d, out_c)
+    np.testing.assert_array_equal(pool_d, pool_c)

@@ -78,20 +78,24 @@ def stage_bytes(p, s_qkv: int, s_ws: int, n_chunks: int):
 
 DECODE_SOURCES = ("gdn_decode.hip", "gdn_internal.h")
 PROMOTE_SOURCES = ("gdn_promote.hip", "gdn_internal.h", "gdn_mfma.h")
+BACKWARD_SOURCES = ("gdn_backward.hip", "gdn_internal.h", "gdn_plan_gate.hip")
 
 
 def kernel_source_hash(kind: str = "prefill") -> str:
     """sha256[:16] over the kernel sources a measurement depends on: for "prefill" every
-    .hip / .h file of csrc except the decode and Promote kernels' own files, for "decode"
-    DECODE_SOURCES, for "promote" PROMOTE_SOURCES."""
+    .hip / .h file of csrc except the decode, Promote and backward kernels' own files, for
+    "decode" DECODE_SOURCES, for "promote" PROMOTE_SOURCES, for "backward"
+    BACKWARD_SOURCES."""
     csrc = os.path.join(ROOT, "gated_deltanet_prefill_gdn_amd", "csrc")
     if kind == "decode":
         files = sorted(DECODE_SOURCES)
     elif kind == "promote":
         files = sorted(PROMOTE_SOURCES)
+    elif kind == "backward":
+        files = sorted(BACKWARD_SOURCES)
     else:
         files = sorted(f for f in os.listdir(csrc) if f.endswith((".hip", ".h"))
-                       and f not in ("gdn_decode.hip", "gdn_promote.hip"))
+                       and f not in ("gdn_decode.hip", "gdn_promote.hip", "gdn_backward.hip"))
     h = hashlib.sha256()
     for f in files:
         h.update(f.encode())
@@ -888,6 +892,17 @@ def backward_bytes(p, s_qkv: int) -> int:
             + 3 * p.B * p.HV * p.dv * p.dk * 4)
 
 
+def backward_flops(p) -> float:
+    """Algorithmic flops of one backward call: per token and value head the forward step
+    (S k and the rank-one update: 4 dv dk) and the reverse step of the recurrence (D += do
+    q^T, S^T do, D k, S_{t-1} k, <D, S_{t-1}>, the three products of dk, and the update of D:
+    19 dv dk), 23 dv dk in all; the per-token gates and norms are left out."""
+    return 23.0 * p.N * p.HV * p.dv * p.dk
+
+
+FP32_VALU_PEAK_TFLOPS = 157.3   # MI355X published vector fp32 (with packed math)
+
+
 def backward_cpu_baseline(p, heads, reps: int = 1):
     """The backward oracle (fp64 numpy reverse mode) as it stands, on a sample of value
     heads; tokens/s scaled to every head."""
@@ -966,6 +981,9 @@ def bench_backward(args):
         torch.cuda.synchronize()
         del src, dst
     nbytes = backward_bytes(p, 2)
+    flops = backward_flops(p)
+    src_hash = kernel_source_hash("backward")
+    ctr = stored_counters("bwd_rows_kernel", "backward_" + workload_tag(p), src_hash)
     res = {
         "metric": BACKWARD_METRIC,
         "value": p.N / (ms_per_step * 1e-3),
@@ -982,13 +1000,21 @@ def bench_backward(args):
                 "torch.randn seed 5)",
         "config": {"workload": gdn_synth.WORKLOADS[WORKLOAD_INDEX], "global_batch": p.B,
                    "seq_len": int(p.N // p.B), "parallelism": "none (1 GPU)"},
-        "roofline": {"bound": "hbm", "kernel": "gdn_prefill_bwd (all kernels)",
-                     "achieved": nbytes / (launch_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": nbytes / (launch_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                     "traffic": None, "algorithmic_bytes_per_launch": nbytes,
+        # The call is bound by the fp32 vector arithmetic of its token recurrence (the row
+        # kernel is about 95% of it); its time is the whole call's, on the launch stream.
+        "roofline": {"bound": "alu", "kernel": "gdn_prefill_bwd (bwd_rows_kernel and the "
+                                               "small token, finish and gate kernels)",
+                     "achieved": flops / (launch_ms * 1e-3) / 1e12,
+                     "peak": FP32_VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": flops / (launch_ms * 1e-3) / 1e12 / FP32_VALU_PEAK_TFLOPS,
+                     "traffic": ctr.get("hbm_bytes_per_launch") if ctr else None,
+                     "traffic_kernel": "bwd_rows_kernel",
+                     "algorithmic_flops_per_launch": flops,
+                     "algorithmic_bytes_per_launch": nbytes,
+                     "hbm_frac": nbytes / (launch_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                      "avg_launch_ms": launch_ms, "avg_launch_ms_events": events_ms,
                      "event_pair_ms": pair_ms},
-        "kernel_source_hash": kernel_source_hash(),
+        "kernel_source_hash": src_hash,
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = backward_cpu_baseline(p, heads=[0])

@@ -19,14 +19,16 @@
 //   token   one wave per (token, q/k head): the normalised q and k rows and, for the value
 //           heads sharing them, alpha and beta, written once so that the sweeps below only
 //           load them.
-//   rows    one workgroup per (request, value head, 16 rows). A forward sweep keeps the
-//           rows' state every 16 tokens; the reverse sweep recomputes 16 tokens at a time
-//           from the checkpoint before them, holds the states before each of them in
-//           registers (the state after token i is the one before token i + 1, or the
-//           sub-chunk's end state), and walks them backwards. Wave w holds rows 4w .. 4w+3,
-//           lane l the dk elements l + 64 e. Row dot products are wave sums; the per-token
-//           sums over the 16 rows go through LDS into a partial buffer per row block (no
-//           atomics: the result does not depend on scheduling).
+//   rows    one workgroup per (request, value head, 16 rows), eight waves. A forward sweep
+//           keeps the rows' state every 8 tokens; the reverse sweep recomputes 8 tokens at a
+//           time (4 at dk = 256) from the checkpoint before them, holds the states before
+//           each of them in registers (the state after token i is the one before token
+//           i + 1, or the sub-chunk's end state), and walks them backwards. Wave w holds
+//           rows 2w and 2w + 1, lane l the dk elements l + 64 e: few registers per wave, so
+//           four waves share each SIMD and hide the latency of the token-to-token chain.
+//           Row dot products are wave sums; the per-token sums over the 16 rows go through
+//           LDS into a partial buffer per row block (no atomics: the result does not depend
+//           on scheduling).
 //   finish  one wave per (token, q/k head): sums the partials over row blocks and over
 //           the value heads that share the q/k head, then the chain rule through the L2
 //           norm (dq = dqh / n - q (q . dqh) / n^3) and the gates (da = dalpha dalpha/dx,
@@ -39,31 +41,31 @@
 namespace gdn {
 namespace {
 
-constexpr int kCk = 16;            // tokens between checkpoints
+constexpr int kCk = 8;             // tokens between checkpoints
 constexpr int kBwdRows = 16;       // state rows per workgroup
-constexpr int kRowsPerWave = 4;
+constexpr int kRowsPerWave = 2;
+constexpr int kRowWaves = kBwdRows / kRowsPerWave;  // waves of a row workgroup
+constexpr int kRowThreads = 64 * kRowWaves;
 template <int DK>
-constexpr int kSub = DK <= 128 ? 16 : 8;  // tokens recomputed and walked back at a time
+constexpr int kSub = DK <= 128 ? 8 : 4;  // tokens recomputed and walked back at a time
 
 __device__ __forceinline__ float ldx(const void* p, int64_t i, bool bf16) {
   return bf16 ? __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(p)[i] << 16)
               : reinterpret_cast<const float*>(p)[i];
 }
 
-// Four consecutive elements starting at a multiple of 4 (8- or 16-byte aligned).
-__device__ __forceinline__ void ld4(const void* p, int64_t i, bool bf16, float (&x)[4]) {
+// kRowsPerWave (2) consecutive elements starting at a multiple of 2 (4- or 8-byte aligned).
+__device__ __forceinline__ void ld_rows(const void* p, int64_t i, bool bf16,
+                                        float (&x)[kRowsPerWave]) {
+  static_assert(kRowsPerWave == 2, "one 2-element load");
   if (bf16) {
-    const uint2 u = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(p) + i);
-    x[0] = __uint_as_float(u.x << 16);
-    x[1] = __uint_as_float(u.x & 0xFFFF0000u);
-    x[2] = __uint_as_float(u.y << 16);
-    x[3] = __uint_as_float(u.y & 0xFFFF0000u);
+    const uint32_t u = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint16_t*>(p) + i);
+    x[0] = __uint_as_float(u << 16);
+    x[1] = __uint_as_float(u & 0xFFFF0000u);
   } else {
-    const float4 f = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(p) + i);
+    const float2 f = *reinterpret_cast<const float2*>(reinterpret_cast<const float*>(p) + i);
     x[0] = f.x;
     x[1] = f.y;
-    x[2] = f.z;
-    x[3] = f.w;
   }
 }
 
@@ -171,7 +173,7 @@ __device__ __forceinline__ void fetch(const BwdArgs& A, int64_t t, int h, int hv
   const float2 ab = *reinterpret_cast<const float2*>(A.ab + (t * A.HV + hv) * 2);
   x.alpha = ab.x;
   x.beta = ab.y;
-  ld4(A.v, (t * A.HV + hv) * (int64_t)A.DV + row0, A.bf16, x.v);
+  ld_rows(A.v, (t * A.HV + hv) * (int64_t)A.DV + row0, A.bf16, x.v);
 }
 
 // One token's step on this wave's rows: s <- alpha s - alpha beta (s kh) kh + beta v kh.
@@ -191,11 +193,11 @@ __device__ __forceinline__ void step(const Token<DK>& x, float (&s)[kRowsPerWave
 }
 
 template <int DK>
-__global__ __launch_bounds__(256) void bwd_rows_kernel(BwdArgs A) {
+__global__ __launch_bounds__(kRowThreads) void bwd_rows_kernel(BwdArgs A) {
   constexpr int E = DK / 64;
   constexpr int SUB = kSub<DK>;
   constexpr int NF = 2 * DK + 2;  // fields per token of a partial: dqh, dkh, dalpha, dbeta
-  __shared__ float part[4][SUB][NF];
+  __shared__ float part[kRowWaves][SUB][NF];
   const int tid = threadIdx.x, l = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nrb = A.DV / kBwdRows;
@@ -278,14 +280,14 @@ __global__ __launch_bounds__(256) void bwd_rows_kernel(BwdArgs A) {
     // step fetches the one before it.
     fetch<DK>(A, t0 + u_hi - 1, h, hv, row0, l, tk);
     float dO[kRowsPerWave], dOn[kRowsPerWave];
-    ld4(A.dout, ((t0 + u_hi - 1) * A.HV + hv) * (int64_t)A.DV + row0, A.bf16, dO);
+    ld_rows(A.dout, ((t0 + u_hi - 1) * A.HV + hv) * (int64_t)A.DV + row0, A.bf16, dO);
 #pragma clang loop unroll(full)
     for (int i = SUB - 1; i >= 0; --i) {
       if (u_lo + i >= u_hi) continue;  // past the request's end (uniform)
       const int64_t t = t0 + u_lo + i;
       const int64_t tp = t0 + u_lo + max(i - 1, 0);
       fetch<DK>(A, tp, h, hv, row0, l, nx);
-      ld4(A.dout, (tp * A.HV + hv) * (int64_t)A.DV + row0, A.bf16, dOn);
+      ld_rows(A.dout, (tp * A.HV + hv) * (int64_t)A.DV + row0, A.bf16, dOn);
       // S_t: the state before the next token, or the sub-chunk's end state
       const bool last = (i == SUB - 1) || (u_lo + i + 1 >= u_hi);
       float dqh[E] = {}, dkh[E] = {};
@@ -316,8 +318,8 @@ __global__ __launch_bounds__(256) void bwd_rows_kernel(BwdArgs A) {
         }
       }
       if (l == 0)
-        *reinterpret_cast<float4*>(A.dv + (t * A.HV + hv) * (int64_t)A.DV + row0) =
-            make_float4(dvr[0], dvr[1], dvr[2], dvr[3]);
+        *reinterpret_cast<float2*>(A.dv + (t * A.HV + hv) * (int64_t)A.DV + row0) =
+            make_float2(dvr[0], dvr[1]);
 #pragma unroll
       for (int e = 0; e < E; ++e) {
         part[w][i][64 * e + l] = dqh[e];
@@ -334,9 +336,11 @@ __global__ __launch_bounds__(256) void bwd_rows_kernel(BwdArgs A) {
     __syncthreads();
     // this row block's partial sums for the sub-chunk's tokens
     const int nt = (int)(u_hi - u_lo);
-    for (int idx = tid; idx < nt * NF; idx += 256) {
+    for (int idx = tid; idx < nt * NF; idx += kRowThreads) {
       const int i = idx / NF, f = idx % NF;
-      const float v = part[0][i][f] + part[1][i][f] + part[2][i][f] + part[3][i][f];
+      float v = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < kRowWaves; ++ww) v += part[ww][i][f];
       A.part[(((int64_t)rb * A.N + t0 + u_lo + i) * A.HV + hv) * NF + f] = v;
     }
     __syncthreads();
@@ -456,7 +460,7 @@ BwdLayout bwd_layout_for(const Shape& s) {
 bool bwd_grids_fit(const Shape& s) {
   const int64_t rows = s.B * s.HV * (s.dv / kBwdRows);
   const int64_t fin = (s.N * s.H + 3) / 4;
-  return rows * 256 <= 0xFFFFFFFFLL && fin * 256 <= 0xFFFFFFFFLL && s.HV <= 0x7FFFFFFF;
+  return rows * kRowThreads <= 0xFFFFFFFFLL && fin * 256 <= 0xFFFFFFFFLL && s.HV <= 0x7FFFFFFF;
 }
 
 hipError_t launch_backward(const Shape& s, const BwdLayout& L, char* ws, const void* q,
@@ -511,7 +515,7 @@ hipError_t launch_backward(const Shape& s, const BwdLayout& L, char* ws, const v
 #define GDN_BWD_CASE(DKv)                                                              \
   if (s.dk == DKv) {                                                                   \
     if (s.N > 0) hipLaunchKernelGGL((bwd_token_kernel<DKv>), fin, dim3(256), 0, st, A); \
-    hipLaunchKernelGGL((bwd_rows_kernel<DKv>), rows, dim3(256), 0, st, A);             \
+    hipLaunchKernelGGL((bwd_rows_kernel<DKv>), rows, dim3(kRowThreads), 0, st, A);     \
     if ((e = hipGetLastError()) != hipSuccess) return e;                               \
     if (s.N > 0) hipLaunchKernelGGL((bwd_finish_kernel<DKv>), fin, dim3(256), 0, st, A); \
   }

@@ -128,10 +128,10 @@ hipError_t launch_chain(const ChainPlan& p, const Shape& s, const void* qf, cons
 
 // Backward of the prefill (fp32 arithmetic): workspace layout and launcher.
 struct BwdLayout {
-  int64_t max_chunks = 0;  // N / 16 + B: checkpoints per value head at most
+  int64_t max_chunks = 0;  // N / 8 + B: checkpoints per value head at most
   size_t chunk_off = 0;    // int32 [B + 1]
   size_t chunk_seq = 0;    // int32 [max_chunks]
-  size_t ck = 0;           // float [max_chunks][HV][dv][dk]: state every 16 tokens
+  size_t ck = 0;           // float [max_chunks][HV][dv][dk]: state every 8 tokens
   size_t part = 0;         // float [dv / 16][N][HV][2 dk + 2]: per-row-block token sums
   size_t dal = 0;          // float [N][HV]
   size_t qn = 0, kn = 0;   // float [N][H][dk]: normalised q and k

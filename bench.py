@@ -78,7 +78,7 @@ def stage_bytes(p, s_qkv: int, s_ws: int, n_chunks: int):
 
 DECODE_SOURCES = ("gdn_decode.hip", "gdn_internal.h")
 PROMOTE_SOURCES = ("gdn_promote.hip", "gdn_internal.h", "gdn_mfma.h")
-BACKWARD_SOURCES = ("gdn_backward.hip", "gdn_internal.h", "gdn_plan_gate.hip")
+BACKWARD_SOURCES = ("gdn_backward.hip", "gdn_backward.h", "gdn_internal.h", "gdn_plan_gate.hip")
 
 
 def kernel_source_hash(kind: str = "prefill") -> str:
@@ -95,7 +95,8 @@ def kernel_source_hash(kind: str = "prefill") -> str:
         files = sorted(BACKWARD_SOURCES)
     else:
         files = sorted(f for f in os.listdir(csrc) if f.endswith((".hip", ".h"))
-                       and f not in ("gdn_decode.hip", "gdn_promote.hip", "gdn_backward.hip"))
+                       and f not in ("gdn_decode.hip", "gdn_promote.hip", "gdn_backward.hip",
+                                     "gdn_backward.h"))
     h = hashlib.sha256()
     for f in files:
         h.update(f.encode())

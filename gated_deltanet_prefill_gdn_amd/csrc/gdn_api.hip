@@ -11,6 +11,7 @@
 
 #include "gdn.h"
 #include "gdn_internal.h"
+#include "gdn_backward.h"
 
 static_assert(gdn::kShortRequest == GDN_SHORT_REQUEST, "one threshold");
 static_assert(gdn::kSplitMeanLength == GDN_SPLIT_MEAN_LENGTH, "one threshold");

@@ -37,6 +37,7 @@
 #include <algorithm>
 
 #include "gdn_internal.h"
+#include "gdn_backward.h"
 
 namespace gdn {
 namespace {

@@ -60,7 +60,10 @@ def compare(p: gdn_synth.Problem, out_gpu, pool_gpu, ref, tol=None, heads=None, 
     Outputs: |do| <= tol_o * rms(o_oracle) + r |o_oracle| element by element, with r the
     half-ulp of the output dtype (2^-8 for bf16, 0 for fp32).
     State: for every touched slot (and compared head), ||dS||_F / ||S||_F <= tol_s.
-    Slots no request touches must equal their input bit for bit."""
+    Slots no request touches must equal their input bit for bit.
+    The report (printed) holds max|do| / rms(o), the worst element's share of its allowance,
+    the compute-only margin max(|do| - r |o|) / rms(o) (the error beyond the output's own
+    rounding, against tol_o) and the worst state error."""
     tol_o, tol_s = tol or TOL[p.dtype]
     heads = list(range(p.HV)) if heads is None else list(heads)
     r0, r1 = (0, p.dv) if rows is None else rows
@@ -75,6 +78,8 @@ def compare(p: gdn_synth.Problem, out_gpu, pool_gpu, ref, tol=None, heads=None, 
         allow = tol_o * rms + OUT_ROUNDING[p.dtype] * np.abs(o_ref)
         report["o_maxerr_over_rms"] = float(d.max()) / max(rms, 1e-30)
         report["o_worst_err_over_allowance"] = float((d / allow).max())
+        report["o_compute_over_rms"] = (float((d - OUT_ROUNDING[p.dtype] * np.abs(o_ref)).max())
+                                        / max(rms, 1e-30))
         o_ok = bool(np.all(d <= allow))
     lengths = np.diff(p.cu_seqlens)
     worst = 0.0
@@ -88,6 +93,7 @@ def compare(p: gdn_synth.Problem, out_gpu, pool_gpu, ref, tol=None, heads=None, 
         rel_err = float(np.linalg.norm(g - r) / denom) if denom > 0 else float(np.linalg.norm(g))
         worst = max(worst, rel_err)
     report["state_rel"] = worst
+    announce("margins " + ", ".join(f"{k}={v:.3g}" for k, v in report.items()))
     assert o_ok, f"output error above the bar: {report}"
     assert worst <= tol_s, f"state rel err {worst:.3e} > {tol_s}: {report}"
     touched = set(int(s) for s, L in zip(p.cache_indices, lengths) if L > 0)

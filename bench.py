@@ -831,7 +831,7 @@ def bench_prefill(args):
     import gdn_synth
 
     main_idx = args.workload if args.workload is not None else WORKLOAD_INDEX
-    p = gdn_synth.workload(main_idx)
+    p = gdn_synth.workload(main_idx, args.dtype)
     m = measure_prefill(p, args.steps, args.warmup, args.cold_steps, args.copy_calibration)
     res = {
         "metric": METRIC,
@@ -846,7 +846,9 @@ def bench_prefill(args):
         "vs_baseline": None,
         "dtype": p.dtype,
         "data": f"synthetic (seeded SplitMix64/Box-Muller, seed {p.seed})",
-        "config": {"workload": gdn_synth.WORKLOADS[main_idx], "global_batch": p.B,
+        "config": {"workload": gdn_synth.WORKLOADS[main_idx]
+                   + (f" [q, k, v, out drawn in {p.dtype}]" if args.dtype else ""),
+                   "global_batch": p.B,
                    "seq_len": int(p.N // max(p.B, 1)), "parallelism": "none (1 GPU)"},
         "roofline": m["roofline"],
         "effective": m["effective"],
@@ -860,10 +862,12 @@ def bench_prefill(args):
     if args.workload is None and not args.no_sub:
         del p
         for wi in SUB_WORKLOADS:
-            sp_ = gdn_synth.workload(wi)
+            sp_ = gdn_synth.workload(wi, args.dtype)
             sm = measure_prefill(sp_, max(3, args.steps // 2), max(3, args.warmup // 2),
                                  args.cold_steps)
-            ent = {"workload": gdn_synth.WORKLOADS[wi], "index": wi,
+            ent = {"workload": gdn_synth.WORKLOADS[wi]
+                   + (f" [q, k, v, out drawn in {sp_.dtype}]" if args.dtype else ""),
+                   "index": wi,
                    "tokens_per_s": sm["tokens_per_s"], "ms_per_step": sm["ms_per_step"],
                    "call_ms_events": sm["call_ms_events"],
                    "path_frac_hbm": sm["effective"]["frac_hbm"],
@@ -1098,6 +1102,9 @@ def main():
                          "workloads 2-4 as sub-results)")
     ap.add_argument("--no-sub", action="store_true",
                     help="skip the sub-results for workloads 2-4")
+    ap.add_argument("--dtype", choices=("bf16", "f32"), default=None,
+                    help="draw the prefill workloads with q, k, v in this dtype instead of "
+                         "their own (f32 runs the fp32-arithmetic kernels)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 512 MiB device copy (calibrates HBM byte counters)")
     args = ap.parse_args()

@@ -45,13 +45,13 @@ WsLayout layout_for(const Shape& s, Path p) {
   L.u = off;
   off = align256(off + el * mc * s.HV * s.C * s.dv);
   L.aqk = off;
-  if (p == Path::kMfma) off = align256(off + 2 * mc * s.HV * s.C * s.C);
+  off = align256(off + el * mc * s.HV * s.C * s.C);
   L.eg = off;
   if (p == Path::kMfma) off = align256(off + sizeof(float) * mc * s.HV * s.C);
   L.kf = off;
-  if (p == Path::kMfma) off = align256(off + 2 * mc * s.HV * s.C * s.dk);
-  L.qf = off;
-  if (p == Path::kMfma) off = align256(off + 2 * mc * s.H * s.C * s.dk);
+  off = align256(off + el * mc * s.HV * s.C * s.dk);
+  L.qf = off;  // per q/k head on the MFMA path, per value head (it carries e^G) on kRef
+  off = align256(off + el * mc * (p == Path::kMfma ? s.H : s.HV) * s.C * s.dk);
   const ChainPlan cp = p == Path::kMfma ? chain_plan(s) : ChainPlan{};
   L.rp = off;
   off = align256(off + chain_rp_bytes(s, cp));
@@ -74,9 +74,9 @@ static bool grid_fits(int64_t blocks, int threads) {
 static bool prefill_grids_fit(const Shape& s, Path path, int64_t max_chunks) {
   if (path == Path::kRef) {
     // gate: 4 (chunk, value head) pairs per 256-thread workgroup; ref prep: (chunk, value
-    // head) grid; ref state: (request, value head, 16 state rows) grid
+    // head) grid; ref state: (request, value head) pairs rounded up to 8, times dv / 16
     return grid_fits((max_chunks * s.HV + 3) / 4, 256) && grid_fits(max_chunks, 256) &&
-           grid_fits(s.B, 256) && s.HV <= 65535 && s.dv / 16 <= 65535;
+           s.HV <= 65535 && grid_fits((s.B * s.HV + 7) / 8 * 8 * (s.dv / 16), 256);
   }
   const ChainPlan cp = chain_plan(s);
   if (cp.use) {
@@ -245,12 +245,16 @@ gdn_status_t run_prefill(const void* q, const void* k, const void* v, const floa
         return GDN_ERR_HIP;
     }
   } else {
-    if (launch_ref_prep(k, v, cu_seqlens, chunk_off, chunk_seq, gcum, beta, s, L.max_chunks,
-                        (float*)w, (float*)u, st) != hipSuccess)
+    float* aqk = (float*)(ws + L.aqk);
+    float* kf = (float*)(ws + L.kf);
+    float* qf = (float*)(ws + L.qf);
+    if (launch_ref_prep(q, k, v, cu_seqlens, chunk_off, chunk_seq, gcum, beta, s, L.max_chunks,
+                        (float*)w, (float*)u, aqk, kf, qf, st) != hipSuccess)
       return GDN_ERR_HIP;
     if (!mark(2) || !mark(3) || !mark(4) || !short_pass()) return GDN_ERR_HIP;
-    if (launch_ref_state(q, k, cu_seqlens, cache_indices, chunk_off, gcum, (const float*)w,
-                         (const float*)u, s, state_pool, out, nonfinite, st) != hipSuccess)
+    if (launch_ref_state(cu_seqlens, cache_indices, chunk_off, gcum, (const float*)w,
+                         (const float*)u, aqk, kf, qf, s, state_pool, out, nonfinite,
+                         st) != hipSuccess)
       return GDN_ERR_HIP;
   }
   if (!mark(5)) return GDN_ERR_HIP;

@@ -26,15 +26,17 @@ struct WsLayout {
   size_t gcum = 0;         // double [max_chunks][HV][C]: chunk-local inclusive sum of log(alpha)
                            //        (kRef only: the MFMA chunk prep forms its own gates)
   size_t beta = 0;         // float  [max_chunks][HV][C]: beta (0 on padding rows) (kRef only)
-  size_t w = 0;            // W<- [max_chunks][HV][C][dk] (fp32 on kRef, fp16 on kMfma)
-  size_t u = 0;            // U~  [max_chunks][HV][C][dv] (fp32 on kRef; fp16 MFMA D tiles on
-                           //     kMfma)
-  size_t aqk = 0;          // fp16   [max_chunks][HV][C][C]: A_qk in fragment order (kMfma only)
+  size_t w = 0;            // W<- [max_chunks][HV][C][dk] (fp32 rows on kRef, fp16 fragments
+                           //     on kMfma)
+  size_t u = 0;            // U~  [max_chunks][HV]: fp32 [dv][C] (transposed) on kRef; fp16 MFMA
+                           //     D tiles on kMfma
+  size_t aqk = 0;          // A_qk [max_chunks][HV][C][C]: fp32 rows on kRef, fp16 fragments on
+                           //      kMfma
   size_t eg = 0;           // float  [max_chunks][HV][C]: e^G per chunk row (kMfma only)
-  size_t kf = 0;           // fp16   [max_chunks][HV][C][dk]: K~ = diag(e^{G_n - G} r_k) K in
-                           //        the state update's fragment order (kMfma only)
-  size_t qf = 0;           // fp16   [max_chunks][H][C][dk]: normalised q in the state
-                           //        pass's fragment order (kMfma only)
+  size_t kf = 0;           // K~ = diag(e^{G_n - G} r_k) K [max_chunks][HV]: fp32 [dk][C]
+                           //      (transposed) on kRef; fp16 [C][dk] fragments on kMfma
+  size_t qf = 0;           // kRef: fp32 [max_chunks][HV][C][dk], diag(e^G r_q) Q;
+                           // kMfma: fp16 [max_chunks][H][C][dk], normalised q in fragments
   size_t rp = 0;           // float  [segments][HV][dv + dk][dk]: each cut segment's state from
                            //        zero (R) and its operator product (P) (segment scan only)
   size_t sstart = 0;       // float  [segments][HV][dv][dk]: start state of every segment of a
@@ -78,14 +80,16 @@ hipError_t launch_gate(const float* a, const float* b, const float* A_log, const
                        const int64_t* cu_seqlens, const int32_t* chunk_off,
                        const int32_t* chunk_seq, const Shape& s, int64_t max_chunks,
                        double* gcum, float* beta, int32_t* nonfinite, hipStream_t st);
-hipError_t launch_ref_prep(const void* k, const void* v, const int64_t* cu_seqlens,
-                           const int32_t* chunk_off, const int32_t* chunk_seq, const double* gcum,
-                           const float* beta, const Shape& s, int64_t max_chunks, float* w,
-                           float* u, hipStream_t st);
-hipError_t launch_ref_state(const void* q, const void* k, const int64_t* cu_seqlens,
-                            const int64_t* cache_indices, const int32_t* chunk_off,
-                            const double* gcum, const float* w, const float* u, const Shape& s,
-                            float* state_pool, void* out, int32_t* nonfinite, hipStream_t st);
+hipError_t launch_ref_prep(const void* q, const void* k, const void* v,
+                           const int64_t* cu_seqlens, const int32_t* chunk_off,
+                           const int32_t* chunk_seq, const double* gcum, const float* beta,
+                           const Shape& s, int64_t max_chunks, float* w, float* ut, float* aqk,
+                           float* kft, float* qf, hipStream_t st);
+hipError_t launch_ref_state(const int64_t* cu_seqlens, const int64_t* cache_indices,
+                            const int32_t* chunk_off, const double* gcum, const float* w,
+                            const float* ut, const float* aqk, const float* kft, const float* qf,
+                            const Shape& s, float* state_pool, void* out, int32_t* nonfinite,
+                            hipStream_t st);
 
 // self_plan (at most kMaxSelfPlanRequests requests): the prep kernel forms the chunk table
 // itself and writes chunk_off (B + 1 entries) for the state pass; chunk_seq is then not

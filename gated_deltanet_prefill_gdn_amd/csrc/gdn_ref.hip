@@ -1,26 +1,40 @@
-// Chunkwise GDN forward in plain fp32 arithmetic (no matrix cores).
+// Chunkwise GDN forward in fp32 arithmetic: products on the fp32 matrix cores
+// (v_mfma_f32_16x16x4f32: fp32 products, fp32 sums), everything else in fp32 vector code.
 //
-// This family serves fp32 inputs, where every operand must stay in fp32. It
-// computes, per chunk of n <= C rows (row convention: S is dv x dk, K and Q are
-// n x dk, V is n x dv; G is the chunk-local inclusive log cumulative gate):
-//   A   = tril(diag(beta) Kh Kh^T, -1)            Kh = diag(r_k) K, r_k = 1/|k|
-//   T   = (I + A)^-1                               the one inverse, M^-1
-//   W<- = diag(e^G) T diag(beta) Kh                W up to the decay (veitner page,
+// This family serves fp32 inputs, where every operand must stay in fp32. Per chunk of
+// n <= C rows (row convention: S is dv x dk, K and Q are n x dk, V is n x dv; G is the
+// chunk-local inclusive log cumulative gate, r_k = 1/|k| and r_q = 1/|q|):
+//   A    = tril(diag(beta r_k) K K^T diag(r_k), -1)
+//   T    = (I + A)^-1                              the one inverse, M^-1
+//   W<-  = diag(e^G) T diag(beta r_k) K            W up to the decay (veitner page,
 //                                                  Reminder, equation for W)
-//   U~  = (Gamma o T) diag(beta) V,  Gamma_ri = exp(G_r - G_i) for i <= r
-//         This is N^-1 B V with N^-1 = G M^-1 G^-1 (veitner page, Save one invert),
-//         applied entry by entry so no 1/gamma is formed.
-// and then, sequentially over the chunks of a request (pymllm gdn_chunkwise page,
-// Algorithm, steps 2 and 3, in row convention):
+//   U~   = (Gamma o T) diag(beta) V,  Gamma_ri = exp(G_r - G_i) for i <= r
+//          This is N^-1 B V with N^-1 = G M^-1 G^-1 (veitner page, Save one invert),
+//          applied entry by entry so no 1/gamma is formed.
+//   A_qk = Gamma o tril0(diag(r_q) Q K^T diag(r_k)),  K~ = diag(e^{G_n - G} r_k) K,
+//   Qf   = diag(e^G r_q) Q
+// (the prep kernel, one workgroup per chunk and value head), and then, sequentially over
+// the chunks of a request (pymllm gdn_chunkwise page, Algorithm, steps 2 and 3, in row
+// convention; the state kernel, one workgroup per request, value head and 16 state rows):
 //   U     = U~ - W<- S^T
-//   O     = diag(e^G) Qh S^T + (Gamma o tril0(Qh Kh^T)) U
-//   S_new = e^{G_n} S + U^T diag(e^{G_n - G}) Kh
+//   O     = Qf S^T + A_qk U
+//   S_new = e^{G_n} S + U^T K~
+//
+// Contraction order. In v_mfma_f32_16x16x4f32 lane (m, g) supplies A[m][k] and B[k][m] for
+// the step's k = g. Over a block of 16 contraction indices these kernels let step s take
+// k = 4g + s (s = 0..3), so each lane's four values of A (and of B) for four consecutive
+// steps are four consecutive floats: one 16-byte load instead of four. The operands are
+// stored (or staged) so that those runs are contiguous: U~ and K~ are written transposed,
+// and U is kept transposed in LDS.
 #include "gdn_internal.h"
+#include "gdn_mfma.h"
 
 namespace gdn {
 namespace {
 
+using namespace mfma;
 constexpr int C = 64;
+constexpr int kBV = 16;  // state rows (dv index) per state workgroup
 
 template <typename T>
 __device__ __forceinline__ float ld(const T* p, int64_t i);
@@ -30,46 +44,48 @@ template <>
 __device__ __forceinline__ float ld<__hip_bfloat16>(const __hip_bfloat16* p, int64_t i) {
   return __bfloat162float(p[i]);
 }
+// Four consecutive input elements from index i (the inputs need no alignment on this path).
+template <typename T>
+__device__ __forceinline__ f32x4 ld4(const T* p, int64_t i) {
+  return f32x4{ld(p, i), ld(p, i + 1), ld(p, i + 2), ld(p, i + 3)};
+}
 __device__ __forceinline__ void st(float* p, int64_t i, float x) { p[i] = x; }
 __device__ __forceinline__ void st(__hip_bfloat16* p, int64_t i, float x) {
   p[i] = __float2bfloat16(x);  // round to nearest even
 }
 
-__device__ __forceinline__ float wave_sum(float x) {
-  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
-  return x;
+// Four fp32 MFMA steps over 16 contraction indices: step s takes k = 4g + s.
+__device__ __forceinline__ f32x4 mma4(f32x4 a, f32x4 b, f32x4 acc) {
+  acc = mma_f32(a[0], b[0], acc);
+  acc = mma_f32(a[1], b[1], acc);
+  acc = mma_f32(a[2], b[2], acc);
+  acc = mma_f32(a[3], b[3], acc);
+  return acc;
 }
 
-// Inverse L2 norms of rows [0, n) of a chunk: s_r[r] = 1 / sqrt(|x_r|^2 + eps).
-template <typename Tin>
-__device__ void row_inv_norms(const Tin* x, int64_t t0, int n, int heads, int h, int d,
-                              float* s_r) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  for (int r = wave; r < C; r += 4) {
-    float acc = 0.f;
-    if (r < n) {
-      const int64_t base = ((t0 + r) * heads + h) * (int64_t)d;
-      for (int j = lane; j < d; j += 64) {
-        const float e = ld(x, base + j);
-        acc += e * e;
-      }
-    }
-    acc = wave_sum(acc);
-    if (lane == 0) s_r[r] = r < n ? (float)(1.0 / sqrt((double)acc + (double)kNormEps)) : 0.f;
-  }
-}
+template <int DM>
+struct RefPrepSmem {
+  float tile[C][DM + 4];  // K rows (zero past n), later V rows
+  float A[C][C + 4];      // A, then T1 = diag(e^G) T diag(beta r_k), then T2
+  float T[C][C + 4];      // T = (I + A)^-1
+  float X[4][16][20];     // per wave: one 16 x 16 tile of the blocked inverse
+  double G[C];
+  float bt[C], rk[C], rq[C], kd[C], eq[C];
+};
 
-// One workgroup per (global chunk, value head).
-template <typename Tin>
+// One workgroup per (global chunk, value head); wave w owns chunk rows 16w .. 16w + 15.
+// Head dims are compile-time constants, so every staging loop has a fixed trip count and
+// issues its loads together.
+template <typename Tin, int DK, int DV>
 __global__ __launch_bounds__(256) void ref_prep_kernel(
-    const Tin* __restrict__ k, const Tin* __restrict__ v, const int64_t* __restrict__ cu,
-    const int32_t* __restrict__ chunk_off, const int32_t* __restrict__ chunk_seq,
-    const double* __restrict__ gcum, const float* __restrict__ beta, int H, int HV, int dk,
-    int dv, float* __restrict__ W, float* __restrict__ U) {
-  __shared__ float s_rk[C], s_bt[C];
-  __shared__ double s_G[C];
-  __shared__ float s_A[C][C + 1];
-  __shared__ float s_T[C][C + 1];
+    const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* __restrict__ v,
+    const int64_t* __restrict__ cu, const int32_t* __restrict__ chunk_off,
+    const int32_t* __restrict__ chunk_seq, const double* __restrict__ gcum,
+    const float* __restrict__ beta, int H, int HV, float* __restrict__ W,
+    float* __restrict__ Ut, float* __restrict__ Aqk, float* __restrict__ Kft,
+    float* __restrict__ Qf) {
+  constexpr int dk = DK, dv = DV;
+  __shared__ RefPrepSmem<(DK > DV ? DK : DV)> sm;
   const int64_t c = blockIdx.x;
   const int hv = blockIdx.y;
   const int32_t seq = chunk_seq[c];
@@ -78,208 +94,440 @@ __global__ __launch_bounds__(256) void ref_prep_kernel(
   const int64_t t0 = cu[seq] + (int64_t)(c - chunk_off[seq]) * C;
   const int n = (int)min((int64_t)C, cu[seq + 1] - t0);
   const int64_t pair = c * HV + hv;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, m = l & 15, g = l >> 4;
+  const int I = w;  // this wave's row tile
+
   if (tid < C) {
-    s_G[tid] = gcum[pair * C + tid];
-    s_bt[tid] = beta[pair * C + tid];
+    sm.G[tid] = gcum[pair * C + tid];
+    sm.bt[tid] = beta[pair * C + tid];
   }
-  row_inv_norms(k, t0, n, H, h, dk, s_rk);
-  __syncthreads();
-  // A = tril(diag(beta) Kh Kh^T, -1)
-  for (int idx = tid; idx < C * C; idx += 256) {
-    const int r = idx / C, i = idx % C;
-    float val = 0.f;
-    if (i < r && r < n) {
-      const int64_t br = ((t0 + r) * H + h) * (int64_t)dk, bi = ((t0 + i) * H + h) * (int64_t)dk;
-      float acc = 0.f;
-      for (int j = 0; j < dk; ++j) acc += ld(k, br + j) * ld(k, bi + j);
-      val = s_bt[r] * s_rk[r] * s_rk[i] * acc;
-    }
-    s_A[r][i] = val;
-  }
-  __syncthreads();
-  // T = (I + A)^-1 by forward substitution; thread `col` owns column col, so the
-  // column it reads back is the one it wrote.
-  if (tid < C) {
-    const int col = tid;
-    for (int r = 0; r < C; ++r) {
-      float val;
-      if (r < col) {
-        val = 0.f;
-      } else if (r == col) {
-        val = 1.f;
-      } else {
-        float acc = 0.f;
-        for (int i = col; i < r; ++i) acc += s_A[r][i] * s_T[i][col];
-        val = -acc;
-      }
-      s_T[r][col] = val;
-    }
-  }
-  __syncthreads();
-  // W<- = diag(e^G) T diag(beta r_k) K
-  for (int idx = tid; idx < C * C; idx += 256) {
-    const int r = idx / C, i = idx % C;
-    s_A[r][i] = (i <= r && r < n) ? expf((float)s_G[r]) * s_T[r][i] * s_bt[i] * s_rk[i] : 0.f;
-  }
-  __syncthreads();
-  float* Wp = W + pair * C * (int64_t)dk;
+#pragma unroll
   for (int idx = tid; idx < C * dk; idx += 256) {
-    const int r = idx / dk, j = idx % dk;
-    float acc = 0.f;
-    for (int i = 0; i <= r && i < n; ++i) acc += s_A[r][i] * ld(k, ((t0 + i) * H + h) * (int64_t)dk + j);
-    Wp[idx] = acc;
+    const int r = idx / dk, j = idx - r * dk;
+    sm.tile[r][j] = r < n ? ld(k, ((t0 + r) * H + h) * (int64_t)dk + j) : 0.f;
+  }
+  // This lane's fragments of Q: row qr = 16 I + m, columns 16 kb + 4g .. 16 kb + 4g + 3
+  // (zero past n), the A operand of A_qk and the source of Qf. Q is read once.
+  const int qr = 16 * I + m;
+  f32x4 qa[dk / 16];
+#pragma unroll
+  for (int kb = 0; kb < dk / 16; ++kb)
+    qa[kb] = qr < n ? ld4(q, ((t0 + qr) * H + h) * (int64_t)dk + 16 * kb + 4 * g)
+                    : f32x4{0.f, 0.f, 0.f, 0.f};
+  // V rows, loaded now and staged in LDS once the K tile is no longer read
+  constexpr int kVPer = C * dv / 256;
+  float vr[kVPer];
+#pragma unroll
+  for (int i = 0; i < kVPer; ++i) {
+    const int idx = tid + 256 * i, r = idx / dv, j = idx - r * dv;
+    vr[i] = r < n ? ld(v, ((t0 + r) * HV + hv) * (int64_t)dv + j) : 0.f;
   }
   __syncthreads();
-  // U~ = (Gamma o T) diag(beta) V
+  // inverse row norms: lane (m, g) sums its columns of row qr, the four lanes of a row add up
+  {
+    float ak = 0.f, aq = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < dk / 16; ++kb) {
+      const f32x4 x = *reinterpret_cast<const f32x4*>(&sm.tile[qr][16 * kb + 4 * g]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        ak += x[e] * x[e];
+        aq += qa[kb][e] * qa[kb][e];
+      }
+    }
+    ak += __shfl_xor(ak, 16, 64);
+    ak += __shfl_xor(ak, 32, 64);
+    aq += __shfl_xor(aq, 16, 64);
+    aq += __shfl_xor(aq, 32, 64);
+    if (g == 0) {
+      sm.rk[qr] = qr < n ? (float)(1.0 / sqrt((double)ak + (double)kNormEps)) : 0.f;
+      sm.rq[qr] = qr < n ? (float)(1.0 / sqrt((double)aq + (double)kNormEps)) : 0.f;
+    }
+  }
+  __syncthreads();
+
+  // ---- A = tril(diag(beta r_k) K K^T diag(r_k), -1): tiles (I, J <= I) of this wave
+  {
+    f32x4 acc[4] = {};
+#pragma unroll
+    for (int k0 = 0; k0 < dk; k0 += 16) {
+      const f32x4 a = *reinterpret_cast<const f32x4*>(&sm.tile[16 * I + m][k0 + 4 * g]);
+#pragma unroll
+      for (int J = 0; J < 4; ++J)
+        if (J <= I) {
+          const f32x4 b = *reinterpret_cast<const f32x4*>(&sm.tile[16 * J + m][k0 + 4 * g]);
+          acc[J] = mma4(a, b, acc[J]);
+        }
+    }
+#pragma unroll
+    for (int J = 0; J < 4; ++J)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * I + 4 * g + i, col = 16 * J + m;
+        sm.A[r][col] = (J <= I && col < r && r < n)
+                           ? sm.bt[r] * sm.rk[r] * sm.rk[col] * acc[J][i]
+                           : 0.f;
+      }
+  }
+  __syncthreads();
+  // ---- T = (I + A)^-1, blocked in 16 x 16 tiles. Diagonal tile (I, I) by forward
+  // substitution in wave I: lane l < 16 holds column l of the tile in registers, and every
+  // lane reads row rr of A_II (the same address, a broadcast). Then by block distance
+  // d = I - J on the matrix cores: T_IJ = -T_II X with X = sum_{J <= K < I} A_IK T_KJ.
+  {
+    float t[16];
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) {
+      float acc = 0.f;
+#pragma unroll
+      for (int i4 = 0; i4 < rr; i4 += 4) {
+        const f32x4 a = *reinterpret_cast<const f32x4*>(&sm.A[16 * I + rr][16 * I + i4]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (i4 + e < rr) acc += a[e] * t[i4 + e];
+      }
+      t[rr] = (rr == m ? 1.f : 0.f) - acc;  // columns l < rr only pick up t[i >= l]
+    }
+    if (l < 16) {
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) sm.T[16 * I + rr][16 * I + l] = rr >= l ? t[rr] : 0.f;
+    }
+    // the tiles above the diagonal
+#pragma unroll
+    for (int J = 0; J < 4; ++J)
+      if (J > I)
+        for (int idx = l; idx < 256; idx += 64) sm.T[16 * I + idx / 16][16 * J + idx % 16] = 0.f;
+  }
+  for (int d = 1; d < 4; ++d) {
+    __syncthreads();  // every tile at distance < d is in sm.T
+    const int J = I - d;
+    if (J >= 0) {
+      f32x4 x = {0.f, 0.f, 0.f, 0.f};
+      for (int K = J; K < I; ++K) {
+        const f32x4 a = *reinterpret_cast<const f32x4*>(&sm.A[16 * I + m][16 * K + 4 * g]);
+        f32x4 b;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) b[e] = sm.T[16 * K + 4 * g + e][16 * J + m];
+        x = mma4(a, b, x);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sm.X[I][4 * g + i][m] = x[i];
+    }
+    __syncthreads();  // X of every wave at this distance is in LDS
+    if (J >= 0) {
+      const f32x4 a = *reinterpret_cast<const f32x4*>(&sm.T[16 * I + m][16 * I + 4 * g]);
+      f32x4 b;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) b[e] = sm.X[I][4 * g + e][m];
+      const f32x4 y = mma4(a, b, f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sm.T[16 * I + 4 * g + i][16 * J + m] = -y[i];
+    }
+  }
+  __syncthreads();
+  // ---- row scales and T1 = diag(e^G) T diag(beta r_k)
+  const double Gn = sm.G[n - 1];
+  if (tid < C) {
+    sm.kd[tid] = tid < n ? expf((float)(Gn - sm.G[tid])) * sm.rk[tid] : 0.f;
+    sm.eq[tid] = tid < n ? expf((float)sm.G[tid]) * sm.rq[tid] : 0.f;
+  }
   for (int idx = tid; idx < C * C; idx += 256) {
     const int r = idx / C, i = idx % C;
-    s_A[r][i] = (i <= r && r < n) ? expf((float)(s_G[r] - s_G[i])) * s_T[r][i] * s_bt[i] : 0.f;
+    sm.A[r][i] = (i <= r && r < n) ? expf((float)sm.G[r]) * sm.T[r][i] * sm.bt[i] * sm.rk[i]
+                                   : 0.f;
   }
   __syncthreads();
-  float* Up = U + pair * C * (int64_t)dv;
-  for (int idx = tid; idx < C * dv; idx += 256) {
-    const int r = idx / dv, j = idx % dv;
-    float acc = 0.f;
-    for (int i = 0; i <= r && i < n; ++i) acc += s_A[r][i] * ld(v, ((t0 + i) * HV + hv) * (int64_t)dv + j);
-    Up[idx] = acc;
+  // ---- W<- = T1 K (rows of tile I), A_qk (tiles J <= I), K~^T, Qf
+  float* Wp = W + pair * (int64_t)C * dk;
+  for (int jd = 0; jd < dk / 16; ++jd) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k0 = 0; k0 < C; k0 += 16) {
+      const f32x4 a = *reinterpret_cast<const f32x4*>(&sm.A[16 * I + m][k0 + 4 * g]);
+      f32x4 b;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) b[s] = sm.tile[k0 + 4 * g + s][16 * jd + m];
+      acc = mma4(a, b, acc);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) Wp[(int64_t)(16 * I + 4 * g + i) * dk + 16 * jd + m] = acc[i];
+  }
+  {
+    f32x4 acc[4] = {};
+#pragma unroll
+    for (int kb = 0; kb < dk / 16; ++kb) {
+#pragma unroll
+      for (int J = 0; J < 4; ++J)
+        if (J <= I) {
+          const f32x4 b = *reinterpret_cast<const f32x4*>(&sm.tile[16 * J + m][16 * kb + 4 * g]);
+          acc[J] = mma4(qa[kb], b, acc[J]);
+        }
+    }
+    float* Ap = Aqk + pair * (int64_t)C * C;
+#pragma unroll
+    for (int J = 0; J < 4; ++J)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int rr = 16 * I + 4 * g + i, col = 16 * J + m;
+        Ap[rr * C + col] = (J <= I && col <= rr && rr < n)
+                               ? expf((float)(sm.G[rr] - sm.G[col])) * sm.rq[rr] * sm.rk[col] *
+                                     acc[J][i]
+                               : 0.f;
+      }
+  }
+  float* Kp = Kft + pair * (int64_t)C * dk;  // K~ transposed: [dk][C]
+#pragma unroll
+  for (int idx = tid; idx < C * dk; idx += 256) {
+    const int j = idx / C, r = idx - j * C;
+    Kp[idx] = sm.kd[r] * sm.tile[r][j];
+  }
+  float* Qp = Qf + pair * (int64_t)C * dk + (int64_t)qr * dk + 4 * g;
+  const float eqr = sm.eq[qr];  // zero past n
+#pragma unroll
+  for (int kb = 0; kb < dk / 16; ++kb)
+    *reinterpret_cast<f32x4*>(Qp + 16 * kb) = eqr * qa[kb];
+  __syncthreads();  // the K tile and T1 are no longer read
+  // ---- U~ = T2 V with T2 = (Gamma o T) diag(beta), written transposed: [dv][C]
+  for (int idx = tid; idx < C * C; idx += 256) {
+    const int r = idx / C, i = idx % C;
+    sm.A[r][i] = (i <= r && r < n) ? expf((float)(sm.G[r] - sm.G[i])) * sm.T[r][i] * sm.bt[i]
+                                   : 0.f;
+  }
+#pragma unroll
+  for (int i = 0; i < kVPer; ++i) {
+    const int idx = tid + 256 * i, r = idx / dv, j = idx - r * dv;
+    sm.tile[r][j] = vr[i];
+  }
+  __syncthreads();
+  float* Up = Ut + pair * (int64_t)C * dv;
+  for (int jd = 0; jd < dv / 16; ++jd) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k0 = 0; k0 < C; k0 += 16) {
+      const f32x4 a = *reinterpret_cast<const f32x4*>(&sm.A[16 * I + m][k0 + 4 * g]);
+      f32x4 b;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) b[s] = sm.tile[k0 + 4 * g + s][16 * jd + m];
+      acc = mma4(a, b, acc);
+    }
+    *reinterpret_cast<f32x4*>(&Up[(int64_t)(16 * jd + m) * C + 16 * I + 4 * g]) = acc;
   }
 }
 
-constexpr int kBV = 16;      // state rows (dv index) per workgroup
-constexpr int kMaxDk = 256;
+template <int DK>
+struct RefStateSmem {
+  float S[kBV][DK + 4];  // this workgroup's rows of S, all dk columns
+  float Ut[kBV][C + 4];  // U of the current chunk, transposed: [column][token]
+};
 
-// One workgroup per (request, value head, block of kBV state rows); walks the
-// request's chunks in order with its rows of S resident in LDS.
-template <typename Tin>
+// One workgroup per (request, value head, kBV state rows); walks the request's chunks in
+// order with its rows of S resident in LDS. Wave w owns chunk rows 16w .. 16w + 15 for U
+// and O, and dk rows 16 jd .. for jd = w (mod 4) of the state update. Each wave holds its
+// fragments of one chunk's operands in registers; a phase that has consumed its
+// fragments loads the next chunk's in their place, so their latency overlaps the rest of
+// the chunk. The workgroup's barriers wait for LDS traffic only.
+// Workgroup id -> (pair, slice): the dv / 16 slices of one (request, value head) pair get
+// consecutive ids of one XCD (ids are dealt to the 8 XCDs in turn), so they are dispatched
+// together and read the pair's per-chunk operands through that XCD's L2.
+template <typename Tin, int DK>
 __global__ __launch_bounds__(256) void ref_state_kernel(
-    const Tin* __restrict__ q, const Tin* __restrict__ k, const int64_t* __restrict__ cu,
-    const int64_t* __restrict__ cache_indices, const int32_t* __restrict__ chunk_off,
-    const double* __restrict__ gcum, const float* __restrict__ W, const float* __restrict__ U,
-    int H, int HV, int dk, int dv, int64_t short_len, float* __restrict__ state_pool,
-    Tin* __restrict__ out, int32_t* __restrict__ nonfinite) {
-  __shared__ float s_S[kBV][kMaxDk + 1];
-  __shared__ float s_U[C][kBV + 1];
-  __shared__ float s_Aqk[C][C + 1];
-  __shared__ float s_rq[C], s_rk[C], s_kd[C], s_eg[C];
-  __shared__ double s_G[C];
-  const int seq = blockIdx.x, hv = blockIdx.y, v0 = blockIdx.z * kBV;
-  const int64_t L = cu[seq + 1] - cu[seq];
-  const int64_t nchunks = path_chunks(L, C, short_len);
+    const int64_t* __restrict__ cu, const int64_t* __restrict__ cache_indices,
+    const int32_t* __restrict__ chunk_off, const double* __restrict__ gcum,
+    const float* __restrict__ W, const float* __restrict__ Ut, const float* __restrict__ Aqk,
+    const float* __restrict__ Kft, const float* __restrict__ Qf, int64_t B, int HV, int dv,
+    int64_t short_len, float* __restrict__ state_pool, Tin* __restrict__ out,
+    int32_t* __restrict__ nonfinite) {
+  constexpr int NK = DK / 16;  // 16-wide contraction blocks over dk
+  constexpr int NT = DK / 64;  // dk tiles of the state update per wave
+  __shared__ RefStateSmem<DK> sm;
+  const int nsl = dv / kBV;
+  const int64_t id = blockIdx.x, slot8 = id / 8;
+  const int64_t pidx = slot8 / nsl * 8 + id % 8;
+  if (pidx >= B * HV) return;  // the pair count rounded up to 8
+  const int64_t seq = pidx / HV;
+  const int hv = (int)(pidx - seq * HV), v0 = (int)(slot8 % nsl) * kBV;
+  const int64_t tb = cu[seq], te = cu[seq + 1];
+  const int64_t nchunks = path_chunks(te - tb, C, short_len);
   if (nchunks == 0) return;  // empty (slot untouched) or evaluated by the token recurrence
   const int64_t slot = cache_indices[seq];
-  const int h = hv / (HV / H);
-  const int tid = threadIdx.x;
-  float* Sg = state_pool + ((slot * HV + hv) * (int64_t)dv + v0) * dk;
-  for (int idx = tid; idx < kBV * dk; idx += 256) s_S[idx / dk][idx % dk] = Sg[idx];
+  const int64_t c0 = chunk_off[seq];
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, m = l & 15, g = l >> 4;
+  float* Sg = state_pool + ((slot * HV + hv) * (int64_t)dv + v0) * DK;
+  for (int idx = tid; idx < kBV * DK; idx += 256) sm.S[idx / DK][idx % DK] = Sg[idx];
+
+  // this wave's fragments of one chunk (lane (m, g): 16-byte runs at contraction 4g)
+  f32x4 wa[NK], qa[NK], aa[4], ka[NT][4], ut;
+  double gn;
+  auto pair_of = [&](int64_t cl) { return (c0 + cl) * HV + hv; };
+  auto load_wu = [&](int64_t cl) {  // W<- rows 16w + m; U~ column v0 + m, tokens 16w + 4g
+    const int64_t p = pair_of(cl);
+    const float* Wp = W + p * (int64_t)C * DK + (16 * w + m) * DK + 4 * g;
+#pragma unroll
+    for (int kb = 0; kb < NK; ++kb) wa[kb] = *reinterpret_cast<const f32x4*>(Wp + 16 * kb);
+    ut = *reinterpret_cast<const f32x4*>(Ut + p * (int64_t)C * dv + (int64_t)(v0 + m) * C +
+                                         16 * w + 4 * g);
+  };
+  auto load_qa = [&](int64_t cl) {  // Qf and A_qk rows 16w + m
+    const int64_t p = pair_of(cl);
+    const float* Qp = Qf + p * (int64_t)C * DK + (16 * w + m) * DK + 4 * g;
+#pragma unroll
+    for (int kb = 0; kb < NK; ++kb) qa[kb] = *reinterpret_cast<const f32x4*>(Qp + 16 * kb);
+    const float* Ap = Aqk + p * (int64_t)C * C + (16 * w + m) * C + 4 * g;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) aa[kb] = *reinterpret_cast<const f32x4*>(Ap + 16 * kb);
+  };
+  auto load_k = [&](int64_t cl) {  // K~^T rows 16 (w + 4t) + m, and G at the chunk's end
+    const int64_t p = pair_of(cl);
+    const float* Kp = Kft + p * (int64_t)C * DK + 4 * g;
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+        ka[t][kb] = *reinterpret_cast<const f32x4*>(Kp + (16 * (w + 4 * t) + m) * C + 16 * kb);
+    const int64_t n = min((int64_t)C, te - tb - cl * C);
+    gn = gcum[p * C + n - 1];
+  };
+  load_wu(0);
+  load_qa(0);
+  load_k(0);
   for (int64_t cl = 0; cl < nchunks; ++cl) {
-    const int64_t c = chunk_off[seq] + cl;
-    const int64_t t0 = cu[seq] + cl * C;
-    const int n = (int)min((int64_t)C, cu[seq + 1] - t0);
-    const int64_t pair = c * HV + hv;
-    __syncthreads();  // previous chunk's S update is complete
-    if (tid < C) s_G[tid] = gcum[pair * C + tid];
-    row_inv_norms(q, t0, n, H, h, dk, s_rq);
-    row_inv_norms(k, t0, n, H, h, dk, s_rk);
-    __syncthreads();
-    if (tid < C) {
-      const double Gn = s_G[n - 1];
-      s_eg[tid] = tid < n ? expf((float)s_G[tid]) : 0.f;
-      s_kd[tid] = tid < n ? expf((float)(Gn - s_G[tid])) * s_rk[tid] : 0.f;
-    }
-    // A_qk = Gamma o tril0(Qh Kh^T)
-    for (int idx = tid; idx < C * C; idx += 256) {
-      const int r = idx / C, i = idx % C;
-      float val = 0.f;
-      if (i <= r && r < n) {
-        const int64_t br = ((t0 + r) * H + h) * (int64_t)dk, bi = ((t0 + i) * H + h) * (int64_t)dk;
-        float acc = 0.f;
-        for (int j = 0; j < dk; ++j) acc += ld(q, br + j) * ld(k, bi + j);
-        val = expf((float)(s_G[r] - s_G[i])) * s_rq[r] * s_rk[i] * acc;
+    const int64_t t0 = tb + cl * C;
+    const int n = (int)min((int64_t)C, te - t0);
+    const bool more = cl + 1 < nchunks;
+    lds_barrier();  // the previous chunk's S update and U reads are complete
+    // ---- U = U~ - W<- S^T for tokens 16w .., this workgroup's columns
+    {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < NK; ++kb) {
+        const f32x4 b = *reinterpret_cast<const f32x4*>(&sm.S[m][16 * kb + 4 * g]);
+        acc = mma4(wa[kb], b, acc);
       }
-      s_Aqk[r][i] = val;
+      // lane (m, g) holds tokens 16w + 4g + i of column v0 + m
+      *reinterpret_cast<f32x4*>(&sm.Ut[m][16 * w + 4 * g]) = ut - acc;
+      if (more) load_wu(cl + 1);
     }
-    // U = U~ - W<- S^T (rows of this block only)
-    const float* Wp = W + pair * C * (int64_t)dk;
-    const float* Up = U + pair * C * (int64_t)dv;
-    for (int idx = tid; idx < C * kBV; idx += 256) {
-      const int r = idx / kBV, cc = idx % kBV;
-      float val = 0.f;
-      if (r < n) {
-        float acc = 0.f;
-        for (int j = 0; j < dk; ++j) acc += Wp[r * (int64_t)dk + j] * s_S[cc][j];
-        val = Up[r * (int64_t)dv + v0 + cc] - acc;
+    lds_barrier();  // U complete
+    // ---- O = Qf S^T + A_qk U for tokens 16w .. (A_qk is causal: tokens up to 16w + 15)
+    {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < NK; ++kb) {
+        const f32x4 b = *reinterpret_cast<const f32x4*>(&sm.S[m][16 * kb + 4 * g]);
+        acc = mma4(qa[kb], b, acc);
       }
-      s_U[r][cc] = val;
-    }
-    __syncthreads();
-    // O = diag(e^G r_q) Q S^T + A_qk U
-    for (int idx = tid; idx < C * kBV; idx += 256) {
-      const int r = idx / kBV, cc = idx % kBV;
-      if (r < n) {
-        const int64_t br = ((t0 + r) * H + h) * (int64_t)dk;
-        float acc = 0.f;
-        for (int j = 0; j < dk; ++j) acc += ld(q, br + j) * s_S[cc][j];
-        float o = s_eg[r] * s_rq[r] * acc;
-        for (int i = 0; i <= r; ++i) o += s_Aqk[r][i] * s_U[i][cc];
-        st(out, ((t0 + r) * HV + hv) * (int64_t)dv + v0 + cc, o);
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+        if (kb <= w) {
+          const f32x4 b = *reinterpret_cast<const f32x4*>(&sm.Ut[m][16 * kb + 4 * g]);
+          acc = mma4(aa[kb], b, acc);
+        }
+      if (more) load_qa(cl + 1);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * w + 4 * g + i;
+        if (r < n) st(out, ((t0 + r) * HV + hv) * (int64_t)dv + v0 + m, acc[i]);
       }
     }
-    __syncthreads();
-    // S <- e^{G_n} S + U^T diag(e^{G_n - G} r_k) K
-    const float egn = expf((float)s_G[n - 1]);
-    for (int idx = tid; idx < kBV * dk; idx += 256) {
-      const int cc = idx / dk, j = idx % dk;
-      float acc = 0.f;
-      for (int r = 0; r < n; ++r) acc += s_U[r][cc] * s_kd[r] * ld(k, ((t0 + r) * H + h) * (int64_t)dk + j);
-      s_S[cc][j] = egn * s_S[cc][j] + acc;
+    lds_barrier();  // every wave has read S for this chunk
+    // ---- S^T <- e^{G_n} S^T + K~^T U, dk tiles jd = w + 4t
+    const float egn = expf((float)gn);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const f32x4 b = *reinterpret_cast<const f32x4*>(&sm.Ut[m][16 * kb + 4 * g]);
+        acc = mma4(ka[t][kb], b, acc);
+      }
+      // lane (m, g) holds S^T rows 16 jd + 4g + i, column m: S[m][16 jd + 4g + i]
+      f32x4* sp = reinterpret_cast<f32x4*>(&sm.S[m][16 * (w + 4 * t) + 4 * g]);
+      *sp = egn * *sp + acc;
     }
+    if (more) load_k(cl + 1);
   }
-  __syncthreads();
+  lds_barrier();
   bool finite = true;
-  for (int idx = tid; idx < kBV * dk; idx += 256) {
-    const float x = s_S[idx / dk][idx % dk];
+  for (int idx = tid; idx < kBV * DK; idx += 256) {
+    const float x = sm.S[idx / DK][idx % DK];
     Sg[idx] = x;
     finite = finite && __builtin_isfinite(x);
   }
   if (!finite) *nonfinite = 1;
 }
 
-}  // namespace
-
-hipError_t launch_ref_prep(const void* k, const void* v, const int64_t* cu_seqlens,
-                           const int32_t* chunk_off, const int32_t* chunk_seq, const double* gcum,
-                           const float* beta, const Shape& s, int64_t max_chunks, float* w,
-                           float* u, hipStream_t st) {
+template <typename Tin, int DK, int DV>
+void launch_prep_t(const void* q, const void* k, const void* v, const int64_t* cu,
+                   const int32_t* chunk_off, const int32_t* chunk_seq, const double* gcum,
+                   const float* beta, const Shape& s, int64_t max_chunks, float* w, float* ut,
+                   float* aqk, float* kft, float* qf, hipStream_t st) {
   const dim3 grid((unsigned)max_chunks, (unsigned)s.HV);
-  if (s.bf16) {
-    hipLaunchKernelGGL(ref_prep_kernel<__hip_bfloat16>, grid, dim3(256), 0, st,
-                       (const __hip_bfloat16*)k, (const __hip_bfloat16*)v, cu_seqlens, chunk_off,
-                       chunk_seq, gcum, beta, s.H, s.HV, s.dk, s.dv, w, u);
-  } else {
-    hipLaunchKernelGGL(ref_prep_kernel<float>, grid, dim3(256), 0, st, (const float*)k,
-                       (const float*)v, cu_seqlens, chunk_off, chunk_seq, gcum, beta, s.H, s.HV,
-                       s.dk, s.dv, w, u);
-  }
-  return hipGetLastError();
+  hipLaunchKernelGGL((ref_prep_kernel<Tin, DK, DV>), grid, dim3(256), 0, st, (const Tin*)q,
+                     (const Tin*)k, (const Tin*)v, cu, chunk_off, chunk_seq, gcum, beta, s.H,
+                     s.HV, w, ut, aqk, kft, qf);
 }
 
-hipError_t launch_ref_state(const void* q, const void* k, const int64_t* cu_seqlens,
-                            const int64_t* cache_indices, const int32_t* chunk_off,
-                            const double* gcum, const float* w, const float* u, const Shape& s,
-                            float* state_pool, void* out, int32_t* nonfinite, hipStream_t st) {
-  const dim3 grid((unsigned)s.B, (unsigned)s.HV, (unsigned)(s.dv / kBV));
-  if (s.bf16) {
-    hipLaunchKernelGGL(ref_state_kernel<__hip_bfloat16>, grid, dim3(256), 0, st,
-                       (const __hip_bfloat16*)q, (const __hip_bfloat16*)k, cu_seqlens,
-                       cache_indices, chunk_off, gcum, w, u, s.H, s.HV, s.dk, s.dv, s.short_len,
-                       state_pool, (__hip_bfloat16*)out, nonfinite);
-  } else {
-    hipLaunchKernelGGL(ref_state_kernel<float>, grid, dim3(256), 0, st, (const float*)q,
-                       (const float*)k, cu_seqlens, cache_indices, chunk_off, gcum, w, u, s.H,
-                       s.HV, s.dk, s.dv, s.short_len, state_pool, (float*)out, nonfinite);
+template <typename Tin, int DK>
+void launch_state_t(const int64_t* cu, const int64_t* idx, const int32_t* chunk_off,
+                    const double* gcum, const float* w, const float* ut, const float* aqk,
+                    const float* kft, const float* qf, const Shape& s, float* pool, void* out,
+                    int32_t* nonfinite, hipStream_t st) {
+  const int64_t blocks = (s.B * s.HV + 7) / 8 * 8 * (s.dv / kBV);
+  hipLaunchKernelGGL((ref_state_kernel<Tin, DK>), dim3((unsigned)blocks), dim3(256), 0, st, cu,
+                     idx, chunk_off, gcum, w, ut, aqk, kft, qf, s.B, s.HV, s.dv, s.short_len,
+                     pool, (Tin*)out, nonfinite);
+}
+
+}  // namespace
+
+hipError_t launch_ref_prep(const void* q, const void* k, const void* v,
+                           const int64_t* cu_seqlens, const int32_t* chunk_off,
+                           const int32_t* chunk_seq, const double* gcum, const float* beta,
+                           const Shape& s, int64_t max_chunks, float* w, float* ut, float* aqk,
+                           float* kft, float* qf, hipStream_t st) {
+#define GDN_REF_PREP(DKv, DVv)                                                                 \
+  if (s.dk == DKv && s.dv == DVv) {                                                            \
+    if (s.bf16)                                                                                \
+      launch_prep_t<__hip_bfloat16, DKv, DVv>(q, k, v, cu_seqlens, chunk_off, chunk_seq, gcum, \
+                                              beta, s, max_chunks, w, ut, aqk, kft, qf, st);   \
+    else                                                                                       \
+      launch_prep_t<float, DKv, DVv>(q, k, v, cu_seqlens, chunk_off, chunk_seq, gcum, beta, s, \
+                                     max_chunks, w, ut, aqk, kft, qf, st);                     \
+    return hipGetLastError();                                                                  \
   }
-  return hipGetLastError();
+  GDN_REF_PREP(64, 64)
+  GDN_REF_PREP(64, 128)
+  GDN_REF_PREP(64, 256)
+  GDN_REF_PREP(128, 64)
+  GDN_REF_PREP(128, 128)
+  GDN_REF_PREP(128, 256)
+  GDN_REF_PREP(256, 64)
+  GDN_REF_PREP(256, 128)
+  GDN_REF_PREP(256, 256)
+#undef GDN_REF_PREP
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_ref_state(const int64_t* cu_seqlens, const int64_t* cache_indices,
+                            const int32_t* chunk_off, const double* gcum, const float* w,
+                            const float* ut, const float* aqk, const float* kft, const float* qf,
+                            const Shape& s, float* state_pool, void* out, int32_t* nonfinite,
+                            hipStream_t st) {
+#define GDN_REF_STATE(DKv)                                                                     \
+  if (s.dk == DKv) {                                                                           \
+    if (s.bf16)                                                                                \
+      launch_state_t<__hip_bfloat16, DKv>(cu_seqlens, cache_indices, chunk_off, gcum, w, ut,   \
+                                          aqk, kft, qf, s, state_pool, out, nonfinite, st);    \
+    else                                                                                       \
+      launch_state_t<float, DKv>(cu_seqlens, cache_indices, chunk_off, gcum, w, ut, aqk, kft, \
+                                 qf, s, state_pool, out, nonfinite, st);                       \
+    return hipGetLastError();                                                                  \
+  }
+  GDN_REF_STATE(64)
+  GDN_REF_STATE(128)
+  GDN_REF_STATE(256)
+#undef GDN_REF_STATE
+  return hipErrorInvalidValue;
 }
 
 }  // namespace gdn

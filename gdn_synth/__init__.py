@@ -247,23 +247,34 @@ def workload_lengths(idx: int) -> list:
     raise ValueError(idx)
 
 
-def workload(idx: int) -> Problem:
-    """The five named workloads (see WORKLOADS)."""
+def workload(idx: int, dtype: Optional[str] = None) -> Problem:
+    """The five named workloads (see WORKLOADS). ``dtype`` ("bf16" or "f32") draws the same
+    workload with q, k, v (and out) in that dtype instead of its own; its name then ends in
+    that dtype."""
+    if dtype is None:
+        return _workload(idx)
+    p = _workload(idx, dtype)
+    p.name = p.name.rsplit("_", 1)[0] + "_" + dtype
+    return p
+
+
+def _workload(idx: int, dtype: Optional[str] = None) -> Problem:
     seed = 1000 + idx
     L = workload_lengths(idx)
+    kw = {} if dtype is None else {"dtype": dtype}
     if idx == 0:
-        return make_problem(seed, L, 1, 1, 64, 64, dtype="f32", name="tiny_f32")
+        return make_problem(seed, L, 1, 1, 64, 64, **{"dtype": "f32", **kw}, name="tiny_f32")
     if idx == 1:
-        return make_problem(seed, L, 16, 16, 128, 128, name="dense_batch_bf16")
+        return make_problem(seed, L, 16, 16, 128, 128, **kw, name="dense_batch_bf16")
     if idx == 2:
         perm = seeded_permutation(seed, TID_PERM, 64)
         return make_problem(seed, L, 16, 32, 128, 128, pool=64, cache_indices=perm[:8],
-                            state_std=0.1, name="varlen_gqa_bf16")
+                            state_std=0.1, **kw, name="varlen_gqa_bf16")
     if idx == 3:
-        return make_problem(seed, L, 8, 8, 256, 256, name="wide_head_bf16")
+        return make_problem(seed, L, 8, 8, 256, 256, **kw, name="wide_head_bf16")
     if idx == 4:
         return make_problem(seed, L, 16, 32, 128, 128, a_mean=-4.0, b_mean=2.0, state_std=0.1,
-                            name="long_decay_bf16")
+                            **kw, name="long_decay_bf16")
     raise ValueError(idx)
 
 

@@ -65,10 +65,10 @@ __device__ __forceinline__ f32x4 mma4(f32x4 a, f32x4 b, f32x4 acc) {
 
 template <int DM>
 struct RefPrepSmem {
-  float tile[C][DM + 4];  // K rows (zero past n), later V rows
-  float A[C][C + 4];      // A, then T1 = diag(e^G) T diag(beta r_k), then T2
-  float T[C][C + 4];      // T = (I + A)^-1
-  float X[4][16][20];     // per wave: one 16 x 16 tile of the blocked inverse
+  alignas(16) float tile[C][DM + 4];  // K rows (zero past n), later V rows
+  alignas(16) float A[C][C + 4];      // A, then T1 = diag(e^G) T diag(beta r_k), then T2
+  alignas(16) float T[C][C + 4];      // T = (I + A)^-1
+  alignas(16) float X[4][16][20];     // per wave: one 16 x 16 tile of the blocked inverse
   double G[C];
   float bt[C], rk[C], rq[C], kd[C], eq[C];
 };
@@ -316,8 +316,8 @@ __global__ __launch_bounds__(256) void ref_prep_kernel(
 
 template <int DK>
 struct RefStateSmem {
-  float S[kBV][DK + 4];  // this workgroup's rows of S, all dk columns
-  float Ut[kBV][C + 4];  // U of the current chunk, transposed: [column][token]
+  alignas(16) float S[kBV][DK + 4];  // this workgroup's rows of S, all dk columns
+  alignas(16) float Ut[kBV][C + 4];  // U of the current chunk, transposed: [column][token]
 };
 
 // One workgroup per (request, value head, kBV state rows); walks the request's chunks in

@@ -185,10 +185,12 @@ __global__ __launch_bounds__(256, (DK + DV <= 256) ? 3 : 1) void mfma_prep_kerne
   constexpr int KP = C * DK / 8 / 256;  // 16-byte pieces per thread of a K or Q tile
   constexpr int VP = C * DV / 8 / 256;  // ... of a V tile
 
-  // Persistent: workgroups stride over the (chunk, value head) items of the chunk_off[B]
-  // real chunks. The next item's rows are loaded into registers while the current one is
-  // processed; the loads are unconditional (the last item reloads itself), so no register
-  // set is merged or copied at the loop back edge.
+  // Persistent: workgroups stride over the (chunk, q/k head) groups of the chunk_off[B]
+  // real chunks and take the HV / H value heads of a group as consecutive items, which
+  // share the group's K rows: those are loaded and staged once per group (the staged K
+  // tile stays in LDS for the group's next item). The next item's rows are loaded into
+  // registers while the current one is processed, so no register set is merged or copied
+  // at the loop back edge.
   struct Item {
     int hv, h, n;
     int64_t c, t0;
@@ -215,10 +217,18 @@ __global__ __launch_bounds__(256, (DK + DV <= 256) ? 3 : 1) void mfma_prep_kerne
   };
   u32x4 kreg[KP], qreg[KP], vreg[VP];
   float areg, breg;  // raw gate inputs a, b of chunk row tid % C
-  auto load_kq = [&](const Item& x) {
-    load_tile_rows<DK>(kreg, k + (x.t0 * H + x.h) * (int64_t)DK, rsk, x.n, tid);
+  auto load_kq = [&](const Item& x, bool with_k) {
+    if (with_k) {
+      load_tile_rows<DK>(kreg, k + (x.t0 * H + x.h) * (int64_t)DK, rsk, x.n, tid);
+    } else {
+      // unused; defined so the registers are not live through the item
+#pragma unroll
+      for (int u = 0; u < KP; ++u) kreg[u] = u32x4{0u, 0u, 0u, 0u};
+    }
     load_tile_rows<DK>(qreg, q + (x.t0 * H + x.h) * (int64_t)DK, rsk, x.n, tid);
   };
+  // the next item shares the current one's K rows (the same chunk and q/k head)
+  auto same_k = [](const Item& a, const Item& b) { return a.c == b.c && a.h == b.h && a.n == b.n; };
   auto load_vg = [&](const Item& x) {
     load_tile_rows<DV>(vreg, v + (x.t0 * HV + x.hv) * (int64_t)DV, (int64_t)HV * DV, x.n, tid);
     if (tid < C) {
@@ -275,25 +285,33 @@ __global__ __launch_bounds__(256, (DK + DV <= 256) ? 3 : 1) void mfma_prep_kerne
   }
   if (blockIdx.x == 0 && tid == 0) *nonfinite = 0;  // the state pass raises it
   const int64_t n_items = (int64_t)(SELF_PLAN ? sm.coff[B] : chunk_off[B]) * HV;
-  if ((int64_t)blockIdx.x >= n_items) return;
+  const int GQ = HV / H;  // value heads per q/k head
+  // the workgroup's j-th item: value head j % GQ of its (j / GQ)-th group
+  auto item_of = [&](int64_t j) {
+    return ((int64_t)blockIdx.x + (int64_t)gridDim.x * (j / GQ)) * GQ + j % GQ;
+  };
+  if (item_of(0) >= n_items) return;
   Item cur;
-  geom(blockIdx.x, cur);
-  load_kq(cur);
+  geom(item_of(0), cur);
+  load_kq(cur, true);
   load_vg(cur);
   if (tid < C) gates(cur, 0);
-  int ib = 0;  // item parity: this item's gate copy
-  for (int64_t it = blockIdx.x; it < n_items; it += gridDim.x, ib ^= 1) {
+  int ib = 0;           // item parity: this item's gate copy
+  bool stage_k = true;  // this item's K rows are in kreg, not yet in LDS
+  for (int64_t jw = 0, it = item_of(0); it < n_items; ++jw, it = item_of(jw), ib ^= 1) {
     // The next item; after the workgroup's last item an empty one (n = 0) whose
-    // prefetch loads nothing, so that the prefetch stays unconditional.
+    // prefetch loads nothing.
+    const int64_t itn = item_of(jw + 1);
     Item nx;
-    geom(it + gridDim.x < n_items ? it + gridDim.x : it, nx);
-    if (it + gridDim.x >= n_items) nx.n = 0;
+    geom(itn < n_items ? itn : it, nx);
+    if (itn >= n_items) nx.n = 0;
     const int hv = cur.hv, h = cur.h, n = cur.n;
     const int64_t c = cur.c, t0 = cur.t0;
     const int64_t pair = c * HV + hv;
 
-    // ---- stage K and Q rows in LDS from the prefetch registers
-    store_tile_rows<DK>(sm.ks, SK, kreg, tid);
+    // ---- stage K (unless this group's previous item left it in LDS) and Q rows in LDS
+    // from the prefetch registers
+    if (stage_k) store_tile_rows<DK>(sm.ks, SK, kreg, tid);
     store_tile_rows<DK>(sm.qv, SQV, qreg, tid);
     const double* G2 = sm.G2[ib];
     const float* bts = sm.bt[ib];
@@ -544,7 +562,9 @@ __global__ __launch_bounds__(256, (DK + DV <= 256) ? 3 : 1) void mfma_prep_kerne
       __builtin_nontemporal_store(to_half4(acc), reinterpret_cast<half4*>(Uout + pair * C * DV + ((cc * 4 + w) * 64 + l) * 4));
     }
     if (tid < C) gates(nx, ib ^ 1);  // wave 0: the next item's gates
-    load_kq(nx);  // issued late so that these registers stay free through the item
+    // issued late so that these registers stay free through the item
+    stage_k = !same_k(nx, cur);
+    load_kq(nx, stage_k);
     lds_barrier();  // (5) every LDS region is free for the next item
     cur = nx;
   }
@@ -564,8 +584,8 @@ hipError_t launch_prep_t(const void* q, const void* k, const void* v, const int6
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
       hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, 256, 0) != hipSuccess)
     return hipErrorInvalidValue;
-  const int64_t items = max_chunks * s.HV;
-  const int64_t grid = std::min<int64_t>(items, (int64_t)std::max(cus, 1) * std::max(per_cu, 1));
+  const int64_t groups = max_chunks * s.H;  // (chunk, q/k head) groups
+  const int64_t grid = std::min<int64_t>(groups, (int64_t)std::max(cus, 1) * std::max(per_cu, 1));
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), 0, st, (const uint16_t*)q,
                      (const uint16_t*)k, (const uint16_t*)v, cu, off, cseq, ga, gb, A_log,
                      dt_bias, (int)s.B, s.H, s.HV, s.short_len, w, u, aqk, eg, kf, qf, nonfinite);

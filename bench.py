@@ -79,13 +79,15 @@ def stage_bytes(p, s_qkv: int, s_ws: int, n_chunks: int):
 DECODE_SOURCES = ("gdn_decode.hip", "gdn_internal.h")
 PROMOTE_SOURCES = ("gdn_promote.hip", "gdn_internal.h", "gdn_mfma.h")
 BACKWARD_SOURCES = ("gdn_backward.hip", "gdn_backward.h", "gdn_internal.h", "gdn_plan_gate.hip")
+PREFILL_F32_SOURCES = ("gdn_ref.hip", "gdn_plan_gate.hip", "gdn_api.hip", "gdn_internal.h",
+                       "gdn_mfma.h")
 
 
 def kernel_source_hash(kind: str = "prefill") -> str:
-    """sha256[:16] over the kernel sources a measurement depends on: for "prefill" every
-    .hip / .h file of csrc except the decode, Promote and backward kernels' own files, for
-    "decode" DECODE_SOURCES, for "promote" PROMOTE_SOURCES, for "backward"
-    BACKWARD_SOURCES."""
+    """sha256[:16] over the kernel sources a measurement depends on: for "prefill" (the
+    bf16 path) every .hip / .h file of csrc except the decode, Promote, backward and fp32
+    kernels' own files, for "prefill_f32" PREFILL_F32_SOURCES, for "decode" DECODE_SOURCES,
+    for "promote" PROMOTE_SOURCES, for "backward" BACKWARD_SOURCES."""
     csrc = os.path.join(ROOT, "gated_deltanet_prefill_gdn_amd", "csrc")
     if kind == "decode":
         files = sorted(DECODE_SOURCES)
@@ -93,10 +95,12 @@ def kernel_source_hash(kind: str = "prefill") -> str:
         files = sorted(PROMOTE_SOURCES)
     elif kind == "backward":
         files = sorted(BACKWARD_SOURCES)
+    elif kind == "prefill_f32":
+        files = sorted(PREFILL_F32_SOURCES)
     else:
         files = sorted(f for f in os.listdir(csrc) if f.endswith((".hip", ".h"))
                        and f not in ("gdn_decode.hip", "gdn_promote.hip", "gdn_backward.hip",
-                                     "gdn_backward.h"))
+                                     "gdn_backward.h", "gdn_ref.hip"))
     h = hashlib.sha256()
     for f in files:
         h.update(f.encode())
@@ -770,7 +774,7 @@ def measure_prefill(p, steps: int, warmup: int, cold_steps: int, copy_calibratio
     kernel_name = kernels[dom]
     pbytes = path_bytes(p, s_qkv)
     flops = algorithmic_flops_per_token_vhead(p.dk, p.dv, p.chunk_size) * p.N * p.HV
-    src_hash = kernel_source_hash()
+    src_hash = kernel_source_hash("prefill" if p.dtype == "bf16" else "prefill_f32")
     io = stage_bytes(p, s_qkv, 2, n_chunks) if p.dtype == "bf16" else {}
     tag = workload_tag(p)
     ctr = stored_counters(kernel_name, tag, src_hash)

@@ -355,29 +355,24 @@ __global__ __launch_bounds__(256) void ref_state_kernel(
   float* Sg = state_pool + ((slot * HV + hv) * (int64_t)dv + v0) * DK;
   for (int idx = tid; idx < kBV * DK; idx += 256) sm.S[idx / DK][idx % DK] = Sg[idx];
 
-  // this wave's fragments of one chunk (lane (m, g): 16-byte runs at contraction 4g)
-  f32x4 wa[NK], qa[NK], aa[4], ka[NT][4], ut;
+  // this wave's fragments of a chunk (lane (m, g): 16-byte runs at contraction 4g). Each
+  // fragment of the next chunk is loaded into its register as soon as the current chunk's
+  // product has taken it, so every load has about a chunk to land.
+  f32x4 wa[NK], qa[NK], ut, aa[4], ka[NT][4];
   double gn;
   auto pair_of = [&](int64_t cl) { return (c0 + cl) * HV + hv; };
-  auto load_wu = [&](int64_t cl) {  // W<- rows 16w + m; U~ column v0 + m, tokens 16w + 4g
-    const int64_t p = pair_of(cl);
-    const float* Wp = W + p * (int64_t)C * DK + (16 * w + m) * DK + 4 * g;
-#pragma unroll
-    for (int kb = 0; kb < NK; ++kb) wa[kb] = *reinterpret_cast<const f32x4*>(Wp + 16 * kb);
-    ut = *reinterpret_cast<const f32x4*>(Ut + p * (int64_t)C * dv + (int64_t)(v0 + m) * C +
-                                         16 * w + 4 * g);
+  auto wq_ptr = [&](const float* base, int64_t cl) {  // rows 16w + m of W<- or Qf
+    return base + pair_of(cl) * (int64_t)C * DK + (16 * w + m) * DK + 4 * g;
   };
-  auto load_qa = [&](int64_t cl) {  // Qf and A_qk rows 16w + m
+  auto load_u = [&](int64_t cl) {  // U~ column v0 + m, tokens 16w + 4g ..
+    ut = *reinterpret_cast<const f32x4*>(Ut + pair_of(cl) * (int64_t)C * dv +
+                                         (int64_t)(v0 + m) * C + 16 * w + 4 * g);
+  };
+  auto load_ak = [&](int64_t cl) {  // A_qk rows 16w + m; K~^T rows 16 (w + 4t) + m; G_n
     const int64_t p = pair_of(cl);
-    const float* Qp = Qf + p * (int64_t)C * DK + (16 * w + m) * DK + 4 * g;
-#pragma unroll
-    for (int kb = 0; kb < NK; ++kb) qa[kb] = *reinterpret_cast<const f32x4*>(Qp + 16 * kb);
     const float* Ap = Aqk + p * (int64_t)C * C + (16 * w + m) * C + 4 * g;
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) aa[kb] = *reinterpret_cast<const f32x4*>(Ap + 16 * kb);
-  };
-  auto load_k = [&](int64_t cl) {  // K~^T rows 16 (w + 4t) + m, and G at the chunk's end
-    const int64_t p = pair_of(cl);
     const float* Kp = Kft + p * (int64_t)C * DK + 4 * g;
 #pragma unroll
     for (int t = 0; t < NT; ++t)
@@ -387,49 +382,48 @@ __global__ __launch_bounds__(256) void ref_state_kernel(
     const int64_t n = min((int64_t)C, te - tb - cl * C);
     gn = gcum[p * C + n - 1];
   };
-  load_wu(0);
-  load_qa(0);
-  load_k(0);
+  {
+    const float* Wp = wq_ptr(W, 0);
+    const float* Qp = wq_ptr(Qf, 0);
+#pragma unroll
+    for (int kb = 0; kb < NK; ++kb) {
+      wa[kb] = *reinterpret_cast<const f32x4*>(Wp + 16 * kb);
+      qa[kb] = *reinterpret_cast<const f32x4*>(Qp + 16 * kb);
+    }
+  }
+  load_u(0);
+  load_ak(0);
+  // Two barriers per chunk: every read of S comes before the first, every write of S after
+  // the second, and U passes through LDS between them.
   for (int64_t cl = 0; cl < nchunks; ++cl) {
     const int64_t t0 = tb + cl * C;
     const int n = (int)min((int64_t)C, te - t0);
-    const bool more = cl + 1 < nchunks;
+    const int64_t nx = min(cl + 1, nchunks - 1);  // the last chunk reloads itself
     lds_barrier();  // the previous chunk's S update and U reads are complete
-    // ---- U = U~ - W<- S^T for tokens 16w .., this workgroup's columns
-    {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    // ---- U = U~ - W<- S^T and the state part Qf S^T of O, tokens 16w .., this
+    // workgroup's columns (two independent accumulator chains)
+    f32x4 pu = {0.f, 0.f, 0.f, 0.f}, po = {0.f, 0.f, 0.f, 0.f};
+    const float* Wn = wq_ptr(W, nx);
+    const float* Qn = wq_ptr(Qf, nx);
 #pragma unroll
-      for (int kb = 0; kb < NK; ++kb) {
-        const f32x4 b = *reinterpret_cast<const f32x4*>(&sm.S[m][16 * kb + 4 * g]);
-        acc = mma4(wa[kb], b, acc);
-      }
-      // lane (m, g) holds tokens 16w + 4g + i of column v0 + m
-      *reinterpret_cast<f32x4*>(&sm.Ut[m][16 * w + 4 * g]) = ut - acc;
-      if (more) load_wu(cl + 1);
+    for (int kb = 0; kb < NK; ++kb) {
+      const f32x4 b = *reinterpret_cast<const f32x4*>(&sm.S[m][16 * kb + 4 * g]);
+      pu = mma4(wa[kb], b, pu);
+      po = mma4(qa[kb], b, po);
+      wa[kb] = *reinterpret_cast<const f32x4*>(Wn + 16 * kb);
+      qa[kb] = *reinterpret_cast<const f32x4*>(Qn + 16 * kb);
     }
-    lds_barrier();  // U complete
-    // ---- O = Qf S^T + A_qk U for tokens 16w .. (A_qk is causal: tokens up to 16w + 15)
-    {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    // lane (m, g) holds tokens 16w + 4g + i of column v0 + m
+    *reinterpret_cast<f32x4*>(&sm.Ut[m][16 * w + 4 * g]) = ut - pu;
+    load_u(nx);
+    lds_barrier();  // U complete; S is not read again in this chunk
+    // ---- O += A_qk U (A_qk is causal: tokens up to 16w + 15)
 #pragma unroll
-      for (int kb = 0; kb < NK; ++kb) {
-        const f32x4 b = *reinterpret_cast<const f32x4*>(&sm.S[m][16 * kb + 4 * g]);
-        acc = mma4(qa[kb], b, acc);
+    for (int kb = 0; kb < 4; ++kb)
+      if (kb <= w) {
+        const f32x4 b = *reinterpret_cast<const f32x4*>(&sm.Ut[m][16 * kb + 4 * g]);
+        po = mma4(aa[kb], b, po);
       }
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-        if (kb <= w) {
-          const f32x4 b = *reinterpret_cast<const f32x4*>(&sm.Ut[m][16 * kb + 4 * g]);
-          acc = mma4(aa[kb], b, acc);
-        }
-      if (more) load_qa(cl + 1);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 16 * w + 4 * g + i;
-        if (r < n) st(out, ((t0 + r) * HV + hv) * (int64_t)dv + v0 + m, acc[i]);
-      }
-    }
-    lds_barrier();  // every wave has read S for this chunk
     // ---- S^T <- e^{G_n} S^T + K~^T U, dk tiles jd = w + 4t
     const float egn = expf((float)gn);
 #pragma unroll
@@ -444,7 +438,12 @@ __global__ __launch_bounds__(256) void ref_state_kernel(
       f32x4* sp = reinterpret_cast<f32x4*>(&sm.S[m][16 * (w + 4 * t) + 4 * g]);
       *sp = egn * *sp + acc;
     }
-    if (more) load_k(cl + 1);
+    load_ak(nx);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * w + 4 * g + i;
+      if (r < n) st(out, ((t0 + r) * HV + hv) * (int64_t)dv + v0 + m, po[i]);
+    }
   }
   lds_barrier();
   bool finite = true;

@@ -175,6 +175,20 @@ def test_random_shapes(case):
     compare(p, out, pool_gpu, oracle.prefill(p))
 
 
+@pytest.mark.parametrize("dtype,G", [("bf16", 2), ("bf16", 8), ("f32", 8)])
+def test_grouped_value_heads(dtype, G):
+    """G value heads per q/k head over more (chunk, q/k head) groups than the bf16 prep's
+    persistent grid holds at once (so each workgroup takes several groups, each as G
+    consecutive items that reuse the group's staged keys), with partial last chunks of
+    different lengths, so that consecutive groups differ only in their row count."""
+    lengths = [10000, 9000, 8001, 63]
+    H = 2
+    p = gdn_synth.make_problem(870 + G, lengths, H, H * G, 64, 64, dtype=dtype,
+                               state_std=0.1, a_mean=-1.0)
+    out, pool, _ = run_gpu(p, f"grouped-{dtype}-G{G}")
+    compare(p, out, pool, oracle.prefill(p))
+
+
 @pytest.mark.parametrize("B", [64, 65])
 def test_chunk_table_switch(B):
     """Up to 64 requests the bf16 chunk prep forms the chunk table itself; from 65 on a

@@ -49,6 +49,7 @@ constexpr int kRowWaves = kBwdRows / kRowsPerWave;  // waves of a row workgroup
 constexpr int kRowThreads = 64 * kRowWaves;
 template <int DK>
 constexpr int kSub = DK <= 128 ? 8 : 4;  // tokens recomputed and walked back at a time
+constexpr int kPf = 3;                   // tokens whose inputs are loaded ahead of use
 
 __device__ __forceinline__ float ldx(const void* p, int64_t i, bool bf16) {
   return bf16 ? __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(p)[i] << 16)
@@ -90,6 +91,56 @@ __device__ __forceinline__ float wave_sum(float x) {
   const auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
                                                   false);
   return __uint_as_float(h[0]) + __uint_as_float(h[1]);
+}
+
+// Sum over each 16-lane row, in every lane of the row (the first four steps above).
+__device__ __forceinline__ float row_sum(float x) {
+  x += dpp<0xB1>(x);
+  x += dpp<0x4E>(x);
+  x += dpp<0x141>(x);
+  return x + dpp<0x140>(x);
+}
+
+// One permlane swap step of a reduce-scatter: returns, in lanes whose (32- or 16-lane)
+// group comes first, a's sum over that group and its partner group, and b's in the
+// others. The permlane32 form pairs the wave's halves, the permlane16 form the two
+// 16-lane rows of each half (rows 0, 1 and rows 2, 3).
+__device__ __forceinline__ float swap_add32(float a, float b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float swap_add16(float a, float b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float lane_value(float x, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), lane));
+}
+
+// Wave sums of two values at once (a reduce-scatter: each step halves the lanes a value
+// occupies instead of reducing each value over all 64 lanes), as wave-uniform results.
+__device__ __forceinline__ void wave_sum2(float a, float b, float& sa, float& sb) {
+  float x = swap_add32(a, b);  // a in lanes 0-31, b in 32-63
+  x = row_sum(swap_add16(x, x));
+  sa = lane_value(x, 0);
+  sb = lane_value(x, 32);
+}
+
+// Wave sums of six values at once, as wave-uniform results.
+__device__ __forceinline__ void wave_sum6(const float (&v)[6], float (&r)[6]) {
+  const float p0 = swap_add32(v[0], v[1]);  // v0 | v1 by wave half
+  const float p1 = swap_add32(v[2], v[3]);  // v2 | v3
+  const float p2 = swap_add32(v[4], v[5]);  // v4 | v5
+  const float y0 = row_sum(swap_add16(p0, p1));  // rows: v0, v2, v1, v3
+  const float y1 = row_sum(swap_add16(p2, p2));  // rows: v4, v4, v5, v5
+  r[0] = lane_value(y0, 0);
+  r[1] = lane_value(y0, 32);
+  r[2] = lane_value(y0, 16);
+  r[3] = lane_value(y0, 48);
+  r[4] = lane_value(y1, 0);
+  r[5] = lane_value(y1, 32);
 }
 
 __device__ __forceinline__ float softplusf(float x) {
@@ -181,13 +232,16 @@ __device__ __forceinline__ void fetch(const BwdArgs& A, int64_t t, int h, int hv
 template <int DK>
 __device__ __forceinline__ void step(const Token<DK>& x, float (&s)[kRowsPerWave][DK / 64]) {
   constexpr int E = DK / 64;
+  static_assert(kRowsPerWave == 2, "the two rows' sums are reduced together");
+  float p[kRowsPerWave] = {}, sk[kRowsPerWave];
+#pragma unroll
+  for (int j = 0; j < kRowsPerWave; ++j)
+#pragma unroll
+    for (int e = 0; e < E; ++e) p[j] += s[j][e] * x.kh[e];
+  wave_sum2(p[0], p[1], sk[0], sk[1]);
 #pragma unroll
   for (int j = 0; j < kRowsPerWave; ++j) {
-    float p = 0.f;
-#pragma unroll
-    for (int e = 0; e < E; ++e) p += s[j][e] * x.kh[e];
-    const float sk = wave_sum(p);
-    const float c = x.beta * (x.v[j] - x.alpha * sk);
+    const float c = x.beta * (x.v[j] - x.alpha * sk[j]);
 #pragma unroll
     for (int e = 0; e < E; ++e) s[j][e] = x.alpha * s[j][e] + c * x.kh[e];
   }
@@ -201,12 +255,15 @@ __global__ __launch_bounds__(kRowThreads) void bwd_rows_kernel(BwdArgs A) {
   __shared__ float part[kRowWaves][SUB][NF];
   const int tid = threadIdx.x, l = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // Workgroup id -> (request, value head, row block): the row blocks of one (request, head)
+  // get consecutive ids of one XCD (ids are dealt to the 8 XCDs in turn), so they run
+  // together and read the same token rows through that XCD's L2.
   const int nrb = A.DV / kBwdRows;
-  const int64_t x = blockIdx.x;
-  const int rb = (int)(x % nrb);
-  const int64_t p = x / nrb;
+  const int64_t x = blockIdx.x, k8 = x >> 3;
+  const int rb = (int)(k8 % nrb);
+  const int64_t p = k8 / nrb * 8 + (x & 7);
+  if (p >= (int64_t)A.B * A.HV) return;  // the pair count rounded up to 8
   const int bq = (int)(p / A.HV), hv = (int)(p % A.HV);
-  if (bq >= A.B) return;
   const int h = hv / (A.HV / A.H);
   const int row0 = rb * kBwdRows + kRowsPerWave * w;  // this wave's first row
   const int64_t t0 = A.cu[bq], L = A.cu[bq + 1] - t0;
@@ -220,25 +277,36 @@ __global__ __launch_bounds__(kRowThreads) void bwd_rows_kernel(BwdArgs A) {
   float* DS0 = A.dstate0 + ((int64_t)bq * A.HV + hv) * A.DV * DK;
   auto ck_at = [&](int64_t c) { return A.ck + ((cbase + c) * A.HV + hv) * (int64_t)A.DV * DK; };
 
+  // Token inputs are loaded kPf tokens ahead of their use into a ring of register slots
+  // whose indices are compile-time constants (the loops over a group of tokens are
+  // unrolled), so several tokens' loads are in flight while the chain runs.
+  auto tok = [&](int64_t t) { return t0 + min(t, L - 1); };  // clamped into the request
+
   // ---- forward sweep: checkpoint every kCk tokens
   float s[kRowsPerWave][E];
 #pragma unroll
   for (int j = 0; j < kRowsPerWave; ++j)
 #pragma unroll
     for (int e = 0; e < E; ++e) s[j][e] = state_at(S0, j, e);
-  Token<DK> tk, nx;
-  if (L > 0) fetch<DK>(A, t0, h, hv, row0, l, tk);
-  for (int64_t t = 0; t < L; ++t) {
-    if (t % kCk == 0) {
-      float* c = ck_at(t / kCk);
+  {
+    Token<DK> fg[kCk];
+    if (L > 0) {
+#pragma unroll
+      for (int i = 0; i < kPf; ++i) fetch<DK>(A, tok(i), h, hv, row0, l, fg[i]);
+    }
+    for (int64_t tb = 0; tb < L; tb += kCk) {
+      float* c = ck_at(tb / kCk);
 #pragma unroll
       for (int j = 0; j < kRowsPerWave; ++j)
 #pragma unroll
         for (int e = 0; e < E; ++e) c[((int64_t)(row0 + j)) * DK + 64 * e + l] = s[j][e];
+#pragma unroll
+      for (int i = 0; i < kCk; ++i) {
+        // token tb + i + kPf (of this group or the next) into the slot it will use
+        fetch<DK>(A, tok(tb + i + kPf), h, hv, row0, l, fg[(i + kPf) % kCk]);
+        if (tb + i < L) step<DK>(fg[i], s);
+      }
     }
-    fetch<DK>(A, t0 + min(t + 1, L - 1), h, hv, row0, l, nx);  // the last token again at the end
-    step<DK>(tk, s);
-    tk = nx;
   }
   // the checkpoints are read back by the same lanes that wrote them: no barrier needed
 
@@ -249,90 +317,118 @@ __global__ __launch_bounds__(kRowThreads) void bwd_rows_kernel(BwdArgs A) {
 #pragma unroll
     for (int e = 0; e < E; ++e) D[j][e] = state_at(DS, j, e);
   const int64_t nsub = (L + SUB - 1) / SUB;
-  for (int64_t u = nsub - 1; u >= 0; --u) {
-    const int64_t u_lo = u * SUB, u_hi = min(u_lo + SUB, L);
-    const int64_t c = u_lo / kCk;
-    // recompute from the checkpoint before this sub-chunk
-    const float* cp = ck_at(c);
+  Token<DK> tg[SUB];                 // slot i: token u_lo + i of the sub-chunk
+  float dOg[SUB][kRowsPerWave];      // its rows of dout
+  float cpr[kRowsPerWave][E];        // the checkpoint the next sub-chunk starts from
+  auto load_ck = [&](int64_t u) {
+    const float* cp = ck_at(u * SUB / kCk);
 #pragma unroll
     for (int j = 0; j < kRowsPerWave; ++j)
 #pragma unroll
-      for (int e = 0; e < E; ++e) s[j][e] = cp[((int64_t)(row0 + j)) * DK + 64 * e + l];
-    fetch<DK>(A, t0 + c * kCk, h, hv, row0, l, tk);
-    for (int64_t t = c * kCk; t < u_lo; ++t) {
-      fetch<DK>(A, t0 + t + 1, h, hv, row0, l, nx);  // t + 1 <= u_lo < L
-      step<DK>(tk, s);
-      tk = nx;
+      for (int e = 0; e < E; ++e) cpr[j][e] = cp[((int64_t)(row0 + j)) * DK + 64 * e + l];
+  };
+  auto load_dout = [&](int64_t t, float (&d)[kRowsPerWave]) {
+    ld_rows(A.dout, (t * A.HV + hv) * (int64_t)A.DV + row0, A.bf16, d);
+  };
+  if (nsub > 0) {
+    load_ck(nsub - 1);
+#pragma unroll
+    for (int i = 0; i < kPf && i < SUB; ++i)
+      fetch<DK>(A, tok((nsub - 1) * SUB + i), h, hv, row0, l, tg[i]);
+  }
+  for (int64_t u = nsub - 1; u >= 0; --u) {
+    const int64_t u_lo = u * SUB, u_hi = min(u_lo + SUB, L);
+    const int64_t c = u_lo / kCk;
+#pragma unroll
+    for (int j = 0; j < kRowsPerWave; ++j)
+#pragma unroll
+      for (int e = 0; e < E; ++e) s[j][e] = cpr[j][e];
+    // recompute from the checkpoint to the sub-chunk (sub-chunks shorter than kCk only)
+    if (c * kCk < u_lo) {
+      Token<DK> pk, pn;
+      fetch<DK>(A, t0 + c * kCk, h, hv, row0, l, pk);
+      for (int64_t t = c * kCk; t < u_lo; ++t) {
+        fetch<DK>(A, t0 + t + 1, h, hv, row0, l, pn);  // t + 1 <= u_lo < L
+        step<DK>(pk, s);
+        pk = pn;
+      }
     }
     float sb[SUB][kRowsPerWave][E];  // S_{t-1} for the sub-chunk's tokens
-#pragma clang loop unroll(full)
+#pragma unroll
     for (int i = 0; i < SUB; ++i) {
+      if (i + kPf < SUB) fetch<DK>(A, tok(u_lo + i + kPf), h, hv, row0, l, tg[i + kPf]);
+      if (i < kPf && i < SUB) load_dout(tok(u_lo + SUB - 1 - i), dOg[SUB - 1 - i]);
       if (u_lo + i < u_hi) {
 #pragma unroll
         for (int j = 0; j < kRowsPerWave; ++j)
 #pragma unroll
           for (int e = 0; e < E; ++e) sb[i][j][e] = s[j][e];
-        fetch<DK>(A, t0 + min(u_lo + i + 1, u_hi - 1), h, hv, row0, l, nx);
-        step<DK>(tk, s);
-        tk = nx;
+        step<DK>(tg[i], s);
       }
     }
-    // s is now the state after the sub-chunk's last token. Walk back from that token; each
-    // step fetches the one before it.
-    fetch<DK>(A, t0 + u_hi - 1, h, hv, row0, l, tk);
-    float dO[kRowsPerWave], dOn[kRowsPerWave];
-    ld_rows(A.dout, ((t0 + u_hi - 1) * A.HV + hv) * (int64_t)A.DV + row0, A.bf16, dO);
-#pragma clang loop unroll(full)
+    if (u > 0) load_ck(u - 1);
+    // s is now the state after the sub-chunk's last token. Walk back from that token. The
+    // slots of the first kPf tokens are refilled kPf steps ahead; once a slot below kPf
+    // has been used, it takes the next sub-chunk's token.
+#pragma unroll
     for (int i = SUB - 1; i >= 0; --i) {
-      if (u_lo + i >= u_hi) continue;  // past the request's end (uniform)
-      const int64_t t = t0 + u_lo + i;
-      const int64_t tp = t0 + u_lo + max(i - 1, 0);
-      fetch<DK>(A, tp, h, hv, row0, l, nx);
-      ld_rows(A.dout, (tp * A.HV + hv) * (int64_t)A.DV + row0, A.bf16, dOn);
-      // S_t: the state before the next token, or the sub-chunk's end state
-      const bool last = (i == SUB - 1) || (u_lo + i + 1 >= u_hi);
-      float dqh[E] = {}, dkh[E] = {};
-      float dal = 0.f, dbe = 0.f;
-      float dvr[kRowsPerWave];
+      if (i - kPf >= 0) {
+        fetch<DK>(A, tok(u_lo + i - kPf), h, hv, row0, l, tg[i - kPf]);
+        load_dout(tok(u_lo + i - kPf), dOg[i - kPf]);
+      }
+      if (u_lo + i < u_hi) {  // (uniform)
+        const Token<DK>& tk = tg[i];
+        const float(&dO)[kRowsPerWave] = dOg[i];
+        const int64_t t = t0 + u_lo + i;
+        // S_t: the state before the next token, or the sub-chunk's end state
+        const bool last = (i == SUB - 1) || (u_lo + i + 1 >= u_hi);
+        float dqh[E] = {}, dkh[E] = {};
+        float dal = 0.f, dbe = 0.f;
+        float dvr[kRowsPerWave];
+        // the three row dot products of both rows, reduced together:
+        // (S_{t-1} kh, D kh, D . S_{t-1})
+        float dots[6] = {}, sums[6];
 #pragma unroll
-      for (int j = 0; j < kRowsPerWave; ++j) {
-        float pk = 0.f, dk_ = 0.f, ds = 0.f;
+        for (int j = 0; j < kRowsPerWave; ++j) {
+#pragma unroll
+          for (int e = 0; e < E; ++e) {
+            const float st = last ? s[j][e] : sb[i < SUB - 1 ? i + 1 : i][j][e];
+            D[j][e] += dO[j] * tk.qh[e];
+            dqh[e] += dO[j] * st;
+            dots[3 * j] += sb[i][j][e] * tk.kh[e];
+            dots[3 * j + 1] += D[j][e] * tk.kh[e];
+            dots[3 * j + 2] += D[j][e] * sb[i][j][e];
+          }
+        }
+        wave_sum6(dots, sums);
+#pragma unroll
+        for (int j = 0; j < kRowsPerWave; ++j) {
+          const float Spk = sums[3 * j], Dk = sums[3 * j + 1], Ds = sums[3 * j + 2];
+          dvr[j] = tk.beta * Dk;
+          dbe += Dk * (tk.v[j] - tk.alpha * Spk);
+          dal += Ds - tk.beta * Dk * Spk;
+          const float cS = -tk.alpha * tk.beta * Spk, cD = -tk.alpha * tk.beta * Dk;
+          const float cV = tk.beta * tk.v[j], cK = tk.alpha * tk.beta * Dk;
+#pragma unroll
+          for (int e = 0; e < E; ++e) {
+            dkh[e] += cS * D[j][e] + cD * sb[i][j][e] + cV * D[j][e];
+            D[j][e] = tk.alpha * D[j][e] - cK * tk.kh[e];
+          }
+        }
+        if (l == 0)
+          *reinterpret_cast<float2*>(A.dv + (t * A.HV + hv) * (int64_t)A.DV + row0) =
+              make_float2(dvr[0], dvr[1]);
 #pragma unroll
         for (int e = 0; e < E; ++e) {
-          const float st = last ? s[j][e] : sb[i < SUB - 1 ? i + 1 : i][j][e];
-          D[j][e] += dO[j] * tk.qh[e];
-          dqh[e] += dO[j] * st;
-          pk += sb[i][j][e] * tk.kh[e];
-          dk_ += D[j][e] * tk.kh[e];
-          ds += D[j][e] * sb[i][j][e];
+          part[w][i][64 * e + l] = dqh[e];
+          part[w][i][DK + 64 * e + l] = dkh[e];
         }
-        const float Spk = wave_sum(pk), Dk = wave_sum(dk_), Ds = wave_sum(ds);
-        dvr[j] = tk.beta * Dk;
-        dbe += Dk * (tk.v[j] - tk.alpha * Spk);
-        dal += Ds - tk.beta * Dk * Spk;
-        const float cS = -tk.alpha * tk.beta * Spk, cD = -tk.alpha * tk.beta * Dk;
-        const float cV = tk.beta * tk.v[j], cK = tk.alpha * tk.beta * Dk;
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-          dkh[e] += cS * D[j][e] + cD * sb[i][j][e] + cV * D[j][e];
-          D[j][e] = tk.alpha * D[j][e] - cK * tk.kh[e];
+        if (l == 0) {
+          part[w][i][2 * DK] = dal;
+          part[w][i][2 * DK + 1] = dbe;
         }
       }
-      if (l == 0)
-        *reinterpret_cast<float2*>(A.dv + (t * A.HV + hv) * (int64_t)A.DV + row0) =
-            make_float2(dvr[0], dvr[1]);
-#pragma unroll
-      for (int e = 0; e < E; ++e) {
-        part[w][i][64 * e + l] = dqh[e];
-        part[w][i][DK + 64 * e + l] = dkh[e];
-      }
-      if (l == 0) {
-        part[w][i][2 * DK] = dal;
-        part[w][i][2 * DK + 1] = dbe;
-      }
-      tk = nx;
-#pragma unroll
-      for (int j = 0; j < kRowsPerWave; ++j) dO[j] = dOn[j];
+      if (i < kPf && u > 0) fetch<DK>(A, tok((u - 1) * SUB + i), h, hv, row0, l, tg[i]);
     }
     __syncthreads();
     // this row block's partial sums for the sub-chunk's tokens
@@ -459,7 +555,7 @@ BwdLayout bwd_layout_for(const Shape& s) {
 }
 
 bool bwd_grids_fit(const Shape& s) {
-  const int64_t rows = s.B * s.HV * (s.dv / kBwdRows);
+  const int64_t rows = (s.B * s.HV + 7) / 8 * 8 * (s.dv / kBwdRows);
   const int64_t fin = (s.N * s.H + 3) / 4;
   return rows * kRowThreads <= 0xFFFFFFFFLL && fin * 256 <= 0xFFFFFFFFLL && s.HV <= 0x7FFFFFFF;
 }
@@ -512,7 +608,8 @@ hipError_t launch_backward(const Shape& s, const BwdLayout& L, char* ws, const v
   A.DV = s.dv;
   A.eps = kNormEps;
   A.bf16 = s.bf16 ? 1 : 0;
-  const dim3 rows((unsigned)(s.B * s.HV * (s.dv / kBwdRows))), fin((unsigned)((s.N * s.H + 3) / 4));
+  const dim3 rows((unsigned)((s.B * s.HV + 7) / 8 * 8 * (s.dv / kBwdRows))),
+      fin((unsigned)((s.N * s.H + 3) / 4));
 #define GDN_BWD_CASE(DKv)                                                              \
   if (s.dk == DKv) {                                                                   \
     if (s.N > 0) hipLaunchKernelGGL((bwd_token_kernel<DKv>), fin, dim3(256), 0, st, A); \

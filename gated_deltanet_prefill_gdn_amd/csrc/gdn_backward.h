@@ -12,7 +12,7 @@ struct BwdLayout {
   size_t chunk_off = 0;    // int32 [B + 1]
   size_t chunk_seq = 0;    // int32 [max_chunks]
   size_t ck = 0;           // float [max_chunks][HV][dv][dk]: state every 8 tokens
-  size_t part = 0;         // float [dv / 16][N][HV][2 dk + 2]: per-row-block token sums
+  size_t part = 0;         // float [dv / 32][N][HV][2 dk + 2]: per-row-block token sums
   size_t dal = 0;          // float [N][HV]
   size_t qn = 0, kn = 0;   // float [N][H][dk]: normalised q and k
   size_t ab = 0;           // float [N][HV][2]: alpha, beta

@@ -19,16 +19,19 @@
 //   token   one wave per (token, q/k head): the normalised q and k rows and, for the value
 //           heads sharing them, alpha and beta, written once so that the sweeps below only
 //           load them.
-//   rows    one workgroup per (request, value head, 16 rows), eight waves. A forward sweep
-//           keeps the rows' state every 8 tokens; the reverse sweep recomputes 8 tokens at a
-//           time (4 at dk = 256) from the checkpoint before them, holds the states before
-//           each of them in registers (the state after token i is the one before token
-//           i + 1, or the sub-chunk's end state), and walks them backwards. Wave w holds
-//           rows 2w and 2w + 1, lane l the dk elements l + 64 e: few registers per wave, so
-//           four waves share each SIMD and hide the latency of the token-to-token chain.
-//           Row dot products are wave sums; the per-token sums over the 16 rows go through
-//           LDS into a partial buffer per row block (no atomics: the result does not depend
-//           on scheduling).
+//   rows    one workgroup per (request, value head, 32 rows), sixteen waves (one
+//           workgroup per CU). A forward sweep keeps the rows' state every 8 tokens; the
+//           reverse sweep recomputes 8 tokens at a time (4 at dk = 256) from the checkpoint
+//           before them, holds the states before each of them in registers (the state
+//           after token i is the one before token i + 1, or the sub-chunk's end state), and
+//           walks them backwards. Wave w holds rows 2w and 2w + 1, lane l the dk elements
+//           l + 64 e: few registers per wave, so four waves share each SIMD and hide the
+//           latency of the token-to-token chain. Each group's token inputs (q, k rows,
+//           gates, the block's rows of v and dout) are staged once per workgroup in LDS,
+//           loaded by all threads one group ahead. A token's row dot products (two per
+//           row) are reduced together: a permlane reduce-scatter, then one 16-lane DPP
+//           reduction. The per-token sums over the 32 rows go through LDS into a partial
+//           buffer per row block (no atomics: the result does not depend on scheduling).
 //   finish  one wave per (token, q/k head): sums the partials over row blocks and over
 //           the value heads that share the q/k head, then the chain rule through the L2
 //           norm (dq = dqh / n - q (q . dqh) / n^3) and the gates (da = dalpha dalpha/dx,
@@ -43,13 +46,12 @@ namespace gdn {
 namespace {
 
 constexpr int kCk = 8;             // tokens between checkpoints
-constexpr int kBwdRows = 16;       // state rows per workgroup
+constexpr int kBwdRows = 32;       // state rows per workgroup
 constexpr int kRowsPerWave = 2;
 constexpr int kRowWaves = kBwdRows / kRowsPerWave;  // waves of a row workgroup
 constexpr int kRowThreads = 64 * kRowWaves;
 template <int DK>
 constexpr int kSub = DK <= 128 ? 8 : 4;  // tokens recomputed and walked back at a time
-constexpr int kPf = 3;                   // tokens whose inputs are loaded ahead of use
 
 __device__ __forceinline__ float ldx(const void* p, int64_t i, bool bf16) {
   return bf16 ? __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(p)[i] << 16)
@@ -228,6 +230,36 @@ __device__ __forceinline__ void fetch(const BwdArgs& A, int64_t t, int h, int hv
   ld_rows(A.v, (t * A.HV + hv) * (int64_t)A.DV + row0, A.bf16, x.v);
 }
 
+// The inputs of a group of SUB consecutive tokens, staged in LDS once per row workgroup
+// (every wave of the workgroup needs the same q and k rows and gates).
+template <int DK, int SUB>
+struct TokBuf {
+  alignas(16) float qh[SUB][DK];
+  float kh[SUB][DK];
+  float ab[SUB][2];             // alpha, beta
+  float v[SUB][kBwdRows];       // the workgroup's rows of v
+  float dout[SUB][kBwdRows];    // ... and of dout
+};
+
+// Token i of the staged group, for this lane's elements and the rows rl, rl + 1 of the
+// workgroup's block.
+template <int DK, int SUB>
+__device__ __forceinline__ void from_lds(const TokBuf<DK, SUB>& b, int i, int rl, int l,
+                                         Token<DK>& x) {
+  constexpr int E = DK / 64;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    x.qh[e] = b.qh[i][64 * e + l];
+    x.kh[e] = b.kh[i][64 * e + l];
+  }
+  const float2 ab = *reinterpret_cast<const float2*>(&b.ab[i][0]);
+  x.alpha = ab.x;
+  x.beta = ab.y;
+  const float2 vv = *reinterpret_cast<const float2*>(&b.v[i][rl]);
+  x.v[0] = vv.x;
+  x.v[1] = vv.y;
+}
+
 // One token's step on this wave's rows: s <- alpha s - alpha beta (s kh) kh + beta v kh.
 template <int DK>
 __device__ __forceinline__ void step(const Token<DK>& x, float (&s)[kRowsPerWave][DK / 64]) {
@@ -277,36 +309,92 @@ __global__ __launch_bounds__(kRowThreads) void bwd_rows_kernel(BwdArgs A) {
   float* DS0 = A.dstate0 + ((int64_t)bq * A.HV + hv) * A.DV * DK;
   auto ck_at = [&](int64_t c) { return A.ck + ((cbase + c) * A.HV + hv) * (int64_t)A.DV * DK; };
 
-  // Token inputs are loaded kPf tokens ahead of their use into a ring of register slots
-  // whose indices are compile-time constants (the loops over a group of tokens are
-  // unrolled), so several tokens' loads are in flight while the chain runs.
   auto tok = [&](int64_t t) { return t0 + min(t, L - 1); };  // clamped into the request
 
-  // ---- forward sweep: checkpoint every kCk tokens
+  // Token inputs go through an LDS buffer of SUB tokens, loaded cooperatively: every thread
+  // loads one 16-byte piece of the q, k rows and one gate, v or dout value of the next
+  // group into registers while the current group is used, and stores them after the
+  // barrier that ends the current group's use.
+  __shared__ TokBuf<DK, SUB> tb;
+  constexpr int P4 = SUB * DK / 4;  // 16-byte pieces of the group's q rows (and of its k rows)
+  struct Pf {
+    float4 qk;
+    float sm;
+  };
+  const int rl = kRowsPerWave * w;  // this wave's first row within the block
+  auto tok_load = [&](int64_t g0, bool with_q, Pf& r) {
+    if (tid < 2 * P4) {
+      const int which = tid / P4, rem = tid % P4, i = rem / (DK / 4), c4 = rem % (DK / 4);
+      if (which == 1 || with_q)
+        r.qk = *reinterpret_cast<const float4*>((which ? A.kn : A.qn) +
+                                                 (tok(g0 + i) * A.H + h) * DK + 4 * c4);
+    }
+    if (tid < 2 * SUB) {
+      const int i = tid >> 1;
+      r.sm = A.ab[(tok(g0 + i) * A.HV + hv) * 2 + (tid & 1)];
+    } else if (tid < 2 * SUB + SUB * kBwdRows) {
+      const int x = tid - 2 * SUB, i = x / kBwdRows, row = x % kBwdRows;
+      r.sm = ldx(A.v, (tok(g0 + i) * A.HV + hv) * (int64_t)A.DV + rb * kBwdRows + row, A.bf16);
+    } else if (with_q && tid < 2 * SUB + 2 * SUB * kBwdRows) {
+      const int x = tid - 2 * SUB - SUB * kBwdRows, i = x / kBwdRows, row = x % kBwdRows;
+      r.sm = ldx(A.dout, (tok(g0 + i) * A.HV + hv) * (int64_t)A.DV + rb * kBwdRows + row,
+                 A.bf16);
+    }
+  };
+  auto tok_store = [&](const Pf& r, bool with_q) {
+    if (tid < 2 * P4) {
+      const int which = tid / P4, rem = tid % P4, i = rem / (DK / 4), c4 = rem % (DK / 4);
+      if (which == 1)
+        *reinterpret_cast<float4*>(&tb.kh[i][4 * c4]) = r.qk;
+      else if (with_q)
+        *reinterpret_cast<float4*>(&tb.qh[i][4 * c4]) = r.qk;
+    }
+    if (tid < 2 * SUB) {
+      tb.ab[tid >> 1][tid & 1] = r.sm;
+    } else if (tid < 2 * SUB + SUB * kBwdRows) {
+      const int x = tid - 2 * SUB;
+      tb.v[x / kBwdRows][x % kBwdRows] = r.sm;
+    } else if (with_q && tid < 2 * SUB + 2 * SUB * kBwdRows) {
+      const int x = tid - 2 * SUB - SUB * kBwdRows;
+      tb.dout[x / kBwdRows][x % kBwdRows] = r.sm;
+    }
+  };
+  Pf pf;
+  pf.qk = float4{0.f, 0.f, 0.f, 0.f};
+  pf.sm = 0.f;
+
+  // ---- forward sweep: checkpoint every kCk tokens, groups of SUB tokens
   float s[kRowsPerWave][E];
 #pragma unroll
   for (int j = 0; j < kRowsPerWave; ++j)
 #pragma unroll
     for (int e = 0; e < E; ++e) s[j][e] = state_at(S0, j, e);
-  {
-    Token<DK> fg[kCk];
-    if (L > 0) {
-#pragma unroll
-      for (int i = 0; i < kPf; ++i) fetch<DK>(A, tok(i), h, hv, row0, l, fg[i]);
-    }
-    for (int64_t tb = 0; tb < L; tb += kCk) {
-      float* c = ck_at(tb / kCk);
+  if (L > 0) {
+    tok_load(0, false, pf);
+    tok_store(pf, false);
+  }
+  __syncthreads();
+  for (int64_t g0 = 0; g0 < L; g0 += SUB) {
+    const bool more = g0 + SUB < L;
+    if (more) tok_load(g0 + SUB, false, pf);
+    if (g0 % kCk == 0) {
+      float* c = ck_at(g0 / kCk);
 #pragma unroll
       for (int j = 0; j < kRowsPerWave; ++j)
 #pragma unroll
         for (int e = 0; e < E; ++e) c[((int64_t)(row0 + j)) * DK + 64 * e + l] = s[j][e];
+    }
 #pragma unroll
-      for (int i = 0; i < kCk; ++i) {
-        // token tb + i + kPf (of this group or the next) into the slot it will use
-        fetch<DK>(A, tok(tb + i + kPf), h, hv, row0, l, fg[(i + kPf) % kCk]);
-        if (tb + i < L) step<DK>(fg[i], s);
+    for (int i = 0; i < SUB; ++i) {
+      if (g0 + i < L) {
+        Token<DK> x;
+        from_lds(tb, i, rl, l, x);
+        step<DK>(x, s);
       }
     }
+    __syncthreads();  // every wave is done with this group
+    if (more) tok_store(pf, false);
+    __syncthreads();  // the next group is staged
   }
   // the checkpoints are read back by the same lanes that wrote them: no barrier needed
 
@@ -317,9 +405,7 @@ __global__ __launch_bounds__(kRowThreads) void bwd_rows_kernel(BwdArgs A) {
 #pragma unroll
     for (int e = 0; e < E; ++e) D[j][e] = state_at(DS, j, e);
   const int64_t nsub = (L + SUB - 1) / SUB;
-  Token<DK> tg[SUB];                 // slot i: token u_lo + i of the sub-chunk
-  float dOg[SUB][kRowsPerWave];      // its rows of dout
-  float cpr[kRowsPerWave][E];        // the checkpoint the next sub-chunk starts from
+  float cpr[kRowsPerWave][E];  // the checkpoint the next sub-chunk starts from
   auto load_ck = [&](int64_t u) {
     const float* cp = ck_at(u * SUB / kCk);
 #pragma unroll
@@ -327,23 +413,22 @@ __global__ __launch_bounds__(kRowThreads) void bwd_rows_kernel(BwdArgs A) {
 #pragma unroll
       for (int e = 0; e < E; ++e) cpr[j][e] = cp[((int64_t)(row0 + j)) * DK + 64 * e + l];
   };
-  auto load_dout = [&](int64_t t, float (&d)[kRowsPerWave]) {
-    ld_rows(A.dout, (t * A.HV + hv) * (int64_t)A.DV + row0, A.bf16, d);
-  };
   if (nsub > 0) {
     load_ck(nsub - 1);
-#pragma unroll
-    for (int i = 0; i < kPf && i < SUB; ++i)
-      fetch<DK>(A, tok((nsub - 1) * SUB + i), h, hv, row0, l, tg[i]);
+    tok_load((nsub - 1) * SUB, true, pf);
+    tok_store(pf, true);  // the forward sweep ended with a barrier
   }
+  __syncthreads();
   for (int64_t u = nsub - 1; u >= 0; --u) {
     const int64_t u_lo = u * SUB, u_hi = min(u_lo + SUB, L);
     const int64_t c = u_lo / kCk;
+    if (u > 0) tok_load(u_lo - SUB, true, pf);  // the next sub-chunk's inputs
 #pragma unroll
     for (int j = 0; j < kRowsPerWave; ++j)
 #pragma unroll
       for (int e = 0; e < E; ++e) s[j][e] = cpr[j][e];
-    // recompute from the checkpoint to the sub-chunk (sub-chunks shorter than kCk only)
+    // recompute from the checkpoint to the sub-chunk (sub-chunks shorter than kCk only),
+    // with the inputs from global memory one token ahead
     if (c * kCk < u_lo) {
       Token<DK> pk, pn;
       fetch<DK>(A, t0 + c * kCk, h, hv, row0, l, pk);
@@ -356,29 +441,25 @@ __global__ __launch_bounds__(kRowThreads) void bwd_rows_kernel(BwdArgs A) {
     float sb[SUB][kRowsPerWave][E];  // S_{t-1} for the sub-chunk's tokens
 #pragma unroll
     for (int i = 0; i < SUB; ++i) {
-      if (i + kPf < SUB) fetch<DK>(A, tok(u_lo + i + kPf), h, hv, row0, l, tg[i + kPf]);
-      if (i < kPf && i < SUB) load_dout(tok(u_lo + SUB - 1 - i), dOg[SUB - 1 - i]);
       if (u_lo + i < u_hi) {
 #pragma unroll
         for (int j = 0; j < kRowsPerWave; ++j)
 #pragma unroll
           for (int e = 0; e < E; ++e) sb[i][j][e] = s[j][e];
-        step<DK>(tg[i], s);
+        Token<DK> x;
+        from_lds(tb, i, rl, l, x);
+        step<DK>(x, s);
       }
     }
     if (u > 0) load_ck(u - 1);
-    // s is now the state after the sub-chunk's last token. Walk back from that token. The
-    // slots of the first kPf tokens are refilled kPf steps ahead; once a slot below kPf
-    // has been used, it takes the next sub-chunk's token.
+    // s is now the state after the sub-chunk's last token. Walk back from that token.
 #pragma unroll
     for (int i = SUB - 1; i >= 0; --i) {
-      if (i - kPf >= 0) {
-        fetch<DK>(A, tok(u_lo + i - kPf), h, hv, row0, l, tg[i - kPf]);
-        load_dout(tok(u_lo + i - kPf), dOg[i - kPf]);
-      }
       if (u_lo + i < u_hi) {  // (uniform)
-        const Token<DK>& tk = tg[i];
-        const float(&dO)[kRowsPerWave] = dOg[i];
+        Token<DK> tk;
+        from_lds(tb, i, rl, l, tk);
+        const float2 dO2 = *reinterpret_cast<const float2*>(&tb.dout[i][rl]);
+        const float dO[kRowsPerWave] = {dO2.x, dO2.y};
         const int64_t t = t0 + u_lo + i;
         // S_t: the state before the next token, or the sub-chunk's end state
         const bool last = (i == SUB - 1) || (u_lo + i + 1 >= u_hi);
@@ -428,9 +509,9 @@ __global__ __launch_bounds__(kRowThreads) void bwd_rows_kernel(BwdArgs A) {
           part[w][i][2 * DK + 1] = dbe;
         }
       }
-      if (i < kPf && u > 0) fetch<DK>(A, tok((u - 1) * SUB + i), h, hv, row0, l, tg[i]);
     }
-    __syncthreads();
+    __syncthreads();  // every wave is done with the staged inputs and has written its sums
+    if (u > 0) tok_store(pf, true);
     // this row block's partial sums for the sub-chunk's tokens
     const int nt = (int)(u_hi - u_lo);
     for (int idx = tid; idx < nt * NF; idx += kRowThreads) {

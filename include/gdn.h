@@ -206,14 +206,14 @@ gdn_status_t gdn_prefill_fwd_events(const void* q, const void* k, const void* v,
  * file is differentiated token by token (its chunked evaluation is the same map, pymllm
  * gdn_chunkwise page, Algorithm; awehrs.io "NRM training kernels", Results: the backward
  * is expensive because of the sequential structure): a forward sweep keeps each state
- * every chunk_size tokens, the reverse sweep recomputes from those and walks back.
+ * every 8 tokens, the reverse sweep recomputes from those and walks back.
  * Inputs: q, k, v, a, b, A_log, dt_bias, cache_indices, cu_seqlens and prob as for
  * gdn_prefill_fwd (q, k, v and dout in qkv_dtype); state_pool holds the INITIAL states
  * (the pool as it was before the forward call, which updates it in place; read only);
  * dout [N, HV, dv] in qkv_dtype; dstate [B, HV, dv, dk] fp32 in request order.
  * chunk_size must be 64. workspace: at least gdn_prefill_bwd_workspace_size bytes,
- * 256-byte aligned (checkpoints, about N/64 x HV x dv x dk x 4 bytes, and per-token sums
- * over blocks of 16 state rows, about N x HV x dv x (2 dk + 2) / 4 bytes).
+ * 256-byte aligned (checkpoints, about N/8 x HV x dv x dk x 4 bytes, and per-token sums
+ * over blocks of 32 state rows, about N x HV x dv x (2 dk + 2) / 8 bytes).
  * Arithmetic in fp32 throughout (no matrix cores); deterministic. N == 0 writes
  * dstate0 = dstate and zero dA_log, ddt_bias; B == 0 is a no-op. Errors as for
  * gdn_prefill_fwd: host checks before any launch. */

@@ -34,7 +34,6 @@ namespace {
 
 using namespace mfma;
 constexpr int C = 64;
-constexpr int kBV = 16;  // state rows (dv index) per state workgroup
 
 template <typename T>
 __device__ __forceinline__ float ld(const T* p, int64_t i);
@@ -314,22 +313,23 @@ __global__ __launch_bounds__(256) void ref_prep_kernel(
   }
 }
 
-template <int DK>
+template <int DK, int NC>
 struct RefStateSmem {
-  alignas(16) float S[kBV][DK + 4];  // this workgroup's rows of S, all dk columns
-  alignas(16) float Ut[kBV][C + 4];  // U of the current chunk, transposed: [column][token]
+  alignas(16) float S[16 * NC][DK + 4];  // this workgroup's rows of S, all dk columns
+  alignas(16) float Ut[16 * NC][C + 4];  // U of the current chunk, transposed: [column][token]
 };
 
-// One workgroup per (request, value head, kBV state rows); walks the request's chunks in
+// One workgroup per (request, value head, 16 NC state rows); walks the request's chunks in
 // order with its rows of S resident in LDS. Wave w owns chunk rows 16w .. 16w + 15 for U
-// and O, and dk rows 16 jd .. for jd = w (mod 4) of the state update. Each wave holds its
-// fragments of one chunk's operands in registers; a phase that has consumed its
-// fragments loads the next chunk's in their place, so their latency overlaps the rest of
-// the chunk. The workgroup's barriers wait for LDS traffic only.
-// Workgroup id -> (pair, slice): the dv / 16 slices of one (request, value head) pair get
+// and O, and dk rows 16 jd .. for jd = w (mod 4) of the state update; its fragments of
+// W<-, Qf, A_qk and K~ serve all NC column tiles. Each wave holds its fragments of the
+// chunk's operands in registers and loads the next chunk's into each register as soon as
+// the current product has taken it, so every load has about a chunk to land. The
+// workgroup's barriers wait for LDS traffic only.
+// Workgroup id -> (pair, slice): the slices of one (request, value head) pair get
 // consecutive ids of one XCD (ids are dealt to the 8 XCDs in turn), so they are dispatched
 // together and read the pair's per-chunk operands through that XCD's L2.
-template <typename Tin, int DK>
+template <typename Tin, int DK, int NC>
 __global__ __launch_bounds__(256) void ref_state_kernel(
     const int64_t* __restrict__ cu, const int64_t* __restrict__ cache_indices,
     const int32_t* __restrict__ chunk_off, const double* __restrict__ gcum,
@@ -339,13 +339,14 @@ __global__ __launch_bounds__(256) void ref_state_kernel(
     int32_t* __restrict__ nonfinite) {
   constexpr int NK = DK / 16;  // 16-wide contraction blocks over dk
   constexpr int NT = DK / 64;  // dk tiles of the state update per wave
-  __shared__ RefStateSmem<DK> sm;
-  const int nsl = dv / kBV;
+  constexpr int BV = 16 * NC;  // state rows of the workgroup
+  __shared__ RefStateSmem<DK, NC> sm;
+  const int nsl = dv / BV;
   const int64_t id = blockIdx.x, slot8 = id / 8;
   const int64_t pidx = slot8 / nsl * 8 + id % 8;
   if (pidx >= B * HV) return;  // the pair count rounded up to 8
   const int64_t seq = pidx / HV;
-  const int hv = (int)(pidx - seq * HV), v0 = (int)(slot8 % nsl) * kBV;
+  const int hv = (int)(pidx - seq * HV), v0 = (int)(slot8 % nsl) * BV;
   const int64_t tb = cu[seq], te = cu[seq + 1];
   const int64_t nchunks = path_chunks(te - tb, C, short_len);
   if (nchunks == 0) return;  // empty (slot untouched) or evaluated by the token recurrence
@@ -353,20 +354,19 @@ __global__ __launch_bounds__(256) void ref_state_kernel(
   const int64_t c0 = chunk_off[seq];
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, m = l & 15, g = l >> 4;
   float* Sg = state_pool + ((slot * HV + hv) * (int64_t)dv + v0) * DK;
-  for (int idx = tid; idx < kBV * DK; idx += 256) sm.S[idx / DK][idx % DK] = Sg[idx];
+  for (int idx = tid; idx < BV * DK; idx += 256) sm.S[idx / DK][idx % DK] = Sg[idx];
 
-  // this wave's fragments of a chunk (lane (m, g): 16-byte runs at contraction 4g). Each
-  // fragment of the next chunk is loaded into its register as soon as the current chunk's
-  // product has taken it, so every load has about a chunk to land.
-  f32x4 wa[NK], qa[NK], ut, aa[4], ka[NT][4];
+  // this wave's fragments of a chunk (lane (m, g): 16-byte runs at contraction 4g)
+  f32x4 wa[NK], qa[NK], ut[NC], aa[4], ka[NT][4];
   double gn;
   auto pair_of = [&](int64_t cl) { return (c0 + cl) * HV + hv; };
   auto wq_ptr = [&](const float* base, int64_t cl) {  // rows 16w + m of W<- or Qf
     return base + pair_of(cl) * (int64_t)C * DK + (16 * w + m) * DK + 4 * g;
   };
-  auto load_u = [&](int64_t cl) {  // U~ column v0 + m, tokens 16w + 4g ..
-    ut = *reinterpret_cast<const f32x4*>(Ut + pair_of(cl) * (int64_t)C * dv +
-                                         (int64_t)(v0 + m) * C + 16 * w + 4 * g);
+  auto load_u = [&](int64_t cl) {  // U~ columns v0 + 16c + m, tokens 16w + 4g ..
+    const float* up = Ut + pair_of(cl) * (int64_t)C * dv + (int64_t)(v0 + m) * C + 16 * w + 4 * g;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) ut[c] = *reinterpret_cast<const f32x4*>(up + 16 * c * C);
   };
   auto load_ak = [&](int64_t cl) {  // A_qk rows 16w + m; K~^T rows 16 (w + 4t) + m; G_n
     const int64_t p = pair_of(cl);
@@ -400,54 +400,72 @@ __global__ __launch_bounds__(256) void ref_state_kernel(
     const int n = (int)min((int64_t)C, te - t0);
     const int64_t nx = min(cl + 1, nchunks - 1);  // the last chunk reloads itself
     lds_barrier();  // the previous chunk's S update and U reads are complete
-    // ---- U = U~ - W<- S^T and the state part Qf S^T of O, tokens 16w .., this
-    // workgroup's columns (two independent accumulator chains)
-    f32x4 pu = {0.f, 0.f, 0.f, 0.f}, po = {0.f, 0.f, 0.f, 0.f};
+    // ---- U = U~ - W<- S^T and the state part Qf S^T of O, tokens 16w .., each column
+    // tile (independent accumulator chains)
+    f32x4 pu[NC], po[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      pu[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+      po[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
     const float* Wn = wq_ptr(W, nx);
     const float* Qn = wq_ptr(Qf, nx);
 #pragma unroll
     for (int kb = 0; kb < NK; ++kb) {
-      const f32x4 b = *reinterpret_cast<const f32x4*>(&sm.S[m][16 * kb + 4 * g]);
-      pu = mma4(wa[kb], b, pu);
-      po = mma4(qa[kb], b, po);
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const f32x4 b = *reinterpret_cast<const f32x4*>(&sm.S[16 * c + m][16 * kb + 4 * g]);
+        pu[c] = mma4(wa[kb], b, pu[c]);
+        po[c] = mma4(qa[kb], b, po[c]);
+      }
       wa[kb] = *reinterpret_cast<const f32x4*>(Wn + 16 * kb);
       qa[kb] = *reinterpret_cast<const f32x4*>(Qn + 16 * kb);
     }
-    // lane (m, g) holds tokens 16w + 4g + i of column v0 + m
-    *reinterpret_cast<f32x4*>(&sm.Ut[m][16 * w + 4 * g]) = ut - pu;
+    // lane (m, g) holds tokens 16w + 4g + i of column v0 + 16c + m
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+      *reinterpret_cast<f32x4*>(&sm.Ut[16 * c + m][16 * w + 4 * g]) = ut[c] - pu[c];
     load_u(nx);
     lds_barrier();  // U complete; S is not read again in this chunk
     // ---- O += A_qk U (A_qk is causal: tokens up to 16w + 15)
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
       if (kb <= w) {
-        const f32x4 b = *reinterpret_cast<const f32x4*>(&sm.Ut[m][16 * kb + 4 * g]);
-        po = mma4(aa[kb], b, po);
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+          const f32x4 b = *reinterpret_cast<const f32x4*>(&sm.Ut[16 * c + m][16 * kb + 4 * g]);
+          po[c] = mma4(aa[kb], b, po[c]);
+        }
       }
     // ---- S^T <- e^{G_n} S^T + K~^T U, dk tiles jd = w + 4t
     const float egn = expf((float)gn);
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        const f32x4 b = *reinterpret_cast<const f32x4*>(&sm.Ut[m][16 * kb + 4 * g]);
-        acc = mma4(ka[t][kb], b, acc);
+      for (int c = 0; c < NC; ++c) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+          const f32x4 b = *reinterpret_cast<const f32x4*>(&sm.Ut[16 * c + m][16 * kb + 4 * g]);
+          acc = mma4(ka[t][kb], b, acc);
+        }
+        // lane (m, g) holds S^T rows 16 jd + 4g + i, column 16c + m
+        f32x4* sp = reinterpret_cast<f32x4*>(&sm.S[16 * c + m][16 * (w + 4 * t) + 4 * g]);
+        *sp = egn * *sp + acc;
       }
-      // lane (m, g) holds S^T rows 16 jd + 4g + i, column m: S[m][16 jd + 4g + i]
-      f32x4* sp = reinterpret_cast<f32x4*>(&sm.S[m][16 * (w + 4 * t) + 4 * g]);
-      *sp = egn * *sp + acc;
     }
     load_ak(nx);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = 16 * w + 4 * g + i;
-      if (r < n) st(out, ((t0 + r) * HV + hv) * (int64_t)dv + v0 + m, po[i]);
-    }
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * w + 4 * g + i;
+        if (r < n) st(out, ((t0 + r) * HV + hv) * (int64_t)dv + v0 + 16 * c + m, po[c][i]);
+      }
   }
   lds_barrier();
   bool finite = true;
-  for (int idx = tid; idx < kBV * DK; idx += 256) {
+  for (int idx = tid; idx < BV * DK; idx += 256) {
     const float x = sm.S[idx / DK][idx % DK];
     Sg[idx] = x;
     finite = finite && __builtin_isfinite(x);
@@ -466,15 +484,24 @@ void launch_prep_t(const void* q, const void* k, const void* v, const int64_t* c
                      s.HV, w, ut, aqk, kft, qf);
 }
 
+// Two column tiles (32 state rows) per workgroup where those workgroups fill the device:
+// the per-chunk operands a workgroup must take in then serve twice the columns (the pass is
+// bound by that intake); one (16 rows) where they would not, which doubles the workgroups
+// walking the chains.
 template <typename Tin, int DK>
 void launch_state_t(const int64_t* cu, const int64_t* idx, const int32_t* chunk_off,
                     const double* gcum, const float* w, const float* ut, const float* aqk,
                     const float* kft, const float* qf, const Shape& s, float* pool, void* out,
                     int32_t* nonfinite, hipStream_t st) {
-  const int64_t blocks = (s.B * s.HV + 7) / 8 * 8 * (s.dv / kBV);
-  hipLaunchKernelGGL((ref_state_kernel<Tin, DK>), dim3((unsigned)blocks), dim3(256), 0, st, cu,
-                     idx, chunk_off, gcum, w, ut, aqk, kft, qf, s.B, s.HV, s.dv, s.short_len,
-                     pool, (Tin*)out, nonfinite);
+  const int64_t pairs8 = (s.B * s.HV + 7) / 8 * 8;
+  if (s.B * s.HV * (s.dv / 32) >= 256)
+    hipLaunchKernelGGL((ref_state_kernel<Tin, DK, 2>), dim3((unsigned)(pairs8 * (s.dv / 32))),
+                       dim3(256), 0, st, cu, idx, chunk_off, gcum, w, ut, aqk, kft, qf, s.B,
+                       s.HV, s.dv, s.short_len, pool, (Tin*)out, nonfinite);
+  else
+    hipLaunchKernelGGL((ref_state_kernel<Tin, DK, 1>), dim3((unsigned)(pairs8 * (s.dv / 16))),
+                       dim3(256), 0, st, cu, idx, chunk_off, gcum, w, ut, aqk, kft, qf, s.B,
+                       s.HV, s.dv, s.short_len, pool, (Tin*)out, nonfinite);
 }
 
 }  // namespace

@@ -31,9 +31,9 @@
 //     dk = 128; at dk = 256 the output waves store O themselves (see kStoreWaves).
 // Every operand comes straight from global memory into MFMA operand registers, in the
 // fragment orders the prep kernel wrote (one contiguous 1 KiB piece per fragment). Two
-// register sets (one at dk = 256) alternate between chunks, each reloaded right after its
-// last use (the output waves' q fragments right after Qh S^T, before barrier B), so every
-// load has about two chunks of the chain to land.
+// register sets (one at dk = 256 and with four column tiles) alternate between chunks,
+// each reloaded right after its last use (the output waves' q fragments right after
+// Qh S^T, before barrier B), so every load has about two chunks of the chain to land.
 //
 // Matrix-core operands, all fp16 with fp32 accumulation: W<- and S for P; normalised q
 // and S for Qh S^T; K~ and U for the update; A_qk and U for A_qk U. The state itself
@@ -420,17 +420,29 @@ hipError_t launch_mfma_state(const void* qf, const void* kf, const int64_t* cu_s
                              int32_t* nonfinite, hipStream_t st) {
   const _Float16* W = (const _Float16*)w;
   const _Float16* U = (const _Float16*)u;
-  // Two column tiles (32 state rows) per workgroup where those workgroups fill the device;
-  // otherwise one (16 rows), which doubles the workgroups walking the chains (measured at
-  // dk = dv = 256 on one request of 8 heads: 533 -> 442 us). dv is a multiple of 32. Loads
-  // run two chunks ahead, one at dk = 256, where two register sets would not fit.
-  const bool narrow = s.B * s.HV * (s.dv / 32) < 256;
+  // The widest column block whose workgroups still fill the device: four column tiles (64
+  // state rows, dk <= 128; every workgroup takes in the chunk's W<-, K~, Qh and A_qk in
+  // full, so wider blocks serve more columns per byte taken in: 410 -> 350 us on the
+  // varlen GQA workload), else two (32 rows), else one (16 rows), which doubles the
+  // workgroups walking the chains (at dk = dv = 256 on one request of 8 heads,
+  // 533 -> 442 us). dv is a multiple of 64. Loads run two chunks ahead with up to two
+  // column tiles at dk <= 128, one chunk ahead otherwise, where two register sets would
+  // not fit.
+  const int64_t pairs = s.B * s.HV;
+  const bool narrow = pairs * (s.dv / 32) < 256;
+  const bool wide = s.dk <= 128 && pairs * (s.dv / 64) >= 256;
 #define GDN_STATE_CASE(DKv, PDv)                                                           \
   if (s.dk == DKv) {                                                                       \
     if (narrow)                                                                            \
       return launch_state_t<DKv, 1, PDv>(qf, kf, cu_seqlens, cache_indices, chunk_off, W, U, \
                                          (const _Float16*)aqk, eg, s, state_pool, out,       \
                                          nonfinite, st);                                     \
+    if constexpr (DKv <= 128) {                                                            \
+      if (wide)                                                                            \
+        return launch_state_t<DKv, 4, 1>(qf, kf, cu_seqlens, cache_indices, chunk_off, W,  \
+                                         U, (const _Float16*)aqk, eg, s, state_pool, out,    \
+                                         nonfinite, st);                                     \
+    }                                                                                      \
     return launch_state_t<DKv, 2, PDv>(qf, kf, cu_seqlens, cache_indices, chunk_off, W, U,   \
                                        (const _Float16*)aqk, eg, s, state_pool, out,         \
                                        nonfinite, st);                                       \

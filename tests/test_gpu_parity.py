@@ -175,6 +175,22 @@ def test_random_shapes(case):
     compare(p, out, pool_gpu, oracle.prefill(p))
 
 
+@pytest.mark.parametrize("dk,dv", [(128, 128), (64, 64), (64, 256)])
+def test_wide_column_blocks(dk, dv):
+    """Enough (request, value head) pairs that the state pass takes four column tiles (64
+    state rows) per workgroup at dk <= 128 (bf16 inputs): ragged requests,
+    grouped heads, a shuffled pool, against the oracle element by element."""
+    rng = np.random.default_rng(880 + dk + dv)
+    B = 16
+    lengths = [int(x) for x in rng.integers(65, 260, B)]
+    pool = B + 3
+    p = gdn_synth.make_problem(880 + dk + dv, lengths, 8, 32, dk, dv, dtype="bf16", pool=pool,
+                               cache_indices=list(rng.permutation(pool)[:B]), state_std=0.1)
+    assert p.B * p.HV * (p.dv // 64) >= 256
+    out, pool_gpu, _ = run_gpu(p, f"wide-blocks-{dk}x{dv}")
+    compare(p, out, pool_gpu, oracle.prefill(p))
+
+
 @pytest.mark.parametrize("dtype,G", [("bf16", 2), ("bf16", 8), ("f32", 8)])
 def test_grouped_value_heads(dtype, G):
     """G value heads per q/k head over more (chunk, q/k head) groups than the bf16 prep's

@@ -34,23 +34,16 @@ namespace {
 
 using namespace mfma;
 constexpr int C = 64;
+constexpr double kLog2e = 1.4426950408889634;
 
-template <typename T>
-__device__ __forceinline__ float ld(const T* p, int64_t i);
-template <>
-__device__ __forceinline__ float ld<float>(const float* p, int64_t i) { return p[i]; }
-template <>
-__device__ __forceinline__ float ld<__hip_bfloat16>(const __hip_bfloat16* p, int64_t i) {
-  return __bfloat162float(p[i]);
-}
-// Four consecutive input elements from index i (the inputs need no alignment on this path).
-template <typename T>
-__device__ __forceinline__ f32x4 ld4(const T* p, int64_t i) {
-  return f32x4{ld(p, i), ld(p, i + 1), ld(p, i + 2), ld(p, i + 3)};
-}
 __device__ __forceinline__ void st(float* p, int64_t i, float x) { p[i] = x; }
-__device__ __forceinline__ void st(__hip_bfloat16* p, int64_t i, float x) {
-  p[i] = __float2bfloat16(x);  // round to nearest even
+
+// Four consecutive input elements from index i: one 16-byte load where the inputs are
+// 16-byte aligned (then every row is: dk and dv are multiples of 4), four otherwise (this
+// path accepts inputs aligned to their element only).
+__device__ __forceinline__ f32x4 ld4(const float* p, int64_t i, bool aligned) {
+  if (aligned) return *reinterpret_cast<const f32x4*>(p + i);
+  return f32x4{p[i], p[i + 1], p[i + 2], p[i + 3]};
 }
 
 // Four fp32 MFMA steps over 16 contraction indices: step s takes k = 4g + s.
@@ -68,19 +61,19 @@ struct RefPrepSmem {
   alignas(16) float A[C][C + 4];      // A, then T1 = diag(e^G) T diag(beta r_k), then T2
   alignas(16) float T[C][C + 4];      // T = (I + A)^-1
   alignas(16) float X[4][16][20];     // per wave: one 16 x 16 tile of the blocked inverse
-  double G[C];
-  float bt[C], rk[C], rq[C], kd[C], eq[C];
+  double G2[C];  // G log2(e)
+  float bt[C], rk[C], rq[C], kd[C], eq[C], eg[C];
 };
 
 // One workgroup per (global chunk, value head); wave w owns chunk rows 16w .. 16w + 15.
 // Head dims are compile-time constants, so every staging loop has a fixed trip count and
 // issues its loads together.
-template <typename Tin, int DK, int DV>
+template <int DK, int DV>
 __global__ __launch_bounds__(256) void ref_prep_kernel(
-    const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* __restrict__ v,
+    const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
     const int64_t* __restrict__ cu, const int32_t* __restrict__ chunk_off,
     const int32_t* __restrict__ chunk_seq, const double* __restrict__ gcum,
-    const float* __restrict__ beta, int H, int HV, float* __restrict__ W,
+    const float* __restrict__ beta, int H, int HV, int aligned, float* __restrict__ W,
     float* __restrict__ Ut, float* __restrict__ Aqk, float* __restrict__ Kft,
     float* __restrict__ Qf) {
   constexpr int dk = DK, dv = DV;
@@ -96,14 +89,17 @@ __global__ __launch_bounds__(256) void ref_prep_kernel(
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, m = l & 15, g = l >> 4;
   const int I = w;  // this wave's row tile
 
+  const bool al = aligned != 0;
   if (tid < C) {
-    sm.G[tid] = gcum[pair * C + tid];
+    sm.G2[tid] = gcum[pair * C + tid] * kLog2e;
     sm.bt[tid] = beta[pair * C + tid];
   }
+  // K rows in 4-element pieces: piece u of thread tid is e = tid + 256u, row e / (dk / 4)
 #pragma unroll
-  for (int idx = tid; idx < C * dk; idx += 256) {
-    const int r = idx / dk, j = idx - r * dk;
-    sm.tile[r][j] = r < n ? ld(k, ((t0 + r) * H + h) * (int64_t)dk + j) : 0.f;
+  for (int e = tid; e < C * dk / 4; e += 256) {
+    const int r = e / (dk / 4), j = 4 * (e % (dk / 4));
+    *reinterpret_cast<f32x4*>(&sm.tile[r][j]) =
+        r < n ? ld4(k, ((t0 + r) * H + h) * (int64_t)dk + j, al) : f32x4{0.f, 0.f, 0.f, 0.f};
   }
   // This lane's fragments of Q: row qr = 16 I + m, columns 16 kb + 4g .. 16 kb + 4g + 3
   // (zero past n), the A operand of A_qk and the source of Qf. Q is read once.
@@ -111,15 +107,16 @@ __global__ __launch_bounds__(256) void ref_prep_kernel(
   f32x4 qa[dk / 16];
 #pragma unroll
   for (int kb = 0; kb < dk / 16; ++kb)
-    qa[kb] = qr < n ? ld4(q, ((t0 + qr) * H + h) * (int64_t)dk + 16 * kb + 4 * g)
+    qa[kb] = qr < n ? ld4(q, ((t0 + qr) * H + h) * (int64_t)dk + 16 * kb + 4 * g, al)
                     : f32x4{0.f, 0.f, 0.f, 0.f};
-  // V rows, loaded now and staged in LDS once the K tile is no longer read
-  constexpr int kVPer = C * dv / 256;
-  float vr[kVPer];
+  // V rows, loaded now (in the same pieces) and staged in LDS once the K tile is no longer
+  // read
+  constexpr int kVPer = C * dv / 4 / 256;
+  f32x4 vr[kVPer];
 #pragma unroll
   for (int i = 0; i < kVPer; ++i) {
-    const int idx = tid + 256 * i, r = idx / dv, j = idx - r * dv;
-    vr[i] = r < n ? ld(v, ((t0 + r) * HV + hv) * (int64_t)dv + j) : 0.f;
+    const int e = tid + 256 * i, r = e / (dv / 4), j = 4 * (e % (dv / 4));
+    vr[i] = r < n ? ld4(v, ((t0 + r) * HV + hv) * (int64_t)dv + j, al) : f32x4{0.f, 0.f, 0.f, 0.f};
   }
   __syncthreads();
   // inverse row norms: lane (m, g) sums its columns of row qr, the four lanes of a row add up
@@ -224,16 +221,19 @@ __global__ __launch_bounds__(256) void ref_prep_kernel(
     }
   }
   __syncthreads();
-  // ---- row scales and T1 = diag(e^G) T diag(beta r_k)
-  const double Gn = sm.G[n - 1];
+  // ---- row scales and T1 = diag(e^G) T diag(beta r_k). Decays are powers of two of
+  // non-positive exponent differences (G is non-increasing), formed with v_exp_f32.
+  const double G2n = sm.G2[n - 1];
   if (tid < C) {
-    sm.kd[tid] = tid < n ? expf((float)(Gn - sm.G[tid])) * sm.rk[tid] : 0.f;
-    sm.eq[tid] = tid < n ? expf((float)sm.G[tid]) * sm.rq[tid] : 0.f;
+    const float egt = __builtin_amdgcn_exp2f((float)sm.G2[tid]);
+    sm.eg[tid] = tid < n ? egt : 0.f;
+    sm.kd[tid] = tid < n ? __builtin_amdgcn_exp2f((float)(G2n - sm.G2[tid])) * sm.rk[tid] : 0.f;
+    sm.eq[tid] = tid < n ? egt * sm.rq[tid] : 0.f;
   }
+  __syncthreads();
   for (int idx = tid; idx < C * C; idx += 256) {
     const int r = idx / C, i = idx % C;
-    sm.A[r][i] = (i <= r && r < n) ? expf((float)sm.G[r]) * sm.T[r][i] * sm.bt[i] * sm.rk[i]
-                                   : 0.f;
+    sm.A[r][i] = (i <= r) ? sm.eg[r] * sm.T[r][i] * sm.bt[i] * sm.rk[i] : 0.f;
   }
   __syncthreads();
   // ---- W<- = T1 K (rows of tile I), A_qk (tiles J <= I), K~^T, Qf
@@ -268,10 +268,11 @@ __global__ __launch_bounds__(256) void ref_prep_kernel(
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int rr = 16 * I + 4 * g + i, col = 16 * J + m;
-        Ap[rr * C + col] = (J <= I && col <= rr && rr < n)
-                               ? expf((float)(sm.G[rr] - sm.G[col])) * sm.rq[rr] * sm.rk[col] *
-                                     acc[J][i]
-                               : 0.f;
+        Ap[rr * C + col] =
+            (J <= I && col <= rr && rr < n)
+                ? __builtin_amdgcn_exp2f((float)(sm.G2[rr] - sm.G2[col])) * sm.rq[rr] *
+                      sm.rk[col] * acc[J][i]
+                : 0.f;
       }
   }
   float* Kp = Kft + pair * (int64_t)C * dk;  // K~ transposed: [dk][C]
@@ -289,13 +290,14 @@ __global__ __launch_bounds__(256) void ref_prep_kernel(
   // ---- U~ = T2 V with T2 = (Gamma o T) diag(beta), written transposed: [dv][C]
   for (int idx = tid; idx < C * C; idx += 256) {
     const int r = idx / C, i = idx % C;
-    sm.A[r][i] = (i <= r && r < n) ? expf((float)(sm.G[r] - sm.G[i])) * sm.T[r][i] * sm.bt[i]
-                                   : 0.f;
+    sm.A[r][i] = (i <= r && r < n)
+                     ? __builtin_amdgcn_exp2f((float)(sm.G2[r] - sm.G2[i])) * sm.T[r][i] * sm.bt[i]
+                     : 0.f;
   }
 #pragma unroll
   for (int i = 0; i < kVPer; ++i) {
-    const int idx = tid + 256 * i, r = idx / dv, j = idx - r * dv;
-    sm.tile[r][j] = vr[i];
+    const int e = tid + 256 * i, r = e / (dv / 4), j = 4 * (e % (dv / 4));
+    *reinterpret_cast<f32x4*>(&sm.tile[r][j]) = vr[i];
   }
   __syncthreads();
   float* Up = Ut + pair * (int64_t)C * dv;
@@ -329,13 +331,13 @@ struct RefStateSmem {
 // Workgroup id -> (pair, slice): the slices of one (request, value head) pair get
 // consecutive ids of one XCD (ids are dealt to the 8 XCDs in turn), so they are dispatched
 // together and read the pair's per-chunk operands through that XCD's L2.
-template <typename Tin, int DK, int NC>
+template <int DK, int NC>
 __global__ __launch_bounds__(256) void ref_state_kernel(
     const int64_t* __restrict__ cu, const int64_t* __restrict__ cache_indices,
     const int32_t* __restrict__ chunk_off, const double* __restrict__ gcum,
     const float* __restrict__ W, const float* __restrict__ Ut, const float* __restrict__ Aqk,
     const float* __restrict__ Kft, const float* __restrict__ Qf, int64_t B, int HV, int dv,
-    int64_t short_len, float* __restrict__ state_pool, Tin* __restrict__ out,
+    int64_t short_len, float* __restrict__ state_pool, float* __restrict__ out,
     int32_t* __restrict__ nonfinite) {
   constexpr int NK = DK / 16;  // 16-wide contraction blocks over dk
   constexpr int NT = DK / 64;  // dk tiles of the state update per wave
@@ -473,53 +475,52 @@ __global__ __launch_bounds__(256) void ref_state_kernel(
   if (!finite) *nonfinite = 1;
 }
 
-template <typename Tin, int DK, int DV>
+template <int DK, int DV>
 void launch_prep_t(const void* q, const void* k, const void* v, const int64_t* cu,
                    const int32_t* chunk_off, const int32_t* chunk_seq, const double* gcum,
                    const float* beta, const Shape& s, int64_t max_chunks, float* w, float* ut,
                    float* aqk, float* kft, float* qf, hipStream_t st) {
   const dim3 grid((unsigned)max_chunks, (unsigned)s.HV);
-  hipLaunchKernelGGL((ref_prep_kernel<Tin, DK, DV>), grid, dim3(256), 0, st, (const Tin*)q,
-                     (const Tin*)k, (const Tin*)v, cu, chunk_off, chunk_seq, gcum, beta, s.H,
-                     s.HV, w, ut, aqk, kft, qf);
+  const int aligned = (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v) & 15) == 0;
+  hipLaunchKernelGGL((ref_prep_kernel<DK, DV>), grid, dim3(256), 0, st, (const float*)q,
+                     (const float*)k, (const float*)v, cu, chunk_off, chunk_seq, gcum, beta, s.H,
+                     s.HV, aligned, w, ut, aqk, kft, qf);
 }
 
 // Two column tiles (32 state rows) per workgroup where those workgroups fill the device:
 // the per-chunk operands a workgroup must take in then serve twice the columns (the pass is
 // bound by that intake); one (16 rows) where they would not, which doubles the workgroups
 // walking the chains.
-template <typename Tin, int DK>
+template <int DK>
 void launch_state_t(const int64_t* cu, const int64_t* idx, const int32_t* chunk_off,
                     const double* gcum, const float* w, const float* ut, const float* aqk,
                     const float* kft, const float* qf, const Shape& s, float* pool, void* out,
                     int32_t* nonfinite, hipStream_t st) {
   const int64_t pairs8 = (s.B * s.HV + 7) / 8 * 8;
   if (s.B * s.HV * (s.dv / 32) >= 256)
-    hipLaunchKernelGGL((ref_state_kernel<Tin, DK, 2>), dim3((unsigned)(pairs8 * (s.dv / 32))),
+    hipLaunchKernelGGL((ref_state_kernel<DK, 2>), dim3((unsigned)(pairs8 * (s.dv / 32))),
                        dim3(256), 0, st, cu, idx, chunk_off, gcum, w, ut, aqk, kft, qf, s.B,
-                       s.HV, s.dv, s.short_len, pool, (Tin*)out, nonfinite);
+                       s.HV, s.dv, s.short_len, pool, (float*)out, nonfinite);
   else
-    hipLaunchKernelGGL((ref_state_kernel<Tin, DK, 1>), dim3((unsigned)(pairs8 * (s.dv / 16))),
+    hipLaunchKernelGGL((ref_state_kernel<DK, 1>), dim3((unsigned)(pairs8 * (s.dv / 16))),
                        dim3(256), 0, st, cu, idx, chunk_off, gcum, w, ut, aqk, kft, qf, s.B,
-                       s.HV, s.dv, s.short_len, pool, (Tin*)out, nonfinite);
+                       s.HV, s.dv, s.short_len, pool, (float*)out, nonfinite);
 }
 
 }  // namespace
 
+// fp32 inputs only (bf16 inputs take the matrix-core kernels).
 hipError_t launch_ref_prep(const void* q, const void* k, const void* v,
                            const int64_t* cu_seqlens, const int32_t* chunk_off,
                            const int32_t* chunk_seq, const double* gcum, const float* beta,
                            const Shape& s, int64_t max_chunks, float* w, float* ut, float* aqk,
                            float* kft, float* qf, hipStream_t st) {
-#define GDN_REF_PREP(DKv, DVv)                                                                 \
-  if (s.dk == DKv && s.dv == DVv) {                                                            \
-    if (s.bf16)                                                                                \
-      launch_prep_t<__hip_bfloat16, DKv, DVv>(q, k, v, cu_seqlens, chunk_off, chunk_seq, gcum, \
-                                              beta, s, max_chunks, w, ut, aqk, kft, qf, st);   \
-    else                                                                                       \
-      launch_prep_t<float, DKv, DVv>(q, k, v, cu_seqlens, chunk_off, chunk_seq, gcum, beta, s, \
-                                     max_chunks, w, ut, aqk, kft, qf, st);                     \
-    return hipGetLastError();                                                                  \
+  if (s.bf16) return hipErrorInvalidValue;
+#define GDN_REF_PREP(DKv, DVv)                                                              \
+  if (s.dk == DKv && s.dv == DVv) {                                                         \
+    launch_prep_t<DKv, DVv>(q, k, v, cu_seqlens, chunk_off, chunk_seq, gcum, beta, s,       \
+                            max_chunks, w, ut, aqk, kft, qf, st);                           \
+    return hipGetLastError();                                                               \
   }
   GDN_REF_PREP(64, 64)
   GDN_REF_PREP(64, 128)
@@ -539,15 +540,12 @@ hipError_t launch_ref_state(const int64_t* cu_seqlens, const int64_t* cache_indi
                             const float* ut, const float* aqk, const float* kft, const float* qf,
                             const Shape& s, float* state_pool, void* out, int32_t* nonfinite,
                             hipStream_t st) {
-#define GDN_REF_STATE(DKv)                                                                     \
-  if (s.dk == DKv) {                                                                           \
-    if (s.bf16)                                                                                \
-      launch_state_t<__hip_bfloat16, DKv>(cu_seqlens, cache_indices, chunk_off, gcum, w, ut,   \
-                                          aqk, kft, qf, s, state_pool, out, nonfinite, st);    \
-    else                                                                                       \
-      launch_state_t<float, DKv>(cu_seqlens, cache_indices, chunk_off, gcum, w, ut, aqk, kft, \
-                                 qf, s, state_pool, out, nonfinite, st);                       \
-    return hipGetLastError();                                                                  \
+  if (s.bf16) return hipErrorInvalidValue;
+#define GDN_REF_STATE(DKv)                                                                  \
+  if (s.dk == DKv) {                                                                        \
+    launch_state_t<DKv>(cu_seqlens, cache_indices, chunk_off, gcum, w, ut, aqk, kft, qf, s, \
+                        state_pool, out, nonfinite, st);                                    \
+    return hipGetLastError();                                                               \
   }
   GDN_REF_STATE(64)
   GDN_REF_STATE(128)

@@ -175,6 +175,37 @@ def test_random_shapes(case):
     compare(p, out, pool_gpu, oracle.prefill(p))
 
 
+@pytest.mark.parametrize("dk,dv", [(64, 64), (128, 256)])
+def test_fp32_inputs_aligned_to_their_element_only(dk, dv):
+    """fp32 q, k and v that start 4 bytes past a 16-byte boundary (views one element into
+    their buffers): the fp32 kernels read them element by element, and the short requests
+    (the batch's mean length is below 64) stay chunked, since the token recurrence needs
+    16-byte alignment. Against the oracle, and bit for bit equal to the same call on the
+    aligned tensors with every request chunked."""
+    import torch
+    import gated_deltanet_prefill_gdn_amd as gdn
+    lengths = [5, 40, 0, 130, 1, 77]
+    p = gdn_synth.make_problem(860 + dk, lengths, 2, 4, dk, dv, dtype="f32", pool=8,
+                               cache_indices=[7, 2, 5, 0, 3, 6], state_std=0.2)
+    d = to_device(p)
+
+    def shifted(x):
+        buf = torch.empty(x.numel() + 1, dtype=x.dtype, device=x.device)
+        y = buf[1:].view(x.shape)
+        y.copy_(x)
+        return y
+
+    d2 = dict(d, q=shifted(d["q"]), k=shifted(d["k"]), v=shifted(d["v"]),
+              state_pool=d["state_pool"].clone())
+    assert all(t.data_ptr() % 16 == 4 for t in (d2["q"], d2["k"], d2["v"]))
+    out, pool_gpu, _ = run_gpu(p, f"fp32-unaligned-{dk}x{dv}", dev_tensors=d2)
+    compare(p, out, pool_gpu, oracle.prefill(p))
+    out_a, pool_a, _ = run_gpu(p, f"fp32-aligned-{dk}x{dv}", dev_tensors=d,
+                               flags=gdn.GDN_FLAG_CHUNK_ALL)
+    np.testing.assert_array_equal(out, out_a)
+    np.testing.assert_array_equal(pool_gpu, pool_a)
+
+
 @pytest.mark.parametrize("dk,dv", [(128, 128), (64, 64), (64, 256)])
 def test_wide_column_blocks(dk, dv):
     """Enough (request, value head) pairs that the state pass takes four column tiles (64

@@ -85,7 +85,8 @@ static bool prefill_grids_fit(const Shape& s, Path path, int64_t max_chunks) {
     return true;
   }
   // column-slice state kernel: (request, value head) pairs rounded up to 8, times dv / 32
-  // slices (dv / 16 where those would not fill the device), workgroups of five waves (the
+  // slices (dv / 16 where those would not fill the device, dv / 64 where those would),
+  // workgroups of five waves; the bound below takes the most slices the rule can pick (the
   // prep kernel's grid is the device's resident capacity)
   const int64_t slices = s.B * s.HV * (s.dv / 32) < 256 ? s.dv / 16 : s.dv / 32;
   return grid_fits((s.B * s.HV + 7) / 8 * 8 * slices, 64 * 5);

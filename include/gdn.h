@@ -171,10 +171,11 @@ gdn_status_t gdn_prefill_nonfinite(const void* workspace, size_t workspace_bytes
 /* Which kernels run the sequential state pass (stages 2-4 below) of a prefill call of this
  * shape; a function of the descriptor only. Host only, no HIP calls. Returns -1 for an
  * invalid or unsupported descriptor or chunk size. For profiling and tests.
- *   GDN_SCHEDULE_COLUMN_SLICES  bf16 inputs: one workgroup per (request, value head, 32 state
- *                               rows), each walking its request's chunks; used when those
- *                               workgroups alone fill the device, when dk = 256 and above 64
- *                               requests.
+ *   GDN_SCHEDULE_COLUMN_SLICES  bf16 inputs: one workgroup per (request, value head, 16, 32
+ *                               or 64 state rows: the widest that still fills the device),
+ *                               each walking its request's chunks; used when the 32-row
+ *                               workgroups alone fill the device, when dk = 256 and above
+ *                               64 requests.
  *   GDN_SCHEDULE_SEGMENTS       bf16 inputs: requests cut into segments of chunks (operator
  *                               pass, combine, output pass) with one workgroup per
  *                               (segment, value head, 128 state rows).

@@ -15,7 +15,8 @@
 //   Qf   = diag(e^G r_q) Q
 // (the prep kernel, one workgroup per chunk and value head), and then, sequentially over
 // the chunks of a request (pymllm gdn_chunkwise page, Algorithm, steps 2 and 3, in row
-// convention; the state kernel, one workgroup per request, value head and 16 state rows):
+// convention; the state kernel, one workgroup per request, value head and 16 or 32 state
+// rows):
 //   U     = U~ - W<- S^T
 //   O     = Qf S^T + A_qk U
 //   S_new = e^{G_n} S + U^T K~

@@ -1030,7 +1030,7 @@ def bench_backward(args):
     print(json.dumps(res), flush=True)
 
 
-CROSSOVER_LENGTHS = (1, 2, 4, 8, 12, 16, 20, 24, 32, 48, 64)
+CROSSOVER_LENGTHS = (1, 2, 4, 8, 9, 10, 11, 12, 16, 20, 24, 32, 48, 64)
 
 
 def bench_crossover(args):

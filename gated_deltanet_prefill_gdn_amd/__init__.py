@@ -48,7 +48,7 @@ GDN_SCHEDULE_SEGMENTS = 1
 GDN_SCHEDULE_FP32 = 2
 
 GDN_FLAG_CHUNK_ALL = 1   # gdn_problem_t.flags: chunk every request
-GDN_SHORT_REQUEST = 12   # requests of at most this many tokens take the token recurrence
+GDN_SHORT_REQUEST = 10   # requests of at most this many tokens take the token recurrence
 GDN_SPLIT_MEAN_LENGTH = 64  # ... in batches whose mean request length is at most this
 
 EXPORTED = ("gdn_prefill_workspace_size", "gdn_prefill_state_schedule", "gdn_prefill_fwd",

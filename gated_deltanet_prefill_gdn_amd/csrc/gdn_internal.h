@@ -59,7 +59,7 @@ struct Shape {
 // every request takes 1.59 ms at L = 1, 1.61 ms at 12 and 16; with the recurrence for the
 // short ones (whose call still launches the chunked kernels, which find nothing to do)
 // 0.53 ms at 1, 1.36 ms at 12 and 1.68 ms at 16.
-constexpr int64_t kShortRequest = 12;  // GDN_SHORT_REQUEST of the public header
+constexpr int64_t kShortRequest = 10;  // GDN_SHORT_REQUEST of the public header
 // The recurrence's launch costs a few microseconds even when it finds no short request
 // (5 us at 8 requests and 32 value heads), so a call splits only when the mean request
 // length N / B is at most this; longer batches are chunked whole.

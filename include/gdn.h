@@ -89,7 +89,7 @@ typedef struct {
  * on the same stream), which is faster for them: a request that short still costs the
  * chunked path a whole chunk of intermediates per value head. Any other bit is an error. */
 #define GDN_FLAG_CHUNK_ALL 1
-#define GDN_SHORT_REQUEST 12
+#define GDN_SHORT_REQUEST 10
 #define GDN_SPLIT_MEAN_LENGTH 64
 
 /* Bytes of device workspace gdn_prefill_fwd needs for this problem and chunk size,

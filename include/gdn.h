@@ -37,7 +37,8 @@
  *
  * Ownership: the caller allocates and owns every buffer, the workspace included
  * (size from gdn_prefill_workspace_size). The library allocates nothing, keeps no
- * pointer after returning, and holds no state: calls are re-entrant. A call is
+ * pointer after returning, and holds no state: calls are re-entrant (the one exception is
+ * gdn_prefill_fwd_noalloc, whose built-in workspace every call on a GPU shares). A call is
  * asynchronous on `stream` (a hipStream_t; NULL = the default stream); buffers
  * must stay valid until the stream reaches the call. `out` must not alias an input.
  * Calls that share a state_pool slot or a workspace must be ordered on one stream.

@@ -58,9 +58,11 @@ def stage_bytes(p, s_qkv: int, s_ws: int, n_chunks: int):
     n_pairs = n_chunks * p.HV
     qk_frag = rows * p.HV * p.dk * 2 + rows * p.H * p.dk * 2   # K~ + normalised q
     touched = int(sum(1 for L in (p.cu_seqlens[1:] - p.cu_seqlens[:-1]) if L > 0))
-    # A_qk is causal: of its 2 x 4 fragments (32-token step x 16-row tile) the two above
-    # the diagonal are zero and neither written nor read
-    aqk = n_pairs * C * C * s_ws * 3 // 4
+    # A_qk is causal: of its (C / 32) x (C / 16) fragments (32-token step x 16-row tile)
+    # those above the diagonal are zero and neither written nor read (2 of 8 at C = 64,
+    # 12 of 32 at C = 128)
+    nrt = C // 16
+    aqk = n_pairs * C * C * s_ws * sum(w // 2 + 1 for w in range(nrt)) // (nrt * (C // 32))
     # stage 0 is the chunk table only: the bf16 chunk prep forms its own gates
     gate = (p.B + 1) * 8 + n_chunks * 4
     # prep: reads q, k, v and the raw gate inputs a, b (fp32); writes W<-, U~, the row
@@ -629,7 +631,8 @@ def workload_tag(p) -> str:
     else:
         t = f"b{p.B}_n{p.N}"
     hv = f"_hv{p.HV}" if p.HV != p.H else ""
-    return f"{p.name}_{t}_h{p.H}{hv}_d{p.dk}"
+    c = f"_c{p.chunk_size}" if p.chunk_size != 64 else ""
+    return f"{p.name}_{t}_h{p.H}{hv}_d{p.dk}{c}"
 
 
 def prefill_cpu_baseline(p, heads=None, reps: int = 3):
@@ -684,7 +687,8 @@ def measure_prefill(p, steps: int, warmup: int, cold_steps: int, copy_calibratio
     idx, cu = t(p.cache_indices), t(p.cu_seqlens)
     out = torch.empty((p.N, p.HV, p.dv), dtype=v.dtype, device=dev)
     prob = gdn.problem_of(q, k, v, pool, idx)
-    ws = torch.empty(gdn.gdn_prefill_workspace_size(prob), dtype=torch.uint8, device=dev)
+    C = p.chunk_size
+    ws = torch.empty(gdn.gdn_prefill_workspace_size(prob, C), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
     hip = Hip()
     rec = hip.lib.hipEventRecord
@@ -693,11 +697,11 @@ def measure_prefill(p, steps: int, warmup: int, cold_steps: int, copy_calibratio
 
     def step(events=None):
         if events is None:
-            gdn.gdn_prefill_fwd(q, k, v, a, b, A_log, dt_bias, pool, idx, cu, out=out,
-                                workspace=ws, stream=stream)
+            gdn.gdn_prefill_fwd(q, k, v, a, b, A_log, dt_bias, pool, idx, cu, chunk_size=C,
+                                out=out, workspace=ws, stream=stream)
         else:
             gdn.gdn_prefill_fwd_events(q, k, v, a, b, A_log, dt_bias, pool, idx, cu, events,
-                                       out=out, workspace=ws, stream=stream)
+                                       chunk_size=C, out=out, workspace=ws, stream=stream)
 
     for _ in range(warmup):
         step()
@@ -769,8 +773,10 @@ def measure_prefill(p, steps: int, warmup: int, cold_steps: int, copy_calibratio
     dom = max(launch, key=launch.get)
     sched = gdn.gdn_prefill_state_schedule(gdn.make_problem(
         p.N, p.B, p.H, p.HV, p.dk, p.dv, p.pool,
-        gdn.GDN_DTYPE_BF16 if p.dtype == "bf16" else gdn.GDN_DTYPE_F32))
-    kernels = gdn.STAGE_KERNELS[sched]
+        gdn.GDN_DTYPE_BF16 if p.dtype == "bf16" else gdn.GDN_DTYPE_F32), C)
+    kernels = dict(gdn.STAGE_KERNELS[sched])
+    if C == 128:
+        kernels["chunk_prep"] = "mfma_prep128_kernel"
     kernel_name = kernels[dom]
     pbytes = path_bytes(p, s_qkv)
     flops = algorithmic_flops_per_token_vhead(p.dk, p.dv, p.chunk_size) * p.N * p.HV
@@ -827,6 +833,7 @@ def measure_prefill(p, steps: int, warmup: int, cold_steps: int, copy_calibratio
                       "algorithmic_flops": flops, "algorithmic_bytes": pbytes},
         "stages": stages,
         "state_schedule": sched,
+        "chunk_size": C,
         "kernel_source_hash": src_hash,
     }
 
@@ -834,8 +841,14 @@ def measure_prefill(p, steps: int, warmup: int, cold_steps: int, copy_calibratio
 def bench_prefill(args):
     import gdn_synth
 
+    import dataclasses
+
+    def load(i):
+        w = gdn_synth.workload(i, args.dtype)
+        return w if args.chunk == 64 else dataclasses.replace(w, chunk_size=args.chunk)
+
     main_idx = args.workload if args.workload is not None else WORKLOAD_INDEX
-    p = gdn_synth.workload(main_idx, args.dtype)
+    p = load(main_idx)
     m = measure_prefill(p, args.steps, args.warmup, args.cold_steps, args.copy_calibration)
     res = {
         "metric": METRIC,
@@ -851,7 +864,8 @@ def bench_prefill(args):
         "dtype": p.dtype,
         "data": f"synthetic (seeded SplitMix64/Box-Muller, seed {p.seed})",
         "config": {"workload": gdn_synth.WORKLOADS[main_idx]
-                   + (f" [q, k, v, out drawn in {p.dtype}]" if args.dtype else ""),
+                   + (f" [q, k, v, out drawn in {p.dtype}]" if args.dtype else "")
+                   + (f" [chunk size {args.chunk}]" if args.chunk != 64 else ""),
                    "global_batch": p.B,
                    "seq_len": int(p.N // max(p.B, 1)), "parallelism": "none (1 GPU)"},
         "roofline": m["roofline"],
@@ -866,11 +880,12 @@ def bench_prefill(args):
     if args.workload is None and not args.no_sub:
         del p
         for wi in SUB_WORKLOADS:
-            sp_ = gdn_synth.workload(wi, args.dtype)
+            sp_ = load(wi)
             sm = measure_prefill(sp_, max(3, args.steps // 2), max(3, args.warmup // 2),
                                  args.cold_steps)
             ent = {"workload": gdn_synth.WORKLOADS[wi]
-                   + (f" [q, k, v, out drawn in {sp_.dtype}]" if args.dtype else ""),
+                   + (f" [q, k, v, out drawn in {sp_.dtype}]" if args.dtype else "")
+                   + (f" [chunk size {args.chunk}]" if args.chunk != 64 else ""),
                    "index": wi,
                    "tokens_per_s": sm["tokens_per_s"], "ms_per_step": sm["ms_per_step"],
                    "call_ms_events": sm["call_ms_events"],
@@ -1109,6 +1124,9 @@ def main():
     ap.add_argument("--dtype", choices=("bf16", "f32"), default=None,
                     help="draw the prefill workloads with q, k, v in this dtype instead of "
                          "their own (f32 runs the fp32-arithmetic kernels)")
+    ap.add_argument("--chunk", type=int, choices=(64, 128), default=64,
+                    help="chunk size of the prefill (128: bf16 inputs with dk of 128 or 256; "
+                         "the measured comparison of the two schedules)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 512 MiB device copy (calibrates HBM byte counters)")
     args = ap.parse_args()

@@ -78,6 +78,12 @@ static bool prefill_grids_fit(const Shape& s, Path path, int64_t max_chunks) {
     return grid_fits((max_chunks * s.HV + 3) / 4, 256) && grid_fits(max_chunks, 256) &&
            s.HV <= 65535 && grid_fits((s.B * s.HV + 7) / 8 * 8 * (s.dv / 16), 256);
   }
+  if (s.C == 128) {
+    // prep: one 512-thread workgroup per (chunk, value head); state: eight waves per
+    // (request, value head) pair rounded up to 8 and column block (at most dv / 16)
+    return grid_fits(max_chunks * s.HV, 512) &&
+           grid_fits((s.B * s.HV + 7) / 8 * 8 * (s.dv / 16), 512);
+  }
   const ChainPlan cp = chain_plan(s);
   if (cp.use) {
     for (int stage = 0; stage < 3; ++stage)
@@ -112,8 +118,10 @@ static gdn_status_t check_problem(const gdn_problem_t* p, int32_t chunk_size, Sh
   s->C = chunk_size;
   s->pool = p->pool_size;
   s->bf16 = p->qkv_dtype == GDN_DTYPE_BF16;
-  if (chunk_size != 64) return GDN_ERR_UNSUPPORTED;
   if (!head_dim_ok(p->head_k) || !head_dim_ok(p->head_v)) return GDN_ERR_UNSUPPORTED;
+  // C = 64 on every path; C = 128 on the bf16 matrix-core path with dk of 128 or 256
+  if (chunk_size != 64 && chunk_size != 128) return GDN_ERR_UNSUPPORTED;
+  if (chunk_size == 128 && !(s->bf16 && s->dk >= 128)) return GDN_ERR_UNSUPPORTED;
   if (p->num_v_heads > 65535) return GDN_ERR_UNSUPPORTED;
   if (p->total_tokens > ((int64_t)1 << 31) - 1 - 64 * (p->batch + 1)) return GDN_ERR_UNSUPPORTED;
   if (p->batch > ((int64_t)1 << 30)) return GDN_ERR_UNSUPPORTED;
@@ -206,7 +214,7 @@ gdn_status_t run_prefill(const void* q, const void* k, const void* v, const floa
 
   // Up to 64 requests the MFMA chunk prep forms the chunk table itself (one scan per
   // workgroup) and writes chunk_off for the state pass: one launch fewer.
-  const bool self_plan = path == Path::kMfma && s.B <= kMaxSelfPlanRequests;
+  const bool self_plan = path == Path::kMfma && s.B <= kMaxSelfPlanRequests && s.C == 64;
   if (!mark(0)) return GDN_ERR_HIP;
   if (!self_plan &&
       launch_plan(cu_seqlens, s, chunk_off, chunk_seq, L.max_chunks, st) != hipSuccess)
@@ -412,7 +420,7 @@ gdn_status_t gdn_promote_scan(const void* K, const void* V, const float* beta, c
 
 size_t gdn_prefill_bwd_workspace_size(const gdn_problem_t* prob, int32_t chunk_size) {
   Shape s;
-  if (check_problem(prob, chunk_size, &s) != GDN_OK) return 0;
+  if (check_problem(prob, chunk_size, &s) != GDN_OK || chunk_size != 64) return 0;
   return bwd_layout_for(s).total;
 }
 
@@ -427,6 +435,7 @@ gdn_status_t gdn_prefill_bwd(const void* q, const void* k, const void* v, const 
   Shape s;
   const gdn_status_t ps = check_problem(prob, chunk_size, &s);
   if (ps != GDN_OK) return ps;
+  if (chunk_size != 64) return GDN_ERR_UNSUPPORTED;  // the backward's schedule is fixed
   if (s.B == 0) return GDN_OK;
   if (!A_log || !dt_bias || !state_pool || !cache_indices || !cu_seqlens || !dstate ||
       !dA_log || !ddt_bias || !dstate0)

@@ -592,6 +592,418 @@ hipError_t launch_prep_t(const void* q, const void* k, const void* v, const int6
   return hipGetLastError();
 }
 
+
+// ======================= C = 128 =======================
+// The same quantities over chunks of 128 rows, in the state pass's fragment orders at
+// C = 128 (eight row tiles, four 32-token steps): one workgroup of eight waves per (chunk,
+// value head), wave w owning chunk rows 16w .. 16w + 15. The structure follows the C = 64
+// kernel with these differences: the inverse has eight diagonal tiles and distances up
+// to 7, so every exchanged tile T_IJ (I <= 6) stays in LDS; Q is not staged (each wave
+// loads the fragments of its own rows, in the contraction order of the state pass, which
+// the Gram K Q^T then uses too); V is staged into the K region once W<- and K~ are
+// formed; the chunk table comes from the plan kernel, one item per workgroup.
+constexpr int C2 = 128;
+constexpr int NRT2 = C2 / 16;  // row tiles
+constexpr int NTS2 = C2 / 32;  // token steps
+
+template <int DK, int DV>
+struct Prep128Smem {
+  static constexpr int SKV = (DK > DV ? DK : DV) + 16;  // row stride (bf16), as at C = 64
+  uint16_t kv[C2 * SKV];  // K rows, later V rows
+  // Dl(T_IJ) for I <= 6 at slot I (I + 1) / 2 + J; slot (w, w) (slot 28 for wave 7) is
+  // first wave w's scratch for the forward substitution (16 x 16 fp32, row stride 16)
+  f32x4 tex[29][64];
+  double G2[C2];  // G log2(e)
+  float bt[C2];   // beta
+  float rk[C2];   // r_k
+};
+
+__device__ __forceinline__ int tex2_slot(int I, int J) { return I * (I + 1) / 2 + J; }
+
+// Rows of a row-major bf16 tile of C2 rows into registers (512 threads), zeros past n.
+template <int D>
+__device__ __forceinline__ void load_rows128(u32x4 (&r)[C2 * D / 8 / 512], const uint16_t* src,
+                                             int64_t rs, int n, int tid) {
+#pragma unroll
+  for (int u = 0; u < C2 * D / 8 / 512; ++u) {
+    const int e = tid + 512 * u, row = e / (D / 8), c8 = (e % (D / 8)) * 8;
+    u32x4 z = {0u, 0u, 0u, 0u};
+    if (row < n) z = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + row * rs + c8));
+    r[u] = z;
+  }
+}
+template <int D>
+__device__ __forceinline__ void store_rows128(uint16_t* dst, int ld,
+                                              const u32x4 (&r)[C2 * D / 8 / 512], int tid) {
+#pragma unroll
+  for (int u = 0; u < C2 * D / 8 / 512; ++u) {
+    const int e = tid + 512 * u, row = e / (D / 8), c8 = (e % (D / 8)) * 8;
+    *reinterpret_cast<u32x4*>(&dst[row * ld + c8]) = r[u];
+  }
+}
+
+template <int DK, int DV>
+__global__ __launch_bounds__(512, (DK + DV <= 256) ? 4 : 2) void mfma_prep128_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const int64_t* __restrict__ cu, const int32_t* __restrict__ chunk_off,
+    const int32_t* __restrict__ chunk_seq, const float* __restrict__ ga,
+    const float* __restrict__ gb, const float* __restrict__ A_log,
+    const float* __restrict__ dt_bias, int H, int HV, _Float16* __restrict__ Wout,
+    _Float16* __restrict__ Uout, _Float16* __restrict__ Aout, float* __restrict__ eg_out,
+    _Float16* __restrict__ Kout, _Float16* __restrict__ Qout, int32_t* __restrict__ nonfinite) {
+  constexpr int C = C2;
+  constexpr int NKS = DK / 32;
+  using Sm = Prep128Smem<DK, DV>;
+  constexpr int SKV = Sm::SKV;
+  constexpr int KP = C * DK / 8 / 512;  // 16-byte pieces per thread of the K tile
+  constexpr int VP = C * DV / 8 / 512;  // ... of the V tile
+  __shared__ Sm sm;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, m = l & 15, g = l >> 4;
+  const int t = 16 * w + m;  // this lane's chunk row
+  if (blockIdx.x == 0 && tid == 0) *nonfinite = 0;  // the state pass raises it
+  const int64_t c = blockIdx.x / HV;
+  const int hv = (int)(blockIdx.x % HV);
+  const int32_t seq = chunk_seq[c];
+  if (seq < 0) return;  // unused chunk slot (uniform over the workgroup)
+  const int h = hv / (HV / H);
+  const int64_t t0 = cu[seq] + (int64_t)(c - chunk_off[seq]) * C;
+  const int n = (int)min((int64_t)C, cu[seq + 1] - t0);
+  const int64_t pair = c * HV + hv;
+  const int64_t rsk = (int64_t)H * DK;
+
+  // ---- loads: K and V rows (V is staged later), the own rows of Q in the state pass's
+  // contraction order (elements 32 sp + kperm(g, .)), zeros past n
+  u32x4 kreg[KP], vreg[VP];
+  load_rows128<DK>(kreg, k + (t0 * H + h) * (int64_t)DK, rsk, n, tid);
+  u32x4 qf[NKS];
+#pragma unroll
+  for (int sp = 0; sp < NKS; ++sp) {
+    u32x4 z = {0u, 0u, 0u, 0u};
+    if (t < n) {
+      const uint16_t* p = q + ((t0 + t) * H + h) * (int64_t)DK + 32 * sp + 4 * g;
+      const u32x2 lo = *reinterpret_cast<const u32x2*>(p);
+      const u32x2 hi = *reinterpret_cast<const u32x2*>(p + 16);
+      z = u32x4{lo[0], lo[1], hi[0], hi[1]};
+    }
+    qf[sp] = z;
+  }
+
+  // ---- gates (wave 0; lane l takes rows l and 64 + l): g = log(alpha) =
+  // -exp(A_log) softplus(a + dt_bias), beta = sigmoid(b), zero on padding rows; G = the
+  // chunk-local inclusive sum of g in fp64
+  if (w == 0) {
+    double G[2];
+    float bt[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int r = l + 64 * j;
+      float gt = 0.f;
+      bt[j] = 0.f;
+      if (r < n) {
+        const int64_t tr = t0 + r;
+        const float xg = ga[tr * HV + hv] + dt_bias[hv];
+        const float sp = fmaxf(xg, 0.f) + log1pf(expf(-fabsf(xg)));
+        gt = -expf(A_log[hv]) * sp;
+        bt[j] = 1.f / (1.f + expf(-gb[tr * HV + hv]));
+      }
+      G[j] = (double)gt;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const double y = __shfl_up(G[j], off, 64);
+        if (l >= off) G[j] += y;
+      }
+    }
+    G[1] += __shfl(G[0], 63, 64);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      sm.G2[l + 64 * j] = G[j] * kLog2e;
+      sm.bt[l + 64 * j] = bt[j];
+    }
+  }
+  store_rows128<DK>(sm.kv, SKV, kreg, tid);
+  lds_barrier();  // (0) K staged, gates
+
+  // ---- norms of the own rows (the four lane groups hold one row)
+  float kss = 0.f, qss = 0.f;
+#pragma unroll
+  for (int sp = 0; sp < NKS; ++sp) {
+    const u32x4 kx = row_frag_kperm(sm.kv, SKV, t, 32 * sp, g);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      kss += bf_lo(kx[j]) * bf_lo(kx[j]) + bf_hi(kx[j]) * bf_hi(kx[j]);
+      qss += bf_lo(qf[sp][j]) * bf_lo(qf[sp][j]) + bf_hi(qf[sp][j]) * bf_hi(qf[sp][j]);
+    }
+  }
+  kss += __shfl_xor(kss, 16, 64);
+  kss += __shfl_xor(kss, 32, 64);
+  qss += __shfl_xor(qss, 16, 64);
+  qss += __shfl_xor(qss, 32, 64);
+  const float rkt = 1.0f / sqrtf(kss + kNormEps);
+  const float rqt = 1.0f / sqrtf(qss + kNormEps);
+  if (g == 0) sm.rk[t] = rkt;
+
+  // ---- normalised q in the state pass's operand order, once per q/k head
+  if (hv % (HV / H) == 0) {
+    const int64_t fo = (c * H + h) * (int64_t)(C * DK);
+#pragma unroll
+    for (int sp = 0; sp < NKS; ++sp) {
+      half8 y;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        y[2 * j] = (_Float16)(bf_lo(qf[sp][j]) * rqt);
+        y[2 * j + 1] = (_Float16)(bf_hi(qf[sp][j]) * rqt);
+      }
+      __builtin_nontemporal_store(y, reinterpret_cast<half8*>(Qout + fo + ((w * NKS + sp) * 64 + l) * 8));
+    }
+  }
+  lds_barrier();  // (1) r_k visible
+
+  // ---- Grams of the own rows against tiles J <= w, transposed, dk step by dk step:
+  // D[J] = Dl(K_J K_w^T), E[J] = Dl(K_J Q_w^T); lane (g, m): row 16J + 4g + i, column t
+  f32x4 D[NRT2], E[NRT2];
+#pragma unroll
+  for (int J = 0; J < NRT2; ++J) {
+    D[J] = f32x4{0.f, 0.f, 0.f, 0.f};
+    E[J] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+#pragma unroll
+  for (int sp = 0; sp < NKS; ++sp) {
+    const bf16x8 kws = bf16x8_from_u32x4(row_frag_kperm(sm.kv, SKV, t, 32 * sp, g));
+    const bf16x8 qws = bf16x8_from_u32x4(qf[sp]);
+#pragma unroll
+    for (int J = 0; J < NRT2; ++J) {
+      if (J < w) {
+        const bf16x8 kj = bf16x8_from_u32x4(row_frag_kperm(sm.kv, SKV, 16 * J + m, 32 * sp, g));
+        D[J] = mma_bf16(kj, kws, D[J]);
+        E[J] = mma_bf16(kj, qws, E[J]);
+      } else if (J == w) {
+        D[J] = mma_bf16(kws, kws, D[J]);
+        E[J] = mma_bf16(kws, qws, E[J]);
+      }
+    }
+  }
+
+  // ---- scale: a[J] = Dl(A_wJ^T) (A[t][i], i = 16J + 4g + ii < t) and the A_qk rows
+  const double G2t = sm.G2[t];
+  const float btt = sm.bt[t];
+  const float egt = __builtin_amdgcn_exp2f((float)G2t);
+  if (g == 0) eg_out[pair * C + t] = egt;
+  const int dm = opaque(m) - 4 * g;  // i < t  <=>  ii < dm on the diagonal tile
+  f32x4 a[NRT2];
+#pragma unroll
+  for (int s = 0; s < NTS2; ++s) {
+    half4 aq[2];
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {
+      const int J = 2 * s + jj;
+      f32x4 x = {0.f, 0.f, 0.f, 0.f};
+      a[J] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (J <= w) {
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+          const int i = 16 * J + 4 * g + ii;
+          const float rki = sm.rk[i];
+          const float av = btt * rkt * rki * D[J][ii];
+          // e^{G_t - G_i} overflows for i > t under strong decay: masked, not multiplied
+          const float xv = __builtin_amdgcn_exp2f((float)(G2t - sm.G2[i])) * rqt * rki * E[J][ii];
+          a[J][ii] = (J < w || ii < dm) ? av : 0.f;
+          x[ii] = (J < w || ii <= dm) ? xv : 0.f;
+        }
+      }
+      aq[jj] = to_half4(x);
+    }
+    // token steps past the own row tile lie above the diagonal: never read
+    if (2 * s <= w)
+      __builtin_nontemporal_store(cat(aq[0], aq[1]), reinterpret_cast<half8*>(Aout + pair * C * C + ((w * NTS2 + s) * 64 + l) * 8));
+  }
+
+  // ---- K~ = diag(e^{G_n - G} r_k) K in fp16: fragment f = (sp * 2 + tt) * 4 + s holds
+  // K~^T rows 32sp + 16tt + m, tokens 32s + kperm(g, .); wave w writes f = w (mod 8)
+  {
+    const int s = w & 3, tt = w >> 2;
+    float kdj[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int tk = 32 * s + kperm(g, j);
+      kdj[j] = __builtin_amdgcn_exp2f((float)(sm.G2[C - 1] - sm.G2[tk])) * sm.rk[tk];
+    }
+    half8* kb = reinterpret_cast<half8*>(Kout + pair * (int64_t)(C * DK)) + w * 64 + opaque(l);
+#pragma unroll
+    for (int sp = 0; sp < NKS; ++sp) {
+      const u32x4 x = col_frag_tr(sm.kv, SKV, 32 * sp + 16 * tt, s, g, m);
+      half8 y;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        y[2 * j] = (_Float16)(bf_lo(x[j]) * kdj[2 * j]);
+        y[2 * j + 1] = (_Float16)(bf_hi(x[j]) * kdj[2 * j + 1]);
+      }
+      __builtin_nontemporal_store(y, kb + sp * 8 * 64);
+    }
+  }
+
+  // ---- diagonal tile: T_ww = (I + A_ww)^-1 by forward substitution, lane = column m
+  float* sqw = reinterpret_cast<float*>(&sm.tex[w < 7 ? tex2_slot(w, w) : 28][0]);
+  {
+    f32x4 aw = a[0];
+#pragma unroll
+    for (int J = 1; J < NRT2; ++J)
+      if (J == w) aw = a[J];
+    *reinterpret_cast<f32x4*>(&sqw[m * 16 + 4 * g]) = aw;  // row m of A_ww, columns 4g..
+  }
+  __builtin_amdgcn_wave_barrier();
+  float x[16];
+  const int mo = opaque(m);
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    float acc = 0.f;
+#pragma unroll
+    for (int i = 0; i < r; ++i) acc += sqw[r * 16 + i] * x[i];
+    x[r] = (r < mo) ? 0.f : ((r == mo) ? 1.f : -acc);
+  }
+  __builtin_amdgcn_wave_barrier();
+  if (g == 0) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sqw[r * 16 + m] = x[r];  // column m of T_ww
+  }
+  __builtin_amdgcn_wave_barrier();
+  const f32x4 tww_t = *reinterpret_cast<const f32x4*>(&sqw[m * 16 + 4 * g]);  // Dl(T_ww^T)
+  f32x4 tww;                                                                  // Dl(T_ww)
+  const int go = opaque(g);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float y = x[i];
+#pragma unroll
+    for (int gg = 1; gg < 4; ++gg)
+      if (go == gg) y = x[4 * gg + i];
+    tww[i] = y;
+  }
+  __builtin_amdgcn_wave_barrier();  // every lane has read the scratch it now overwrites
+  if (w < 7) sm.tex[tex2_slot(w, w)][l] = tww;
+  f32x4 ttr[NRT2];  // Dl(T_wJ^T), J <= w
+#pragma unroll
+  for (int J = 0; J < NRT2; ++J) ttr[J] = (J == w) ? tww_t : f32x4{0.f, 0.f, 0.f, 0.f};
+  lds_barrier();  // (2)
+
+  // ---- off-diagonal tiles by distance d: X = sum_{J <= K < w} A_wK T_KJ, T_wJ = -T_ww X
+#pragma unroll
+  for (int d = 1; d < NRT2; ++d) {
+    if (w >= d) {
+      const int J = w - d;
+      f32x4 X = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int K = 0; K < NRT2 - 1; ++K) {
+        if (K >= J && K < w) {
+          const f32x4 tkj = sm.tex[tex2_slot(K, J)][l];
+#pragma unroll
+          for (int s = 0; s < 4; ++s) X = mma_f32(a[K][s], tkj[s], X);
+        }
+      }
+      f32x4 Y = {0.f, 0.f, 0.f, 0.f}, Z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        Y = mma_f32(tww_t[s], X[s], Y);  // Dl(T_ww X)
+        Z = mma_f32(X[s], tww_t[s], Z);  // Dl(X^T T_ww^T)
+      }
+      if (w < 7) sm.tex[tex2_slot(w, J)][l] = -Y;  // read at larger distances
+#pragma unroll
+      for (int JJ = 0; JJ < NRT2 - 1; ++JJ)
+        if (JJ == J) ttr[JJ] = -Z;
+    }
+    if (d < NRT2 - 1) lds_barrier();  // (3) .. (8)
+  }
+
+  load_rows128<DV>(vreg, v + (t0 * HV + hv) * (int64_t)DV, (int64_t)HV * DV, n, tid);
+
+  // ---- W<-^T = K^T T1^T for the own token columns, T1 = diag(e^G) T diag(beta r_k) in
+  // bf16 hi + lo: D tiles (dk 32sp + 16tt, rows t)
+  const int ns = (w >> 1) + 1;  // token steps that hold tiles J <= w
+  {
+    bf16x4 t1h[NRT2], t1l[NRT2];
+#pragma unroll
+    for (int J = 0; J < NRT2; ++J) {
+      f32x4 x1 = {0.f, 0.f, 0.f, 0.f};
+      if (J <= w) {
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+          const int i = 16 * J + 4 * g + ii;
+          x1[ii] = egt * ttr[J][ii] * sm.bt[i] * sm.rk[i];  // T[t][i] is zero for i > t
+        }
+      }
+      t1h[J] = to_bf16x4(x1);
+      t1l[J] = to_bf16x4(x1 - to_f32x4(t1h[J]));
+    }
+#pragma unroll
+    for (int sp = 0; sp < NKS; ++sp) {
+      f32x4 acc[2];
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        acc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < NTS2; ++s) {
+          if (s < ns) {
+            const bf16x8 ka = bf16x8_from_u32x4(col_frag_tr(sm.kv, SKV, 32 * sp + 16 * tt, s, g, m));
+            acc[tt] = mma_bf16(ka, cat_bf(t1h[2 * s], t1h[2 * s + 1]), acc[tt]);
+            acc[tt] = mma_bf16(ka, cat_bf(t1l[2 * s], t1l[2 * s + 1]), acc[tt]);
+          }
+        }
+      }
+      __builtin_nontemporal_store(cat(to_half4(acc[0]), to_half4(acc[1])), reinterpret_cast<half8*>(Wout + pair * C * DK + ((w * NKS + sp) * 64 + l) * 8));
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  lds_barrier();  // (9) the K tile is no longer read
+  store_rows128<DV>(sm.kv, SKV, vreg, tid);
+
+  // ---- T2 = (Gamma o T) diag(beta) in bf16 hi + lo, tiles J <= w
+  bf16x4 t2h[NRT2], t2l[NRT2];
+  const int dm2 = opaque(m) - 4 * g;  // i <= t  <=>  ii <= dm2 on the diagonal tile
+#pragma unroll
+  for (int J = 0; J < NRT2; ++J) {
+    f32x4 x2 = {0.f, 0.f, 0.f, 0.f};
+    if (J <= w) {
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        const int i = 16 * J + 4 * g + ii;
+        const float ev = __builtin_amdgcn_exp2f((float)(G2t - sm.G2[i])) * ttr[J][ii] * sm.bt[i];
+        x2[ii] = (J < w || ii <= dm2) ? ev : 0.f;
+      }
+    }
+    t2h[J] = to_bf16x4(x2);
+    t2l[J] = to_bf16x4(x2 - to_f32x4(t2h[J]));
+  }
+  lds_barrier();  // (10) V staged
+
+  // ---- U~ = T2 V for the own rows: D tiles (rows 16w.., dv 16cc..)
+#pragma unroll
+  for (int cc = 0; cc < DV / 16; ++cc) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < NTS2; ++s) {
+      if (s < ns) {
+        const bf16x8 vb = bf16x8_from_u32x4(col_frag_tr(sm.kv, SKV, 16 * cc, s, g, m));
+        acc = mma_bf16(cat_bf(t2h[2 * s], t2h[2 * s + 1]), vb, acc);
+        acc = mma_bf16(cat_bf(t2l[2 * s], t2l[2 * s + 1]), vb, acc);
+      }
+    }
+    __builtin_nontemporal_store(to_half4(acc), reinterpret_cast<half4*>(Uout + pair * C * DV + ((cc * NRT2 + w) * 64 + l) * 4));
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+template <int DK, int DV>
+hipError_t launch_prep128_t(const void* q, const void* k, const void* v, const int64_t* cu,
+                            const int32_t* off, const int32_t* cseq, const float* ga,
+                            const float* gb, const float* A_log, const float* dt_bias,
+                            const Shape& s, int64_t max_chunks, _Float16* w, _Float16* u,
+                            _Float16* aqk, float* eg, _Float16* kf, _Float16* qf,
+                            int32_t* nonfinite, hipStream_t st) {
+  const int64_t items = max_chunks * s.HV;  // (chunk, value head); unused chunks return
+  hipLaunchKernelGGL((mfma_prep128_kernel<DK, DV>), dim3((unsigned)items), dim3(512), 0, st,
+                     (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, cu, off, cseq,
+                     ga, gb, A_log, dt_bias, s.H, s.HV, w, u, aqk, eg, kf, qf, nonfinite);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_mfma_prep(const void* q, const void* k, const void* v,
@@ -600,9 +1012,25 @@ hipError_t launch_mfma_prep(const void* q, const void* k, const void* v,
                             const float* b, const float* A_log, const float* dt_bias,
                             const Shape& s, int64_t max_chunks, void* w, void* u, void* aqk,
                             float* eg, void* kf, void* qf, int32_t* nonfinite, hipStream_t st) {
-  if (self_plan && s.B > kMaxSelfPlanRequests) return hipErrorInvalidValue;
+  if (self_plan && (s.B > kMaxSelfPlanRequests || s.C != 64)) return hipErrorInvalidValue;
   _Float16* W = (_Float16*)w;
   _Float16* U = (_Float16*)u;
+  if (s.C == 128) {
+#define GDN_PREP128_CASE(DKv, DVv)                                                           \
+  if (s.dk == DKv && s.dv == DVv)                                                            \
+    return launch_prep128_t<DKv, DVv>(q, k, v, cu_seqlens, chunk_off, chunk_seq, a, b, A_log, \
+                                      dt_bias, s, max_chunks, W, U, (_Float16*)aqk, eg,     \
+                                      (_Float16*)kf, (_Float16*)qf, nonfinite, st);
+    GDN_PREP128_CASE(128, 64)
+    GDN_PREP128_CASE(128, 128)
+    GDN_PREP128_CASE(128, 256)
+    GDN_PREP128_CASE(256, 64)
+    GDN_PREP128_CASE(256, 128)
+    GDN_PREP128_CASE(256, 256)
+#undef GDN_PREP128_CASE
+    return hipErrorInvalidValue;
+  }
+  if (s.C != 64) return hipErrorInvalidValue;
 #define GDN_PREP_CASE(DKv, DVv)                                                               \
   if (s.dk == DKv && s.dv == DVv)                                                             \
     return launch_prep_t<DKv, DVv>(q, k, v, cu_seqlens, chunk_off, chunk_seq, self_plan, a, b, \

@@ -47,18 +47,23 @@ namespace gdn {
 namespace {
 
 using namespace mfma;
-constexpr int C = 64;
-constexpr int NO = 2;        // output waves per workgroup
-constexpr int NRO = 4 / NO;  // row tiles per output wave
+// Waves per workgroup by chunk size CC (64 or 128): CC / 32 state waves, each owning one
+// 32-token step of the chunk and DK / (CC / 32) rows of S^T, and CC / 32 output waves of
+// two row tiles each.
+template <int CC>
+constexpr int kStateWaves = CC / 32;
+template <int CC>
+constexpr int kOutWaves = CC / 32;
+constexpr int NRO = 2;  // row tiles per output wave
 
-template <int NKS, int NC>
+template <int NKS, int NC, int CC>
 struct StateSmem {
   // Row stride (bf16) of the output tile: 16 bytes of padding spread the rows that the
   // 8-byte writes of one wave touch evenly over the banks.
   static constexpr int SO = 16 * NC + 8;
   half8 s16[2][NC][NKS][64];  // fp16 S^T fragments: chunk parity, column tile, dk step
-  half8 u16[2][NC][2][64];    // fp16 U fragments: chunk parity, column tile, token step
-  uint16_t o16[2][C][SO];     // bf16 rows of O (16 NC columns): chunk parity, token
+  half8 u16[2][NC][CC / 32][64];  // fp16 U fragments: chunk parity, column tile, token step
+  uint16_t o16[2][CC][SO];        // bf16 rows of O (16 NC columns): chunk parity, token
 };
 
 __device__ __forceinline__ bf16x4 to_bf16x4(f32x4 x) {
@@ -70,22 +75,31 @@ __device__ __forceinline__ bf16x4 to_bf16x4(f32x4 x) {
   return h;
 }
 
-// Store waves: one up to dk = 128. At dk = 256 the state and output waves need more than
-// half of a SIMD's registers, so they keep a SIMD each and store O themselves.
-template <int DK>
-constexpr int kStoreWaves = DK <= 128 ? 1 : 0;
+// Store waves: one up to dk = 128 at C = 64. At dk = 256 the state and output waves need
+// more than half of a SIMD's registers, so they keep a SIMD each and store O themselves;
+// at C = 128 the eight state and output waves take two per SIMD already.
+template <int DK, int CC>
+constexpr int kStoreWaves = (DK <= 128 && CC == 64) ? 1 : 0;
+template <int DK, int CC>
+constexpr int kStateThreads = 64 * (kStateWaves<CC> + kOutWaves<CC> + kStoreWaves<DK, CC>);
 
-template <int DK, int NC, int PD>
-__global__ __launch_bounds__(64 * (2 + NO + kStoreWaves<DK>)) void mfma_state_kernel(
+template <int DK, int NC, int PD, int CC>
+__global__ __launch_bounds__((kStateThreads<DK, CC>)) void mfma_state_kernel(
     const _Float16* __restrict__ Qf, const _Float16* __restrict__ Kf,
     const int64_t* __restrict__ cu, const int64_t* __restrict__ cache_indices,
     const int32_t* __restrict__ chunk_off, const _Float16* __restrict__ W, const _Float16* __restrict__ Ut,
     const _Float16* __restrict__ Aqk, const float* __restrict__ egws, int B, int H, int HV,
     int DV, int64_t short_len, float* __restrict__ state_pool, uint16_t* __restrict__ out,
     int32_t* __restrict__ nonfinite) {
-  constexpr int NKS = DK / 32;    // 32-wide dk steps
-  constexpr int NOWN = NKS / 2;   // dk steps of S^T held by each state wave
-  __shared__ StateSmem<NKS, NC> sm;
+  constexpr int C = CC;
+  constexpr int NSW = kStateWaves<CC>;  // state waves = token steps of 32
+  constexpr int NO = kOutWaves<CC>;
+  constexpr int NRT = C / 16;           // row tiles of a chunk
+  constexpr int NKS = DK / 32;          // 32-wide dk steps
+  constexpr int NOWN = NKS / NSW;       // dk steps of S^T held by each state wave
+  constexpr int NOTH = NSW - 1;         // the other state waves
+  static_assert(NOWN >= 1 && NOWN * NSW == NKS, "dk steps split evenly over the state waves");
+  __shared__ StateSmem<NKS, NC, CC> sm;
 
   // Blocks of the same (request, head) share blockIdx.x mod 8, so they run on one
   // XCD and re-read the fragment blocks from its L2.
@@ -107,10 +121,11 @@ __global__ __launch_bounds__(64 * (2 + NO + kStoreWaves<DK>)) void mfma_state_ke
   const int64_t tend = cu[seq + 1];
   auto pair_of = [&](int cl) { return (cbase + cl) * HV + hv; };
 
-  if (wv < 2) {
+  if (wv < NSW) {
     // ======================= state wave =======================
     const int hs = wv;
-    const int ho = 1 - hs;
+    // the other state waves, in turn (NSW is a power of two)
+    auto other = [hs](int o) { return NSW == 2 ? 1 - hs : (hs + 1 + o) & (NSW - 1); };
     float* Sg = state_pool + ((slot * HV + hv) * (int64_t)DV + 16 * ct0 + m) * DK;
     f32x4 S[NC][NOWN][2];  // S^T rows 32 (hs NOWN + sp) + 16 tt + 4g + i, column 16 c + m
 #pragma unroll
@@ -126,9 +141,10 @@ __global__ __launch_bounds__(64 * (2 + NO + kStoreWaves<DK>)) void mfma_state_ke
     // every index into them is static. PD sets take the chunks in turn: each is reloaded
     // right after its last use with the chunk PD ahead.
     struct Regs {
-      u32x4 wfo[2][NOWN], wfx[2][NOWN];  // W<- fragments, row tiles 2hs + r: own / other dk
-      u32x2 uf[NC][2];                   // U~ D tiles: column tile, own row tile
-      u32x4 kf[NOWN][2][2];  // K~^T fragments: own dk step, 16-row half, own/other tokens
+      u32x4 wfo[2][NOWN];         // W<- fragments, row tiles 2hs + r: own dk steps
+      u32x4 wfx[2][NOTH][NOWN];   // ... the other waves' dk steps
+      u32x2 uf[NC][2];            // U~ D tiles: column tile, own row tile
+      u32x4 kf[NOWN][2][NSW];  // K~^T fragments: own dk step, 16-row half, own/other tokens
       float egn;             // e^{G_n}: e^G of the chunk's last row (padding rows do not decay)
     };
     auto load_wu = [&](Regs& R, int cl) {
@@ -140,12 +156,14 @@ __global__ __launch_bounds__(64 * (2 + NO + kStoreWaves<DK>)) void mfma_state_ke
         for (int sp = 0; sp < NOWN; ++sp) {
           R.wfo[r][sp] = *reinterpret_cast<const u32x4*>(
               wb + (((2 * hs + r) * NKS + hs * NOWN + sp) * 64 + l) * 8);
-          R.wfx[r][sp] = *reinterpret_cast<const u32x4*>(
-              wb + (((2 * hs + r) * NKS + ho * NOWN + sp) * 64 + l) * 8);
+#pragma unroll
+          for (int o = 0; o < NOTH; ++o)
+            R.wfx[r][o][sp] = *reinterpret_cast<const u32x4*>(
+                wb + (((2 * hs + r) * NKS + other(o) * NOWN + sp) * 64 + l) * 8);
         }
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
-        const _Float16* ub = Ut + pr * C * DV + ((ct0 + c) * 4 * 64 + l) * 4;
+        const _Float16* ub = Ut + pr * C * DV + ((ct0 + c) * NRT * 64 + l) * 4;
 #pragma unroll
         for (int r = 0; r < 2; ++r)
           R.uf[c][r] = *reinterpret_cast<const u32x2*>(ub + (2 * hs + r) * 64 * 4);
@@ -158,9 +176,12 @@ __global__ __launch_bounds__(64 * (2 + NO + kStoreWaves<DK>)) void mfma_state_ke
       for (int sp = 0; sp < NOWN; ++sp)
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
-          const int f = ((hs * NOWN + sp) * 2 + tt) * 2;
+          const int f = ((hs * NOWN + sp) * 2 + tt) * NSW;
           R.kf[sp][tt][0] = *reinterpret_cast<const u32x4*>(kb + ((f + hs) * 64 + l) * 8);
-          R.kf[sp][tt][1] = *reinterpret_cast<const u32x4*>(kb + ((f + ho) * 64 + l) * 8);
+#pragma unroll
+          for (int o = 0; o < NOTH; ++o)
+            R.kf[sp][tt][1 + o] =
+                *reinterpret_cast<const u32x4*>(kb + ((f + other(o)) * 64 + l) * 8);
         }
       R.egn = egws[pr * C + C - 1];
     };
@@ -194,9 +215,11 @@ __global__ __launch_bounds__(64 * (2 + NO + kStoreWaves<DK>)) void mfma_state_ke
       half8 uo[NC];
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
-        half8 sx[NOWN];
+        half8 sx[NOTH][NOWN];
 #pragma unroll
-        for (int sp = 0; sp < NOWN; ++sp) sx[sp] = sm.s16[b][c][ho * NOWN + sp][l];
+        for (int o = 0; o < NOTH; ++o)
+#pragma unroll
+          for (int sp = 0; sp < NOWN; ++sp) sx[o][sp] = sm.s16[b][c][other(o) * NOWN + sp][l];
         f32x4 nu[2];
 #pragma unroll
         for (int r = 0; r < 2; ++r) {
@@ -205,7 +228,9 @@ __global__ __launch_bounds__(64 * (2 + NO + kStoreWaves<DK>)) void mfma_state_ke
 #pragma unroll
           for (int sp = 0; sp < NOWN; ++sp) {
             nu[r] = mma_f16(half8_from_u32x4(R.wfo[r][sp]), so[c][sp], nu[r]);
-            nu[r] = mma_f16(half8_from_u32x4(R.wfx[r][sp]), sx[sp], nu[r]);
+#pragma unroll
+            for (int o = 0; o < NOTH; ++o)
+              nu[r] = mma_f16(half8_from_u32x4(R.wfx[r][o][sp]), sx[o][sp], nu[r]);
           }
         }
         // U in fp16, tokens 32 hs + kperm: B operand of the update and of A_qk U
@@ -213,18 +238,23 @@ __global__ __launch_bounds__(64 * (2 + NO + kStoreWaves<DK>)) void mfma_state_ke
         sm.u16[b][c][hs][l] = uo[c];
       }
       load_wu(R, nx);
-      lds_barrier();  // (B) both halves of U visible
+      lds_barrier();  // (B) every token step of U visible
 
       // ---- S^T <- e^{G_n} S^T + K~^T U on the own dk rows
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
-        const half8 ux = sm.u16[b][c][ho][l];
+        half8 ux[NOTH];
+#pragma unroll
+        for (int o = 0; o < NOTH; ++o) ux[o] = sm.u16[b][c][other(o)][l];
 #pragma unroll
         for (int sp = 0; sp < NOWN; ++sp)
 #pragma unroll
           for (int tt = 0; tt < 2; ++tt) {
             f32x4 acc = mma_f16(half8_from_u32x4(R.kf[sp][tt][0]), uo[c], S[c][sp][tt]);
-            S[c][sp][tt] = mma_f16(half8_from_u32x4(R.kf[sp][tt][1]), ux, acc);
+#pragma unroll
+            for (int o = 0; o < NOTH; ++o)
+              acc = mma_f16(half8_from_u32x4(R.kf[sp][tt][1 + o]), ux[o], acc);
+            S[c][sp][tt] = acc;
           }
       }
       load_k(R, nx);
@@ -260,7 +290,7 @@ __global__ __launch_bounds__(64 * (2 + NO + kStoreWaves<DK>)) void mfma_state_ke
           for (int i = 0; i < 4; ++i) finite = finite && __builtin_isfinite(S[c][sp][tt][i]);
         }
     if (__ballot(!finite) != 0 && l == 0) *nonfinite = 1;
-  } else if (wv < 2 + NO) {
+  } else if (wv < NSW + NO) {
     // ======================= output wave =======================
     // Output wave ow finishes row tiles I = NRO ow .. NRO ow + NRO - 1 of every column
     // tile: Qh S^T after barrier (A) of chunk cl, A_qk U after barrier (B). Computed as
@@ -272,7 +302,7 @@ __global__ __launch_bounds__(64 * (2 + NO + kStoreWaves<DK>)) void mfma_state_ke
       constexpr int ow = decltype(OWc)::value;
       struct Regs {
         u32x4 qf[NRO][NKS];  // Qh fragments: own row tile, dk step
-        u32x4 af[NRO][2];    // A_qk fragments: own row tile, token step
+        u32x4 af[NRO][C / 32];  // A_qk fragments: own row tile, token step
         float egr[NRO];      // e^G of row 16 I + m
       };
       // The Qh fragments are reloaded as soon as Qh S^T has used them, while the wave
@@ -293,10 +323,10 @@ __global__ __launch_bounds__(64 * (2 + NO + kStoreWaves<DK>)) void mfma_state_ke
         for (int r = 0; r < NRO; ++r) {
           const int I = NRO * ow + r;
 #pragma unroll
-          for (int s = 0; s < 2; ++s)
-            if (s == 0 || I >= 2)
-              R.af[r][s] =
-                  *reinterpret_cast<const u32x4*>(Aqk + pr * C * C + ((I * 2 + s) * 64 + l) * 8);
+          for (int s = 0; s < C / 32; ++s)
+            if (I >= 2 * s)  // token steps past the row tile are above the diagonal
+              R.af[r][s] = *reinterpret_cast<const u32x4*>(Aqk + pr * C * C +
+                                                           ((I * (C / 32) + s) * 64 + l) * 8);
           R.egr[r] = egws[pr * C + 16 * I + m];
         }
       };
@@ -324,12 +354,16 @@ __global__ __launch_bounds__(64 * (2 + NO + kStoreWaves<DK>)) void mfma_state_ke
         f32x4 au[NRO][NC];
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
-          const half8 uh0 = sm.u16[b][c][0][l], uh1 = sm.u16[b][c][1][l];
+          half8 uh[C / 32];
+#pragma unroll
+          for (int s = 0; s < C / 32; ++s) uh[s] = sm.u16[b][c][s][l];
 #pragma unroll
           for (int r = 0; r < NRO; ++r) {
             const int I = NRO * ow + r;
-            au[r][c] = mma_f16(uh0, half8_from_u32x4(R.af[r][0]), f32x4{0.f, 0.f, 0.f, 0.f});
-            if (I >= 2) au[r][c] = mma_f16(uh1, half8_from_u32x4(R.af[r][1]), au[r][c]);
+            au[r][c] = mma_f16(uh[0], half8_from_u32x4(R.af[r][0]), f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+            for (int s = 1; s < C / 32; ++s)
+              if (I >= 2 * s) au[r][c] = mma_f16(uh[s], half8_from_u32x4(R.af[r][s]), au[r][c]);
           }
         }
         const int64_t t0 = tseq + (int64_t)cl * C;
@@ -340,7 +374,7 @@ __global__ __launch_bounds__(64 * (2 + NO + kStoreWaves<DK>)) void mfma_state_ke
           for (int r = 0; r < NRO; ++r) {
             const int I = NRO * ow + r;
             const bf16x4 ov = to_bf16x4(R.egr[r] * o1[r][c] + au[r][c]);  // nearest even
-            if constexpr (kStoreWaves<DK> > 0) {
+            if constexpr (kStoreWaves<DK, CC> > 0) {
               *reinterpret_cast<bf16x4*>(&sm.o16[b][16 * I + m][16 * c + 4 * g]) = ov;
             } else if (16 * I + m < n) {
               *reinterpret_cast<bf16x4*>(reinterpret_cast<__bf16*>(out) +
@@ -362,12 +396,18 @@ __global__ __launch_bounds__(64 * (2 + NO + kStoreWaves<DK>)) void mfma_state_ke
       }
       lds_barrier();  // (F)
     };
-    static_assert(NO == 2, "one code copy per output wave");
-    if (wv == 2)
+    // one code copy per output wave
+    if (wv == NSW)
       run(std::integral_constant<int, 0>{});
-    else
+    else if (NO == 2 || wv == NSW + 1)
       run(std::integral_constant<int, 1>{});
-  } else if constexpr (kStoreWaves<DK> > 0) {
+    else if constexpr (NO == 4) {
+      if (wv == NSW + 2)
+        run(std::integral_constant<int, 2>{});
+      else
+        run(std::integral_constant<int, 3>{});
+    }
+  } else if constexpr (kStoreWaves<DK, CC> > 0) {
     // ======================= store wave =======================
     // Copies each chunk's output tile from LDS to out once it is complete (after barrier
     // (A) of the next chunk, or the final barrier), 16 bytes per lane, so that one store
@@ -398,16 +438,17 @@ __global__ __launch_bounds__(64 * (2 + NO + kStoreWaves<DK>)) void mfma_state_ke
   }
 }
 
-template <int DK, int NC, int PD>
+template <int DK, int NC, int PD, int CC>
 hipError_t launch_state_t(const void* qf, const void* kf, const int64_t* cu, const int64_t* idx,
                           const int32_t* off, const _Float16* w,
                           const _Float16* u, const _Float16* aqk, const float* eg, const Shape& s,
                           float* pool, void* out, int32_t* nonfinite, hipStream_t st) {
   const int64_t pairs8 = (s.B * s.HV + 7) / 8;
   const int64_t blocks = pairs8 * 8 * (s.dv / (16 * NC));
-  hipLaunchKernelGGL((mfma_state_kernel<DK, NC, PD>), dim3((unsigned)blocks), dim3(64 * (2 + NO + kStoreWaves<DK>)), 0,
-                     st, (const _Float16*)qf, (const _Float16*)kf, cu, idx, off, w, u, aqk,
-                     eg, (int)s.B, s.H, s.HV, s.dv, s.short_len, pool, (uint16_t*)out, nonfinite);
+  hipLaunchKernelGGL((mfma_state_kernel<DK, NC, PD, CC>), dim3((unsigned)blocks),
+                     dim3(kStateThreads<DK, CC>), 0, st, (const _Float16*)qf,
+                     (const _Float16*)kf, cu, idx, off, w, u, aqk, eg, (int)s.B, s.H, s.HV, s.dv,
+                     s.short_len, pool, (uint16_t*)out, nonfinite);
   return hipGetLastError();
 }
 
@@ -425,32 +466,32 @@ hipError_t launch_mfma_state(const void* qf, const void* kf, const int64_t* cu_s
   // full, so wider blocks serve more columns per byte taken in: 410 -> 350 us on the
   // varlen GQA workload), else two (32 rows), else one (16 rows), which doubles the
   // workgroups walking the chains (at dk = dv = 256 on one request of 8 heads,
-  // 533 -> 442 us). dv is a multiple of 64. Loads run two chunks ahead with up to two
-  // column tiles at dk <= 128, one chunk ahead otherwise, where two register sets would
-  // not fit.
+  // 533 -> 442 us). dv is a multiple of 64. At C = 64 loads run two chunks ahead with up
+  // to two column tiles at dk <= 128, one chunk ahead otherwise, where two register sets
+  // would not fit; at C = 128 (twice the operands per chunk) one chunk ahead, two at
+  // dk = 128 with up to two column tiles.
   const int64_t pairs = s.B * s.HV;
   const bool narrow = pairs * (s.dv / 32) < 256;
   const bool wide = s.dk <= 128 && pairs * (s.dv / 64) >= 256;
-#define GDN_STATE_CASE(DKv, PDv)                                                           \
-  if (s.dk == DKv) {                                                                       \
-    if (narrow)                                                                            \
-      return launch_state_t<DKv, 1, PDv>(qf, kf, cu_seqlens, cache_indices, chunk_off, W, U, \
-                                         (const _Float16*)aqk, eg, s, state_pool, out,       \
-                                         nonfinite, st);                                     \
-    if constexpr (DKv <= 128) {                                                            \
-      if (wide)                                                                            \
-        return launch_state_t<DKv, 4, 1>(qf, kf, cu_seqlens, cache_indices, chunk_off, W,  \
-                                         U, (const _Float16*)aqk, eg, s, state_pool, out,    \
-                                         nonfinite, st);                                     \
-    }                                                                                      \
-    return launch_state_t<DKv, 2, PDv>(qf, kf, cu_seqlens, cache_indices, chunk_off, W, U,   \
-                                       (const _Float16*)aqk, eg, s, state_pool, out,         \
-                                       nonfinite, st);                                       \
+#define GDN_STATE_ARGS                                                                   \
+  qf, kf, cu_seqlens, cache_indices, chunk_off, W, U, (const _Float16*)aqk, eg, s, state_pool, \
+      out, nonfinite, st
+#define GDN_STATE_CASE(DKv, PDv, CCv)                                                    \
+  if (s.dk == DKv && s.C == CCv) {                                                       \
+    if (narrow) return launch_state_t<DKv, 1, PDv, CCv>(GDN_STATE_ARGS);                 \
+    if constexpr (DKv <= 128) {                                                          \
+      if (wide) return launch_state_t<DKv, 4, 1, CCv>(GDN_STATE_ARGS);                   \
+    }                                                                                    \
+    return launch_state_t<DKv, 2, PDv, CCv>(GDN_STATE_ARGS);                             \
   }
-  GDN_STATE_CASE(64, 2)
-  GDN_STATE_CASE(128, 2)
-  GDN_STATE_CASE(256, 1)
+  GDN_STATE_CASE(64, 2, 64)
+  GDN_STATE_CASE(128, 2, 64)
+  GDN_STATE_CASE(256, 1, 64)
+  GDN_STATE_CASE(128, 2, 128)
+  // dk = 256 at C = 128: one column tile (two would spill)
+  if (s.dk == 256 && s.C == 128) return launch_state_t<256, 1, 1, 128>(GDN_STATE_ARGS);
 #undef GDN_STATE_CASE
+#undef GDN_STATE_ARGS
   return hipErrorInvalidValue;
 }
 

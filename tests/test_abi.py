@@ -62,7 +62,7 @@ def test_workspace_size():
     assert gdn.gdn_prefill_workspace_size(prob(flags=2)) == 0
     # grows with the chunk upper bound N / C + B
     assert gdn.gdn_prefill_workspace_size(prob(B=40)) > ws
-    assert gdn.gdn_prefill_workspace_size(prob(), 32) == 0          # only C = 64
+    assert gdn.gdn_prefill_workspace_size(prob(), 32) == 0          # C = 64 or 128 only
     assert gdn.gdn_prefill_workspace_size(prob(HV=24)) == 0         # HV % H != 0
     assert gdn.gdn_prefill_workspace_size(prob(dk=96)) == 0         # unsupported head dim
     assert gdn.gdn_prefill_workspace_size(prob(dtype=7)) == 0
@@ -83,7 +83,7 @@ def test_error_paths_return_before_launch():
     assert call(prob(N=-1)) == gdn.GDN_ERR_INVALID_ARG
     assert call(prob(dtype=3)) == gdn.GDN_ERR_INVALID_ARG
     assert call(prob(), chunk=0) == gdn.GDN_ERR_INVALID_ARG
-    assert call(prob(), chunk=128) == gdn.GDN_ERR_UNSUPPORTED
+    assert call(prob(), chunk=96) == gdn.GDN_ERR_UNSUPPORTED
     assert call(prob(dk=96)) == gdn.GDN_ERR_UNSUPPORTED
     assert call(prob(dv=512)) == gdn.GDN_ERR_UNSUPPORTED
     assert call(prob(pool=0)) == gdn.GDN_ERR_INVALID_ARG
@@ -110,7 +110,25 @@ def test_state_schedule():
     assert S(prob(N=8192, B=63, H=1, HV=1, pool=63)) == gdn.GDN_SCHEDULE_SEGMENTS
     assert S(prob(dtype=gdn.GDN_DTYPE_F32)) == gdn.GDN_SCHEDULE_FP32
     assert S(prob(HV=24)) == -1
-    assert S(prob(), 128) == -1
+    assert S(prob(), 96) == -1
+    # C = 128: column slices, never segments
+    assert S(prob(N=131072, B=1, HV=32, pool=1), 128) == gdn.GDN_SCHEDULE_COLUMN_SLICES
+
+
+def test_chunk_size_128():
+    """C = 128 serves bf16 inputs with dk of 128 or 256; fp32 inputs, dk = 64 and the
+    backward take C = 64 only. Its workspace holds half as many chunks, each with twice the
+    rows of A_qk."""
+    ws64 = gdn.gdn_prefill_workspace_size(prob())
+    ws128 = gdn.gdn_prefill_workspace_size(prob(), 128)
+    assert ws128 > 0 and ws128 % 256 == 0 and ws128 != ws64
+    assert gdn.gdn_prefill_workspace_size(prob(dk=256, dv=64), 128) > 0
+    assert gdn.gdn_prefill_workspace_size(prob(dtype=gdn.GDN_DTYPE_F32), 128) == 0
+    assert gdn.gdn_prefill_workspace_size(prob(dk=64), 128) == 0
+    assert gdn.gdn_prefill_bwd_workspace_size(prob(), 128) == 0
+    assert call(prob(dtype=gdn.GDN_DTYPE_F32), chunk=128) == gdn.GDN_ERR_UNSUPPORTED
+    assert call(prob(dk=64), chunk=128) == gdn.GDN_ERR_UNSUPPORTED
+    assert call(prob(), chunk=128, ws_bytes=1024) == gdn.GDN_ERR_WORKSPACE
 
 
 def test_grids_beyond_launch_limits_are_refused():

@@ -13,22 +13,25 @@
 // between chunks remains sequential over ceil(T/C) steps).
 //
 // Work split: one workgroup per (request, value head, NC x 16 state rows), with three
-// roles.
-//   * Two state waves. Wave hs holds dk rows hs * DK/2 .. of the NC x 16 columns of S^T
-//     in fp32 registers for the whole request, and forms P = W<- S^T and U for tokens
-//     32 hs .. 32 hs + 31 over all of dk. The fp16 copies of the two S^T halves and of
-//     the two U halves, which the output waves need anyway, are the only data the two
-//     waves exchange (LDS, double-buffered). Each wave then updates its own rows with
-//     both halves of U. Two barriers per chunk: one after the S^T copies, one after the
-//     U copies.
-//   * NO output waves form O from those LDS copies off the state chain: Qh S^T between
-//     the two barriers, A_qk U after the second. They compute O^T (operands swapped), so
-//     each lane holds four consecutive columns of one token row, and write O in bf16 to
-//     a double-buffered output tile in LDS.
+// roles; the chunk size C is 64 or 128.
+//   * C / 32 state waves (two at C = 64). Wave hs holds dk rows hs * DK / (C / 32) .. of
+//     the NC x 16 columns of S^T in fp32 registers for the whole request, and forms
+//     P = W<- S^T and U for tokens 32 hs .. 32 hs + 31 over all of dk. The fp16 copies of
+//     the S^T slices and of the U token steps, which the output waves need anyway, are
+//     the only data the state waves exchange (LDS, double-buffered). Each wave then
+//     updates its own rows with every token step of U. Two barriers per chunk: one after
+//     the S^T copies, one after the U copies.
+//   * C / 32 output waves form O from those LDS copies off the state chain: Qh S^T between
+//     the two barriers, A_qk U after the second, two row tiles each. They compute O^T
+//     (operands swapped), so each lane holds four consecutive columns of one token row,
+//     and write O in bf16 to a double-buffered output tile in LDS.
 //   * One store wave copies each finished tile to out with row-contiguous 16-byte
 //     stores, so that no wave that waits for its prefetched operands has stores queued
 //     among its loads (a wave's loads and stores retire in order). This is up to
-//     dk = 128; at dk = 256 the output waves store O themselves (see kStoreWaves).
+//     dk = 128 at C = 64; otherwise the output waves store O themselves (see
+//     kStoreWaves).
+// With C / 32 state waves each wave's share of a chunk's operands, and so its registers,
+// is the same at both chunk sizes.
 // Every operand comes straight from global memory into MFMA operand registers, in the
 // fragment orders the prep kernel wrote (one contiguous 1 KiB piece per fragment). Two
 // register sets (one at dk = 256 and with four column tiles) alternate between chunks,
@@ -468,8 +471,8 @@ hipError_t launch_mfma_state(const void* qf, const void* kf, const int64_t* cu_s
   // workgroups walking the chains (at dk = dv = 256 on one request of 8 heads,
   // 533 -> 442 us). dv is a multiple of 64. At C = 64 loads run two chunks ahead with up
   // to two column tiles at dk <= 128, one chunk ahead otherwise, where two register sets
-  // would not fit; at C = 128 (twice the operands per chunk) one chunk ahead, two at
-  // dk = 128 with up to two column tiles.
+  // would not fit. At C = 128 the same rule at dk = 128; at dk = 256 one column tile and
+  // one chunk ahead (two column tiles would spill).
   const int64_t pairs = s.B * s.HV;
   const bool narrow = pairs * (s.dv / 32) < 256;
   const bool wide = s.dk <= 128 && pairs * (s.dv / 64) >= 256;

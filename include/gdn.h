@@ -97,7 +97,13 @@ typedef struct {
  * or 0 if the problem or chunk size is invalid. Host only, no HIP calls. */
 size_t gdn_prefill_workspace_size(const gdn_problem_t* prob, int32_t chunk_size);
 
-/* The prefill forward (see the top of this file). chunk_size must be 64.
+/* The prefill forward (see the top of this file). chunk_size: 64, or 128 for bf16 inputs
+ * with dk of 128 or 256 (the pymllm page's Torch function defaults to 128, its kernel entry
+ * point to 64, Module Contents); any other value, or 128 with fp32 inputs or dk = 64,
+ * returns GDN_ERR_UNSUPPORTED. The result does not depend on it beyond rounding; 64 is the
+ * faster schedule on every measured shape (128 doubles the per-token work of the chunk
+ * preparation and leaves the state pass's time per token unchanged), and the segment scan
+ * of long requests runs at 64 only.
  * workspace: device memory of at least gdn_prefill_workspace_size bytes, 256-byte
  * aligned; its contents on entry do not matter. stream: a hipStream_t or NULL.
  * When N <= GDN_SPLIT_MEAN_LENGTH * B, requests of 1 .. GDN_SHORT_REQUEST tokens run
@@ -150,8 +156,9 @@ gdn_status_t gdn_prefill_fwd_noalloc(const void* q, const void* k, const void* v
 
 /* Stages of one call, in launch order, for gdn_prefill_fwd_events. */
 #define GDN_NUM_STAGES 5 /* 0: chunk table (and, for fp32 inputs, the gates and log
-                            cumulative decay; for bf16 inputs of at most 64 requests the
-                            chunk prep forms the table and this stage launches nothing);
+                            cumulative decay; for bf16 inputs of at most 64 requests at
+                            C = 64 the chunk prep forms the table and this stage launches
+                            nothing);
                             1: chunk prep (for bf16 inputs including the gates; Grams, the
                             one inverse, W<- and U~); 2: operator pass of the segment scan
                             (requests cut into segments: each segment's state from zero and
@@ -175,8 +182,8 @@ gdn_status_t gdn_prefill_nonfinite(const void* workspace, size_t workspace_bytes
  *   GDN_SCHEDULE_COLUMN_SLICES  bf16 inputs: one workgroup per (request, value head, 16, 32
  *                               or 64 state rows: the widest that still fills the device),
  *                               each walking its request's chunks; used when the 32-row
- *                               workgroups alone fill the device, when dk = 256 and above
- *                               64 requests.
+ *                               workgroups alone fill the device, when dk = 256, above
+ *                               64 requests and at chunk size 128.
  *   GDN_SCHEDULE_SEGMENTS       bf16 inputs: requests cut into segments of chunks (operator
  *                               pass, combine, output pass) with one workgroup per
  *                               (segment, value head, 128 state rows).

@@ -125,3 +125,21 @@ def test_c128_determinism_and_c64_agreement():
     rel = np.linalg.norm(pool64 - outs[0][1]) / np.linalg.norm(pool64)
     assert rel <= 2e-3, rel
     torch.cuda.synchronize()
+
+
+def test_short_requests_split_at_c128():
+    """A batch of short requests on average (N <= 64 B) at C = 128: the requests of at
+    most GDN_SHORT_REQUEST tokens take the token recurrence, the others the C = 128 chunked
+    kernels, in one call; against the oracle, and against the same call with every
+    request chunked."""
+    import gated_deltanet_prefill_gdn_amd as gdn
+    lengths = [3, 70, 5, 130, 1, 9, 40, 10, 11, 0]
+    assert sum(lengths) <= 64 * len(lengths)
+    p = gdn_synth.make_problem(1296, lengths, 2, 4, 128, 128, dtype="bf16", pool=11,
+                               cache_indices=[10, 0, 9, 1, 8, 2, 7, 3, 6, 4], state_std=0.2)
+    ref = oracle.prefill(p)
+    out, pool, _ = run_gpu(p, "c128-split", chunk_size=128)
+    compare(p, out, pool, ref)
+    out_all, pool_all, _ = run_gpu(p, "c128-chunk-all", chunk_size=128,
+                                   flags=gdn.GDN_FLAG_CHUNK_ALL)
+    compare(p, out_all, pool_all, ref)

@@ -1,6 +1,7 @@
-// Chunk preparation on matrix cores (bf16 inputs): one workgroup per (chunk, value head).
+// Chunk preparation on matrix cores (bf16 inputs), at C = 64 (this kernel) and C = 128 (the
+// second kernel of this file).
 //
-// Row convention (S is dv x dk; K, Q, V are the chunk's n <= 64 rows; G the chunk-local
+// Row convention (S is dv x dk; K, Q, V are the chunk's n <= C rows; G the chunk-local
 // inclusive log cumulative gate; r_k = 1/|k|, r_q = 1/|q|):
 //   A    = tril(diag(beta r_k) K K^T diag(r_k), -1)       Gram of raw bf16 keys, exact
 //                                                         products, fp32 accumulation

@@ -143,3 +143,28 @@ def test_short_requests_split_at_c128():
     out_all, pool_all, _ = run_gpu(p, "c128-chunk-all", chunk_size=128,
                                    flags=gdn.GDN_FLAG_CHUNK_ALL)
     compare(p, out_all, pool_all, ref)
+
+
+@pytest.mark.parametrize("case", range(6))
+def test_random_shapes_at_c128(case):
+    """Seeded random configurations at C = 128: request counts on both sides of 64, lengths
+    with empty and partial chunks on both sides of 64 and 128, grouped-head ratios up to 4,
+    dk of 128 or 256 with every dv, a shuffled pool with spare slots, gates from gentle to
+    strong decay, with and without the short-request split."""
+    import gated_deltanet_prefill_gdn_amd as gdn
+    rng = np.random.default_rng(1300 + case)
+    B = int(rng.choice([1, 3, 17, 70]))
+    lengths = [int(x) if rng.random() > 0.15 else 0 for x in rng.integers(1, 400, B)]
+    H = int(rng.choice([1, 2, 4]))
+    HV = H * int(rng.choice([1, 2, 4]))
+    dk = int(rng.choice([128, 256]))
+    dv = int(rng.choice([64, 128, 256]))
+    pool = B + int(rng.integers(0, 5))
+    p = gdn_synth.make_problem(1300 + case, lengths, H, HV, dk, dv, dtype="bf16", pool=pool,
+                               cache_indices=list(rng.permutation(pool)[:B]),
+                               a_mean=float(rng.uniform(-3.0, 1.0)),
+                               b_mean=float(rng.uniform(-1.0, 1.0)),
+                               state_std=float(rng.choice([0.0, 0.1, 0.5])))
+    flags = gdn.GDN_FLAG_CHUNK_ALL if case % 2 else 0
+    out, pool_gpu, _ = run_gpu(p, f"c128-random-{case}", chunk_size=128, flags=flags)
+    compare(p, out, pool_gpu, oracle.prefill(p))

@@ -14,7 +14,9 @@
 // workgroup covers kRowsPerThread rows per lane group of one (request, value head), so
 // a wave keeps kRowsPerThread x 2 KiB of state loads in flight, all issued before the
 // first wait. The state is read once and written once: the kernel is bound by HBM
-// bandwidth.
+// bandwidth. Both the state loads and the state stores are non-temporal (the rows are
+// touched once per call): with both, the decode workload's step takes 0.376 ms instead of
+// 0.415 (5.8 instead of 5.2 TB/s); either alone changes nothing (measured).
 #include "gdn_internal.h"
 
 namespace gdn {
@@ -136,8 +138,9 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
   f32x4 s[NR][2];
 #pragma unroll
   for (int j = 0; j < NR; ++j) {
-    s[j][0] = *reinterpret_cast<const f32x4*>(Sp + j * RPW * DK);
-    s[j][1] = *reinterpret_cast<const f32x4*>(Sp + j * RPW * DK + DK / 2);
+    s[j][0] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(Sp + j * RPW * DK));
+    s[j][1] =
+        __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(Sp + j * RPW * DK + DK / 2));
   }
 
   // Normalised k and q slices, and kh . qh.
@@ -201,8 +204,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
       n0[e] = __builtin_fmaf(alpha, s[j][0][e], u * kk[e]);
       n1[e] = __builtin_fmaf(alpha, s[j][1][e], u * kk[4 + e]);
     }
-    *reinterpret_cast<f32x4*>(Sp + j * RPW * DK) = n0;
-    *reinterpret_cast<f32x4*>(Sp + j * RPW * DK + DK / 2) = n1;
+    __builtin_nontemporal_store(n0, reinterpret_cast<f32x4*>(Sp + j * RPW * DK));
+    __builtin_nontemporal_store(n1, reinterpret_cast<f32x4*>(Sp + j * RPW * DK + DK / 2));
     if (gl == 0) {
       const float o = __builtin_fmaf(alpha, pq[j], kq * u);
       const int64_t oi = pair * DV + r;
@@ -253,8 +256,9 @@ __global__ __launch_bounds__(kDecodeThreads) void recurrent_kernel(
   f32x4 s[NR][2];
 #pragma unroll
   for (int j = 0; j < NR; ++j) {
-    s[j][0] = *reinterpret_cast<const f32x4*>(Sp + j * RPW * DK);
-    s[j][1] = *reinterpret_cast<const f32x4*>(Sp + j * RPW * DK + DK / 2);
+    s[j][0] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(Sp + j * RPW * DK));
+    s[j][1] =
+        __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(Sp + j * RPW * DK + DK / 2));
   }
 
   // One token's inputs; the next token's are loaded while the current one is applied
@@ -346,8 +350,8 @@ __global__ __launch_bounds__(kDecodeThreads) void recurrent_kernel(
   }
 #pragma unroll
   for (int j = 0; j < NR; ++j) {
-    *reinterpret_cast<f32x4*>(Sp + j * RPW * DK) = s[j][0];
-    *reinterpret_cast<f32x4*>(Sp + j * RPW * DK + DK / 2) = s[j][1];
+    __builtin_nontemporal_store(s[j][0], reinterpret_cast<f32x4*>(Sp + j * RPW * DK));
+    __builtin_nontemporal_store(s[j][1], reinterpret_cast<f32x4*>(Sp + j * RPW * DK + DK / 2));
   }
 }
 

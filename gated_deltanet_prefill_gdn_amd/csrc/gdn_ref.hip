@@ -27,6 +27,11 @@
 // steps are four consecutive floats: one 16-byte load instead of four. The operands are
 // stored (or staged) so that those runs are contiguous: U~ and K~ are written transposed,
 // and U is kept transposed in LDS.
+//
+// The prep kernel writes its outputs with non-temporal stores: the state kernel reads each
+// block once per workgroup from the L2 it is written through, and dirty lines left in the
+// caches slow those reads (measured: 2.6% off the dense batch's call, 1.2% off the wide-head
+// one).
 #include "gdn_internal.h"
 #include "gdn_mfma.h"
 
@@ -250,7 +255,8 @@ __global__ __launch_bounds__(256) void ref_prep_kernel(
       acc = mma4(a, b, acc);
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) Wp[(int64_t)(16 * I + 4 * g + i) * dk + 16 * jd + m] = acc[i];
+    for (int i = 0; i < 4; ++i)
+      __builtin_nontemporal_store(acc[i], &Wp[(int64_t)(16 * I + 4 * g + i) * dk + 16 * jd + m]);
   }
   {
     f32x4 acc[4] = {};
@@ -269,24 +275,24 @@ __global__ __launch_bounds__(256) void ref_prep_kernel(
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int rr = 16 * I + 4 * g + i, col = 16 * J + m;
-        Ap[rr * C + col] =
-            (J <= I && col <= rr && rr < n)
-                ? __builtin_amdgcn_exp2f((float)(sm.G2[rr] - sm.G2[col])) * sm.rq[rr] *
-                      sm.rk[col] * acc[J][i]
-                : 0.f;
+        const float x = (J <= I && col <= rr && rr < n)
+                            ? __builtin_amdgcn_exp2f((float)(sm.G2[rr] - sm.G2[col])) *
+                                  sm.rq[rr] * sm.rk[col] * acc[J][i]
+                            : 0.f;
+        __builtin_nontemporal_store(x, &Ap[rr * C + col]);
       }
   }
   float* Kp = Kft + pair * (int64_t)C * dk;  // K~ transposed: [dk][C]
 #pragma unroll
   for (int idx = tid; idx < C * dk; idx += 256) {
     const int j = idx / C, r = idx - j * C;
-    Kp[idx] = sm.kd[r] * sm.tile[r][j];
+    __builtin_nontemporal_store(sm.kd[r] * sm.tile[r][j], &Kp[idx]);
   }
   float* Qp = Qf + pair * (int64_t)C * dk + (int64_t)qr * dk + 4 * g;
   const float eqr = sm.eq[qr];  // zero past n
 #pragma unroll
   for (int kb = 0; kb < dk / 16; ++kb)
-    *reinterpret_cast<f32x4*>(Qp + 16 * kb) = eqr * qa[kb];
+    __builtin_nontemporal_store(eqr * qa[kb], reinterpret_cast<f32x4*>(Qp + 16 * kb));
   __syncthreads();  // the K tile and T1 are no longer read
   // ---- U~ = T2 V with T2 = (Gamma o T) diag(beta), written transposed: [dv][C]
   for (int idx = tid; idx < C * C; idx += 256) {
@@ -312,7 +318,8 @@ __global__ __launch_bounds__(256) void ref_prep_kernel(
       for (int s = 0; s < 4; ++s) b[s] = sm.tile[k0 + 4 * g + s][16 * jd + m];
       acc = mma4(a, b, acc);
     }
-    *reinterpret_cast<f32x4*>(&Up[(int64_t)(16 * jd + m) * C + 16 * I + 4 * g]) = acc;
+    __builtin_nontemporal_store(
+        acc, reinterpret_cast<f32x4*>(&Up[(int64_t)(16 * jd + m) * C + 16 * I + 4 * g]));
   }
 }
 

@@ -173,3 +173,36 @@ def test_random_shapes_at_c128(case):
     flags = gdn.GDN_FLAG_CHUNK_ALL if case % 2 else 0
     out, pool_gpu, _ = run_gpu(p, f"c128-random-{case}", chunk_size=128, flags=flags)
     compare(p, out, pool_gpu, oracle.prefill(p))
+
+
+def test_other_entry_points_at_c128():
+    """At C = 128 the no-allocation entry point (built-in workspace) and the per-stage
+    events entry point give the workspace entry point's result bit for bit."""
+    import torch
+    import gated_deltanet_prefill_gdn_amd as gdn
+    p = gdn_synth.make_problem(1297, [700, 129, 64], 2, 4, 128, 128, dtype="bf16",
+                               state_std=0.2)
+    d = to_device(p)
+    pool0 = d["state_pool"].clone()
+    args = lambda: (d["q"], d["k"], d["v"], d["a"], d["b"], d["A_log"], d["dt_bias"],
+                    d["state_pool"], d["cache_indices"], d["cu_seqlens"])
+    announce("c128 gdn_prefill_fwd (workspace)")
+    ref = gdn.gdn_prefill_fwd(*args(), chunk_size=128)
+    torch.cuda.synchronize()
+    pool_ref = d["state_pool"].clone()
+    d["state_pool"].copy_(pool0)
+    announce("c128 gdn_prefill_fwd_noalloc")
+    out = torch.empty_like(ref)
+    gdn.gdn_prefill_fwd_noalloc(*args(), out, chunk_size=128)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref) and torch.equal(d["state_pool"], pool_ref)
+    d["state_pool"].copy_(pool0)
+    announce("c128 gdn_prefill_fwd_events")
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(gdn.GDN_NUM_STAGES + 1)]
+    for e in evs:
+        e.record()  # creates the underlying event
+    out2 = gdn.gdn_prefill_fwd_events(*args(), [e.cuda_event for e in evs], chunk_size=128)
+    torch.cuda.synchronize()
+    assert torch.equal(out2, ref) and torch.equal(d["state_pool"], pool_ref)
+    compare(p, ref.float().cpu().numpy().astype(np.float64), pool_ref.cpu().numpy(),
+            oracle.prefill(p))

@@ -212,8 +212,9 @@ gdn_status_t run_prefill(const void* q, const void* k, const void* v, const floa
   float* beta = (float*)(ws + L.beta);
   int32_t* nonfinite = (int32_t*)(ws + L.flags);
 
-  // Up to 64 requests the MFMA chunk prep forms the chunk table itself (one scan per
-  // workgroup) and writes chunk_off for the state pass: one launch fewer.
+  // Up to 64 requests the MFMA chunk prep at C = 64 forms the chunk table itself (one scan
+  // per workgroup) and writes chunk_off for the state pass: one launch fewer. The C = 128
+  // prep reads the plan kernel's table.
   const bool self_plan = path == Path::kMfma && s.B <= kMaxSelfPlanRequests && s.C == 64;
   if (!mark(0)) return GDN_ERR_HIP;
   if (!self_plan &&

@@ -50,10 +50,7 @@ namespace {
 using namespace mfma;
 constexpr int C = 64;
 constexpr int kComputeWaves = 4;
-#ifndef GDN_CHAIN_LOADERS
-#define GDN_CHAIN_LOADERS 1
-#endif
-constexpr int kLoaderWaves = GDN_CHAIN_LOADERS;
+constexpr int kLoaderWaves = 1;
 constexpr int kColsPerBlock = 128;  // state columns of one workgroup
 
 typedef __attribute__((address_space(3))) void* lds_ptr;

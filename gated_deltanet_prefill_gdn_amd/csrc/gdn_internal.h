@@ -91,9 +91,10 @@ hipError_t launch_ref_state(const int64_t* cu_seqlens, const int64_t* cache_indi
                             const Shape& s, float* state_pool, void* out, int32_t* nonfinite,
                             hipStream_t st);
 
-// self_plan (at most kMaxSelfPlanRequests requests): the prep kernel forms the chunk table
-// itself and writes chunk_off (B + 1 entries) for the state pass; chunk_seq is then not
-// read and the plan kernel need not run.
+// The chunk prep and the state pass at s.C = 64 or 128 (128: dk of 128 or 256).
+// self_plan (C = 64, at most kMaxSelfPlanRequests requests): the prep kernel forms the
+// chunk table itself and writes chunk_off (B + 1 entries) for the state pass; chunk_seq is
+// then not read and the plan kernel need not run.
 constexpr int kMaxSelfPlanRequests = 64;
 hipError_t launch_mfma_prep(const void* q, const void* k, const void* v,
                             const int64_t* cu_seqlens, int32_t* chunk_off,

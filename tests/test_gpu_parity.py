@@ -404,3 +404,18 @@ def test_long_batches_are_chunked_whole():
     out_c, pool_c, _ = run_gpu(p, "long-batch-chunk-all", flags=gdn.GDN_FLAG_CHUNK_ALL)
     np.testing.assert_array_equal(out_d, out_c)
     np.testing.assert_array_equal(pool_d, pool_c)
+
+
+@pytest.mark.parametrize("dtype,H,G,chunk", [("bf16", 3, 3, 64), ("bf16", 5, 2, 64),
+                                             ("f32", 3, 3, 64), ("bf16", 3, 3, 128)])
+def test_grouped_value_heads_odd_ratios(dtype, H, G, chunk):
+    """Grouped value heads with ratios and head counts that are not powers of two (H = 3
+    or 5, HV = H G): the head map h = hv / G, the prep's group items and the state pass's
+    pair numbering, against the oracle, with ragged requests and a shuffled pool."""
+    import gated_deltanet_prefill_gdn_amd as gdn
+    lengths = [700, 65, 0, 300, 1, 129]
+    p = gdn_synth.make_problem(890 + H * G + chunk, lengths, H, H * G, 128, 128, dtype=dtype,
+                               pool=8, cache_indices=[7, 1, 4, 0, 6, 2], state_std=0.2)
+    out, pool, _ = run_gpu(p, f"odd-groups-{dtype}-H{H}-G{G}-C{chunk}", chunk_size=chunk,
+                           flags=gdn.GDN_FLAG_CHUNK_ALL)
+    compare(p, out, pool, oracle.prefill(p))

@@ -86,6 +86,11 @@ CASES = {
                         a_mean=-3.0, state_std=0.2),
     "dk64-dv256": dict(seed=94, lengths=[70], H=1, HV=2, dk=64, dv=256, dtype="bf16",
                        b_mean=1.0, state_std=0.2),
+    # three value heads per q/k head (dq, dk sum over them), strong decay
+    "odd-groups-strong-decay": dict(seed=98, lengths=[100, 33, 257], H=3, HV=9, dk=128,
+                                    dv=128, dtype="bf16", a_mean=2.0, state_std=0.3),
+    "dk256-dv256": dict(seed=99, lengths=[50, 20], H=1, HV=2, dk=256, dv=256, dtype="f32",
+                        a_mean=-2.0, state_std=0.2),
 }
 
 
@@ -115,3 +120,34 @@ def test_backward_is_deterministic():
     g2, _ = _run(p, 98, "bwd-det-2")
     for n in NAMES:
         np.testing.assert_array_equal(g1[n], g2[n])
+
+
+def test_backward_workload1_sampled_head():
+    """The dense-batch workload (4 x 4096 tokens, 16 heads) at full size on the GPU, the
+    gradients of value head 0 (and of its q/k head: H = HV) against the oracle's backward of
+    that head alone over every token; the heads are independent when H = HV."""
+    import copy
+    import torch
+    import gated_deltanet_prefill_gdn_amd as gdn
+    p = gdn_synth.workload(1)
+    d = to_device(p)
+    dout_dev, dout_val, dstate = _upstream(p, 96)
+    t = torch.from_numpy(np.ascontiguousarray(dout_dev))
+    dout = t.view(torch.bfloat16).to("cuda:0")
+    announce(f"workload1 gdn_prefill_bwd N={p.N} B={p.B} H={p.H} HV={p.HV}")
+    g = gdn.gdn_prefill_bwd(d["q"], d["k"], d["v"], d["a"], d["b"], d["A_log"], d["dt_bias"],
+                            d["state_pool"], d["cache_indices"], d["cu_seqlens"], dout,
+                            torch.from_numpy(dstate).to("cuda:0"))
+    torch.cuda.synchronize()
+    sub = copy.copy(p)
+    sub.q, sub.k, sub.v = p.q[:, [0]], p.k[:, [0]], p.v[:, [0]]
+    sub.a, sub.b = p.a[:, [0]], p.b[:, [0]]
+    sub.A_log, sub.dt_bias = p.A_log[[0]], p.dt_bias[[0]]
+    sub.state_pool = p.state_pool[:, [0]]
+    sub.H, sub.HV = 1, 1
+    ref = bw.prefill_backward(sub, dout_val[:, [0]], dstate[:, [0]].astype(np.float64))
+    got = {"dq": g["dq"][:, [0]], "dk": g["dk"][:, [0]], "dv": g["dv"][:, [0]],
+           "da": g["da"][:, [0]], "db": g["db"][:, [0]], "dA_log": g["dA_log"][[0]],
+           "ddt_bias": g["ddt_bias"][[0]], "dstate0": g["dstate0"][:, [0]]}
+    got = {n: x.cpu().numpy().astype(np.float64) for n, x in got.items()}
+    _compare(got, ref, "workload1 head 0")

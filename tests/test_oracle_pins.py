@@ -199,7 +199,7 @@ def test_chunk_forms_equal_recurrence_gentle(C):
         assert rel(pool, r.state_pool) < 1e-12, variant
 
 
-@pytest.mark.parametrize("C", [4, 16, 64])
+@pytest.mark.parametrize("C", [4, 16, 64, 128])
 def test_chunk_forms_equal_recurrence_strong_decay(C):
     """a ~ N(0,1), exp(A_log) up to 16: the log cumulative gate reaches hundreds
     inside a chunk; only the forms without 1/gamma stay finite."""

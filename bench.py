@@ -2,7 +2,9 @@
 
 A step is one gdn_prefill_fwd call (every stage of the path) over the dense-batch
 bf16 workload: 4 requests x 4096 tokens, H = HV = 16, dk = dv = 128, C = 64, with
-inputs resident in HBM. Prints one JSON line.
+inputs resident in HBM. Prints one JSON line. Workloads 2-4 are timed as sub-results, and
+every bf16 workload with dk >= 128 also at chunk size 128 on the same inputs
+(``chunk_128``), the measured comparison of the two schedules.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 
@@ -756,6 +758,21 @@ def measure_prefill(p, steps: int, warmup: int, cold_steps: int, copy_calibratio
         hip.destroy(e1)
         del scratch
 
+    # The same inputs at chunk size 128, where the call takes it (bf16, dk >= 128): the
+    # measured comparison of the two schedules, timed like the sub-results.
+    c128 = None
+    if C == 64 and p.dtype == "bf16" and p.dk >= 128:
+        ws128 = torch.empty(gdn.gdn_prefill_workspace_size(prob, 128), dtype=torch.uint8,
+                            device=dev)
+        step128 = lambda: gdn.gdn_prefill_fwd(q, k, v, a, b, A_log, dt_bias, pool, idx, cu,
+                                              chunk_size=128, out=out, workspace=ws128,
+                                              stream=stream)
+        ms128, ev128, _, _ = _time_launches(step128, stream, max(3, steps // 2),
+                                            max(3, warmup // 2))
+        c128 = {"chunk_size": 128, "ms_per_step": ms128, "tokens_per_s": p.N / (ms128 * 1e-3),
+                "call_ms_events": ev128, "vs_chunk_64": ms_per_step / ms128}
+        del ws128
+
     if copy_calibration:
         src = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev).fill_(3)
         dst = torch.empty_like(src)
@@ -834,6 +851,7 @@ def measure_prefill(p, steps: int, warmup: int, cold_steps: int, copy_calibratio
         "stages": stages,
         "state_schedule": sched,
         "chunk_size": C,
+        "chunk_128": c128,
         "kernel_source_hash": src_hash,
     }
 
@@ -872,6 +890,7 @@ def bench_prefill(args):
         "effective": m["effective"],
         "call_ms_events": m["call_ms_events"],
         "stages": m["stages"],
+        "chunk_128": m["chunk_128"],
         "kernel_source_hash": m["kernel_source_hash"],
     }
     if not args.no_cpu_baseline:
@@ -893,7 +912,8 @@ def bench_prefill(args):
                    "effective_tflops": sm["effective"]["tflops"],
                    "dominant_kernel": sm["roofline"]["kernel"],
                    "dominant_kernel_frac": sm["roofline"]["frac"],
-                   "roofline": sm["roofline"], "stages": sm["stages"]}
+                   "roofline": sm["roofline"], "stages": sm["stages"],
+                   "chunk_128": sm["chunk_128"]}
             if not args.no_cpu_baseline:
                 # the long request's 32 heads: two sampled heads bound the oracle's time
                 heads = [0, sp_.HV - 1] if sp_.N * sp_.HV > (1 << 21) else None

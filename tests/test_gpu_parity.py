@@ -419,3 +419,28 @@ def test_grouped_value_heads_odd_ratios(dtype, H, G, chunk):
     out, pool, _ = run_gpu(p, f"odd-groups-{dtype}-H{H}-G{G}-C{chunk}", chunk_size=chunk,
                            flags=gdn.GDN_FLAG_CHUNK_ALL)
     compare(p, out, pool, oracle.prefill(p))
+
+
+def test_concurrent_calls_on_two_streams():
+    """The library keeps no state between calls: two different problems run at the same
+    time on two streams (default priority), each with its own workspace, pool and output,
+    give the oracle's results, as they do one after the other."""
+    import torch
+    import gated_deltanet_prefill_gdn_amd as gdn
+    pa = gdn_synth.make_problem(980, [900, 300, 17], 2, 4, 128, 128, dtype="bf16",
+                                state_std=0.2)
+    pb = gdn_synth.make_problem(981, [1500, 64], 1, 2, 64, 256, dtype="bf16", state_std=0.3)
+    da, db = to_device(pa), to_device(pb)
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+    torch.cuda.synchronize()
+    announce("two streams: gdn_prefill_fwd x 2")
+    outs = []
+    for d, st in ((da, sa), (db, sb)):
+        with torch.cuda.stream(st):
+            outs.append(gdn.gdn_prefill_fwd(d["q"], d["k"], d["v"], d["a"], d["b"], d["A_log"],
+                                            d["dt_bias"], d["state_pool"], d["cache_indices"],
+                                            d["cu_seqlens"], stream=st))
+    torch.cuda.synchronize()
+    for p, d, out in ((pa, da, outs[0]), (pb, db, outs[1])):
+        compare(p, out.float().cpu().numpy().astype(np.float64), d["state_pool"].cpu().numpy(),
+                oracle.prefill(p))

@@ -1,7 +1,8 @@
 """The no-allocation prefill entry point (built-in device workspace) through the C ABI:
 its outputs and states equal those of gdn_prefill_fwd with a caller workspace, on two calls
-in a row (the second smaller, on the other state schedule), and a problem whose workspace
-exceeds the built-in array is refused before anything runs."""
+in a row (the second smaller, on the other state schedule); a problem whose workspace
+exceeds the built-in array is refused before anything runs; and the call captured into a
+HIP graph replays to the eager result."""
 import numpy as np
 import pytest
 
@@ -79,3 +80,43 @@ def test_noalloc_refuses_problems_beyond_its_array():
     torch.cuda.synchronize()
     assert torch.all(out == 7.0)
     np.testing.assert_array_equal(d["state_pool"].cpu().numpy(), p.state_pool)
+
+
+@pytest.mark.parametrize("lengths", [[300, 65, 7], [3, 70, 5, 9, 40]])
+def test_noalloc_replayed_from_a_hip_graph(lengths):
+    """The callers this entry point is for include code under graph capture: the call
+    captured into a HIP graph (torch.cuda.graph) and replayed four times, with eager pool
+    resets and synchronisations between the replays, gives the eager call's outputs and
+    states bit for bit every time (the second case takes the short-request split, so the
+    token recurrence is captured too)."""
+    import torch
+    import gated_deltanet_prefill_gdn_amd as gdn
+    p = gdn_synth.make_problem(990 + len(lengths), lengths, 2, 4, 128, 128, dtype="bf16",
+                               state_std=0.2)
+    d = to_device(p)
+    pool0 = d["state_pool"].clone()
+    out = torch.empty((p.N, p.HV, p.dv), dtype=d["v"].dtype, device="cuda:0")
+    args = (d["q"], d["k"], d["v"], d["a"], d["b"], d["A_log"], d["dt_bias"], d["state_pool"],
+            d["cache_indices"], d["cu_seqlens"])
+    s = torch.cuda.Stream()
+    announce(f"graph lengths={lengths}: eager call")
+    with torch.cuda.stream(s):
+        gdn.gdn_prefill_fwd_noalloc(*args, out, stream=s)
+    torch.cuda.synchronize()
+    ref_out, ref_pool = out.clone(), d["state_pool"].clone()
+    d["state_pool"].copy_(pool0)
+    torch.cuda.synchronize()
+    announce(f"graph lengths={lengths}: capture")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        gdn.gdn_prefill_fwd_noalloc(*args, out, stream=s)
+    torch.cuda.synchronize()
+    for i in range(4):
+        d["state_pool"].copy_(pool0)
+        out.zero_()
+        torch.cuda.synchronize()
+        announce(f"graph lengths={lengths}: replay {i}")
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_out), f"replay {i}: outputs differ"
+        assert torch.equal(d["state_pool"], ref_pool), f"replay {i}: states differ"

@@ -213,8 +213,10 @@ def gdn_recurrent_fwd(q, k, v, a, b, A_log, dt_bias, state_pool, cache_indices, 
 
 def gdn_prefill_fwd(q, k, v, a, b, A_log, dt_bias, state_pool, cache_indices, cu_seqlens,
                     chunk_size: int = 64, out=None, workspace=None, stream=None, flags: int = 0):
-    """``flags``: GDN_FLAG_* bits of the problem descriptor (GDN_FLAG_CHUNK_ALL: chunk every
-    request, none through the token recurrence)."""
+    """``chunk_size``: 64, or 128 for bf16 inputs with dk of 128 or 256 (the same result
+    within rounding; 64 is the faster schedule). ``flags``: GDN_FLAG_* bits of the problem
+    descriptor (GDN_FLAG_CHUNK_ALL: chunk every request, none through the token
+    recurrence)."""
     return _prefill(q, k, v, a, b, A_log, dt_bias, state_pool, cache_indices, cu_seqlens,
                     chunk_size, out, workspace, stream, None, flags)
 

@@ -126,7 +126,14 @@ size_t gdn_prefill_workspace_size(const gdn_problem_t* prob, int32_t chunk_size)
  *   - at magnitudes down to about 2^-10 (1e-3) the results keep the bf16 accuracy
  *     (outputs within 2e-2 rms plus their own bf16 rounding, states within 1e-3 relative
  *     of the fp64 recurrence); smaller values lose relative precision in fp16's
- *     subnormal range, silently.
+ *     subnormal range, silently;
+ *   - the read-out of a state takes fp16 copies of the state and of q, so an output also
+ *     carries an absolute error of a few 1e-4 (at most about 1e-3) of the initial
+ *     states' entry scale. That is within 2e-2 rms(o) while the outputs are not much
+ *     smaller than the states (as on the benchmarked workloads). Where the initial states
+ *     are about 50 times the outputs' rms or more (unit-scale states, small beta, strong
+ *     decay), a request's first outputs can exceed that part of the bar by up to this
+ *     error; the states keep their bar.
  * Inputs outside that range belong on the fp32 path (GDN_DTYPE_F32), which holds the
  * state, every intermediate and the output in fp32. */
 gdn_status_t gdn_prefill_fwd(const void* q, const void* k, const void* v, const float* a,

@@ -42,16 +42,17 @@ def _scaled_problem(shape, scale, seed):
     return p
 
 
-def _run(p, label):
+def _run(p, label, flags=0):
     import torch
     import gated_deltanet_prefill_gdn_amd as gdn
     d = to_device(p)
-    prob = gdn.problem_of(d["q"], d["k"], d["v"], d["state_pool"], d["cache_indices"])
+    prob = gdn.problem_of(d["q"], d["k"], d["v"], d["state_pool"], d["cache_indices"], flags)
     ws = torch.empty(gdn.gdn_prefill_workspace_size(prob), dtype=torch.uint8, device="cuda:0")
     ws.fill_(0xFF)  # the call itself must clear the flag
     announce(f"{label} N={p.N} B={p.B} HV={p.HV} schedule={gdn.gdn_prefill_state_schedule(prob)}")
     out = gdn.gdn_prefill_fwd(d["q"], d["k"], d["v"], d["a"], d["b"], d["A_log"], d["dt_bias"],
-                              d["state_pool"], d["cache_indices"], d["cu_seqlens"], workspace=ws)
+                              d["state_pool"], d["cache_indices"], d["cu_seqlens"], workspace=ws,
+                              flags=flags)
     flag = gdn.gdn_prefill_nonfinite(ws)
     return (out.float().cpu().numpy().astype(np.float64), d["state_pool"].cpu().numpy(), flag,
             gdn.gdn_prefill_state_schedule(prob))
@@ -82,3 +83,30 @@ def test_flag_clear_on_the_fp32_path():
     out, pool, flag, sched = _run(p, "flag-fp32")
     assert sched == 2 and not flag
     compare(p, out, pool, oracle.prefill(p))
+
+
+def test_initial_state_much_larger_than_the_outputs():
+    """Unit-scale initial states at dk = dv = 256 with small beta and strong decay: every
+    request's first outputs read the state (S q, entries of order 1), the rest are two
+    orders smaller, so rms(o) is about 1/50 of the state's entry scale. The read-out takes
+    the state and q as fp16 operand copies, whose rounding (2^-12 relative) leaves an
+    absolute error of a few 1e-4 of the state's scale on those first outputs: within the
+    documented envelope 2e-2 rms(o) + 2^-8 |o| + 1e-3 rms(S0), though not always within the
+    plain bar. The states keep their 1e-3 bar."""
+    import gated_deltanet_prefill_gdn_amd as gdn
+    lengths = [int(x) for x in np.random.default_rng(1400).integers(1, 600, 90)]
+    p = gdn_synth.make_problem(1400, lengths, 1, 4, 256, 256, dtype="bf16", a_mean=0.46,
+                               b_mean=-1.7, state_std=1.0)
+    out, pool, flag, _ = _run(p, "large-state", gdn.GDN_FLAG_CHUNK_ALL)
+    ref = oracle.prefill(p)
+    rms = float(np.sqrt(np.mean(ref.out ** 2)))
+    s0 = float(np.sqrt(np.mean(p.state_pool[p.cache_indices].astype(np.float64) ** 2)))
+    excess = np.abs(out - ref.out) - 2.0 ** -8 * np.abs(ref.out) - 2e-2 * rms
+    announce(f"large-state rms(o)={rms:.4f} rms(S0)={s0:.3f} "
+             f"max excess over the plain bar = {excess.max() / s0:.2e} rms(S0)")
+    assert s0 / rms > 20, "the case must have a state much larger than its outputs"
+    assert excess.max() <= 1e-3 * s0
+    for bi, slot in enumerate(p.cache_indices):
+        r = ref.state_pool[slot]
+        assert np.linalg.norm(pool[slot] - r) / np.linalg.norm(r) <= 1e-3
+    assert flag == 0

@@ -15,7 +15,8 @@ firings x 64 pairs, dk = dv = 128, bf16, every firing's state kept); with ``--op
 one gdn_recurrent_fwd call over a speculative-verification batch (512 requests x 4 tokens,
 the decode workload's heads and pool), the chunked gdn_prefill_fwd on the same call timed
 beside it; with ``--op backward`` one gdn_prefill_bwd call on the dense-batch workload. The
-JSON line then reports that call.
+JSON line then reports that call. ``--op pipelined`` times successive prefill calls back to
+back and pipelined over two streams (bench_pipelined).
 """
 from __future__ import annotations
 
@@ -1124,10 +1125,94 @@ def bench_crossover(args):
         "rows": rows, "kernel_source_hash": kernel_source_hash()}), flush=True)
 
 
+def bench_pipelined(args):
+    """Successive prefill calls as a serving loop issues them: back to back on one stream,
+    and pipelined over two streams, where each call starts once the previous call's chunk
+    prep has ended (gdn_prefill_fwd_events marks it), so that its prep overlaps the previous
+    call's state pass; the calls alternate between two sets of workspace, output and pool.
+    Prints one JSON line with the wall ms per call of each on workloads 1-4 (or the one
+    named by --workload): where a single call leaves compute units idle (one long request
+    at d = 256 fills half of the device in its state pass), the second stream fills them."""
+    import numpy as np
+    import torch
+
+    import gated_deltanet_prefill_gdn_amd as gdn
+    import gdn_synth
+
+    dev = torch.device("cuda:0")
+
+    def t(x, dt=None):
+        x = torch.from_numpy(np.ascontiguousarray(x))
+        return (x.view(dt) if dt is not None else x).to(dev)
+
+    rows = []
+    for wi in ([args.workload] if args.workload is not None else [1] + list(SUB_WORKLOADS)):
+        p = gdn_synth.workload(wi)
+        q, k, v = (t(getattr(p, n).view(np.int16), torch.bfloat16) for n in "qkv")
+        a, b, A_log, dt_bias = t(p.a), t(p.b), t(p.A_log), t(p.dt_bias)
+        idx, cu = t(p.cache_indices), t(p.cu_seqlens)
+        sets = []
+        for _ in range(2):
+            pool = t(p.state_pool.copy())
+            ws_bytes = gdn.gdn_prefill_workspace_size(gdn.problem_of(q, k, v, pool, idx))
+            evs = [torch.cuda.Event() for _ in range(gdn.GDN_NUM_STAGES + 1)]
+            for e in evs:
+                e.record()  # creates the event
+            sets.append({"pool": pool, "evs": evs,
+                         "out": torch.empty((p.N, p.HV, p.dv), dtype=v.dtype, device=dev),
+                         "ws": torch.empty(ws_bytes, dtype=torch.uint8, device=dev)})
+        streams = [torch.cuda.Stream(dev), torch.cuda.Stream(dev)]
+        torch.cuda.synchronize()
+
+        def call(st, stream):
+            gdn.gdn_prefill_fwd_events(q, k, v, a, b, A_log, dt_bias, st["pool"], idx, cu,
+                                       [e.cuda_event for e in st["evs"]], out=st["out"],
+                                       workspace=st["ws"], stream=stream)
+
+        def serial(n):
+            for i in range(n):
+                call(sets[i % 2], streams[0])
+
+        def pipelined(n):
+            for i in range(n):
+                if i > 0:  # event 2 is recorded when the previous call's prep has ended
+                    streams[i % 2].wait_event(sets[(i - 1) % 2]["evs"][2])
+                call(sets[i % 2], streams[i % 2])
+
+        def per_call_ms(f):
+            f(max(2, args.warmup))
+            torch.cuda.synchronize()
+            best = float("inf")
+            for _ in range(3):
+                t0 = time.perf_counter()
+                f(args.steps)
+                torch.cuda.synchronize()
+                best = min(best, (time.perf_counter() - t0) * 1e3 / args.steps)
+            return best
+
+        ms_s, ms_p = per_call_ms(serial), per_call_ms(pipelined)
+        row = {"workload": gdn_synth.WORKLOADS[wi], "index": wi, "tokens": int(p.N),
+               "serial_ms_per_call": round(ms_s, 4), "pipelined_ms_per_call": round(ms_p, 4),
+               "pipelined_tokens_per_s": p.N / (ms_p * 1e-3),
+               "pipelined_over_serial_rate": round(ms_s / ms_p, 3)}
+        rows.append(row)
+        print(json.dumps(row), file=sys.stderr, flush=True)
+        del q, k, v, a, b, sets
+        torch.cuda.empty_cache()
+    print(json.dumps({
+        "metric": "successive gdn_prefill_fwd calls: wall ms per call back to back on one "
+                  "stream and pipelined over two streams (each call after the previous "
+                  "call's chunk prep)",
+        "value": None, "unit": "ms", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "higher_is_better": False, "dtype": "bf16",
+        "data": "synthetic (seeded SplitMix64/Box-Muller)", "rows": rows,
+        "kernel_source_hash": kernel_source_hash()}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--op", choices=("prefill", "decode", "promote", "verify", "backward",
-                                     "crossover"),
+                                     "crossover", "pipelined"),
                     default="prefill",
                     help="the call a step times (default: the prefill forward)")
     ap.add_argument("--gpus", type=int, default=1)
@@ -1168,6 +1253,9 @@ def main():
         return
     if args.op == "crossover":
         bench_crossover(args)
+        return
+    if args.op == "pipelined":
+        bench_pipelined(args)
         return
 
     bench_prefill(args)

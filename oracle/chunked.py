@@ -16,7 +16,7 @@ Variants (all must agree with the recurrence):
 * ``saved_inverse`` -- same page, section Save one invert: N^-1 = G M^-1 G^-1 with
   the diagonal matrices G = diag(gamma), G^-1 = diag(1/gamma) taken literally
   (finite only while gamma does not underflow).
-* ``p3_literal`` -- the pymllm gdn_chunkwise page's form (section Algorithm): values
+* ``decay_divided`` -- the form of the pymllm gdn_chunkwise page (section Algorithm): values
   divided by the cumulative decay before the WY solve, u~ = M^-1 B G^-1 V, with the
   decay multiplied back in the output and state equations.
   The extracted w_i recursion is ill-typed; it is read as the matrix form of the
@@ -35,7 +35,7 @@ from __future__ import annotations
 import numpy as np
 from scipy.linalg import solve_triangular
 
-VARIANTS = ("two_inverses", "saved_inverse", "p3_literal", "safe")
+VARIANTS = ("two_inverses", "saved_inverse", "decay_divided", "safe")
 
 
 def l2norm_rows(x: np.ndarray, eps: float) -> np.ndarray:
@@ -97,7 +97,7 @@ def chunk_step(S, Q, K, V, g, beta, variant: str):
         S_new = gamma[-1] * S + U.T @ (np.diag(gamma[-1] / gamma) @ K)
         O = Gd @ Q @ S.T + (Gam * QKt) @ U
         return O, S_new
-    if variant == "p3_literal":
+    if variant == "decay_divided":
         gamma = np.cumprod(np.exp(g))
         dk, dv = K.shape[1], V.shape[1]
         W = np.zeros((n, dk))
